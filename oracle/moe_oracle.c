@@ -1,0 +1,191 @@
+/*
+ * Plain, slow CPU oracle of the sparse Mixture-of-Experts layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this file's library. It shares no code,
+ * header, table or helper with the GPU library, and the GPU library never
+ * calls it.
+ *
+ * Every floating-point step is carried out in double precision on the exact
+ * input values (bf16 and fp32 inputs widen to double without error). Loops
+ * follow the definitions on the pages one to one; there is no blocking, no
+ * fusion and no reordering beyond the definitions. OpenMP only splits the
+ * independent per-token and per-row loops; the slot pass is serial.
+ * Limits: E <= 1024 (fixed per-token arrays); the Python wrapper checks it.
+ *
+ * Sources (page title, then the step, slide or panel used):
+ *   [P1] "Mixture of Experts (MoE) 12段階極小ビジュアル解剖シミュレーター"
+ *        (12-step single-token MoE walk-through):
+ *        STEP 2 (router scores), STEP 3-4 (noise), STEP 5 (KeepTopK with a
+ *        -inf mask), STEP 6 (softmax), STEP 7 (dispatch), STEP 8-10 (expert
+ *        FFN: up-projection, ReLU, down-projection), STEP 11-12 (gate scaling
+ *        and weighted sum).
+ *   [P2] "nanoMoEの深層解剖：Mixture of Expertsにおける条件分岐を排除した並列演算実装"
+ *        (nanoMoE slides): slide 11 (router in full precision),
+ *        slides 12-13 (top-k then masked softmax), slide 14 and slides 15-23
+ *        (capacity: rank of each assignment in top-1-first, token order;
+ *        ranks at or past capacity dropped), slides 24-29 and 33-40 (combine
+ *        weights are the raw gates; a dropped assignment contributes 0).
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes):
+ *   - The pages' router runs in full precision (fp32). The ranking decision is
+ *     therefore taken on the float32 rounding of the double-precision score.
+ *   - Equal scores rank the lower expert index first.
+ *   - Capacity C = ceil(cf * k * N / E) over the call's N tokens (the slide's
+ *     get_capacity body is elided), evaluated in double.
+ *   - No renormalisation of gates after drops; all-dropped tokens output 0.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+/* ---------------------------------------------------------------------- */
+/* [P1 STEP 2, STEP 4]  s = W_g x + eps; the caller passes eps (= sigma*N(0,1)
+ * plus any constant score offset) as a dense [N,E] tensor or NULL.          */
+/* [P2 slide 11] the router runs in full precision: the decision value is the
+ * float32 rounding of the exact score.                                      */
+/* [P1 STEP 5] KeepTopK: the k largest scores, in descending order.          */
+/* [P1 STEP 6] softmax over the -inf-masked vector = softmax over the k kept
+ * scores, since exp(-inf) = 0.                                              */
+void oracle_router(int64_t N, int64_t d, int64_t E, int32_t k,
+                   const double *x, const double *Wg, const double *noise,
+                   float *scores, int32_t *idx, double *gate)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < N; ++t) {
+        float s[1024];
+        unsigned char taken[1024];
+        const double *xt = x + t * d;
+        for (int64_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            const double *w = Wg + e * d;
+            for (int64_t i = 0; i < d; ++i)
+                acc += w[i] * xt[i];
+            if (noise)
+                acc += noise[t * E + e];
+            s[e] = (float)acc;
+            taken[e] = 0;
+            if (scores)
+                scores[t * E + e] = s[e];
+        }
+        /* top-k by repeated selection; strict '>' keeps the lower index on ties */
+        for (int32_t j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || s[e] > s[best])
+                    best = e;
+            }
+            taken[best] = 1;
+            idx[t * k + j] = (int32_t)best;
+        }
+        /* softmax over the k survivors (shifted by the largest; same value) */
+        double m = (double)s[idx[t * k]];
+        double den = 0.0;
+        for (int32_t j = 0; j < k; ++j)
+            den += exp((double)s[idx[t * k + j]] - m);
+        for (int32_t j = 0; j < k; ++j)
+            gate[t * k + j] = exp((double)s[idx[t * k + j]] - m) / den;
+    }
+}
+
+/* [P2 slide 14] per-expert capacity for a call of N tokens.                 */
+int64_t oracle_capacity(int64_t N, int64_t E, int32_t k, double cf)
+{
+    if (N <= 0)
+        return 0;
+    return (int64_t)ceil(cf * (double)((int64_t)k * N) / (double)E);
+}
+
+/* [P2 slides 14-23] slot of each assignment: its rank among the assignments
+ * to the same expert, counted over all top-1 choices in token order, then all
+ * top-2 choices in token order, and so on. Ranks >= C are dropped (-1).
+ * used[e] = number of kept assignments of expert e.                         */
+void oracle_assign(int64_t N, int64_t E, int32_t k, int64_t C,
+                   const int32_t *idx, int32_t *slot, int32_t *used)
+{
+    for (int64_t e = 0; e < E; ++e)
+        used[e] = 0;
+    int64_t count[1024];
+    for (int64_t e = 0; e < E; ++e)
+        count[e] = 0;
+    for (int32_t j = 0; j < k; ++j) {
+        for (int64_t t = 0; t < N; ++t) {
+            int32_t e = idx[t * k + j];
+            int64_t r = count[e]++;
+            slot[t * k + j] = (r < C) ? (int32_t)r : -1;
+        }
+    }
+    for (int64_t e = 0; e < E; ++e)
+        used[e] = (int32_t)(count[e] < C ? count[e] : C);
+}
+
+/* [P1 STEP 8-10] one expert on a list of its tokens: for each listed token
+ * row x_t, z = W_up x_t, h = ReLU(z), y = W_down h. W_up is [d_ff, d] and
+ * W_down is [d, d_ff], row-major. y is [n, d]. hbuf must hold
+ * (OpenMP team size) * d_ff doubles.                                        */
+void oracle_expert_rows(int64_t d, int64_t d_ff, int64_t n, const int64_t *tokens,
+                        const double *x, const double *Wup, const double *Wdown,
+                        double *y, double *hbuf)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+        int tid = 0;
+#ifdef _OPENMP
+        extern int omp_get_thread_num(void);
+        tid = omp_get_thread_num();
+#endif
+        double *h = hbuf + (int64_t)tid * d_ff;
+        const double *xt = x + tokens[r] * d;
+        for (int64_t f = 0; f < d_ff; ++f) {
+            double z = 0.0;
+            const double *w = Wup + f * d;
+            for (int64_t i = 0; i < d; ++i)
+                z += w[i] * xt[i];
+            h[f] = z > 0.0 ? z : 0.0;
+        }
+        double *yr = y + r * d;
+        for (int64_t o = 0; o < d; ++o) {
+            double acc = 0.0;
+            const double *w = Wdown + o * d_ff;
+            for (int64_t f = 0; f < d_ff; ++f)
+                acc += w[f] * h[f];
+            yr[o] = acc;
+        }
+    }
+}
+
+/* [P1 STEP 11-12, P2 slides 38-40] output rows: each kept assignment's
+ * expert output scaled by its gate, summed in choice order j = 0..k-1.
+ * Dropped assignments (slot -1) contribute nothing, so a token with every
+ * choice dropped gets 0. gate, slot are [n, k]; y is [n, k, d]; out [n, d]. */
+void oracle_combine(int64_t n, int64_t d, int32_t k, const double *gate,
+                    const int32_t *slot, const double *y, double *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        double *o = out + r * d;
+        for (int64_t i = 0; i < d; ++i)
+            o[i] = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            if (slot[r * k + j] < 0)
+                continue;
+            double g = gate[r * k + j];
+            const double *yj = y + (r * k + j) * d;
+            for (int64_t i = 0; i < d; ++i)
+                o[i] += g * yj[i];
+        }
+    }
+}
+
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,66 @@
+"""The seeded input generator: determinism, dtype rounding, the separation
+screen, and the skewed layer's calibration (about 60% of first choices to
+expert 0)."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_mixture_experts_20_amd import workloads as W
+
+
+def test_bf16_rounding_is_nearest_even():
+    vals = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.5, 1.0 + 2**-9, 3.0e-3], np.float32)
+    bits = W.f32_to_bf16_bits(vals)
+    back = W.bf16_bits_to_f32(bits)
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to even -> 1
+    assert back[0] == 1.0 and back[1] == 1.0
+    assert back[2] == np.float32(1.0 + 2**-6)
+    assert back[3] == -2.5 and back[4] == 1.0
+    assert abs(back[5] - 3.0e-3) <= 3.0e-3 * 2**-8
+
+
+def test_generation_is_deterministic():
+    a, b = W.make("tiny"), W.make("tiny")
+    np.testing.assert_array_equal(a.x, b.x)
+    np.testing.assert_array_equal(a.wg, b.wg)
+    for e in range(a.E):
+        np.testing.assert_array_equal(a.w_up(e), b.w_up(e))
+        np.testing.assert_array_equal(a.w_down(e), b.w_down(e))
+    c = W.make("nanomoe")
+    d = W.make("nanomoe")
+    np.testing.assert_array_equal(c.x, d.x)
+    np.testing.assert_array_equal(c.noise, d.noise)
+    np.testing.assert_array_equal(c.w_up(3), d.w_up(3))
+    assert not np.array_equal(c.w_up(3), c.w_up(4))
+
+
+def test_shapes_and_dtypes():
+    wl = W.make("nanomoe")
+    assert wl.x.shape == (2048, 768) and wl.x.dtype == np.uint16
+    assert wl.wg.shape == (8, 768) and wl.wg.dtype == np.float32
+    assert wl.noise.shape == (2048, 8) and wl.noise.dtype == np.float32
+    assert wl.w_up(0).shape == (3072, 768) and wl.w_down(0).shape == (768, 3072)
+    t = W.make("tiny")
+    assert t.x.dtype == np.float32 and t.noise is None
+
+
+@pytest.mark.parametrize("name", ["tiny", "nanomoe", "mixtral"])
+def test_screen_leaves_no_ambiguous_token(name):
+    wl = W.make(name)
+    bad = W.separation_screen(wl.x64(), wl.wg64(), wl.noise64(), wl.k)
+    assert not bad.any()
+    # the oracle's float32 ranking agrees with the float64 ranking
+    scores, idx, _ = oracle.router(wl.x64(), wl.wg64(), wl.noise64(), wl.k)
+    s64 = wl.x64() @ wl.wg64().T + (0 if wl.noise is None else wl.noise64())
+    np.testing.assert_array_equal(idx, np.argsort(-s64, axis=1, kind="stable")[:, :wl.k])
+
+
+def test_skewed_layer_sends_sixty_percent_to_expert0():
+    wl = W.make("skew")
+    _, idx, _ = oracle.router(wl.x64(), wl.wg64(), wl.noise64(), wl.k)
+    frac = float((idx[:, 0] == 0).mean())
+    assert 0.57 < frac < 0.63, frac
+    C = oracle.capacity(wl.N, wl.E, wl.k, wl.cfg.cf)
+    slot, used = oracle.assign(idx, wl.E, C)
+    assert C == 2048 and used[0] == C
+    assert 8000 < int((slot < 0).sum()) < 13000

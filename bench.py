@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse MoE layer forward on one MI355X.
+
+One step = one moe_forward call (router, dispatch plan, grouped expert FFN,
+combine) over one batch of seeded synthetic tokens already resident in HBM.
+Default workload: the nanoMoE-shaped layer (2048 tokens, d=768, E=8, k=2,
+d_ff=3072, bf16, capacity factor 1.25, noise sigma 1.0).
+
+Prints ONE JSON line on stdout. Besides the contract fields it carries:
+  roofline      the dominant kernel (the larger of the two expert GEMMs)
+                against bf16 MFMA peak, its duration timed with HIP events on
+                the stream it runs on;
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample;
+  stages        per-stage average durations (HIP events) and derived rates.
+Diagnostics go to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at 1 MI355X; expert-GEMM % MFMA peak; router HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_20_amd", "csrc", "experts.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(f"{kernel}/{workload}")
+    if not e or e.get("source_sha") != source_sha(GEMM_SRC):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, target_s=15.0):
+    """The oracle as it stands: routing and slots for all N tokens, expert FFN
+    and combine for a seeded sample of S tokens sized for ~target_s of work."""
+    import numpy as np
+    import oracle
+
+    x64 = wl.x64()
+    t0 = time.perf_counter()
+    _, idx, gate = oracle.router(x64, wl.wg64(), wl.noise64(), wl.k)
+    C = oracle.capacity(wl.N, wl.E, wl.k, wl.cfg.cf)
+    slot, used = oracle.assign(idx, wl.E, C)
+    t_route = time.perf_counter() - t0
+
+    rng = np.random.default_rng(0)
+    # experts' weights as float64, regenerated once and excluded from timing
+    def ffn(rows):
+        y = np.zeros((len(rows), wl.k, wl.d))
+        sel_i, sel_s = idx[rows], slot[rows]
+        t = 0.0
+        for e in np.unique(sel_i[sel_s >= 0]):
+            r_pos, j_pos = np.nonzero((sel_i == e) & (sel_s >= 0))
+            wu, wd = wl.as_f64(wl.w_up(int(e))), wl.as_f64(wl.w_down(int(e)))
+            a = time.perf_counter()
+            y[r_pos, j_pos] = oracle.expert_rows(x64, rows[r_pos], wu, wd)
+            t += time.perf_counter() - a
+        a = time.perf_counter()
+        oracle.combine(gate[rows], slot[rows], y)
+        return t + time.perf_counter() - a
+
+    probe = np.sort(rng.choice(wl.N, size=min(wl.N, 16), replace=False))
+    t_probe = ffn(probe)
+    per_tok = t_probe / len(probe)
+    S = int(min(wl.N, max(16, target_s / max(per_tok, 1e-9))))
+    rows = np.sort(rng.choice(wl.N, size=S, replace=False))
+    t_ffn = ffn(rows)
+    est_full = t_route + t_ffn * wl.N / S
+    return {
+        "value": wl.N / est_full,
+        "unit": "tokens/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": (f"routing+slots for all {wl.N} tokens ({t_route:.2f} s); expert FFN+combine "
+                   f"for {S} seeded tokens ({t_ffn:.2f} s); tokens/s = N / (t_route + "
+                   f"t_ffn*N/S), float64 C loops with OpenMP"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="nanomoe",
+                    choices=["nanomoe", "mixtral", "skew", "finegrained", "tiny"])
+    ap.add_argument("--stage-reps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); the layer has no multi-GPU path in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_mixture_experts_20_amd import binding as B
+    from sparse_mixture_experts_20_amd import device as D
+    from sparse_mixture_experts_20_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    B.lib()
+    wl = W.make(args.workload)
+    cfg = wl.cfg
+    log(f"[bench] workload {cfg.name}: N={wl.N} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff} "
+        f"{cfg.dtype} cf={cfg.cf}")
+    dev = D.upload(wl, keep_host=not args.no_cpu_baseline)
+    fwd = B.Forward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
+                    cfg.cf, export=True)
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        fwd()
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = max(wall_ms, ev_ms)
+    used = fwd.used.cpu().numpy()
+    kept = int(used.sum())
+    C = int(fwd.stats.capacity)
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f}, "
+        f"events {ev_ms * 1e3:.1f}); kept {kept}/{wl.N * wl.k}, C={C}")
+
+    # ---- per-stage timing through the stage entry points (HIP events) ----
+    x, wg, nz, wu, wd = dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"]
+    idx, gate = B.router(x, wg, nz, wl.k)
+    slot, usedt, slot_token, tiles = B.dispatch(idx, wl.E, C)
+    ceff = min(C, wl.N)
+    H = torch.empty((wl.E, max(ceff, 1), wl.d_ff), dtype=x.dtype, device="cuda")
+    Y = torch.empty((wl.N * wl.k, wl.d), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(x)
+    stages = {
+        "router": lambda: B.router(x, wg, nz, wl.k, idx, gate),
+        "dispatch": lambda: B.lib().moe_dispatch(wl.N, wl.E, wl.k, C, B._ptr(idx), B._ptr(slot),
+                                                 B._ptr(usedt), B._ptr(slot_token),
+                                                 B._ptr(tiles), B._stream()),
+        "expert_up": lambda: B.expert_up(x, wu, wl.k, C, usedt, slot_token, tiles, H),
+        "expert_down": lambda: B.expert_down(wl.N, wd, wl.k, C, usedt, slot_token, tiles, H, Y),
+        "combine": lambda: B.combine(Y, gate, slot, out),
+    }
+    st_ms = {}
+    for name, fn in stages.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.stage_reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        st_ms[name] = e0.elapsed_time(e1) / args.stage_reps
+    gemm_flops = 2.0 * kept * wl.d * wl.d_ff          # one of the two products
+    s = dict(st_ms)
+    xbytes = 2 if cfg.dtype == "bf16" else 4
+    router_bytes = wl.N * wl.d * xbytes + wl.E * wl.d * 4 + wl.N * wl.k * 8 + (
+        wl.N * wl.E * 4 if wl.noise is not None else 0)
+    combine_bytes = kept * wl.d * 4 + wl.N * wl.k * 8 + wl.N * wl.d * xbytes
+    up_tflops = gemm_flops / (s["expert_up"] * 1e-3) / 1e12
+    down_tflops = gemm_flops / (s["expert_down"] * 1e-3) / 1e12
+    ffn_frac = (2 * gemm_flops) / ((s["expert_up"] + s["expert_down"]) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+    router_gbps = router_bytes / (s["router"] * 1e-3) / 1e9
+    combine_gbps = combine_bytes / (s["combine"] * 1e-3) / 1e9
+    for n, v in s.items():
+        log(f"[bench] stage {n:12s} {v * 1e3:9.2f} us")
+    log(f"[bench] expert_up {up_tflops:.0f} TFLOP/s, expert_down {down_tflops:.0f} TFLOP/s, "
+        f"FFN {100 * ffn_frac:.1f}% of bf16 peak; router {router_gbps:.0f} GB/s; "
+        f"combine {combine_gbps:.0f} GB/s")
+
+    dom = "expert_up" if s["expert_up"] >= s["expert_down"] else "expert_down"
+    dom_kernel = ("experts_bf16_kernel<0>" if dom == "expert_up" else "experts_bf16_kernel<1>")
+    achieved = gemm_flops / (s[dom] * 1e-3) / 1e12
+    roofline = {
+        "kernel": dom_kernel,
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic_for(dom_kernel, cfg.name),
+        "algorithmic_per_launch": f"2*kept*d*d_ff = {gemm_flops:.4g} flop (kept={kept})",
+        "avg_launch_us": round(s[dom] * 1e3, 2),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(wl)
+        log(f"[bench] cpu_baseline {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    value = wl.N / (ms_per_step * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Gaussian inputs and random-init weights)",
+        "config": {
+            "workload": cfg.description or cfg.name,
+            "tokens": wl.N, "d": wl.d, "experts": wl.E, "top_k": wl.k, "d_ff": wl.d_ff,
+            "capacity_factor": cfg.cf, "capacity": C, "noise_sigma": cfg.sigma,
+            "seed": cfg.seed, "kept_assignments": kept, "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": {
+            "expert_gemm_pct_mfma_peak": round(100 * ffn_frac, 2),
+            "router_hbm_GBps": round(router_gbps, 1),
+            "combine_hbm_GBps": round(combine_gbps, 1),
+            "expert_tflops": round(2 * gemm_flops / ((s["expert_up"] + s["expert_down"]) * 1e-3)
+                                   / 1e12, 1),
+            "stage_us": {k: round(v * 1e3, 2) for k, v in s.items()},
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * moe.h — C ABI of the sparse Mixture-of-Experts layer forward for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer (page 1, "Mixture of Experts (MoE) 12段階極小ビジュアル解剖シミュレーター",
+ * STEP 1-12; nanoMoE slides, "nanoMoEの深層解剖：Mixture of Expertsにおける
+ * 条件分岐を排除した並列演算実装", slides 11-40) computes, for every token row x_t:
+ *
+ *   s      = W_g x_t + noise_t                         (STEP 2-4; slide 11)
+ *   I_t    = the k largest scores, in descending order  (STEP 5; slide 12)
+ *   g_t,j  = softmax of the k kept scores               (STEP 6; slide 13)
+ *   slot   = rank of (j, t) among all assignments to expert I_t[j], counted
+ *            over every token's first choice in token order, then every
+ *            second choice, ...; ranks >= C are dropped  (slides 14-23)
+ *   y_t    = sum over kept j of g_t,j * W_down[e] ReLU(W_up[e] x_t),
+ *            e = I_t[j]; 0 when every choice is dropped (STEP 7-12; slides 33-40)
+ *
+ * with capacity C = ceil(capacity_factor * k * N / E) for a call of N tokens
+ * (slide 14's get_capacity(num_tokens); its body is not shown, this is the
+ * plain reading).
+ *
+ * Conventions for every entry point:
+ *  - All tensor data pointers are DEVICE pointers owned by the caller; the
+ *    library never allocates, frees or retains device memory, and keeps no
+ *    global mutable state. Tensors are row-major and contiguous.
+ *  - Work is enqueued on the given HIP stream (hipStream_t passed as void*;
+ *    NULL = the default stream). Calls return without synchronising; the
+ *    results are valid once the stream reaches them.
+ *  - Arguments are validated on the host before anything is enqueued. On
+ *    error nothing is enqueued and nothing is written; the return value is a
+ *    negative MOE_ERR_* code (see moe_error_string). MOE_ERR_HIP reports a
+ *    failed launch; earlier launches of the same call may already be queued.
+ *  - Work on one stream is ordered; two calls sharing a workspace must not
+ *    run concurrently on different streams.
+ *  - Results are deterministic: no floating-point atomics, fixed summation
+ *    orders; two calls on the same inputs give bitwise-identical outputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* return codes */
+enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,        /* a required pointer is NULL                      */
+    MOE_ERR_SHAPE = -2,       /* tensor ranks or extents are inconsistent        */
+    MOE_ERR_DTYPE = -3,       /* element type not allowed for this tensor        */
+    MOE_ERR_ARG = -4,         /* k < 1, k > E, capacity_factor <= 0 or not finite, negative sizes */
+    MOE_ERR_WORKSPACE = -5,   /* workspace smaller than moe_workspace_size()     */
+    MOE_ERR_UNSUPPORTED = -6, /* outside the documented limits below             */
+    MOE_ERR_ALIGN = -7,       /* pointer not aligned as required                 */
+    MOE_ERR_HIP = -8          /* a HIP launch failed                             */
+};
+
+/* Limits (MOE_ERR_UNSUPPORTED beyond them): E <= 256 experts, k <= 16,
+ * N * k < 2^31 assignments, E * min(C, N) < 2^31 slots. bf16 tensors need
+ * d and d_ff to be multiples of 8 and 16-byte aligned data pointers. */
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 16
+
+/* A tensor view: data (device), element type, rank and extents (row-major,
+ * contiguous). A 3-D activation [B, T, d] is read as [B*T, d]. */
+typedef struct {
+    void *data;
+    int32_t dtype;     /* MOE_F32 or MOE_BF16 */
+    int32_t ndim;      /* 1..4 */
+    int64_t shape[4];
+} moe_tensor;
+
+/* Launch context and optional exports of moe_forward.
+ * Inputs:  stream, workspace (device, 256-byte aligned) and its size.
+ * Optional device outputs (NULL = not exported; the library then keeps the
+ * values in the workspace):
+ *   topk_idx       int32 [N, k]  expert ids, highest score first
+ *   topk_gate      fp32  [N, k]  gates of those experts (sum to 1 per token)
+ *   slot           int32 [N, k]  capacity slot of each assignment, -1 = dropped
+ *   used_capacity  int32 [E]     kept assignments per expert (= min(count, C))
+ * Host output: capacity (C), written before anything is enqueued.
+ * Dropped assignments per call = N*k - sum(used_capacity). */
+typedef struct {
+    void *stream;
+    void *workspace;
+    size_t workspace_bytes;
+    int32_t *topk_idx;
+    float *topk_gate;
+    int32_t *slot;
+    int32_t *used_capacity;
+    int64_t capacity;
+} moe_stats;
+
+/* The whole layer forward (page 1 STEP 1-12; nanoMoE slides 11-40).
+ *   x      [N, d] (or [B, T, d])   MOE_F32 or MOE_BF16
+ *   W_g    [E, d]                  MOE_F32 (the router runs in full precision, slide 11)
+ *   noise  [N, E] MOE_F32, or NULL for sigma = 0. The caller draws it: it is
+ *          sigma * eps with eps ~ N(0, 1) (STEP 3-4) plus any constant score
+ *          offset; the library has no random number generator.
+ *   W_up   [E, d_ff, d]            same dtype as x (row f of expert e is the
+ *          f-th hidden neuron: z = W_up[e] x, STEP 8)
+ *   W_down [E, d, d_ff]            same dtype as x (E_i(x) = W_down[e] h, STEP 10)
+ *   k      experts per token, 1 <= k <= min(E, 16)
+ *   capacity_factor  > 0, finite
+ *   out    [N, d] (same shape as x) same dtype as x; every row is written
+ *   stats  launch context and optional exports (required)
+ * Numerics: scores, top-k and gates in fp32; expert products accumulate in
+ * fp32 (bf16 inputs on matrix cores); the hidden activation is stored in the
+ * dtype of x; the combine accumulates in fp32 in choice order and rounds
+ * once to the dtype of out (round to nearest even).
+ * N = 0 is valid: capacity is 0, used_capacity (if given) is zeroed. */
+int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                const moe_tensor *W_up, const moe_tensor *W_down, int k,
+                float capacity_factor, moe_tensor *out, moe_stats *stats);
+
+/* Bytes of workspace moe_forward needs for these sizes (0 on invalid sizes). */
+size_t moe_workspace_size(int64_t N, int64_t d, int64_t E, int64_t d_ff, int k,
+                          float capacity_factor, int32_t dtype);
+
+/* Per-expert capacity C = ceil(capacity_factor * k * N / E), in double
+ * (nanoMoE slide 14, get_capacity of the call's token count). -1 on
+ * invalid arguments; 0 when N = 0. */
+int64_t moe_capacity(int64_t N, int64_t E, int k, float capacity_factor);
+
+/* Static description of a return code. */
+const char *moe_error_string(int code);
+
+/* ---------------------------------------------------------------------------
+ * The four stages moe_forward enqueues, exported for callers that run them
+ * separately (and for per-stage testing). Same conventions as above.
+ * ------------------------------------------------------------------------- */
+
+/* Router (page 1 STEP 2-6; slides 11-13): fp32 scores s = W_g x + noise,
+ * top-k in descending order (equal scores: lower expert id first), softmax
+ * over the k kept scores. Writes topk_idx [N, k] int32 and topk_gate [N, k]
+ * fp32 (device). x, W_g, noise as in moe_forward. */
+int moe_router(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+               int k, int32_t *topk_idx, float *topk_gate, void *stream);
+
+/* Capacity-limited dispatch plan (slides 14-29). From topk_idx [N, k] and the
+ * capacity C (moe_capacity), writes:
+ *   slot        int32 [N, k]          rank among the expert's assignments in
+ *                                     (choice, token) order, -1 if >= C
+ *   used        int32 [E]             kept assignments per expert
+ *   slot_token  int32 [E, min(C, N)]  for r < used[e]: the assignment id
+ *                                     t*k + j holding slot r of expert e
+ *                                     (rows past used[e] are left untouched)
+ *   tiles       int32 [2*(E+1)]       prefix sums of ceil(used[e]/128) and
+ *                                     ceil(used[e]/64): the expert kernels'
+ *                                     tile schedule
+ * An id outside [0, E) in topk_idx is not counted and its slot is -1. */
+int moe_dispatch(int64_t N, int64_t E, int k, int64_t capacity, const int32_t *topk_idx,
+                 int32_t *slot, int32_t *used, int32_t *slot_token, int32_t *tiles,
+                 void *stream);
+
+/* Grouped expert FFN (page 1 STEP 7-10; slides 32-37) over the dispatch plan.
+ * For each expert e and r < used[e], with a = slot_token[e, r], t = a / k:
+ *   H[e, r, :] = ReLU(W_up[e] x_t)      stored in the dtype of x   [E, min(C,N), d_ff]
+ *   Y[a, :]    = W_down[e] H[e, r, :]   fp32                       [N*k, d]
+ * The gather of token rows is fused into the first product. Rows of Y whose
+ * assignment was dropped are not written. H and Y are caller device buffers. */
+int moe_experts(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W_down,
+                int k, int64_t capacity, const int32_t *used, const int32_t *slot_token,
+                const int32_t *tiles, void *H, float *Y, void *stream);
+
+/* The two halves of moe_experts, one kernel each (page 1 STEP 8-9 and STEP 10):
+ * moe_expert_up writes H from x and W_up; moe_expert_down writes Y from H and
+ * W_down ([E, d, d_ff]; H has W_down's dtype and [E, min(C,N), d_ff] rows,
+ * Y is [N*k, d] fp32). */
+int moe_expert_up(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t capacity,
+                  const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
+                  void *H, void *stream);
+int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
+                    const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
+                    const void *H, float *Y, void *stream);
+
+/* Combine (page 1 STEP 11-12; slides 38-40): out[t] = sum over j < k with
+ * slot[t, j] >= 0 of topk_gate[t, j] * Y[t*k + j], accumulated in fp32 in
+ * order j = 0..k-1, rounded once to out's dtype; rows with every choice
+ * dropped become 0. out is [N, d] MOE_F32 or MOE_BF16. */
+int moe_combine(int64_t N, int64_t d, int k, const float *Y, const float *topk_gate,
+                const int32_t *slot, moe_tensor *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,281 @@
+"""ctypes binding of the C ABI in ``include/moe.h`` (argument marshalling only).
+
+Every step of the layer runs in ``libmoe.so``'s HIP kernels; this module only
+turns torch device tensors into ``moe_tensor`` descriptors, passes torch's
+current HIP stream, and raises :class:`MoeError` on a non-zero return code.
+There is no fallback: if the library is missing, :func:`lib` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_MAX_EXPERTS, MOE_MAX_TOPK = 256, 16
+
+#: every function the header declares
+EXPORTS = ("moe_forward", "moe_workspace_size", "moe_capacity", "moe_error_string",
+           "moe_router", "moe_dispatch", "moe_experts", "moe_expert_up", "moe_expert_down",
+           "moe_combine")
+
+
+class MoeTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4)]
+
+
+class MoeStats(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t),
+                ("topk_idx", ctypes.c_void_p), ("topk_gate", ctypes.c_void_p),
+                ("slot", ctypes.c_void_p), ("used_capacity", ctypes.c_void_p),
+                ("capacity", ctypes.c_int64)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: error {code} ({error_string(code)})")
+
+
+_lib = None
+_T = ctypes.POINTER(MoeTensor)
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+def lib():
+    """Load ``libmoe.so`` (built in-tree by ``sparse_mixture_experts_20_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -m sparse_mixture_experts_20_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_forward.argtypes = [_T, _T, _T, _T, _T, ctypes.c_int, ctypes.c_float, _T,
+                                  ctypes.POINTER(MoeStats)]
+        L.moe_forward.restype = ctypes.c_int
+        L.moe_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
+                                         ctypes.c_int32]
+        L.moe_workspace_size.restype = ctypes.c_size_t
+        L.moe_capacity.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_float]
+        L.moe_capacity.restype = _i64
+        L.moe_error_string.argtypes = [ctypes.c_int]
+        L.moe_error_string.restype = ctypes.c_char_p
+        L.moe_router.argtypes = [_T, _T, _T, ctypes.c_int, _vp, _vp, _vp]
+        L.moe_router.restype = ctypes.c_int
+        L.moe_dispatch.argtypes = [_i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_dispatch.restype = ctypes.c_int
+        L.moe_experts.argtypes = [_T, _T, _T, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_experts.restype = ctypes.c_int
+        L.moe_expert_up.argtypes = [_T, _T, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp]
+        L.moe_expert_up.restype = ctypes.c_int
+        L.moe_expert_down.argtypes = [_i64, _T, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_expert_down.restype = ctypes.c_int
+        L.moe_combine.argtypes = [_i64, _i64, ctypes.c_int, _vp, _vp, _vp, _T, _vp]
+        L.moe_combine.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def error_string(code: int) -> str:
+    return lib().moe_error_string(code).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise MoeError(rc, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def desc(t: Optional[torch.Tensor]):
+    """A ``moe_tensor`` for a contiguous device tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    shape = (ctypes.c_int64 * 4)(*(list(t.shape) + [0] * (4 - t.dim())))
+    return MoeTensor(ctypes.c_void_p(t.data_ptr()), _dtype_code(t), t.dim(), shape)
+
+
+def _ref(d):
+    return None if d is None else ctypes.byref(d)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def capacity(N: int, E: int, k: int, capacity_factor: float) -> int:
+    return int(lib().moe_capacity(N, E, k, capacity_factor))
+
+
+def workspace_size(N: int, d: int, E: int, d_ff: int, k: int, capacity_factor: float,
+                   dtype: torch.dtype) -> int:
+    code = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(lib().moe_workspace_size(N, d, E, d_ff, k, capacity_factor, code))
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    # torch's caching allocator returns 256-byte (or better) aligned blocks
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+class Stats:
+    def __init__(self, idx, gate, slot, used, capacity):
+        self.idx, self.gate, self.slot, self.used, self.capacity = idx, gate, slot, used, capacity
+
+
+def forward(x: torch.Tensor, W_g: torch.Tensor, noise: Optional[torch.Tensor],
+            W_up: torch.Tensor, W_down: torch.Tensor, k: int, capacity_factor: float,
+            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            export: bool = True, stream=None):
+    """Run ``moe_forward``. Returns ``(out, Stats)``; with ``export=False`` the
+    routing arrays stay in the workspace and Stats only carries the capacity."""
+    N = x.numel() // x.shape[-1]
+    d = x.shape[-1]
+    E, d_ff = W_up.shape[0], W_up.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_size(N, d, E, d_ff, k, capacity_factor, x.dtype),
+                                    x.device)
+    dev = x.device
+    idx = gate = slot = used = None
+    if export:
+        idx = torch.empty((N, k), dtype=torch.int32, device=dev)
+        gate = torch.empty((N, k), dtype=torch.float32, device=dev)
+        slot = torch.empty((N, k), dtype=torch.int32, device=dev)
+        used = torch.empty((E,), dtype=torch.int32, device=dev)
+    st = MoeStats(_stream(stream), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                  _ptr(idx), _ptr(gate), _ptr(slot), _ptr(used), -1)
+    dx, dg, dn, du, dd, do = desc(x), desc(W_g), desc(noise), desc(W_up), desc(W_down), desc(out)
+    rc = lib().moe_forward(_ref(dx), _ref(dg), _ref(dn), _ref(du), _ref(dd), k,
+                           capacity_factor, _ref(do), ctypes.byref(st))
+    _check(rc, "moe_forward")
+    return out, Stats(idx, gate, slot, used, int(st.capacity))
+
+
+class Forward:
+    """A reusable call: descriptors, workspace and stats built once, so that
+    timing loops measure only the enqueue of the kernels."""
+
+    def __init__(self, x, W_g, noise, W_up, W_down, k, capacity_factor, out=None,
+                 export=False, stream=None):
+        self.tensors = (x, W_g, noise, W_up, W_down)
+        N, d = x.numel() // x.shape[-1], x.shape[-1]
+        E, d_ff = W_up.shape[0], W_up.shape[1]
+        self.out = torch.empty_like(x) if out is None else out
+        self.workspace = alloc_workspace(
+            workspace_size(N, d, E, d_ff, k, capacity_factor, x.dtype), x.device)
+        dev = x.device
+        self.idx = self.gate = self.slot = self.used = None
+        if export:
+            self.idx = torch.empty((N, k), dtype=torch.int32, device=dev)
+            self.gate = torch.empty((N, k), dtype=torch.float32, device=dev)
+            self.slot = torch.empty((N, k), dtype=torch.int32, device=dev)
+            self.used = torch.empty((E,), dtype=torch.int32, device=dev)
+        self.k, self.cf = k, capacity_factor
+        self._d = [desc(x), desc(W_g), desc(noise), desc(W_up), desc(W_down), desc(self.out)]
+        self.stats = MoeStats(_stream(stream), ctypes.c_void_p(self.workspace.data_ptr()),
+                              self.workspace.numel(), _ptr(self.idx), _ptr(self.gate),
+                              _ptr(self.slot), _ptr(self.used), -1)
+        self._args = [_ref(a) for a in self._d]
+        self._fn = lib().moe_forward
+
+    def __call__(self):
+        a = self._args
+        rc = self._fn(a[0], a[1], a[2], a[3], a[4], self.k, self.cf, a[5],
+                      ctypes.byref(self.stats))
+        if rc != 0:
+            raise MoeError(rc, "moe_forward")
+        return self.out
+
+
+def router(x, W_g, noise, k, idx=None, gate=None, stream=None):
+    N = x.numel() // x.shape[-1]
+    if idx is None:
+        idx = torch.empty((N, k), dtype=torch.int32, device=x.device)
+    if gate is None:
+        gate = torch.empty((N, k), dtype=torch.float32, device=x.device)
+    dx, dg, dn = desc(x), desc(W_g), desc(noise)
+    _check(lib().moe_router(_ref(dx), _ref(dg), _ref(dn), k, _ptr(idx), _ptr(gate),
+                            _stream(stream)), "moe_router")
+    return idx, gate
+
+
+def dispatch(idx: torch.Tensor, E: int, capacity_: int, stream=None):
+    """Returns (slot [N,k], used [E], slot_token [E, min(C,N)], tiles [2(E+1)])."""
+    N, k = idx.shape
+    ceff = min(capacity_, N)
+    dev = idx.device
+    slot = torch.empty((N, k), dtype=torch.int32, device=dev)
+    used = torch.empty((E,), dtype=torch.int32, device=dev)
+    slot_token = torch.full((E, max(ceff, 1)), -1, dtype=torch.int32, device=dev)
+    tiles = torch.empty((2 * (E + 1),), dtype=torch.int32, device=dev)
+    _check(lib().moe_dispatch(N, E, k, capacity_, _ptr(idx), _ptr(slot), _ptr(used),
+                              _ptr(slot_token), _ptr(tiles), _stream(stream)), "moe_dispatch")
+    return slot, used, slot_token, tiles
+
+
+def experts(x, W_up, W_down, k, capacity_, used, slot_token, tiles, H=None, Y=None,
+            stream=None):
+    """Returns (H [E, min(C,N), d_ff] in x's dtype, Y [N*k, d] fp32)."""
+    N, d = x.numel() // x.shape[-1], x.shape[-1]
+    E, d_ff = W_up.shape[0], W_up.shape[1]
+    ceff = min(capacity_, N)
+    if H is None:
+        H = torch.zeros((E, max(ceff, 1), d_ff), dtype=x.dtype, device=x.device)
+    if Y is None:
+        Y = torch.zeros((N * k, d), dtype=torch.float32, device=x.device)
+    dx, du, dd = desc(x), desc(W_up), desc(W_down)
+    if not slot_token.is_contiguous():
+        raise ValueError("slot_token must be a contiguous [E, min(C, N)] tensor")
+    _check(lib().moe_experts(_ref(dx), _ref(du), _ref(dd), k, capacity_, _ptr(used),
+                             _ptr(slot_token), _ptr(tiles), _ptr(H), _ptr(Y), _stream(stream)),
+           "moe_experts")
+    return H, Y
+
+
+def expert_up(x, W_up, k, capacity_, used, slot_token, tiles, H, stream=None):
+    dx, du = desc(x), desc(W_up)
+    _check(lib().moe_expert_up(_ref(dx), _ref(du), k, capacity_, _ptr(used), _ptr(slot_token),
+                               _ptr(tiles), _ptr(H), _stream(stream)), "moe_expert_up")
+    return H
+
+
+def expert_down(N, W_down, k, capacity_, used, slot_token, tiles, H, Y, stream=None):
+    dd = desc(W_down)
+    _check(lib().moe_expert_down(N, _ref(dd), k, capacity_, _ptr(used), _ptr(slot_token),
+                                 _ptr(tiles), _ptr(H), _ptr(Y), _stream(stream)),
+           "moe_expert_down")
+    return Y
+
+
+def combine(Y, gate, slot, out, stream=None):
+    N, k = gate.shape
+    d = out.shape[-1]
+    do = desc(out)
+    _check(lib().moe_combine(N, d, k, _ptr(Y), _ptr(gate), _ptr(slot), _ref(do),
+                             _stream(stream)), "moe_combine")
+    return out

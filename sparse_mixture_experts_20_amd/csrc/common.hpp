@@ -1,0 +1,74 @@
+// Private helpers shared by the gfx950 kernels of the MoE layer (not part of
+// the C ABI). Wave size is 64 on CDNA; every kernel here assumes it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 256;
+constexpr int kMaxQ = kMaxExperts / kWave;   // router scores per lane
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// float -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
+    unsigned int u = __builtin_bit_cast(unsigned int, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (unsigned short)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (unsigned short)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {
+    return __builtin_bit_cast(float, (unsigned int)b << 16);
+}
+
+// 64-bit lane masks
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const unsigned lane = __lane_id();
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// Launchers (one per stage). All return hipSuccess or the launch error.
+// ---------------------------------------------------------------------------
+namespace moe {
+
+hipError_t launch_router_bf16(const void *x, const float *wg, const float *noise,
+                              int64_t N, int64_t d, int E, int k,
+                              int32_t *idx, float *gate, hipStream_t s);
+hipError_t launch_router_f32(const float *x, const float *wg, const float *noise,
+                             int64_t N, int64_t d, int E, int k,
+                             int32_t *idx, float *gate, hipStream_t s);
+
+hipError_t launch_dispatch(const int32_t *idx, int64_t N, int E, int k, int64_t ceff,
+                           int32_t *slot, int32_t *used, int32_t *slot_token,
+                           int32_t *tiles, hipStream_t s);
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
+
+// Grouped expert products. mode 0: H = ReLU(x[gather] W_up^T); mode 1:
+// Y[scatter] = H W_down^T.
+// bf16 != 0: bf16 operands on matrix cores; otherwise fp32 operands.
+hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t d,
+                            int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
+                            const int32_t *slot_token, const int32_t *tiles, void *H,
+                            hipStream_t s);
+hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int64_t d,
+                              int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
+                              const int32_t *slot_token, const int32_t *tiles, float *Y,
+                              hipStream_t s);
+
+hipError_t launch_combine(const float *Y, const float *gate, const int32_t *slot,
+                          int64_t N, int64_t d, int k, void *out, int out_dtype,
+                          hipStream_t s);
+
+}  // namespace moe

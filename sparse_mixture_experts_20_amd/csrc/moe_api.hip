@@ -1,0 +1,407 @@
+// C ABI of the MoE layer forward: argument validation, workspace layout and
+// the order of the stages (router -> dispatch plan -> grouped expert FFN ->
+// combine). Every check runs on the host before anything is enqueued.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t dtype_size(int32_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+bool valid_dtype(int32_t dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t capacity_of(int64_t N, int64_t E, int k, float cf) {
+    if (N <= 0)
+        return 0;
+    return (int64_t)ceil((double)cf * (double)((int64_t)k * N) / (double)E);
+}
+
+// Sizes of one call, as validated.
+struct Dims {
+    int64_t N, d, E, d_ff;
+    int k;
+    int64_t C, ceff;
+    int32_t dtype;
+};
+
+// Workspace regions (byte offsets from the base).
+struct Layout {
+    size_t idx, gate, slot, used, tiles, slot_token, H, Y, total;
+};
+
+Layout layout_of(const Dims &m) {
+    Layout L;
+    size_t o = 0;
+    const size_t nk = (size_t)m.N * m.k;
+    L.idx = o;        o += align_up(nk * 4);
+    L.gate = o;       o += align_up(nk * 4);
+    L.slot = o;       o += align_up(nk * 4);
+    L.used = o;       o += align_up((size_t)m.E * 4);
+    L.tiles = o;      o += align_up((size_t)(2 * (m.E + 1)) * 4);
+    L.slot_token = o; o += align_up((size_t)(m.E * m.ceff) * 4);
+    L.H = o;          o += align_up((size_t)(m.E * m.ceff * m.d_ff) * dtype_size(m.dtype));
+    L.Y = o;          o += align_up(nk * (size_t)m.d * 4);
+    L.total = o;
+    return L;
+}
+
+// Common size checks; fills C and ceff.
+int check_sizes(Dims &m) {
+    if (m.N < 0 || m.d <= 0 || m.E <= 0 || m.d_ff <= 0)
+        return MOE_ERR_ARG;
+    if (m.k < 1 || m.k > m.E)
+        return MOE_ERR_ARG;
+    if (m.E > MOE_MAX_EXPERTS || m.k > MOE_MAX_TOPK)
+        return MOE_ERR_UNSUPPORTED;
+    if (m.d > INT32_MAX || m.d_ff > INT32_MAX || m.N * (int64_t)m.k >= ((int64_t)1 << 31))
+        return MOE_ERR_UNSUPPORTED;
+    if (m.ceff * m.E >= ((int64_t)1 << 31))
+        return MOE_ERR_UNSUPPORTED;
+    if (m.dtype == MOE_BF16 && ((m.d % 8) != 0 || (m.d_ff % 8) != 0))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+bool cf_ok(float cf) { return isfinite(cf) && cf > 0.f; }
+
+// Rows of an activation tensor: [N, d] or [B, T, d] flattened.
+bool act_rows(const moe_tensor *t, int64_t &N, int64_t &d) {
+    if (t->ndim < 2 || t->ndim > 3)
+        return false;
+    d = t->shape[t->ndim - 1];
+    N = 1;
+    for (int i = 0; i < t->ndim - 1; ++i) {
+        if (t->shape[i] < 0)
+            return false;
+        N *= t->shape[i];
+    }
+    return d > 0;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                         \
+    do {                                      \
+        hipError_t e_ = (expr);               \
+        if (e_ != hipSuccess)                 \
+            return MOE_ERR_HIP;               \
+    } while (0)
+
+int router_checked(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                   int64_t N, int64_t d, int64_t E, int k, int32_t *idx, float *gate,
+                   hipStream_t s) {
+    const float *nz = noise ? static_cast<const float *>(noise->data) : nullptr;
+    if (x->dtype == MOE_BF16)
+        return hip_status(moe::launch_router_bf16(x->data, static_cast<const float *>(W_g->data),
+                                                  nz, N, d, (int)E, k, idx, gate, s));
+    return hip_status(moe::launch_router_f32(static_cast<const float *>(x->data),
+                                             static_cast<const float *>(W_g->data), nz, N, d,
+                                             (int)E, k, idx, gate, s));
+}
+
+// Validates x, W_g, noise; returns N, d, E.
+int check_router_args(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                      int k, int64_t &N, int64_t &d, int64_t &E) {
+    if (!x || !W_g)
+        return MOE_ERR_NULL;
+    if (!act_rows(x, N, d))
+        return MOE_ERR_SHAPE;
+    if (N > 0 && !x->data)
+        return MOE_ERR_NULL;
+    if (!W_g->data)
+        return MOE_ERR_NULL;
+    if (!valid_dtype(x->dtype) || W_g->dtype != MOE_F32)
+        return MOE_ERR_DTYPE;
+    if (W_g->ndim != 2 || W_g->shape[1] != d || W_g->shape[0] <= 0)
+        return MOE_ERR_SHAPE;
+    E = W_g->shape[0];
+    if (noise) {
+        if (N > 0 && !noise->data)
+            return MOE_ERR_NULL;
+        if (noise->dtype != MOE_F32)
+            return MOE_ERR_DTYPE;
+        if (noise->ndim != 2 || noise->shape[0] != N || noise->shape[1] != E)
+            return MOE_ERR_SHAPE;
+    }
+    if (k < 1 || k > E)
+        return MOE_ERR_ARG;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK)
+        return MOE_ERR_UNSUPPORTED;
+    if (N * (int64_t)k >= ((int64_t)1 << 31) || d > INT32_MAX)
+        return MOE_ERR_UNSUPPORTED;
+    if (x->dtype == MOE_BF16) {
+        if (d % 8 != 0)
+            return MOE_ERR_UNSUPPORTED;
+        if (!aligned(x->data, 16) || !aligned(W_g->data, 16))
+            return MOE_ERR_ALIGN;
+    }
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_error_string(int code) {
+    switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "tensor ranks or extents are inconsistent";
+    case MOE_ERR_DTYPE: return "element type not allowed for this tensor";
+    case MOE_ERR_ARG: return "invalid argument (k, capacity factor or sizes)";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_size()";
+    case MOE_ERR_UNSUPPORTED: return "outside the documented limits";
+    case MOE_ERR_ALIGN: return "pointer not aligned as required";
+    case MOE_ERR_HIP: return "a HIP launch failed";
+    default: return "unknown error code";
+    }
+}
+
+int64_t moe_capacity(int64_t N, int64_t E, int k, float capacity_factor) {
+    if (N < 0 || E <= 0 || k < 1 || k > E || !cf_ok(capacity_factor))
+        return -1;
+    return capacity_of(N, E, k, capacity_factor);
+}
+
+size_t moe_workspace_size(int64_t N, int64_t d, int64_t E, int64_t d_ff, int k,
+                          float capacity_factor, int32_t dtype) {
+    if (!valid_dtype(dtype) || !cf_ok(capacity_factor))
+        return 0;
+    Dims m{N, d, E, d_ff, k, 0, 0, dtype};
+    if (N < 0 || E <= 0 || k < 1 || k > E)
+        return 0;
+    m.C = capacity_of(N, E, k, capacity_factor);
+    m.ceff = m.C < N ? m.C : N;
+    if (check_sizes(m) != MOE_OK)
+        return 0;
+    return layout_of(m).total;
+}
+
+int moe_router(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise, int k,
+               int32_t *topk_idx, float *topk_gate, void *stream) {
+    int64_t N, d, E;
+    int rc = check_router_args(x, W_g, noise, k, N, d, E);
+    if (rc != MOE_OK)
+        return rc;
+    if (N == 0)
+        return MOE_OK;
+    if (!topk_idx || !topk_gate)
+        return MOE_ERR_NULL;
+    return router_checked(x, W_g, noise, N, d, E, k, topk_idx, topk_gate,
+                          static_cast<hipStream_t>(stream));
+}
+
+int moe_dispatch(int64_t N, int64_t E, int k, int64_t capacity, const int32_t *topk_idx,
+                 int32_t *slot, int32_t *used, int32_t *slot_token, int32_t *tiles,
+                 void *stream) {
+    if (N < 0 || E <= 0 || k < 1 || k > E || capacity < 0 || (N > 0 && capacity == 0))
+        return MOE_ERR_ARG;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || N * (int64_t)k >= ((int64_t)1 << 31))
+        return MOE_ERR_UNSUPPORTED;
+    const int64_t ceff = capacity < N ? capacity : N;
+    if (ceff * E >= ((int64_t)1 << 31))
+        return MOE_ERR_UNSUPPORTED;
+    if (!used || !tiles || (N > 0 && (!topk_idx || !slot || !slot_token)))
+        return MOE_ERR_NULL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (N == 0) {
+        MOE_TRY(moe::launch_fill_i32(used, E, 0, s));
+        return hip_status(moe::launch_fill_i32(tiles, 2 * (E + 1), 0, s));
+    }
+    return hip_status(moe::launch_dispatch(topk_idx, N, (int)E, k, ceff, slot, used,
+                                           slot_token, tiles, s));
+}
+
+int moe_expert_up(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t capacity,
+                  const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
+                  void *H, void *stream) {
+    if (!x || !W_up)
+        return MOE_ERR_NULL;
+    int64_t N, d;
+    if (!act_rows(x, N, d))
+        return MOE_ERR_SHAPE;
+    if (!valid_dtype(x->dtype) || W_up->dtype != x->dtype)
+        return MOE_ERR_DTYPE;
+    if (W_up->ndim != 3 || W_up->shape[2] != d)
+        return MOE_ERR_SHAPE;
+    const int64_t E = W_up->shape[0], d_ff = W_up->shape[1];
+    if (capacity < 0 || (N > 0 && capacity == 0))
+        return MOE_ERR_ARG;
+    Dims m{N, d, E, d_ff, k, capacity, capacity < N ? capacity : N, x->dtype};
+    int rc = check_sizes(m);
+    if (rc != MOE_OK)
+        return rc;
+    if (N == 0)
+        return MOE_OK;
+    if (!x->data || !W_up->data || !used || !slot_token || !tiles || !H)
+        return MOE_ERR_NULL;
+    const bool bf16 = x->dtype == MOE_BF16;
+    if (bf16 && (!aligned(x->data, 16) || !aligned(W_up->data, 16) || !aligned(H, 16)))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_expert_up(bf16, x->data, W_up->data, d, d_ff, (int)E, k,
+                                            m.ceff, used, slot_token, tiles, H,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
+                    const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
+                    const void *H, float *Y, void *stream) {
+    if (!W_down)
+        return MOE_ERR_NULL;
+    if (!valid_dtype(W_down->dtype))
+        return MOE_ERR_DTYPE;
+    if (W_down->ndim != 3)
+        return MOE_ERR_SHAPE;
+    const int64_t E = W_down->shape[0], d = W_down->shape[1], d_ff = W_down->shape[2];
+    if (N < 0 || capacity < 0 || (N > 0 && capacity == 0))
+        return MOE_ERR_ARG;
+    Dims m{N, d, E, d_ff, k, capacity, capacity < N ? capacity : N, W_down->dtype};
+    int rc = check_sizes(m);
+    if (rc != MOE_OK)
+        return rc;
+    if (N == 0)
+        return MOE_OK;
+    if (!W_down->data || !used || !slot_token || !tiles || !H || !Y)
+        return MOE_ERR_NULL;
+    const bool bf16 = W_down->dtype == MOE_BF16;
+    if (bf16 && (!aligned(W_down->data, 16) || !aligned(H, 16)))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_expert_down(bf16, H, W_down->data, d, d_ff, (int)E, k, m.ceff,
+                                              used, slot_token, tiles, Y,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int moe_experts(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W_down, int k,
+                int64_t capacity, const int32_t *used, const int32_t *slot_token,
+                const int32_t *tiles, void *H, float *Y, void *stream) {
+    if (!x || !W_up || !W_down)
+        return MOE_ERR_NULL;
+    int64_t N, d;
+    if (!act_rows(x, N, d))
+        return MOE_ERR_SHAPE;
+    if (W_up->ndim != 3 || W_down->ndim != 3)
+        return MOE_ERR_SHAPE;
+    if (W_down->dtype != W_up->dtype)
+        return MOE_ERR_DTYPE;
+    if (W_down->shape[0] != W_up->shape[0] || W_down->shape[1] != d ||
+        W_down->shape[2] != W_up->shape[1])
+        return MOE_ERR_SHAPE;
+    // validate both halves before enqueuing either
+    int rc = moe_expert_up(x, W_up, k, capacity, used, slot_token, tiles, nullptr, nullptr);
+    if (rc != MOE_OK && rc != MOE_ERR_NULL)
+        return rc;
+    if (N > 0 && (!H || !Y))
+        return MOE_ERR_NULL;
+    rc = moe_expert_up(x, W_up, k, capacity, used, slot_token, tiles, H, stream);
+    if (rc != MOE_OK)
+        return rc;
+    return moe_expert_down(N, W_down, k, capacity, used, slot_token, tiles, H, Y, stream);
+}
+
+int moe_combine(int64_t N, int64_t d, int k, const float *Y, const float *topk_gate,
+                const int32_t *slot, moe_tensor *out, void *stream) {
+    if (!out)
+        return MOE_ERR_NULL;
+    if (N < 0 || d <= 0 || k < 1 || k > MOE_MAX_TOPK)
+        return MOE_ERR_ARG;
+    int64_t oN, od;
+    if (!act_rows(out, oN, od) || oN != N || od != d)
+        return MOE_ERR_SHAPE;
+    if (!valid_dtype(out->dtype))
+        return MOE_ERR_DTYPE;
+    if (N == 0)
+        return MOE_OK;
+    if (!Y || !topk_gate || !slot || !out->data)
+        return MOE_ERR_NULL;
+    if (d % 4 == 0 && (!aligned(Y, 16) || !aligned(out->data, out->dtype == MOE_BF16 ? 8 : 16)))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_combine(Y, topk_gate, slot, N, d, k, out->data, out->dtype,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                const moe_tensor *W_up, const moe_tensor *W_down, int k, float capacity_factor,
+                moe_tensor *out, moe_stats *stats) {
+    if (!stats || !W_up || !W_down || !out)
+        return MOE_ERR_NULL;
+    int64_t N, d, E;
+    int rc = check_router_args(x, W_g, noise, k, N, d, E);
+    if (rc != MOE_OK)
+        return rc;
+    if (!cf_ok(capacity_factor))
+        return MOE_ERR_ARG;
+    if (W_up->dtype != x->dtype || W_down->dtype != x->dtype || out->dtype != x->dtype)
+        return MOE_ERR_DTYPE;
+    if (W_up->ndim != 3 || W_down->ndim != 3)
+        return MOE_ERR_SHAPE;
+    const int64_t d_ff = W_up->shape[1];
+    if (W_up->shape[0] != E || W_up->shape[2] != d || W_down->shape[0] != E ||
+        W_down->shape[1] != d || W_down->shape[2] != d_ff)
+        return MOE_ERR_SHAPE;
+    int64_t oN, od;
+    if (!act_rows(out, oN, od) || oN != N || od != d)
+        return MOE_ERR_SHAPE;
+    Dims m{N, d, E, d_ff, k, 0, 0, x->dtype};
+    m.C = capacity_of(N, E, k, capacity_factor);
+    m.ceff = m.C < N ? m.C : N;
+    rc = check_sizes(m);
+    if (rc != MOE_OK)
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stats->stream);
+    if (N == 0) {
+        stats->capacity = 0;
+        if (stats->used_capacity)
+            return hip_status(moe::launch_fill_i32(stats->used_capacity, E, 0, s));
+        return MOE_OK;
+    }
+    if (!W_up->data || !W_down->data || !out->data)
+        return MOE_ERR_NULL;
+    if (!stats->workspace)
+        return MOE_ERR_NULL;
+    if (!aligned(stats->workspace, kAlign))
+        return MOE_ERR_ALIGN;
+    if (x->dtype == MOE_BF16 &&
+        (!aligned(W_up->data, 16) || !aligned(W_down->data, 16) || !aligned(out->data, 16)))
+        return MOE_ERR_ALIGN;
+    if (x->dtype == MOE_F32 && !aligned(out->data, 16) && d % 4 == 0)
+        return MOE_ERR_ALIGN;
+    const Layout L = layout_of(m);
+    if (stats->workspace_bytes < L.total)
+        return MOE_ERR_WORKSPACE;
+
+    char *ws = static_cast<char *>(stats->workspace);
+    int32_t *idx = stats->topk_idx ? stats->topk_idx : reinterpret_cast<int32_t *>(ws + L.idx);
+    float *gate = stats->topk_gate ? stats->topk_gate : reinterpret_cast<float *>(ws + L.gate);
+    int32_t *slot = stats->slot ? stats->slot : reinterpret_cast<int32_t *>(ws + L.slot);
+    int32_t *used = stats->used_capacity ? stats->used_capacity
+                                         : reinterpret_cast<int32_t *>(ws + L.used);
+    int32_t *tiles = reinterpret_cast<int32_t *>(ws + L.tiles);
+    int32_t *slot_token = reinterpret_cast<int32_t *>(ws + L.slot_token);
+    void *H = ws + L.H;
+    float *Y = reinterpret_cast<float *>(ws + L.Y);
+    stats->capacity = m.C;
+
+    rc = router_checked(x, W_g, noise, N, d, E, k, idx, gate, s);
+    if (rc != MOE_OK)
+        return rc;
+    MOE_TRY(moe::launch_dispatch(idx, N, (int)E, k, m.ceff, slot, used, slot_token, tiles, s));
+    const bool bf16 = x->dtype == MOE_BF16;
+    MOE_TRY(moe::launch_expert_up(bf16, x->data, W_up->data, d, d_ff, (int)E, k, m.ceff, used,
+                                  slot_token, tiles, H, s));
+    MOE_TRY(moe::launch_expert_down(bf16, H, W_down->data, d, d_ff, (int)E, k, m.ceff, used,
+                                    slot_token, tiles, Y, s));
+    MOE_TRY(moe::launch_combine(Y, gate, slot, N, d, k, out->data, out->dtype, s));
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,252 @@
+// Router: scores s = W_g x + noise in fp32, top-k in descending order (equal
+// scores: lower expert id first), softmax over the k kept scores.
+// Page 1 ("Mixture of Experts (MoE) 12段階極小ビジュアル解剖シミュレーター"),
+// STEP 2 (s_raw = W_g x), STEP 4 (s = s_raw + eps), STEP 5 (KeepTopK with a
+// -inf mask), STEP 6 (softmax: masked experts get exactly 0, so only the k
+// kept scores enter the sum); nanoMoE slides 11-13 (router in full precision,
+// top-k then masked softmax).
+//
+// bf16 activations: the score product is a skinny GEMM [N, d] x [d, E]. It
+// runs on the matrix cores without losing fp32 accuracy: every fp32 router
+// weight w is split exactly into three bf16 terms w = hi + mid + lo (each
+// residual is exact in fp32 and the last one fits in bf16's 8-bit
+// significand), and a bf16 activation times a bf16 term is exact in the fp32
+// accumulator. Three bf16 MFMAs per K-step therefore give an fp32-accumulated
+// dot product of the exact inputs, at a fraction of the cost of fp32 MFMA.
+#include "common.hpp"
+
+#include <float.h>
+#include <limits.h>
+
+namespace moe {
+namespace {
+
+constexpr int kTokTile = 16;   // tokens per block (one MFMA M-tile)
+constexpr int kWaves = 4;      // split-K over the waves of a block
+
+__device__ __forceinline__ void split3(float w, unsigned short &hi, unsigned short &mid,
+                                       unsigned short &lo) {
+    hi = f32_to_bf16_bits(w);
+    const float r1 = w - bf16_bits_to_f32(hi);      // exact
+    mid = f32_to_bf16_bits(r1);
+    const float r2 = r1 - bf16_bits_to_f32(mid);    // exact, <= 8 significant bits
+    lo = f32_to_bf16_bits(r2);                      // exact
+}
+
+// Top-k of one token's scores held across the wave (lane l holds experts
+// l, l+64, ...) and the softmax of the kept scores. Every lane returns with
+// the same selection; lanes j < k write choice j.
+template <int Q>
+__device__ __forceinline__ void topk_softmax_wave(const float (&v)[Q], int E, int k, int64_t t,
+                                                  int32_t *__restrict__ idx_out,
+                                                  float *__restrict__ gate_out) {
+    const int lane = __lane_id();
+    unsigned taken = 0;
+    float my_v = -INFINITY, v0 = -INFINITY;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int be = INT_MAX;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int e = lane + 64 * q;
+            if (e < E && !((taken >> q) & 1u)) {
+                if (v[q] > bv || (v[q] == bv && e < be)) {
+                    bv = v[q];
+                    be = e;
+                }
+            }
+        }
+        // wave arg-max under the total order (score desc, id asc)
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oe = __shfl_xor(be, off);
+            if (ov > bv || (ov == bv && oe < be)) {
+                bv = ov;
+                be = oe;
+            }
+        }
+        if ((be & 63) == lane)
+            taken |= 1u << (be >> 6);
+        if (lane == j) {
+            my_v = bv;
+            my_e = be;
+        }
+        if (j == 0)
+            v0 = bv;
+    }
+    const float ex = lane < k ? expf(my_v - v0) : 0.f;
+    float den = 0.f;
+    for (int j = 0; j < k; ++j)   // choice order, identical on every lane
+        den += __shfl(ex, j);
+    if (lane < k) {
+        idx_out[t * k + lane] = my_e;
+        gate_out[t * k + lane] = ex / den;
+    }
+}
+
+// One block = 16 tokens; wave w accumulates K-chunks c = w, w+4, ... with
+// 16x16x32 bf16 MFMAs over NT tiles of 16 experts, then the four partial
+// score tiles are summed in wave order through LDS.
+template <int NT>
+__global__ __launch_bounds__(256) void router_bf16_kernel(
+    const unsigned short *__restrict__ x, const float *__restrict__ wg,
+    const float *__restrict__ noise, int N, int d, int E, int k,
+    int32_t *__restrict__ idx_out, float *__restrict__ gate_out) {
+    constexpr int EP = NT * 16;
+    constexpr int Q = (EP + 63) / 64;
+    __shared__ float red[kWaves * kTokTile * EP];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int row = lane & 15;   // token row (A) / expert column (B) of this lane
+    const int kg = lane >> 4;    // 8-element K group of this lane
+    const int64_t t0 = (int64_t)blockIdx.x * kTokTile;
+    const int64_t tok = t0 + row;
+    const bool tok_ok = tok < N;
+    const unsigned short *xrow = x + (tok_ok ? tok : 0) * (int64_t)d;
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nchunks = (d + 31) / 32;
+    for (int c = w; c < nchunks; c += kWaves) {
+        const int kof = c * 32 + kg * 8;
+        const bool k_ok = kof < d;   // d % 8 == 0: a group is all in or all out
+        u32x4 xa = {0u, 0u, 0u, 0u};
+        if (tok_ok && k_ok)
+            xa = *reinterpret_cast<const u32x4 *>(xrow + kof);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, xa);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int e = nt * 16 + row;
+            f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
+            if (e < E && k_ok) {
+                const float *wp = wg + (int64_t)e * d + kof;
+                w0 = *reinterpret_cast<const f32x4 *>(wp);
+                w1 = *reinterpret_cast<const f32x4 *>(wp + 4);
+            }
+            u16x8 hi, mid, lo;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                unsigned short h, m, l;
+                split3(w0[i], h, m, l);
+                hi[i] = h; mid[i] = m; lo[i] = l;
+                split3(w1[i], h, m, l);
+                hi[i + 4] = h; mid[i + 4] = m; lo[i + 4] = l;
+            }
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, hi), acc[nt], 0, 0, 0);
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, mid), acc[nt], 0, 0, 0);
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, lo), acc[nt], 0, 0, 0);
+        }
+    }
+    // acc[nt][i] holds the partial score of token 4*kg+i for expert nt*16+row
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            red[(w * kTokTile + 4 * kg + i) * EP + nt * 16 + row] = acc[nt][i];
+    __syncthreads();
+
+    // wave w ranks tokens 4w .. 4w+3 of the tile
+    for (int tt = 0; tt < kTokTile / kWaves; ++tt) {
+        const int m = w * (kTokTile / kWaves) + tt;
+        const int64_t t = t0 + m;
+        if (t >= N)
+            break;
+        float v[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int e = lane + 64 * q;
+            float s = -INFINITY;
+            if (e < E) {
+                s = red[(0 * kTokTile + m) * EP + e];
+#pragma unroll
+                for (int ww = 1; ww < kWaves; ++ww)
+                    s += red[(ww * kTokTile + m) * EP + e];
+                if (noise)
+                    s += noise[t * E + e];
+                if (s != s)
+                    s = -INFINITY;   // a NaN score never outranks a number
+            }
+            v[q] = s;
+        }
+        topk_softmax_wave<Q>(v, E, k, t, idx_out, gate_out);
+    }
+}
+
+// fp32 activations: one wave per token, lanes stride over d, the wave then
+// reduces each expert's partial sums in a fixed butterfly order.
+__global__ __launch_bounds__(256) void router_f32_kernel(
+    const float *__restrict__ x, const float *__restrict__ wg, const float *__restrict__ noise,
+    int N, int d, int E, int k, int32_t *__restrict__ idx_out, float *__restrict__ gate_out) {
+    constexpr int Q = kMaxQ;
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= N)
+        return;
+    const float *xr = x + t * (int64_t)d;
+    float v[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+        v[q] = -INFINITY;
+    for (int e = 0; e < E; ++e) {
+        float p = 0.f;
+        for (int i = lane; i < d; i += 64)
+            p = fmaf(wg[(int64_t)e * d + i], xr[i], p);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1)
+            p += __shfl_xor(p, off);
+        p = __shfl(p, 0);   // every lane takes lane 0's sum
+        if (noise)
+            p += noise[t * E + e];
+        if (p != p)
+            p = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            if (e == lane + 64 * q)
+                v[q] = p;
+    }
+    topk_softmax_wave<Q>(v, E, k, t, idx_out, gate_out);
+}
+
+template <int NT>
+hipError_t launch_nt(const void *x, const float *wg, const float *noise, int64_t N, int64_t d,
+                     int E, int k, int32_t *idx, float *gate, hipStream_t s) {
+    const int blocks = (int)((N + kTokTile - 1) / kTokTile);
+    hipLaunchKernelGGL(router_bf16_kernel<NT>, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const unsigned short *>(x), wg, noise, (int)N, (int)d, E, k,
+                       idx, gate);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_router_bf16(const void *x, const float *wg, const float *noise, int64_t N,
+                              int64_t d, int E, int k, int32_t *idx, float *gate,
+                              hipStream_t s) {
+    if (N == 0)
+        return hipSuccess;
+    const int nt = (E + 15) / 16;
+    if (nt <= 1) return launch_nt<1>(x, wg, noise, N, d, E, k, idx, gate, s);
+    if (nt <= 2) return launch_nt<2>(x, wg, noise, N, d, E, k, idx, gate, s);
+    if (nt <= 4) return launch_nt<4>(x, wg, noise, N, d, E, k, idx, gate, s);
+    if (nt <= 8) return launch_nt<8>(x, wg, noise, N, d, E, k, idx, gate, s);
+    return launch_nt<16>(x, wg, noise, N, d, E, k, idx, gate, s);
+}
+
+hipError_t launch_router_f32(const float *x, const float *wg, const float *noise, int64_t N,
+                             int64_t d, int E, int k, int32_t *idx, float *gate,
+                             hipStream_t s) {
+    if (N == 0)
+        return hipSuccess;
+    const int blocks = (int)((N + 3) / 4);
+    hipLaunchKernelGGL(router_f32_kernel, dim3(blocks), dim3(256), 0, s, x, wg, noise, (int)N,
+                       (int)d, E, k, idx, gate);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -185,6 +185,11 @@ class Workload:
         self.expert_seed = expert_seed
         self._fixed = fixed_experts
         self.resampled = resampled
+        self._memo = {}
+
+    def memo(self, which: str, e: int, a: np.ndarray) -> None:
+        """Keep an already generated expert matrix for later calls."""
+        self._memo[(which, e)] = a
 
     # shapes ---------------------------------------------------------------
     @property
@@ -202,6 +207,8 @@ class Workload:
     def w_up(self, e: int) -> np.ndarray:
         if self._fixed is not None:
             return self._fixed[0][e]
+        if ("up", e) in self._memo:
+            return self._memo[("up", e)]
         a = _rng(self.expert_seed, _S_WUP, e).standard_normal((self.d_ff, self.d), dtype=np.float32)
         a *= np.float32(self.cfg.w_std)
         return _cast(a, self.cfg.dtype)
@@ -209,6 +216,8 @@ class Workload:
     def w_down(self, e: int) -> np.ndarray:
         if self._fixed is not None:
             return self._fixed[1][e]
+        if ("down", e) in self._memo:
+            return self._memo[("down", e)]
         a = _rng(self.expert_seed, _S_WDOWN, e).standard_normal((self.d, self.d_ff), dtype=np.float32)
         a *= np.float32(self.cfg.w_std)
         return _cast(a, self.cfg.dtype)

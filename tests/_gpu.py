@@ -1,0 +1,89 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare it with the oracle on the same seeded inputs.
+
+Tolerances (fixed by the layer's contract):
+  * expert ids, slots, used counts, capacity: bit-exact;
+  * gates: |gpu - oracle| <= 1e-5 (fp32 softmax vs float64);
+  * fp32 layer outputs: max |gpu - oracle| <= 1e-4;
+  * bf16 layer outputs: relative L2 <= 1e-2 and max abs <= 5e-2.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+GATE_TOL = 1e-5
+F32_MAX_ABS = 1e-4
+BF16_REL_L2 = 1e-2
+BF16_MAX_ABS = 5e-2
+
+
+def have_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_np(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def out_f64(wl, out_t, rows=None):
+    from sparse_mixture_experts_20_amd import workloads as W
+    a = to_np(out_t)
+    if rows is not None:
+        a = a[rows]
+    if a.dtype == np.uint16:
+        return W.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def run_forward(dev):
+    from sparse_mixture_experts_20_amd import binding as B
+    return B.forward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"],
+                     dev["k"], dev["cf"], export=True)
+
+
+def check_routing(res, stats):
+    """Bit-exact ids, slots, used and capacity; gates within GATE_TOL."""
+    assert stats.capacity == res.C
+    np.testing.assert_array_equal(to_np(stats.idx), res.idx)
+    g = to_np(stats.gate).astype(np.float64)
+    assert np.abs(g - res.gate).max() <= GATE_TOL
+    np.testing.assert_array_equal(to_np(stats.slot), res.slot)
+    np.testing.assert_array_equal(to_np(stats.used), res.used)
+
+
+def check_out(dtype, got, ref):
+    """got, ref: float64 arrays of the same rows."""
+    err = np.abs(got - ref)
+    if dtype == "f32":
+        assert err.max() <= F32_MAX_ABS, err.max()
+    else:
+        rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+        assert rel <= BF16_REL_L2, rel
+        assert err.max() <= BF16_MAX_ABS, err.max()
+    return float(err.max())
+
+
+def sample_rows(res, n, seed=0):
+    """A seeded sample of token rows: the first and last token, tokens that
+    lost at least one choice to capacity (if any), and random tokens."""
+    rng = np.random.default_rng(seed)
+    N = res.N
+    dropped = np.nonzero((res.slot < 0).any(axis=1))[0]
+    pick = [0, N - 1]
+    if len(dropped):
+        pick += list(rng.choice(dropped, size=min(len(dropped), n // 4), replace=False))
+    pick += list(rng.choice(N, size=min(N, n), replace=False))
+    return np.unique(np.array(pick, dtype=np.int64))

@@ -1,0 +1,164 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, and rejects bad arguments before enqueuing anything (no GPU needed:
+every call here fails validation, which runs before any HIP call)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from sparse_mixture_experts_20_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+F32, BF16 = B.MOE_F32, B.MOE_BF16
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(L):
+    names = _declared()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_error_strings(L):
+    for code in range(0, -9, -1):
+        s = B.error_string(code)
+        assert s and s != "unknown error code"
+    assert B.error_string(7) == "unknown error code"
+
+
+def test_capacity_helper(L):
+    assert B.capacity(2048, 8, 2, 1.25) == 640
+    assert B.capacity(4, 3, 2, 0.375) == 1
+    assert B.capacity(16384, 16, 2, 1.0) == 2048
+    assert B.capacity(8192, 256, 8, 1.5) == 384
+    assert B.capacity(0, 8, 2, 1.0) == 0
+    assert B.capacity(10, 8, 9, 1.0) == -1
+    assert B.capacity(10, 8, 2, 0.0) == -1
+    assert B.capacity(10, 8, 2, float("nan")) == -1
+    assert B.capacity(10, 8, 2, float("inf")) == -1
+
+
+def test_workspace_size(L):
+    ws = B.lib().moe_workspace_size
+    n = ws(2048, 768, 8, 3072, 2, 1.25, BF16)
+    # at least H (E*C*d_ff bf16) and Y (N*k*d fp32)
+    assert n >= 8 * 640 * 3072 * 2 + 2048 * 2 * 768 * 4
+    assert n % 256 == 0
+    assert ws(2048, 768, 8, 3072, 9, 1.25, BF16) == 0      # k > E
+    assert ws(2048, 768, 8, 3072, 2, -1.0, BF16) == 0      # cf <= 0
+    assert ws(2048, 768, 8, 3072, 2, 1.0, 7) == 0          # dtype
+    assert ws(2048, 770, 8, 3072, 2, 1.0, BF16) == 0       # bf16 needs d % 8 == 0
+    assert ws(2048, 770, 8, 3072, 2, 1.0, F32) > 0
+    assert ws(10, 8, 300, 8, 2, 1.0, F32) == 0             # E > 256
+    assert ws(0, 8, 4, 8, 2, 1.0, F32) > 0                 # empty call is valid
+
+
+def _t(ptr, dtype, *shape):
+    sh = (ctypes.c_int64 * 4)(*(list(shape) + [0] * (4 - len(shape))))
+    return B.MoeTensor(ctypes.c_void_p(ptr), dtype, len(shape), sh)
+
+
+FAKE = 0x10000  # never dereferenced: validation fails first
+
+
+def _call(x, wg, noise, wu, wd, k, cf, out, stats):
+    r = ctypes.byref
+    return B.lib().moe_forward(r(x) if x else None, r(wg) if wg else None,
+                               r(noise) if noise else None, r(wu) if wu else None,
+                               r(wd) if wd else None, k, cf, r(out) if out else None,
+                               r(stats) if stats else None)
+
+
+def _good(N=64, d=16, E=4, dff=32, dt=BF16):
+    x = _t(FAKE, dt, N, d)
+    wg = _t(FAKE, F32, E, d)
+    wu = _t(FAKE, dt, E, dff, d)
+    wd = _t(FAKE, dt, E, d, dff)
+    out = _t(FAKE, dt, N, d)
+    st = B.MoeStats(None, ctypes.c_void_p(FAKE), 1, None, None, None, None, -1)
+    return x, wg, wu, wd, out, st
+
+
+def test_forward_rejects_bad_arguments(L):
+    x, wg, wu, wd, out, st = _good()
+    E = B
+    assert _call(x, wg, None, wu, wd, 2, 1.0, out, None) == -1          # stats NULL
+    assert _call(None, wg, None, wu, wd, 2, 1.0, out, st) == -1         # x NULL
+    assert _call(x, wg, None, wu, wd, 0, 1.0, out, st) == -4            # k < 1
+    assert _call(x, wg, None, wu, wd, 5, 1.0, out, st) == -4            # k > E
+    assert _call(x, wg, None, wu, wd, 2, 0.0, out, st) == -4            # cf = 0
+    assert _call(x, wg, None, wu, wd, 2, -2.0, out, st) == -4           # cf < 0
+    assert _call(x, wg, None, wu, wd, 2, math.nan, out, st) == -4       # cf NaN
+    assert _call(x, wg, None, wu, wd, 2, math.inf, out, st) == -4       # cf inf
+    # workspace far too small
+    assert _call(x, wg, None, wu, wd, 2, 1.0, out, st) == -5
+    # W_g must be fp32
+    assert _call(x, _t(FAKE, BF16, 4, 16), None, wu, wd, 2, 1.0, out, st) == -3
+    # weights must share x's dtype
+    assert _call(x, wg, None, _t(FAKE, F32, 4, 32, 16), wd, 2, 1.0, out, st) == -3
+    assert _call(x, wg, None, wu, wd, 2, 1.0, _t(FAKE, F32, 64, 16), st) == -3
+    # shapes
+    assert _call(x, _t(FAKE, F32, 4, 17), None, wu, wd, 2, 1.0, out, st) == -2
+    assert _call(x, wg, None, _t(FAKE, BF16, 4, 32, 8), wd, 2, 1.0, out, st) == -2
+    assert _call(x, wg, None, wu, _t(FAKE, BF16, 4, 16, 31), 2, 1.0, out, st) == -2
+    assert _call(x, wg, None, wu, wd, 2, 1.0, _t(FAKE, BF16, 63, 16), st) == -2
+    assert _call(x, wg, _t(FAKE, F32, 64, 3), wu, wd, 2, 1.0, out, st) == -2   # noise [N,E]
+    assert _call(x, wg, _t(FAKE, BF16, 64, 4), wu, wd, 2, 1.0, out, st) == -3  # noise fp32
+    # noise given but data NULL
+    assert _call(x, wg, _t(0, F32, 64, 4), wu, wd, 2, 1.0, out, st) == -1
+    # limits: E > 256, k > 16, bf16 d % 8
+    x2, wg2, wu2, wd2, out2, st2 = _good(E=300)
+    assert _call(x2, wg2, None, wu2, wd2, 2, 1.0, out2, st2) == -6
+    x3, wg3, wu3, wd3, out3, st3 = _good(E=32)
+    assert _call(x3, wg3, None, wu3, wd3, 17, 1.0, out3, st3) == -6
+    x4, wg4, wu4, wd4, out4, st4 = _good(d=12)
+    assert _call(x4, wg4, None, wu4, wd4, 2, 1.0, out4, st4) == -6
+    # misaligned workspace
+    st5 = B.MoeStats(None, ctypes.c_void_p(FAKE + 4), 1 << 40, None, None, None, None, -1)
+    assert _call(x, wg, None, wu, wd, 2, 1.0, out, st5) == -7
+    # misaligned bf16 activation
+    assert _call(_t(FAKE + 2, BF16, 64, 16), wg, None, wu, wd, 2, 1.0, out, st) == -7
+    # nothing was reported as a capacity on failure paths before validation passed
+    assert st.capacity == -1
+
+
+def test_stage_entry_points_reject_bad_arguments(L):
+    v = ctypes.c_void_p(FAKE)
+    # dispatch: k > E, capacity 0 with tokens, E > 256, NULL outputs
+    assert L.moe_dispatch(10, 4, 5, 3, v, v, v, v, v, None) == -4
+    assert L.moe_dispatch(10, 4, 2, 0, v, v, v, v, v, None) == -4
+    assert L.moe_dispatch(10, 300, 2, 3, v, v, v, v, v, None) == -6
+    assert L.moe_dispatch(10, 4, 2, 3, None, v, v, v, v, None) == -1
+    # combine: shape mismatch, bad dtype
+    out = _t(FAKE, F32, 10, 8)
+    assert L.moe_combine(11, 8, 2, v, v, v, ctypes.byref(out), None) == -2
+    bad = _t(FAKE, 5, 10, 8)
+    assert L.moe_combine(10, 8, 2, v, v, v, ctypes.byref(bad), None) == -3
+    assert L.moe_combine(10, 8, 2, None, v, v, ctypes.byref(out), None) == -1
+    # router: k > E, W_g dtype
+    x = _t(FAKE, BF16, 10, 16)
+    wg = _t(FAKE, F32, 4, 16)
+    assert L.moe_router(ctypes.byref(x), ctypes.byref(wg), None, 5, v, v, None) == -4
+    wgb = _t(FAKE, BF16, 4, 16)
+    assert L.moe_router(ctypes.byref(x), ctypes.byref(wgb), None, 2, v, v, None) == -3
+    assert L.moe_router(ctypes.byref(x), ctypes.byref(wg), None, 2, None, v, None) == -1
+    # experts: mismatched weight shapes
+    wu = _t(FAKE, BF16, 4, 32, 16)
+    wd = _t(FAKE, BF16, 4, 16, 31)
+    assert L.moe_experts(ctypes.byref(x), ctypes.byref(wu), ctypes.byref(wd), 2, 5, v, v, v, v,
+                         v, None) == -2

@@ -1,0 +1,139 @@
+"""Each stage of the layer on its own, through its C-ABI entry point, against
+the oracle's function for that step on the same inputs."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_mixture_experts_20_amd import workloads as W
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_mod():
+    if not G.have_gpu():
+        pytest.skip("no HIP device")
+    import torch
+    from sparse_mixture_experts_20_amd import binding as B
+    B.lib()
+    return torch
+
+
+@pytest.mark.parametrize("N,E,k,C,seed", [
+    (5000, 37, 3, 300, 1), (4096, 8, 2, 640, 2), (20000, 16, 2, 1500, 3),
+    (7, 4, 2, 1, 4), (65536 // 8, 256, 8, 200, 5), (1, 1, 1, 1, 6), (4097, 5, 5, 4097, 7),
+])
+def test_dispatch_matches_oracle(torch_mod, N, E, k, C, seed):
+    torch = torch_mod
+    from sparse_mixture_experts_20_amd import binding as B
+    G.say(f"[stage] dispatch N={N} E={E} k={k} C={C}")
+    rng = np.random.default_rng(seed)
+    # skewed expert popularity so that some experts overflow
+    p = rng.dirichlet(np.full(E, 0.5))
+    idx = np.empty((N, k), np.int32)
+    for t in range(N):
+        idx[t] = rng.choice(E, size=k, replace=False, p=p if k < E else None)
+    slot, used, slot_token, tiles = B.dispatch(torch.from_numpy(idx).cuda(), E, C)
+    torch.cuda.synchronize()
+    ref_slot, ref_used = oracle.assign(idx, E, C)
+    np.testing.assert_array_equal(G.to_np(slot), ref_slot)
+    np.testing.assert_array_equal(G.to_np(used), ref_used)
+    st = G.to_np(slot_token)
+    ceff = min(C, N)
+    for e in range(E):
+        a = st[e, :ref_used[e]]
+        t, j = a // k, a % k
+        np.testing.assert_array_equal(idx[t, j], e)
+        np.testing.assert_array_equal(ref_slot[t, j], np.arange(ref_used[e]))
+    tl = G.to_np(tiles)
+    c128 = np.concatenate([[0], np.cumsum((ref_used + 127) // 128)])
+    c64 = np.concatenate([[0], np.cumsum((ref_used + 63) // 64)])
+    np.testing.assert_array_equal(tl[:E + 1], c128)
+    np.testing.assert_array_equal(tl[E + 1:], c64)
+    assert st.shape == (E, max(ceff, 1))
+
+
+@pytest.mark.parametrize("name", ["nanomoe", "skew"])
+def test_router_matches_oracle(torch_mod, name):
+    torch = torch_mod
+    from sparse_mixture_experts_20_amd import binding as B
+    from sparse_mixture_experts_20_amd import device as D
+    wl = W.make(name)
+    G.say(f"[stage] router {name}")
+    x = D._t(wl.x, "cuda")
+    wg = D._t(wl.wg, "cuda")
+    nz = None if wl.noise is None else D._t(wl.noise, "cuda")
+    idx, gate = B.router(x, wg, nz, wl.k)
+    torch.cuda.synchronize()
+    _, ridx, rgate = oracle.router(wl.x64(), wl.wg64(), wl.noise64(), wl.k)
+    np.testing.assert_array_equal(G.to_np(idx), ridx)
+    assert np.abs(G.to_np(gate) - rgate).max() <= G.GATE_TOL
+
+
+def test_router_many_experts(torch_mod):
+    torch = torch_mod
+    from sparse_mixture_experts_20_amd import binding as B
+    from sparse_mixture_experts_20_amd import device as D
+    wl = W.custom("router256", N=2000, d=1024, E=256, k=8, d_ff=8, dtype="bf16", cf=1.0,
+                  sigma=0.0, seed=31)
+    G.say("[stage] router E=256")
+    idx, gate = B.router(D._t(wl.x, "cuda"), D._t(wl.wg, "cuda"), None, wl.k)
+    torch.cuda.synchronize()
+    _, ridx, rgate = oracle.router(wl.x64(), wl.wg64(), None, wl.k)
+    np.testing.assert_array_equal(G.to_np(idx), ridx)
+    assert np.abs(G.to_np(gate) - rgate).max() <= G.GATE_TOL
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_combine_matches_oracle(torch_mod, dt):
+    torch = torch_mod
+    from sparse_mixture_experts_20_amd import binding as B
+    G.say(f"[stage] combine {dt}")
+    rng = np.random.default_rng(41)
+    N, k, d = 3001, 3, 520
+    y = rng.standard_normal((N, k, d)).astype(np.float32)
+    gate = rng.dirichlet(np.ones(k), size=N).astype(np.float32)
+    slot = np.where(rng.random((N, k)) < 0.2, -1, 0).astype(np.int32)
+    slot[5] = -1   # a token with every choice dropped
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out = torch.empty((N, d), dtype=tdt, device="cuda")
+    B.combine(torch.from_numpy(y.reshape(N * k, d)).cuda(), torch.from_numpy(gate).cuda(),
+              torch.from_numpy(slot).cuda(), out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(gate.astype(np.float64), slot, y.astype(np.float64))
+    got = G.to_np(out)
+    got = W.bf16_bits_to_f32(got).astype(np.float64) if dt == "bf16" else got.astype(np.float64)
+    assert np.all(got[5] == 0.0)
+    if dt == "f32":
+        assert np.abs(got - ref).max() <= 1e-5
+    else:
+        # one rounding to bf16: within half an ulp of the fp32 sum
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0**-8 + 1e-6)
+
+
+@pytest.mark.parametrize("name", ["ragged", "mid"])
+def test_experts_match_oracle(torch_mod, name):
+    """Grouped FFN over the oracle's own dispatch plan: every kept
+    assignment's expert output row Y[t*k+j] against the oracle's y."""
+    torch = torch_mod
+    from sparse_mixture_experts_20_amd import binding as B
+    from sparse_mixture_experts_20_amd import device as D
+    if name == "ragged":
+        wl = W.custom("x", N=700, d=200, E=6, k=2, d_ff=328, dtype="bf16", cf=0.9, sigma=0.4,
+                      seed=51, w_std=0.05)
+    else:
+        wl = W.custom("x", N=2048, d=768, E=8, k=2, d_ff=3072, dtype="bf16", cf=1.25,
+                      sigma=1.0, seed=52, w_std=0.02)
+    G.say(f"[stage] experts {name}")
+    res = oracle.forward(wl, want_y=True)
+    dev = D.upload(wl)
+    slot, used, slot_token, tiles = B.dispatch(torch.from_numpy(res.idx).cuda(), wl.E, res.C)
+    H, Y = B.experts(dev["x"], dev["W_up"], dev["W_down"], wl.k, res.C, used, slot_token, tiles)
+    torch.cuda.synchronize()
+    Yg = G.to_np(Y).reshape(wl.N, wl.k, wl.d).astype(np.float64)
+    kept = res.slot >= 0
+    got, ref = Yg[kept], res.y[kept]
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel <= G.BF16_REL_L2, rel
+    assert np.abs(got - ref).max() <= G.BF16_MAX_ABS

@@ -152,7 +152,7 @@ int moe_router(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noi
  *                                     t*k + j holding slot r of expert e
  *                                     (rows past used[e] are left untouched)
  *   tiles       int32 [2*(E+1)]       prefix sums of ceil(used[e]/128) and
- *                                     ceil(used[e]/64): the expert kernels'
+ *                                     ceil(used[e]/256): the expert kernels'
  *                                     tile schedule
  * An id outside [0, E) in topk_idx is not counted and its slot is -1. */
 int moe_dispatch(int64_t N, int64_t E, int k, int64_t capacity, const int32_t *topk_idx,

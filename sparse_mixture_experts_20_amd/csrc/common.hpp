@@ -58,14 +58,15 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 // Grouped expert products. mode 0: H = ReLU(x[gather] W_up^T); mode 1:
 // Y[scatter] = H W_down^T.
 // bf16 != 0: bf16 operands on matrix cores; otherwise fp32 operands.
+// rows_per_expert: the expected kept rows per expert (picks the tile shape).
 hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t d,
                             int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                             const int32_t *slot_token, const int32_t *tiles, void *H,
-                            hipStream_t s);
+                            int64_t rows_per_expert, hipStream_t s);
 hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int64_t d,
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, float *Y,
-                              hipStream_t s);
+                              int64_t rows_per_expert, hipStream_t s);
 
 hipError_t launch_combine(const float *Y, const float *gate, const int32_t *slot,
                           int64_t N, int64_t d, int k, void *out, int out_dtype,

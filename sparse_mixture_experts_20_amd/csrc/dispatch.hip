@@ -108,17 +108,17 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
         used[e] = base[e] < ceff ? base[e] : ceff;
     __syncthreads();
     if (tid == 0) {
-        // tile schedule of the expert kernels: prefix sums of row tiles of 128 and 64
-        int a128 = 0, a64 = 0;
+        // tile schedule of the expert kernels: prefix sums of row tiles of 128 and 256
+        int a128 = 0, a256 = 0;
         for (int e = 0; e < E; ++e) {
             tiles[e] = a128;
-            tiles[E + 1 + e] = a64;
+            tiles[E + 1 + e] = a256;
             const int u = base[e] < ceff ? base[e] : ceff;
             a128 += (u + 127) / 128;
-            a64 += (u + 63) / 64;
+            a256 += (u + 255) / 256;
         }
         tiles[E] = a128;
-        tiles[2 * E + 1] = a64;
+        tiles[2 * E + 1] = a256;
     }
 }
 

@@ -15,38 +15,88 @@
 // is ever written; the down product scatters its rows straight into the
 // assignment-ordered buffer the combine reads.
 //
-// bf16 tile: 128 x 128 outputs, K-step 64, 256 threads = 2 x 2 waves of
-// 64 x 64, each built from 16x16x32 bf16 MFMAs with fp32 accumulation; A and
-// B tiles double-buffered in LDS (rows padded by 16 bytes so the 16-byte
-// reads of a wave hit distinct banks). Tiles are enumerated only for rows that
-// exist (the dispatch plan's prefix of ceil(used[e]/128)); consecutive tiles
-// of one expert walk its row tiles fastest so the blocks in flight share each
-// weight tile, and each XCD (blocks b with the same b % 8) receives one
-// contiguous range of tiles so that sharing happens inside one L2.
+// bf16 kernel: a BM x BN output tile per workgroup, K-step 64, waves laid out
+// WAVES_M x WAVES_N with a 16x16x32 bf16 MFMA grid each (fp32 accumulation).
+// A and B K-tiles are double-buffered in LDS (rows padded by 16 bytes so the
+// 16-byte operand reads of a wave hit distinct banks) and staged through
+// registers P tiles ahead of use: the loads of tile kt+P are issued before
+// the MFMAs of tile kt. Barriers wait on LDS traffic only, so those loads
+// stay in flight across them (a workgroup fence would drain them every
+// K-step). The epilogue transposes each wave's 16-row strips through LDS so
+// every lane stores 16 contiguous bytes.
+//
+// Scheduling: tiles exist only for rows that exist (the dispatch plan's
+// prefix of ceil(used[e]/BM), read on the device, so no host sync). The tile
+// index walks an expert's row tiles fastest, so the blocks in flight share
+// each weight tile, and block b (placed on XCD b mod 8 by the dispatcher)
+// takes tile (b mod 8) * T/8 + b/8: every XCD works through one contiguous
+// range of tiles and the sharing happens inside its own L2.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDK = BK + 8;            // padded LDS row (bf16 elements)
-constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 
-template <int MODE>   // 0: up (gather x rows, ReLU, store H in bf16); 1: down (fp32, scatter to Y)
-__global__ __launch_bounds__(kThreads, 2) void experts_bf16_kernel(
+// Workgroup barrier that waits for this wave's LDS traffic only (no memory
+// fence, so the compiler does not drain outstanding global loads here).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 32-bit LDS offset of a pointer into __shared__ memory.
+__device__ __forceinline__ unsigned lds_off(const void *p) {
+    return (unsigned)(uintptr_t)((__attribute__((address_space(3))) const void *)p);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// LDS offset m0 + 16*l (one wave moves 1 KB). Issued in asm so that the
+// compiler's wait insertion does not treat every later LDS read as aliasing
+// it; the waits are explicit (wait_vm).
+__device__ __forceinline__ void dma16(unsigned lds_base, const void *g) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 ::"s"(lds_base), "v"(g)
+                 : "memory", "m0");
+}
+
+// BM x BN output tile, K-step BKT, S-stage LDS ring filled by direct loads.
+// Each K-tile row is BKT bf16 = RB bytes of 16-byte chunks; chunk c of row r
+// is stored at position c ^ ((r / RPB) % CPR) (RPB rows share one 256-byte
+// bank row), so the 16 lanes that read 16 consecutive rows at one chunk hit
+// 16 distinct bank groups.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BKT, int S, int MODE>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void expert_gemm_kernel(
     const unsigned short *__restrict__ A_src, const unsigned short *__restrict__ W, int K,
     int Nout, int E, int k, int ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
     unsigned short *__restrict__ H_out, float *__restrict__ Y_out) {
-    __shared__ unsigned short As[2][BM * LDK];
-    __shared__ unsigned short Bs[2][BN * LDK];
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int NTHR = NW * 64;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;   // wave tile
+    constexpr int FM = WTM / 16, FN = WTN / 16;              // MFMA tiles per wave
+    constexpr int RB = BKT * 2;                              // bytes per K-tile row
+    constexpr int CPR = BKT / 8;                             // 16-byte chunks per row
+    constexpr int RPB = 256 / RB;                            // rows per 256-byte bank row
+    constexpr int RPI = 1024 / RB;                           // rows per direct-load wave op
+    constexpr int IA = BM / (RPI * NW), IB = BN / (RPI * NW);  // ops per wave per stage
+    constexpr int G = IA + IB;
+    constexpr int STAGE = (BM + BN) * RB;                    // bytes per stage
+    static_assert(BKT % 32 == 0 && S >= 2, "K-step is a multiple of one MFMA K");
+    static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile/waves mismatch");
+    static_assert(WTN % 32 == 0, "epilogue splits a wave row into 4 lanes x 8k columns");
+    static_assert(NW * 16 * (WTN + 4) * 4 <= S * STAGE, "epilogue scratch");
+    __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
     __shared__ int s_mt[kMaxExperts + 1];
 
     const int tid = threadIdx.x;
     const int NT = (Nout + BN - 1) / BN;
-
-    for (int i = tid; i <= E; i += kThreads)
+    for (int i = tid; i <= E; i += NTHR)
         s_mt[i] = mt_off[i];
     __syncthreads();
     const int T = s_mt[E] * NT;
@@ -70,113 +120,160 @@ __global__ __launch_bounds__(kThreads, 2) void experts_bf16_kernel(
     const int n0 = (local / mte) * BN;
     const int rows = used[e];
 
-    // global -> LDS copy assignment: 8 threads per 64-element row, 32 rows per pass
-    const int lrow = tid >> 3;
-    const int lk = (tid & 7) * 8;
-    const unsigned short *arow[4];
-    const unsigned short *brow[4];
-    bool aok[4], bok[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int r = m0 + p * 32 + lrow;
-        aok[p] = r < rows;
-        int64_t src = 0;
-        if (aok[p]) {
-            const int64_t srow = (int64_t)e * ceff + r;
-            src = MODE == 0 ? (int64_t)(slot_token[srow] / k) : srow;
-        }
-        arow[p] = A_src + src * K;
-        const int n = n0 + p * 32 + lrow;
-        bok[p] = n < Nout;
-        brow[p] = W + ((int64_t)e * Nout + (bok[p] ? n : 0)) * K;
-    }
-
     const int lane = tid & 63;
-    const int wv = tid >> 6;
-    const int wm = wv >> 1, wn = wv & 1;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv / WAVES_N, wn = wv % WAVES_N;
 
-    f32x4 acc[4][4];
+    // Direct-load sources of this lane: one row and one 16-byte chunk per op.
+    // Rows past the tile edge read row 0 of the expert (their outputs are
+    // never stored); the K tail is zeroed in LDS after the last step lands.
+    const unsigned short *ga[IA];
+    const unsigned short *gb[IB];
+    int ca[IA], cb[IB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    u32x4 ra[4], rb[4];
-    auto gload = [&](int kt) {
-        const int kk = kt * BK + lk;
-        const bool kok = kk < K;   // K % 8 == 0
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            ra[p] = (aok[p] && kok) ? *reinterpret_cast<const u32x4 *>(arow[p] + kk)
-                                    : u32x4{0u, 0u, 0u, 0u};
-            rb[p] = (bok[p] && kok) ? *reinterpret_cast<const u32x4 *>(brow[p] + kk)
-                                    : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto sstore = [&](int st) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            *reinterpret_cast<u32x4 *>(&As[st][(p * 32 + lrow) * LDK + lk]) = ra[p];
-            *reinterpret_cast<u32x4 *>(&Bs[st][(p * 32 + lrow) * LDK + lk]) = rb[p];
-        }
-    };
-
-    const int KT = (K + BK - 1) / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int st = kt & 1;
-        if (kt + 1 < KT)
-            gload(kt + 1);
-#pragma unroll
-        for (int ks = 0; ks < BK; ks += 32) {
-            const int kof = ks + (lane >> 4) * 8;
-            bf16x8 af[4], bfr[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wm * 64 + i * 16 + (lane & 15);
-                af[i] = *reinterpret_cast<const bf16x8 *>(&As[st][r * LDK + kof]);
-                const int c = wn * 64 + i * 16 + (lane & 15);
-                bfr[i] = *reinterpret_cast<const bf16x8 *>(&Bs[st][c * LDK + kof]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < KT)
-            sstore(st ^ 1);
-        __syncthreads();
+    for (int i = 0; i < IA; ++i) {
+        const int row = (wv * IA + i) * RPI + lane / CPR;
+        ca[i] = (lane % CPR) ^ ((row / RPB) % CPR);
+        const int r = m0 + row;
+        const int64_t srow = (int64_t)e * ceff + (r < rows ? r : 0);
+        const int64_t src = MODE == 0 ? (int64_t)(slot_token[srow] / k) : srow;
+        ga[i] = A_src + src * K;
     }
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+        const int row = (wv * IB + i) * RPI + lane / CPR;
+        cb[i] = (lane % CPR) ^ ((row / RPB) % CPR);
+        const int n = n0 + row;
+        gb[i] = W + ((int64_t)e * Nout + (n < Nout ? n : 0)) * K;
+    }
+    const unsigned smem_off = lds_off(smem);
+    auto issue = [&](int kt) {
+        const unsigned base = smem_off + (unsigned)((kt % S) * STAGE);
+#pragma unroll
+        for (int i = 0; i < IA; ++i) {
+            const int kk = min(kt * BKT + ca[i] * 8, K - 8);
+            dma16(base + (unsigned)((wv * IA + i) * 1024), ga[i] + kk);
+        }
+#pragma unroll
+        for (int i = 0; i < IB; ++i) {
+            const int kk = min(kt * BKT + cb[i] * 8, K - 8);
+            dma16(base + (unsigned)(BM * RB + (wv * IB + i) * 1024), gb[i] + kk);
+        }
+    };
 
-    // epilogue: acc[i][j][q] is row wm*64 + i*16 + 4*(lane/16) + q, column wn*64 + j*16 + lane%16
+    // operand reads: row r, chunk c sits at r*RB + ((c ^ ((r/RPB)%CPR)) * 16);
+    // for this lane's rows the swizzle term is the same for every 16-row tile
+    const int ra0 = wm * WTM + (lane & 15), rb0 = wn * WTN + (lane & 15);
+    const int xa = (ra0 / RPB) % CPR, xb = (rb0 / RPB) % CPR;
+    f32x4 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + q;
-            if (r >= rows)
-                continue;
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int st) {
+        const char *As = smem + st * STAGE;
+        const char *Bs = As + BM * RB;
+#pragma unroll
+        for (int ks = 0; ks < BKT; ks += 32) {
+            const int c = ks / 8 + (lane >> 4);
+            bf16x8 af[FM], bfr[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8 *>(As + (ra0 + i * 16) * RB + ((c ^ xa) << 4));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8 *>(Bs + (rb0 + j * 16) * RB + ((c ^ xb) << 4));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j],
+                                                                       0, 0, 0);
+        }
+    };
+    // zero the chunks of the last K-tile that lie past K (both operands)
+    auto zero_tail = [&](int kt) {
+        char *st = smem + (kt % S) * STAGE;
+        for (int q = tid; q < (BM + BN) * CPR; q += NTHR) {
+            const int row = q / CPR, c = q % CPR;
+            if (kt * BKT + c * 8 >= K)
+                *reinterpret_cast<u32x4 *>(st + row * RB + ((c ^ ((row / RPB) % CPR)) << 4)) =
+                    u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
+    const int KT = (K + BKT - 1) / BKT;
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+        if (s < KT)
+            issue(s);
+    for (int kt = 0; kt < KT; ++kt) {
+        // tile kt must have landed: later tiles issued so far may stay in flight
+        const int later = min(S - 2, KT - 1 - kt);
+        if (later >= S - 2) {
+            wait_vm<(S - 2) * G>();
+        } else if constexpr (S > 2) {
+            if (later == 0) wait_vm<0>();
+            else if (later == 1) wait_vm<G>();
+            else wait_vm<0>();
+        }
+        lds_barrier();
+        if (kt + S - 1 < KT)
+            issue(kt + S - 1);
+        if (kt == KT - 1 && (K % BKT) != 0) {
+            zero_tail(kt);
+            lds_barrier();
+        }
+        compute(kt % S);
+    }
+    lds_barrier();
+
+    // epilogue: per wave, one 16-row strip at a time through a private LDS
+    // scratch, then 16-byte stores of CPL contiguous columns per lane.
+    // acc[i][j][q] is wave row i*16 + 4*(lane/16) + q, column j*16 + lane%16.
+    constexpr int SLD = WTN + 4;
+    constexpr int CPL = WTN / 4;          // columns per lane on read-back
+    float *scr = reinterpret_cast<float *>(smem) + wv * 16 * SLD;
+    const int rr = lane >> 2;            // strip row read back by this lane
+    const int cg = (lane & 3) * CPL;     // its first column
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                scr[((lane >> 4) * 4 + q) * SLD + j * 16 + (lane & 15)] = acc[i][j][q];
+        const int r = m0 + wm * WTM + i * 16 + rr;
+        const int nb = n0 + wn * WTN + cg;
+        f32x4 v[CPL / 4];
+#pragma unroll
+        for (int c = 0; c < CPL / 4; ++c)
+            v[c] = *reinterpret_cast<const f32x4 *>(&scr[rr * SLD + cg + 4 * c]);
+        if (r < rows) {
             const int64_t srow = (int64_t)e * ceff + r;
             if (MODE == 0) {
-                unsigned short *dst = H_out + srow * Nout;
+                unsigned short *dst = H_out + srow * Nout + nb;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int n = n0 + wn * 64 + j * 16 + (lane & 15);
-                    if (n < Nout)
-                        dst[n] = f32_to_bf16_bits(fmaxf(acc[i][j][q], 0.f));
+                for (int h = 0; h < CPL / 8; ++h) {
+                    if (nb + 8 * h + 8 <= Nout) {
+                        u32x4 pk;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const float lo = fmaxf(v[2 * h + c / 2][(c % 2) * 2], 0.f);
+                            const float hi = fmaxf(v[2 * h + c / 2][(c % 2) * 2 + 1], 0.f);
+                            pk[c] = (unsigned)f32_to_bf16_bits(lo) |
+                                    ((unsigned)f32_to_bf16_bits(hi) << 16);
+                        }
+                        *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
+                    }
                 }
             } else {
-                float *dst = Y_out + (int64_t)slot_token[srow] * Nout;
+                float *dst = Y_out + (int64_t)slot_token[srow] * Nout + nb;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int n = n0 + wn * 64 + j * 16 + (lane & 15);
-                    if (n < Nout)
-                        dst[n] = acc[i][j][q];
-                }
+                for (int c = 0; c < CPL / 4; ++c)
+                    if (nb + 4 * c + 4 <= Nout)
+                        *reinterpret_cast<f32x4 *>(dst + 4 * c) = v[c];
             }
         }
     }
@@ -250,52 +347,79 @@ __global__ __launch_bounds__(256) void experts_f32_kernel(
 
 }  // namespace
 
+namespace {
+
+// Tile shapes: 256x256 with 8 waves (128x64 each, one workgroup per CU) for
+// experts with many rows; 128x128 with 4 waves (64x64 each, two workgroups
+// per CU, loads staged two K-tiles ahead) otherwise.
+enum class Tile { k128, k256 };
+
+Tile pick_tile(int64_t rows_per_expert, int64_t Nout, int E) {
+    const int64_t t256 = (int64_t)E * ((rows_per_expert + 255) / 256) * ((Nout + 255) / 256);
+    if (rows_per_expert >= 512 && t256 >= 256)
+        return Tile::k256;
+    return Tile::k128;
+}
+
+template <int MODE>
+hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W, int64_t K,
+                       int64_t Nout, int E, int k, int64_t ceff, const int32_t *used,
+                       const int32_t *slot_token, const int32_t *tiles, unsigned short *H,
+                       float *Y, hipStream_t s) {
+    if (t == Tile::k256) {
+        const int64_t grid = (E * ((ceff + 255) / 256) * ((Nout + 255) / 256) + kXcds - 1) /
+                             kXcds * kXcds;
+        hipLaunchKernelGGL((expert_gemm_kernel<256, 256, 2, 4, 64, 2, MODE>), dim3((unsigned)grid),
+                           dim3(512), 0, s, A, W, (int)K, (int)Nout, E, k, (int)ceff, used,
+                           slot_token, tiles + E + 1, H, Y);
+    } else {
+        const int64_t grid = (E * ((ceff + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) /
+                             kXcds * kXcds;
+        hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, 64, 2, MODE>), dim3((unsigned)grid),
+                           dim3(256), 0, s, A, W, (int)K, (int)Nout, E, k, (int)ceff, used,
+                           slot_token, tiles, H, Y);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t d,
                             int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                             const int32_t *slot_token, const int32_t *tiles, void *H,
-                            hipStream_t s) {
+                            int64_t rows_per_expert, hipStream_t s) {
     if (ceff == 0)
         return hipSuccess;
-    if (bf16) {
-        const int64_t mt_max = (ceff + BM - 1) / BM;
-        const int64_t nt = (d_ff + BN - 1) / BN;
-        const int64_t grid = (E * mt_max * nt + kXcds - 1) / kXcds * kXcds;
-        hipLaunchKernelGGL(experts_bf16_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                           static_cast<const unsigned short *>(x),
-                           static_cast<const unsigned short *>(w_up), (int)d, (int)d_ff, E, k,
-                           (int)ceff, used, slot_token, tiles,
-                           static_cast<unsigned short *>(H), (float *)nullptr);
-    } else {
-        hipLaunchKernelGGL(experts_f32_kernel<0>,
-                           dim3((unsigned)((d_ff + 63) / 64), (unsigned)((ceff + 63) / 64), E),
-                           dim3(256), 0, s, static_cast<const float *>(x),
-                           static_cast<const float *>(w_up), (int)d, (int)d_ff, k, (int)ceff,
-                           used, slot_token, static_cast<float *>(H), (float *)nullptr);
-    }
+    if (bf16)
+        return launch_gemm<0>(pick_tile(rows_per_expert, d_ff, E),
+                              static_cast<const unsigned short *>(x),
+                              static_cast<const unsigned short *>(w_up), d, d_ff, E, k, ceff,
+                              used, slot_token, tiles, static_cast<unsigned short *>(H), nullptr,
+                              s);
+    hipLaunchKernelGGL(experts_f32_kernel<0>,
+                       dim3((unsigned)((d_ff + 63) / 64), (unsigned)((ceff + 63) / 64), E),
+                       dim3(256), 0, s, static_cast<const float *>(x),
+                       static_cast<const float *>(w_up), (int)d, (int)d_ff, k, (int)ceff, used,
+                       slot_token, static_cast<float *>(H), (float *)nullptr);
     return hipGetLastError();
 }
 
 hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int64_t d,
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, float *Y,
-                              hipStream_t s) {
+                              int64_t rows_per_expert, hipStream_t s) {
     if (ceff == 0)
         return hipSuccess;
-    if (bf16) {
-        const int64_t mt_max = (ceff + BM - 1) / BM;
-        const int64_t nt = (d + BN - 1) / BN;
-        const int64_t grid = (E * mt_max * nt + kXcds - 1) / kXcds * kXcds;
-        hipLaunchKernelGGL(experts_bf16_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                           static_cast<const unsigned short *>(H),
-                           static_cast<const unsigned short *>(w_down), (int)d_ff, (int)d, E, k,
-                           (int)ceff, used, slot_token, tiles, (unsigned short *)nullptr, Y);
-    } else {
-        hipLaunchKernelGGL(experts_f32_kernel<1>,
-                           dim3((unsigned)((d + 63) / 64), (unsigned)((ceff + 63) / 64), E),
-                           dim3(256), 0, s, static_cast<const float *>(H),
-                           static_cast<const float *>(w_down), (int)d_ff, (int)d, k, (int)ceff,
-                           used, slot_token, (float *)nullptr, Y);
-    }
+    if (bf16)
+        return launch_gemm<1>(pick_tile(rows_per_expert, d, E),
+                              static_cast<const unsigned short *>(H),
+                              static_cast<const unsigned short *>(w_down), d_ff, d, E, k, ceff,
+                              used, slot_token, tiles, nullptr, Y, s);
+    hipLaunchKernelGGL(experts_f32_kernel<1>,
+                       dim3((unsigned)((d + 63) / 64), (unsigned)((ceff + 63) / 64), E),
+                       dim3(256), 0, s, static_cast<const float *>(H),
+                       static_cast<const float *>(w_down), (int)d_ff, (int)d, k, (int)ceff, used,
+                       slot_token, (float *)nullptr, Y);
     return hipGetLastError();
 }
 

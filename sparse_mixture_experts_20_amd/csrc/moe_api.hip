@@ -90,6 +90,12 @@ bool act_rows(const moe_tensor *t, int64_t &N, int64_t &d) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Expected kept rows per expert: min(C, ceil(N*k/E)).
+int64_t rows_per_expert(int64_t N, int k, int64_t E, int64_t ceff) {
+    const int64_t avg = (N * k + E - 1) / E;
+    return avg < ceff ? avg : ceff;
+}
+
 #define MOE_TRY(expr)                         \
     do {                                      \
         hipError_t e_ = (expr);               \
@@ -250,6 +256,7 @@ int moe_expert_up(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t ca
         return MOE_ERR_ALIGN;
     return hip_status(moe::launch_expert_up(bf16, x->data, W_up->data, d, d_ff, (int)E, k,
                                             m.ceff, used, slot_token, tiles, H,
+                                            rows_per_expert(N, k, E, m.ceff),
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -278,6 +285,7 @@ int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity
         return MOE_ERR_ALIGN;
     return hip_status(moe::launch_expert_down(bf16, H, W_down->data, d, d_ff, (int)E, k, m.ceff,
                                               used, slot_token, tiles, Y,
+                                              rows_per_expert(N, k, E, m.ceff),
                                               static_cast<hipStream_t>(stream)));
 }
 
@@ -396,10 +404,11 @@ int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *no
         return rc;
     MOE_TRY(moe::launch_dispatch(idx, N, (int)E, k, m.ceff, slot, used, slot_token, tiles, s));
     const bool bf16 = x->dtype == MOE_BF16;
+    const int64_t rpe = rows_per_expert(N, k, E, m.ceff);
     MOE_TRY(moe::launch_expert_up(bf16, x->data, W_up->data, d, d_ff, (int)E, k, m.ceff, used,
-                                  slot_token, tiles, H, s));
+                                  slot_token, tiles, H, rpe, s));
     MOE_TRY(moe::launch_expert_down(bf16, H, W_down->data, d, d_ff, (int)E, k, m.ceff, used,
-                                    slot_token, tiles, Y, s));
+                                    slot_token, tiles, Y, rpe, s));
     MOE_TRY(moe::launch_combine(Y, gate, slot, N, d, k, out->data, out->dtype, s));
     return MOE_OK;
 }

@@ -48,9 +48,9 @@ def test_dispatch_matches_oracle(torch_mod, N, E, k, C, seed):
         np.testing.assert_array_equal(ref_slot[t, j], np.arange(ref_used[e]))
     tl = G.to_np(tiles)
     c128 = np.concatenate([[0], np.cumsum((ref_used + 127) // 128)])
-    c64 = np.concatenate([[0], np.cumsum((ref_used + 63) // 64)])
+    c256 = np.concatenate([[0], np.cumsum((ref_used + 255) // 256)])
     np.testing.assert_array_equal(tl[:E + 1], c128)
-    np.testing.assert_array_equal(tl[E + 1:], c64)
+    np.testing.assert_array_equal(tl[E + 1:], c256)
     assert st.shape == (E, max(ceff, 1))
 
 

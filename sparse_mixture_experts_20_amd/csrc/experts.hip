@@ -171,25 +171,35 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void expert_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](int st) {
+    // Operand fragments of K-step ks (32 wide) of stage st; the next step's
+    // fragments are read before the current step's MFMAs are issued.
+    constexpr int KS = BKT / 32;
+    auto read_frags = [&](int st, int ks, bf16x8 (&af)[FM], bf16x8 (&bfr)[FN]) {
         const char *As = smem + st * STAGE;
         const char *Bs = As + BM * RB;
+        const int c = ks * 4 + (lane >> 4);
 #pragma unroll
-        for (int ks = 0; ks < BKT; ks += 32) {
-            const int c = ks / 8 + (lane >> 4);
-            bf16x8 af[FM], bfr[FN];
+        for (int i = 0; i < FM; ++i)
+            af[i] = *reinterpret_cast<const bf16x8 *>(As + (ra0 + i * 16) * RB + ((c ^ xa) << 4));
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8 *>(As + (ra0 + i * 16) * RB + ((c ^ xa) << 4));
+        for (int j = 0; j < FN; ++j)
+            bfr[j] = *reinterpret_cast<const bf16x8 *>(Bs + (rb0 + j * 16) * RB + ((c ^ xb) << 4));
+    };
+    auto mma = [&](const bf16x8 (&af)[FM], const bf16x8 (&bfr)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8 *>(Bs + (rb0 + j * 16) * RB + ((c ^ xb) << 4));
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+    auto compute = [&](int st) {
+        bf16x8 af[2][FM], bfr[2][FN];
+        read_frags(st, 0, af[0], bfr[0]);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j],
-                                                                       0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS)
+                read_frags(st, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+            mma(af[ks & 1], bfr[ks & 1]);
         }
     };
     // zero the chunks of the last K-tile that lie past K (both operands)

@@ -33,14 +33,16 @@ __device__ __forceinline__ void split3(float w, unsigned short &hi, unsigned sho
     lo = f32_to_bf16_bits(r2);                      // exact
 }
 
-// Top-k of one token's scores held across the wave (lane l holds experts
-// l, l+64, ...) and the softmax of the kept scores. Every lane returns with
-// the same selection; lanes j < k write choice j.
-template <int Q>
-__device__ __forceinline__ void topk_softmax_wave(const float (&v)[Q], int E, int k, int64_t t,
-                                                  int32_t *__restrict__ idx_out,
-                                                  float *__restrict__ gate_out) {
+// Top-k of one token's scores held by a group of G lanes (lane g of the
+// group holds experts g, g+G, ...; a wave ranks 64/G tokens at once) and the
+// softmax of the kept scores. Every lane of a group ends with the same
+// selection; lanes j < k of the group write choice j.
+template <int G, int Q>
+__device__ __forceinline__ void topk_softmax_group(const float (&v)[Q], int E, int k, int64_t t,
+                                                   bool active, int32_t *__restrict__ idx_out,
+                                                   float *__restrict__ gate_out) {
     const int lane = __lane_id();
+    const int lg = lane % G, gbase = lane - lg;
     unsigned taken = 0;
     float my_v = -INFINITY, v0 = -INFINITY;
     int my_e = 0;
@@ -49,7 +51,7 @@ __device__ __forceinline__ void topk_softmax_wave(const float (&v)[Q], int E, in
         int be = INT_MAX;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            const int e = lane + 64 * q;
+            const int e = lg + G * q;
             if (e < E && !((taken >> q) & 1u)) {
                 if (v[q] > bv || (v[q] == bv && e < be)) {
                     bv = v[q];
@@ -57,9 +59,9 @@ __device__ __forceinline__ void topk_softmax_wave(const float (&v)[Q], int E, in
                 }
             }
         }
-        // wave arg-max under the total order (score desc, id asc)
+        // group arg-max under the total order (score desc, id asc)
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
+        for (int off = G / 2; off >= 1; off >>= 1) {
             const float ov = __shfl_xor(bv, off);
             const int oe = __shfl_xor(be, off);
             if (ov > bv || (ov == bv && oe < be)) {
@@ -67,22 +69,22 @@ __device__ __forceinline__ void topk_softmax_wave(const float (&v)[Q], int E, in
                 be = oe;
             }
         }
-        if ((be & 63) == lane)
-            taken |= 1u << (be >> 6);
-        if (lane == j) {
+        if ((be % G) == lg)
+            taken |= 1u << (be / G);
+        if (lg == j) {
             my_v = bv;
             my_e = be;
         }
         if (j == 0)
             v0 = bv;
     }
-    const float ex = lane < k ? expf(my_v - v0) : 0.f;
+    const float ex = lg < k ? expf(my_v - v0) : 0.f;
     float den = 0.f;
-    for (int j = 0; j < k; ++j)   // choice order, identical on every lane
-        den += __shfl(ex, j);
-    if (lane < k) {
-        idx_out[t * k + lane] = my_e;
-        gate_out[t * k + lane] = ex / den;
+    for (int j = 0; j < k; ++j)   // choice order, identical on every lane of the group
+        den += __shfl(ex, gbase + j);
+    if (active && lg < k) {
+        idx_out[t * k + lg] = my_e;
+        gate_out[t * k + lg] = ex / den;
     }
 }
 
@@ -95,7 +97,6 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     const float *__restrict__ noise, int N, int d, int E, int k,
     int32_t *__restrict__ idx_out, float *__restrict__ gate_out) {
     constexpr int EP = NT * 16;
-    constexpr int Q = (EP + 63) / 64;
     __shared__ float red[kWaves * kTokTile * EP];
 
     const int lane = threadIdx.x & 63;
@@ -112,35 +113,68 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     for (int nt = 0; nt < NT; ++nt)
         acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Ranking layout: groups of G lanes rank one token each, 64/G tokens per
+    // pass, TPW/TPP passes for the 4 tokens 4w .. 4w+3 this wave ranks. Their
+    // noise rows are loaded up front, overlapping the score product.
+    constexpr int TPW = kTokTile / kWaves;
+    constexpr int G = EP <= 16 ? 16 : (EP <= 32 ? 32 : 64);
+    constexpr int QG = (EP + G - 1) / G;   // scores per lane
+    constexpr int TPP = 64 / G;             // tokens per pass
+    constexpr int PASSES = TPW / TPP;
+    const int lg = lane % G;
+    float nz[PASSES][QG];
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+        const int64_t t = t0 + w * TPW + ps * TPP + lane / G;
+#pragma unroll
+        for (int q = 0; q < QG; ++q) {
+            const int e = lg + G * q;
+            nz[ps][q] = (noise && t < N && e < E) ? noise[t * E + e] : 0.f;
+        }
+    }
+    // K-chunks are processed in batches of U: all loads of a batch are issued
+    // before any of its MFMAs (from clamped, always valid addresses; chunks
+    // past d or experts past E are masked to zero afterwards), so a wave
+    // waits for memory once per batch rather than once per chunk.
+    constexpr int U = NT >= 8 ? 1 : 8 / NT;
     const int nchunks = (d + 31) / 32;
-    for (int c = w; c < nchunks; c += kWaves) {
-        const int kof = c * 32 + kg * 8;
-        const bool k_ok = kof < d;   // d % 8 == 0: a group is all in or all out
-        u32x4 xa = {0u, 0u, 0u, 0u};
-        if (tok_ok && k_ok)
-            xa = *reinterpret_cast<const u32x4 *>(xrow + kof);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, xa);
+    for (int c0 = w; c0 < nchunks; c0 += kWaves * U) {
+        u32x4 xa[U];
+        f32x4 w0[U][NT], w1[U][NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int e = nt * 16 + row;
-            f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
-            if (e < E && k_ok) {
-                const float *wp = wg + (int64_t)e * d + kof;
-                w0 = *reinterpret_cast<const f32x4 *>(wp);
-                w1 = *reinterpret_cast<const f32x4 *>(wp + 4);
-            }
-            u16x8 hi, mid, lo;
+        for (int u = 0; u < U; ++u) {
+            const int kof = (c0 + u * kWaves) * 32 + kg * 8;
+            const int kc = kof < d ? kof : 0;   // d % 8 == 0: a group is all in or all out
+            xa[u] = *reinterpret_cast<const u32x4 *>(xrow + kc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                unsigned short h, m, l;
-                split3(w0[i], h, m, l);
-                hi[i] = h; mid[i] = m; lo[i] = l;
-                split3(w1[i], h, m, l);
-                hi[i + 4] = h; mid[i + 4] = m; lo[i + 4] = l;
+            for (int nt = 0; nt < NT; ++nt) {
+                const int e = nt * 16 + row;
+                const float *wp = wg + (int64_t)(e < E ? e : 0) * d + kc;
+                w0[u][nt] = *reinterpret_cast<const f32x4 *>(wp);
+                w1[u][nt] = *reinterpret_cast<const f32x4 *>(wp + 4);
             }
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, hi), acc[nt], 0, 0, 0);
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, mid), acc[nt], 0, 0, 0);
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, lo), acc[nt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool k_ok = (c0 + u * kWaves) * 32 + kg * 8 < d;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const bf16x8 a = __builtin_bit_cast(bf16x8, (tok_ok && k_ok) ? xa[u] : z);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const bool w_ok = k_ok && (nt * 16 + row < E);
+                u16x8 hi, mid, lo;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    unsigned short h, m, l;
+                    split3(w_ok ? w0[u][nt][i] : 0.f, h, m, l);
+                    hi[i] = h; mid[i] = m; lo[i] = l;
+                    split3(w_ok ? w1[u][nt][i] : 0.f, h, m, l);
+                    hi[i + 4] = h; mid[i + 4] = m; lo[i + 4] = l;
+                }
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, hi), acc[nt], 0, 0, 0);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, mid), acc[nt], 0, 0, 0);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, lo), acc[nt], 0, 0, 0);
+            }
         }
     }
     // acc[nt][i] holds the partial score of token 4*kg+i for expert nt*16+row
@@ -151,16 +185,14 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
             red[(w * kTokTile + 4 * kg + i) * EP + nt * 16 + row] = acc[nt][i];
     __syncthreads();
 
-    // wave w ranks tokens 4w .. 4w+3 of the tile
-    for (int tt = 0; tt < kTokTile / kWaves; ++tt) {
-        const int m = w * (kTokTile / kWaves) + tt;
-        const int64_t t = t0 + m;
-        if (t >= N)
-            break;
-        float v[Q];
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int e = lane + 64 * q;
+    for (int ps = 0; ps < PASSES; ++ps) {
+        const int m = w * TPW + ps * TPP + lane / G;
+        const int64_t t = t0 + m;
+        float v[QG];
+#pragma unroll
+        for (int q = 0; q < QG; ++q) {
+            const int e = lg + G * q;
             float s = -INFINITY;
             if (e < E) {
                 s = red[(0 * kTokTile + m) * EP + e];
@@ -168,13 +200,13 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
                 for (int ww = 1; ww < kWaves; ++ww)
                     s += red[(ww * kTokTile + m) * EP + e];
                 if (noise)
-                    s += noise[t * E + e];
+                    s += nz[ps][q];
                 if (s != s)
                     s = -INFINITY;   // a NaN score never outranks a number
             }
             v[q] = s;
         }
-        topk_softmax_wave<Q>(v, E, k, t, idx_out, gate_out);
+        topk_softmax_group<G, QG>(v, E, k, t, t < N, idx_out, gate_out);
     }
 }
 
@@ -210,7 +242,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
             if (e == lane + 64 * q)
                 v[q] = p;
     }
-    topk_softmax_wave<Q>(v, E, k, t, idx_out, gate_out);
+    topk_softmax_group<64, Q>(v, E, k, t, true, idx_out, gate_out);
 }
 
 template <int NT>

@@ -174,9 +174,10 @@ def main():
                               B.desc(out))
     s_ = B._stream()
     p = B._ptr
+    rws = B.alloc_workspace(B.router_workspace_size(wl.N, wl.d, wl.E, x.dtype))
     stages = {
         "router": lambda: L.moe_router(r(dx), r(dg), r(dn) if dn else None, wl.k, p(idx),
-                                       p(gate), s_),
+                                       p(gate), p(rws), rws.numel(), s_),
         "dispatch": lambda: L.moe_dispatch(wl.N, wl.E, wl.k, C, p(idx), p(slot), p(usedt),
                                            p(slot_token), p(tiles), s_),
         "expert_up": lambda: L.moe_expert_up(r(dx), r(du), wl.k, C, p(usedt), p(slot_token),

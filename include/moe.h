@@ -139,9 +139,16 @@ const char *moe_error_string(int code);
 /* Router (page 1 STEP 2-6; slides 11-13): fp32 scores s = W_g x + noise,
  * top-k in descending order (equal scores: lower expert id first), softmax
  * over the k kept scores. Writes topk_idx [N, k] int32 and topk_gate [N, k]
- * fp32 (device). x, W_g, noise as in moe_forward. */
+ * fp32 (device). x, W_g, noise as in moe_forward. workspace: device scratch
+ * of moe_router_workspace_size() bytes, 256-byte aligned (may be NULL when
+ * that size is 0). */
 int moe_router(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
-               int k, int32_t *topk_idx, float *topk_gate, void *stream);
+               int k, int32_t *topk_idx, float *topk_gate, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/* Bytes of router scratch for N tokens of width d and E experts (0 on invalid
+ * sizes or when the dtype needs none). */
+size_t moe_router_workspace_size(int64_t N, int64_t d, int64_t E, int32_t dtype);
 
 /* Capacity-limited dispatch plan (slides 14-29). From topk_idx [N, k] and the
  * capacity C (moe_capacity), writes:

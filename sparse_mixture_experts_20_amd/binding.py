@@ -21,8 +21,8 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK = 256, 16
 
 #: every function the header declares
 EXPORTS = ("moe_forward", "moe_workspace_size", "moe_capacity", "moe_error_string",
-           "moe_router", "moe_dispatch", "moe_experts", "moe_expert_up", "moe_expert_down",
-           "moe_combine")
+           "moe_router", "moe_router_workspace_size", "moe_dispatch", "moe_experts",
+           "moe_expert_up", "moe_expert_down", "moe_combine")
 
 
 class MoeTensor(ctypes.Structure):
@@ -68,8 +68,10 @@ def lib():
         L.moe_capacity.restype = _i64
         L.moe_error_string.argtypes = [ctypes.c_int]
         L.moe_error_string.restype = ctypes.c_char_p
-        L.moe_router.argtypes = [_T, _T, _T, ctypes.c_int, _vp, _vp, _vp]
+        L.moe_router.argtypes = [_T, _T, _T, ctypes.c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_router.restype = ctypes.c_int
+        L.moe_router_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.c_int32]
+        L.moe_router_workspace_size.restype = ctypes.c_size_t
         L.moe_dispatch.argtypes = [_i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_dispatch.restype = ctypes.c_int
         L.moe_experts.argtypes = [_T, _T, _T, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -212,15 +214,23 @@ class Forward:
         return self.out
 
 
-def router(x, W_g, noise, k, idx=None, gate=None, stream=None):
+def router_workspace_size(N: int, d: int, E: int, dtype: torch.dtype) -> int:
+    code = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(lib().moe_router_workspace_size(N, d, E, code))
+
+
+def router(x, W_g, noise, k, idx=None, gate=None, workspace=None, stream=None):
     N = x.numel() // x.shape[-1]
     if idx is None:
         idx = torch.empty((N, k), dtype=torch.int32, device=x.device)
     if gate is None:
         gate = torch.empty((N, k), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(router_workspace_size(N, x.shape[-1], W_g.shape[0], x.dtype),
+                                    x.device)
     dx, dg, dn = desc(x), desc(W_g), desc(noise)
     _check(lib().moe_router(_ref(dx), _ref(dg), _ref(dn), k, _ptr(idx), _ptr(gate),
-                            _stream(stream)), "moe_router")
+                            _ptr(workspace), workspace.numel(), _stream(stream)), "moe_router")
     return idx, gate
 
 

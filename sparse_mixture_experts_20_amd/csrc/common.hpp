@@ -10,9 +10,11 @@ namespace moe {
 constexpr int kWave = 64;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxQ = kMaxExperts / kWave;   // router scores per lane
+constexpr int kFusedMaxExperts = 32;          // larger routers use the GEMM path
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -43,9 +45,11 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // ---------------------------------------------------------------------------
 namespace moe {
 
+// ws: router_workspace_bytes(N, d, E) bytes of device scratch (256-aligned).
+size_t router_workspace_bytes(int64_t N, int64_t d, int E);
 hipError_t launch_router_bf16(const void *x, const float *wg, const float *noise,
                               int64_t N, int64_t d, int E, int k,
-                              int32_t *idx, float *gate, hipStream_t s);
+                              int32_t *idx, float *gate, void *ws, hipStream_t s);
 hipError_t launch_router_f32(const float *x, const float *wg, const float *noise,
                              int64_t N, int64_t d, int E, int k,
                              int32_t *idx, float *gate, hipStream_t s);
@@ -67,6 +71,10 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, float *Y,
                               int64_t rows_per_expert, hipStream_t s);
+
+// Y[rows, Nout] (fp32) = A[rows, K] * W[Nout, K]^T, bf16 operands.
+hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, int64_t K,
+                                  int64_t Nout, float *Y, hipStream_t s);
 
 hipError_t launch_combine(const float *Y, const float *gate, const int32_t *slot,
                           int64_t N, int64_t d, int k, void *out, int out_dtype,

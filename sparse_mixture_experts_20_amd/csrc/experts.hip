@@ -70,8 +70,14 @@ __device__ __forceinline__ void dma16(unsigned lds_base, const void *g) {
 // is stored at position c ^ ((r / RPB) % CPR) (RPB rows share one 256-byte
 // bank row), so the 16 lanes that read 16 consecutive rows at one chunk hit
 // 16 distinct bank groups.
+// Two waves per SIMD (the LDS budget allows no more), so the compiler may use
+// up to 256 registers per lane and schedule for latency rather than occupancy.
+// MODE 0: up product (gathered token rows, ReLU, bf16 H); 1: down product
+// (fp32 rows scattered to their assignment); 2: plain product of ceff rows of
+// A into fp32 rows of Y (no gather, no schedule table).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BKT, int S, int MODE>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void expert_gemm_kernel(
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void expert_gemm_kernel(
     const unsigned short *__restrict__ A_src, const unsigned short *__restrict__ W, int K,
     int Nout, int E, int k, int ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void expert_gemm_kernel(
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int NTHR = NW * 64;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;   // wave tile
-    constexpr int FM = WTM / 16, FN = WTN / 16;              // MFMA tiles per wave
+    constexpr int FM = WTM / 16, FN = WTN / 16;              // 16x16 MFMA tiles per wave
     constexpr int RB = BKT * 2;                              // bytes per K-tile row
     constexpr int CPR = BKT / 8;                             // 16-byte chunks per row
     constexpr int RPB = 256 / RB;                            // rows per 256-byte bank row
@@ -89,36 +95,49 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void expert_gemm_kernel(
     constexpr int STAGE = (BM + BN) * RB;                    // bytes per stage
     static_assert(BKT % 32 == 0 && S >= 2, "K-step is a multiple of one MFMA K");
     static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile/waves mismatch");
-    static_assert(WTN % 32 == 0, "epilogue splits a wave row into 4 lanes x 8k columns");
+    static_assert(WTM % 16 == 0 && WTN % 32 == 0, "16x16 MFMA tiles; 4 lanes x 8k columns per row");
     static_assert(NW * 16 * (WTN + 4) * 4 <= S * STAGE, "epilogue scratch");
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
     __shared__ int s_mt[kMaxExperts + 1];
 
     const int tid = threadIdx.x;
     const int NT = (Nout + BN - 1) / BN;
-    for (int i = tid; i <= E; i += NTHR)
-        s_mt[i] = mt_off[i];
-    __syncthreads();
-    const int T = s_mt[E] * NT;
-    const int T8 = (T + kXcds - 1) / kXcds * kXcds;
+    int T, e, mte, local, rows;
     const int b = blockIdx.x;
+    if constexpr (MODE == 2) {
+        // plain product over ceff rows, one "expert": no schedule table
+        mte = (ceff + BM - 1) / BM;
+        T = mte * NT;
+    } else {
+        for (int i = tid; i <= E; i += NTHR)
+            s_mt[i] = mt_off[i];
+        __syncthreads();
+        T = s_mt[E] * NT;
+    }
+    const int T8 = (T + kXcds - 1) / kXcds * kXcds;
     if (b >= T8)
         return;
     const int L = (b % kXcds) * (T8 / kXcds) + b / kXcds;
     if (L >= T)
         return;
-    // expert owning tile L: the last e with s_mt[e] * NT <= L
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_mt[mid] * NT <= L) lo = mid; else hi = mid - 1;
+    if constexpr (MODE == 2) {
+        e = 0;
+        local = L;
+        rows = ceff;
+    } else {
+        // expert owning tile L: the last e with s_mt[e] * NT <= L
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_mt[mid] * NT <= L) lo = mid; else hi = mid - 1;
+        }
+        e = lo;
+        mte = s_mt[e + 1] - s_mt[e];
+        local = L - s_mt[e] * NT;
+        rows = used[e];
     }
-    const int e = lo;
-    const int mte = s_mt[e + 1] - s_mt[e];
-    const int local = L - s_mt[e] * NT;
     const int m0 = (local % mte) * BM;
     const int n0 = (local / mte) * BN;
-    const int rows = used[e];
 
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -279,7 +298,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void expert_gemm_kernel(
                     }
                 }
             } else {
-                float *dst = Y_out + (int64_t)slot_token[srow] * Nout + nb;
+                const int64_t orow = MODE == 1 ? (int64_t)slot_token[srow] : (int64_t)r;
+                float *dst = Y_out + orow * Nout + nb;
 #pragma unroll
                 for (int c = 0; c < CPL / 4; ++c)
                     if (nb + 4 * c + 4 <= Nout)
@@ -393,6 +413,19 @@ hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W,
 }
 
 }  // namespace
+
+hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, int64_t K,
+                                  int64_t Nout, float *Y, hipStream_t s) {
+    if (rows == 0)
+        return hipSuccess;
+    const int64_t grid = (((rows + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, 64, 2, 2>), dim3((unsigned)grid),
+                       dim3(256), 0, s, static_cast<const unsigned short *>(A),
+                       static_cast<const unsigned short *>(W), (int)K, (int)Nout, 1, 1, (int)rows,
+                       (const int32_t *)nullptr, (const int32_t *)nullptr,
+                       (const int32_t *)nullptr, (unsigned short *)nullptr, Y);
+    return hipGetLastError();
+}
 
 hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t d,
                             int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,

@@ -36,8 +36,13 @@ struct Dims {
 
 // Workspace regions (byte offsets from the base).
 struct Layout {
-    size_t idx, gate, slot, used, tiles, slot_token, H, Y, total;
+    size_t idx, gate, slot, used, tiles, slot_token, H, Y, router, total;
 };
+
+// Router scratch: the bf16 split of W_g (and partial scores for many experts).
+size_t router_bytes(int64_t N, int64_t d, int64_t E, int32_t dtype) {
+    return dtype == MOE_BF16 ? align_up(moe::router_workspace_bytes(N, d, (int)E)) : 0;
+}
 
 Layout layout_of(const Dims &m) {
     Layout L;
@@ -51,6 +56,7 @@ Layout layout_of(const Dims &m) {
     L.slot_token = o; o += align_up((size_t)(m.E * m.ceff) * 4);
     L.H = o;          o += align_up((size_t)(m.E * m.ceff * m.d_ff) * dtype_size(m.dtype));
     L.Y = o;          o += align_up(nk * (size_t)m.d * 4);
+    L.router = o;     o += router_bytes(m.N, m.d, m.E, m.dtype);
     L.total = o;
     return L;
 }
@@ -105,11 +111,11 @@ int64_t rows_per_expert(int64_t N, int k, int64_t E, int64_t ceff) {
 
 int router_checked(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
                    int64_t N, int64_t d, int64_t E, int k, int32_t *idx, float *gate,
-                   hipStream_t s) {
+                   void *ws, hipStream_t s) {
     const float *nz = noise ? static_cast<const float *>(noise->data) : nullptr;
     if (x->dtype == MOE_BF16)
         return hip_status(moe::launch_router_bf16(x->data, static_cast<const float *>(W_g->data),
-                                                  nz, N, d, (int)E, k, idx, gate, s));
+                                                  nz, N, d, (int)E, k, idx, gate, ws, s));
     return hip_status(moe::launch_router_f32(static_cast<const float *>(x->data),
                                              static_cast<const float *>(W_g->data), nz, N, d,
                                              (int)E, k, idx, gate, s));
@@ -193,8 +199,15 @@ size_t moe_workspace_size(int64_t N, int64_t d, int64_t E, int64_t d_ff, int k,
     return layout_of(m).total;
 }
 
+size_t moe_router_workspace_size(int64_t N, int64_t d, int64_t E, int32_t dtype) {
+    if (!valid_dtype(dtype) || N < 0 || d <= 0 || E <= 0 || E > MOE_MAX_EXPERTS)
+        return 0;
+    return router_bytes(N, d, E, dtype);
+}
+
 int moe_router(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise, int k,
-               int32_t *topk_idx, float *topk_gate, void *stream) {
+               int32_t *topk_idx, float *topk_gate, void *workspace, size_t workspace_bytes,
+               void *stream) {
     int64_t N, d, E;
     int rc = check_router_args(x, W_g, noise, k, N, d, E);
     if (rc != MOE_OK)
@@ -203,7 +216,16 @@ int moe_router(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noi
         return MOE_OK;
     if (!topk_idx || !topk_gate)
         return MOE_ERR_NULL;
-    return router_checked(x, W_g, noise, N, d, E, k, topk_idx, topk_gate,
+    const size_t need = router_bytes(N, d, E, x->dtype);
+    if (need > 0) {
+        if (!workspace)
+            return MOE_ERR_NULL;
+        if (!aligned(workspace, kAlign))
+            return MOE_ERR_ALIGN;
+        if (workspace_bytes < need)
+            return MOE_ERR_WORKSPACE;
+    }
+    return router_checked(x, W_g, noise, N, d, E, k, topk_idx, topk_gate, workspace,
                           static_cast<hipStream_t>(stream));
 }
 
@@ -399,7 +421,7 @@ int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *no
     float *Y = reinterpret_cast<float *>(ws + L.Y);
     stats->capacity = m.C;
 
-    rc = router_checked(x, W_g, noise, N, d, E, k, idx, gate, s);
+    rc = router_checked(x, W_g, noise, N, d, E, k, idx, gate, ws + L.router, s);
     if (rc != MOE_OK)
         return rc;
     MOE_TRY(moe::launch_dispatch(idx, N, (int)E, k, m.ceff, slot, used, slot_token, tiles, s));

@@ -13,6 +13,12 @@
 // significand), and a bf16 activation times a bf16 term is exact in the fp32
 // accumulator. Three bf16 MFMAs per K-step therefore give an fp32-accumulated
 // dot product of the exact inputs, at a fraction of the cost of fp32 MFMA.
+// The split is done once per call into the workspace (rows e, Ep+e, 2Ep+e of
+// a [3*Ep, d] bf16 matrix hold hi, mid, lo of expert e; Ep = E rounded up to
+// 16, padding rows zero). Up to 32 experts one fused kernel computes the
+// scores of 16 tokens in registers and ranks them; with more experts the
+// score product is a plain GEMM on the expert-product kernel ([N, 3*Ep]
+// fp32 partial scores) followed by a ranking kernel.
 #include "common.hpp"
 
 #include <float.h>
@@ -88,12 +94,72 @@ __device__ __forceinline__ void topk_softmax_group(const float (&v)[Q], int E, i
     }
 }
 
+// W_g [E, d] fp32 -> Wsp [3*Ep, d] bf16 (hi, mid, lo blocks); 8 elements per thread.
+__global__ __launch_bounds__(256) void split_router_weights_kernel(const float *__restrict__ wg,
+                                                                   int E, int Ep, int d,
+                                                                   unsigned short *__restrict__ wsp) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // group of 8
+    const int64_t groups = (int64_t)Ep * (d / 8);
+    if (g >= groups)
+        return;
+    const int e = (int)(g / (d / 8));
+    const int i = (int)(g - (int64_t)e * (d / 8)) * 8;
+    f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
+    if (e < E) {
+        w0 = *reinterpret_cast<const f32x4 *>(wg + (int64_t)e * d + i);
+        w1 = *reinterpret_cast<const f32x4 *>(wg + (int64_t)e * d + i + 4);
+    }
+    u16x8 hi, mid, lo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        unsigned short h, m, l;
+        split3(w0[q], h, m, l);
+        hi[q] = h; mid[q] = m; lo[q] = l;
+        split3(w1[q], h, m, l);
+        hi[q + 4] = h; mid[q + 4] = m; lo[q + 4] = l;
+    }
+    *reinterpret_cast<u16x8 *>(wsp + (int64_t)e * d + i) = hi;
+    *reinterpret_cast<u16x8 *>(wsp + ((int64_t)Ep + e) * d + i) = mid;
+    *reinterpret_cast<u16x8 *>(wsp + ((int64_t)2 * Ep + e) * d + i) = lo;
+}
+
+// Ranking of one token per G-lane group from precomputed partial scores
+// s3 [N, 3*Ep] (hi, mid, lo products, summed here in that order) plus noise.
+template <int G, int Q>
+__global__ __launch_bounds__(256) void rank_scores_kernel(const float *__restrict__ s3,
+                                                          const float *__restrict__ noise, int N,
+                                                          int E, int Ep, int k,
+                                                          int32_t *__restrict__ idx_out,
+                                                          float *__restrict__ gate_out) {
+    const int lane = threadIdx.x & 63;
+    const int lg = lane % G;
+    const int64_t t = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / G) + lane / G;
+    const bool active = t < N;
+    const int64_t tc = active ? t : 0;
+    float v[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int e = lg + G * q;
+        float sc = -INFINITY;
+        if (e < E) {
+            const float *r = s3 + tc * 3 * Ep;
+            sc = (r[e] + r[Ep + e]) + r[2 * Ep + e];
+            if (noise)
+                sc += noise[tc * E + e];
+            if (sc != sc)
+                sc = -INFINITY;
+        }
+        v[q] = sc;
+    }
+    topk_softmax_group<G, Q>(v, E, k, t, active, idx_out, gate_out);
+}
+
 // One block = 16 tokens; wave w accumulates K-chunks c = w, w+4, ... with
 // 16x16x32 bf16 MFMAs over NT tiles of 16 experts, then the four partial
 // score tiles are summed in wave order through LDS.
 template <int NT>
 __global__ __launch_bounds__(256) void router_bf16_kernel(
-    const unsigned short *__restrict__ x, const float *__restrict__ wg,
+    const unsigned short *__restrict__ x, const unsigned short *__restrict__ wsp,
     const float *__restrict__ noise, int N, int d, int E, int k,
     int32_t *__restrict__ idx_out, float *__restrict__ gate_out) {
     constexpr int EP = NT * 16;
@@ -134,25 +200,24 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     }
     // K-chunks are processed in batches of U: all loads of a batch are issued
     // before any of its MFMAs (from clamped, always valid addresses; chunks
-    // past d or experts past E are masked to zero afterwards), so a wave
-    // waits for memory once per batch rather than once per chunk.
-    constexpr int U = NT >= 8 ? 1 : 8 / NT;
+    // past d are masked to zero afterwards; padding experts have zero rows),
+    // so a wave waits for memory once per batch rather than once per chunk.
+    constexpr int U = NT >= 2 ? 4 : 8;
     const int nchunks = (d + 31) / 32;
     for (int c0 = w; c0 < nchunks; c0 += kWaves * U) {
         u32x4 xa[U];
-        f32x4 w0[U][NT], w1[U][NT];
+        u32x4 wp[U][NT][3];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int kof = (c0 + u * kWaves) * 32 + kg * 8;
             const int kc = kof < d ? kof : 0;   // d % 8 == 0: a group is all in or all out
             xa[u] = *reinterpret_cast<const u32x4 *>(xrow + kc);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int e = nt * 16 + row;
-                const float *wp = wg + (int64_t)(e < E ? e : 0) * d + kc;
-                w0[u][nt] = *reinterpret_cast<const f32x4 *>(wp);
-                w1[u][nt] = *reinterpret_cast<const f32x4 *>(wp + 4);
-            }
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int pc = 0; pc < 3; ++pc)
+                    wp[u][nt][pc] = *reinterpret_cast<const u32x4 *>(
+                        wsp + ((int64_t)pc * EP + nt * 16 + row) * d + kc);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -160,21 +225,11 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
             const u32x4 z = {0u, 0u, 0u, 0u};
             const bf16x8 a = __builtin_bit_cast(bf16x8, (tok_ok && k_ok) ? xa[u] : z);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const bool w_ok = k_ok && (nt * 16 + row < E);
-                u16x8 hi, mid, lo;
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    unsigned short h, m, l;
-                    split3(w_ok ? w0[u][nt][i] : 0.f, h, m, l);
-                    hi[i] = h; mid[i] = m; lo[i] = l;
-                    split3(w_ok ? w1[u][nt][i] : 0.f, h, m, l);
-                    hi[i + 4] = h; mid[i + 4] = m; lo[i + 4] = l;
-                }
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, hi), acc[nt], 0, 0, 0);
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, mid), acc[nt], 0, 0, 0);
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, lo), acc[nt], 0, 0, 0);
-            }
+                for (int pc = 0; pc < 3; ++pc)
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a, __builtin_bit_cast(bf16x8, wp[u][nt][pc]), acc[nt], 0, 0, 0);
         }
     }
     // acc[nt][i] holds the partial score of token 4*kg+i for expert nt*16+row
@@ -246,28 +301,60 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 }
 
 template <int NT>
-hipError_t launch_nt(const void *x, const float *wg, const float *noise, int64_t N, int64_t d,
-                     int E, int k, int32_t *idx, float *gate, hipStream_t s) {
+hipError_t launch_fused(const void *x, const unsigned short *wsp, const float *noise, int64_t N,
+                        int64_t d, int E, int k, int32_t *idx, float *gate, hipStream_t s) {
     const int blocks = (int)((N + kTokTile - 1) / kTokTile);
     hipLaunchKernelGGL(router_bf16_kernel<NT>, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const unsigned short *>(x), wg, noise, (int)N, (int)d, E, k,
+                       static_cast<const unsigned short *>(x), wsp, noise, (int)N, (int)d, E, k,
                        idx, gate);
+    return hipGetLastError();
+}
+
+template <int G, int Q>
+hipError_t launch_rank(const float *s3, const float *noise, int64_t N, int E, int Ep, int k,
+                       int32_t *idx, float *gate, hipStream_t s) {
+    const int64_t tokens_per_block = 4 * (64 / G);
+    const int blocks = (int)((N + tokens_per_block - 1) / tokens_per_block);
+    hipLaunchKernelGGL((rank_scores_kernel<G, Q>), dim3(blocks), dim3(256), 0, s, s3, noise,
+                       (int)N, E, Ep, k, idx, gate);
     return hipGetLastError();
 }
 
 }  // namespace
 
+int64_t router_padded_experts(int E) { return (E + 15) / 16 * 16; }
+
+size_t router_workspace_bytes(int64_t N, int64_t d, int E) {
+    const int64_t Ep = router_padded_experts(E);
+    size_t b = (size_t)(3 * Ep * d * 2 + 255) / 256 * 256;
+    if (Ep > kFusedMaxExperts)
+        b += (size_t)(N * 3 * Ep * 4 + 255) / 256 * 256;
+    return b;
+}
+
 hipError_t launch_router_bf16(const void *x, const float *wg, const float *noise, int64_t N,
-                              int64_t d, int E, int k, int32_t *idx, float *gate,
+                              int64_t d, int E, int k, int32_t *idx, float *gate, void *ws,
                               hipStream_t s) {
     if (N == 0)
         return hipSuccess;
-    const int nt = (E + 15) / 16;
-    if (nt <= 1) return launch_nt<1>(x, wg, noise, N, d, E, k, idx, gate, s);
-    if (nt <= 2) return launch_nt<2>(x, wg, noise, N, d, E, k, idx, gate, s);
-    if (nt <= 4) return launch_nt<4>(x, wg, noise, N, d, E, k, idx, gate, s);
-    if (nt <= 8) return launch_nt<8>(x, wg, noise, N, d, E, k, idx, gate, s);
-    return launch_nt<16>(x, wg, noise, N, d, E, k, idx, gate, s);
+    const int Ep = (int)router_padded_experts(E);
+    unsigned short *wsp = static_cast<unsigned short *>(ws);
+    const int64_t groups = (int64_t)Ep * (d / 8);
+    hipLaunchKernelGGL(split_router_weights_kernel, dim3((unsigned)((groups + 255) / 256)),
+                       dim3(256), 0, s, wg, E, Ep, (int)d, wsp);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    if (Ep <= 16) return launch_fused<1>(x, wsp, noise, N, d, E, k, idx, gate, s);
+    if (Ep <= 32) return launch_fused<2>(x, wsp, noise, N, d, E, k, idx, gate, s);
+    float *s3 = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                          (size_t)(3 * Ep * d * 2 + 255) / 256 * 256);
+    err = launch_plain_gemm_bf16(x, wsp, N, d, 3 * Ep, s3, s);
+    if (err != hipSuccess)
+        return err;
+    if (Ep <= 64) return launch_rank<64, 1>(s3, noise, N, E, Ep, k, idx, gate, s);
+    if (Ep <= 128) return launch_rank<64, 2>(s3, noise, N, E, Ep, k, idx, gate, s);
+    return launch_rank<64, 4>(s3, noise, N, E, Ep, k, idx, gate, s);
 }
 
 hipError_t launch_router_f32(const float *x, const float *wg, const float *noise, int64_t N,

@@ -54,6 +54,21 @@ def traffic_for(kernel, workload):
     return e.get("bytes_per_launch")
 
 
+def gemm_kernel_name(wl, C, mode):
+    """Name of the expert-GEMM instantiation the library launches for this
+    workload (mirrors the library's tile choice: 256x256 when experts hold
+    >= 512 rows on average and that gives >= 256 tiles or a wide product;
+    128x64 when 128x128 would give fewer than 384 tiles; else 128x128)."""
+    rpe = min(C, -(-wl.N * wl.k // wl.E))
+    nout = wl.d_ff if mode == 0 else wl.d
+    t256 = wl.E * -(-rpe // 256) * -(-nout // 256)
+    if rpe >= 512 and (t256 >= 256 or nout >= 2048):
+        return f"expert_gemm_kernel<256, 256, 2, 4, 64, 2, {mode}>"
+    if wl.E * -(-rpe // 128) * -(-nout // 128) < 384:
+        return f"expert_gemm_kernel<128, 64, 2, 2, 64, 2, {mode}>"
+    return f"expert_gemm_kernel<128, 128, 2, 2, 64, 2, {mode}>"
+
+
 def cpu_baseline(wl, target_s=15.0):
     """The oracle as it stands: routing and slots for all N tokens, expert FFN
     and combine for a seeded sample of S tokens sized for ~target_s of work."""
@@ -217,7 +232,7 @@ def main():
         f"combine {combine_gbps:.0f} GB/s")
 
     dom = "expert_up" if s["expert_up"] >= s["expert_down"] else "expert_down"
-    dom_kernel = ("experts_bf16_kernel<0>" if dom == "expert_up" else "experts_bf16_kernel<1>")
+    dom_kernel = gemm_kernel_name(wl, C, 0 if dom == "expert_up" else 1)
     achieved = gemm_flops / (s[dom] * 1e-3) / 1e12
     roofline = {
         "kernel": dom_kernel,

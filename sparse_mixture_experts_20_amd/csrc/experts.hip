@@ -379,15 +379,21 @@ __global__ __launch_bounds__(256) void experts_f32_kernel(
 
 namespace {
 
-// Tile shapes: 256x256 with 8 waves (128x64 each, one workgroup per CU) for
-// experts with many rows; 128x128 with 4 waves (64x64 each, two workgroups
-// per CU, loads staged two K-tiles ahead) otherwise.
-enum class Tile { k128, k256 };
+// Tile shapes (rows_per_expert = expected kept rows per expert):
+//  - 256x256, 8 waves of 128x64, one workgroup per CU: experts with >= 512
+//    rows when that still gives a full grid or the product is wide;
+//  - 128x64, 4 waves of 64x32: when 128x128 tiles would leave CUs idle
+//    (fewer than 384 tiles), trading operand reuse for parallelism;
+//  - 128x128, 4 waves of 64x64, two workgroups per CU: otherwise.
+enum class Tile { k128, k128x64, k256 };
 
 Tile pick_tile(int64_t rows_per_expert, int64_t Nout, int E) {
     const int64_t t256 = (int64_t)E * ((rows_per_expert + 255) / 256) * ((Nout + 255) / 256);
-    if (rows_per_expert >= 512 && t256 >= 256)
+    if (rows_per_expert >= 512 && (t256 >= 256 || Nout >= 2048))
         return Tile::k256;
+    const int64_t t128 = (int64_t)E * ((rows_per_expert + 127) / 128) * ((Nout + 127) / 128);
+    if (t128 < 384)
+        return Tile::k128x64;
     return Tile::k128;
 }
 
@@ -402,6 +408,12 @@ hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W,
         hipLaunchKernelGGL((expert_gemm_kernel<256, 256, 2, 4, 64, 2, MODE>), dim3((unsigned)grid),
                            dim3(512), 0, s, A, W, (int)K, (int)Nout, E, k, (int)ceff, used,
                            slot_token, tiles + E + 1, H, Y);
+    } else if (t == Tile::k128x64) {
+        const int64_t grid = (E * ((ceff + 127) / 128) * ((Nout + 63) / 64) + kXcds - 1) /
+                             kXcds * kXcds;
+        hipLaunchKernelGGL((expert_gemm_kernel<128, 64, 2, 2, 64, 2, MODE>), dim3((unsigned)grid),
+                           dim3(256), 0, s, A, W, (int)K, (int)Nout, E, k, (int)ceff, used,
+                           slot_token, tiles, H, Y);
     } else {
         const int64_t grid = (E * ((ceff + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) /
                              kXcds * kXcds;

@@ -13,12 +13,13 @@
 // significand), and a bf16 activation times a bf16 term is exact in the fp32
 // accumulator. Three bf16 MFMAs per K-step therefore give an fp32-accumulated
 // dot product of the exact inputs, at a fraction of the cost of fp32 MFMA.
-// The split is done once per call into the workspace (rows e, Ep+e, 2Ep+e of
-// a [3*Ep, d] bf16 matrix hold hi, mid, lo of expert e; Ep = E rounded up to
-// 16, padding rows zero). Up to 32 experts one fused kernel computes the
-// scores of 16 tokens in registers and ranks them; with more experts the
-// score product is a plain GEMM on the expert-product kernel ([N, 3*Ep]
-// fp32 partial scores) followed by a ranking kernel.
+// Up to 32 experts one fused kernel splits the weights in registers,
+// computes the scores of 16 tokens and ranks them. With more experts the
+// split is done once per call into the workspace (rows e, Ep+e, 2Ep+e of a
+// [3*Ep, d] bf16 matrix hold hi, mid, lo of expert e; Ep = E rounded up to
+// 16, padding rows zero), the score product is a plain GEMM on the
+// expert-product kernel ([N, 3*Ep] fp32 partial scores), and a ranking
+// kernel finishes.
 #include "common.hpp"
 
 #include <float.h>
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(256) void rank_scores_kernel(const float *__restric
 // score tiles are summed in wave order through LDS.
 template <int NT>
 __global__ __launch_bounds__(256) void router_bf16_kernel(
-    const unsigned short *__restrict__ x, const unsigned short *__restrict__ wsp,
+    const unsigned short *__restrict__ x, const float *__restrict__ wg,
     const float *__restrict__ noise, int N, int d, int E, int k,
     int32_t *__restrict__ idx_out, float *__restrict__ gate_out) {
     constexpr int EP = NT * 16;
@@ -200,24 +201,27 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     }
     // K-chunks are processed in batches of U: all loads of a batch are issued
     // before any of its MFMAs (from clamped, always valid addresses; chunks
-    // past d are masked to zero afterwards; padding experts have zero rows),
-    // so a wave waits for memory once per batch rather than once per chunk.
+    // past d or experts past E are masked to zero afterwards), so a wave
+    // waits for memory once per batch rather than once per chunk. With at
+    // most 32 experts the fp32 weights are split in registers (a few VALU
+    // operations per weight), which saves a separate split kernel.
     constexpr int U = NT >= 2 ? 4 : 8;
     const int nchunks = (d + 31) / 32;
     for (int c0 = w; c0 < nchunks; c0 += kWaves * U) {
         u32x4 xa[U];
-        u32x4 wp[U][NT][3];
+        f32x4 w0[U][NT], w1[U][NT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int kof = (c0 + u * kWaves) * 32 + kg * 8;
             const int kc = kof < d ? kof : 0;   // d % 8 == 0: a group is all in or all out
             xa[u] = *reinterpret_cast<const u32x4 *>(xrow + kc);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int pc = 0; pc < 3; ++pc)
-                    wp[u][nt][pc] = *reinterpret_cast<const u32x4 *>(
-                        wsp + ((int64_t)pc * EP + nt * 16 + row) * d + kc);
+            for (int nt = 0; nt < NT; ++nt) {
+                const int e = nt * 16 + row;
+                const float *wp = wg + (int64_t)(e < E ? e : 0) * d + kc;
+                w0[u][nt] = *reinterpret_cast<const f32x4 *>(wp);
+                w1[u][nt] = *reinterpret_cast<const f32x4 *>(wp + 4);
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -225,11 +229,21 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
             const u32x4 z = {0u, 0u, 0u, 0u};
             const bf16x8 a = __builtin_bit_cast(bf16x8, (tok_ok && k_ok) ? xa[u] : z);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt) {
+                const bool w_ok = k_ok && (nt * 16 + row < E);
+                u16x8 hi, mid, lo;
 #pragma unroll
-                for (int pc = 0; pc < 3; ++pc)
-                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        a, __builtin_bit_cast(bf16x8, wp[u][nt][pc]), acc[nt], 0, 0, 0);
+                for (int i = 0; i < 4; ++i) {
+                    unsigned short h, m, l;
+                    split3(w_ok ? w0[u][nt][i] : 0.f, h, m, l);
+                    hi[i] = h; mid[i] = m; lo[i] = l;
+                    split3(w_ok ? w1[u][nt][i] : 0.f, h, m, l);
+                    hi[i + 4] = h; mid[i + 4] = m; lo[i + 4] = l;
+                }
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, hi), acc[nt], 0, 0, 0);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, mid), acc[nt], 0, 0, 0);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, lo), acc[nt], 0, 0, 0);
+            }
         }
     }
     // acc[nt][i] holds the partial score of token 4*kg+i for expert nt*16+row
@@ -301,11 +315,11 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 }
 
 template <int NT>
-hipError_t launch_fused(const void *x, const unsigned short *wsp, const float *noise, int64_t N,
+hipError_t launch_fused(const void *x, const float *wg, const float *noise, int64_t N,
                         int64_t d, int E, int k, int32_t *idx, float *gate, hipStream_t s) {
     const int blocks = (int)((N + kTokTile - 1) / kTokTile);
     hipLaunchKernelGGL(router_bf16_kernel<NT>, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const unsigned short *>(x), wsp, noise, (int)N, (int)d, E, k,
+                       static_cast<const unsigned short *>(x), wg, noise, (int)N, (int)d, E, k,
                        idx, gate);
     return hipGetLastError();
 }
@@ -326,10 +340,9 @@ int64_t router_padded_experts(int E) { return (E + 15) / 16 * 16; }
 
 size_t router_workspace_bytes(int64_t N, int64_t d, int E) {
     const int64_t Ep = router_padded_experts(E);
-    size_t b = (size_t)(3 * Ep * d * 2 + 255) / 256 * 256;
-    if (Ep > kFusedMaxExperts)
-        b += (size_t)(N * 3 * Ep * 4 + 255) / 256 * 256;
-    return b;
+    if (Ep <= kFusedMaxExperts)
+        return 0;
+    return (size_t)(3 * Ep * d * 2 + 255) / 256 * 256 + (size_t)(N * 3 * Ep * 4 + 255) / 256 * 256;
 }
 
 hipError_t launch_router_bf16(const void *x, const float *wg, const float *noise, int64_t N,
@@ -338,6 +351,8 @@ hipError_t launch_router_bf16(const void *x, const float *wg, const float *noise
     if (N == 0)
         return hipSuccess;
     const int Ep = (int)router_padded_experts(E);
+    if (Ep <= 16) return launch_fused<1>(x, wg, noise, N, d, E, k, idx, gate, s);
+    if (Ep <= 32) return launch_fused<2>(x, wg, noise, N, d, E, k, idx, gate, s);
     unsigned short *wsp = static_cast<unsigned short *>(ws);
     const int64_t groups = (int64_t)Ep * (d / 8);
     hipLaunchKernelGGL(split_router_weights_kernel, dim3((unsigned)((groups + 255) / 256)),
@@ -345,8 +360,6 @@ hipError_t launch_router_bf16(const void *x, const float *wg, const float *noise
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    if (Ep <= 16) return launch_fused<1>(x, wsp, noise, N, d, E, k, idx, gate, s);
-    if (Ep <= 32) return launch_fused<2>(x, wsp, noise, N, d, E, k, idx, gate, s);
     float *s3 = reinterpret_cast<float *>(static_cast<char *>(ws) +
                                           (size_t)(3 * Ep * d * 2 + 255) / 256 * 256);
     err = launch_plain_gemm_bf16(x, wsp, N, d, 3 * Ep, s3, s);

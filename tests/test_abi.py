@@ -157,12 +157,14 @@ def test_stage_entry_points_reject_bad_arguments(L):
     wgb = _t(FAKE, BF16, 4, 16)
     assert L.moe_router(ctypes.byref(x), ctypes.byref(wgb), None, 2, v, v, v, 1 << 30, None) == -3
     assert L.moe_router(ctypes.byref(x), ctypes.byref(wg), None, 2, None, v, v, 1 << 30, None) == -1
-    # bf16 needs router scratch: missing, too small, misaligned
-    assert L.moe_router_workspace_size(10, 16, 4, BF16) > 0
-    assert L.moe_router_workspace_size(10, 16, 4, F32) == 0
-    assert L.moe_router(ctypes.byref(x), ctypes.byref(wg), None, 2, v, v, None, 0, None) == -1
-    assert L.moe_router(ctypes.byref(x), ctypes.byref(wg), None, 2, v, v, v, 16, None) == -5
-    assert L.moe_router(ctypes.byref(x), ctypes.byref(wg), None, 2, v, v,
+    # a bf16 router with more than 32 experts needs scratch: missing, too small, misaligned
+    assert L.moe_router_workspace_size(10, 16, 4, BF16) == 0
+    assert L.moe_router_workspace_size(10, 16, 64, BF16) > 0
+    assert L.moe_router_workspace_size(10, 16, 64, F32) == 0
+    wg64 = _t(FAKE, F32, 64, 16)
+    assert L.moe_router(ctypes.byref(x), ctypes.byref(wg64), None, 2, v, v, None, 0, None) == -1
+    assert L.moe_router(ctypes.byref(x), ctypes.byref(wg64), None, 2, v, v, v, 16, None) == -5
+    assert L.moe_router(ctypes.byref(x), ctypes.byref(wg64), None, 2, v, v,
                         ctypes.c_void_p(FAKE + 8), 1 << 30, None) == -7
     # experts: mismatched weight shapes
     wu = _t(FAKE, BF16, 4, 32, 16)

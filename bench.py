@@ -190,15 +190,16 @@ def main():
     s_ = B._stream()
     p = B._ptr
     rws = B.alloc_workspace(B.router_workspace_size(wl.N, wl.d, wl.E, x.dtype))
+    ews = B.alloc_workspace(B.expert_workspace_size(x.dtype))
     stages = {
         "router": lambda: L.moe_router(r(dx), r(dg), r(dn) if dn else None, wl.k, p(idx),
                                        p(gate), p(rws), rws.numel(), s_),
         "dispatch": lambda: L.moe_dispatch(wl.N, wl.E, wl.k, C, p(idx), p(slot), p(usedt),
                                            p(slot_token), p(tiles), s_),
         "expert_up": lambda: L.moe_expert_up(r(dx), r(du), wl.k, C, p(usedt), p(slot_token),
-                                             p(tiles), p(H), s_),
+                                             p(tiles), p(H), p(ews), ews.numel(), s_),
         "expert_down": lambda: L.moe_expert_down(wl.N, r(dd), wl.k, C, p(usedt), p(slot_token),
-                                                 p(tiles), p(H), p(Y), s_),
+                                                 p(tiles), p(H), p(Y), p(ews), ews.numel(), s_),
         "combine": lambda: L.moe_combine(wl.N, wl.d, wl.k, p(Y), p(gate), p(slot), r(do), s_),
     }
     st_ms = {}

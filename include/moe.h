@@ -171,21 +171,35 @@ int moe_dispatch(int64_t N, int64_t E, int k, int64_t capacity, const int32_t *t
  *   H[e, r, :] = ReLU(W_up[e] x_t)      stored in the dtype of x   [E, min(C,N), d_ff]
  *   Y[a, :]    = W_down[e] H[e, r, :]   fp32                       [N*k, d]
  * The gather of token rows is fused into the first product. Rows of Y whose
- * assignment was dropped are not written. H and Y are caller device buffers. */
+ * assignment was dropped are not written. H and Y are caller device buffers.
+ * workspace: optional device scratch of workspace_bytes (256-byte aligned,
+ * MOE_ERR_ALIGN otherwise) in which the bf16 path keeps fp32 partial tiles
+ * when it cuts the K loop of a product's last, partly idle round of tiles
+ * into ranges; NULL, or too few bytes for one partial tile per workgroup the
+ * device runs at once, computes every tile whole (moe_expert_workspace_size()
+ * bytes are enough on a device with up to 256 compute units). Either way the
+ * result is deterministic; the two differ only in fp32 summation order.
+ * Calls that share a workspace must not overlap. */
 int moe_experts(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W_down,
                 int k, int64_t capacity, const int32_t *used, const int32_t *slot_token,
-                const int32_t *tiles, void *H, float *Y, void *stream);
+                const int32_t *tiles, void *H, float *Y, void *workspace,
+                size_t workspace_bytes, void *stream);
 
-/* The two halves of moe_experts, one kernel each (page 1 STEP 8-9 and STEP 10):
- * moe_expert_up writes H from x and W_up; moe_expert_down writes Y from H and
- * W_down ([E, d, d_ff]; H has W_down's dtype and [E, min(C,N), d_ff] rows,
- * Y is [N*k, d] fp32). */
+/* Bytes of expert scratch that enable the K-split on any device with up to
+ * 256 compute units (0 for MOE_F32 and for an unknown dtype). */
+size_t moe_expert_workspace_size(int32_t dtype);
+
+/* The two halves of moe_experts, one product each (page 1 STEP 8-9 and STEP
+ * 10): moe_expert_up writes H from x and W_up; moe_expert_down writes Y from
+ * H and W_down ([E, d, d_ff]; H has W_down's dtype and [E, min(C,N), d_ff]
+ * rows, Y is [N*k, d] fp32). workspace as for moe_experts. */
 int moe_expert_up(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t capacity,
                   const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
-                  void *H, void *stream);
+                  void *H, void *workspace, size_t workspace_bytes, void *stream);
 int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
                     const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
-                    const void *H, float *Y, void *stream);
+                    const void *H, float *Y, void *workspace, size_t workspace_bytes,
+                    void *stream);
 
 /* Combine (page 1 STEP 11-12; slides 38-40): out[t] = sum over j < k with
  * slot[t, j] >= 0 of topk_gate[t, j] * Y[t*k + j], accumulated in fp32 in

@@ -22,7 +22,7 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK = 256, 16
 #: every function the header declares
 EXPORTS = ("moe_forward", "moe_workspace_size", "moe_capacity", "moe_error_string",
            "moe_router", "moe_router_workspace_size", "moe_dispatch", "moe_experts",
-           "moe_expert_up", "moe_expert_down", "moe_combine")
+           "moe_expert_up", "moe_expert_down", "moe_expert_workspace_size", "moe_combine")
 
 
 class MoeTensor(ctypes.Structure):
@@ -74,12 +74,17 @@ def lib():
         L.moe_router_workspace_size.restype = ctypes.c_size_t
         L.moe_dispatch.argtypes = [_i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_dispatch.restype = ctypes.c_int
-        L.moe_experts.argtypes = [_T, _T, _T, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_experts.argtypes = [_T, _T, _T, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  ctypes.c_size_t, _vp]
         L.moe_experts.restype = ctypes.c_int
-        L.moe_expert_up.argtypes = [_T, _T, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp]
+        L.moe_expert_up.argtypes = [_T, _T, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp,
+                                    ctypes.c_size_t, _vp]
         L.moe_expert_up.restype = ctypes.c_int
-        L.moe_expert_down.argtypes = [_i64, _T, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_expert_down.argtypes = [_i64, _T, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      ctypes.c_size_t, _vp]
         L.moe_expert_down.restype = ctypes.c_int
+        L.moe_expert_workspace_size.argtypes = [ctypes.c_int32]
+        L.moe_expert_workspace_size.restype = ctypes.c_size_t
         L.moe_combine.argtypes = [_i64, _i64, ctypes.c_int, _vp, _vp, _vp, _T, _vp]
         L.moe_combine.restype = ctypes.c_int
         _lib = L
@@ -248,8 +253,27 @@ def dispatch(idx: torch.Tensor, E: int, capacity_: int, stream=None):
     return slot, used, slot_token, tiles
 
 
+def expert_workspace_size(dtype: torch.dtype) -> int:
+    code = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(lib().moe_expert_workspace_size(code))
+
+
+def _expert_ws(workspace, dtype, device):
+    """``"auto"``: scratch of moe_expert_workspace_size(); None: no K-split."""
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+        n = expert_workspace_size(dtype)
+        return alloc_workspace(n, device) if n > 0 else None
+    return workspace
+
+
+def _ws_args(ws):
+    return (None, 0) if ws is None else (ctypes.c_void_p(ws.data_ptr()), ws.numel())
+
+
 def experts(x, W_up, W_down, k, capacity_, used, slot_token, tiles, H=None, Y=None,
-            stream=None):
+            workspace="auto", stream=None):
     """Returns (H [E, min(C,N), d_ff] in x's dtype, Y [N*k, d] fp32)."""
     N, d = x.numel() // x.shape[-1], x.shape[-1]
     E, d_ff = W_up.shape[0], W_up.shape[1]
@@ -261,23 +285,29 @@ def experts(x, W_up, W_down, k, capacity_, used, slot_token, tiles, H=None, Y=No
     dx, du, dd = desc(x), desc(W_up), desc(W_down)
     if not slot_token.is_contiguous():
         raise ValueError("slot_token must be a contiguous [E, min(C, N)] tensor")
+    wp, wn = _ws_args(_expert_ws(workspace, x.dtype, x.device))
     _check(lib().moe_experts(_ref(dx), _ref(du), _ref(dd), k, capacity_, _ptr(used),
-                             _ptr(slot_token), _ptr(tiles), _ptr(H), _ptr(Y), _stream(stream)),
+                             _ptr(slot_token), _ptr(tiles), _ptr(H), _ptr(Y), wp, wn,
+                             _stream(stream)),
            "moe_experts")
     return H, Y
 
 
-def expert_up(x, W_up, k, capacity_, used, slot_token, tiles, H, stream=None):
+def expert_up(x, W_up, k, capacity_, used, slot_token, tiles, H, workspace="auto",
+              stream=None):
     dx, du = desc(x), desc(W_up)
+    wp, wn = _ws_args(_expert_ws(workspace, x.dtype, x.device))
     _check(lib().moe_expert_up(_ref(dx), _ref(du), k, capacity_, _ptr(used), _ptr(slot_token),
-                               _ptr(tiles), _ptr(H), _stream(stream)), "moe_expert_up")
+                               _ptr(tiles), _ptr(H), wp, wn, _stream(stream)), "moe_expert_up")
     return H
 
 
-def expert_down(N, W_down, k, capacity_, used, slot_token, tiles, H, Y, stream=None):
+def expert_down(N, W_down, k, capacity_, used, slot_token, tiles, H, Y, workspace="auto",
+                stream=None):
     dd = desc(W_down)
+    wp, wn = _ws_args(_expert_ws(workspace, W_down.dtype, W_down.device))
     _check(lib().moe_expert_down(N, _ref(dd), k, capacity_, _ptr(used), _ptr(slot_token),
-                                 _ptr(tiles), _ptr(H), _ptr(Y), _stream(stream)),
+                                 _ptr(tiles), _ptr(H), _ptr(Y), wp, wn, _stream(stream)),
            "moe_expert_down")
     return Y
 

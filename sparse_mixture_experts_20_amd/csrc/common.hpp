@@ -63,14 +63,22 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 // Y[scatter] = H W_down^T.
 // bf16 != 0: bf16 operands on matrix cores; otherwise fp32 operands.
 // rows_per_expert: the expected kept rows per expert (picks the tile shape).
+// part/part_bytes: device scratch for the K-split of a product's last round
+// of tiles (NULL, or smaller than one partial tile per resident workgroup:
+// no split). split_workspace_bytes() is enough for every tile shape on a
+// device with up to 256 CUs.
+constexpr size_t kSplitWorkspaceBytes = (size_t)256 * 256 * 256 * sizeof(float);
+size_t split_workspace_bytes();
 hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t d,
                             int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                             const int32_t *slot_token, const int32_t *tiles, void *H,
-                            int64_t rows_per_expert, hipStream_t s);
+                            int64_t rows_per_expert, void *part, size_t part_bytes,
+                            hipStream_t s);
 hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int64_t d,
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, float *Y,
-                              int64_t rows_per_expert, hipStream_t s);
+                              int64_t rows_per_expert, void *part, size_t part_bytes,
+                              hipStream_t s);
 
 // Y[rows, Nout] (fp32) = A[rows, K] * W[Nout, K]^T, bf16 operands.
 hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, int64_t K,

@@ -31,6 +31,8 @@
 // each weight tile, and block b (placed on XCD b mod 8 by the dispatcher)
 // takes tile (b mod 8) * T/8 + b/8: every XCD works through one contiguous
 // range of tiles and the sharing happens inside its own L2.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -65,6 +67,65 @@ __device__ __forceinline__ void dma16(unsigned lds_base, const void *g) {
                  : "memory", "m0");
 }
 
+// Work split of a grouped product with T output tiles of KT K-steps over P
+// workgroups that can run at once. Whole tiles fill the full rounds. When
+// the last round would leave most workgroups idle, its `tail` tiles are cut
+// into nsplit K-ranges; each range's fp32 partial tile goes to a scratch
+// slot and split_fixup_kernel adds the ranges of a tile in K order. The cut
+// is taken only when it shortens the product by at least 15% on paper
+// ((1 - 1/nsplit) of one round out of R + 1): with many full rounds the
+// rounds blur (tiles differ in cost) and the partial-tile traffic eats the
+// gain. The plan depends only on (T, KT, P), so it and the result are the
+// same on every run.
+struct SplitPlan {
+    int Tdp;      // tiles computed whole
+    int tail;     // tiles cut into K-ranges (the last `tail` tile indices)
+    int nsplit;   // K-ranges per cut tile (1: no split)
+};
+
+constexpr int kSplitMinSteps = 8;   // K-steps of the shortest range
+
+__device__ __forceinline__ SplitPlan split_plan(int T, int KT, int P) {
+    SplitPlan p{T, 0, 1};
+    if (P <= 0 || T < P)
+        return p;
+    const int R = T / P, tail = T % P;
+    if (tail == 0)
+        return p;
+    int ns = P / tail;
+    if (ns > KT / kSplitMinSteps)
+        ns = KT / kSplitMinSteps;
+    if (ns < 2 || 20 * (ns - 1) < 3 * (R + 1) * ns)
+        return p;
+    p.Tdp = T - tail;
+    p.tail = tail;
+    p.nsplit = ns;
+    return p;
+}
+
+// Expert e owning tile L of the grouped schedule (tiles of expert e are
+// s_mt[e]*NT .. s_mt[e+1]*NT - 1, row tiles fastest), and its tile origin.
+__device__ __forceinline__ void decode_tile(int L, const int *s_mt, int E, int NT, int BM,
+                                            int BN, int &e, int &m0, int &n0) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_mt[mid] * NT <= L) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+    const int mte = s_mt[e + 1] - s_mt[e];
+    const int local = L - s_mt[e] * NT;
+    m0 = (local % mte) * BM;
+    n0 = (local / mte) * BN;
+}
+
+// Block b of a launch whose first T8 blocks take whole tiles: block b runs on
+// XCD b mod 8, and takes index (b mod 8) * T8/8 + b/8, so every XCD works
+// through one contiguous range of indices (sharing operands in its own L2).
+__device__ __forceinline__ int xcd_index(int b, int T8) {
+    return (b % kXcds) * (T8 / kXcds) + b / kXcds;
+}
+
 // BM x BN output tile, K-step BKT, S-stage LDS ring filled by direct loads.
 // Each K-tile row is BKT bf16 = RB bytes of 16-byte chunks; chunk c of row r
 // is stored at position c ^ ((r / RPB) % CPR) (RPB rows share one 256-byte
@@ -74,14 +135,17 @@ __device__ __forceinline__ void dma16(unsigned lds_base, const void *g) {
 // up to 256 registers per lane and schedule for latency rather than occupancy.
 // MODE 0: up product (gathered token rows, ReLU, bf16 H); 1: down product
 // (fp32 rows scattered to their assignment); 2: plain product of ceff rows of
-// A into fp32 rows of Y (no gather, no schedule table).
+// A into fp32 rows of Y (no gather, no schedule table, no split).
+// part: scratch for the split of the last round (NULL: no split), P: the
+// number of workgroups of this kernel that fit on the device at once.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BKT, int S, int MODE>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void expert_gemm_kernel(
     const unsigned short *__restrict__ A_src, const unsigned short *__restrict__ W, int K,
     int Nout, int E, int k, int ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
-    unsigned short *__restrict__ H_out, float *__restrict__ Y_out) {
+    unsigned short *__restrict__ H_out, float *__restrict__ Y_out, float *__restrict__ part,
+    int P) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int NTHR = NW * 64;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;   // wave tile
@@ -102,42 +166,53 @@ void expert_gemm_kernel(
 
     const int tid = threadIdx.x;
     const int NT = (Nout + BN - 1) / BN;
-    int T, e, mte, local, rows;
+    const int KT = (K + BKT - 1) / BKT;
     const int b = blockIdx.x;
+    int e, m0, n0, rows;
+    int kb = 0, ke = KT;   // K-steps of this workgroup
+    int piece = -1;        // scratch slot of a K-range, or -1 for a whole tile
     if constexpr (MODE == 2) {
         // plain product over ceff rows, one "expert": no schedule table
-        mte = (ceff + BM - 1) / BM;
-        T = mte * NT;
+        const int mte = (ceff + BM - 1) / BM;
+        const int T = mte * NT;
+        const int T8 = (T + kXcds - 1) / kXcds * kXcds;
+        if (b >= T8)
+            return;
+        const int L = xcd_index(b, T8);
+        if (L >= T)
+            return;
+        e = 0;
+        rows = ceff;
+        m0 = (L % mte) * BM;
+        n0 = (L / mte) * BN;
     } else {
         for (int i = tid; i <= E; i += NTHR)
             s_mt[i] = mt_off[i];
         __syncthreads();
-        T = s_mt[E] * NT;
-    }
-    const int T8 = (T + kXcds - 1) / kXcds * kXcds;
-    if (b >= T8)
-        return;
-    const int L = (b % kXcds) * (T8 / kXcds) + b / kXcds;
-    if (L >= T)
-        return;
-    if constexpr (MODE == 2) {
-        e = 0;
-        local = L;
-        rows = ceff;
-    } else {
-        // expert owning tile L: the last e with s_mt[e] * NT <= L
-        int lo = 0, hi = E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_mt[mid] * NT <= L) lo = mid; else hi = mid - 1;
+        const int T = s_mt[E] * NT;
+        const SplitPlan sp = split_plan(T, KT, part ? P : 0);
+        const int T8 = (sp.Tdp + kXcds - 1) / kXcds * kXcds;
+        int L;
+        if (b < T8) {
+            L = xcd_index(b, T8);
+            if (L >= sp.Tdp)
+                return;
+        } else {
+            const int np = sp.tail * sp.nsplit;
+            const int np8 = (np + kXcds - 1) / kXcds * kXcds;
+            if (b - T8 >= np8)
+                return;
+            piece = xcd_index(b - T8, np8);
+            if (piece >= np)
+                return;
+            L = sp.Tdp + piece / sp.nsplit;
+            const int s = piece % sp.nsplit;
+            kb = (int)((int64_t)s * KT / sp.nsplit);
+            ke = (int)((int64_t)(s + 1) * KT / sp.nsplit);
         }
-        e = lo;
-        mte = s_mt[e + 1] - s_mt[e];
-        local = L - s_mt[e] * NT;
+        decode_tile(L, s_mt, E, NT, BM, BN, e, m0, n0);
         rows = used[e];
     }
-    const int m0 = (local % mte) * BM;
-    const int n0 = (local / mte) * BN;
 
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -190,6 +265,11 @@ void expert_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // 16-row strips of this wave that hold kept rows: the rest of the tile is
+    // padding past used[e], whose products are never stored, so the last
+    // row tile of an expert skips their matrix instructions.
+    int nvf = (rows - m0 - wm * WTM + 15) / 16;
+    nvf = __builtin_amdgcn_readfirstlane(nvf < 0 ? 0 : (nvf > FM ? FM : nvf));
     // Operand fragments of K-step ks (32 wide) of stage st; the next step's
     // fragments are read before the current step's MFMAs are issued.
     constexpr int KS = BKT / 32;
@@ -204,21 +284,25 @@ void expert_gemm_kernel(
         for (int j = 0; j < FN; ++j)
             bfr[j] = *reinterpret_cast<const bf16x8 *>(Bs + (rb0 + j * 16) * RB + ((c ^ xb) << 4));
     };
-    auto mma = [&](const bf16x8 (&af)[FM], const bf16x8 (&bfr)[FN]) {
+    auto mma = [&](const bf16x8 (&af)[FM], const bf16x8 (&bfr)[FN], auto full) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i) {
+            if (decltype(full)::value || i < nvf) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j],
+                                                                         0, 0, 0);
+            }
+        }
     };
-    auto compute = [&](int st) {
+    auto compute = [&](int st, auto full) {
         bf16x8 af[2][FM], bfr[2][FN];
         read_frags(st, 0, af[0], bfr[0]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 1 < KS)
                 read_frags(st, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
-            mma(af[ks & 1], bfr[ks & 1]);
+            mma(af[ks & 1], bfr[ks & 1], full);
         }
     };
     // zero the chunks of the last K-tile that lie past K (both operands)
@@ -232,30 +316,35 @@ void expert_gemm_kernel(
         }
     };
 
-    const int KT = (K + BKT - 1) / BKT;
+    auto mainloop = [&](auto full) {
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-        if (s < KT)
-            issue(s);
-    for (int kt = 0; kt < KT; ++kt) {
-        // tile kt must have landed: later tiles issued so far may stay in flight
-        const int later = min(S - 2, KT - 1 - kt);
-        if (later >= S - 2) {
-            wait_vm<(S - 2) * G>();
-        } else if constexpr (S > 2) {
-            if (later == 0) wait_vm<0>();
-            else if (later == 1) wait_vm<G>();
-            else wait_vm<0>();
-        }
-        lds_barrier();
-        if (kt + S - 1 < KT)
-            issue(kt + S - 1);
-        if (kt == KT - 1 && (K % BKT) != 0) {
-            zero_tail(kt);
+        for (int s = 0; s < S - 1; ++s)
+            if (kb + s < ke)
+                issue(kb + s);
+        for (int kt = kb; kt < ke; ++kt) {
+            // step kt must have landed: later steps issued so far may stay in flight
+            const int later = min(S - 2, ke - 1 - kt);
+            if (later >= S - 2) {
+                wait_vm<(S - 2) * G>();
+            } else if constexpr (S > 2) {
+                if (later == 0) wait_vm<0>();
+                else if (later == 1) wait_vm<G>();
+                else wait_vm<0>();
+            }
             lds_barrier();
+            if (kt + S - 1 < ke)
+                issue(kt + S - 1);
+            if (kt == KT - 1 && (K % BKT) != 0) {
+                zero_tail(kt);
+                lds_barrier();
+            }
+            compute(kt % S, full);
         }
-        compute(kt % S);
-    }
+    };
+    if (nvf == FM)
+        mainloop(std::true_type{});
+    else
+        mainloop(std::false_type{});
     lds_barrier();
 
     // epilogue: per wave, one 16-row strip at a time through a private LDS
@@ -273,15 +362,24 @@ void expert_gemm_kernel(
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 scr[((lane >> 4) * 4 + q) * SLD + j * 16 + (lane & 15)] = acc[i][j][q];
-        const int r = m0 + wm * WTM + i * 16 + rr;
-        const int nb = n0 + wn * WTN + cg;
+        const int tr = wm * WTM + i * 16 + rr;   // row within the tile
+        const int r = m0 + tr;
+        const int tc = wn * WTN + cg;            // column within the tile
+        const int nb = n0 + tc;
         f32x4 v[CPL / 4];
 #pragma unroll
         for (int c = 0; c < CPL / 4; ++c)
             v[c] = *reinterpret_cast<const f32x4 *>(&scr[rr * SLD + cg + 4 * c]);
         if (r < rows) {
             const int64_t srow = (int64_t)e * ceff + r;
-            if (MODE == 0) {
+            if (piece >= 0) {
+                // fp32 partial of a K-range, tile-local [BM][BN] slot
+                float *dst = part + ((int64_t)piece * BM + tr) * BN + tc;
+#pragma unroll
+                for (int c = 0; c < CPL / 4; ++c)
+                    if (nb + 4 * c + 4 <= Nout)
+                        *reinterpret_cast<f32x4 *>(dst + 4 * c) = v[c];
+            } else if (MODE == 0) {
                 unsigned short *dst = H_out + srow * Nout + nb;
 #pragma unroll
                 for (int h = 0; h < CPL / 8; ++h) {
@@ -305,6 +403,54 @@ void expert_gemm_kernel(
                     if (nb + 4 * c + 4 <= Nout)
                         *reinterpret_cast<f32x4 *>(dst + 4 * c) = v[c];
             }
+        }
+    }
+}
+
+// Sum of the K-range partials of the cut tiles, in K order, then the same
+// epilogue as a whole tile (MODE 0: ReLU, bf16 H; MODE 1: fp32 row of Y).
+// One workgroup per 16-row strip of a cut tile; 4 columns per thread.
+template <int BM, int BN, int BKT, int MODE>
+__global__ __launch_bounds__(256) void split_fixup_kernel(
+    int K, int Nout, int E, int ceff, const int32_t *__restrict__ used,
+    const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
+    const float *__restrict__ part, int P, unsigned short *__restrict__ H_out,
+    float *__restrict__ Y_out) {
+    constexpr int STRIPS = BM / 16;
+    __shared__ int s_mt[kMaxExperts + 1];
+    for (int i = threadIdx.x; i <= E; i += 256)
+        s_mt[i] = mt_off[i];
+    __syncthreads();
+    const int NT = (Nout + BN - 1) / BN;
+    const int KT = (K + BKT - 1) / BKT;
+    const SplitPlan sp = split_plan(s_mt[E] * NT, KT, P);
+    const int t = blockIdx.x / STRIPS, strip = blockIdx.x % STRIPS;
+    if (sp.nsplit < 2 || t >= sp.tail)
+        return;
+    int e, m0, n0;
+    decode_tile(sp.Tdp + t, s_mt, E, NT, BM, BN, e, m0, n0);
+    const int rows = used[e];
+    for (int i = threadIdx.x; i < 16 * (BN / 4); i += 256) {
+        const int rr = i / (BN / 4), c4 = i % (BN / 4);
+        const int tr = strip * 16 + rr;
+        const int r = m0 + tr;
+        const int n = n0 + 4 * c4;
+        if (r >= rows || n + 4 > Nout)
+            continue;
+        const float *src = part + ((int64_t)t * sp.nsplit * BM + tr) * BN + 4 * c4;
+        f32x4 v = *reinterpret_cast<const f32x4 *>(src);
+        for (int s = 1; s < sp.nsplit; ++s)
+            v += *reinterpret_cast<const f32x4 *>(src + (int64_t)s * BM * BN);
+        const int64_t srow = (int64_t)e * ceff + r;
+        if (MODE == 0) {
+            u32x2 pk;
+            pk[0] = (unsigned)f32_to_bf16_bits(fmaxf(v[0], 0.f)) |
+                    ((unsigned)f32_to_bf16_bits(fmaxf(v[1], 0.f)) << 16);
+            pk[1] = (unsigned)f32_to_bf16_bits(fmaxf(v[2], 0.f)) |
+                    ((unsigned)f32_to_bf16_bits(fmaxf(v[3], 0.f)) << 16);
+            *reinterpret_cast<u32x2 *>(H_out + srow * Nout + n) = pk;
+        } else {
+            *reinterpret_cast<f32x4 *>(Y_out + (int64_t)slot_token[srow] * Nout + n) = v;
         }
     }
 }
@@ -387,6 +533,8 @@ namespace {
 //  - 128x128, 4 waves of 64x64, two workgroups per CU: otherwise.
 enum class Tile { k128, k128x64, k256 };
 
+constexpr int kBK = 64;   // K-step of every bf16 tile shape
+
 Tile pick_tile(int64_t rows_per_expert, int64_t Nout, int E) {
     const int64_t t256 = (int64_t)E * ((rows_per_expert + 255) / 256) * ((Nout + 255) / 256);
     if (rows_per_expert >= 512 && (t256 >= 256 || Nout >= 2048))
@@ -397,52 +545,101 @@ Tile pick_tile(int64_t rows_per_expert, int64_t Nout, int E) {
     return Tile::k128;
 }
 
+constexpr int kMaxDevices = 64;
+
+// Workgroups of `kernel` that run at once on the current device (-1 if unknown).
+template <typename Kern>
+int resident_blocks(Kern kernel, int threads) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        cus * per_cu <= 0)
+        return -1;
+    return cus * per_cu;
+}
+
+// One bf16 grouped product on tile shape BM x BN, plus the fix-up of the
+// split last round when the scratch `part` can hold it.
+template <int BM, int BN, int WM, int WN, int MODE>
+hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_t K, int64_t Nout,
+                        int E, int k, int64_t ceff, const int32_t *used,
+                        const int32_t *slot_token, const int32_t *mt, unsigned short *H,
+                        float *Y, float *part, size_t part_bytes, hipStream_t s) {
+    auto kern = expert_gemm_kernel<BM, BN, WM, WN, kBK, 2, MODE>;
+    constexpr int NTHR = WM * WN * 64;
+    static int resident[kMaxDevices];   // per device, filled on first use (0 = unset)
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        dev = -1;
+    int P = 0;
+    if (dev >= 0) {
+        if (resident[dev] == 0)
+            resident[dev] = resident_blocks(kern, NTHR);
+        P = resident[dev];
+    }
+    const int64_t slot = (int64_t)BM * BN * sizeof(float);
+    if (!part || P <= 0 || (int64_t)P * slot > (int64_t)part_bytes)
+        P = 0;
+    const int64_t KT = (K + kBK - 1) / kBK;
+    const int64_t tmax = (int64_t)E * ((ceff + BM - 1) / BM) * ((Nout + BN - 1) / BN);
+    // a split needs at least two ranges of kSplitMinSteps, at least one full
+    // round of tiles and (by the 15% rule of split_plan) fewer than six
+    const bool split =
+        P > 0 && KT >= 2 * kSplitMinSteps && tmax >= P && tmax < 6 * (int64_t)P;
+    const int64_t grid = (tmax + kXcds - 1) / kXcds * kXcds +
+                         (split ? (int64_t)(P + kXcds - 1) / kXcds * kXcds : 0);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHR), 0, s, A, W, (int)K, (int)Nout, E,
+                       k, (int)ceff, used, slot_token, mt, H, Y, split ? part : nullptr,
+                       split ? P : 0);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || !split)
+        return err;
+    hipLaunchKernelGGL((split_fixup_kernel<BM, BN, kBK, MODE>), dim3((unsigned)(P * (BM / 16))),
+                       dim3(256), 0, s, (int)K, (int)Nout, E, (int)ceff, used, slot_token, mt,
+                       (const float *)part, P, H, Y);
+    return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W, int64_t K,
                        int64_t Nout, int E, int k, int64_t ceff, const int32_t *used,
                        const int32_t *slot_token, const int32_t *tiles, unsigned short *H,
-                       float *Y, hipStream_t s) {
-    if (t == Tile::k256) {
-        const int64_t grid = (E * ((ceff + 255) / 256) * ((Nout + 255) / 256) + kXcds - 1) /
-                             kXcds * kXcds;
-        hipLaunchKernelGGL((expert_gemm_kernel<256, 256, 2, 4, 64, 2, MODE>), dim3((unsigned)grid),
-                           dim3(512), 0, s, A, W, (int)K, (int)Nout, E, k, (int)ceff, used,
-                           slot_token, tiles + E + 1, H, Y);
-    } else if (t == Tile::k128x64) {
-        const int64_t grid = (E * ((ceff + 127) / 128) * ((Nout + 63) / 64) + kXcds - 1) /
-                             kXcds * kXcds;
-        hipLaunchKernelGGL((expert_gemm_kernel<128, 64, 2, 2, 64, 2, MODE>), dim3((unsigned)grid),
-                           dim3(256), 0, s, A, W, (int)K, (int)Nout, E, k, (int)ceff, used,
-                           slot_token, tiles, H, Y);
-    } else {
-        const int64_t grid = (E * ((ceff + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) /
-                             kXcds * kXcds;
-        hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, 64, 2, MODE>), dim3((unsigned)grid),
-                           dim3(256), 0, s, A, W, (int)K, (int)Nout, E, k, (int)ceff, used,
-                           slot_token, tiles, H, Y);
-    }
-    return hipGetLastError();
+                       float *Y, void *part, size_t part_bytes, hipStream_t s) {
+    float *pf = static_cast<float *>(part);
+    if (t == Tile::k256)
+        return launch_tiles<256, 256, 2, 4, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
+                                                  tiles + E + 1, H, Y, pf, part_bytes, s);
+    if (t == Tile::k128x64)
+        return launch_tiles<128, 64, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
+                                                 tiles, H, Y, pf, part_bytes, s);
+    return launch_tiles<128, 128, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token, tiles,
+                                              H, Y, pf, part_bytes, s);
 }
 
 }  // namespace
+
+size_t split_workspace_bytes() { return kSplitWorkspaceBytes; }
 
 hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, int64_t K,
                                   int64_t Nout, float *Y, hipStream_t s) {
     if (rows == 0)
         return hipSuccess;
     const int64_t grid = (((rows + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, 64, 2, 2>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, kBK, 2, 2>), dim3((unsigned)grid),
                        dim3(256), 0, s, static_cast<const unsigned short *>(A),
                        static_cast<const unsigned short *>(W), (int)K, (int)Nout, 1, 1, (int)rows,
                        (const int32_t *)nullptr, (const int32_t *)nullptr,
-                       (const int32_t *)nullptr, (unsigned short *)nullptr, Y);
+                       (const int32_t *)nullptr, (unsigned short *)nullptr, Y, (float *)nullptr,
+                       0);
     return hipGetLastError();
 }
 
 hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t d,
                             int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                             const int32_t *slot_token, const int32_t *tiles, void *H,
-                            int64_t rows_per_expert, hipStream_t s) {
+                            int64_t rows_per_expert, void *part, size_t part_bytes,
+                            hipStream_t s) {
     if (ceff == 0)
         return hipSuccess;
     if (bf16)
@@ -450,7 +647,7 @@ hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t 
                               static_cast<const unsigned short *>(x),
                               static_cast<const unsigned short *>(w_up), d, d_ff, E, k, ceff,
                               used, slot_token, tiles, static_cast<unsigned short *>(H), nullptr,
-                              s);
+                              part, part_bytes, s);
     hipLaunchKernelGGL(experts_f32_kernel<0>,
                        dim3((unsigned)((d_ff + 63) / 64), (unsigned)((ceff + 63) / 64), E),
                        dim3(256), 0, s, static_cast<const float *>(x),
@@ -462,14 +659,15 @@ hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t 
 hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int64_t d,
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, float *Y,
-                              int64_t rows_per_expert, hipStream_t s) {
+                              int64_t rows_per_expert, void *part, size_t part_bytes,
+                              hipStream_t s) {
     if (ceff == 0)
         return hipSuccess;
     if (bf16)
         return launch_gemm<1>(pick_tile(rows_per_expert, d, E),
                               static_cast<const unsigned short *>(H),
                               static_cast<const unsigned short *>(w_down), d_ff, d, E, k, ceff,
-                              used, slot_token, tiles, nullptr, Y, s);
+                              used, slot_token, tiles, nullptr, Y, part, part_bytes, s);
     hipLaunchKernelGGL(experts_f32_kernel<1>,
                        dim3((unsigned)((d + 63) / 64), (unsigned)((ceff + 63) / 64), E),
                        dim3(256), 0, s, static_cast<const float *>(H),

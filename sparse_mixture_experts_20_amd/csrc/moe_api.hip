@@ -36,12 +36,17 @@ struct Dims {
 
 // Workspace regions (byte offsets from the base).
 struct Layout {
-    size_t idx, gate, slot, used, tiles, slot_token, H, Y, router, total;
+    size_t idx, gate, slot, used, tiles, slot_token, H, Y, router, part, total;
 };
 
 // Router scratch: the bf16 split of W_g (and partial scores for many experts).
 size_t router_bytes(int64_t N, int64_t d, int64_t E, int32_t dtype) {
     return dtype == MOE_BF16 ? align_up(moe::router_workspace_bytes(N, d, (int)E)) : 0;
+}
+
+// Expert scratch: fp32 partial tiles of the K-split last round (bf16 path).
+size_t expert_bytes(int32_t dtype) {
+    return dtype == MOE_BF16 ? align_up(moe::split_workspace_bytes()) : 0;
 }
 
 Layout layout_of(const Dims &m) {
@@ -57,6 +62,7 @@ Layout layout_of(const Dims &m) {
     L.H = o;          o += align_up((size_t)(m.E * m.ceff * m.d_ff) * dtype_size(m.dtype));
     L.Y = o;          o += align_up(nk * (size_t)m.d * 4);
     L.router = o;     o += router_bytes(m.N, m.d, m.E, m.dtype);
+    L.part = o;       o += expert_bytes(m.dtype);
     L.total = o;
     return L;
 }
@@ -160,6 +166,14 @@ int check_router_args(const moe_tensor *x, const moe_tensor *W_g, const moe_tens
     return MOE_OK;
 }
 
+// Optional expert scratch: NULL runs without the K-split; a non-NULL pointer
+// must be 256-byte aligned.
+int check_expert_ws(const void *ws) {
+    if (ws && !aligned(ws, kAlign))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -203,6 +217,10 @@ size_t moe_router_workspace_size(int64_t N, int64_t d, int64_t E, int32_t dtype)
     if (!valid_dtype(dtype) || N < 0 || d <= 0 || E <= 0 || E > MOE_MAX_EXPERTS)
         return 0;
     return router_bytes(N, d, E, dtype);
+}
+
+size_t moe_expert_workspace_size(int32_t dtype) {
+    return valid_dtype(dtype) ? expert_bytes(dtype) : 0;
 }
 
 int moe_router(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise, int k,
@@ -252,7 +270,7 @@ int moe_dispatch(int64_t N, int64_t E, int k, int64_t capacity, const int32_t *t
 
 int moe_expert_up(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t capacity,
                   const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
-                  void *H, void *stream) {
+                  void *H, void *workspace, size_t workspace_bytes, void *stream) {
     if (!x || !W_up)
         return MOE_ERR_NULL;
     int64_t N, d;
@@ -276,15 +294,20 @@ int moe_expert_up(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t ca
     const bool bf16 = x->dtype == MOE_BF16;
     if (bf16 && (!aligned(x->data, 16) || !aligned(W_up->data, 16) || !aligned(H, 16)))
         return MOE_ERR_ALIGN;
+    rc = check_expert_ws(workspace);
+    if (rc != MOE_OK)
+        return rc;
     return hip_status(moe::launch_expert_up(bf16, x->data, W_up->data, d, d_ff, (int)E, k,
                                             m.ceff, used, slot_token, tiles, H,
-                                            rows_per_expert(N, k, E, m.ceff),
+                                            rows_per_expert(N, k, E, m.ceff), workspace,
+                                            workspace ? workspace_bytes : 0,
                                             static_cast<hipStream_t>(stream)));
 }
 
 int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
                     const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
-                    const void *H, float *Y, void *stream) {
+                    const void *H, float *Y, void *workspace, size_t workspace_bytes,
+                    void *stream) {
     if (!W_down)
         return MOE_ERR_NULL;
     if (!valid_dtype(W_down->dtype))
@@ -305,15 +328,20 @@ int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity
     const bool bf16 = W_down->dtype == MOE_BF16;
     if (bf16 && (!aligned(W_down->data, 16) || !aligned(H, 16)))
         return MOE_ERR_ALIGN;
+    rc = check_expert_ws(workspace);
+    if (rc != MOE_OK)
+        return rc;
     return hip_status(moe::launch_expert_down(bf16, H, W_down->data, d, d_ff, (int)E, k, m.ceff,
                                               used, slot_token, tiles, Y,
-                                              rows_per_expert(N, k, E, m.ceff),
+                                              rows_per_expert(N, k, E, m.ceff), workspace,
+                                              workspace ? workspace_bytes : 0,
                                               static_cast<hipStream_t>(stream)));
 }
 
 int moe_experts(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W_down, int k,
                 int64_t capacity, const int32_t *used, const int32_t *slot_token,
-                const int32_t *tiles, void *H, float *Y, void *stream) {
+                const int32_t *tiles, void *H, float *Y, void *workspace,
+                size_t workspace_bytes, void *stream) {
     if (!x || !W_up || !W_down)
         return MOE_ERR_NULL;
     int64_t N, d;
@@ -327,15 +355,21 @@ int moe_experts(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W
         W_down->shape[2] != W_up->shape[1])
         return MOE_ERR_SHAPE;
     // validate both halves before enqueuing either
-    int rc = moe_expert_up(x, W_up, k, capacity, used, slot_token, tiles, nullptr, nullptr);
+    int rc = moe_expert_up(x, W_up, k, capacity, used, slot_token, tiles, nullptr, nullptr, 0,
+                           nullptr);
     if (rc != MOE_OK && rc != MOE_ERR_NULL)
         return rc;
     if (N > 0 && (!H || !Y))
         return MOE_ERR_NULL;
-    rc = moe_expert_up(x, W_up, k, capacity, used, slot_token, tiles, H, stream);
+    rc = check_expert_ws(workspace);
     if (rc != MOE_OK)
         return rc;
-    return moe_expert_down(N, W_down, k, capacity, used, slot_token, tiles, H, Y, stream);
+    rc = moe_expert_up(x, W_up, k, capacity, used, slot_token, tiles, H, workspace,
+                       workspace_bytes, stream);
+    if (rc != MOE_OK)
+        return rc;
+    return moe_expert_down(N, W_down, k, capacity, used, slot_token, tiles, H, Y, workspace,
+                           workspace_bytes, stream);
 }
 
 int moe_combine(int64_t N, int64_t d, int k, const float *Y, const float *topk_gate,
@@ -427,10 +461,12 @@ int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *no
     MOE_TRY(moe::launch_dispatch(idx, N, (int)E, k, m.ceff, slot, used, slot_token, tiles, s));
     const bool bf16 = x->dtype == MOE_BF16;
     const int64_t rpe = rows_per_expert(N, k, E, m.ceff);
+    void *part = ws + L.part;
+    const size_t part_bytes = L.total - L.part;
     MOE_TRY(moe::launch_expert_up(bf16, x->data, W_up->data, d, d_ff, (int)E, k, m.ceff, used,
-                                  slot_token, tiles, H, rpe, s));
+                                  slot_token, tiles, H, rpe, part, part_bytes, s));
     MOE_TRY(moe::launch_expert_down(bf16, H, W_down->data, d, d_ff, (int)E, k, m.ceff, used,
-                                    slot_token, tiles, Y, rpe, s));
+                                    slot_token, tiles, Y, rpe, part, part_bytes, s));
     MOE_TRY(moe::launch_combine(Y, gate, slot, N, d, k, out->data, out->dtype, s));
     return MOE_OK;
 }

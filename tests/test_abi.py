@@ -170,4 +170,22 @@ def test_stage_entry_points_reject_bad_arguments(L):
     wu = _t(FAKE, BF16, 4, 32, 16)
     wd = _t(FAKE, BF16, 4, 16, 31)
     assert L.moe_experts(ctypes.byref(x), ctypes.byref(wu), ctypes.byref(wd), 2, 5, v, v, v, v,
-                         v, None) == -2
+                         v, None, 0, None) == -2
+    # experts: a misaligned split scratch is refused before anything runs
+    wd_ok = _t(FAKE, BF16, 4, 16, 32)
+    assert L.moe_experts(ctypes.byref(x), ctypes.byref(wu), ctypes.byref(wd_ok), 2, 5, v, v, v,
+                         v, v, ctypes.c_void_p(FAKE + 8), 1 << 30, None) == -7
+    assert L.moe_expert_up(ctypes.byref(x), ctypes.byref(wu), 2, 5, v, v, v, v,
+                           ctypes.c_void_p(FAKE + 8), 1 << 30, None) == -7
+    assert L.moe_expert_down(10, ctypes.byref(wd_ok), 2, 5, v, v, v, v, v,
+                             ctypes.c_void_p(FAKE + 8), 1 << 30, None) == -7
+
+
+def test_expert_workspace_size(L):
+    # one fp32 256x256 partial tile for each of up to 256 resident workgroups
+    assert B.lib().moe_expert_workspace_size(BF16) == 256 * 256 * 256 * 4
+    assert B.lib().moe_expert_workspace_size(F32) == 0
+    assert B.lib().moe_expert_workspace_size(7) == 0
+    # and moe_forward's workspace holds it
+    assert (B.lib().moe_workspace_size(2048, 768, 8, 3072, 2, 1.25, BF16)
+            >= 8 * 640 * 3072 * 2 + 2048 * 2 * 768 * 4 + 256 * 256 * 256 * 4)

@@ -137,3 +137,41 @@ def test_experts_match_oracle(torch_mod, name):
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert rel <= G.BF16_REL_L2, rel
     assert np.abs(got - ref).max() <= G.BF16_MAX_ABS
+
+
+def test_experts_split_last_round(torch_mod):
+    """Shapes whose last round of 256x256 tiles is cut into K-ranges (16
+    experts of ~600 rows: 384 tiles per product against 256 resident
+    workgroups): sampled rows against the oracle, with and without the
+    split scratch, and the split result identical from run to run."""
+    torch = torch_mod
+    from sparse_mixture_experts_20_amd import binding as B
+    from sparse_mixture_experts_20_amd import device as D
+    wl = W.custom("split", N=4800, d=2048, E=16, k=2, d_ff=2048, dtype="bf16", cf=1.25,
+                  sigma=0.5, seed=53, w_std=0.02)
+    G.say("[stage] experts split last round")
+    _, idx, _ = oracle.router(wl.x64(), wl.wg64(), wl.noise64(), wl.k)
+    rng = np.random.default_rng(3)
+    # the cut tiles are the last ones: those of the highest expert ids
+    late = np.nonzero((idx >= wl.E - 3).any(axis=1))[0]
+    rows = np.unique(np.concatenate([[0, wl.N - 1], rng.choice(late, 64, replace=False),
+                                     rng.choice(wl.N, 96, replace=False)]))
+    res = oracle.forward(wl, rows=rows, want_y=True)
+    dev = D.upload(wl)
+    slot, used, slot_token, tiles = B.dispatch(torch.from_numpy(res.idx).cuda(), wl.E, res.C)
+    ys = []
+    for ws in ("auto", "auto", None):
+        _, Y = B.experts(dev["x"], dev["W_up"], dev["W_down"], wl.k, res.C, used, slot_token,
+                         tiles, workspace=ws)
+        torch.cuda.synchronize()
+        ys.append(G.to_np(Y).reshape(wl.N, wl.k, wl.d).astype(np.float64))
+    np.testing.assert_array_equal(ys[0], ys[1])
+    kept = res.slot[rows] >= 0
+    for Yg in (ys[0], ys[2]):
+        got, ref = Yg[rows][kept], res.y[kept]
+        rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert rel <= G.BF16_REL_L2, rel
+        assert np.abs(got - ref).max() <= G.BF16_MAX_ABS
+    # the split and the whole-tile sums differ only in fp32 summation order
+    a, b = ys[0][rows][kept], ys[2][rows][kept]
+    assert np.abs(a - b).max() <= 1e-3 * max(1.0, np.abs(b).max())

@@ -31,13 +31,35 @@ namespace {
 constexpr int kTokTile = 16;   // tokens per block (one MFMA M-tile)
 constexpr int kWaves = 4;      // split-K over the waves of a block
 
-__device__ __forceinline__ void split3(float w, unsigned short &hi, unsigned short &mid,
-                                       unsigned short &lo) {
-    hi = f32_to_bf16_bits(w);
-    const float r1 = w - bf16_bits_to_f32(hi);      // exact
-    mid = f32_to_bf16_bits(r1);
-    const float r2 = r1 - bf16_bits_to_f32(mid);    // exact, <= 8 significant bits
-    lo = f32_to_bf16_bits(r2);                      // exact
+// Exact three-term split of two fp32 weights, w = hi + mid + lo, by
+// truncation: hi keeps the upper 16 bits of w (sign, exponent and the top 7
+// stored significand bits), mid the upper 16 bits of the residual w - hi
+// (exact, at most 16 significant bits), and lo = (w - hi) - mid, which is
+// exact and has at most 8 significant bits, so it is a bf16 value too. A
+// term's bf16 encoding is its upper 16 bits; the pair is packed with a in the
+// low half, b in the high half (bf16 elements 2j and 2j+1 of a vector).
+__device__ __forceinline__ void split3x2(float a, float b, unsigned &hi, unsigned &mid,
+                                         unsigned &lo) {
+    const unsigned ha = __float_as_uint(a) & 0xffff0000u, hb = __float_as_uint(b) & 0xffff0000u;
+    const float ra = a - __uint_as_float(ha), rb = b - __uint_as_float(hb);
+    const unsigned ma = __float_as_uint(ra) & 0xffff0000u, mb = __float_as_uint(rb) & 0xffff0000u;
+    const float la = ra - __uint_as_float(ma), lb = rb - __uint_as_float(mb);
+    hi = (ha >> 16) | hb;
+    mid = (ma >> 16) | mb;
+    lo = (__float_as_uint(la) >> 16) | (__float_as_uint(lb) & 0xffff0000u);
+}
+
+// Split of 8 consecutive weights (w0 = elements 0-3, w1 = elements 4-7).
+__device__ __forceinline__ void split8(const f32x4 &w0, const f32x4 &w1, u32x4 &hi, u32x4 &mid,
+                                       u32x4 &lo) {
+    unsigned h[4], m[4], l[4];
+    split3x2(w0[0], w0[1], h[0], m[0], l[0]);
+    split3x2(w0[2], w0[3], h[1], m[1], l[1]);
+    split3x2(w1[0], w1[1], h[2], m[2], l[2]);
+    split3x2(w1[2], w1[3], h[3], m[3], l[3]);
+    hi = u32x4{h[0], h[1], h[2], h[3]};
+    mid = u32x4{m[0], m[1], m[2], m[3]};
+    lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
 // Top-k of one token's scores held by a group of G lanes (lane g of the
@@ -110,18 +132,11 @@ __global__ __launch_bounds__(256) void split_router_weights_kernel(const float *
         w0 = *reinterpret_cast<const f32x4 *>(wg + (int64_t)e * d + i);
         w1 = *reinterpret_cast<const f32x4 *>(wg + (int64_t)e * d + i + 4);
     }
-    u16x8 hi, mid, lo;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        unsigned short h, m, l;
-        split3(w0[q], h, m, l);
-        hi[q] = h; mid[q] = m; lo[q] = l;
-        split3(w1[q], h, m, l);
-        hi[q + 4] = h; mid[q + 4] = m; lo[q + 4] = l;
-    }
-    *reinterpret_cast<u16x8 *>(wsp + (int64_t)e * d + i) = hi;
-    *reinterpret_cast<u16x8 *>(wsp + ((int64_t)Ep + e) * d + i) = mid;
-    *reinterpret_cast<u16x8 *>(wsp + ((int64_t)2 * Ep + e) * d + i) = lo;
+    u32x4 hi, mid, lo;
+    split8(w0, w1, hi, mid, lo);
+    *reinterpret_cast<u32x4 *>(wsp + (int64_t)e * d + i) = hi;
+    *reinterpret_cast<u32x4 *>(wsp + ((int64_t)Ep + e) * d + i) = mid;
+    *reinterpret_cast<u32x4 *>(wsp + ((int64_t)2 * Ep + e) * d + i) = lo;
 }
 
 // Ranking of one token per G-lane group from precomputed partial scores
@@ -231,15 +246,9 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const bool w_ok = k_ok && (nt * 16 + row < E);
-                u16x8 hi, mid, lo;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    unsigned short h, m, l;
-                    split3(w_ok ? w0[u][nt][i] : 0.f, h, m, l);
-                    hi[i] = h; mid[i] = m; lo[i] = l;
-                    split3(w_ok ? w1[u][nt][i] : 0.f, h, m, l);
-                    hi[i + 4] = h; mid[i + 4] = m; lo[i + 4] = l;
-                }
+                const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+                u32x4 hi, mid, lo;
+                split8(w_ok ? w0[u][nt] : zf, w_ok ? w1[u][nt] : zf, hi, mid, lo);
                 acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, hi), acc[nt], 0, 0, 0);
                 acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, mid), acc[nt], 0, 0, 0);
                 acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, lo), acc[nt], 0, 0, 0);

@@ -83,6 +83,7 @@ def cpu_baseline(wl, target_s=15.0):
     t_route = time.perf_counter() - t0
 
     rng = np.random.default_rng(0)
+    bup, bdown = wl.b_up(), wl.b_down()
     # experts' weights as float64, regenerated once and excluded from timing
     def ffn(rows):
         y = np.zeros((len(rows), wl.k, wl.d))
@@ -92,7 +93,9 @@ def cpu_baseline(wl, target_s=15.0):
             r_pos, j_pos = np.nonzero((sel_i == e) & (sel_s >= 0))
             wu, wd = wl.as_f64(wl.w_up(int(e))), wl.as_f64(wl.w_down(int(e)))
             a = time.perf_counter()
-            y[r_pos, j_pos] = oracle.expert_rows(x64, rows[r_pos], wu, wd)
+            bu = None if bup is None else bup[int(e)].astype(np.float64)
+            bd = None if bdown is None else bdown[int(e)].astype(np.float64)
+            y[r_pos, j_pos] = oracle.expert_rows(x64, rows[r_pos], wu, wd, wl.cfg.act, bu, bd)
             t += time.perf_counter() - a
         a = time.perf_counter()
         oracle.combine(gate[rows], slot[rows], y)

@@ -44,7 +44,8 @@ def lib():
         L.oracle_capacity.restype = _i64
         L.oracle_assign.argtypes = [_i64, _i64, _i32, _i64, _ip, _ip, _ip]
         L.oracle_assign.restype = None
-        L.oracle_expert_rows.argtypes = [_i64, _i64, _i64, _lp, _dp, _dp, _dp, _dp, _dp]
+        L.oracle_expert_rows.argtypes = [_i64, _i64, _i64, _lp, _dp, _dp, _dp, _i32, _dp, _dp,
+                                         _dp, _dp]
         L.oracle_expert_rows.restype = None
         L.oracle_combine.argtypes = [_i64, _i64, _i32, _dp, _ip, _dp, _dp]
         L.oracle_combine.restype = None
@@ -101,21 +102,33 @@ def assign(idx: np.ndarray, E: int, C: int):
     return slot, used
 
 
+ACTS = {"relu": 0, "gelu": 1}
+
+
 def expert_rows(x64: np.ndarray, tokens: Sequence[int], wup64: np.ndarray,
-                wdown64: np.ndarray) -> np.ndarray:
-    """One expert's output y [n,d] for the listed token rows of x."""
+                wdown64: np.ndarray, act: str = "relu", bup64: Optional[np.ndarray] = None,
+                bdown64: Optional[np.ndarray] = None) -> np.ndarray:
+    """One expert's output y [n,d] for the listed token rows of x (ReLU and no
+    biases as on page 1; GELU and biases as in the nanoMoE slides' expert)."""
     x64 = _c(x64, np.float64)
     tokens = _c(tokens, np.int64)
     wup64 = _c(wup64, np.float64)
     wdown64 = _c(wdown64, np.float64)
     d = x64.shape[1]
     d_ff = wup64.shape[0]
+    bup64 = None if bup64 is None else _c(bup64, np.float64)
+    bdown64 = None if bdown64 is None else _c(bdown64, np.float64)
+    if bup64 is not None and bup64.shape != (d_ff,):
+        raise ValueError("b_up must be [d_ff]")
+    if bdown64 is not None and bdown64.shape != (d,):
+        raise ValueError("b_down must be [d]")
     n = len(tokens)
     y = np.empty((n, d), np.float64)
     if n:
         hbuf = np.empty((threads() + 1) * d_ff, np.float64)
         lib().oracle_expert_rows(d, d_ff, n, _ptr(tokens, _lp), _ptr(x64, _dp),
-                                 _ptr(wup64, _dp), _ptr(wdown64, _dp), _ptr(y, _dp),
+                                 _ptr(wup64, _dp), _ptr(wdown64, _dp), ACTS[act],
+                                 _ptr(bup64, _dp), _ptr(bdown64, _dp), _ptr(y, _dp),
                                  _ptr(hbuf, _dp))
     return y
 
@@ -163,10 +176,13 @@ def forward(wl, rows: Optional[Sequence[int]] = None, want_y: bool = False) -> R
     # group the kept assignments of the selected rows by expert
     sel_idx = idx[rows]
     sel_slot = slot[rows]
+    bup, bdown = wl.b_up(), wl.b_down()
     for e in np.unique(sel_idx[sel_slot >= 0]):
         r_pos, j_pos = np.nonzero((sel_idx == e) & (sel_slot >= 0))
         ye = expert_rows(x64, rows[r_pos], wl.as_f64(wl.w_up(int(e))),
-                         wl.as_f64(wl.w_down(int(e))))
+                         wl.as_f64(wl.w_down(int(e))), wl.cfg.act,
+                         None if bup is None else bup[int(e)].astype(np.float64),
+                         None if bdown is None else bdown[int(e)].astype(np.float64))
         y[r_pos, j_pos] = ye
     out = combine(gate[rows], slot[rows], y)
     return Result(N=N, E=E, k=k, C=C, scores=scores, idx=idx, gate=gate, slot=slot,

@@ -122,12 +122,24 @@ void oracle_assign(int64_t N, int64_t E, int32_t k, int64_t C,
         used[e] = (int32_t)(count[e] < C ? count[e] : C);
 }
 
+/* [P2 slide 32] the nanoMoE expert's activation, torch's default GELU:
+ * x * Phi(x) with Phi the standard normal distribution function,
+ * Phi(x) = (1 + erf(x / sqrt(2))) / 2 (C library erf, double).            */
+static double oracle_gelu(double z)
+{
+    return 0.5 * z * (1.0 + erf(z * 0.70710678118654752440));
+}
+
 /* [P1 STEP 8-10] one expert on a list of its tokens: for each listed token
  * row x_t, z = W_up x_t, h = ReLU(z), y = W_down h. W_up is [d_ff, d] and
  * W_down is [d, d_ff], row-major. y is [n, d]. hbuf must hold
- * (OpenMP team size) * d_ff doubles.                                        */
+ * (OpenMP team size) * d_ff doubles.
+ * [P2 slide 32] the slides' expert variant: z gets the bias bup[f] before
+ * the activation, which is GELU when act == 1, and y gets bdown[o] (either
+ * bias may be NULL: none).                                                  */
 void oracle_expert_rows(int64_t d, int64_t d_ff, int64_t n, const int64_t *tokens,
                         const double *x, const double *Wup, const double *Wdown,
+                        int32_t act, const double *bup, const double *bdown,
                         double *y, double *hbuf)
 {
     #pragma omp parallel for schedule(dynamic, 1)
@@ -144,7 +156,9 @@ void oracle_expert_rows(int64_t d, int64_t d_ff, int64_t n, const int64_t *token
             const double *w = Wup + f * d;
             for (int64_t i = 0; i < d; ++i)
                 z += w[i] * xt[i];
-            h[f] = z > 0.0 ? z : 0.0;
+            if (bup)
+                z += bup[f];
+            h[f] = act == 1 ? oracle_gelu(z) : (z > 0.0 ? z : 0.0);
         }
         double *yr = y + r * d;
         for (int64_t o = 0; o < d; ++o) {
@@ -152,6 +166,8 @@ void oracle_expert_rows(int64_t d, int64_t d_ff, int64_t n, const int64_t *token
             const double *w = Wdown + o * d_ff;
             for (int64_t f = 0; f < d_ff; ++f)
                 acc += w[f] * h[f];
+            if (bdown)
+                acc += bdown[o];
             yr[o] = acc;
         }
     }

@@ -40,7 +40,7 @@ import numpy as np
 SEPARATION = 1e-4
 
 # spawn_key namespaces of the random streams
-_S_X, _S_WG, _S_NOISE, _S_RESAMPLE, _S_WUP, _S_WDOWN = range(6)
+_S_X, _S_WG, _S_NOISE, _S_RESAMPLE, _S_WUP, _S_WDOWN, _S_BUP, _S_BDOWN = range(8)
 
 
 # --------------------------------------------------------------------------
@@ -82,6 +82,8 @@ class Config:
     B: int = 0
     T: int = 0
     description: str = ""
+    act: str = "relu"      # expert activation: "relu" (page 1) or "gelu" (nanoMoE slide 32)
+    bias_std: float = 0.0  # std of the fp32 expert biases (nanoMoE slide 32); 0 -> no biases
 
     @property
     def has_noise(self) -> bool:
@@ -109,6 +111,12 @@ CONFIGS = {
     "finegrained": Config("finegrained", N=8192, d=7168, E=256, k=8, d_ff=2048, dtype="bf16",
                           cf=1.5, seed=20265,
                           description="fine-grained: 8192 tokens, d=7168, E=256, k=8, d_ff=2048"),
+    # the nanoMoE slides' own expert (slide 32): GELU and biases, nanoMoE shape
+    "nanomoe_gelu": Config("nanomoe_gelu", N=2048, B=8, T=256, d=768, E=8, k=2, d_ff=3072,
+                           dtype="bf16", cf=1.25, sigma=1.0, seed=20268, act="gelu",
+                           bias_std=0.02,
+                           description="nanoMoE-shaped with the slides' GELU expert and "
+                                       "biases: 2048 tokens, d=768, E=8, k=2, d_ff=3072, bf16"),
 }
 
 #: Benchmark-table order of the five layer shapes.
@@ -222,6 +230,20 @@ class Workload:
         a *= np.float32(self.cfg.w_std)
         return _cast(a, self.cfg.dtype)
 
+    def b_up(self) -> Optional[np.ndarray]:
+        """Up-projection biases [E, d_ff] fp32, or None (nanoMoE slide 32)."""
+        if self.cfg.bias_std == 0.0:
+            return None
+        a = _rng(self.expert_seed, _S_BUP).standard_normal((self.E, self.d_ff), dtype=np.float32)
+        return a * np.float32(self.cfg.bias_std)
+
+    def b_down(self) -> Optional[np.ndarray]:
+        """Down-projection biases [E, d] fp32, or None."""
+        if self.cfg.bias_std == 0.0:
+            return None
+        a = _rng(self.expert_seed, _S_BDOWN).standard_normal((self.E, self.d), dtype=np.float32)
+        return a * np.float32(self.cfg.bias_std)
+
     def experts(self, which: str, threads: int = 8):
         """Yield (e, array) for every expert, generated on a thread pool in order."""
         fn = self.w_up if which == "up" else self.w_down
@@ -334,9 +356,12 @@ def capacity_example() -> Workload:
 
 def custom(name: str, N: int, d: int, E: int, k: int, d_ff: int, dtype: str, cf: float,
            sigma: float = 0.0, bias0: float = 0.0, seed: int = 1, w_std: float = 0.05,
-           wg_std: float = 0.0) -> Workload:
+           wg_std: float = 0.0, act: str = "relu", bias_std: float = 0.0) -> Workload:
     """A seeded workload of any shape (test cases: ragged tails, edge cases)."""
+    if act not in ("relu", "gelu"):
+        raise ValueError("act must be 'relu' or 'gelu'")
     cfg = Config(name, N=N, d=d, E=E, k=k, d_ff=d_ff, dtype=dtype, cf=cf, sigma=sigma,
-                 bias0=bias0, seed=seed, w_std=w_std, wg_std=wg_std)
+                 bias0=bias0, seed=seed, w_std=w_std, wg_std=wg_std, act=act,
+                 bias_std=bias_std)
     return make(cfg)
 

@@ -326,3 +326,61 @@ def test_drops_fill_capacity_in_order():
         kept = [(j, t) for (j, t) in order if slot[t, j] >= 0]
         assert kept == order[:C] if len(order) > C else kept == order
         assert used[e] == min(len(order), C)
+
+
+# ----------------------------------------------------------------------------
+# the nanoMoE slides' expert variant (slide 32): biases and GELU
+# ----------------------------------------------------------------------------
+#: the standard normal distribution function at tabulated points
+PHI = {1.0: 0.8413447460685429, -1.0: 0.15865525393145707, 2.0: 0.9772498680518208,
+       0.5: 0.6914624612740131, -3.0: 0.0013498980316301035}
+
+
+def _one(z, act, bup=None, bdown=None):
+    """A 1 -> 1 -> 1 expert with unit weights on the scalar input z."""
+    b1 = None if bup is None else np.array([bup])
+    b2 = None if bdown is None else np.array([bdown])
+    return oracle.expert_rows(np.array([[z]]), [0], np.eye(1), np.eye(1), act, b1, b2)[0, 0]
+
+
+def test_gelu_is_x_times_the_normal_cdf():
+    """torch's default GELU (slide 32) is x * Phi(x): checked at the table values."""
+    for z, phi in PHI.items():
+        assert _one(z, "gelu") == pytest.approx(z * phi, rel=1e-14, abs=1e-300)
+    assert _one(0.0, "gelu") == 0.0
+
+
+def test_gelu_odd_part_is_the_identity():
+    """Phi(x) + Phi(-x) = 1 gives GELU(x) - GELU(-x) = x."""
+    for z in np.random.default_rng(31).standard_normal(50) * 3:
+        assert _one(z, "gelu") - _one(-z, "gelu") == pytest.approx(z, rel=1e-14, abs=1e-15)
+
+
+def test_biases_enter_before_and_after_the_activation():
+    """Identity experts (d_ff = d, W = I) with ReLU and x + b_up > 0 give
+    y = x + b_up + b_down; with GELU, y = GELU(x + b_up) + b_down."""
+    rng = np.random.default_rng(32)
+    d = 5
+    x = np.abs(rng.standard_normal((7, d))) + 0.1
+    bup = np.abs(rng.standard_normal(d))
+    bdown = rng.standard_normal(d)
+    y = oracle.expert_rows(x, np.arange(7), np.eye(d), np.eye(d), "relu", bup, bdown)
+    np.testing.assert_allclose(y, x + bup + bdown, rtol=1e-15, atol=1e-15)
+    # GELU: 0.5 + 0.5 = 1 and -4 + 1 = -3 land on tabulated points
+    assert _one(0.5, "gelu", 0.5, 0.25) == pytest.approx(PHI[1.0] + 0.25, rel=1e-14)
+    assert _one(-4.0, "gelu", 1.0, -1.0) == pytest.approx(-3.0 * PHI[-3.0] - 1.0, rel=1e-14)
+
+
+@pytest.mark.parametrize("act,seed", [("gelu", 41), ("relu", 42), ("gelu", 43)])
+def test_expert_variant_equals_bruteforce_without_drops(act, seed):
+    """Full layer with biases (and GELU) against the all-experts brute force."""
+    wl = W.custom("bfv", N=19, d=6, E=5, k=2, d_ff=11, dtype="f32", cf=5.0, sigma=0.4,
+                  seed=seed, w_std=0.5, wg_std=0.7, act=act, bias_std=0.3)
+    assert wl.b_up().shape == (5, 11) and wl.b_down().shape == (5, 6)
+    r = oracle.forward(wl)
+    assert r.drops == 0
+    x64, wg64, n64, wups, wdowns = _bf_inputs(wl)
+    ref, _, order = BF.layer(x64, wg64, n64, wl.k, wups, wdowns, act,
+                             wl.b_up().astype(np.float64), wl.b_down().astype(np.float64))
+    np.testing.assert_array_equal(r.idx, order)
+    assert np.abs(r.out - ref).max() <= 1e-12 * max(np.abs(ref).max(), 1.0)

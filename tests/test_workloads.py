@@ -64,3 +64,14 @@ def test_skewed_layer_sends_sixty_percent_to_expert0():
     slot, used = oracle.assign(idx, wl.E, C)
     assert C == 2048 and used[0] == C
     assert 8000 < int((slot < 0).sum()) < 13000
+
+
+def test_expert_variant_workload():
+    """The slides' expert variant: GELU, fp32 biases from their own streams."""
+    wl = W.make("nanomoe_gelu")
+    assert wl.cfg.act == "gelu" and (wl.N, wl.d, wl.E, wl.k, wl.d_ff) == (2048, 768, 8, 2, 3072)
+    bu, bd = wl.b_up(), wl.b_down()
+    assert bu.dtype == np.float32 and bu.shape == (8, 3072) and bd.shape == (8, 768)
+    np.testing.assert_array_equal(bu, wl.b_up())          # deterministic
+    assert 0.015 < float(bu.std()) < 0.025
+    assert W.make("nanomoe").b_up() is None

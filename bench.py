@@ -126,7 +126,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="nanomoe",
-                    choices=["nanomoe", "mixtral", "skew", "finegrained", "tiny"])
+                    choices=["nanomoe", "mixtral", "skew", "finegrained", "tiny", "nanomoe_gelu"])
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -152,7 +152,8 @@ def main():
         f"{cfg.dtype} cf={cfg.cf}")
     dev = D.upload(wl, keep_host=not args.no_cpu_baseline)
     fwd = B.Forward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
-                    cfg.cf, export=True)
+                    cfg.cf, export=True, act=dev["act"],
+                    b_up=dev["b_up"], b_down=dev["b_down"])
 
     for _ in range(args.warmup):
         fwd()
@@ -194,15 +195,19 @@ def main():
     p = B._ptr
     rws = B.alloc_workspace(B.router_workspace_size(wl.N, wl.d, wl.E, x.dtype))
     ews = B.alloc_workspace(B.expert_workspace_size(x.dtype))
+    eo = B.ExpertOpts(dev["act"], dev["b_up"], dev["b_down"])   # the workload's expert
+    opts = eo.ref()
     stages = {
         "router": lambda: L.moe_router(r(dx), r(dg), r(dn) if dn else None, wl.k, p(idx),
                                        p(gate), p(rws), rws.numel(), s_),
         "dispatch": lambda: L.moe_dispatch(wl.N, wl.E, wl.k, C, p(idx), p(slot), p(usedt),
                                            p(slot_token), p(tiles), s_),
-        "expert_up": lambda: L.moe_expert_up(r(dx), r(du), wl.k, C, p(usedt), p(slot_token),
-                                             p(tiles), p(H), p(ews), ews.numel(), s_),
-        "expert_down": lambda: L.moe_expert_down(wl.N, r(dd), wl.k, C, p(usedt), p(slot_token),
-                                                 p(tiles), p(H), p(Y), p(ews), ews.numel(), s_),
+        "expert_up": lambda: L.moe_expert_up_ex(r(dx), r(du), opts, wl.k, C, p(usedt),
+                                                p(slot_token), p(tiles), p(H), p(ews),
+                                                ews.numel(), s_),
+        "expert_down": lambda: L.moe_expert_down_ex(wl.N, r(dd), opts, wl.k, C, p(usedt),
+                                                    p(slot_token), p(tiles), p(H), p(Y), p(ews),
+                                                    ews.numel(), s_),
         "combine": lambda: L.moe_combine(wl.N, wl.d, wl.k, p(Y), p(gate), p(slot), r(do), s_),
     }
     st_ms = {}

@@ -119,6 +119,29 @@ int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *no
                 const moe_tensor *W_up, const moe_tensor *W_down, int k,
                 float capacity_factor, moe_tensor *out, moe_stats *stats);
 
+/* The expert variant of the nanoMoE slides (slide 32: a bias after each
+ * projection and GELU between them) for moe_forward_ex and moe_experts_ex.
+ * activation: MOE_ACT_RELU (page 1 STEP 9) or MOE_ACT_GELU, x * Phi(x) with
+ * Phi the standard normal distribution function (erf form), evaluated in
+ * fp32 before H is rounded; MOE_ERR_ARG for any other value.
+ * b_up:   [E, d_ff] MOE_F32 added to W_up[e] x before the activation, or NULL
+ * b_down: [E, d]    MOE_F32 added to W_down[e] h, or NULL
+ * Bias data are device pointers, 16-byte aligned (MOE_ERR_ALIGN), checked
+ * for dtype and extents like every other tensor. Dropout (training only)
+ * is not applied. */
+enum { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1 };
+typedef struct {
+    int32_t activation;
+    const moe_tensor *b_up;
+    const moe_tensor *b_down;
+} moe_expert_opts;
+
+/* moe_forward with the expert variant above; opts NULL is moe_forward. */
+int moe_forward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                   const moe_tensor *W_up, const moe_tensor *W_down,
+                   const moe_expert_opts *opts, int k, float capacity_factor, moe_tensor *out,
+                   moe_stats *stats);
+
 /* Bytes of workspace moe_forward needs for these sizes (0 on invalid sizes). */
 size_t moe_workspace_size(int64_t N, int64_t d, int64_t E, int64_t d_ff, int k,
                           float capacity_factor, int32_t dtype);
@@ -184,6 +207,25 @@ int moe_experts(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W
                 int k, int64_t capacity, const int32_t *used, const int32_t *slot_token,
                 const int32_t *tiles, void *H, float *Y, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/* moe_experts with the expert variant of moe_expert_opts (NULL: ReLU, no
+ * biases). */
+int moe_experts_ex(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W_down,
+                   const moe_expert_opts *opts, int k, int64_t capacity, const int32_t *used,
+                   const int32_t *slot_token, const int32_t *tiles, void *H, float *Y,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* moe_expert_up and moe_expert_down with the expert variant of
+ * moe_expert_opts: the up product adds b_up and applies the activation, the
+ * down product adds b_down (b_up and the activation are ignored there). */
+int moe_expert_up_ex(const moe_tensor *x, const moe_tensor *W_up, const moe_expert_opts *opts,
+                     int k, int64_t capacity, const int32_t *used, const int32_t *slot_token,
+                     const int32_t *tiles, void *H, void *workspace, size_t workspace_bytes,
+                     void *stream);
+int moe_expert_down_ex(int64_t N, const moe_tensor *W_down, const moe_expert_opts *opts, int k,
+                       int64_t capacity, const int32_t *used, const int32_t *slot_token,
+                       const int32_t *tiles, const void *H, float *Y, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* Bytes of expert scratch that enable the K-split on any device with up to
  * 256 compute units (0 for MOE_F32 and for an unknown dtype). */

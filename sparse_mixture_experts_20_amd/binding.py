@@ -22,7 +22,11 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK = 256, 16
 #: every function the header declares
 EXPORTS = ("moe_forward", "moe_workspace_size", "moe_capacity", "moe_error_string",
            "moe_router", "moe_router_workspace_size", "moe_dispatch", "moe_experts",
-           "moe_expert_up", "moe_expert_down", "moe_expert_workspace_size", "moe_combine")
+           "moe_expert_up", "moe_expert_down", "moe_expert_workspace_size", "moe_combine",
+           "moe_forward_ex", "moe_experts_ex", "moe_expert_up_ex", "moe_expert_down_ex")
+
+MOE_ACT_RELU, MOE_ACT_GELU = 0, 1
+ACTS = {"relu": MOE_ACT_RELU, "gelu": MOE_ACT_GELU}
 
 
 class MoeTensor(ctypes.Structure):
@@ -36,6 +40,11 @@ class MoeStats(ctypes.Structure):
                 ("topk_idx", ctypes.c_void_p), ("topk_gate", ctypes.c_void_p),
                 ("slot", ctypes.c_void_p), ("used_capacity", ctypes.c_void_p),
                 ("capacity", ctypes.c_int64)]
+
+
+class MoeExpertOpts(ctypes.Structure):
+    _fields_ = [("activation", ctypes.c_int32), ("b_up", ctypes.c_void_p),
+                ("b_down", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -61,6 +70,19 @@ def lib():
         L.moe_forward.argtypes = [_T, _T, _T, _T, _T, ctypes.c_int, ctypes.c_float, _T,
                                   ctypes.POINTER(MoeStats)]
         L.moe_forward.restype = ctypes.c_int
+        L.moe_forward_ex.argtypes = [_T, _T, _T, _T, _T, ctypes.POINTER(MoeExpertOpts),
+                                     ctypes.c_int, ctypes.c_float, _T, ctypes.POINTER(MoeStats)]
+        L.moe_forward_ex.restype = ctypes.c_int
+        L.moe_experts_ex.argtypes = [_T, _T, _T, ctypes.POINTER(MoeExpertOpts), ctypes.c_int,
+                                     _i64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.moe_experts_ex.restype = ctypes.c_int
+        L.moe_expert_up_ex.argtypes = [_T, _T, ctypes.POINTER(MoeExpertOpts), ctypes.c_int, _i64,
+                                       _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.moe_expert_up_ex.restype = ctypes.c_int
+        L.moe_expert_down_ex.argtypes = [_i64, _T, ctypes.POINTER(MoeExpertOpts), ctypes.c_int,
+                                         _i64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                         _vp]
+        L.moe_expert_down_ex.restype = ctypes.c_int
         L.moe_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
                                          ctypes.c_int32]
         L.moe_workspace_size.restype = ctypes.c_size_t
@@ -133,6 +155,29 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+class ExpertOpts:
+    """``moe_expert_opts`` for an activation name and optional fp32 bias tensors
+    (b_up [E, d_ff], b_down [E, d]); keeps the descriptors alive."""
+
+    def __init__(self, act: str = "relu", b_up: Optional[torch.Tensor] = None,
+                 b_down: Optional[torch.Tensor] = None):
+        if act not in ACTS:
+            raise ValueError("act must be 'relu' or 'gelu'")
+        self._d = (desc(b_up), desc(b_down))
+        self.c = MoeExpertOpts(ACTS[act],
+                               None if self._d[0] is None else ctypes.addressof(self._d[0]),
+                               None if self._d[1] is None else ctypes.addressof(self._d[1]))
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _opts(act, b_up, b_down):
+    if act == "relu" and b_up is None and b_down is None:
+        return None
+    return ExpertOpts(act, b_up, b_down)
+
+
 def capacity(N: int, E: int, k: int, capacity_factor: float) -> int:
     return int(lib().moe_capacity(N, E, k, capacity_factor))
 
@@ -156,7 +201,8 @@ class Stats:
 def forward(x: torch.Tensor, W_g: torch.Tensor, noise: Optional[torch.Tensor],
             W_up: torch.Tensor, W_down: torch.Tensor, k: int, capacity_factor: float,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-            export: bool = True, stream=None):
+            export: bool = True, stream=None, act: str = "relu",
+            b_up: Optional[torch.Tensor] = None, b_down: Optional[torch.Tensor] = None):
     """Run ``moe_forward``. Returns ``(out, Stats)``; with ``export=False`` the
     routing arrays stay in the workspace and Stats only carries the capacity."""
     N = x.numel() // x.shape[-1]
@@ -177,8 +223,13 @@ def forward(x: torch.Tensor, W_g: torch.Tensor, noise: Optional[torch.Tensor],
     st = MoeStats(_stream(stream), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                   _ptr(idx), _ptr(gate), _ptr(slot), _ptr(used), -1)
     dx, dg, dn, du, dd, do = desc(x), desc(W_g), desc(noise), desc(W_up), desc(W_down), desc(out)
-    rc = lib().moe_forward(_ref(dx), _ref(dg), _ref(dn), _ref(du), _ref(dd), k,
-                           capacity_factor, _ref(do), ctypes.byref(st))
+    o = _opts(act, b_up, b_down)
+    if o is None:
+        rc = lib().moe_forward(_ref(dx), _ref(dg), _ref(dn), _ref(du), _ref(dd), k,
+                               capacity_factor, _ref(do), ctypes.byref(st))
+    else:
+        rc = lib().moe_forward_ex(_ref(dx), _ref(dg), _ref(dn), _ref(du), _ref(dd), o.ref(), k,
+                                  capacity_factor, _ref(do), ctypes.byref(st))
     _check(rc, "moe_forward")
     return out, Stats(idx, gate, slot, used, int(st.capacity))
 
@@ -188,7 +239,7 @@ class Forward:
     timing loops measure only the enqueue of the kernels."""
 
     def __init__(self, x, W_g, noise, W_up, W_down, k, capacity_factor, out=None,
-                 export=False, stream=None):
+                 export=False, stream=None, act="relu", b_up=None, b_down=None):
         self.tensors = (x, W_g, noise, W_up, W_down)
         N, d = x.numel() // x.shape[-1], x.shape[-1]
         E, d_ff = W_up.shape[0], W_up.shape[1]
@@ -208,12 +259,18 @@ class Forward:
                               self.workspace.numel(), _ptr(self.idx), _ptr(self.gate),
                               _ptr(self.slot), _ptr(self.used), -1)
         self._args = [_ref(a) for a in self._d]
-        self._fn = lib().moe_forward
+        self._opts = _opts(act, b_up, b_down)
+        self._biases = (b_up, b_down)
+        self._fn = lib().moe_forward if self._opts is None else lib().moe_forward_ex
 
     def __call__(self):
         a = self._args
-        rc = self._fn(a[0], a[1], a[2], a[3], a[4], self.k, self.cf, a[5],
-                      ctypes.byref(self.stats))
+        if self._opts is None:
+            rc = self._fn(a[0], a[1], a[2], a[3], a[4], self.k, self.cf, a[5],
+                          ctypes.byref(self.stats))
+        else:
+            rc = self._fn(a[0], a[1], a[2], a[3], a[4], self._opts.ref(), self.k, self.cf, a[5],
+                          ctypes.byref(self.stats))
         if rc != 0:
             raise MoeError(rc, "moe_forward")
         return self.out
@@ -273,7 +330,7 @@ def _ws_args(ws):
 
 
 def experts(x, W_up, W_down, k, capacity_, used, slot_token, tiles, H=None, Y=None,
-            workspace="auto", stream=None):
+            workspace="auto", stream=None, act="relu", b_up=None, b_down=None):
     """Returns (H [E, min(C,N), d_ff] in x's dtype, Y [N*k, d] fp32)."""
     N, d = x.numel() // x.shape[-1], x.shape[-1]
     E, d_ff = W_up.shape[0], W_up.shape[1]
@@ -286,29 +343,49 @@ def experts(x, W_up, W_down, k, capacity_, used, slot_token, tiles, H=None, Y=No
     if not slot_token.is_contiguous():
         raise ValueError("slot_token must be a contiguous [E, min(C, N)] tensor")
     wp, wn = _ws_args(_expert_ws(workspace, x.dtype, x.device))
-    _check(lib().moe_experts(_ref(dx), _ref(du), _ref(dd), k, capacity_, _ptr(used),
-                             _ptr(slot_token), _ptr(tiles), _ptr(H), _ptr(Y), wp, wn,
-                             _stream(stream)),
-           "moe_experts")
+    o = _opts(act, b_up, b_down)
+    if o is None:
+        _check(lib().moe_experts(_ref(dx), _ref(du), _ref(dd), k, capacity_, _ptr(used),
+                                 _ptr(slot_token), _ptr(tiles), _ptr(H), _ptr(Y), wp, wn,
+                                 _stream(stream)),
+               "moe_experts")
+    else:
+        _check(lib().moe_experts_ex(_ref(dx), _ref(du), _ref(dd), o.ref(), k, capacity_,
+                                    _ptr(used), _ptr(slot_token), _ptr(tiles), _ptr(H), _ptr(Y),
+                                    wp, wn, _stream(stream)),
+               "moe_experts_ex")
     return H, Y
 
 
 def expert_up(x, W_up, k, capacity_, used, slot_token, tiles, H, workspace="auto",
-              stream=None):
+              stream=None, act="relu", b_up=None):
     dx, du = desc(x), desc(W_up)
     wp, wn = _ws_args(_expert_ws(workspace, x.dtype, x.device))
-    _check(lib().moe_expert_up(_ref(dx), _ref(du), k, capacity_, _ptr(used), _ptr(slot_token),
-                               _ptr(tiles), _ptr(H), wp, wn, _stream(stream)), "moe_expert_up")
+    o = _opts(act, b_up, None)
+    if o is None:
+        rc = lib().moe_expert_up(_ref(dx), _ref(du), k, capacity_, _ptr(used), _ptr(slot_token),
+                                 _ptr(tiles), _ptr(H), wp, wn, _stream(stream))
+    else:
+        rc = lib().moe_expert_up_ex(_ref(dx), _ref(du), o.ref(), k, capacity_, _ptr(used),
+                                    _ptr(slot_token), _ptr(tiles), _ptr(H), wp, wn,
+                                    _stream(stream))
+    _check(rc, "moe_expert_up")
     return H
 
 
 def expert_down(N, W_down, k, capacity_, used, slot_token, tiles, H, Y, workspace="auto",
-                stream=None):
+                stream=None, b_down=None):
     dd = desc(W_down)
     wp, wn = _ws_args(_expert_ws(workspace, W_down.dtype, W_down.device))
-    _check(lib().moe_expert_down(N, _ref(dd), k, capacity_, _ptr(used), _ptr(slot_token),
-                                 _ptr(tiles), _ptr(H), _ptr(Y), wp, wn, _stream(stream)),
-           "moe_expert_down")
+    o = _opts("relu", None, b_down)
+    if o is None:
+        rc = lib().moe_expert_down(N, _ref(dd), k, capacity_, _ptr(used), _ptr(slot_token),
+                                   _ptr(tiles), _ptr(H), _ptr(Y), wp, wn, _stream(stream))
+    else:
+        rc = lib().moe_expert_down_ex(N, _ref(dd), o.ref(), k, capacity_, _ptr(used),
+                                      _ptr(slot_token), _ptr(tiles), _ptr(H), _ptr(Y), wp, wn,
+                                      _stream(stream))
+    _check(rc, "moe_expert_down")
     return Y
 
 

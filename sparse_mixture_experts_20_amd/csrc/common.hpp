@@ -11,6 +11,7 @@ constexpr int kWave = 64;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxQ = kMaxExperts / kWave;   // router scores per lane
 constexpr int kFusedMaxExperts = 32;          // larger routers use the GEMM path
+constexpr int kActRelu = 0, kActGelu = 1;     // expert activations (values of the C ABI)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -69,16 +70,18 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 // device with up to 256 CUs.
 constexpr size_t kSplitWorkspaceBytes = (size_t)256 * 256 * 256 * sizeof(float);
 size_t split_workspace_bytes();
+// act: kActRelu or kActGelu (up product); b_up [E, d_ff] / b_down [E, d]
+// fp32 biases or NULL.
 hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t d,
                             int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                             const int32_t *slot_token, const int32_t *tiles, void *H,
-                            int64_t rows_per_expert, void *part, size_t part_bytes,
-                            hipStream_t s);
+                            int64_t rows_per_expert, void *part, size_t part_bytes, int act,
+                            const float *b_up, hipStream_t s);
 hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int64_t d,
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, float *Y,
                               int64_t rows_per_expert, void *part, size_t part_bytes,
-                              hipStream_t s);
+                              const float *b_down, hipStream_t s);
 
 // Y[rows, Nout] (fp32) = A[rows, K] * W[Nout, K]^T, bf16 operands.
 hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, int64_t K,

@@ -57,6 +57,34 @@ __device__ __forceinline__ unsigned lds_off(const void *p) {
     return (unsigned)(uintptr_t)((__attribute__((address_space(3))) const void *)p);
 }
 
+// GELU of the nanoMoE slides' expert (slide 32): z * Phi(z), Phi(z) =
+// (1 + erf(z / sqrt 2)) / 2, with erf from Abramowitz and Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26: for u >= 0,
+// 1 - erf(u) = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-u^2),
+// t = 1 / (1 + p u), with absolute error below 1.5e-7 (far below the bf16
+// rounding of H that follows). For z < 0 the complement is used directly, so
+// small GELU values keep their relative accuracy.
+__device__ __forceinline__ float gelu(float z) {
+    const float u = fabsf(z) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, u, 1.0f));
+    const float poly =
+        t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
+                         -0.284496736f),
+                 0.254829592f);
+    const float q = poly * __expf(-u * u);   // 1 - erf(u)
+    return 0.5f * z * (z >= 0.f ? 2.0f - q : q);
+}
+
+// Expert activation: ReLU (page 1 STEP 9) or GELU, chosen at compile time so
+// that the ReLU epilogue carries no trace of the other.
+template <bool GELU>
+__device__ __forceinline__ float activate(float z) {
+    if constexpr (GELU)
+        return gelu(z);
+    else
+        return fmaxf(z, 0.f);
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
 // LDS offset m0 + 16*l (one wave moves 1 KB). Issued in asm so that the
 // compiler's wait insertion does not treat every later LDS read as aliasing
@@ -138,6 +166,9 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // A into fp32 rows of Y (no gather, no schedule table, no split).
 // part: scratch for the split of the last round (NULL: no split), P: the
 // number of workgroups of this kernel that fit on the device at once.
+// act: activation of the up product (kActRelu, kActGelu); bias: [E, Nout]
+// fp32 added to the product before the activation (MODE 0) or to the output
+// row (MODE 1), or NULL. K-range partials take neither (the fix-up does).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BKT, int S, int MODE>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void expert_gemm_kernel(
@@ -145,7 +176,7 @@ void expert_gemm_kernel(
     int Nout, int E, int k, int ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
     unsigned short *__restrict__ H_out, float *__restrict__ Y_out, float *__restrict__ part,
-    int P) {
+    int P, int act, const float *__restrict__ bias) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int NTHR = NW * 64;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;   // wave tile
@@ -381,41 +412,58 @@ void expert_gemm_kernel(
                         *reinterpret_cast<f32x4 *>(dst + 4 * c) = v[c];
             } else if (MODE == 0) {
                 unsigned short *dst = H_out + srow * Nout + nb;
+                const float *bp = bias ? bias + (int64_t)e * Nout + nb : nullptr;
+                auto store_h = [&](auto use_gelu) {
 #pragma unroll
-                for (int h = 0; h < CPL / 8; ++h) {
-                    if (nb + 8 * h + 8 <= Nout) {
-                        u32x4 pk;
+                    for (int h = 0; h < CPL / 8; ++h) {
+                        if (nb + 8 * h + 8 <= Nout) {
+                            f32x4 z0 = v[2 * h], z1 = v[2 * h + 1];
+                            if (bp) {
+                                z0 += *reinterpret_cast<const f32x4 *>(bp + 8 * h);
+                                z1 += *reinterpret_cast<const f32x4 *>(bp + 8 * h + 4);
+                            }
+                            u32x4 pk;
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const float lo = fmaxf(v[2 * h + c / 2][(c % 2) * 2], 0.f);
-                            const float hi = fmaxf(v[2 * h + c / 2][(c % 2) * 2 + 1], 0.f);
-                            pk[c] = (unsigned)f32_to_bf16_bits(lo) |
-                                    ((unsigned)f32_to_bf16_bits(hi) << 16);
+                            for (int c = 0; c < 4; ++c) {
+                                const f32x4 &z = c < 2 ? z0 : z1;
+                                const float lo = activate<decltype(use_gelu)::value>(z[(c % 2) * 2]);
+                                const float hi =
+                                    activate<decltype(use_gelu)::value>(z[(c % 2) * 2 + 1]);
+                                pk[c] = (unsigned)f32_to_bf16_bits(lo) |
+                                        ((unsigned)f32_to_bf16_bits(hi) << 16);
+                            }
+                            *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
                         }
-                        *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
                     }
-                }
+                };
+                if (act == kActGelu)
+                    store_h(std::true_type{});
+                else
+                    store_h(std::false_type{});
             } else {
                 const int64_t orow = MODE == 1 ? (int64_t)slot_token[srow] : (int64_t)r;
                 float *dst = Y_out + orow * Nout + nb;
+                const float *bp = MODE == 1 && bias ? bias + (int64_t)e * Nout + nb : nullptr;
 #pragma unroll
                 for (int c = 0; c < CPL / 4; ++c)
                     if (nb + 4 * c + 4 <= Nout)
-                        *reinterpret_cast<f32x4 *>(dst + 4 * c) = v[c];
+                        *reinterpret_cast<f32x4 *>(dst + 4 * c) =
+                            bp ? v[c] + *reinterpret_cast<const f32x4 *>(bp + 4 * c) : v[c];
             }
         }
     }
 }
 
 // Sum of the K-range partials of the cut tiles, in K order, then the same
-// epilogue as a whole tile (MODE 0: ReLU, bf16 H; MODE 1: fp32 row of Y).
+// epilogue as a whole tile (MODE 0: bias, activation, bf16 H; MODE 1: bias,
+// fp32 row of Y).
 // One workgroup per 16-row strip of a cut tile; 4 columns per thread.
 template <int BM, int BN, int BKT, int MODE>
 __global__ __launch_bounds__(256) void split_fixup_kernel(
     int K, int Nout, int E, int ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
     const float *__restrict__ part, int P, unsigned short *__restrict__ H_out,
-    float *__restrict__ Y_out) {
+    float *__restrict__ Y_out, int act, const float *__restrict__ bias) {
     constexpr int STRIPS = BM / 16;
     __shared__ int s_mt[kMaxExperts + 1];
     for (int i = threadIdx.x; i <= E; i += 256)
@@ -442,12 +490,16 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
         for (int s = 1; s < sp.nsplit; ++s)
             v += *reinterpret_cast<const f32x4 *>(src + (int64_t)s * BM * BN);
         const int64_t srow = (int64_t)e * ceff + r;
+        if (bias)
+            v += *reinterpret_cast<const f32x4 *>(bias + (int64_t)e * Nout + n);
         if (MODE == 0) {
+            if (act == kActGelu)
+                v = f32x4{gelu(v[0]), gelu(v[1]), gelu(v[2]), gelu(v[3])};
+            else
+                v = f32x4{fmaxf(v[0], 0.f), fmaxf(v[1], 0.f), fmaxf(v[2], 0.f), fmaxf(v[3], 0.f)};
             u32x2 pk;
-            pk[0] = (unsigned)f32_to_bf16_bits(fmaxf(v[0], 0.f)) |
-                    ((unsigned)f32_to_bf16_bits(fmaxf(v[1], 0.f)) << 16);
-            pk[1] = (unsigned)f32_to_bf16_bits(fmaxf(v[2], 0.f)) |
-                    ((unsigned)f32_to_bf16_bits(fmaxf(v[3], 0.f)) << 16);
+            pk[0] = (unsigned)f32_to_bf16_bits(v[0]) | ((unsigned)f32_to_bf16_bits(v[1]) << 16);
+            pk[1] = (unsigned)f32_to_bf16_bits(v[2]) | ((unsigned)f32_to_bf16_bits(v[3]) << 16);
             *reinterpret_cast<u32x2 *>(H_out + srow * Nout + n) = pk;
         } else {
             *reinterpret_cast<f32x4 *>(Y_out + (int64_t)slot_token[srow] * Nout + n) = v;
@@ -461,7 +513,8 @@ template <int MODE>
 __global__ __launch_bounds__(256) void experts_f32_kernel(
     const float *__restrict__ A_src, const float *__restrict__ W, int K, int Nout, int k,
     int ceff, const int32_t *__restrict__ used, const int32_t *__restrict__ slot_token,
-    float *__restrict__ H_out, float *__restrict__ Y_out) {
+    float *__restrict__ H_out, float *__restrict__ Y_out, int act,
+    const float *__restrict__ bias) {
     constexpr int TM = 64, TN = 64, TK = 16;
     __shared__ float As[TK][TM + 4];
     __shared__ float Bs[TK][TN + 4];
@@ -513,10 +566,11 @@ __global__ __launch_bounds__(256) void experts_f32_kernel(
             const int n = n0 + tc * 4 + j;
             if (n >= Nout)
                 continue;
+            const float z = bias ? acc[i][j] + bias[(int64_t)e * Nout + n] : acc[i][j];
             if (MODE == 0)
-                H_out[srow * Nout + n] = fmaxf(acc[i][j], 0.f);
+                H_out[srow * Nout + n] = act == kActGelu ? gelu(z) : fmaxf(z, 0.f);
             else
-                Y_out[(int64_t)slot_token[srow] * Nout + n] = acc[i][j];
+                Y_out[(int64_t)slot_token[srow] * Nout + n] = z;
         }
     }
 }
@@ -565,7 +619,8 @@ template <int BM, int BN, int WM, int WN, int MODE>
 hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_t K, int64_t Nout,
                         int E, int k, int64_t ceff, const int32_t *used,
                         const int32_t *slot_token, const int32_t *mt, unsigned short *H,
-                        float *Y, float *part, size_t part_bytes, hipStream_t s) {
+                        float *Y, float *part, size_t part_bytes, int act, const float *bias,
+                        hipStream_t s) {
     auto kern = expert_gemm_kernel<BM, BN, WM, WN, kBK, 2, MODE>;
     constexpr int NTHR = WM * WN * 64;
     static int resident[kMaxDevices];   // per device, filled on first use (0 = unset)
@@ -591,13 +646,13 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
                          (split ? (int64_t)(P + kXcds - 1) / kXcds * kXcds : 0);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHR), 0, s, A, W, (int)K, (int)Nout, E,
                        k, (int)ceff, used, slot_token, mt, H, Y, split ? part : nullptr,
-                       split ? P : 0);
+                       split ? P : 0, act, bias);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !split)
         return err;
     hipLaunchKernelGGL((split_fixup_kernel<BM, BN, kBK, MODE>), dim3((unsigned)(P * (BM / 16))),
                        dim3(256), 0, s, (int)K, (int)Nout, E, (int)ceff, used, slot_token, mt,
-                       (const float *)part, P, H, Y);
+                       (const float *)part, P, H, Y, act, bias);
     return hipGetLastError();
 }
 
@@ -605,16 +660,18 @@ template <int MODE>
 hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W, int64_t K,
                        int64_t Nout, int E, int k, int64_t ceff, const int32_t *used,
                        const int32_t *slot_token, const int32_t *tiles, unsigned short *H,
-                       float *Y, void *part, size_t part_bytes, hipStream_t s) {
+                       float *Y, void *part, size_t part_bytes, int act, const float *bias,
+                       hipStream_t s) {
     float *pf = static_cast<float *>(part);
     if (t == Tile::k256)
         return launch_tiles<256, 256, 2, 4, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
-                                                  tiles + E + 1, H, Y, pf, part_bytes, s);
+                                                  tiles + E + 1, H, Y, pf, part_bytes, act, bias,
+                                                  s);
     if (t == Tile::k128x64)
         return launch_tiles<128, 64, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
-                                                 tiles, H, Y, pf, part_bytes, s);
+                                                 tiles, H, Y, pf, part_bytes, act, bias, s);
     return launch_tiles<128, 128, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token, tiles,
-                                              H, Y, pf, part_bytes, s);
+                                              H, Y, pf, part_bytes, act, bias, s);
 }
 
 }  // namespace
@@ -631,15 +688,15 @@ hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, in
                        static_cast<const unsigned short *>(W), (int)K, (int)Nout, 1, 1, (int)rows,
                        (const int32_t *)nullptr, (const int32_t *)nullptr,
                        (const int32_t *)nullptr, (unsigned short *)nullptr, Y, (float *)nullptr,
-                       0);
+                       0, kActRelu, (const float *)nullptr);
     return hipGetLastError();
 }
 
 hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t d,
                             int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                             const int32_t *slot_token, const int32_t *tiles, void *H,
-                            int64_t rows_per_expert, void *part, size_t part_bytes,
-                            hipStream_t s) {
+                            int64_t rows_per_expert, void *part, size_t part_bytes, int act,
+                            const float *b_up, hipStream_t s) {
     if (ceff == 0)
         return hipSuccess;
     if (bf16)
@@ -647,12 +704,12 @@ hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t 
                               static_cast<const unsigned short *>(x),
                               static_cast<const unsigned short *>(w_up), d, d_ff, E, k, ceff,
                               used, slot_token, tiles, static_cast<unsigned short *>(H), nullptr,
-                              part, part_bytes, s);
+                              part, part_bytes, act, b_up, s);
     hipLaunchKernelGGL(experts_f32_kernel<0>,
                        dim3((unsigned)((d_ff + 63) / 64), (unsigned)((ceff + 63) / 64), E),
                        dim3(256), 0, s, static_cast<const float *>(x),
                        static_cast<const float *>(w_up), (int)d, (int)d_ff, k, (int)ceff, used,
-                       slot_token, static_cast<float *>(H), (float *)nullptr);
+                       slot_token, static_cast<float *>(H), (float *)nullptr, act, b_up);
     return hipGetLastError();
 }
 
@@ -660,19 +717,20 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, float *Y,
                               int64_t rows_per_expert, void *part, size_t part_bytes,
-                              hipStream_t s) {
+                              const float *b_down, hipStream_t s) {
     if (ceff == 0)
         return hipSuccess;
     if (bf16)
         return launch_gemm<1>(pick_tile(rows_per_expert, d, E),
                               static_cast<const unsigned short *>(H),
                               static_cast<const unsigned short *>(w_down), d_ff, d, E, k, ceff,
-                              used, slot_token, tiles, nullptr, Y, part, part_bytes, s);
+                              used, slot_token, tiles, nullptr, Y, part, part_bytes, kActRelu,
+                              b_down, s);
     hipLaunchKernelGGL(experts_f32_kernel<1>,
                        dim3((unsigned)((d + 63) / 64), (unsigned)((ceff + 63) / 64), E),
                        dim3(256), 0, s, static_cast<const float *>(H),
                        static_cast<const float *>(w_down), (int)d_ff, (int)d, k, (int)ceff, used,
-                       slot_token, (float *)nullptr, Y);
+                       slot_token, (float *)nullptr, Y, kActRelu, b_down);
     return hipGetLastError();
 }
 

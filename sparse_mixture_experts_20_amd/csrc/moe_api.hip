@@ -166,6 +166,41 @@ int check_router_args(const moe_tensor *x, const moe_tensor *W_g, const moe_tens
     return MOE_OK;
 }
 
+// Expert variant options: activation and fp32 biases [E, d_ff] / [E, d].
+struct ExpertOpts {
+    int act = moe::kActRelu;
+    const float *b_up = nullptr, *b_down = nullptr;
+};
+
+int check_bias(const moe_tensor *b, int64_t E, int64_t n, const float *&out) {
+    out = nullptr;
+    if (!b)
+        return MOE_OK;
+    if (b->dtype != MOE_F32)
+        return MOE_ERR_DTYPE;
+    if (b->ndim != 2 || b->shape[0] != E || b->shape[1] != n)
+        return MOE_ERR_SHAPE;
+    if (!b->data)
+        return MOE_ERR_NULL;
+    if (!aligned(b->data, 16))
+        return MOE_ERR_ALIGN;
+    out = static_cast<const float *>(b->data);
+    return MOE_OK;
+}
+
+int check_opts(const moe_expert_opts *o, int64_t E, int64_t d, int64_t d_ff, ExpertOpts &r) {
+    r = ExpertOpts{};
+    if (!o)
+        return MOE_OK;
+    if (o->activation != MOE_ACT_RELU && o->activation != MOE_ACT_GELU)
+        return MOE_ERR_ARG;
+    r.act = o->activation == MOE_ACT_GELU ? moe::kActGelu : moe::kActRelu;
+    int rc = check_bias(o->b_up, E, d_ff, r.b_up);
+    if (rc != MOE_OK)
+        return rc;
+    return check_bias(o->b_down, E, d, r.b_down);
+}
+
 // Optional expert scratch: NULL runs without the K-split; a non-NULL pointer
 // must be 256-byte aligned.
 int check_expert_ws(const void *ws) {
@@ -268,9 +303,10 @@ int moe_dispatch(int64_t N, int64_t E, int k, int64_t capacity, const int32_t *t
                                            slot_token, tiles, s));
 }
 
-int moe_expert_up(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t capacity,
-                  const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
-                  void *H, void *workspace, size_t workspace_bytes, void *stream) {
+static int expert_up_impl(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t capacity,
+                          const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
+                          void *H, void *workspace, size_t workspace_bytes, void *stream,
+                          const ExpertOpts &o) {
     if (!x || !W_up)
         return MOE_ERR_NULL;
     int64_t N, d;
@@ -300,14 +336,38 @@ int moe_expert_up(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t ca
     return hip_status(moe::launch_expert_up(bf16, x->data, W_up->data, d, d_ff, (int)E, k,
                                             m.ceff, used, slot_token, tiles, H,
                                             rows_per_expert(N, k, E, m.ceff), workspace,
-                                            workspace ? workspace_bytes : 0,
+                                            workspace ? workspace_bytes : 0, o.act, o.b_up,
                                             static_cast<hipStream_t>(stream)));
 }
 
-int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
-                    const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
-                    const void *H, float *Y, void *workspace, size_t workspace_bytes,
-                    void *stream) {
+int moe_expert_up(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t capacity,
+                  const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
+                  void *H, void *workspace, size_t workspace_bytes, void *stream) {
+    return expert_up_impl(x, W_up, k, capacity, used, slot_token, tiles, H, workspace,
+                          workspace_bytes, stream, ExpertOpts{});
+}
+
+int moe_expert_up_ex(const moe_tensor *x, const moe_tensor *W_up, const moe_expert_opts *opts,
+                     int k, int64_t capacity, const int32_t *used, const int32_t *slot_token,
+                     const int32_t *tiles, void *H, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    if (!x || !W_up)
+        return MOE_ERR_NULL;
+    if (W_up->ndim != 3)
+        return MOE_ERR_SHAPE;
+    ExpertOpts o;
+    const int64_t d = W_up->shape[2];
+    const int rc = check_opts(opts, W_up->shape[0], d, W_up->shape[1], o);
+    if (rc != MOE_OK)
+        return rc;
+    return expert_up_impl(x, W_up, k, capacity, used, slot_token, tiles, H, workspace,
+                          workspace_bytes, stream, o);
+}
+
+static int expert_down_impl(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
+                            const int32_t *used, const int32_t *slot_token,
+                            const int32_t *tiles, const void *H, float *Y, void *workspace,
+                            size_t workspace_bytes, void *stream, const ExpertOpts &o) {
     if (!W_down)
         return MOE_ERR_NULL;
     if (!valid_dtype(W_down->dtype))
@@ -334,14 +394,38 @@ int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity
     return hip_status(moe::launch_expert_down(bf16, H, W_down->data, d, d_ff, (int)E, k, m.ceff,
                                               used, slot_token, tiles, Y,
                                               rows_per_expert(N, k, E, m.ceff), workspace,
-                                              workspace ? workspace_bytes : 0,
+                                              workspace ? workspace_bytes : 0, o.b_down,
                                               static_cast<hipStream_t>(stream)));
 }
 
-int moe_experts(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W_down, int k,
-                int64_t capacity, const int32_t *used, const int32_t *slot_token,
-                const int32_t *tiles, void *H, float *Y, void *workspace,
-                size_t workspace_bytes, void *stream) {
+int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
+                    const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
+                    const void *H, float *Y, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    return expert_down_impl(N, W_down, k, capacity, used, slot_token, tiles, H, Y, workspace,
+                            workspace_bytes, stream, ExpertOpts{});
+}
+
+int moe_expert_down_ex(int64_t N, const moe_tensor *W_down, const moe_expert_opts *opts, int k,
+                       int64_t capacity, const int32_t *used, const int32_t *slot_token,
+                       const int32_t *tiles, const void *H, float *Y, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    if (!W_down)
+        return MOE_ERR_NULL;
+    if (W_down->ndim != 3)
+        return MOE_ERR_SHAPE;
+    ExpertOpts o;
+    const int rc = check_opts(opts, W_down->shape[0], W_down->shape[1], W_down->shape[2], o);
+    if (rc != MOE_OK)
+        return rc;
+    return expert_down_impl(N, W_down, k, capacity, used, slot_token, tiles, H, Y, workspace,
+                            workspace_bytes, stream, o);
+}
+
+int moe_experts_ex(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W_down,
+                   const moe_expert_opts *opts, int k, int64_t capacity, const int32_t *used,
+                   const int32_t *slot_token, const int32_t *tiles, void *H, float *Y,
+                   void *workspace, size_t workspace_bytes, void *stream) {
     if (!x || !W_up || !W_down)
         return MOE_ERR_NULL;
     int64_t N, d;
@@ -354,9 +438,13 @@ int moe_experts(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W
     if (W_down->shape[0] != W_up->shape[0] || W_down->shape[1] != d ||
         W_down->shape[2] != W_up->shape[1])
         return MOE_ERR_SHAPE;
+    ExpertOpts o;
+    int rc = check_opts(opts, W_up->shape[0], d, W_up->shape[1], o);
+    if (rc != MOE_OK)
+        return rc;
     // validate both halves before enqueuing either
-    int rc = moe_expert_up(x, W_up, k, capacity, used, slot_token, tiles, nullptr, nullptr, 0,
-                           nullptr);
+    rc = expert_up_impl(x, W_up, k, capacity, used, slot_token, tiles, nullptr, nullptr, 0,
+                        nullptr, o);
     if (rc != MOE_OK && rc != MOE_ERR_NULL)
         return rc;
     if (N > 0 && (!H || !Y))
@@ -364,12 +452,20 @@ int moe_experts(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W
     rc = check_expert_ws(workspace);
     if (rc != MOE_OK)
         return rc;
-    rc = moe_expert_up(x, W_up, k, capacity, used, slot_token, tiles, H, workspace,
-                       workspace_bytes, stream);
+    rc = expert_up_impl(x, W_up, k, capacity, used, slot_token, tiles, H, workspace,
+                        workspace_bytes, stream, o);
     if (rc != MOE_OK)
         return rc;
-    return moe_expert_down(N, W_down, k, capacity, used, slot_token, tiles, H, Y, workspace,
-                           workspace_bytes, stream);
+    return expert_down_impl(N, W_down, k, capacity, used, slot_token, tiles, H, Y, workspace,
+                            workspace_bytes, stream, o);
+}
+
+int moe_experts(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W_down, int k,
+                int64_t capacity, const int32_t *used, const int32_t *slot_token,
+                const int32_t *tiles, void *H, float *Y, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    return moe_experts_ex(x, W_up, W_down, nullptr, k, capacity, used, slot_token, tiles, H, Y,
+                          workspace, workspace_bytes, stream);
 }
 
 int moe_combine(int64_t N, int64_t d, int k, const float *Y, const float *topk_gate,
@@ -393,9 +489,10 @@ int moe_combine(int64_t N, int64_t d, int k, const float *Y, const float *topk_g
                                           static_cast<hipStream_t>(stream)));
 }
 
-int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
-                const moe_tensor *W_up, const moe_tensor *W_down, int k, float capacity_factor,
-                moe_tensor *out, moe_stats *stats) {
+int moe_forward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                   const moe_tensor *W_up, const moe_tensor *W_down,
+                   const moe_expert_opts *opts, int k, float capacity_factor, moe_tensor *out,
+                   moe_stats *stats) {
     if (!stats || !W_up || !W_down || !out)
         return MOE_ERR_NULL;
     int64_t N, d, E;
@@ -412,6 +509,10 @@ int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *no
     if (W_up->shape[0] != E || W_up->shape[2] != d || W_down->shape[0] != E ||
         W_down->shape[1] != d || W_down->shape[2] != d_ff)
         return MOE_ERR_SHAPE;
+    ExpertOpts o;
+    rc = check_opts(opts, E, d, d_ff, o);
+    if (rc != MOE_OK)
+        return rc;
     int64_t oN, od;
     if (!act_rows(out, oN, od) || oN != N || od != d)
         return MOE_ERR_SHAPE;
@@ -464,11 +565,17 @@ int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *no
     void *part = ws + L.part;
     const size_t part_bytes = L.total - L.part;
     MOE_TRY(moe::launch_expert_up(bf16, x->data, W_up->data, d, d_ff, (int)E, k, m.ceff, used,
-                                  slot_token, tiles, H, rpe, part, part_bytes, s));
+                                  slot_token, tiles, H, rpe, part, part_bytes, o.act, o.b_up, s));
     MOE_TRY(moe::launch_expert_down(bf16, H, W_down->data, d, d_ff, (int)E, k, m.ceff, used,
-                                    slot_token, tiles, Y, rpe, part, part_bytes, s));
+                                    slot_token, tiles, Y, rpe, part, part_bytes, o.b_down, s));
     MOE_TRY(moe::launch_combine(Y, gate, slot, N, d, k, out->data, out->dtype, s));
     return MOE_OK;
+}
+
+int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                const moe_tensor *W_up, const moe_tensor *W_down, int k, float capacity_factor,
+                moe_tensor *out, moe_stats *stats) {
+    return moe_forward_ex(x, W_g, noise, W_up, W_down, nullptr, k, capacity_factor, out, stats);
 }
 
 }  // extern "C"

@@ -17,7 +17,8 @@ def _t(a: np.ndarray, device) -> torch.Tensor:
 
 
 def upload(wl, device="cuda", threads: int = 16, keep_host: bool = False) -> dict:
-    """Device tensors for ``wl``: x, W_g, noise (or None), W_up, W_down.
+    """Device tensors for ``wl``: x, W_g, noise (or None), W_up, W_down, the
+    expert biases b_up, b_down (fp32, or None) and the activation name.
 
     With ``keep_host`` the generated expert matrices are also memoised in the
     workload so that later CPU-side consumers do not regenerate them."""
@@ -29,6 +30,9 @@ def upload(wl, device="cuda", threads: int = 16, keep_host: bool = False) -> dic
         "noise": None if wl.noise is None else _t(wl.noise, device),
         "W_up": torch.empty((E, d_ff, d), dtype=dt, device=device),
         "W_down": torch.empty((E, d, d_ff), dtype=dt, device=device),
+        "b_up": None if wl.b_up() is None else _t(wl.b_up(), device),
+        "b_down": None if wl.b_down() is None else _t(wl.b_down(), device),
+        "act": wl.cfg.act,
     }
     for which, key in (("up", "W_up"), ("down", "W_down")):
         for e, a in wl.experts(which, threads):

@@ -30,7 +30,8 @@ def main(workload: str = "nanomoe", steps: int = 3, info_path: str = "") -> None
     wl = W.make(workload)
     dev = D.upload(wl)
     fwd = B.Forward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
-                    wl.cfg.cf, export=True)
+                    wl.cfg.cf, export=True, act=dev["act"],
+                    b_up=dev["b_up"], b_down=dev["b_down"])
     for _ in range(steps):
         fwd()
     torch.cuda.synchronize()

@@ -189,3 +189,38 @@ def test_expert_workspace_size(L):
     # and moe_forward's workspace holds it
     assert (B.lib().moe_workspace_size(2048, 768, 8, 3072, 2, 1.25, BF16)
             >= 8 * 640 * 3072 * 2 + 2048 * 2 * 768 * 4 + 256 * 256 * 256 * 4)
+
+
+def test_expert_variant_options_are_validated(L):
+    """moe_forward_ex / moe_experts_ex reject a bad activation or bias tensor
+    before anything is enqueued."""
+    x, wg, wu, wd, out, st = _good(N=64, d=16, E=4, dff=32)
+    r = ctypes.byref
+
+    def fwd(opts):
+        return L.moe_forward_ex(r(x), r(wg), None, r(wu), r(wd), r(opts) if opts else None, 2,
+                                1.0, r(out), r(st))
+
+    def opts(act=B.MOE_ACT_GELU, bu=None, bd=None):
+        o = B.MoeExpertOpts(act, None if bu is None else ctypes.addressof(bu),
+                            None if bd is None else ctypes.addressof(bd))
+        o._keep = (bu, bd)
+        return o
+
+    ok_up, ok_down = _t(FAKE, F32, 4, 32), _t(FAKE, F32, 4, 16)
+    assert fwd(opts(act=7)) == -4                                  # unknown activation
+    assert fwd(opts(bu=_t(FAKE, BF16, 4, 32))) == -3               # biases are fp32
+    assert fwd(opts(bu=_t(FAKE, F32, 4, 31))) == -2                # b_up [E, d_ff]
+    assert fwd(opts(bu=ok_up, bd=_t(FAKE, F32, 3, 16))) == -2      # b_down [E, d]
+    assert fwd(opts(bu=_t(FAKE + 4, F32, 4, 32))) == -7            # 16-byte aligned
+    assert fwd(opts(bd=_t(0, F32, 4, 16))) == -1                   # data NULL
+    # valid options get as far as the workspace check (1 byte here)
+    assert fwd(opts(bu=ok_up, bd=ok_down)) == -5
+    assert fwd(None) == -5
+    v = ctypes.c_void_p(FAKE)
+    assert L.moe_experts_ex(r(x), r(wu), r(wd), r(opts(act=3)), 2, 5, v, v, v, v, v, None, 0,
+                            None) == -4
+    assert L.moe_expert_up_ex(r(x), r(wu), r(opts(bu=_t(FAKE, F32, 4, 16))), 2, 5, v, v, v, v,
+                              None, 0, None) == -2
+    assert L.moe_expert_down_ex(64, r(wd), r(opts(bd=_t(FAKE, F32, 4, 32))), 2, 5, v, v, v, v, v,
+                                None, 0, None) == -2

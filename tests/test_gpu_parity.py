@@ -55,7 +55,21 @@ SMALL = {
 }
 
 
+# the nanoMoE slides' expert variant (slide 32): biases, GELU
+# name -> (N, d, E, k, d_ff, dtype, cf, sigma, seed, act, bias_std)
+VARIANT = {
+    "gelu_bias_f32": (77, 13, 6, 3, 21, "f32", 0.7, 0.5, 201, "gelu", 0.3),
+    "gelu_bias_bf16": (700, 200, 6, 2, 328, "bf16", 0.9, 0.4, 202, "gelu", 0.05),
+    "relu_bias_bf16": (1000, 264, 16, 4, 392, "bf16", 0.8, 0.5, 203, "relu", 0.05),
+    "gelu_nobias_bf16": (333, 136, 5, 2, 200, "bf16", 1.0, 0.3, 204, "gelu", 0.0),
+}
+
+
 def _small(name):
+    if name in VARIANT:
+        N, d, E, k, d_ff, dt, cf, sg, seed, act, bstd = VARIANT[name]
+        return W.custom(name, N=N, d=d, E=E, k=k, d_ff=d_ff, dtype=dt, cf=cf, sigma=sg,
+                        seed=seed, w_std=0.05, act=act, bias_std=bstd)
     if name == "tiny":
         return W.make("tiny")
     if name == "router_example":
@@ -67,12 +81,13 @@ def _small(name):
                     seed=seed, w_std=0.05)
 
 
-@pytest.mark.parametrize("name", ["tiny", "router_example", "capacity_example"] + list(SMALL))
+@pytest.mark.parametrize("name", ["tiny", "router_example", "capacity_example"] + list(SMALL) +
+                         list(VARIANT))
 def test_small_layer_matches_oracle(torch_mod, name):
     torch = torch_mod
     wl = _small(name)
     G.say(f"[parity] {name}: N={wl.N} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff} "
-          f"{wl.cfg.dtype} cf={wl.cfg.cf}")
+          f"{wl.cfg.dtype} cf={wl.cfg.cf} act={wl.cfg.act} bias_std={wl.cfg.bias_std}")
     res = oracle.forward(wl)
     dev = _upload(wl)
     out, st = G.run_forward(dev)
@@ -89,7 +104,8 @@ def test_small_layer_matches_oracle(torch_mod, name):
     _free(torch, dev, out)
 
 
-FULL = [("nanomoe", 256), ("mixtral", 48), ("skew", 96), ("finegrained", 32)]
+FULL = [("nanomoe", 256), ("mixtral", 48), ("skew", 96), ("finegrained", 32),
+        ("nanomoe_gelu", 256)]
 
 
 @pytest.mark.parametrize("name,nrows", FULL)

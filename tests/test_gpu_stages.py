@@ -139,17 +139,19 @@ def test_experts_match_oracle(torch_mod, name):
     assert np.abs(got - ref).max() <= G.BF16_MAX_ABS
 
 
-def test_experts_split_last_round(torch_mod):
+@pytest.mark.parametrize("act,bias_std", [("relu", 0.0), ("gelu", 0.05)])
+def test_experts_split_last_round(torch_mod, act, bias_std):
     """Shapes whose last round of 256x256 tiles is cut into K-ranges (16
     experts of ~600 rows: 384 tiles per product against 256 resident
     workgroups): sampled rows against the oracle, with and without the
-    split scratch, and the split result identical from run to run."""
+    split scratch, and the split result identical from run to run; also with
+    the slides' expert variant (the fix-up applies bias and activation)."""
     torch = torch_mod
     from sparse_mixture_experts_20_amd import binding as B
     from sparse_mixture_experts_20_amd import device as D
     wl = W.custom("split", N=4800, d=2048, E=16, k=2, d_ff=2048, dtype="bf16", cf=1.25,
-                  sigma=0.5, seed=53, w_std=0.02)
-    G.say("[stage] experts split last round")
+                  sigma=0.5, seed=53, w_std=0.02, act=act, bias_std=bias_std)
+    G.say(f"[stage] experts split last round act={act} bias_std={bias_std}")
     _, idx, _ = oracle.router(wl.x64(), wl.wg64(), wl.noise64(), wl.k)
     rng = np.random.default_rng(3)
     # the cut tiles are the last ones: those of the highest expert ids
@@ -162,7 +164,8 @@ def test_experts_split_last_round(torch_mod):
     ys = []
     for ws in ("auto", "auto", None):
         _, Y = B.experts(dev["x"], dev["W_up"], dev["W_down"], wl.k, res.C, used, slot_token,
-                         tiles, workspace=ws)
+                         tiles, workspace=ws, act=dev["act"], b_up=dev["b_up"],
+                         b_down=dev["b_down"])
         torch.cuda.synchronize()
         ys.append(G.to_np(Y).reshape(wl.N, wl.k, wl.d).astype(np.float64))
     np.testing.assert_array_equal(ys[0], ys[1])

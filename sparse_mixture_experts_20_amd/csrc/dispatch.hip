@@ -7,14 +7,18 @@
 // running count per expert, minus one, masked by rank < capacity; slide 19:
 // the top-1 block comes first so first choices have priority.
 //
-// The running count is never materialised as a [k*N, E] one-hot matrix. One
-// workgroup walks the k*N assignments in (j, t) order, 4096 per phase (the
-// next phase's ids are loaded while the current one is ranked): each wave
-// ranks its 4 x 64 assignments against the lanes holding the same id, found
-// with one ballot per id bit, the per-wave counts are turned into exclusive
-// prefixes across the 16 waves in LDS, and a running per-expert base carries
-// the count into the next phase. Ranks are positional, never taken from
-// atomics, so the plan is the same on every run.
+// The running count is never materialised as a [k*N, E] one-hot matrix.
+// Assignments are taken in (j, t) order in chunks of 4096, one workgroup per
+// chunk. A workgroup first counts, per expert, the assignments of all earlier
+// chunks (a histogram: integer counts, so the order of the additions does not
+// matter), then ranks its own chunk: each wave ranks its 4 x 64 assignments
+// against the lanes holding the same id, found with one ballot per id bit,
+// the per-wave counts are turned into exclusive prefixes across the 16 waves
+// in LDS, and the rank is the earlier chunks' count plus the rank inside the
+// chunk. Ranks are positional, never taken from atomics, so the plan is the
+// same on every run. The last workgroup also writes used[] and the GEMM tile
+// schedule. (Re-counting earlier chunks costs the last workgroup one pass
+// over k*N ids; it replaces a second kernel and a global scratch.)
 #include "common.hpp"
 
 namespace moe {
@@ -22,8 +26,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWavesPerBlock = kThreads / kWave;   // 16
-constexpr int kItems = 4;                           // 64-assignment groups per wave per phase
-constexpr int kPhase = kThreads * kItems;           // 4096 assignments per phase
+constexpr int kItems = 4;                           // 64-assignment groups per wave per chunk
+constexpr int kPhase = kThreads * kItems;           // 4096 assignments per chunk
 
 // Lanes of the wave holding the same expert id as this lane (among lanes
 // with valid ids): one ballot per id bit, O(log E) with no memory traffic.
@@ -41,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     const int32_t *__restrict__ idx, int N, int E, int k, int ceff,
     int32_t *__restrict__ slot, int32_t *__restrict__ used, int32_t *__restrict__ slot_token,
     int32_t *__restrict__ tiles) {
-    __shared__ int base[kMaxExperts];                     // assignments counted so far
+    __shared__ int base[kMaxExperts];                     // assignments of earlier chunks
     __shared__ int wcnt[kWavesPerBlock * kMaxExperts];    // per-wave counts, then prefixes
 
     const int tid = threadIdx.x;
@@ -50,88 +54,101 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     const uint64_t lt = lanemask_lt();
     const int total = N * k;   // < 2^31
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    const int64_t p0 = (int64_t)blockIdx.x * kPhase;   // this workgroup's chunk
+
+    // (choice, token) order: p = j*N + t; assignment id a = t*k + j
+    auto assignment = [&](int p) {
+        const int j = p / N;
+        return (p - j * N) * k + j;
+    };
+
+    // this chunk's ids, loaded first so that they arrive during the count
+    int cur_e[kItems], cur_a[kItems];
+#pragma unroll
+    for (int s = 0; s < kItems; ++s) {
+        const int64_t p = p0 + w * (kItems * 64) + s * 64 + lane;
+        cur_a[s] = assignment(p < total ? (int)p : 0);
+        cur_e[s] = idx[cur_a[s]];
+    }
 
     for (int e = tid; e < E; e += kThreads)
         base[e] = 0;
-
-    // (choice, token) order: p = j*N + t; assignment id a = t*k + j
-    auto load_phase = [&](int64_t p0, int (&ids)[kItems], int (&as)[kItems]) {
+    for (int i = tid; i < kWavesPerBlock * E; i += kThreads)
+        wcnt[i] = 0;
+    __syncthreads();
+    // histogram of the earlier chunks, 8 ids per thread in flight at a time;
+    // with few experts one LDS add per distinct id per wave (adds to one bin
+    // would serialise), with many a plain add per id
+    constexpr int U = 8;
+    for (int p = tid; p < (int)p0; p += kThreads * U) {
+        int ev[U];
 #pragma unroll
-        for (int s = 0; s < kItems; ++s) {
-            const int64_t p = p0 + w * (kItems * 64) + s * 64 + lane;
-            const int pc = p < total ? (int)p : 0;
-            const int j = pc / N;
-            as[s] = (pc - j * N) * k + j;
-            ids[s] = idx[as[s]];
+        for (int u = 0; u < U; ++u) {
+            const int pp = p + u * kThreads;
+            ev[u] = pp < (int)p0 ? idx[assignment(pp)] : -1;
         }
-    };
-    int cur_e[kItems], cur_a[kItems];
-    load_phase(0, cur_e, cur_a);
-
-    for (int64_t p0 = 0; p0 < total; p0 += kPhase) {
-        int nxt_e[kItems], nxt_a[kItems];
-        const bool more = p0 + kPhase < total;
-        if (more)
-            load_phase(p0 + kPhase, nxt_e, nxt_a);   // in flight during this phase
-
-        for (int i = tid; i < kWavesPerBlock * E; i += kThreads)
-            wcnt[i] = 0;
-        __syncthreads();
-
-        // rank of each assignment among the wave's earlier ones with its id
-        int my_r[kItems];
 #pragma unroll
-        for (int s = 0; s < kItems; ++s) {
-            const int64_t p = p0 + w * (kItems * 64) + s * 64 + lane;
-            int e = -1;
-            if (p < total) {
-                e = cur_e[s];
-                if (e < 0 || e >= E) {   // not an expert id: the assignment is dropped
-                    slot[cur_a[s]] = -1;
-                    e = -1;
-                }
-            }
-            const uint64_t m = match_ids(e, e >= 0, nbits);
-            const int before = __popcll(m & lt);
-            my_r[s] = e >= 0 ? wcnt[w * E + e] + before : 0;
-            if (e >= 0 && before == 0)
-                wcnt[w * E + e] += __popcll(m);   // one lane per distinct id
-            cur_e[s] = e;
-        }
-        __syncthreads();
-        // per expert: exclusive prefix over the waves, starting at the base
-        for (int e = tid; e < E; e += kThreads) {
-            int run = base[e];
-            for (int ww = 0; ww < kWavesPerBlock; ++ww) {
-                const int c = wcnt[ww * E + e];
-                wcnt[ww * E + e] = run;
-                run += c;
-            }
-            base[e] = run;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int s = 0; s < kItems; ++s) {
-            const int e = cur_e[s];
-            if (e < 0)
-                continue;
-            const int r = wcnt[w * E + e] + my_r[s];
-            const int a = cur_a[s];
-            const bool kept = r < ceff;   // r < N always, so r < C <=> r < min(C, N)
-            slot[a] = kept ? r : -1;
-            if (kept)
-                slot_token[(int64_t)e * ceff + r] = a;
-        }
-        __syncthreads();
-        if (more) {
-#pragma unroll
-            for (int s = 0; s < kItems; ++s) {
-                cur_e[s] = nxt_e[s];
-                cur_a[s] = nxt_a[s];
+        for (int u = 0; u < U; ++u) {
+            const int e = ev[u];
+            const bool ok = e >= 0 && e < E;
+            if (E > 64) {
+                if (ok)
+                    atomicAdd(&base[e], 1);
+            } else {
+                const uint64_t m = match_ids(e, ok, nbits);
+                if (ok && __popcll(m & lt) == 0)
+                    atomicAdd(&base[e], __popcll(m));
             }
         }
     }
 
+    // rank of each assignment among the wave's earlier ones with its id
+    int my_r[kItems];
+#pragma unroll
+    for (int s = 0; s < kItems; ++s) {
+        const int64_t p = p0 + w * (kItems * 64) + s * 64 + lane;
+        int e = -1;
+        if (p < total) {
+            e = cur_e[s];
+            if (e < 0 || e >= E) {   // not an expert id: the assignment is dropped
+                slot[cur_a[s]] = -1;
+                e = -1;
+            }
+        }
+        const uint64_t m = match_ids(e, e >= 0, nbits);
+        const int before = __popcll(m & lt);
+        my_r[s] = e >= 0 ? wcnt[w * E + e] + before : 0;
+        if (e >= 0 && before == 0)
+            wcnt[w * E + e] += __popcll(m);   // one lane per distinct id
+        cur_e[s] = e;
+    }
+    __syncthreads();
+    // per expert: exclusive prefix over the waves, starting at the base
+    for (int e = tid; e < E; e += kThreads) {
+        int run = base[e];
+        for (int ww = 0; ww < kWavesPerBlock; ++ww) {
+            const int c = wcnt[ww * E + e];
+            wcnt[ww * E + e] = run;
+            run += c;
+        }
+        base[e] = run;   // assignments up to the end of this chunk
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kItems; ++s) {
+        const int e = cur_e[s];
+        if (e < 0)
+            continue;
+        const int r = wcnt[w * E + e] + my_r[s];
+        const int a = cur_a[s];
+        const bool kept = r < ceff;   // r < N always, so r < C <=> r < min(C, N)
+        slot[a] = kept ? r : -1;
+        if (kept)
+            slot_token[(int64_t)e * ceff + r] = a;
+    }
+
+    if (blockIdx.x != gridDim.x - 1)
+        return;
     for (int e = tid; e < E; e += kThreads)
         used[e] = base[e] < ceff ? base[e] : ceff;
     if (tid == 0) {
@@ -160,8 +177,9 @@ __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
 hipError_t launch_dispatch(const int32_t *idx, int64_t N, int E, int k, int64_t ceff,
                            int32_t *slot, int32_t *used, int32_t *slot_token, int32_t *tiles,
                            hipStream_t s) {
-    hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), 0, s, idx, (int)N, E, k,
-                       (int)ceff, slot, used, slot_token, tiles);
+    const int64_t chunks = (N * k + kPhase - 1) / kPhase;
+    hipLaunchKernelGGL(dispatch_kernel, dim3((unsigned)chunks), dim3(kThreads), 0, s, idx, (int)N,
+                       E, k, (int)ceff, slot, used, slot_token, tiles);
     return hipGetLastError();
 }
 

@@ -111,9 +111,10 @@ typedef struct {
  *   out    [N, d] (same shape as x) same dtype as x; every row is written
  *   stats  launch context and optional exports (required)
  * Numerics: scores, top-k and gates in fp32; expert products accumulate in
- * fp32 (bf16 inputs on matrix cores); the hidden activation is stored in the
- * dtype of x; the combine accumulates in fp32 in choice order and rounds
- * once to the dtype of out (round to nearest even).
+ * fp32 (bf16 inputs on matrix cores); the hidden activation and each
+ * expert's output row are stored in the dtype of x; the combine accumulates
+ * in fp32 in choice order and rounds once to the dtype of out (round to
+ * nearest even).
  * N = 0 is valid: capacity is 0, used_capacity (if given) is zeroed. */
 int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
                 const moe_tensor *W_up, const moe_tensor *W_down, int k,
@@ -192,9 +193,12 @@ int moe_dispatch(int64_t N, int64_t E, int k, int64_t capacity, const int32_t *t
 /* Grouped expert FFN (page 1 STEP 7-10; slides 32-37) over the dispatch plan.
  * For each expert e and r < used[e], with a = slot_token[e, r], t = a / k:
  *   H[e, r, :] = ReLU(W_up[e] x_t)      stored in the dtype of x   [E, min(C,N), d_ff]
- *   Y[a, :]    = W_down[e] H[e, r, :]   fp32                       [N*k, d]
- * The gather of token rows is fused into the first product. Rows of Y whose
- * assignment was dropped are not written. H and Y are caller device buffers.
+ *   Y[a, :]    = W_down[e] H[e, r, :]   stored in the dtype of x   [N*k, d]
+ * Both products accumulate in fp32 and round once to the stored dtype (bf16
+ * expert outputs, as the slides' experts run under bf16 autocast). The
+ * gather of token rows is fused into the first product. Rows of Y whose
+ * assignment was dropped are not written. H and Y are caller device buffers
+ * (16-byte aligned for bf16).
  * workspace: optional device scratch of workspace_bytes (256-byte aligned,
  * MOE_ERR_ALIGN otherwise) in which the bf16 path keeps fp32 partial tiles
  * when it cuts the K loop of a product's last, partly idle round of tiles
@@ -205,14 +209,14 @@ int moe_dispatch(int64_t N, int64_t E, int k, int64_t capacity, const int32_t *t
  * Calls that share a workspace must not overlap. */
 int moe_experts(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W_down,
                 int k, int64_t capacity, const int32_t *used, const int32_t *slot_token,
-                const int32_t *tiles, void *H, float *Y, void *workspace,
+                const int32_t *tiles, void *H, void *Y, void *workspace,
                 size_t workspace_bytes, void *stream);
 
 /* moe_experts with the expert variant of moe_expert_opts (NULL: ReLU, no
  * biases). */
 int moe_experts_ex(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W_down,
                    const moe_expert_opts *opts, int k, int64_t capacity, const int32_t *used,
-                   const int32_t *slot_token, const int32_t *tiles, void *H, float *Y,
+                   const int32_t *slot_token, const int32_t *tiles, void *H, void *Y,
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* moe_expert_up and moe_expert_down with the expert variant of
@@ -224,7 +228,7 @@ int moe_expert_up_ex(const moe_tensor *x, const moe_tensor *W_up, const moe_expe
                      void *stream);
 int moe_expert_down_ex(int64_t N, const moe_tensor *W_down, const moe_expert_opts *opts, int k,
                        int64_t capacity, const int32_t *used, const int32_t *slot_token,
-                       const int32_t *tiles, const void *H, float *Y, void *workspace,
+                       const int32_t *tiles, const void *H, void *Y, void *workspace,
                        size_t workspace_bytes, void *stream);
 
 /* Bytes of expert scratch that enable the K-split on any device with up to
@@ -234,20 +238,21 @@ size_t moe_expert_workspace_size(int32_t dtype);
 /* The two halves of moe_experts, one product each (page 1 STEP 8-9 and STEP
  * 10): moe_expert_up writes H from x and W_up; moe_expert_down writes Y from
  * H and W_down ([E, d, d_ff]; H has W_down's dtype and [E, min(C,N), d_ff]
- * rows, Y is [N*k, d] fp32). workspace as for moe_experts. */
+ * rows, Y is [N*k, d] in W_down's dtype). workspace as for moe_experts. */
 int moe_expert_up(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t capacity,
                   const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
                   void *H, void *workspace, size_t workspace_bytes, void *stream);
 int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
                     const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
-                    const void *H, float *Y, void *workspace, size_t workspace_bytes,
+                    const void *H, void *Y, void *workspace, size_t workspace_bytes,
                     void *stream);
 
 /* Combine (page 1 STEP 11-12; slides 38-40): out[t] = sum over j < k with
  * slot[t, j] >= 0 of topk_gate[t, j] * Y[t*k + j], accumulated in fp32 in
  * order j = 0..k-1, rounded once to out's dtype; rows with every choice
- * dropped become 0. out is [N, d] MOE_F32 or MOE_BF16. */
-int moe_combine(int64_t N, int64_t d, int k, const float *Y, const float *topk_gate,
+ * dropped become 0. Y is [N*k, d] MOE_F32 or MOE_BF16 (read as exact fp32
+ * values), out is [N, d] MOE_F32 or MOE_BF16. */
+int moe_combine(int64_t N, int64_t d, int k, const moe_tensor *Y, const float *topk_gate,
                 const int32_t *slot, moe_tensor *out, void *stream);
 
 #ifdef __cplusplus

@@ -107,7 +107,7 @@ def lib():
         L.moe_expert_down.restype = ctypes.c_int
         L.moe_expert_workspace_size.argtypes = [ctypes.c_int32]
         L.moe_expert_workspace_size.restype = ctypes.c_size_t
-        L.moe_combine.argtypes = [_i64, _i64, ctypes.c_int, _vp, _vp, _vp, _T, _vp]
+        L.moe_combine.argtypes = [_i64, _i64, ctypes.c_int, _T, _vp, _vp, _T, _vp]
         L.moe_combine.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -331,14 +331,14 @@ def _ws_args(ws):
 
 def experts(x, W_up, W_down, k, capacity_, used, slot_token, tiles, H=None, Y=None,
             workspace="auto", stream=None, act="relu", b_up=None, b_down=None):
-    """Returns (H [E, min(C,N), d_ff] in x's dtype, Y [N*k, d] fp32)."""
+    """Returns (H [E, min(C,N), d_ff] and Y [N*k, d], both in x's dtype)."""
     N, d = x.numel() // x.shape[-1], x.shape[-1]
     E, d_ff = W_up.shape[0], W_up.shape[1]
     ceff = min(capacity_, N)
     if H is None:
         H = torch.zeros((E, max(ceff, 1), d_ff), dtype=x.dtype, device=x.device)
     if Y is None:
-        Y = torch.zeros((N * k, d), dtype=torch.float32, device=x.device)
+        Y = torch.zeros((N * k, d), dtype=x.dtype, device=x.device)
     dx, du, dd = desc(x), desc(W_up), desc(W_down)
     if not slot_token.is_contiguous():
         raise ValueError("slot_token must be a contiguous [E, min(C, N)] tensor")
@@ -390,9 +390,10 @@ def expert_down(N, W_down, k, capacity_, used, slot_token, tiles, H, Y, workspac
 
 
 def combine(Y, gate, slot, out, stream=None):
+    """Y: [N*k, d] fp32 or bf16 expert outputs, assignment-major."""
     N, k = gate.shape
     d = out.shape[-1]
-    do = desc(out)
-    _check(lib().moe_combine(N, d, k, _ptr(Y), _ptr(gate), _ptr(slot), _ref(do),
+    dy, do = desc(Y), desc(out)
+    _check(lib().moe_combine(N, d, k, _ref(dy), _ptr(gate), _ptr(slot), _ref(do),
                              _stream(stream)), "moe_combine")
     return out

@@ -5,18 +5,52 @@
 // gates, so a dropped assignment contributes nothing and a token whose every
 // choice was dropped gets 0).
 //
-// Each thread owns a 4-wide column slice of one token row: it reads the k
-// fp32 expert rows of that token (stored contiguously, assignment-major),
-// accumulates in fp32 in choice order and rounds once to the output type.
-// A pure streaming kernel: k*d*4 bytes read per token (kept rows only) and
-// d * sizeof(out) bytes written.
+// Each thread owns a VEC-wide column slice of one token row: it reads the k
+// expert rows of that token (stored contiguously, assignment-major; bf16 or
+// fp32), accumulates in fp32 in choice order and rounds once to the output
+// type. A pure streaming kernel: k*d*sizeof(Y) bytes read per token (kept
+// rows only) and d*sizeof(out) bytes written. bf16 rows are read 8 columns
+// (16 bytes) at a time.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
-template <bool BF16, int VEC>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ Y,
+template <int VEC>
+__device__ __forceinline__ void load_row(const float *y, float (&v)[VEC]) {
+    if constexpr (VEC % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < VEC / 4; ++q) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(y + 4 * q);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[4 * q + i] = a[i];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+            v[i] = y[i];
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_row(const unsigned short *y, float (&v)[VEC]) {
+    if constexpr (VEC == 8) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(y);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(a[i] << 16);
+            v[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+            v[i] = bf16_bits_to_f32(y[i]);
+    }
+}
+
+template <typename YT, bool BF16, int VEC>
+__global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ Y,
                                                       const float *__restrict__ gate,
                                                       const int32_t *__restrict__ slot,
                                                       int64_t N, int d, int k,
@@ -36,25 +70,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
             if (slot[a] < 0)
                 continue;
             const float g = gate[a];
-            const float *yr = Y + a * d + c;
-            if (VEC == 4) {
-                const f32x4 y = *reinterpret_cast<const f32x4 *>(yr);
+            float y[VEC];
+            load_row<VEC>(Y + a * d + c, y);
 #pragma unroll
-                for (int v = 0; v < VEC; ++v)
-                    acc[v] += g * y[v];
-            } else {
-#pragma unroll
-                for (int v = 0; v < VEC; ++v)
-                    acc[v] += g * yr[v];
-            }
+            for (int v = 0; v < VEC; ++v)
+                acc[v] += g * y[v];
         }
         if (BF16) {
             unsigned short *o = static_cast<unsigned short *>(out) + t * d + c;
-            if (VEC == 4) {
-                u32x2 pk;
-                pk[0] = (unsigned)f32_to_bf16_bits(acc[0]) | ((unsigned)f32_to_bf16_bits(acc[1]) << 16);
-                pk[1] = (unsigned)f32_to_bf16_bits(acc[2]) | ((unsigned)f32_to_bf16_bits(acc[3]) << 16);
-                *reinterpret_cast<u32x2 *>(o) = pk;
+            if constexpr (VEC % 4 == 0) {
+#pragma unroll
+                for (int q = 0; q < VEC / 4; ++q) {
+                    u32x2 pk;
+                    pk[0] = (unsigned)f32_to_bf16_bits(acc[4 * q]) |
+                            ((unsigned)f32_to_bf16_bits(acc[4 * q + 1]) << 16);
+                    pk[1] = (unsigned)f32_to_bf16_bits(acc[4 * q + 2]) |
+                            ((unsigned)f32_to_bf16_bits(acc[4 * q + 3]) << 16);
+                    *reinterpret_cast<u32x2 *>(o + 4 * q) = pk;
+                }
             } else {
 #pragma unroll
                 for (int v = 0; v < VEC; ++v)
@@ -69,30 +102,39 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     }
 }
 
-template <bool BF16, int VEC>
-hipError_t launch(const float *Y, const float *gate, const int32_t *slot, int64_t N, int64_t d,
+template <typename YT, bool BF16, int VEC>
+hipError_t launch(const void *Y, const float *gate, const int32_t *slot, int64_t N, int64_t d,
                   int k, void *out, hipStream_t s) {
     const int64_t total = N * (d / VEC);
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536)
         blocks = 65536;
-    hipLaunchKernelGGL((combine_kernel<BF16, VEC>), dim3((unsigned)blocks), dim3(256), 0, s, Y,
-                       gate, slot, N, (int)d, k, out);
+    hipLaunchKernelGGL((combine_kernel<YT, BF16, VEC>), dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const YT *>(Y), gate, slot, N, (int)d, k, out);
     return hipGetLastError();
+}
+
+template <typename YT, int VEC>
+hipError_t launch_out(const void *Y, const float *gate, const int32_t *slot, int64_t N, int64_t d,
+                      int k, void *out, int out_dtype, hipStream_t s) {
+    return out_dtype == 1 ? launch<YT, true, VEC>(Y, gate, slot, N, d, k, out, s)
+                          : launch<YT, false, VEC>(Y, gate, slot, N, d, k, out, s);
 }
 
 }  // namespace
 
-hipError_t launch_combine(const float *Y, const float *gate, const int32_t *slot, int64_t N,
-                          int64_t d, int k, void *out, int out_dtype, hipStream_t s) {
+hipError_t launch_combine(const void *Y, int y_dtype, const float *gate, const int32_t *slot,
+                          int64_t N, int64_t d, int k, void *out, int out_dtype, hipStream_t s) {
     if (N == 0 || d == 0)
         return hipSuccess;
-    const bool vec4 = (d % 4) == 0;
-    if (out_dtype == 1)
-        return vec4 ? launch<true, 4>(Y, gate, slot, N, d, k, out, s)
-                    : launch<true, 1>(Y, gate, slot, N, d, k, out, s);
-    return vec4 ? launch<false, 4>(Y, gate, slot, N, d, k, out, s)
-                : launch<false, 1>(Y, gate, slot, N, d, k, out, s);
+    if (y_dtype == 1) {
+        if (d % 8 == 0)
+            return launch_out<unsigned short, 8>(Y, gate, slot, N, d, k, out, out_dtype, s);
+        return launch_out<unsigned short, 1>(Y, gate, slot, N, d, k, out, out_dtype, s);
+    }
+    if (d % 4 == 0)
+        return launch_out<float, 4>(Y, gate, slot, N, d, k, out, out_dtype, s);
+    return launch_out<float, 1>(Y, gate, slot, N, d, k, out, out_dtype, s);
 }
 
 }  // namespace moe

@@ -60,8 +60,9 @@ hipError_t launch_dispatch(const int32_t *idx, int64_t N, int E, int k, int64_t 
                            int32_t *tiles, hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 
-// Grouped expert products. mode 0: H = ReLU(x[gather] W_up^T); mode 1:
-// Y[scatter] = H W_down^T.
+// Grouped expert products. mode 0: H = act(x[gather] W_up^T + b_up); mode 1:
+// Y[scatter] = H W_down^T + b_down. H and Y have the operands' dtype (bf16 or
+// fp32).
 // bf16 != 0: bf16 operands on matrix cores; otherwise fp32 operands.
 // rows_per_expert: the expected kept rows per expert (picks the tile shape).
 // part/part_bytes: device scratch for the K-split of a product's last round
@@ -79,7 +80,7 @@ hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t 
                             const float *b_up, hipStream_t s);
 hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int64_t d,
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
-                              const int32_t *slot_token, const int32_t *tiles, float *Y,
+                              const int32_t *slot_token, const int32_t *tiles, void *Y,
                               int64_t rows_per_expert, void *part, size_t part_bytes,
                               const float *b_down, hipStream_t s);
 
@@ -87,7 +88,8 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
 hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, int64_t K,
                                   int64_t Nout, float *Y, hipStream_t s);
 
-hipError_t launch_combine(const float *Y, const float *gate, const int32_t *slot,
+// Y: [N*k, d] rows of dtype y_dtype (0 fp32, 1 bf16); out of dtype out_dtype.
+hipError_t launch_combine(const void *Y, int y_dtype, const float *gate, const int32_t *slot,
                           int64_t N, int64_t d, int k, void *out, int out_dtype,
                           hipStream_t s);
 

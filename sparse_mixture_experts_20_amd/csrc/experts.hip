@@ -161,9 +161,10 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // 16 distinct bank groups.
 // Two waves per SIMD (the LDS budget allows no more), so the compiler may use
 // up to 256 registers per lane and schedule for latency rather than occupancy.
-// MODE 0: up product (gathered token rows, ReLU, bf16 H); 1: down product
-// (fp32 rows scattered to their assignment); 2: plain product of ceff rows of
-// A into fp32 rows of Y (no gather, no schedule table, no split).
+// MODE 0: up product (gathered token rows, activation, bf16 H into O16);
+// 1: down product (bf16 rows of Y scattered to their assignment, into O16);
+// 2: plain product of ceff rows of A into fp32 rows of O32 (no gather, no
+// schedule table, no split).
 // part: scratch for the split of the last round (NULL: no split), P: the
 // number of workgroups of this kernel that fit on the device at once.
 // act: activation of the up product (kActRelu, kActGelu); bias: [E, Nout]
@@ -175,7 +176,7 @@ void expert_gemm_kernel(
     const unsigned short *__restrict__ A_src, const unsigned short *__restrict__ W, int K,
     int Nout, int E, int k, int ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
-    unsigned short *__restrict__ H_out, float *__restrict__ Y_out, float *__restrict__ part,
+    unsigned short *__restrict__ O16, float *__restrict__ O32, float *__restrict__ part,
     int P, int act, const float *__restrict__ bias) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int NTHR = NW * 64;
@@ -411,7 +412,7 @@ void expert_gemm_kernel(
                     if (nb + 4 * c + 4 <= Nout)
                         *reinterpret_cast<f32x4 *>(dst + 4 * c) = v[c];
             } else if (MODE == 0) {
-                unsigned short *dst = H_out + srow * Nout + nb;
+                unsigned short *dst = O16 + srow * Nout + nb;
                 const float *bp = bias ? bias + (int64_t)e * Nout + nb : nullptr;
                 auto store_h = [&](auto use_gelu) {
 #pragma unroll
@@ -440,15 +441,34 @@ void expert_gemm_kernel(
                     store_h(std::true_type{});
                 else
                     store_h(std::false_type{});
+            } else if (MODE == 1) {
+                // bf16 row of Y at the assignment's position
+                unsigned short *dst = O16 + (int64_t)slot_token[srow] * Nout + nb;
+                const float *bp = bias ? bias + (int64_t)e * Nout + nb : nullptr;
+#pragma unroll
+                for (int h = 0; h < CPL / 8; ++h) {
+                    if (nb + 8 * h + 8 <= Nout) {
+                        f32x4 z0 = v[2 * h], z1 = v[2 * h + 1];
+                        if (bp) {
+                            z0 += *reinterpret_cast<const f32x4 *>(bp + 8 * h);
+                            z1 += *reinterpret_cast<const f32x4 *>(bp + 8 * h + 4);
+                        }
+                        u32x4 pk;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const f32x4 &z = c < 2 ? z0 : z1;
+                            pk[c] = (unsigned)f32_to_bf16_bits(z[(c % 2) * 2]) |
+                                    ((unsigned)f32_to_bf16_bits(z[(c % 2) * 2 + 1]) << 16);
+                        }
+                        *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
+                    }
+                }
             } else {
-                const int64_t orow = MODE == 1 ? (int64_t)slot_token[srow] : (int64_t)r;
-                float *dst = Y_out + orow * Nout + nb;
-                const float *bp = MODE == 1 && bias ? bias + (int64_t)e * Nout + nb : nullptr;
+                float *dst = O32 + (int64_t)r * Nout + nb;
 #pragma unroll
                 for (int c = 0; c < CPL / 4; ++c)
                     if (nb + 4 * c + 4 <= Nout)
-                        *reinterpret_cast<f32x4 *>(dst + 4 * c) =
-                            bp ? v[c] + *reinterpret_cast<const f32x4 *>(bp + 4 * c) : v[c];
+                        *reinterpret_cast<f32x4 *>(dst + 4 * c) = v[c];
             }
         }
     }
@@ -456,14 +476,14 @@ void expert_gemm_kernel(
 
 // Sum of the K-range partials of the cut tiles, in K order, then the same
 // epilogue as a whole tile (MODE 0: bias, activation, bf16 H; MODE 1: bias,
-// fp32 row of Y).
+// bf16 row of Y).
 // One workgroup per 16-row strip of a cut tile; 4 columns per thread.
 template <int BM, int BN, int BKT, int MODE>
 __global__ __launch_bounds__(256) void split_fixup_kernel(
     int K, int Nout, int E, int ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
-    const float *__restrict__ part, int P, unsigned short *__restrict__ H_out,
-    float *__restrict__ Y_out, int act, const float *__restrict__ bias) {
+    const float *__restrict__ part, int P, unsigned short *__restrict__ O16, int act,
+    const float *__restrict__ bias) {
     constexpr int STRIPS = BM / 16;
     __shared__ int s_mt[kMaxExperts + 1];
     for (int i = threadIdx.x; i <= E; i += 256)
@@ -492,18 +512,18 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
         const int64_t srow = (int64_t)e * ceff + r;
         if (bias)
             v += *reinterpret_cast<const f32x4 *>(bias + (int64_t)e * Nout + n);
+        int64_t orow = (int64_t)slot_token[srow];   // MODE 1: the row of Y
         if (MODE == 0) {
+            orow = srow;                              // the row of H
             if (act == kActGelu)
                 v = f32x4{gelu(v[0]), gelu(v[1]), gelu(v[2]), gelu(v[3])};
             else
                 v = f32x4{fmaxf(v[0], 0.f), fmaxf(v[1], 0.f), fmaxf(v[2], 0.f), fmaxf(v[3], 0.f)};
-            u32x2 pk;
-            pk[0] = (unsigned)f32_to_bf16_bits(v[0]) | ((unsigned)f32_to_bf16_bits(v[1]) << 16);
-            pk[1] = (unsigned)f32_to_bf16_bits(v[2]) | ((unsigned)f32_to_bf16_bits(v[3]) << 16);
-            *reinterpret_cast<u32x2 *>(H_out + srow * Nout + n) = pk;
-        } else {
-            *reinterpret_cast<f32x4 *>(Y_out + (int64_t)slot_token[srow] * Nout + n) = v;
         }
+        u32x2 pk;
+        pk[0] = (unsigned)f32_to_bf16_bits(v[0]) | ((unsigned)f32_to_bf16_bits(v[1]) << 16);
+        pk[1] = (unsigned)f32_to_bf16_bits(v[2]) | ((unsigned)f32_to_bf16_bits(v[3]) << 16);
+        *reinterpret_cast<u32x2 *>(O16 + orow * Nout + n) = pk;
     }
 }
 
@@ -618,8 +638,8 @@ int resident_blocks(Kern kernel, int threads) {
 template <int BM, int BN, int WM, int WN, int MODE>
 hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_t K, int64_t Nout,
                         int E, int k, int64_t ceff, const int32_t *used,
-                        const int32_t *slot_token, const int32_t *mt, unsigned short *H,
-                        float *Y, float *part, size_t part_bytes, int act, const float *bias,
+                        const int32_t *slot_token, const int32_t *mt, unsigned short *O16,
+                        float *part, size_t part_bytes, int act, const float *bias,
                         hipStream_t s) {
     auto kern = expert_gemm_kernel<BM, BN, WM, WN, kBK, 2, MODE>;
     constexpr int NTHR = WM * WN * 64;
@@ -645,33 +665,33 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
     const int64_t grid = (tmax + kXcds - 1) / kXcds * kXcds +
                          (split ? (int64_t)(P + kXcds - 1) / kXcds * kXcds : 0);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHR), 0, s, A, W, (int)K, (int)Nout, E,
-                       k, (int)ceff, used, slot_token, mt, H, Y, split ? part : nullptr,
-                       split ? P : 0, act, bias);
+                       k, (int)ceff, used, slot_token, mt, O16, (float *)nullptr,
+                       split ? part : nullptr, split ? P : 0, act, bias);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !split)
         return err;
     hipLaunchKernelGGL((split_fixup_kernel<BM, BN, kBK, MODE>), dim3((unsigned)(P * (BM / 16))),
                        dim3(256), 0, s, (int)K, (int)Nout, E, (int)ceff, used, slot_token, mt,
-                       (const float *)part, P, H, Y, act, bias);
+                       (const float *)part, P, O16, act, bias);
     return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W, int64_t K,
                        int64_t Nout, int E, int k, int64_t ceff, const int32_t *used,
-                       const int32_t *slot_token, const int32_t *tiles, unsigned short *H,
-                       float *Y, void *part, size_t part_bytes, int act, const float *bias,
+                       const int32_t *slot_token, const int32_t *tiles, unsigned short *O16,
+                       void *part, size_t part_bytes, int act, const float *bias,
                        hipStream_t s) {
     float *pf = static_cast<float *>(part);
     if (t == Tile::k256)
         return launch_tiles<256, 256, 2, 4, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
-                                                  tiles + E + 1, H, Y, pf, part_bytes, act, bias,
+                                                  tiles + E + 1, O16, pf, part_bytes, act, bias,
                                                   s);
     if (t == Tile::k128x64)
         return launch_tiles<128, 64, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
-                                                 tiles, H, Y, pf, part_bytes, act, bias, s);
+                                                 tiles, O16, pf, part_bytes, act, bias, s);
     return launch_tiles<128, 128, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token, tiles,
-                                              H, Y, pf, part_bytes, act, bias, s);
+                                              O16, pf, part_bytes, act, bias, s);
 }
 
 }  // namespace
@@ -703,8 +723,8 @@ hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t 
         return launch_gemm<0>(pick_tile(rows_per_expert, d_ff, E),
                               static_cast<const unsigned short *>(x),
                               static_cast<const unsigned short *>(w_up), d, d_ff, E, k, ceff,
-                              used, slot_token, tiles, static_cast<unsigned short *>(H), nullptr,
-                              part, part_bytes, act, b_up, s);
+                              used, slot_token, tiles, static_cast<unsigned short *>(H), part,
+                              part_bytes, act, b_up, s);
     hipLaunchKernelGGL(experts_f32_kernel<0>,
                        dim3((unsigned)((d_ff + 63) / 64), (unsigned)((ceff + 63) / 64), E),
                        dim3(256), 0, s, static_cast<const float *>(x),
@@ -715,7 +735,7 @@ hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t 
 
 hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int64_t d,
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
-                              const int32_t *slot_token, const int32_t *tiles, float *Y,
+                              const int32_t *slot_token, const int32_t *tiles, void *Y,
                               int64_t rows_per_expert, void *part, size_t part_bytes,
                               const float *b_down, hipStream_t s) {
     if (ceff == 0)
@@ -724,13 +744,13 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
         return launch_gemm<1>(pick_tile(rows_per_expert, d, E),
                               static_cast<const unsigned short *>(H),
                               static_cast<const unsigned short *>(w_down), d_ff, d, E, k, ceff,
-                              used, slot_token, tiles, nullptr, Y, part, part_bytes, kActRelu,
-                              b_down, s);
+                              used, slot_token, tiles, static_cast<unsigned short *>(Y), part,
+                              part_bytes, kActRelu, b_down, s);
     hipLaunchKernelGGL(experts_f32_kernel<1>,
                        dim3((unsigned)((d + 63) / 64), (unsigned)((ceff + 63) / 64), E),
                        dim3(256), 0, s, static_cast<const float *>(H),
                        static_cast<const float *>(w_down), (int)d_ff, (int)d, k, (int)ceff, used,
-                       slot_token, (float *)nullptr, Y, kActRelu, b_down);
+                       slot_token, (float *)nullptr, static_cast<float *>(Y), kActRelu, b_down);
     return hipGetLastError();
 }
 

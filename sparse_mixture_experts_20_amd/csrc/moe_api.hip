@@ -60,7 +60,7 @@ Layout layout_of(const Dims &m) {
     L.tiles = o;      o += align_up((size_t)(2 * (m.E + 1)) * 4);
     L.slot_token = o; o += align_up((size_t)(m.E * m.ceff) * 4);
     L.H = o;          o += align_up((size_t)(m.E * m.ceff * m.d_ff) * dtype_size(m.dtype));
-    L.Y = o;          o += align_up(nk * (size_t)m.d * 4);
+    L.Y = o;          o += align_up(nk * (size_t)m.d * dtype_size(m.dtype));
     L.router = o;     o += router_bytes(m.N, m.d, m.E, m.dtype);
     L.part = o;       o += expert_bytes(m.dtype);
     L.total = o;
@@ -366,7 +366,7 @@ int moe_expert_up_ex(const moe_tensor *x, const moe_tensor *W_up, const moe_expe
 
 static int expert_down_impl(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
                             const int32_t *used, const int32_t *slot_token,
-                            const int32_t *tiles, const void *H, float *Y, void *workspace,
+                            const int32_t *tiles, const void *H, void *Y, void *workspace,
                             size_t workspace_bytes, void *stream, const ExpertOpts &o) {
     if (!W_down)
         return MOE_ERR_NULL;
@@ -386,7 +386,7 @@ static int expert_down_impl(int64_t N, const moe_tensor *W_down, int k, int64_t 
     if (!W_down->data || !used || !slot_token || !tiles || !H || !Y)
         return MOE_ERR_NULL;
     const bool bf16 = W_down->dtype == MOE_BF16;
-    if (bf16 && (!aligned(W_down->data, 16) || !aligned(H, 16)))
+    if (bf16 && (!aligned(W_down->data, 16) || !aligned(H, 16) || !aligned(Y, 16)))
         return MOE_ERR_ALIGN;
     rc = check_expert_ws(workspace);
     if (rc != MOE_OK)
@@ -400,7 +400,7 @@ static int expert_down_impl(int64_t N, const moe_tensor *W_down, int k, int64_t 
 
 int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
                     const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
-                    const void *H, float *Y, void *workspace, size_t workspace_bytes,
+                    const void *H, void *Y, void *workspace, size_t workspace_bytes,
                     void *stream) {
     return expert_down_impl(N, W_down, k, capacity, used, slot_token, tiles, H, Y, workspace,
                             workspace_bytes, stream, ExpertOpts{});
@@ -408,7 +408,7 @@ int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity
 
 int moe_expert_down_ex(int64_t N, const moe_tensor *W_down, const moe_expert_opts *opts, int k,
                        int64_t capacity, const int32_t *used, const int32_t *slot_token,
-                       const int32_t *tiles, const void *H, float *Y, void *workspace,
+                       const int32_t *tiles, const void *H, void *Y, void *workspace,
                        size_t workspace_bytes, void *stream) {
     if (!W_down)
         return MOE_ERR_NULL;
@@ -424,7 +424,7 @@ int moe_expert_down_ex(int64_t N, const moe_tensor *W_down, const moe_expert_opt
 
 int moe_experts_ex(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W_down,
                    const moe_expert_opts *opts, int k, int64_t capacity, const int32_t *used,
-                   const int32_t *slot_token, const int32_t *tiles, void *H, float *Y,
+                   const int32_t *slot_token, const int32_t *tiles, void *H, void *Y,
                    void *workspace, size_t workspace_bytes, void *stream) {
     if (!x || !W_up || !W_down)
         return MOE_ERR_NULL;
@@ -462,30 +462,34 @@ int moe_experts_ex(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor
 
 int moe_experts(const moe_tensor *x, const moe_tensor *W_up, const moe_tensor *W_down, int k,
                 int64_t capacity, const int32_t *used, const int32_t *slot_token,
-                const int32_t *tiles, void *H, float *Y, void *workspace,
+                const int32_t *tiles, void *H, void *Y, void *workspace,
                 size_t workspace_bytes, void *stream) {
     return moe_experts_ex(x, W_up, W_down, nullptr, k, capacity, used, slot_token, tiles, H, Y,
                           workspace, workspace_bytes, stream);
 }
 
-int moe_combine(int64_t N, int64_t d, int k, const float *Y, const float *topk_gate,
+int moe_combine(int64_t N, int64_t d, int k, const moe_tensor *Y, const float *topk_gate,
                 const int32_t *slot, moe_tensor *out, void *stream) {
-    if (!out)
+    if (!out || !Y)
         return MOE_ERR_NULL;
     if (N < 0 || d <= 0 || k < 1 || k > MOE_MAX_TOPK)
         return MOE_ERR_ARG;
     int64_t oN, od;
     if (!act_rows(out, oN, od) || oN != N || od != d)
         return MOE_ERR_SHAPE;
-    if (!valid_dtype(out->dtype))
+    if (Y->ndim != 2 || Y->shape[0] != N * k || Y->shape[1] != d)
+        return MOE_ERR_SHAPE;
+    if (!valid_dtype(out->dtype) || !valid_dtype(Y->dtype))
         return MOE_ERR_DTYPE;
     if (N == 0)
         return MOE_OK;
-    if (!Y || !topk_gate || !slot || !out->data)
+    if (!Y->data || !topk_gate || !slot || !out->data)
         return MOE_ERR_NULL;
-    if (d % 4 == 0 && (!aligned(Y, 16) || !aligned(out->data, out->dtype == MOE_BF16 ? 8 : 16)))
+    const bool vec = Y->dtype == MOE_BF16 ? d % 8 == 0 : d % 4 == 0;
+    if (vec && (!aligned(Y->data, 16) || !aligned(out->data, out->dtype == MOE_BF16 ? 8 : 16)))
         return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_combine(Y, topk_gate, slot, N, d, k, out->data, out->dtype,
+    return hip_status(moe::launch_combine(Y->data, Y->dtype == MOE_BF16 ? 1 : 0, topk_gate, slot,
+                                          N, d, k, out->data, out->dtype,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -553,7 +557,7 @@ int moe_forward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor 
     int32_t *tiles = reinterpret_cast<int32_t *>(ws + L.tiles);
     int32_t *slot_token = reinterpret_cast<int32_t *>(ws + L.slot_token);
     void *H = ws + L.H;
-    float *Y = reinterpret_cast<float *>(ws + L.Y);
+    void *Y = ws + L.Y;   // expert outputs in the dtype of x
     stats->capacity = m.C;
 
     rc = router_checked(x, W_g, noise, N, d, E, k, idx, gate, ws + L.router, s);
@@ -568,7 +572,7 @@ int moe_forward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor 
                                   slot_token, tiles, H, rpe, part, part_bytes, o.act, o.b_up, s));
     MOE_TRY(moe::launch_expert_down(bf16, H, W_down->data, d, d_ff, (int)E, k, m.ceff, used,
                                     slot_token, tiles, Y, rpe, part, part_bytes, o.b_down, s));
-    MOE_TRY(moe::launch_combine(Y, gate, slot, N, d, k, out->data, out->dtype, s));
+    MOE_TRY(moe::launch_combine(Y, bf16 ? 1 : 0, gate, slot, N, d, k, out->data, out->dtype, s));
     return MOE_OK;
 }
 

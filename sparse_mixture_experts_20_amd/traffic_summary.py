@@ -61,11 +61,11 @@ def algorithmic(kernel, p):
     if m and m.group(1) == "0":       # x (whole), W_up, H rows written
         return N * d * sx + E * dff * d * sx + kept * dff * sx, "x + W_up + H"
     if m and m.group(1) == "1":       # H rows read, W_down, Y rows written
-        return kept * dff * sx + E * d * dff * sx + kept * d * 4, "H + W_down + Y (fp32)"
+        return kept * dff * sx + E * d * dff * sx + kept * d * sx, "H + W_down + Y"
     if kernel.startswith("router"):
         return N * d * sx + E * d * 4 + noise + N * k * 8, "x + W_g + noise + ids/gates"
     if kernel.startswith("combine"):
-        return kept * d * 4 + N * k * 8 + N * d * sx, "Y + ids/gates + out"
+        return kept * d * sx + N * k * 8 + N * d * sx, "Y + ids/gates + out"
     return None, ""
 
 

@@ -38,6 +38,15 @@ def to_np(t):
     return t.cpu().numpy()
 
 
+def f64(t):
+    """A device tensor (fp32 or bf16) as a float64 numpy array of its exact values."""
+    from sparse_mixture_experts_20_amd import workloads as W
+    a = to_np(t)
+    if a.dtype == np.uint16:
+        return W.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
 def out_f64(wl, out_t, rows=None):
     from sparse_mixture_experts_20_amd import workloads as W
     a = to_np(out_t)

@@ -56,8 +56,8 @@ def test_capacity_helper(L):
 def test_workspace_size(L):
     ws = B.lib().moe_workspace_size
     n = ws(2048, 768, 8, 3072, 2, 1.25, BF16)
-    # at least H (E*C*d_ff bf16) and Y (N*k*d fp32)
-    assert n >= 8 * 640 * 3072 * 2 + 2048 * 2 * 768 * 4
+    # at least H (E*C*d_ff) and Y (N*k*d), both bf16 here
+    assert n >= 8 * 640 * 3072 * 2 + 2048 * 2 * 768 * 2
     assert n % 256 == 0
     assert ws(2048, 768, 8, 3072, 9, 1.25, BF16) == 0      # k > E
     assert ws(2048, 768, 8, 3072, 2, -1.0, BF16) == 0      # cf <= 0
@@ -144,12 +144,18 @@ def test_stage_entry_points_reject_bad_arguments(L):
     assert L.moe_dispatch(10, 4, 2, 0, v, v, v, v, v, None) == -4
     assert L.moe_dispatch(10, 300, 2, 3, v, v, v, v, v, None) == -6
     assert L.moe_dispatch(10, 4, 2, 3, None, v, v, v, v, None) == -1
-    # combine: shape mismatch, bad dtype
+    # combine: shape mismatch, bad dtype, Y rows [N*k, d] of fp32 or bf16
     out = _t(FAKE, F32, 10, 8)
-    assert L.moe_combine(11, 8, 2, v, v, v, ctypes.byref(out), None) == -2
+    yb = _t(FAKE, BF16, 20, 8)
+    r = ctypes.byref
+    assert L.moe_combine(11, 8, 2, r(yb), v, v, r(out), None) == -2
     bad = _t(FAKE, 5, 10, 8)
-    assert L.moe_combine(10, 8, 2, v, v, v, ctypes.byref(bad), None) == -3
-    assert L.moe_combine(10, 8, 2, None, v, v, ctypes.byref(out), None) == -1
+    assert L.moe_combine(10, 8, 2, r(yb), v, v, r(bad), None) == -3
+    assert L.moe_combine(10, 8, 2, None, v, v, r(out), None) == -1
+    assert L.moe_combine(10, 8, 2, r(_t(FAKE, BF16, 21, 8)), v, v, r(out), None) == -2
+    assert L.moe_combine(10, 8, 2, r(_t(FAKE, 5, 20, 8)), v, v, r(out), None) == -3
+    assert L.moe_combine(10, 8, 2, r(_t(0, BF16, 20, 8)), v, v, r(out), None) == -1
+    assert L.moe_combine(10, 8, 2, r(_t(FAKE + 8, BF16, 20, 8)), v, v, r(out), None) == -7
     # router: k > E, W_g dtype
     x = _t(FAKE, BF16, 10, 16)
     wg = _t(FAKE, F32, 4, 16)
@@ -188,7 +194,7 @@ def test_expert_workspace_size(L):
     assert B.lib().moe_expert_workspace_size(7) == 0
     # and moe_forward's workspace holds it
     assert (B.lib().moe_workspace_size(2048, 768, 8, 3072, 2, 1.25, BF16)
-            >= 8 * 640 * 3072 * 2 + 2048 * 2 * 768 * 4 + 256 * 256 * 256 * 4)
+            >= 8 * 640 * 3072 * 2 + 2048 * 2 * 768 * 2 + 256 * 256 * 256 * 4)
 
 
 def test_expert_variant_options_are_validated(L):

@@ -117,7 +117,7 @@ def test_combine_matches_oracle(torch_mod, dt, ydt):
         assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0**-8 + 1e-6)
 
 
-@pytest.mark.parametrize("name", ["ragged", "mid"])
+@pytest.mark.parametrize("name", ["ragged", "mid", "expert_height"])
 def test_experts_match_oracle(torch_mod, name):
     """Grouped FFN over the oracle's own dispatch plan: every kept
     assignment's expert output row Y[t*k+j] against the oracle's y."""
@@ -127,9 +127,12 @@ def test_experts_match_oracle(torch_mod, name):
     if name == "ragged":
         wl = W.custom("x", N=700, d=200, E=6, k=2, d_ff=328, dtype="bf16", cf=0.9, sigma=0.4,
                       seed=51, w_std=0.05)
-    else:
+    elif name == "mid":
         wl = W.custom("x", N=2048, d=768, E=8, k=2, d_ff=3072, dtype="bf16", cf=1.25,
                       sigma=1.0, seed=52, w_std=0.02)
+    else:   # ~200 rows per expert over 32 experts (two 128-row tiles, the second ragged)
+        wl = W.custom("x", N=3200, d=264, E=32, k=2, d_ff=392, dtype="bf16", cf=1.5,
+                      sigma=0.5, seed=54, w_std=0.05)
     G.say(f"[stage] experts {name}")
     res = oracle.forward(wl, want_y=True)
     dev = D.upload(wl)

@@ -18,6 +18,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -36,8 +37,14 @@ def log(*a):
 
 
 def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source with its comments and spacing removed (an edit
+    of comments alone does not change the kernel the counters measured)."""
+    with open(path) as f:
+        t = f.read()
+    t = re.sub(r"//[^\n]*", "", t)
+    t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)
+    t = re.sub(r"\s+", " ", t).strip()
+    return hashlib.sha256(t.encode()).hexdigest()[:16]
 
 
 def traffic_for(kernel, workload):

@@ -2,10 +2,11 @@
 // Page 1 ("Mixture of Experts (MoE) 12段階極小ビジュアル解剖シミュレーター"),
 // STEP 7 (each token is copied only to its kept experts), STEP 8 (z = W_up x),
 // STEP 9 (h = ReLU(z)), STEP 10 (E(x) = W_down h); nanoMoE slides 32-37 (the
-// experts are batched: one product per expert over its packed token rows).
+// experts are batched: one product per expert over its packed token rows;
+// slide 32 also gives the expert variant with biases and GELU).
 //
-//   up:   H[e, r, :] = ReLU(W_up[e] x_t)   for r < used[e], t = slot_token[e, r] / k
-//   down: Y[a, :]    = W_down[e] H[e, r, :]  with a = slot_token[e, r]
+//   up:   H[e, r, :] = act(W_up[e] x_t + b_up[e])  for r < used[e], t = slot_token[e, r] / k
+//   down: Y[a, :]    = W_down[e] H[e, r, :] + b_down[e]  with a = slot_token[e, r]
 //
 // Both are "NT" products: every operand row is contiguous along the
 // reduction dimension (activation rows along d or d_ff, weight rows are
@@ -13,24 +14,27 @@
 // a CDNA matrix instruction want. The gather of token rows (dispatch) is
 // fused into the up product's operand load, so no packed copy of the tokens
 // is ever written; the down product scatters its rows straight into the
-// assignment-ordered buffer the combine reads.
+// assignment-ordered buffer the combine reads. Both accumulate in fp32 and
+// round once to bf16 in the epilogue.
 //
 // bf16 kernel: a BM x BN output tile per workgroup, K-step 64, waves laid out
-// WAVES_M x WAVES_N with a 16x16x32 bf16 MFMA grid each (fp32 accumulation).
-// A and B K-tiles are double-buffered in LDS (rows padded by 16 bytes so the
-// 16-byte operand reads of a wave hit distinct banks) and staged through
-// registers P tiles ahead of use: the loads of tile kt+P are issued before
-// the MFMAs of tile kt. Barriers wait on LDS traffic only, so those loads
-// stay in flight across them (a workgroup fence would drain them every
-// K-step). The epilogue transposes each wave's 16-row strips through LDS so
-// every lane stores 16 contiguous bytes.
+// WAVES_M x WAVES_N with a 16x16x32 bf16 MFMA grid each. A and B K-tiles go
+// from global memory straight into a two-stage LDS ring (direct 16-byte
+// loads, no register round trip; 16-byte chunks XOR-swizzled per row so the
+// operand reads of a wave hit distinct banks); the loads of step kt+1 are
+// issued before the MFMAs of step kt and stay in flight across the barrier,
+// which waits on LDS traffic only. Waves skip the MFMAs of 16-row strips
+// that lie wholly past used[e]. The epilogue transposes each wave's 16-row
+// strips through LDS so every lane stores 16 contiguous bytes.
 //
 // Scheduling: tiles exist only for rows that exist (the dispatch plan's
 // prefix of ceil(used[e]/BM), read on the device, so no host sync). The tile
 // index walks an expert's row tiles fastest, so the blocks in flight share
 // each weight tile, and block b (placed on XCD b mod 8 by the dispatcher)
 // takes tile (b mod 8) * T/8 + b/8: every XCD works through one contiguous
-// range of tiles and the sharing happens inside its own L2.
+// range of tiles and the sharing happens inside its own L2. When the last
+// round of tiles would leave most workgroups idle, its tiles are cut into
+// K-ranges (split_plan below).
 #include <type_traits>
 
 #include "common.hpp"

@@ -27,8 +27,14 @@ COPY_BYTES = 1 << 30
 
 
 def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source with its comments and spacing removed (the
+    same definition bench.py checks against)."""
+    with open(path) as f:
+        t = f.read()
+    t = re.sub(r"//[^\n]*", "", t)
+    t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)
+    t = re.sub(r"\s+", " ", t).strip()
+    return hashlib.sha256(t.encode()).hexdigest()[:16]
 
 
 def short(name):

@@ -49,6 +49,9 @@ def lib():
         L.oracle_expert_rows.restype = None
         L.oracle_combine.argtypes = [_i64, _i64, _i32, _dp, _ip, _dp, _dp]
         L.oracle_combine.restype = None
+        L.oracle_backward.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _dp, _dp, _dp, _dp, _dp,
+                                      _dp, _dp, _dp, _dp, _dp]
+        L.oracle_backward.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = ctypes.c_int
         _lib = L
@@ -145,6 +148,35 @@ def combine(gate: np.ndarray, slot: np.ndarray, y: np.ndarray) -> np.ndarray:
         lib().oracle_combine(n, d, k, _ptr(gate, _dp), _ptr(slot, _ip), _ptr(y, _dp),
                              _ptr(out, _dp))
     return out
+
+
+def backward(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout64):
+    """Gradients of the layer (ReLU experts, no biases) for the output
+    gradient dout [N, d]: returns (dx [N, d], dW_g [E, d], dW_up [E, d_ff, d],
+    dW_down [E, d, d_ff]), all float64. wups64/wdowns64 are [E, d_ff, d] and
+    [E, d, d_ff] arrays (or lists of per-expert matrices)."""
+    x64 = _c(x64, np.float64)
+    wg64 = _c(wg64, np.float64)
+    wu = _c(np.stack(list(wups64)) if isinstance(wups64, (list, tuple)) else wups64, np.float64)
+    wd = _c(np.stack(list(wdowns64)) if isinstance(wdowns64, (list, tuple)) else wdowns64,
+            np.float64)
+    n64 = None if noise64 is None else _c(noise64, np.float64)
+    dout64 = _c(dout64, np.float64)
+    N, d = x64.shape
+    E, d_ff = wu.shape[0], wu.shape[1]
+    if wd.shape != (E, d, d_ff) or dout64.shape != (N, d) or wg64.shape != (E, d):
+        raise ValueError("shapes")
+    C = capacity(N, E, k, cf)
+    dx = np.empty((N, d))
+    dwg = np.empty((E, d))
+    dwu = np.empty((E, d_ff, d))
+    dwd = np.empty((E, d, d_ff))
+    rc = lib().oracle_backward(N, d, E, k, d_ff, C, _ptr(x64, _dp), _ptr(wg64, _dp),
+                               _ptr(n64, _dp), _ptr(wu, _dp), _ptr(wd, _dp), _ptr(dout64, _dp),
+                               _ptr(dx, _dp), _ptr(dwg, _dp), _ptr(dwu, _dp), _ptr(dwd, _dp))
+    if rc != 0:
+        raise MemoryError("oracle_backward: allocation failed")
+    return dx, dwg, dwu, dwd
 
 
 class Result:

@@ -39,6 +39,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 /* ---------------------------------------------------------------------- */
 /* [P1 STEP 2, STEP 4]  s = W_g x + eps; the caller passes eps (= sigma*N(0,1)
@@ -171,6 +172,133 @@ void oracle_expert_rows(int64_t d, int64_t d_ff, int64_t n, const int64_t *token
             yr[o] = acc;
         }
     }
+}
+
+/* The layer's backward pass (the next row after the forward: gradients
+ * through the gates to the router and through the experts; ReLU experts
+ * without biases, dropout off). Derived by the chain rule from the forward
+ * above, for a loss whose gradient with respect to out is dout [N, d]:
+ *   combine  out_t = sum_j g_tj y_tj (kept j)      -> dy_tj = g_tj dout_t,
+ *                                                     dg_tj = <dout_t, y_tj>
+ *            (dropped j: dy = 0 and dg = 0)
+ *   softmax  g_tj = exp(s_j) / sum_l exp(s_l) over the k kept scores
+ *                                                  -> ds_j = g_j (dg_j - sum_l g_l dg_l);
+ *            scores outside the top-k get no gradient (the -inf mask; the
+ *            choice of the top k is piecewise constant)
+ *   scores   s_te = W_g[e] x_t + noise_te           -> dW_g[e] += ds_te x_t,
+ *                                                     dx_t += ds_te W_g[e]
+ *   expert   z = W_up x_t, h = ReLU(z), y = W_down h -> dW_down += dy h^T,
+ *            dh = W_down^T dy, dz = dh (z > 0), dW_up += dz x_t^T,
+ *            dx_t += W_up^T dz
+ * The gate derivative treats the float32 rounding of the scores as the
+ * identity. Sums over tokens run in token order, then choice order.
+ * dx [N, d], dWg [E, d], dWup [E, d_ff, d], dWdown [E, d, d_ff]; C = capacity.
+ * Scratch is allocated here (test infrastructure; not a hot path). Returns 0,
+ * or -1 if an allocation fails. Serial on purpose: the sums into the weight
+ * gradients have one fixed order. */
+int oracle_backward(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff, int64_t C,
+                    const double *x, const double *Wg, const double *noise,
+                    const double *Wup, const double *Wdown, const double *dout,
+                    double *dx, double *dWg, double *dWup, double *dWdown)
+{
+    float *scores = (float *)malloc(sizeof(float) * (size_t)(N * E));
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N * k));
+    double *gate = (double *)malloc(sizeof(double) * (size_t)(N * k));
+    int32_t *slot = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N * k));
+    int32_t *used = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    double *z = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *h = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *y = (double *)malloc(sizeof(double) * (size_t)d);
+    double *dz = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *dg = (double *)malloc(sizeof(double) * (size_t)k);
+    int rc = 0;
+    if (!scores || !idx || !gate || !slot || !used || !z || !h || !y || !dz || !dg) {
+        rc = -1;
+        goto done;
+    }
+    oracle_router(N, d, E, k, x, Wg, noise, scores, idx, gate);
+    oracle_assign(N, E, k, C, idx, slot, used);
+    for (int64_t i = 0; i < N * d; ++i)
+        dx[i] = 0.0;
+    for (int64_t i = 0; i < E * d; ++i)
+        dWg[i] = 0.0;
+    for (int64_t i = 0; i < E * d_ff * d; ++i) {
+        dWup[i] = 0.0;
+        dWdown[i] = 0.0;
+    }
+    for (int64_t t = 0; t < N; ++t) {
+        const double *xt = x + t * d;
+        const double *go = dout + t * d;
+        double *dxt = dx + t * d;
+        for (int32_t j = 0; j < k; ++j) {
+            dg[j] = 0.0;
+            if (slot[t * k + j] < 0)
+                continue;                      /* dropped: contributes nothing */
+            const int64_t e = idx[t * k + j];
+            const double g = gate[t * k + j];
+            const double *wu = Wup + e * d_ff * d;
+            const double *wd = Wdown + e * d * d_ff;
+            for (int64_t f = 0; f < d_ff; ++f) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < d; ++i)
+                    acc += wu[f * d + i] * xt[i];
+                z[f] = acc;
+                h[f] = acc > 0.0 ? acc : 0.0;
+            }
+            for (int64_t o = 0; o < d; ++o) {
+                double acc = 0.0;
+                for (int64_t f = 0; f < d_ff; ++f)
+                    acc += wd[o * d_ff + f] * h[f];
+                y[o] = acc;
+            }
+            /* combine: dg = <dout_t, y>, dy = g dout_t */
+            double a = 0.0;
+            for (int64_t o = 0; o < d; ++o)
+                a += go[o] * y[o];
+            dg[j] = a;
+            /* down: dW_down += dy h^T; dh = W_down^T dy; ReLU */
+            double *gwd = dWdown + e * d * d_ff;
+            for (int64_t o = 0; o < d; ++o) {
+                const double dyo = g * go[o];
+                for (int64_t f = 0; f < d_ff; ++f)
+                    gwd[o * d_ff + f] += dyo * h[f];
+            }
+            for (int64_t f = 0; f < d_ff; ++f) {
+                double acc = 0.0;
+                if (z[f] > 0.0)
+                    for (int64_t o = 0; o < d; ++o)
+                        acc += wd[o * d_ff + f] * (g * go[o]);
+                dz[f] = acc;
+            }
+            /* up: dW_up += dz x_t^T; dx_t += W_up^T dz */
+            double *gwu = dWup + e * d_ff * d;
+            for (int64_t f = 0; f < d_ff; ++f)
+                for (int64_t i = 0; i < d; ++i)
+                    gwu[f * d + i] += dz[f] * xt[i];
+            for (int64_t i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int64_t f = 0; f < d_ff; ++f)
+                    acc += wu[f * d + i] * dz[f];
+                dxt[i] += acc;
+            }
+        }
+        /* softmax over the kept scores, then the score product */
+        double gdg = 0.0;
+        for (int32_t j = 0; j < k; ++j)
+            gdg += gate[t * k + j] * dg[j];
+        for (int32_t j = 0; j < k; ++j) {
+            const int64_t e = idx[t * k + j];
+            const double ds = gate[t * k + j] * (dg[j] - gdg);
+            for (int64_t i = 0; i < d; ++i) {
+                dWg[e * d + i] += ds * xt[i];
+                dxt[i] += ds * Wg[e * d + i];
+            }
+        }
+    }
+done:
+    free(scores); free(idx); free(gate); free(slot); free(used);
+    free(z); free(h); free(y); free(dz); free(dg);
+    return rc;
 }
 
 /* [P1 STEP 11-12, P2 slides 38-40] output rows: each kept assignment's

@@ -255,6 +255,39 @@ int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity
 int moe_combine(int64_t N, int64_t d, int k, const moe_tensor *Y, const float *topk_gate,
                 const int32_t *slot, moe_tensor *out, void *stream);
 
+/* Backward pass of the layer (the row after the forward: gradients through
+ * the gates to the router and through the experts), for bf16 layers with
+ * ReLU experts and no biases; dropout is not applied. For a loss whose
+ * gradient with respect to out is dout, by the chain rule of moe_forward:
+ *   combine: dy = g * dout, dg = <dout, y> (kept choices; dropped: 0);
+ *   masked softmax over the kept scores: ds_j = g_j (dg_j - sum_l g_l dg_l),
+ *   and no gradient through the top-k choice or to experts outside it;
+ *   scores: dW_g = ds^T x, dx += ds W_g;
+ *   experts: dZ = (dY W_down) where H > 0, dW_down = dY^T H, dW_up = dZ^T X,
+ *   dx += the kept choices' dZ W_up rows, summed in choice order.
+ * The forward state (routing, dispatch plan, H and the experts' outputs in
+ * fp32) is recomputed from the inputs in the workspace, so the call takes
+ * the forward's arguments plus:
+ *   dout    [N, d]         same dtype as x (MOE_BF16)
+ *   dx      [N, d]         MOE_F32, written
+ *   dW_g    [E, d]         MOE_F32, written
+ *   dW_up   [E, d_ff, d]   MOE_F32, written
+ *   dW_down [E, d, d_ff]   MOE_F32, written
+ *   stats   as for moe_forward, with moe_backward_workspace_size() bytes
+ * Products run on the matrix cores with bf16 operands (dy and dZ are rounded
+ * to bf16; fp32 ds is split exactly into three bf16 terms) and fp32
+ * accumulation; every sum has a fixed order. MOE_ERR_UNSUPPORTED for fp32
+ * layers. Device pointers 16-byte aligned (MOE_ERR_ALIGN). */
+int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                 const moe_tensor *W_up, const moe_tensor *W_down, int k, float capacity_factor,
+                 const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g, moe_tensor *dW_up,
+                 moe_tensor *dW_down, moe_stats *stats);
+
+/* Bytes of workspace moe_backward needs (0 on invalid sizes or a dtype
+ * other than MOE_BF16). */
+size_t moe_backward_workspace_size(int64_t N, int64_t d, int64_t E, int64_t d_ff, int k,
+                                   float capacity_factor, int32_t dtype);
+
 #ifdef __cplusplus
 }
 #endif

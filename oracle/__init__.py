@@ -52,6 +52,9 @@ def lib():
         L.oracle_backward.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _dp, _dp, _dp, _dp, _dp,
                                       _dp, _dp, _dp, _dp, _dp]
         L.oracle_backward.restype = ctypes.c_int
+        L.oracle_backward_rows.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _dp, _dp, _dp,
+                                           _dp, _dp, _dp, _i64, _lp, _dp]
+        L.oracle_backward_rows.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = ctypes.c_int
         _lib = L
@@ -177,6 +180,35 @@ def backward(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout64):
     if rc != 0:
         raise MemoryError("oracle_backward: allocation failed")
     return dx, dwg, dwu, dwd
+
+
+def backward_rows(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout64,
+                  rows: Sequence[int]):
+    """dx [len(rows), d] (float64) of the listed tokens, as ``backward``
+    computes it; the routing covers every token, the expert terms only the
+    listed ones (for layers too large for the full backward)."""
+    x64 = _c(x64, np.float64)
+    wg64 = _c(wg64, np.float64)
+    wu = _c(np.stack(list(wups64)) if isinstance(wups64, (list, tuple)) else wups64, np.float64)
+    wd = _c(np.stack(list(wdowns64)) if isinstance(wdowns64, (list, tuple)) else wdowns64,
+            np.float64)
+    n64 = None if noise64 is None else _c(noise64, np.float64)
+    dout64 = _c(dout64, np.float64)
+    N, d = x64.shape
+    E, d_ff = wu.shape[0], wu.shape[1]
+    if wd.shape != (E, d, d_ff) or dout64.shape != (N, d) or wg64.shape != (E, d):
+        raise ValueError("shapes")
+    r = _c(np.asarray(rows, dtype=np.int64), np.int64)
+    if r.size and (r.min() < 0 or r.max() >= N):
+        raise ValueError("rows out of range")
+    dx = np.empty((r.size, d))
+    rc = lib().oracle_backward_rows(N, d, E, k, d_ff, capacity(N, E, k, cf), _ptr(x64, _dp),
+                                    _ptr(wg64, _dp), _ptr(n64, _dp), _ptr(wu, _dp),
+                                    _ptr(wd, _dp), _ptr(dout64, _dp), r.size, _ptr(r, _lp),
+                                    _ptr(dx, _dp))
+    if rc != 0:
+        raise MemoryError("oracle_backward_rows: allocation failed")
+    return dx
 
 
 class Result:

@@ -174,6 +174,137 @@ void oracle_expert_rows(int64_t d, int64_t d_ff, int64_t n, const int64_t *token
     }
 }
 
+/* The backward of one token t: adds its terms to dx_t and, when the
+ * pointers are not NULL, to dWg, dWup and dWdown. gate, slot, idx are the
+ * routing of all tokens; z, h, y, dz [d_ff or d] and dg [k] are scratch. */
+static void backward_token(int64_t t, int64_t d, int32_t k, int64_t d_ff,
+                           const double *x, const double *Wg, const double *Wup,
+                           const double *Wdown, const double *dout, const int32_t *idx,
+                           const double *gate, const int32_t *slot, double *dxt,
+                           double *dWg, double *dWup, double *dWdown, double *z, double *h,
+                           double *y, double *dz, double *dg)
+{
+    const double *xt = x + t * d;
+    const double *go = dout + t * d;
+    for (int32_t j = 0; j < k; ++j) {
+        dg[j] = 0.0;
+        if (slot[t * k + j] < 0)
+            continue;                      /* dropped: contributes nothing */
+        const int64_t e = idx[t * k + j];
+        const double g = gate[t * k + j];
+        const double *wu = Wup + e * d_ff * d;
+        const double *wd = Wdown + e * d * d_ff;
+        for (int64_t f = 0; f < d_ff; ++f) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < d; ++i)
+                acc += wu[f * d + i] * xt[i];
+            z[f] = acc;
+            h[f] = acc > 0.0 ? acc : 0.0;
+        }
+        for (int64_t o = 0; o < d; ++o) {
+            double acc = 0.0;
+            for (int64_t f = 0; f < d_ff; ++f)
+                acc += wd[o * d_ff + f] * h[f];
+            y[o] = acc;
+        }
+        /* combine: dg = <dout_t, y>, dy = g dout_t */
+        double a = 0.0;
+        for (int64_t o = 0; o < d; ++o)
+            a += go[o] * y[o];
+        dg[j] = a;
+        /* down: dW_down += dy h^T; dh = W_down^T dy; ReLU */
+        if (dWdown) {
+            double *gwd = dWdown + e * d * d_ff;
+            for (int64_t o = 0; o < d; ++o) {
+                const double dyo = g * go[o];
+                for (int64_t f = 0; f < d_ff; ++f)
+                    gwd[o * d_ff + f] += dyo * h[f];
+            }
+        }
+        for (int64_t f = 0; f < d_ff; ++f) {
+            double acc = 0.0;
+            if (z[f] > 0.0)
+                for (int64_t o = 0; o < d; ++o)
+                    acc += wd[o * d_ff + f] * (g * go[o]);
+            dz[f] = acc;
+        }
+        /* up: dW_up += dz x_t^T; dx_t += W_up^T dz */
+        if (dWup) {
+            double *gwu = dWup + e * d_ff * d;
+            for (int64_t f = 0; f < d_ff; ++f)
+                for (int64_t i = 0; i < d; ++i)
+                    gwu[f * d + i] += dz[f] * xt[i];
+        }
+        for (int64_t i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int64_t f = 0; f < d_ff; ++f)
+                acc += wu[f * d + i] * dz[f];
+            dxt[i] += acc;
+        }
+    }
+    /* softmax over the kept scores, then the score product */
+    double gdg = 0.0;
+    for (int32_t j = 0; j < k; ++j)
+        gdg += gate[t * k + j] * dg[j];
+    for (int32_t j = 0; j < k; ++j) {
+        const int64_t e = idx[t * k + j];
+        const double ds = gate[t * k + j] * (dg[j] - gdg);
+        for (int64_t i = 0; i < d; ++i) {
+            if (dWg)
+                dWg[e * d + i] += ds * xt[i];
+            dxt[i] += ds * Wg[e * d + i];
+        }
+    }
+}
+
+/* Routing of all tokens followed by the backward of the tokens listed in
+ * rows (all N when rows is NULL). Weight gradients are accumulated when
+ * their pointers are not NULL; dx holds one row per listed token. */
+static int backward_impl(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff, int64_t C,
+                         const double *x, const double *Wg, const double *noise,
+                         const double *Wup, const double *Wdown, const double *dout,
+                         int64_t nrows, const int64_t *rows, double *dx, double *dWg,
+                         double *dWup, double *dWdown)
+{
+    float *scores = (float *)malloc(sizeof(float) * (size_t)(N * E + 1));
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N * k + 1));
+    double *gate = (double *)malloc(sizeof(double) * (size_t)(N * k + 1));
+    int32_t *slot = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N * k + 1));
+    int32_t *used = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    double *z = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *h = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *y = (double *)malloc(sizeof(double) * (size_t)d);
+    double *dz = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    double *dg = (double *)malloc(sizeof(double) * (size_t)k);
+    int rc = 0;
+    if (!scores || !idx || !gate || !slot || !used || !z || !h || !y || !dz || !dg) {
+        rc = -1;
+        goto done;
+    }
+    oracle_router(N, d, E, k, x, Wg, noise, scores, idx, gate);
+    oracle_assign(N, E, k, C, idx, slot, used);
+    for (int64_t i = 0; i < nrows * d; ++i)
+        dx[i] = 0.0;
+    if (dWg)
+        for (int64_t i = 0; i < E * d; ++i)
+            dWg[i] = 0.0;
+    if (dWup)
+        for (int64_t i = 0; i < E * d_ff * d; ++i)
+            dWup[i] = 0.0;
+    if (dWdown)
+        for (int64_t i = 0; i < E * d * d_ff; ++i)
+            dWdown[i] = 0.0;
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t t = rows ? rows[r] : r;
+        backward_token(t, d, k, d_ff, x, Wg, Wup, Wdown, dout, idx, gate, slot, dx + r * d,
+                       dWg, dWup, dWdown, z, h, y, dz, dg);
+    }
+done:
+    free(scores); free(idx); free(gate); free(slot); free(used);
+    free(z); free(h); free(y); free(dz); free(dg);
+    return rc;
+}
+
 /* The layer's backward pass (the next row after the forward: gradients
  * through the gates to the router and through the experts; ReLU experts
  * without biases, dropout off). Derived by the chain rule from the forward
@@ -201,104 +332,21 @@ int oracle_backward(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff, in
                     const double *Wup, const double *Wdown, const double *dout,
                     double *dx, double *dWg, double *dWup, double *dWdown)
 {
-    float *scores = (float *)malloc(sizeof(float) * (size_t)(N * E));
-    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N * k));
-    double *gate = (double *)malloc(sizeof(double) * (size_t)(N * k));
-    int32_t *slot = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N * k));
-    int32_t *used = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
-    double *z = (double *)malloc(sizeof(double) * (size_t)d_ff);
-    double *h = (double *)malloc(sizeof(double) * (size_t)d_ff);
-    double *y = (double *)malloc(sizeof(double) * (size_t)d);
-    double *dz = (double *)malloc(sizeof(double) * (size_t)d_ff);
-    double *dg = (double *)malloc(sizeof(double) * (size_t)k);
-    int rc = 0;
-    if (!scores || !idx || !gate || !slot || !used || !z || !h || !y || !dz || !dg) {
-        rc = -1;
-        goto done;
-    }
-    oracle_router(N, d, E, k, x, Wg, noise, scores, idx, gate);
-    oracle_assign(N, E, k, C, idx, slot, used);
-    for (int64_t i = 0; i < N * d; ++i)
-        dx[i] = 0.0;
-    for (int64_t i = 0; i < E * d; ++i)
-        dWg[i] = 0.0;
-    for (int64_t i = 0; i < E * d_ff * d; ++i) {
-        dWup[i] = 0.0;
-        dWdown[i] = 0.0;
-    }
-    for (int64_t t = 0; t < N; ++t) {
-        const double *xt = x + t * d;
-        const double *go = dout + t * d;
-        double *dxt = dx + t * d;
-        for (int32_t j = 0; j < k; ++j) {
-            dg[j] = 0.0;
-            if (slot[t * k + j] < 0)
-                continue;                      /* dropped: contributes nothing */
-            const int64_t e = idx[t * k + j];
-            const double g = gate[t * k + j];
-            const double *wu = Wup + e * d_ff * d;
-            const double *wd = Wdown + e * d * d_ff;
-            for (int64_t f = 0; f < d_ff; ++f) {
-                double acc = 0.0;
-                for (int64_t i = 0; i < d; ++i)
-                    acc += wu[f * d + i] * xt[i];
-                z[f] = acc;
-                h[f] = acc > 0.0 ? acc : 0.0;
-            }
-            for (int64_t o = 0; o < d; ++o) {
-                double acc = 0.0;
-                for (int64_t f = 0; f < d_ff; ++f)
-                    acc += wd[o * d_ff + f] * h[f];
-                y[o] = acc;
-            }
-            /* combine: dg = <dout_t, y>, dy = g dout_t */
-            double a = 0.0;
-            for (int64_t o = 0; o < d; ++o)
-                a += go[o] * y[o];
-            dg[j] = a;
-            /* down: dW_down += dy h^T; dh = W_down^T dy; ReLU */
-            double *gwd = dWdown + e * d * d_ff;
-            for (int64_t o = 0; o < d; ++o) {
-                const double dyo = g * go[o];
-                for (int64_t f = 0; f < d_ff; ++f)
-                    gwd[o * d_ff + f] += dyo * h[f];
-            }
-            for (int64_t f = 0; f < d_ff; ++f) {
-                double acc = 0.0;
-                if (z[f] > 0.0)
-                    for (int64_t o = 0; o < d; ++o)
-                        acc += wd[o * d_ff + f] * (g * go[o]);
-                dz[f] = acc;
-            }
-            /* up: dW_up += dz x_t^T; dx_t += W_up^T dz */
-            double *gwu = dWup + e * d_ff * d;
-            for (int64_t f = 0; f < d_ff; ++f)
-                for (int64_t i = 0; i < d; ++i)
-                    gwu[f * d + i] += dz[f] * xt[i];
-            for (int64_t i = 0; i < d; ++i) {
-                double acc = 0.0;
-                for (int64_t f = 0; f < d_ff; ++f)
-                    acc += wu[f * d + i] * dz[f];
-                dxt[i] += acc;
-            }
-        }
-        /* softmax over the kept scores, then the score product */
-        double gdg = 0.0;
-        for (int32_t j = 0; j < k; ++j)
-            gdg += gate[t * k + j] * dg[j];
-        for (int32_t j = 0; j < k; ++j) {
-            const int64_t e = idx[t * k + j];
-            const double ds = gate[t * k + j] * (dg[j] - gdg);
-            for (int64_t i = 0; i < d; ++i) {
-                dWg[e * d + i] += ds * xt[i];
-                dxt[i] += ds * Wg[e * d + i];
-            }
-        }
-    }
-done:
-    free(scores); free(idx); free(gate); free(slot); free(used);
-    free(z); free(h); free(y); free(dz); free(dg);
-    return rc;
+    return backward_impl(N, d, E, k, d_ff, C, x, Wg, noise, Wup, Wdown, dout, N, NULL, dx, dWg,
+                         dWup, dWdown);
+}
+
+/* dx of the listed tokens only (rows[r] in [0, N)), as oracle_backward
+ * computes it: the routing covers all N tokens, since capacity decides a
+ * token's kept choices from every earlier assignment, but the expert terms
+ * are evaluated for the listed tokens alone. dx_rows is [nrows, d]. */
+int oracle_backward_rows(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff, int64_t C,
+                         const double *x, const double *Wg, const double *noise,
+                         const double *Wup, const double *Wdown, const double *dout,
+                         int64_t nrows, const int64_t *rows, double *dx_rows)
+{
+    return backward_impl(N, d, E, k, d_ff, C, x, Wg, noise, Wup, Wdown, dout, nrows, rows,
+                         dx_rows, NULL, NULL, NULL);
 }
 
 /* [P1 STEP 11-12, P2 slides 38-40] output rows: each kept assignment's

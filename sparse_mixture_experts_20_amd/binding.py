@@ -23,7 +23,8 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK = 256, 16
 EXPORTS = ("moe_forward", "moe_workspace_size", "moe_capacity", "moe_error_string",
            "moe_router", "moe_router_workspace_size", "moe_dispatch", "moe_experts",
            "moe_expert_up", "moe_expert_down", "moe_expert_workspace_size", "moe_combine",
-           "moe_forward_ex", "moe_experts_ex", "moe_expert_up_ex", "moe_expert_down_ex")
+           "moe_forward_ex", "moe_experts_ex", "moe_expert_up_ex", "moe_expert_down_ex",
+           "moe_backward", "moe_backward_workspace_size")
 
 MOE_ACT_RELU, MOE_ACT_GELU = 0, 1
 ACTS = {"relu": MOE_ACT_RELU, "gelu": MOE_ACT_GELU}
@@ -83,6 +84,12 @@ def lib():
                                          _i64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                          _vp]
         L.moe_expert_down_ex.restype = ctypes.c_int
+        L.moe_backward.argtypes = [_T, _T, _T, _T, _T, ctypes.c_int, ctypes.c_float, _T, _T, _T,
+                                   _T, _T, ctypes.POINTER(MoeStats)]
+        L.moe_backward.restype = ctypes.c_int
+        L.moe_backward_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int,
+                                                  ctypes.c_float, ctypes.c_int32]
+        L.moe_backward_workspace_size.restype = ctypes.c_size_t
         L.moe_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
                                          ctypes.c_int32]
         L.moe_workspace_size.restype = ctypes.c_size_t
@@ -232,6 +239,45 @@ def forward(x: torch.Tensor, W_g: torch.Tensor, noise: Optional[torch.Tensor],
                                   capacity_factor, _ref(do), ctypes.byref(st))
     _check(rc, "moe_forward")
     return out, Stats(idx, gate, slot, used, int(st.capacity))
+
+
+def backward_workspace_size(N: int, d: int, E: int, d_ff: int, k: int, capacity_factor: float,
+                            dtype: torch.dtype) -> int:
+    code = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(lib().moe_backward_workspace_size(N, d, E, d_ff, k, capacity_factor, code))
+
+
+def backward(x, W_g, noise, W_up, W_down, k: int, capacity_factor: float, dout,
+             workspace=None, stream=None, export: bool = False):
+    """Run ``moe_backward``: returns (dx [N, d], dW_g [E, d], dW_up [E, d_ff, d],
+    dW_down [E, d, d_ff]), all fp32. With ``export=True`` returns
+    ``(grads, Stats)`` with the recomputed routing, as ``forward`` does."""
+    N, d = x.numel() // x.shape[-1], x.shape[-1]
+    E, d_ff = W_up.shape[0], W_up.shape[1]
+    dev = x.device
+    dx = torch.empty((N, d), dtype=torch.float32, device=dev)
+    dwg = torch.empty((E, d), dtype=torch.float32, device=dev)
+    dwu = torch.empty((E, d_ff, d), dtype=torch.float32, device=dev)
+    dwd = torch.empty((E, d, d_ff), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(
+            backward_workspace_size(N, d, E, d_ff, k, capacity_factor, x.dtype), dev)
+    idx = gate = slot = used = None
+    if export:
+        idx = torch.empty((N, k), dtype=torch.int32, device=dev)
+        gate = torch.empty((N, k), dtype=torch.float32, device=dev)
+        slot = torch.empty((N, k), dtype=torch.int32, device=dev)
+        used = torch.empty((E,), dtype=torch.int32, device=dev)
+    st = MoeStats(_stream(stream), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                  _ptr(idx), _ptr(gate), _ptr(slot), _ptr(used), -1)
+    ds = [desc(t) for t in (x, W_g, noise, W_up, W_down, dout, dx, dwg, dwu, dwd)]
+    _check(lib().moe_backward(_ref(ds[0]), _ref(ds[1]), _ref(ds[2]), _ref(ds[3]), _ref(ds[4]), k,
+                              capacity_factor, _ref(ds[5]), _ref(ds[6]), _ref(ds[7]),
+                              _ref(ds[8]), _ref(ds[9]), ctypes.byref(st)), "moe_backward")
+    grads = (dx, dwg, dwu, dwd)
+    if export:
+        return grads, Stats(idx, gate, slot, used, int(st.capacity))
+    return grads
 
 
 class Forward:

@@ -9,6 +9,7 @@ namespace moe {
 
 constexpr int kWave = 64;
 constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 16;
 constexpr int kMaxQ = kMaxExperts / kWave;   // router scores per lane
 constexpr int kFusedMaxExperts = 32;          // larger routers use the GEMM path
 constexpr int kActRelu = 0, kActGelu = 1;     // expert activations (values of the C ABI)
@@ -83,6 +84,43 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
                               const int32_t *slot_token, const int32_t *tiles, void *Y,
                               int64_t rows_per_expert, void *part, size_t part_bytes,
                               const float *b_down, hipStream_t s);
+
+// Backward products over the dispatch plan (bf16 operands, fp32 accumulate):
+// dZ[e, r, :] = (dY[slot_token[e, r]] W_down[e]) where H[e, r, :] > 0, with
+// W_down transposed ([E, d_ff, d]), bf16 into [E, ceff, d_ff];
+// out[slot_token[e, r], :] = A[e, r, :] W_t[e]^T (A dense [E, ceff, K], W_t
+// [E, Nout, K]), fp32.
+hipError_t launch_expert_dz(const void *dY, const void *w_down_t, const void *H, int64_t d,
+                            int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
+                            const int32_t *slot_token, const int32_t *tiles, void *dZ,
+                            int64_t rows_per_expert, hipStream_t s);
+hipError_t launch_expert_rows_f32(const void *A, const void *w_t, int64_t K, int64_t Nout, int E,
+                                  int k, int64_t ceff, const int32_t *used,
+                                  const int32_t *slot_token, const int32_t *tiles, float *out,
+                                  int64_t rows_per_expert, hipStream_t s);
+// C[b] (fp32 [M, Nout]) = A[b] [M, K] * W[b] [Nout, K]^T for b < batch, with
+// element strides sa, sb, sc between batches; bf16 operands, K % 8 == 0.
+hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int64_t K,
+                                    int64_t Nout, int batch, int64_t sa, int64_t sb, int64_t sc,
+                                    float *C, hipStream_t s);
+
+// Backward element-wise and layout kernels (backward.hip).
+// dY rows (bf16, kept choices) = gate * dout; ds [N, k] = gate * (dg - sum gate*dg)
+// with dg = <dout, Yf> (Yf: fp32 expert outputs, assignment-major).
+hipError_t launch_combine_backward(const void *dout, const float *Yf, const float *gate,
+                                   const int32_t *slot, int64_t N, int64_t d, int k, void *dY,
+                                   float *ds, hipStream_t s);
+// dsT3 [E, 3*Np] bf16: exact three-term split of ds(t, e) at columns t, Np+t, 2Np+t.
+hipError_t launch_ds_split(const float *ds, const int32_t *idx, int64_t N, int64_t Np, int E,
+                           int k, void *dsT3, hipStream_t s);
+// out[b][c][q*Kp + r] = src row R(b, r), column c (0 past the rows), for q < copies;
+// map 0: b*ceff + r, 1: slot_token[b*ceff + r], 2: slot_token[...] / k, 3: r.
+hipError_t launch_transpose_rows(const void *src, int64_t C, int64_t ceff, const int32_t *used,
+                                 int64_t nrows, const int32_t *slot_token, int k, int map,
+                                 int64_t Kp, int copies, int batch, void *out, hipStream_t s);
+// dx = sum of the kept choices' dX rows + sum_j ds[t, j] W_g[idx[t, j]] (fp32, d % 4 == 0).
+hipError_t launch_dx(const float *dXa, const float *ds, const int32_t *idx, const int32_t *slot,
+                     const float *Wg, int64_t N, int64_t d, int k, float *dx, hipStream_t s);
 
 // Y[rows, Nout] (fp32) = A[rows, K] * W[Nout, K]^T, bf16 operands.
 hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, int64_t K,

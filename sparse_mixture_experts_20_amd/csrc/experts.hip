@@ -168,7 +168,13 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // MODE 0: up product (gathered token rows, activation, bf16 H into O16);
 // 1: down product (bf16 rows of Y scattered to their assignment, into O16);
 // 2: plain product of ceff rows of A into fp32 rows of O32 (no gather, no
-// schedule table, no split).
+// schedule table, no split), batched over blockIdx.y with element strides
+// bsa, bsb, bsc of A, W and O32;
+// 3: backward of the down product, dZ = (dY W_down) masked by H > 0: A rows
+// are assignment rows of dY gathered by slot_token, W is W_down transposed,
+// bf16 [E, ceff, Nout] into O16; mask = H;
+// 4: backward of the up product, dX = dZ W_up: A rows dense like MODE 1, W
+// is W_up transposed, fp32 rows scattered to their assignment into O32.
 // part: scratch for the split of the last round (NULL: no split), P: the
 // number of workgroups of this kernel that fit on the device at once.
 // act: activation of the up product (kActRelu, kActGelu); bias: [E, Nout]
@@ -181,7 +187,8 @@ void expert_gemm_kernel(
     int Nout, int E, int k, int ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
     unsigned short *__restrict__ O16, float *__restrict__ O32, float *__restrict__ part,
-    int P, int act, const float *__restrict__ bias) {
+    int P, int act, const float *__restrict__ bias, const unsigned short *__restrict__ mask,
+    int64_t bsa, int64_t bsb, int64_t bsc) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int NTHR = NW * 64;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;   // wave tile
@@ -208,7 +215,10 @@ void expert_gemm_kernel(
     int kb = 0, ke = KT;   // K-steps of this workgroup
     int piece = -1;        // scratch slot of a K-range, or -1 for a whole tile
     if constexpr (MODE == 2) {
-        // plain product over ceff rows, one "expert": no schedule table
+        // plain product over ceff rows, one "expert" per blockIdx.y: no schedule table
+        A_src += blockIdx.y * bsa;
+        W += blockIdx.y * bsb;
+        O32 += blockIdx.y * bsc;
         const int mte = (ceff + BM - 1) / BM;
         const int T = mte * NT;
         const int T8 = (T + kXcds - 1) / kXcds * kXcds;
@@ -266,7 +276,9 @@ void expert_gemm_kernel(
         ca[i] = (lane % CPR) ^ ((row / RPB) % CPR);
         const int r = m0 + row;
         const int64_t srow = (int64_t)e * ceff + (r < rows ? r : 0);
-        const int64_t src = MODE == 0 ? (int64_t)(slot_token[srow] / k) : srow;
+        const int64_t src = MODE == 0   ? (int64_t)(slot_token[srow] / k)
+                            : MODE == 3 ? (int64_t)slot_token[srow]
+                                        : srow;
         ga[i] = A_src + src * K;
     }
 #pragma unroll
@@ -467,8 +479,31 @@ void expert_gemm_kernel(
                         *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
                     }
                 }
+            } else if (MODE == 3) {
+                // dZ = dH where H > 0 (ReLU backward), bf16 like H
+                unsigned short *dst = O16 + srow * Nout + nb;
+                const unsigned short *hm = mask + srow * Nout + nb;
+#pragma unroll
+                for (int h = 0; h < CPL / 8; ++h) {
+                    if (nb + 8 * h + 8 <= Nout) {
+                        const u32x4 hb = *reinterpret_cast<const u32x4 *>(hm + 8 * h);
+                        u32x4 pk;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const f32x4 &z = c < 2 ? v[2 * h] : v[2 * h + 1];
+                            const unsigned hl = hb[c] & 0xffffu, hh = hb[c] >> 16;
+                            // a bf16 value > 0: sign clear and not zero
+                            const float lo = (hl - 1u) < 0x7fffu ? z[(c % 2) * 2] : 0.f;
+                            const float hi = (hh - 1u) < 0x7fffu ? z[(c % 2) * 2 + 1] : 0.f;
+                            pk[c] = (unsigned)f32_to_bf16_bits(lo) |
+                                    ((unsigned)f32_to_bf16_bits(hi) << 16);
+                        }
+                        *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
+                    }
+                }
             } else {
-                float *dst = O32 + (int64_t)r * Nout + nb;
+                const int64_t orow = MODE == 4 ? (int64_t)slot_token[srow] : (int64_t)r;
+                float *dst = O32 + orow * Nout + nb;
 #pragma unroll
                 for (int c = 0; c < CPL / 4; ++c)
                     if (nb + 4 * c + 4 <= Nout)
@@ -644,7 +679,8 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
                         int E, int k, int64_t ceff, const int32_t *used,
                         const int32_t *slot_token, const int32_t *mt, unsigned short *O16,
                         float *part, size_t part_bytes, int act, const float *bias,
-                        hipStream_t s) {
+                        hipStream_t s, const unsigned short *mask = nullptr,
+                        float *O32 = nullptr) {
     auto kern = expert_gemm_kernel<BM, BN, WM, WN, kBK, 2, MODE>;
     constexpr int NTHR = WM * WN * 64;
     static int resident[kMaxDevices];   // per device, filled on first use (0 = unset)
@@ -664,17 +700,18 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
     const int64_t tmax = (int64_t)E * ((ceff + BM - 1) / BM) * ((Nout + BN - 1) / BN);
     // a split needs at least two ranges of kSplitMinSteps, at least one full
     // round of tiles and (by the 15% rule of split_plan) fewer than six
-    const bool split =
-        P > 0 && KT >= 2 * kSplitMinSteps && tmax >= P && tmax < 6 * (int64_t)P;
+    const bool split = (MODE == 0 || MODE == 1) && P > 0 && KT >= 2 * kSplitMinSteps &&
+                       tmax >= P && tmax < 6 * (int64_t)P;
     const int64_t grid = (tmax + kXcds - 1) / kXcds * kXcds +
                          (split ? (int64_t)(P + kXcds - 1) / kXcds * kXcds : 0);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHR), 0, s, A, W, (int)K, (int)Nout, E,
-                       k, (int)ceff, used, slot_token, mt, O16, (float *)nullptr,
-                       split ? part : nullptr, split ? P : 0, act, bias);
+                       k, (int)ceff, used, slot_token, mt, O16, O32, split ? part : nullptr,
+                       split ? P : 0, act, bias, mask, (int64_t)0, (int64_t)0, (int64_t)0);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !split)
         return err;
-    hipLaunchKernelGGL((split_fixup_kernel<BM, BN, kBK, MODE>), dim3((unsigned)(P * (BM / 16))),
+    hipLaunchKernelGGL((split_fixup_kernel<BM, BN, kBK, MODE == 1 ? 1 : 0>),
+                       dim3((unsigned)(P * (BM / 16))),
                        dim3(256), 0, s, (int)K, (int)Nout, E, (int)ceff, used, slot_token, mt,
                        (const float *)part, P, O16, act, bias);
     return hipGetLastError();
@@ -685,17 +722,19 @@ hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W,
                        int64_t Nout, int E, int k, int64_t ceff, const int32_t *used,
                        const int32_t *slot_token, const int32_t *tiles, unsigned short *O16,
                        void *part, size_t part_bytes, int act, const float *bias,
-                       hipStream_t s) {
+                       hipStream_t s, const unsigned short *mask = nullptr,
+                       float *O32 = nullptr) {
     float *pf = static_cast<float *>(part);
     if (t == Tile::k256)
         return launch_tiles<256, 256, 2, 4, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
                                                   tiles + E + 1, O16, pf, part_bytes, act, bias,
-                                                  s);
+                                                  s, mask, O32);
     if (t == Tile::k128x64)
         return launch_tiles<128, 64, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
-                                                 tiles, O16, pf, part_bytes, act, bias, s);
+                                                 tiles, O16, pf, part_bytes, act, bias, s, mask,
+                                                 O32);
     return launch_tiles<128, 128, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token, tiles,
-                                              O16, pf, part_bytes, act, bias, s);
+                                              O16, pf, part_bytes, act, bias, s, mask, O32);
 }
 
 }  // namespace
@@ -712,7 +751,8 @@ hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, in
                        static_cast<const unsigned short *>(W), (int)K, (int)Nout, 1, 1, (int)rows,
                        (const int32_t *)nullptr, (const int32_t *)nullptr,
                        (const int32_t *)nullptr, (unsigned short *)nullptr, Y, (float *)nullptr,
-                       0, kActRelu, (const float *)nullptr);
+                       0, kActRelu, (const float *)nullptr, (const unsigned short *)nullptr,
+                       (int64_t)0, (int64_t)0, (int64_t)0);
     return hipGetLastError();
 }
 
@@ -755,6 +795,51 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
                        dim3(256), 0, s, static_cast<const float *>(H),
                        static_cast<const float *>(w_down), (int)d_ff, (int)d, k, (int)ceff, used,
                        slot_token, (float *)nullptr, static_cast<float *>(Y), kActRelu, b_down);
+    return hipGetLastError();
+}
+
+// ---- backward-pass products (bf16 operands, fp32 accumulation) ----------
+
+hipError_t launch_expert_dz(const void *dY, const void *w_down_t, const void *H, int64_t d,
+                            int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
+                            const int32_t *slot_token, const int32_t *tiles, void *dZ,
+                            int64_t rows_per_expert, hipStream_t s) {
+    if (ceff == 0)
+        return hipSuccess;
+    return launch_gemm<3>(pick_tile(rows_per_expert, d_ff, E),
+                          static_cast<const unsigned short *>(dY),
+                          static_cast<const unsigned short *>(w_down_t), d, d_ff, E, k, ceff,
+                          used, slot_token, tiles, static_cast<unsigned short *>(dZ), nullptr, 0,
+                          kActRelu, nullptr, s, static_cast<const unsigned short *>(H));
+}
+
+hipError_t launch_expert_rows_f32(const void *A, const void *w_t, int64_t K, int64_t Nout, int E,
+                                  int k, int64_t ceff, const int32_t *used,
+                                  const int32_t *slot_token, const int32_t *tiles, float *out,
+                                  int64_t rows_per_expert, hipStream_t s) {
+    if (ceff == 0)
+        return hipSuccess;
+    return launch_gemm<4>(pick_tile(rows_per_expert, Nout, E),
+                          static_cast<const unsigned short *>(A),
+                          static_cast<const unsigned short *>(w_t), K, Nout, E, k, ceff, used,
+                          slot_token, tiles, nullptr, nullptr, 0, kActRelu, nullptr, s, nullptr,
+                          out);
+}
+
+hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int64_t K,
+                                    int64_t Nout, int batch, int64_t sa, int64_t sb, int64_t sc,
+                                    float *C, hipStream_t s) {
+    if (M == 0 || batch == 0)
+        return hipSuccess;
+    const int64_t grid = (((M + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, kBK, 2, 2>),
+                       dim3((unsigned)grid, (unsigned)batch), dim3(256), 0, s,
+                       static_cast<const unsigned short *>(A),
+                       static_cast<const unsigned short *>(W), (int)K, (int)Nout, 1, 1, (int)M,
+                       (const int32_t *)nullptr, (const int32_t *)nullptr,
+                       (const int32_t *)nullptr, (unsigned short *)nullptr, C, (float *)nullptr,
+                       0, kActRelu, (const float *)nullptr, (const unsigned short *)nullptr, sa,
+                       sb, sc);
     return hipGetLastError();
 }
 

@@ -67,6 +67,56 @@ Layout layout_of(const Dims &m) {
     return L;
 }
 
+// Workspace of the backward pass (bf16 layers): the recomputed forward state
+// and the gradient intermediates.
+struct BwdLayout {
+    size_t idx, gate, slot, used, tiles, slot_token, H, Yf, dY, ds, dZ, dXa, WT, T1, T2, dsT3,
+        xT3, router, total;
+    int64_t Kp, Np;
+};
+
+BwdLayout bwd_layout_of(const Dims &m) {
+    BwdLayout L;
+    size_t o = 0;
+    const size_t nk = (size_t)m.N * m.k;
+    L.Kp = (m.ceff + 7) / 8 * 8;
+    L.Np = (m.N + 7) / 8 * 8;
+    L.idx = o;        o += align_up(nk * 4);
+    L.gate = o;       o += align_up(nk * 4);
+    L.slot = o;       o += align_up(nk * 4);
+    L.used = o;       o += align_up((size_t)m.E * 4);
+    L.tiles = o;      o += align_up((size_t)(2 * (m.E + 1)) * 4);
+    L.slot_token = o; o += align_up((size_t)(m.E * m.ceff) * 4);
+    L.H = o;          o += align_up((size_t)(m.E * m.ceff * m.d_ff) * 2);
+    L.Yf = o;         o += align_up(nk * (size_t)m.d * 4);
+    L.dY = o;         o += align_up(nk * (size_t)m.d * 2);
+    L.ds = o;         o += align_up(nk * 4);
+    L.dZ = o;         o += align_up((size_t)(m.E * m.ceff * m.d_ff) * 2);
+    L.dXa = o;        o += align_up(nk * (size_t)m.d * 4);
+    L.WT = o;         o += align_up((size_t)(m.E * m.d * m.d_ff) * 2);
+    L.T1 = o;         o += align_up((size_t)(m.E * m.d * L.Kp) * 2);
+    L.T2 = o;         o += align_up((size_t)(m.E * m.d_ff * L.Kp) * 2);
+    L.dsT3 = o;       o += align_up((size_t)(m.E * 3 * L.Np) * 2);
+    L.xT3 = o;        o += align_up((size_t)(m.d * 3 * L.Np) * 2);
+    L.router = o;     o += router_bytes(m.N, m.d, m.E, m.dtype);
+    L.total = o;
+    return L;
+}
+
+// An fp32 gradient tensor of the given extents.
+int check_grad(const moe_tensor *g, int ndim, const int64_t *ext) {
+    if (!g)
+        return MOE_ERR_NULL;
+    if (g->dtype != MOE_F32)
+        return MOE_ERR_DTYPE;
+    if (g->ndim != ndim)
+        return MOE_ERR_SHAPE;
+    for (int i = 0; i < ndim; ++i)
+        if (g->shape[i] != ext[i])
+            return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
 // Common size checks; fills C and ceff.
 int check_sizes(Dims &m) {
     if (m.N < 0 || m.d <= 0 || m.E <= 0 || m.d_ff <= 0)
@@ -580,6 +630,152 @@ int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *no
                 const moe_tensor *W_up, const moe_tensor *W_down, int k, float capacity_factor,
                 moe_tensor *out, moe_stats *stats) {
     return moe_forward_ex(x, W_g, noise, W_up, W_down, nullptr, k, capacity_factor, out, stats);
+}
+
+size_t moe_backward_workspace_size(int64_t N, int64_t d, int64_t E, int64_t d_ff, int k,
+                                   float capacity_factor, int32_t dtype) {
+    if (dtype != MOE_BF16 || !cf_ok(capacity_factor))
+        return 0;
+    if (N < 0 || E <= 0 || k < 1 || k > E)
+        return 0;
+    Dims m{N, d, E, d_ff, k, 0, 0, dtype};
+    m.C = capacity_of(N, E, k, capacity_factor);
+    m.ceff = m.C < N ? m.C : N;
+    if (check_sizes(m) != MOE_OK)
+        return 0;
+    return bwd_layout_of(m).total;
+}
+
+int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                 const moe_tensor *W_up, const moe_tensor *W_down, int k, float capacity_factor,
+                 const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g, moe_tensor *dW_up,
+                 moe_tensor *dW_down, moe_stats *stats) {
+    if (!stats || !W_up || !W_down || !dout)
+        return MOE_ERR_NULL;
+    int64_t N, d, E;
+    int rc = check_router_args(x, W_g, noise, k, N, d, E);
+    if (rc != MOE_OK)
+        return rc;
+    if (!cf_ok(capacity_factor))
+        return MOE_ERR_ARG;
+    if (x->dtype != MOE_BF16)
+        return MOE_ERR_UNSUPPORTED;   // the backward runs on bf16 layers
+    if (W_up->dtype != x->dtype || W_down->dtype != x->dtype || dout->dtype != x->dtype)
+        return MOE_ERR_DTYPE;
+    if (W_up->ndim != 3 || W_down->ndim != 3)
+        return MOE_ERR_SHAPE;
+    const int64_t d_ff = W_up->shape[1];
+    if (W_up->shape[0] != E || W_up->shape[2] != d || W_down->shape[0] != E ||
+        W_down->shape[1] != d || W_down->shape[2] != d_ff)
+        return MOE_ERR_SHAPE;
+    int64_t gN, gd;
+    if (!act_rows(dout, gN, gd) || gN != N || gd != d)
+        return MOE_ERR_SHAPE;
+    {
+        const int64_t e_dx[2] = {N, d}, e_wg[2] = {E, d}, e_up[3] = {E, d_ff, d},
+                      e_dn[3] = {E, d, d_ff};
+        if (!dx || !dW_g || !dW_up || !dW_down)
+            return MOE_ERR_NULL;
+        int64_t xN, xd;
+        if (dx->dtype != MOE_F32)
+            return MOE_ERR_DTYPE;
+        if (!act_rows(dx, xN, xd) || xN != e_dx[0] || xd != e_dx[1])
+            return MOE_ERR_SHAPE;
+        if ((rc = check_grad(dW_g, 2, e_wg)) != MOE_OK ||
+            (rc = check_grad(dW_up, 3, e_up)) != MOE_OK ||
+            (rc = check_grad(dW_down, 3, e_dn)) != MOE_OK)
+            return rc;
+    }
+    Dims m{N, d, E, d_ff, k, 0, 0, x->dtype};
+    m.C = capacity_of(N, E, k, capacity_factor);
+    m.ceff = m.C < N ? m.C : N;
+    rc = check_sizes(m);
+    if (rc != MOE_OK)
+        return rc;
+    // the weight gradients are written even without tokens
+    if (!dW_g->data || !dW_up->data || !dW_down->data)
+        return MOE_ERR_NULL;
+    if (!aligned(dW_g->data, 16) || !aligned(dW_up->data, 16) || !aligned(dW_down->data, 16))
+        return MOE_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stats->stream);
+    if (N == 0) {
+        // no tokens: every gradient is zero
+        // (fill kernels, not memset nodes: the call may be captured in a graph)
+        stats->capacity = 0;
+        MOE_TRY(moe::launch_fill_i32(static_cast<int32_t *>(dW_g->data), E * d, 0, s));
+        MOE_TRY(moe::launch_fill_i32(static_cast<int32_t *>(dW_up->data), E * d_ff * d, 0, s));
+        MOE_TRY(moe::launch_fill_i32(static_cast<int32_t *>(dW_down->data), E * d * d_ff, 0, s));
+        if (stats->used_capacity)
+            return hip_status(moe::launch_fill_i32(stats->used_capacity, E, 0, s));
+        return MOE_OK;
+    }
+    if (!W_up->data || !W_down->data || !dout->data || !dx->data)
+        return MOE_ERR_NULL;
+    if (!stats->workspace)
+        return MOE_ERR_NULL;
+    if (!aligned(stats->workspace, kAlign))
+        return MOE_ERR_ALIGN;
+    if (!aligned(W_up->data, 16) || !aligned(W_down->data, 16) || !aligned(dout->data, 16) ||
+        !aligned(dx->data, 16))
+        return MOE_ERR_ALIGN;
+    const BwdLayout L = bwd_layout_of(m);
+    if (stats->workspace_bytes < L.total)
+        return MOE_ERR_WORKSPACE;
+    stats->capacity = m.C;
+
+    char *ws = static_cast<char *>(stats->workspace);
+    int32_t *idx = stats->topk_idx ? stats->topk_idx : reinterpret_cast<int32_t *>(ws + L.idx);
+    float *gate = stats->topk_gate ? stats->topk_gate : reinterpret_cast<float *>(ws + L.gate);
+    int32_t *slot = stats->slot ? stats->slot : reinterpret_cast<int32_t *>(ws + L.slot);
+    int32_t *used = stats->used_capacity ? stats->used_capacity
+                                         : reinterpret_cast<int32_t *>(ws + L.used);
+    int32_t *tiles = reinterpret_cast<int32_t *>(ws + L.tiles);
+    int32_t *st = reinterpret_cast<int32_t *>(ws + L.slot_token);
+    void *H = ws + L.H, *dY = ws + L.dY, *dZ = ws + L.dZ, *WT = ws + L.WT;
+    void *T1 = ws + L.T1, *T2 = ws + L.T2, *dsT3 = ws + L.dsT3, *xT3 = ws + L.xT3;
+    float *Yf = reinterpret_cast<float *>(ws + L.Yf);
+    float *ds = reinterpret_cast<float *>(ws + L.ds);
+    float *dXa = reinterpret_cast<float *>(ws + L.dXa);
+    const int64_t ceff = m.ceff, Kp = L.Kp, Np = L.Np;
+    const int64_t rpe = rows_per_expert(N, k, E, ceff);
+    const int Ei = (int)E;
+
+    // forward state: routing, plan, H, and the experts' outputs in fp32
+    rc = router_checked(x, W_g, noise, N, d, E, k, idx, gate, ws + L.router, s);
+    if (rc != MOE_OK)
+        return rc;
+    MOE_TRY(moe::launch_dispatch(idx, N, Ei, k, ceff, slot, used, st, tiles, s));
+    MOE_TRY(moe::launch_expert_up(true, x->data, W_up->data, d, d_ff, Ei, k, ceff, used, st,
+                                  tiles, H, rpe, nullptr, 0, moe::kActRelu, nullptr, s));
+    MOE_TRY(moe::launch_expert_rows_f32(H, W_down->data, d_ff, d, Ei, k, ceff, used, st, tiles,
+                                        Yf, rpe, s));
+    // combine and softmax backward; router weights: dW_g = ds^T x on split ds
+    MOE_TRY(moe::launch_combine_backward(dout->data, Yf, gate, slot, N, d, k, dY, ds, s));
+    MOE_TRY(moe::launch_ds_split(ds, idx, N, Np, Ei, k, dsT3, s));
+    MOE_TRY(moe::launch_transpose_rows(x->data, d, 0, nullptr, N, nullptr, k, 3, Np, 3, 1, xT3,
+                                       s));
+    MOE_TRY(moe::launch_batched_gemm_bf16(dsT3, xT3, E, 3 * Np, d, 1, 0, 0, 0,
+                                          static_cast<float *>(dW_g->data), s));
+    // experts, input side: dZ = (dY W_down) [H > 0]; dX = dZ W_up; dx
+    MOE_TRY(moe::launch_transpose_rows(W_down->data, d_ff, d, nullptr, d, nullptr, k, 0, d, 1, Ei,
+                                       WT, s));
+    MOE_TRY(moe::launch_expert_dz(dY, WT, H, d, d_ff, Ei, k, ceff, used, st, tiles, dZ, rpe, s));
+    MOE_TRY(moe::launch_transpose_rows(W_up->data, d, d_ff, nullptr, d_ff, nullptr, k, 0, d_ff, 1,
+                                       Ei, WT, s));
+    MOE_TRY(moe::launch_expert_rows_f32(dZ, WT, d_ff, d, Ei, k, ceff, used, st, tiles, dXa, rpe,
+                                        s));
+    MOE_TRY(moe::launch_dx(dXa, ds, idx, slot, static_cast<const float *>(W_g->data), N, d, k,
+                           static_cast<float *>(dx->data), s));
+    // experts, weight side: dW_down = dY^T H, dW_up = dZ^T X (K = kept rows)
+    MOE_TRY(moe::launch_transpose_rows(dY, d, ceff, used, 0, st, k, 1, Kp, 1, Ei, T1, s));
+    MOE_TRY(moe::launch_transpose_rows(H, d_ff, ceff, used, 0, st, k, 0, Kp, 1, Ei, T2, s));
+    MOE_TRY(moe::launch_batched_gemm_bf16(T1, T2, d, Kp, d_ff, Ei, d * Kp, d_ff * Kp, d * d_ff,
+                                          static_cast<float *>(dW_down->data), s));
+    MOE_TRY(moe::launch_transpose_rows(x->data, d, ceff, used, 0, st, k, 2, Kp, 1, Ei, T1, s));
+    MOE_TRY(moe::launch_transpose_rows(dZ, d_ff, ceff, used, 0, st, k, 0, Kp, 1, Ei, T2, s));
+    MOE_TRY(moe::launch_batched_gemm_bf16(T2, T1, d_ff, Kp, d, Ei, d_ff * Kp, d * Kp, d_ff * d,
+                                          static_cast<float *>(dW_up->data), s));
+    return MOE_OK;
 }
 
 }  // extern "C"

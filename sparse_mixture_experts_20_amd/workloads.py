@@ -40,7 +40,7 @@ import numpy as np
 SEPARATION = 1e-4
 
 # spawn_key namespaces of the random streams
-_S_X, _S_WG, _S_NOISE, _S_RESAMPLE, _S_WUP, _S_WDOWN, _S_BUP, _S_BDOWN = range(8)
+_S_X, _S_WG, _S_NOISE, _S_RESAMPLE, _S_WUP, _S_WDOWN, _S_BUP, _S_BDOWN, _S_DOUT = range(9)
 
 
 # --------------------------------------------------------------------------
@@ -272,6 +272,14 @@ class Workload:
 
     def noise64(self) -> Optional[np.ndarray]:
         return None if self.noise is None else self.noise.astype(np.float64)
+
+    def dout(self, scale: float = 1.0) -> np.ndarray:
+        """A seeded output gradient [N, d] in the workload dtype (standard
+        normal times ``scale``), the input of the backward pass."""
+        a = _rng(self.cfg.seed, _S_DOUT).standard_normal((self.N, self.d), dtype=np.float32)
+        if scale != 1.0:
+            a *= np.float32(scale)
+        return _cast(a, self.cfg.dtype)
 
 
 def _draw_x(cfg: Config, rng: np.random.Generator, n: int) -> np.ndarray:

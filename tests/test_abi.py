@@ -230,3 +230,53 @@ def test_expert_variant_options_are_validated(L):
                               None, 0, None) == -2
     assert L.moe_expert_down_ex(64, r(wd), r(opts(bd=_t(FAKE, F32, 4, 32))), 2, 5, v, v, v, v, v,
                                 None, 0, None) == -2
+
+
+def test_backward_workspace_size(L):
+    ws = L.moe_backward_workspace_size
+    n = ws(2048, 768, 8, 3072, 2, 1.25, BF16)
+    # at least H and dZ (E*C*d_ff bf16 each), Y and dX in fp32 (N*k*d each)
+    assert n >= 2 * (8 * 640 * 3072 * 2) + 2 * (2048 * 2 * 768 * 4)
+    assert n % 256 == 0
+    assert ws(2048, 768, 8, 3072, 2, 1.25, F32) == 0       # bf16 layers only
+    assert ws(2048, 768, 8, 3072, 9, 1.25, BF16) == 0      # k > E
+    assert ws(2048, 768, 8, 3072, 2, 0.0, BF16) == 0       # cf <= 0
+    assert ws(2048, 770, 8, 3072, 2, 1.0, BF16) == 0       # d % 8
+    assert ws(0, 8, 4, 8, 2, 1.0, BF16) > 0                # empty call is valid
+
+
+def test_backward_rejects_bad_arguments(L):
+    N, d, E, dff = 64, 16, 4, 32
+    x, wg, wu, wd, out, st = _good(N=N, d=d, E=E, dff=dff)
+    dout = _t(FAKE, BF16, N, d)
+    r = ctypes.byref
+
+    def grads(dx=None, dwg=None, dwu=None, dwd=None):
+        return (dx or _t(FAKE, F32, N, d), dwg or _t(FAKE, F32, E, d),
+                dwu or _t(FAKE, F32, E, dff, d), dwd or _t(FAKE, F32, E, d, dff))
+
+    def bwd(x=x, wu=wu, wd=wd, k=2, cf=1.0, dout=dout, g=None, st=st):
+        g = g or grads()
+        return L.moe_backward(r(x), r(wg), None, r(wu), r(wd), k, cf, r(dout), r(g[0]),
+                              r(g[1]), r(g[2]), r(g[3]), r(st) if st else None)
+
+    assert bwd(st=None) == -1                                        # stats NULL
+    assert bwd(k=5) == -4                                            # k > E
+    assert bwd(cf=math.nan) == -4                                    # cf NaN
+    xf, _, wuf, wdf, _, _ = _good(N=N, d=d, E=E, dff=dff, dt=F32)
+    assert bwd(x=xf, wu=wuf, wd=wdf, dout=_t(FAKE, F32, N, d)) == -6  # fp32 layers
+    assert bwd(dout=_t(FAKE, F32, N, d)) == -3                       # dout in x's dtype
+    assert bwd(dout=_t(FAKE, BF16, N - 1, d)) == -2                  # dout [N, d]
+    assert bwd(g=grads(dx=_t(FAKE, BF16, N, d))) == -3               # gradients are fp32
+    assert bwd(g=grads(dx=_t(FAKE, F32, N, d + 8))) == -2
+    assert bwd(g=grads(dwg=_t(FAKE, F32, E + 1, d))) == -2           # dW_g [E, d]
+    assert bwd(g=grads(dwu=_t(FAKE, F32, E, d, dff))) == -2          # dW_up [E, d_ff, d]
+    assert bwd(g=grads(dwd=_t(FAKE, F32, E, dff, d))) == -2          # dW_down [E, d, d_ff]
+    assert bwd(g=grads(dwu=_t(FAKE, F32, E, dff))) == -2
+    assert bwd(g=grads(dx=_t(0, F32, N, d))) == -1                   # data NULL
+    assert bwd(g=grads(dwd=_t(FAKE + 4, F32, E, d, dff))) == -7      # 16-byte aligned
+    assert bwd(dout=_t(FAKE + 2, BF16, N, d)) == -7
+    assert bwd() == -5                                               # 1-byte workspace
+    st2 = B.MoeStats(None, ctypes.c_void_p(FAKE + 4), 1 << 40, None, None, None, None, -1)
+    assert bwd(st=st2) == -7                                         # misaligned workspace
+    assert st.capacity == -1

@@ -130,3 +130,19 @@ def test_dropped_assignments_carry_no_expert_gradient():
     for e in range(3):
         if e not in kept:
             assert np.all(dwu[e] == 0.0) and np.all(dwd[e] == 0.0)
+
+
+def test_backward_rows_match_the_full_backward():
+    """dx of listed tokens (any order, repeats) equals the full backward's
+    rows exactly: same routing, same per-token sums in the same order."""
+    wl = W.custom("bwd_rows", N=40, d=16, E=5, k=2, d_ff=24, dtype="f32", cf=0.7, sigma=0.3,
+                  seed=66, w_std=0.2)
+    x, wg, noise, wu, wd = _arrays(wl)
+    dout = np.random.default_rng(67).standard_normal((wl.N, wl.d))
+    dx, _, _, _ = oracle.backward(x, wg, noise, wu, wd, wl.k, wl.cfg.cf, dout)
+    rows = [39, 0, 17, 17, 5]
+    got = oracle.backward_rows(x, wg, noise, wu, wd, wl.k, wl.cfg.cf, dout, rows)
+    np.testing.assert_array_equal(got, dx[rows])
+    assert oracle.backward_rows(x, wg, noise, wu, wd, wl.k, wl.cfg.cf, dout, []).shape == (0, 16)
+    with pytest.raises(ValueError):
+        oracle.backward_rows(x, wg, noise, wu, wd, wl.k, wl.cfg.cf, dout, [40])

@@ -6,6 +6,10 @@ combine) over one batch of seeded synthetic tokens already resident in HBM.
 Default workload: the nanoMoE-shaped layer (2048 tokens, d=768, E=8, k=2,
 d_ff=3072, bf16, capacity factor 1.25, noise sigma 1.0).
 
+With --pass backward, one step is one moe_backward call instead (the
+forward state recomputed, then the gradients of x, W_g, W_up and W_down for
+a seeded output gradient), reported in the same JSON form.
+
 Prints ONE JSON line on stdout. Besides the contract fields it carries:
   roofline      the dominant kernel (the larger of the two expert GEMMs)
                 against bf16 MFMA peak, its duration timed with HIP events on
@@ -126,6 +130,119 @@ def cpu_baseline(wl, target_s=15.0):
     }
 
 
+def cpu_baseline_backward(wl, target_s=15.0):
+    """The oracle's backward as it stands, on the first S tokens of the
+    workload (same weights; capacity recomputed for S tokens), S sized for
+    ~target_s of work."""
+    import numpy as np
+    import oracle
+
+    x64, wg64 = wl.x64(), wl.wg64()
+    nz = wl.noise64()
+    dout = wl.as_f64(wl.dout())
+    wu = np.stack([wl.as_f64(wl.w_up(e)) for e in range(wl.E)])
+    wd = np.stack([wl.as_f64(wl.w_down(e)) for e in range(wl.E)])
+
+    def run(S):
+        a = time.perf_counter()
+        oracle.backward(x64[:S], wg64, None if nz is None else nz[:S], wu, wd, wl.k, wl.cfg.cf,
+                        dout[:S])
+        return time.perf_counter() - a
+
+    S = min(wl.N, 8)
+    t = run(S)
+    S = int(min(wl.N, max(8, target_s * S / max(t, 1e-9))))
+    t = run(S)
+    return {
+        "value": S / t,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"full backward (all four gradients) of the first {S} tokens with the "
+                   f"workload's weights, capacity recomputed for {S} tokens ({t:.2f} s); "
+                   f"tokens/s = S / t, serial float64 C loops"),
+    }
+
+
+def bench_backward(args, wl, dev):
+    """One step = one moe_backward call (forward state recomputed, then every
+    gradient) over the workload, with a seeded output gradient."""
+    import numpy as np
+    import torch
+    from sparse_mixture_experts_20_amd import binding as B
+
+    cfg = wl.cfg
+    if cfg.dtype != "bf16" or cfg.act != "relu" or cfg.bias_std:
+        print("the backward pass runs on bf16 ReLU layers without biases", file=sys.stderr)
+        sys.exit(2)
+    dout = torch.from_numpy(wl.dout().view(np.int16)).view(torch.bfloat16).to("cuda")
+    bwd = B.Backward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
+                     cfg.cf, dout)
+    for _ in range(args.warmup):
+        bwd()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        bwd()
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = max(wall_ms, ev_ms)
+    _, st = B.forward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
+                      cfg.cf, export=True)
+    kept = int(st.used.sum().item())
+    C = st.capacity
+    prod = 2.0 * kept * wl.d * wl.d_ff
+    flops = 6 * prod + 2 * 2.0 * wl.N * wl.k * wl.d
+    achieved = flops / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] backward {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall "
+        f"{wall_ms * 1e3:.1f}, events {ev_ms * 1e3:.1f}); {achieved:.0f} TFLOP/s over the pass")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle's backward on a bounded sample ...")
+        cpu = cpu_baseline_backward(wl)
+        log(f"[bench] cpu_baseline {cpu['value']:.1f} tokens/s")
+    line = {
+        "metric": "MoE-layer backward tokens/sec at 1 MI355X",
+        "value": round(wl.N / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Gaussian inputs, output gradient and random-init weights)",
+        "config": {
+            "workload": (cfg.description or cfg.name) + "; backward pass",
+            "tokens": wl.N, "d": wl.d, "experts": wl.E, "top_k": wl.k, "d_ff": wl.d_ff,
+            "capacity_factor": cfg.cf, "capacity": C, "noise_sigma": cfg.sigma,
+            "seed": cfg.seed, "kept_assignments": kept, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "moe_backward pass (6 expert products on the expert GEMM kernel + "
+                      "router gradient)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_per_launch": (f"6*2*kept*d*d_ff + 4*N*k*d = {flops:.4g} flop "
+                                       f"(kept={kept}; forward recomputed: 2 of the 6)"),
+            "avg_launch_us": round(ms_per_step * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -136,6 +253,8 @@ def main():
                     choices=["nanomoe", "mixtral", "skew", "finegrained", "tiny", "nanomoe_gelu"])
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
+                    help="time the layer's forward (default) or its backward pass")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -158,6 +277,9 @@ def main():
     log(f"[bench] workload {cfg.name}: N={wl.N} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff} "
         f"{cfg.dtype} cf={cfg.cf}")
     dev = D.upload(wl, keep_host=not args.no_cpu_baseline)
+    if args.which == "backward":
+        bench_backward(args, wl, dev)
+        return
     fwd = B.Forward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
                     cfg.cf, export=True, act=dev["act"],
                     b_up=dev["b_up"], b_down=dev["b_down"])

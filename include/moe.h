@@ -265,9 +265,9 @@ int moe_combine(int64_t N, int64_t d, int k, const moe_tensor *Y, const float *t
  *   scores: dW_g = ds^T x, dx += ds W_g;
  *   experts: dZ = (dY W_down) where H > 0, dW_down = dY^T H, dW_up = dZ^T X,
  *   dx += the kept choices' dZ W_up rows, summed in choice order.
- * The forward state (routing, dispatch plan, H and the experts' outputs in
- * fp32) is recomputed from the inputs in the workspace, so the call takes
- * the forward's arguments plus:
+ * The forward state (routing, dispatch plan, H and the experts' bf16
+ * outputs, as the forward combined them) is recomputed from the inputs in
+ * the workspace, so the call takes the forward's arguments plus:
  *   dout    [N, d]         same dtype as x (MOE_BF16)
  *   dx      [N, d]         MOE_F32, written
  *   dW_g    [E, d]         MOE_F32, written

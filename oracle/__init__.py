@@ -55,6 +55,10 @@ def lib():
         L.oracle_backward_rows.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _dp, _dp, _dp,
                                            _dp, _dp, _dp, _i64, _lp, _dp]
         L.oracle_backward_rows.restype = ctypes.c_int
+        L.oracle_backward_expert_units.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _dp, _dp,
+                                                   _dp, _i64, _dp, _dp, _dp, _i64, _lp, _dp,
+                                                   _dp]
+        L.oracle_backward_expert_units.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = ctypes.c_int
         _lib = L
@@ -209,6 +213,38 @@ def backward_rows(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout6
     if rc != 0:
         raise MemoryError("oracle_backward_rows: allocation failed")
     return dx
+
+
+def backward_expert_units(x64, wg64, noise64, e: int, wup_e64, wdown_e64, k: int, cf: float,
+                          dout64, units: Sequence[int]):
+    """Sampled weight gradients of expert e, as ``backward`` computes them:
+    returns (rows f of dW_up[e] [len(units), d], columns f of dW_down[e]
+    [len(units), d]) for the listed hidden units f. Takes only expert e's
+    matrices (wup_e64 [d_ff, d], wdown_e64 [d, d_ff])."""
+    x64 = _c(x64, np.float64)
+    wg64 = _c(wg64, np.float64)
+    wu = _c(wup_e64, np.float64)
+    wd = _c(wdown_e64, np.float64)
+    n64 = None if noise64 is None else _c(noise64, np.float64)
+    dout64 = _c(dout64, np.float64)
+    N, d = x64.shape
+    E = wg64.shape[0]
+    d_ff = wu.shape[0]
+    if wu.shape != (d_ff, d) or wd.shape != (d, d_ff) or dout64.shape != (N, d) or not (
+            0 <= e < E):
+        raise ValueError("shapes")
+    f = _c(np.asarray(units, dtype=np.int64), np.int64)
+    if f.size and (f.min() < 0 or f.max() >= d_ff):
+        raise ValueError("units out of range")
+    up = np.empty((f.size, d))
+    down = np.empty((f.size, d))
+    rc = lib().oracle_backward_expert_units(N, d, E, k, d_ff, capacity(N, E, k, cf),
+                                            _ptr(x64, _dp), _ptr(wg64, _dp), _ptr(n64, _dp), e,
+                                            _ptr(wu, _dp), _ptr(wd, _dp), _ptr(dout64, _dp),
+                                            f.size, _ptr(f, _lp), _ptr(up, _dp), _ptr(down, _dp))
+    if rc != 0:
+        raise MemoryError("oracle_backward_expert_units: allocation failed")
+    return up, down
 
 
 class Result:

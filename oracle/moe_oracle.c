@@ -349,6 +349,66 @@ int oracle_backward_rows(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_f
                          dx_rows, NULL, NULL, NULL);
 }
 
+/* Sampled weight gradients of one expert e: for each listed hidden unit f,
+ * row f of dW_up[e] (dWup_rows [nf, d]) and column f of dW_down[e]
+ * (dWdown_cols [nf, d], entry o = dW_down[e][o][f]), with the same terms and
+ * token order as oracle_backward. Wup_e [d_ff, d] and Wdown_e [d, d_ff] are
+ * expert e's matrices; the routing covers all N tokens. Per token routed to
+ * e and kept: g = its gate, dy = g dout_t, z_f = W_up[e][f] x_t,
+ * dW_down[e][:, f] += dy relu(z_f), dz_f = [z_f > 0] <W_down[e][:, f], dy>,
+ * dW_up[e][f] += dz_f x_t. Returns 0, or -1 if an allocation fails. */
+int oracle_backward_expert_units(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff,
+                                 int64_t C, const double *x, const double *Wg,
+                                 const double *noise, int64_t e, const double *Wup_e,
+                                 const double *Wdown_e, const double *dout, int64_t nf,
+                                 const int64_t *fs, double *dWup_rows, double *dWdown_cols)
+{
+    float *scores = (float *)malloc(sizeof(float) * (size_t)(N * E + 1));
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N * k + 1));
+    double *gate = (double *)malloc(sizeof(double) * (size_t)(N * k + 1));
+    int32_t *slot = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N * k + 1));
+    int32_t *used = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    int rc = 0;
+    if (!scores || !idx || !gate || !slot || !used) {
+        rc = -1;
+        goto done;
+    }
+    oracle_router(N, d, E, k, x, Wg, noise, scores, idx, gate);
+    oracle_assign(N, E, k, C, idx, slot, used);
+    for (int64_t i = 0; i < nf * d; ++i) {
+        dWup_rows[i] = 0.0;
+        dWdown_cols[i] = 0.0;
+    }
+    for (int64_t t = 0; t < N; ++t) {
+        const double *xt = x + t * d;
+        const double *go = dout + t * d;
+        for (int32_t j = 0; j < k; ++j) {
+            if (idx[t * k + j] != e || slot[t * k + j] < 0)
+                continue;
+            const double g = gate[t * k + j];
+            for (int64_t q = 0; q < nf; ++q) {
+                const int64_t f = fs[q];
+                double z = 0.0;
+                for (int64_t i = 0; i < d; ++i)
+                    z += Wup_e[f * d + i] * xt[i];
+                const double h = z > 0.0 ? z : 0.0;
+                double dh = 0.0;
+                for (int64_t o = 0; o < d; ++o) {
+                    const double dyo = g * go[o];
+                    dWdown_cols[q * d + o] += dyo * h;
+                    dh += Wdown_e[o * d_ff + f] * dyo;
+                }
+                const double dz = z > 0.0 ? dh : 0.0;
+                for (int64_t i = 0; i < d; ++i)
+                    dWup_rows[q * d + i] += dz * xt[i];
+            }
+        }
+    }
+done:
+    free(scores); free(idx); free(gate); free(slot); free(used);
+    return rc;
+}
+
 /* [P1 STEP 11-12, P2 slides 38-40] output rows: each kept assignment's
  * expert output scaled by its gate, summed in choice order j = 0..k-1.
  * Dropped assignments (slot -1) contribute nothing, so a token with every

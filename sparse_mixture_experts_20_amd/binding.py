@@ -322,6 +322,37 @@ class Forward:
         return self.out
 
 
+class Backward:
+    """A prepared ``moe_backward`` call: the gradient tensors, workspace and
+    descriptors are built once, so repeated calls only cross the C ABI."""
+
+    def __init__(self, x, W_g, noise, W_up, W_down, k, capacity_factor, dout, stream=None):
+        N, d = x.numel() // x.shape[-1], x.shape[-1]
+        E, d_ff = W_up.shape[0], W_up.shape[1]
+        dev = x.device
+        self.tensors = (x, W_g, noise, W_up, W_down, dout)
+        self.dx = torch.empty((N, d), dtype=torch.float32, device=dev)
+        self.dW_g = torch.empty((E, d), dtype=torch.float32, device=dev)
+        self.dW_up = torch.empty((E, d_ff, d), dtype=torch.float32, device=dev)
+        self.dW_down = torch.empty((E, d, d_ff), dtype=torch.float32, device=dev)
+        self.workspace = alloc_workspace(
+            backward_workspace_size(N, d, E, d_ff, k, capacity_factor, x.dtype), dev)
+        self.k, self.cf = k, capacity_factor
+        self._d = [desc(t) for t in (x, W_g, noise, W_up, W_down, dout, self.dx, self.dW_g,
+                                     self.dW_up, self.dW_down)]
+        self._args = [_ref(a) for a in self._d]
+        self.stats = MoeStats(_stream(stream), ctypes.c_void_p(self.workspace.data_ptr()),
+                              self.workspace.numel(), None, None, None, None, -1)
+
+    def __call__(self):
+        a = self._args
+        rc = lib().moe_backward(a[0], a[1], a[2], a[3], a[4], self.k, self.cf, a[5], a[6], a[7],
+                                a[8], a[9], ctypes.byref(self.stats))
+        if rc != 0:
+            raise MoeError(rc, "moe_backward")
+        return self.dx, self.dW_g, self.dW_up, self.dW_down
+
+
 def router_workspace_size(N: int, d: int, E: int, dtype: torch.dtype) -> int:
     code = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
     return int(lib().moe_router_workspace_size(N, d, E, code))

@@ -34,15 +34,17 @@ __device__ __forceinline__ void split3_bits(float a, unsigned short &hi, unsigne
 
 // One wave per token: dY rows (bf16, kept choices), dg by a wave reduction in
 // a fixed butterfly order, then ds for every choice (dropped ones have dg 0
-// but still took part in the softmax).
+// but still took part in the softmax). Y holds the experts' bf16 outputs, the
+// values the forward combined; 8 columns per lane and load.
 __global__ __launch_bounds__(256) void combine_backward_kernel(
-    const unsigned short *__restrict__ dout, const float *__restrict__ Yf,
+    const unsigned short *__restrict__ dout, const unsigned short *__restrict__ Y,
     const float *__restrict__ gate, const int32_t *__restrict__ slot, int N, int d, int k,
     unsigned short *__restrict__ dY, float *__restrict__ ds) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= N)
         return;
+    const int chunks = d / 8;
     const unsigned short *go = dout + t * d;
     float dg[kMaxTopK];
     float gdg = 0.f;
@@ -51,12 +53,22 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
         float p = 0.f;
         if (slot[a] >= 0) {
             const float g = gate[a];
-            const float *yr = Yf + a * d;
+            const unsigned short *yr = Y + a * d;
             unsigned short *dyr = dY + a * d;
-            for (int i = lane; i < d; i += 64) {
-                const float o = bf16_bits_to_f32(go[i]);
-                p = fmaf(o, yr[i], p);
-                dyr[i] = f32_to_bf16_bits(g * o);
+            for (int c = lane; c < chunks; c += 64) {
+                const u32x4 ov = *reinterpret_cast<const u32x4 *>(go + 8 * c);
+                const u32x4 yv = *reinterpret_cast<const u32x4 *>(yr + 8 * c);
+                u32x4 w;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float o0 = __uint_as_float(ov[q] << 16);
+                    const float o1 = __uint_as_float(ov[q] & 0xffff0000u);
+                    p = fmaf(o0, __uint_as_float(yv[q] << 16), p);
+                    p = fmaf(o1, __uint_as_float(yv[q] & 0xffff0000u), p);
+                    w[q] = (unsigned)f32_to_bf16_bits(g * o0) |
+                           ((unsigned)f32_to_bf16_bits(g * o1) << 16);
+                }
+                *reinterpret_cast<u32x4 *>(dyr + 8 * c) = w;
             }
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1)
@@ -74,16 +86,21 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
     }
 }
 
-// dsT3 [E, 3*Np] bf16: row e holds the three bf16 terms of ds(t, e) at
-// columns t, Np + t, 2*Np + t (0 where token t did not choose e or t >= N).
+// Token-chunked operands of the router-weight product dW_g = ds^T x: chunk s
+// holds tokens [s*Tc, (s+1)*Tc). dsT3[s][e][q*Tc + i] is term q of the exact
+// three-term split of ds(s*Tc + i, e) (0 where that token did not choose e or
+// lies past N).
 __global__ __launch_bounds__(256) void ds_split_kernel(const float *__restrict__ ds,
                                                        const int32_t *__restrict__ idx, int N,
-                                                       int Np, int E, int k,
+                                                       int Tc, int S, int E, int k,
                                                        unsigned short *__restrict__ dsT3) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)E * Np)
+    if (i >= (int64_t)S * E * Tc)
         return;
-    const int e = (int)(i / Np), t = (int)(i - (int64_t)e * Np);
+    const int tt = (int)(i % Tc);
+    const int64_t se = i / Tc;             // s * E + e
+    const int e = (int)(se % E);
+    const int t = (int)(se / E) * Tc + tt;
     float v = 0.f;
     if (t < N)
         for (int j = 0; j < k; ++j)
@@ -91,49 +108,92 @@ __global__ __launch_bounds__(256) void ds_split_kernel(const float *__restrict__
                 v = ds[(int64_t)t * k + j];
     unsigned short h, m, l;
     split3_bits(v, h, m, l);
-    unsigned short *row = dsT3 + (int64_t)e * 3 * Np;
-    row[t] = h;
-    row[Np + t] = m;
-    row[2 * Np + t] = l;
+    unsigned short *row = dsT3 + se * 3 * Tc;
+    row[tt] = h;
+    row[Tc + tt] = m;
+    row[2 * Tc + tt] = l;
 }
 
-// Tiled transpose through LDS: out[e][c][r] = src row R(e, r), column c, for
-// r < used[e] (used == NULL: every r < nrows), and 0 for the rest of the Kp
-// columns. Row map: 0: e*ceff + r (dense [E, ceff, C]); 1: slot_token[e*ceff
-// + r] (assignment rows); 2: slot_token[...] / k (token rows); 3: r (a plain
-// [rows, C] matrix, one batch). out has `copies` copies side by side along
-// the last dimension (row length copies * Kp). 64 x 64 tiles, 256 threads.
+// dW_g[e][c] = sum over chunks s (in order) of part[s][e][c].
+__global__ __launch_bounds__(256) void chunk_sum_kernel(const float *__restrict__ part, int S,
+                                                        int64_t n, float *__restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n)
+        return;
+    float acc = 0.f;
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            v[q] = part[(int64_t)(s + q) * n + i];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc += v[q];
+    }
+    for (; s < S; ++s)
+        acc += part[(int64_t)s * n + i];
+    out[i] = acc;
+}
+
+// Tiled transpose through LDS: out[b][c][q*Kp + r] = src row R(b, r), column
+// c, for r below the batch's row count, and 0 for the rest of the Kp columns,
+// for each of `copies` copies q. Row map: 0: b*ceff + r (dense batches of
+// ceff rows; without `used`, the batch holds min(ceff, nrows - b*ceff) rows);
+// 1: slot_token[b*ceff + r] (assignment rows); 2: slot_token[...] / k (token
+// rows); with `used`, batch b holds used[b] rows. 64 x 64 tiles, 256
+// threads, 16-byte loads and stores (C and Kp multiples of 8).
 __global__ __launch_bounds__(256) void transpose_rows_kernel(
     const unsigned short *__restrict__ src, int C, int64_t ceff, const int32_t *__restrict__ used,
-    int nrows, const int32_t *__restrict__ slot_token, int k, int map, int Kp, int copies,
+    int64_t nrows, const int32_t *__restrict__ slot_token, int k, int map, int Kp, int copies,
     unsigned short *__restrict__ out) {
-    __shared__ unsigned short tile[64][66];
-    const int e = blockIdx.z;
+    constexpr int LD = 64 + 2;               // padded row of the LDS tile (u16)
+    __shared__ unsigned short tile[64 * LD];
+    const int b = blockIdx.z;
     const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-    const int rows = used ? used[e] : nrows;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 64 x 4
-    for (int rr = ty; rr < 64; rr += 4) {
-        const int r = r0 + rr, c = c0 + tx;
-        unsigned short v = 0;
+    int64_t rows;
+    if (used)
+        rows = used[b];
+    else {
+        rows = nrows - (int64_t)b * ceff;
+        rows = rows < ceff ? rows : ceff;
+    }
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int q = tid + 256 * p;
+        const int rr = q >> 3, cc = (q & 7) * 8;
+        const int r = r0 + rr, c = c0 + cc;
+        u32x4 v = {0u, 0u, 0u, 0u};
         if (r < rows && c < C) {
-            int64_t row;
-            const int64_t sr = (int64_t)e * ceff + r;
-            if (map == 0) row = sr;
-            else if (map == 1) row = slot_token[sr];
-            else if (map == 2) row = slot_token[sr] / k;
-            else row = r;
-            v = src[row * C + c];
+            const int64_t sr = (int64_t)b * ceff + r;
+            const int64_t row = map == 0 ? sr
+                              : map == 1 ? (int64_t)slot_token[sr]
+                                         : (int64_t)(slot_token[sr] / k);
+            v = *reinterpret_cast<const u32x4 *>(src + row * C + c);
         }
-        tile[rr][tx] = v;
+        unsigned short *dst = tile + rr * LD + cc;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            dst[2 * h] = (unsigned short)(v[h] & 0xffffu);
+            dst[2 * h + 1] = (unsigned short)(v[h] >> 16);
+        }
     }
     __syncthreads();
-    for (int cc = ty; cc < 64; cc += 4) {
-        const int c = c0 + cc, r = r0 + tx;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int q = tid + 256 * p;
+        const int cc = q >> 3, rr = (q & 7) * 8;
+        const int c = c0 + cc, r = r0 + rr;
         if (c < C && r < Kp) {
-            const unsigned short v = tile[tx][cc];
-            unsigned short *o = out + ((int64_t)e * C + c) * ((int64_t)copies * Kp) + r;
-            for (int q = 0; q < copies; ++q)
-                o[(int64_t)q * Kp] = v;
+            u32x4 w;
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+                w[h] = (unsigned)tile[(rr + 2 * h) * LD + cc] |
+                       ((unsigned)tile[(rr + 2 * h + 1) * LD + cc] << 16);
+            unsigned short *o = out + ((int64_t)b * C + c) * ((int64_t)copies * Kp) + r;
+            for (int qq = 0; qq < copies; ++qq)
+                *reinterpret_cast<u32x4 *>(o + (int64_t)qq * Kp) = w;
         }
     }
 }
@@ -169,24 +229,33 @@ __global__ __launch_bounds__(256) void dx_kernel(const float *__restrict__ dXa,
 
 }  // namespace
 
-hipError_t launch_combine_backward(const void *dout, const float *Yf, const float *gate,
+hipError_t launch_combine_backward(const void *dout, const void *Y, const float *gate,
                                    const int32_t *slot, int64_t N, int64_t d, int k, void *dY,
                                    float *ds, hipStream_t s) {
     if (N == 0)
         return hipSuccess;
     hipLaunchKernelGGL(combine_backward_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s,
-                       static_cast<const unsigned short *>(dout), Yf, gate, slot, (int)N, (int)d,
-                       k, static_cast<unsigned short *>(dY), ds);
+                       static_cast<const unsigned short *>(dout),
+                       static_cast<const unsigned short *>(Y), gate, slot, (int)N, (int)d, k,
+                       static_cast<unsigned short *>(dY), ds);
     return hipGetLastError();
 }
 
-hipError_t launch_ds_split(const float *ds, const int32_t *idx, int64_t N, int64_t Np, int E,
-                           int k, void *dsT3, hipStream_t s) {
-    const int64_t n = (int64_t)E * Np;
+hipError_t launch_ds_split(const float *ds, const int32_t *idx, int64_t N, int64_t Tc, int64_t S,
+                           int E, int k, void *dsT3, hipStream_t s) {
+    const int64_t n = S * E * Tc;
     if (n == 0)
         return hipSuccess;
     hipLaunchKernelGGL(ds_split_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ds,
-                       idx, (int)N, (int)Np, E, k, static_cast<unsigned short *>(dsT3));
+                       idx, (int)N, (int)Tc, (int)S, E, k, static_cast<unsigned short *>(dsT3));
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_sum(const float *part, int64_t S, int64_t n, float *out, hipStream_t s) {
+    if (n == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(chunk_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part,
+                       (int)S, n, out);
     return hipGetLastError();
 }
 
@@ -195,11 +264,13 @@ hipError_t launch_transpose_rows(const void *src, int64_t C, int64_t ceff, const
                                  int64_t Kp, int copies, int batch, void *out, hipStream_t s) {
     if (Kp == 0 || C == 0 || batch == 0)
         return hipSuccess;
+    if (C % 8 != 0 || Kp % 8 != 0 || map < 0 || map > 2)
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL(transpose_rows_kernel,
                        dim3((unsigned)((Kp + 63) / 64), (unsigned)((C + 63) / 64),
                             (unsigned)batch),
                        dim3(256), 0, s, static_cast<const unsigned short *>(src), (int)C, ceff,
-                       used, (int)nrows, slot_token, k, map, (int)Kp, copies,
+                       used, nrows, slot_token, k, map, (int)Kp, copies,
                        static_cast<unsigned short *>(out));
     return hipGetLastError();
 }

@@ -106,15 +106,19 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
 
 // Backward element-wise and layout kernels (backward.hip).
 // dY rows (bf16, kept choices) = gate * dout; ds [N, k] = gate * (dg - sum gate*dg)
-// with dg = <dout, Yf> (Yf: fp32 expert outputs, assignment-major).
-hipError_t launch_combine_backward(const void *dout, const float *Yf, const float *gate,
+// with dg = <dout, Y> (Y: the experts' bf16 outputs, assignment-major). d % 8 == 0.
+hipError_t launch_combine_backward(const void *dout, const void *Y, const float *gate,
                                    const int32_t *slot, int64_t N, int64_t d, int k, void *dY,
                                    float *ds, hipStream_t s);
-// dsT3 [E, 3*Np] bf16: exact three-term split of ds(t, e) at columns t, Np+t, 2Np+t.
-hipError_t launch_ds_split(const float *ds, const int32_t *idx, int64_t N, int64_t Np, int E,
-                           int k, void *dsT3, hipStream_t s);
-// out[b][c][q*Kp + r] = src row R(b, r), column c (0 past the rows), for q < copies;
-// map 0: b*ceff + r, 1: slot_token[b*ceff + r], 2: slot_token[...] / k, 3: r.
+// dsT3 [S][E][3*Tc] bf16: exact three-term split of ds(s*Tc + i, e) at columns
+// i, Tc + i, 2*Tc + i (tokens chunked by Tc).
+hipError_t launch_ds_split(const float *ds, const int32_t *idx, int64_t N, int64_t Tc, int64_t S,
+                           int E, int k, void *dsT3, hipStream_t s);
+// out[i] = sum over s < S (in order) of part[s * n + i].
+hipError_t launch_chunk_sum(const float *part, int64_t S, int64_t n, float *out, hipStream_t s);
+// out[b][c][q*Kp + r] = src row R(b, r), column c (0 past the batch's rows), for
+// q < copies; map 0: b*ceff + r (without used: min(ceff, nrows - b*ceff) rows),
+// 1: slot_token[b*ceff + r], 2: slot_token[...] / k. C % 8 == 0, Kp % 8 == 0.
 hipError_t launch_transpose_rows(const void *src, int64_t C, int64_t ceff, const int32_t *used,
                                  int64_t nrows, const int32_t *slot_token, int k, int map,
                                  int64_t Kp, int copies, int batch, void *out, hipStream_t s);

@@ -831,15 +831,28 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
                                     float *C, hipStream_t s) {
     if (M == 0 || batch == 0)
         return hipSuccess;
+    const auto *a = static_cast<const unsigned short *>(A);
+    const auto *w = static_cast<const unsigned short *>(W);
+    // 256x256 tiles for large products (at least four rounds of them), else
+    // 128x128
+    const int64_t t256 = ((M + 255) / 256) * ((Nout + 255) / 256);
+    if (M >= 512 && Nout >= 512 && K >= 256 && t256 * batch >= 1024) {
+        const int64_t grid = (t256 + kXcds - 1) / kXcds * kXcds;
+        hipLaunchKernelGGL((expert_gemm_kernel<256, 256, 2, 4, kBK, 2, 2>),
+                           dim3((unsigned)grid, (unsigned)batch), dim3(512), 0, s, a, w, (int)K,
+                           (int)Nout, 1, 1, (int)M, (const int32_t *)nullptr,
+                           (const int32_t *)nullptr, (const int32_t *)nullptr,
+                           (unsigned short *)nullptr, C, (float *)nullptr, 0, kActRelu,
+                           (const float *)nullptr, (const unsigned short *)nullptr, sa, sb, sc);
+        return hipGetLastError();
+    }
     const int64_t grid = (((M + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) / kXcds * kXcds;
     hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, kBK, 2, 2>),
-                       dim3((unsigned)grid, (unsigned)batch), dim3(256), 0, s,
-                       static_cast<const unsigned short *>(A),
-                       static_cast<const unsigned short *>(W), (int)K, (int)Nout, 1, 1, (int)M,
+                       dim3((unsigned)grid, (unsigned)batch), dim3(256), 0, s, a, w, (int)K,
+                       (int)Nout, 1, 1, (int)M, (const int32_t *)nullptr,
                        (const int32_t *)nullptr, (const int32_t *)nullptr,
-                       (const int32_t *)nullptr, (unsigned short *)nullptr, C, (float *)nullptr,
-                       0, kActRelu, (const float *)nullptr, (const unsigned short *)nullptr, sa,
-                       sb, sc);
+                       (unsigned short *)nullptr, C, (float *)nullptr, 0, kActRelu,
+                       (const float *)nullptr, (const unsigned short *)nullptr, sa, sb, sc);
     return hipGetLastError();
 }
 

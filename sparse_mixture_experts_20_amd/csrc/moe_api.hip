@@ -70,17 +70,33 @@ Layout layout_of(const Dims &m) {
 // Workspace of the backward pass (bf16 layers): the recomputed forward state
 // and the gradient intermediates.
 struct BwdLayout {
-    size_t idx, gate, slot, used, tiles, slot_token, H, Yf, dY, ds, dZ, dXa, WT, T1, T2, dsT3,
-        xT3, router, total;
-    int64_t Kp, Np;
+    size_t idx, gate, slot, used, tiles, slot_token, H, Y, dY, ds, dZ, dXa, WT, T1, T2, dsT3,
+        xT3, gpart, router, total;
+    int64_t Kp, Tc, S;
 };
+
+// Token chunks of the router-weight product dW_g = ds^T x: Tc tokens (a
+// multiple of 64) per chunk, enough chunks for ~512 product tiles, and the
+// per-chunk fp32 partials within 32 MiB.
+void dwg_chunks(int64_t N, int64_t E, int64_t d, int64_t &Tc, int64_t &S) {
+    const int64_t tiles = ((E + 127) / 128) * ((d + 127) / 128);
+    int64_t want = (512 + tiles - 1) / tiles;
+    const int64_t cap = ((int64_t)32 << 20) / (E * d * 4);
+    if (want > cap) want = cap;
+    if (want > (N + 63) / 64) want = (N + 63) / 64;
+    if (want < 1) want = 1;
+    Tc = ((N + want - 1) / want + 63) / 64 * 64;
+    if (Tc < 64) Tc = 64;
+    S = (N + Tc - 1) / Tc;
+}
 
 BwdLayout bwd_layout_of(const Dims &m) {
     BwdLayout L;
     size_t o = 0;
     const size_t nk = (size_t)m.N * m.k;
     L.Kp = (m.ceff + 7) / 8 * 8;
-    L.Np = (m.N + 7) / 8 * 8;
+    dwg_chunks(m.N, m.E, m.d, L.Tc, L.S);
+    const size_t tok = (size_t)(L.S * L.Tc);     // chunked token columns
     L.idx = o;        o += align_up(nk * 4);
     L.gate = o;       o += align_up(nk * 4);
     L.slot = o;       o += align_up(nk * 4);
@@ -88,7 +104,7 @@ BwdLayout bwd_layout_of(const Dims &m) {
     L.tiles = o;      o += align_up((size_t)(2 * (m.E + 1)) * 4);
     L.slot_token = o; o += align_up((size_t)(m.E * m.ceff) * 4);
     L.H = o;          o += align_up((size_t)(m.E * m.ceff * m.d_ff) * 2);
-    L.Yf = o;         o += align_up(nk * (size_t)m.d * 4);
+    L.Y = o;          o += align_up(nk * (size_t)m.d * 2);
     L.dY = o;         o += align_up(nk * (size_t)m.d * 2);
     L.ds = o;         o += align_up(nk * 4);
     L.dZ = o;         o += align_up((size_t)(m.E * m.ceff * m.d_ff) * 2);
@@ -96,8 +112,9 @@ BwdLayout bwd_layout_of(const Dims &m) {
     L.WT = o;         o += align_up((size_t)(m.E * m.d * m.d_ff) * 2);
     L.T1 = o;         o += align_up((size_t)(m.E * m.d * L.Kp) * 2);
     L.T2 = o;         o += align_up((size_t)(m.E * m.d_ff * L.Kp) * 2);
-    L.dsT3 = o;       o += align_up((size_t)(m.E * 3 * L.Np) * 2);
-    L.xT3 = o;        o += align_up((size_t)(m.d * 3 * L.Np) * 2);
+    L.dsT3 = o;       o += align_up((size_t)m.E * 3 * tok * 2);
+    L.xT3 = o;        o += align_up((size_t)m.d * 3 * tok * 2);
+    L.gpart = o;      o += align_up((size_t)(L.S * m.E * m.d) * 4);
     L.router = o;     o += router_bytes(m.N, m.d, m.E, m.dtype);
     L.total = o;
     return L;
@@ -731,37 +748,39 @@ int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *n
                                          : reinterpret_cast<int32_t *>(ws + L.used);
     int32_t *tiles = reinterpret_cast<int32_t *>(ws + L.tiles);
     int32_t *st = reinterpret_cast<int32_t *>(ws + L.slot_token);
-    void *H = ws + L.H, *dY = ws + L.dY, *dZ = ws + L.dZ, *WT = ws + L.WT;
+    void *H = ws + L.H, *Y = ws + L.Y, *dY = ws + L.dY, *dZ = ws + L.dZ, *WT = ws + L.WT;
     void *T1 = ws + L.T1, *T2 = ws + L.T2, *dsT3 = ws + L.dsT3, *xT3 = ws + L.xT3;
-    float *Yf = reinterpret_cast<float *>(ws + L.Yf);
     float *ds = reinterpret_cast<float *>(ws + L.ds);
     float *dXa = reinterpret_cast<float *>(ws + L.dXa);
-    const int64_t ceff = m.ceff, Kp = L.Kp, Np = L.Np;
+    float *gpart = reinterpret_cast<float *>(ws + L.gpart);
+    const int64_t ceff = m.ceff, Kp = L.Kp, Tc = L.Tc, S = L.S;
     const int64_t rpe = rows_per_expert(N, k, E, ceff);
     const int Ei = (int)E;
 
-    // forward state: routing, plan, H, and the experts' outputs in fp32
+    // forward state: routing, plan, H and the experts' bf16 outputs
     rc = router_checked(x, W_g, noise, N, d, E, k, idx, gate, ws + L.router, s);
     if (rc != MOE_OK)
         return rc;
     MOE_TRY(moe::launch_dispatch(idx, N, Ei, k, ceff, slot, used, st, tiles, s));
     MOE_TRY(moe::launch_expert_up(true, x->data, W_up->data, d, d_ff, Ei, k, ceff, used, st,
                                   tiles, H, rpe, nullptr, 0, moe::kActRelu, nullptr, s));
-    MOE_TRY(moe::launch_expert_rows_f32(H, W_down->data, d_ff, d, Ei, k, ceff, used, st, tiles,
-                                        Yf, rpe, s));
-    // combine and softmax backward; router weights: dW_g = ds^T x on split ds
-    MOE_TRY(moe::launch_combine_backward(dout->data, Yf, gate, slot, N, d, k, dY, ds, s));
-    MOE_TRY(moe::launch_ds_split(ds, idx, N, Np, Ei, k, dsT3, s));
-    MOE_TRY(moe::launch_transpose_rows(x->data, d, 0, nullptr, N, nullptr, k, 3, Np, 3, 1, xT3,
-                                       s));
-    MOE_TRY(moe::launch_batched_gemm_bf16(dsT3, xT3, E, 3 * Np, d, 1, 0, 0, 0,
-                                          static_cast<float *>(dW_g->data), s));
+    MOE_TRY(moe::launch_expert_down(true, H, W_down->data, d, d_ff, Ei, k, ceff, used, st, tiles,
+                                    Y, rpe, nullptr, 0, nullptr, s));
+    // combine and softmax backward; router weights: dW_g = ds^T x, per token
+    // chunk on the exact split of ds, then the chunks summed in order
+    MOE_TRY(moe::launch_combine_backward(dout->data, Y, gate, slot, N, d, k, dY, ds, s));
+    MOE_TRY(moe::launch_ds_split(ds, idx, N, Tc, S, Ei, k, dsT3, s));
+    MOE_TRY(moe::launch_transpose_rows(x->data, d, Tc, nullptr, N, nullptr, k, 0, Tc, 3, (int)S,
+                                       xT3, s));
+    MOE_TRY(moe::launch_batched_gemm_bf16(dsT3, xT3, E, 3 * Tc, d, (int)S, E * 3 * Tc,
+                                          d * 3 * Tc, E * d, gpart, s));
+    MOE_TRY(moe::launch_chunk_sum(gpart, S, E * d, static_cast<float *>(dW_g->data), s));
     // experts, input side: dZ = (dY W_down) [H > 0]; dX = dZ W_up; dx
-    MOE_TRY(moe::launch_transpose_rows(W_down->data, d_ff, d, nullptr, d, nullptr, k, 0, d, 1, Ei,
-                                       WT, s));
-    MOE_TRY(moe::launch_expert_dz(dY, WT, H, d, d_ff, Ei, k, ceff, used, st, tiles, dZ, rpe, s));
-    MOE_TRY(moe::launch_transpose_rows(W_up->data, d, d_ff, nullptr, d_ff, nullptr, k, 0, d_ff, 1,
+    MOE_TRY(moe::launch_transpose_rows(W_down->data, d_ff, d, nullptr, E * d, nullptr, k, 0, d, 1,
                                        Ei, WT, s));
+    MOE_TRY(moe::launch_expert_dz(dY, WT, H, d, d_ff, Ei, k, ceff, used, st, tiles, dZ, rpe, s));
+    MOE_TRY(moe::launch_transpose_rows(W_up->data, d, d_ff, nullptr, E * d_ff, nullptr, k, 0,
+                                       d_ff, 1, Ei, WT, s));
     MOE_TRY(moe::launch_expert_rows_f32(dZ, WT, d_ff, d, Ei, k, ceff, used, st, tiles, dXa, rpe,
                                         s));
     MOE_TRY(moe::launch_dx(dXa, ds, idx, slot, static_cast<const float *>(W_g->data), N, d, k,

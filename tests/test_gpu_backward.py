@@ -9,11 +9,12 @@ dW_up, dW_down):
 The GPU path rounds H, dY = g * dout and dZ to bf16 (relative error 2^-9
 each) and accumulates in fp32; the errors of the few such roundings on any
 path to a gradient entry stay near 1e-2 of an entry's size at worst, and
-the L2 norm averages them down to a few 1e-3. Small cases compare every
-entry; the nanoMoE layer compares dx on sampled token rows (the oracle's
-backward is serial and sized for tests), the weight gradients of a layer of
-several row tiles per expert in full, and checks that two runs agree bit for
-bit.
+the L2 norm averages them down to a few 1e-3. Small cases (several row
+tiles per expert, ragged tails, drops, edge shapes) compare every entry. At
+the nanoMoE and Mixtral shapes, in the launch configuration the backward
+benchmark times, dx is compared on sampled token rows and the weight
+gradients on sampled hidden units (whole rows of dW_up, whole columns of
+dW_down), and two runs must agree bit for bit.
 """
 import numpy as np
 import pytest
@@ -152,4 +153,35 @@ def test_nanomoe_backward_sampled_rows(torch_mod):
     x, wg, noise, wu, wd, dout = _host(wl)
     ref = oracle.backward_rows(x, wg, noise, wu, wd, wl.k, wl.cfg.cf, dout, rows)
     _close("dx[rows]", G.to_np(dx)[rows], ref)
+    del dev
+
+
+@pytest.mark.parametrize("name,nunits", [("nanomoe", 6), ("mixtral", 4)])
+def test_benchmark_layer_weight_gradients_sampled(torch_mod, name, nunits):
+    """The benchmark's layer shapes in the launch configuration the backward
+    benchmark times: routing for every token, and for two experts (the most
+    loaded one and a seeded other) sampled rows of dW_up and columns of
+    dW_down, each an exact sum over all of the expert's kept tokens."""
+    torch = torch_mod
+    wl = W.make(name)
+    G.say(f"[backward] {name}: N={wl.N} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff}")
+    dev = _upload(wl, keep_host=False)
+    (dx, dwg, dwu, dwd), st = _run(dev, wl.k, wl.cfg.cf, stats=True)
+    torch.cuda.synchronize()
+    route = oracle.forward(wl, rows=[0])
+    G.check_routing(route, st)
+    rng = np.random.default_rng(3)
+    x, wg, noise, dout = wl.x64(), wl.wg64(), wl.noise64(), wl.as_f64(wl.dout())
+    top = int(np.argmax(route.used))
+    other = int(rng.choice([e for e in range(wl.E) if e != top]))
+    for e in (top, other):
+        fs = np.sort(rng.choice(wl.d_ff, size=nunits, replace=False))
+        G.say(f"[backward] {name}: expert {e} ({route.used[e]} rows), units {fs.tolist()}")
+        up, down = oracle.backward_expert_units(x, wg, noise, e, wl.as_f64(wl.w_up(e)),
+                                                wl.as_f64(wl.w_down(e)), wl.k, wl.cfg.cf, dout,
+                                                fs)
+        idx = torch.from_numpy(fs).to("cuda")
+        _close(f"dW_up[{e}][f]", G.to_np(dwu[e].index_select(0, idx)), up)
+        _close(f"dW_down[{e}][:, f]", G.to_np(dwd[e].index_select(1, idx).t().contiguous()),
+               down)
     del dev

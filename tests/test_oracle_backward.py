@@ -146,3 +146,22 @@ def test_backward_rows_match_the_full_backward():
     assert oracle.backward_rows(x, wg, noise, wu, wd, wl.k, wl.cfg.cf, dout, []).shape == (0, 16)
     with pytest.raises(ValueError):
         oracle.backward_rows(x, wg, noise, wu, wd, wl.k, wl.cfg.cf, dout, [40])
+
+
+def test_backward_expert_units_match_the_full_backward():
+    """Rows of dW_up[e] and columns of dW_down[e] for listed hidden units
+    equal the full backward's entries (same terms, same token order), with
+    drops in play."""
+    wl = W.custom("bwd_units", N=60, d=16, E=4, k=2, d_ff=24, dtype="f32", cf=0.6, sigma=0.3,
+                  seed=68, w_std=0.2)
+    x, wg, noise, wu, wd = _arrays(wl)
+    dout = np.random.default_rng(69).standard_normal((wl.N, wl.d))
+    _, _, dwu, dwd = oracle.backward(x, wg, noise, wu, wd, wl.k, wl.cfg.cf, dout)
+    units = [23, 0, 7]
+    for e in range(wl.E):
+        up, down = oracle.backward_expert_units(x, wg, noise, e, wu[e], wd[e], wl.k, wl.cfg.cf,
+                                                dout, units)
+        np.testing.assert_allclose(up, dwu[e][units], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(down, dwd[e][:, units].T, rtol=1e-12, atol=1e-14)
+    with pytest.raises(ValueError):
+        oracle.backward_expert_units(x, wg, noise, 0, wu[0], wd[0], wl.k, wl.cfg.cf, dout, [24])

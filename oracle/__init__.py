@@ -50,14 +50,14 @@ def lib():
         L.oracle_combine.argtypes = [_i64, _i64, _i32, _dp, _ip, _dp, _dp]
         L.oracle_combine.restype = None
         L.oracle_backward.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _dp, _dp, _dp, _dp, _dp,
-                                      _dp, _dp, _dp, _dp, _dp]
+                                      _i32, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         L.oracle_backward.restype = ctypes.c_int
         L.oracle_backward_rows.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _dp, _dp, _dp,
-                                           _dp, _dp, _dp, _i64, _lp, _dp]
+                                           _dp, _dp, _i32, _dp, _dp, _dp, _i64, _lp, _dp]
         L.oracle_backward_rows.restype = ctypes.c_int
         L.oracle_backward_expert_units.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _dp, _dp,
-                                                   _dp, _i64, _dp, _dp, _dp, _i64, _lp, _dp,
-                                                   _dp]
+                                                   _dp, _i64, _dp, _dp, _i32, _dp, _dp, _i64,
+                                                   _lp, _dp, _dp]
         L.oracle_backward_expert_units.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = ctypes.c_int
@@ -157,11 +157,13 @@ def combine(gate: np.ndarray, slot: np.ndarray, y: np.ndarray) -> np.ndarray:
     return out
 
 
-def backward(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout64):
-    """Gradients of the layer (ReLU experts, no biases) for the output
-    gradient dout [N, d]: returns (dx [N, d], dW_g [E, d], dW_up [E, d_ff, d],
-    dW_down [E, d, d_ff]), all float64. wups64/wdowns64 are [E, d_ff, d] and
-    [E, d, d_ff] arrays (or lists of per-expert matrices)."""
+def _act_code(act: str) -> int:
+    if act not in ("relu", "gelu"):
+        raise ValueError("act must be 'relu' or 'gelu'")
+    return 1 if act == "gelu" else 0
+
+
+def _bwd_inputs(x64, wg64, noise64, wups64, wdowns64, dout64):
     x64 = _c(x64, np.float64)
     wg64 = _c(wg64, np.float64)
     wu = _c(np.stack(list(wups64)) if isinstance(wups64, (list, tuple)) else wups64, np.float64)
@@ -173,54 +175,75 @@ def backward(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout64):
     E, d_ff = wu.shape[0], wu.shape[1]
     if wd.shape != (E, d, d_ff) or dout64.shape != (N, d) or wg64.shape != (E, d):
         raise ValueError("shapes")
+    return x64, wg64, n64, wu, wd, dout64, N, d, E, d_ff
+
+
+def _bias(b, shape):
+    if b is None:
+        return None
+    b = _c(b, np.float64)
+    if b.shape != shape:
+        raise ValueError("bias shape")
+    return b
+
+
+def backward(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout64,
+             act: str = "relu", bup64=None, bdown64=None):
+    """Gradients of the layer for the output gradient dout [N, d]: returns
+    (dx [N, d], dW_g [E, d], dW_up [E, d_ff, d], dW_down [E, d, d_ff]), all
+    float64, and with biases (bup64 [E, d_ff], bdown64 [E, d]) also
+    (db_up [E, d_ff], db_down [E, d]). wups64/wdowns64 are [E, d_ff, d] and
+    [E, d, d_ff] arrays (or lists of per-expert matrices)."""
+    x64, wg64, n64, wu, wd, dout64, N, d, E, d_ff = _bwd_inputs(x64, wg64, noise64, wups64,
+                                                                wdowns64, dout64)
+    bu, bd = _bias(bup64, (E, d_ff)), _bias(bdown64, (E, d))
+    biased = bu is not None or bd is not None
     C = capacity(N, E, k, cf)
     dx = np.empty((N, d))
     dwg = np.empty((E, d))
     dwu = np.empty((E, d_ff, d))
     dwd = np.empty((E, d, d_ff))
+    dbu = np.empty((E, d_ff)) if biased else None
+    dbd = np.empty((E, d)) if biased else None
     rc = lib().oracle_backward(N, d, E, k, d_ff, C, _ptr(x64, _dp), _ptr(wg64, _dp),
-                               _ptr(n64, _dp), _ptr(wu, _dp), _ptr(wd, _dp), _ptr(dout64, _dp),
-                               _ptr(dx, _dp), _ptr(dwg, _dp), _ptr(dwu, _dp), _ptr(dwd, _dp))
+                               _ptr(n64, _dp), _ptr(wu, _dp), _ptr(wd, _dp), _act_code(act),
+                               _ptr(bu, _dp), _ptr(bd, _dp), _ptr(dout64, _dp), _ptr(dx, _dp),
+                               _ptr(dwg, _dp), _ptr(dwu, _dp), _ptr(dwd, _dp), _ptr(dbu, _dp),
+                               _ptr(dbd, _dp))
     if rc != 0:
         raise MemoryError("oracle_backward: allocation failed")
+    if biased:
+        return dx, dwg, dwu, dwd, dbu, dbd
     return dx, dwg, dwu, dwd
 
 
 def backward_rows(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout64,
-                  rows: Sequence[int]):
+                  rows: Sequence[int], act: str = "relu", bup64=None, bdown64=None):
     """dx [len(rows), d] (float64) of the listed tokens, as ``backward``
     computes it; the routing covers every token, the expert terms only the
     listed ones (for layers too large for the full backward)."""
-    x64 = _c(x64, np.float64)
-    wg64 = _c(wg64, np.float64)
-    wu = _c(np.stack(list(wups64)) if isinstance(wups64, (list, tuple)) else wups64, np.float64)
-    wd = _c(np.stack(list(wdowns64)) if isinstance(wdowns64, (list, tuple)) else wdowns64,
-            np.float64)
-    n64 = None if noise64 is None else _c(noise64, np.float64)
-    dout64 = _c(dout64, np.float64)
-    N, d = x64.shape
-    E, d_ff = wu.shape[0], wu.shape[1]
-    if wd.shape != (E, d, d_ff) or dout64.shape != (N, d) or wg64.shape != (E, d):
-        raise ValueError("shapes")
+    x64, wg64, n64, wu, wd, dout64, N, d, E, d_ff = _bwd_inputs(x64, wg64, noise64, wups64,
+                                                                wdowns64, dout64)
+    bu, bd = _bias(bup64, (E, d_ff)), _bias(bdown64, (E, d))
     r = _c(np.asarray(rows, dtype=np.int64), np.int64)
     if r.size and (r.min() < 0 or r.max() >= N):
         raise ValueError("rows out of range")
     dx = np.empty((r.size, d))
     rc = lib().oracle_backward_rows(N, d, E, k, d_ff, capacity(N, E, k, cf), _ptr(x64, _dp),
                                     _ptr(wg64, _dp), _ptr(n64, _dp), _ptr(wu, _dp),
-                                    _ptr(wd, _dp), _ptr(dout64, _dp), r.size, _ptr(r, _lp),
-                                    _ptr(dx, _dp))
+                                    _ptr(wd, _dp), _act_code(act), _ptr(bu, _dp), _ptr(bd, _dp),
+                                    _ptr(dout64, _dp), r.size, _ptr(r, _lp), _ptr(dx, _dp))
     if rc != 0:
         raise MemoryError("oracle_backward_rows: allocation failed")
     return dx
 
 
 def backward_expert_units(x64, wg64, noise64, e: int, wup_e64, wdown_e64, k: int, cf: float,
-                          dout64, units: Sequence[int]):
+                          dout64, units: Sequence[int], act: str = "relu", bup_e64=None):
     """Sampled weight gradients of expert e, as ``backward`` computes them:
     returns (rows f of dW_up[e] [len(units), d], columns f of dW_down[e]
     [len(units), d]) for the listed hidden units f. Takes only expert e's
-    matrices (wup_e64 [d_ff, d], wdown_e64 [d, d_ff])."""
+    matrices (wup_e64 [d_ff, d], wdown_e64 [d, d_ff]) and up bias [d_ff]."""
     x64 = _c(x64, np.float64)
     wg64 = _c(wg64, np.float64)
     wu = _c(wup_e64, np.float64)
@@ -233,6 +256,7 @@ def backward_expert_units(x64, wg64, noise64, e: int, wup_e64, wdown_e64, k: int
     if wu.shape != (d_ff, d) or wd.shape != (d, d_ff) or dout64.shape != (N, d) or not (
             0 <= e < E):
         raise ValueError("shapes")
+    bu = _bias(bup_e64, (d_ff,))
     f = _c(np.asarray(units, dtype=np.int64), np.int64)
     if f.size and (f.min() < 0 or f.max() >= d_ff):
         raise ValueError("units out of range")
@@ -240,8 +264,9 @@ def backward_expert_units(x64, wg64, noise64, e: int, wup_e64, wdown_e64, k: int
     down = np.empty((f.size, d))
     rc = lib().oracle_backward_expert_units(N, d, E, k, d_ff, capacity(N, E, k, cf),
                                             _ptr(x64, _dp), _ptr(wg64, _dp), _ptr(n64, _dp), e,
-                                            _ptr(wu, _dp), _ptr(wd, _dp), _ptr(dout64, _dp),
-                                            f.size, _ptr(f, _lp), _ptr(up, _dp), _ptr(down, _dp))
+                                            _ptr(wu, _dp), _ptr(wd, _dp), _act_code(act),
+                                            _ptr(bu, _dp), _ptr(dout64, _dp), f.size,
+                                            _ptr(f, _lp), _ptr(up, _dp), _ptr(down, _dp))
     if rc != 0:
         raise MemoryError("oracle_backward_expert_units: allocation failed")
     return up, down

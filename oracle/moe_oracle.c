@@ -174,15 +174,45 @@ void oracle_expert_rows(int64_t d, int64_t d_ff, int64_t n, const int64_t *token
     }
 }
 
+/* Derivative of the exact GELU z Phi(z): Phi(z) + z phi(z), with Phi the
+ * standard normal distribution function and phi its density. */
+static double oracle_gelu_grad(double z)
+{
+    const double Phi = 0.5 * (1.0 + erf(z * 0.70710678118654752440));
+    const double phi = 0.39894228040143267794 * exp(-0.5 * z * z);
+    return Phi + z * phi;
+}
+
+/* The expert variant the backward differentiates: activation (0 ReLU,
+ * 1 GELU), optional biases bup [E, d_ff] and bdown [E, d], and where their
+ * gradients go (dbup, dbdown; NULL: not accumulated). */
+typedef struct {
+    int32_t act;
+    const double *bup, *bdown;
+    double *dbup, *dbdown;
+} expert_variant;
+
+static double act_of(int32_t act, double z)
+{
+    return act == 1 ? oracle_gelu(z) : (z > 0.0 ? z : 0.0);
+}
+
+static double act_grad(int32_t act, double z)
+{
+    return act == 1 ? oracle_gelu_grad(z) : (z > 0.0 ? 1.0 : 0.0);
+}
+
 /* The backward of one token t: adds its terms to dx_t and, when the
- * pointers are not NULL, to dWg, dWup and dWdown. gate, slot, idx are the
- * routing of all tokens; z, h, y, dz [d_ff or d] and dg [k] are scratch. */
+ * pointers are not NULL, to dWg, dWup, dWdown and the bias gradients.
+ * gate, slot, idx are the routing of all tokens; z, h, y, dz [d_ff or d] and
+ * dg [k] are scratch. */
 static void backward_token(int64_t t, int64_t d, int32_t k, int64_t d_ff,
                            const double *x, const double *Wg, const double *Wup,
-                           const double *Wdown, const double *dout, const int32_t *idx,
-                           const double *gate, const int32_t *slot, double *dxt,
-                           double *dWg, double *dWup, double *dWdown, double *z, double *h,
-                           double *y, double *dz, double *dg)
+                           const double *Wdown, const expert_variant *v,
+                           const double *dout, const int32_t *idx, const double *gate,
+                           const int32_t *slot, double *dxt, double *dWg, double *dWup,
+                           double *dWdown, double *z, double *h, double *y, double *dz,
+                           double *dg)
 {
     const double *xt = x + t * d;
     const double *go = dout + t * d;
@@ -198,13 +228,17 @@ static void backward_token(int64_t t, int64_t d, int32_t k, int64_t d_ff,
             double acc = 0.0;
             for (int64_t i = 0; i < d; ++i)
                 acc += wu[f * d + i] * xt[i];
+            if (v->bup)
+                acc += v->bup[e * d_ff + f];
             z[f] = acc;
-            h[f] = acc > 0.0 ? acc : 0.0;
+            h[f] = act_of(v->act, acc);
         }
         for (int64_t o = 0; o < d; ++o) {
             double acc = 0.0;
             for (int64_t f = 0; f < d_ff; ++f)
                 acc += wd[o * d_ff + f] * h[f];
+            if (v->bdown)
+                acc += v->bdown[e * d + o];
             y[o] = acc;
         }
         /* combine: dg = <dout_t, y>, dy = g dout_t */
@@ -212,7 +246,7 @@ static void backward_token(int64_t t, int64_t d, int32_t k, int64_t d_ff,
         for (int64_t o = 0; o < d; ++o)
             a += go[o] * y[o];
         dg[j] = a;
-        /* down: dW_down += dy h^T; dh = W_down^T dy; ReLU */
+        /* down: dW_down += dy h^T, db_down += dy; dh = W_down^T dy */
         if (dWdown) {
             double *gwd = dWdown + e * d * d_ff;
             for (int64_t o = 0; o < d; ++o) {
@@ -221,20 +255,26 @@ static void backward_token(int64_t t, int64_t d, int32_t k, int64_t d_ff,
                     gwd[o * d_ff + f] += dyo * h[f];
             }
         }
+        if (v->dbdown)
+            for (int64_t o = 0; o < d; ++o)
+                v->dbdown[e * d + o] += g * go[o];
+        /* activation: dz = dh act'(z) */
         for (int64_t f = 0; f < d_ff; ++f) {
             double acc = 0.0;
-            if (z[f] > 0.0)
-                for (int64_t o = 0; o < d; ++o)
-                    acc += wd[o * d_ff + f] * (g * go[o]);
-            dz[f] = acc;
+            for (int64_t o = 0; o < d; ++o)
+                acc += wd[o * d_ff + f] * (g * go[o]);
+            dz[f] = acc * act_grad(v->act, z[f]);
         }
-        /* up: dW_up += dz x_t^T; dx_t += W_up^T dz */
+        /* up: dW_up += dz x_t^T, db_up += dz; dx_t += W_up^T dz */
         if (dWup) {
             double *gwu = dWup + e * d_ff * d;
             for (int64_t f = 0; f < d_ff; ++f)
                 for (int64_t i = 0; i < d; ++i)
                     gwu[f * d + i] += dz[f] * xt[i];
         }
+        if (v->dbup)
+            for (int64_t f = 0; f < d_ff; ++f)
+                v->dbup[e * d_ff + f] += dz[f];
         for (int64_t i = 0; i < d; ++i) {
             double acc = 0.0;
             for (int64_t f = 0; f < d_ff; ++f)
@@ -262,9 +302,9 @@ static void backward_token(int64_t t, int64_t d, int32_t k, int64_t d_ff,
  * their pointers are not NULL; dx holds one row per listed token. */
 static int backward_impl(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff, int64_t C,
                          const double *x, const double *Wg, const double *noise,
-                         const double *Wup, const double *Wdown, const double *dout,
-                         int64_t nrows, const int64_t *rows, double *dx, double *dWg,
-                         double *dWup, double *dWdown)
+                         const double *Wup, const double *Wdown, const expert_variant *v,
+                         const double *dout, int64_t nrows, const int64_t *rows, double *dx,
+                         double *dWg, double *dWup, double *dWdown)
 {
     float *scores = (float *)malloc(sizeof(float) * (size_t)(N * E + 1));
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N * k + 1));
@@ -294,9 +334,15 @@ static int backward_impl(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_f
     if (dWdown)
         for (int64_t i = 0; i < E * d * d_ff; ++i)
             dWdown[i] = 0.0;
+    if (v->dbup)
+        for (int64_t i = 0; i < E * d_ff; ++i)
+            v->dbup[i] = 0.0;
+    if (v->dbdown)
+        for (int64_t i = 0; i < E * d; ++i)
+            v->dbdown[i] = 0.0;
     for (int64_t r = 0; r < nrows; ++r) {
         const int64_t t = rows ? rows[r] : r;
-        backward_token(t, d, k, d_ff, x, Wg, Wup, Wdown, dout, idx, gate, slot, dx + r * d,
+        backward_token(t, d, k, d_ff, x, Wg, Wup, Wdown, v, dout, idx, gate, slot, dx + r * d,
                        dWg, dWup, dWdown, z, h, y, dz, dg);
     }
 done:
@@ -306,9 +352,9 @@ done:
 }
 
 /* The layer's backward pass (the next row after the forward: gradients
- * through the gates to the router and through the experts; ReLU experts
- * without biases, dropout off). Derived by the chain rule from the forward
- * above, for a loss whose gradient with respect to out is dout [N, d]:
+ * through the gates to the router and through the experts; dropout off).
+ * Derived by the chain rule from the forward above, for a loss whose
+ * gradient with respect to out is dout [N, d]:
  *   combine  out_t = sum_j g_tj y_tj (kept j)      -> dy_tj = g_tj dout_t,
  *                                                     dg_tj = <dout_t, y_tj>
  *            (dropped j: dy = 0 and dg = 0)
@@ -318,22 +364,28 @@ done:
  *            choice of the top k is piecewise constant)
  *   scores   s_te = W_g[e] x_t + noise_te           -> dW_g[e] += ds_te x_t,
  *                                                     dx_t += ds_te W_g[e]
- *   expert   z = W_up x_t, h = ReLU(z), y = W_down h -> dW_down += dy h^T,
- *            dh = W_down^T dy, dz = dh (z > 0), dW_up += dz x_t^T,
- *            dx_t += W_up^T dz
- * The gate derivative treats the float32 rounding of the scores as the
- * identity. Sums over tokens run in token order, then choice order.
- * dx [N, d], dWg [E, d], dWup [E, d_ff, d], dWdown [E, d, d_ff]; C = capacity.
- * Scratch is allocated here (test infrastructure; not a hot path). Returns 0,
- * or -1 if an allocation fails. Serial on purpose: the sums into the weight
- * gradients have one fixed order. */
+ *   expert   z = W_up x_t + b_up, h = act(z),       -> dW_down += dy h^T, db_down += dy,
+ *            y = W_down h + b_down                     dh = W_down^T dy, dz = dh act'(z),
+ *                                                     dW_up += dz x_t^T, db_up += dz,
+ *                                                     dx_t += W_up^T dz
+ * with act ReLU (act == 0; act'(z) = [z > 0]) or the exact GELU (act == 1;
+ * [P2 slide 32]); bup [E, d_ff] and bdown [E, d] may be NULL (no biases),
+ * and dbup, dbdown are written when not NULL. The gate derivative treats
+ * the float32 rounding of the scores as the identity. Sums over tokens run
+ * in token order, then choice order. dx [N, d], dWg [E, d], dWup
+ * [E, d_ff, d], dWdown [E, d, d_ff]; C = capacity. Scratch is allocated here
+ * (test infrastructure; not a hot path). Returns 0, or -1 if an allocation
+ * fails. Serial on purpose: the sums into the weight gradients have one
+ * fixed order. */
 int oracle_backward(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff, int64_t C,
                     const double *x, const double *Wg, const double *noise,
-                    const double *Wup, const double *Wdown, const double *dout,
-                    double *dx, double *dWg, double *dWup, double *dWdown)
+                    const double *Wup, const double *Wdown, int32_t act, const double *bup,
+                    const double *bdown, const double *dout, double *dx, double *dWg,
+                    double *dWup, double *dWdown, double *dbup, double *dbdown)
 {
-    return backward_impl(N, d, E, k, d_ff, C, x, Wg, noise, Wup, Wdown, dout, N, NULL, dx, dWg,
-                         dWup, dWdown);
+    const expert_variant v = {act, bup, bdown, dbup, dbdown};
+    return backward_impl(N, d, E, k, d_ff, C, x, Wg, noise, Wup, Wdown, &v, dout, N, NULL, dx,
+                         dWg, dWup, dWdown);
 }
 
 /* dx of the listed tokens only (rows[r] in [0, N)), as oracle_backward
@@ -342,10 +394,12 @@ int oracle_backward(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff, in
  * are evaluated for the listed tokens alone. dx_rows is [nrows, d]. */
 int oracle_backward_rows(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff, int64_t C,
                          const double *x, const double *Wg, const double *noise,
-                         const double *Wup, const double *Wdown, const double *dout,
+                         const double *Wup, const double *Wdown, int32_t act,
+                         const double *bup, const double *bdown, const double *dout,
                          int64_t nrows, const int64_t *rows, double *dx_rows)
 {
-    return backward_impl(N, d, E, k, d_ff, C, x, Wg, noise, Wup, Wdown, dout, nrows, rows,
+    const expert_variant v = {act, bup, bdown, NULL, NULL};
+    return backward_impl(N, d, E, k, d_ff, C, x, Wg, noise, Wup, Wdown, &v, dout, nrows, rows,
                          dx_rows, NULL, NULL, NULL);
 }
 
@@ -353,15 +407,17 @@ int oracle_backward_rows(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_f
  * row f of dW_up[e] (dWup_rows [nf, d]) and column f of dW_down[e]
  * (dWdown_cols [nf, d], entry o = dW_down[e][o][f]), with the same terms and
  * token order as oracle_backward. Wup_e [d_ff, d] and Wdown_e [d, d_ff] are
- * expert e's matrices; the routing covers all N tokens. Per token routed to
- * e and kept: g = its gate, dy = g dout_t, z_f = W_up[e][f] x_t,
- * dW_down[e][:, f] += dy relu(z_f), dz_f = [z_f > 0] <W_down[e][:, f], dy>,
- * dW_up[e][f] += dz_f x_t. Returns 0, or -1 if an allocation fails. */
+ * expert e's matrices, bup_e [d_ff] its up bias or NULL; the routing covers
+ * all N tokens. Per token routed to e and kept: g = its gate, dy = g dout_t,
+ * z_f = W_up[e][f] x_t + b_up[e][f], dW_down[e][:, f] += dy act(z_f),
+ * dz_f = act'(z_f) <W_down[e][:, f], dy>, dW_up[e][f] += dz_f x_t. Returns
+ * 0, or -1 if an allocation fails. */
 int oracle_backward_expert_units(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff,
                                  int64_t C, const double *x, const double *Wg,
                                  const double *noise, int64_t e, const double *Wup_e,
-                                 const double *Wdown_e, const double *dout, int64_t nf,
-                                 const int64_t *fs, double *dWup_rows, double *dWdown_cols)
+                                 const double *Wdown_e, int32_t act, const double *bup_e,
+                                 const double *dout, int64_t nf, const int64_t *fs,
+                                 double *dWup_rows, double *dWdown_cols)
 {
     float *scores = (float *)malloc(sizeof(float) * (size_t)(N * E + 1));
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N * k + 1));
@@ -391,14 +447,16 @@ int oracle_backward_expert_units(int64_t N, int64_t d, int64_t E, int32_t k, int
                 double z = 0.0;
                 for (int64_t i = 0; i < d; ++i)
                     z += Wup_e[f * d + i] * xt[i];
-                const double h = z > 0.0 ? z : 0.0;
+                if (bup_e)
+                    z += bup_e[f];
+                const double h = act_of(act, z);
                 double dh = 0.0;
                 for (int64_t o = 0; o < d; ++o) {
                     const double dyo = g * go[o];
                     dWdown_cols[q * d + o] += dyo * h;
                     dh += Wdown_e[o * d_ff + f] * dyo;
                 }
-                const double dz = z > 0.0 ? dh : 0.0;
+                const double dz = dh * act_grad(act, z);
                 for (int64_t i = 0; i < d; ++i)
                     dWup_rows[q * d + i] += dz * xt[i];
             }

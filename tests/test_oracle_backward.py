@@ -16,7 +16,7 @@ def _arrays(wl):
     return wl.x64(), wl.wg64(), wl.noise64(), wu, wd
 
 
-def _forward(x, wg, noise, wu, wd, k, cf):
+def _forward(x, wg, noise, wu, wd, k, cf, act="relu", bu=None, bd=None):
     """out [N, d] and the routing, from the oracle's forward pieces."""
     N, d = x.shape
     E = wg.shape[0]
@@ -27,7 +27,9 @@ def _forward(x, wg, noise, wu, wd, k, cf):
     for e in range(E):
         r, j = np.nonzero((idx == e) & (slot >= 0))
         if len(r):
-            y[r, j] = oracle.expert_rows(x, r, wu[e], wd[e])
+            y[r, j] = oracle.expert_rows(x, r, wu[e], wd[e], act,
+                                         None if bu is None else bu[e],
+                                         None if bd is None else bd[e])
     return oracle.combine(gate, slot, y), idx, slot
 
 
@@ -79,6 +81,41 @@ def test_backward_matches_finite_differences(cf, seed):
     # that this rounding is ~1e-4 of the difference, and a tolerance to match
     _fd_check("W_g", wg, every(wg), loss, dwg, 3e-3, 3e-3, 2e-5, (idx, slot), 25)
     _fd_check("x", x, every(x), loss, dx, 3e-3, 3e-3, 2e-5, (idx, slot), 45)
+
+
+@pytest.mark.parametrize("cf,seed", [(5.0, 71), (0.6, 72)])
+def test_gelu_bias_backward_matches_finite_differences(cf, seed):
+    """The slides' expert variant (exact GELU, biases on both products):
+    every gradient, the bias gradients included, against central
+    differences of sum(dout * out)."""
+    wl = W.custom("bwg", N=9, d=6, E=5, k=2, d_ff=7, dtype="f32", cf=cf, sigma=0.5,
+                  seed=seed, w_std=0.5, wg_std=0.8, act="gelu", bias_std=0.5)
+    x, wg, noise, wu, wd = _arrays(wl)
+    bu = wl.b_up().astype(np.float64)
+    bd = wl.b_down().astype(np.float64)
+    rng = np.random.default_rng(seed)
+    dout = rng.standard_normal((wl.N, wl.d))
+    dx, dwg, dwu, dwd, dbu, dbd = oracle.backward(x, wg, noise, wu, wd, wl.k, cf, dout,
+                                                  act="gelu", bup64=bu, bdown64=bd)
+    out, idx, slot = _forward(x, wg, noise, wu, wd, wl.k, cf, "gelu", bu, bd)
+    if cf < 1:
+        assert (slot < 0).any()
+
+    def loss():
+        o, i, s = _forward(x, wg, noise, wu, wd, wl.k, cf, "gelu", bu, bd)
+        return float((dout * o).sum()), (i, s)
+
+    every = lambda a: list(np.ndindex(a.shape))
+    _fd_check("W_up", wu, every(wu), loss, dwu, 1e-6, 1e-6, 1e-9, (idx, slot), 200)
+    _fd_check("W_down", wd, every(wd), loss, dwd, 1e-6, 1e-6, 1e-9, (idx, slot), 200)
+    _fd_check("b_up", bu, every(bu), loss, dbu, 1e-6, 1e-6, 1e-9, (idx, slot), 30)
+    _fd_check("b_down", bd, every(bd), loss, dbd, 1e-6, 1e-6, 1e-9, (idx, slot), 25)
+    _fd_check("W_g", wg, every(wg), loss, dwg, 3e-3, 3e-3, 2e-5, (idx, slot), 15)
+    _fd_check("x", x, every(x), loss, dx, 3e-3, 3e-3, 2e-5, (idx, slot), 45)
+    # experts that kept nothing get no bias gradient
+    used = np.bincount(idx[slot >= 0], minlength=wl.E)
+    for e in np.nonzero(used == 0)[0]:
+        assert not dbu[e].any() and not dbd[e].any()
 
 
 def test_single_expert_is_a_dense_mlp_backward():

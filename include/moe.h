@@ -257,7 +257,8 @@ int moe_combine(int64_t N, int64_t d, int k, const moe_tensor *Y, const float *t
 
 /* Backward pass of the layer (the row after the forward: gradients through
  * the gates to the router and through the experts), for bf16 layers with
- * ReLU experts and no biases; dropout is not applied. For a loss whose
+ * ReLU experts and no biases (moe_backward_ex: the GELU / bias variants);
+ * dropout is not applied. For a loss whose
  * gradient with respect to out is dout, by the chain rule of moe_forward:
  *   combine: dy = g * dout, dg = <dout, y> (kept choices; dropped: 0);
  *   masked softmax over the kept scores: ds_j = g_j (dg_j - sum_l g_l dg_l),
@@ -282,6 +283,23 @@ int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *n
                  const moe_tensor *W_up, const moe_tensor *W_down, int k, float capacity_factor,
                  const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g, moe_tensor *dW_up,
                  moe_tensor *dW_down, moe_stats *stats);
+
+/* moe_backward for the expert variants of moe_forward_ex (page 2, slide
+ * 32): opts as there (NULL: ReLU, no biases). With GELU, dZ = dH gelu'(z),
+ * gelu'(z) = Phi(z) + z phi(z), on the bf16 pre-activations z the recomputed
+ * up product keeps. Bias gradients, fp32, written exactly when the layer has
+ * that bias (else they must be NULL: MOE_ERR_ARG; a missing one:
+ * MOE_ERR_NULL), each the sum over the expert's kept assignments in a fixed
+ * order:
+ *   db_up   [E, d_ff]   sum of the dZ rows
+ *   db_down [E, d]      sum of the dY rows (g * dout)
+ * Same workspace as moe_backward. */
+int moe_backward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                    const moe_tensor *W_up, const moe_tensor *W_down,
+                    const moe_expert_opts *opts, int k, float capacity_factor,
+                    const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g, moe_tensor *dW_up,
+                    moe_tensor *dW_down, moe_tensor *db_up, moe_tensor *db_down,
+                    moe_stats *stats);
 
 /* Bytes of workspace moe_backward needs (0 on invalid sizes or a dtype
  * other than MOE_BF16). */

@@ -24,7 +24,7 @@ EXPORTS = ("moe_forward", "moe_workspace_size", "moe_capacity", "moe_error_strin
            "moe_router", "moe_router_workspace_size", "moe_dispatch", "moe_experts",
            "moe_expert_up", "moe_expert_down", "moe_expert_workspace_size", "moe_combine",
            "moe_forward_ex", "moe_experts_ex", "moe_expert_up_ex", "moe_expert_down_ex",
-           "moe_backward", "moe_backward_workspace_size")
+           "moe_backward", "moe_backward_ex", "moe_backward_workspace_size")
 
 MOE_ACT_RELU, MOE_ACT_GELU = 0, 1
 ACTS = {"relu": MOE_ACT_RELU, "gelu": MOE_ACT_GELU}
@@ -87,6 +87,10 @@ def lib():
         L.moe_backward.argtypes = [_T, _T, _T, _T, _T, ctypes.c_int, ctypes.c_float, _T, _T, _T,
                                    _T, _T, ctypes.POINTER(MoeStats)]
         L.moe_backward.restype = ctypes.c_int
+        L.moe_backward_ex.argtypes = [_T, _T, _T, _T, _T, ctypes.POINTER(MoeExpertOpts),
+                                      ctypes.c_int, ctypes.c_float, _T, _T, _T, _T, _T, _T, _T,
+                                      ctypes.POINTER(MoeStats)]
+        L.moe_backward_ex.restype = ctypes.c_int
         L.moe_backward_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int,
                                                   ctypes.c_float, ctypes.c_int32]
         L.moe_backward_workspace_size.restype = ctypes.c_size_t
@@ -248,9 +252,12 @@ def backward_workspace_size(N: int, d: int, E: int, d_ff: int, k: int, capacity_
 
 
 def backward(x, W_g, noise, W_up, W_down, k: int, capacity_factor: float, dout,
-             workspace=None, stream=None, export: bool = False):
-    """Run ``moe_backward``: returns (dx [N, d], dW_g [E, d], dW_up [E, d_ff, d],
-    dW_down [E, d, d_ff]), all fp32. With ``export=True`` returns
+             workspace=None, stream=None, export: bool = False, act: str = "relu",
+             b_up: Optional[torch.Tensor] = None, b_down: Optional[torch.Tensor] = None):
+    """Run ``moe_backward`` (``moe_backward_ex`` for GELU or biases): returns
+    (dx [N, d], dW_g [E, d], dW_up [E, d_ff, d], dW_down [E, d, d_ff]), all
+    fp32, followed by db_up [E, d_ff] and db_down [E, d] (None where the layer
+    has no such bias) when the layer has a bias. With ``export=True`` returns
     ``(grads, Stats)`` with the recomputed routing, as ``forward`` does."""
     N, d = x.numel() // x.shape[-1], x.shape[-1]
     E, d_ff = W_up.shape[0], W_up.shape[1]
@@ -259,6 +266,8 @@ def backward(x, W_g, noise, W_up, W_down, k: int, capacity_factor: float, dout,
     dwg = torch.empty((E, d), dtype=torch.float32, device=dev)
     dwu = torch.empty((E, d_ff, d), dtype=torch.float32, device=dev)
     dwd = torch.empty((E, d, d_ff), dtype=torch.float32, device=dev)
+    dbu = None if b_up is None else torch.empty((E, d_ff), dtype=torch.float32, device=dev)
+    dbd = None if b_down is None else torch.empty((E, d), dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = alloc_workspace(
             backward_workspace_size(N, d, E, d_ff, k, capacity_factor, x.dtype), dev)
@@ -270,11 +279,19 @@ def backward(x, W_g, noise, W_up, W_down, k: int, capacity_factor: float, dout,
         used = torch.empty((E,), dtype=torch.int32, device=dev)
     st = MoeStats(_stream(stream), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                   _ptr(idx), _ptr(gate), _ptr(slot), _ptr(used), -1)
-    ds = [desc(t) for t in (x, W_g, noise, W_up, W_down, dout, dx, dwg, dwu, dwd)]
-    _check(lib().moe_backward(_ref(ds[0]), _ref(ds[1]), _ref(ds[2]), _ref(ds[3]), _ref(ds[4]), k,
-                              capacity_factor, _ref(ds[5]), _ref(ds[6]), _ref(ds[7]),
-                              _ref(ds[8]), _ref(ds[9]), ctypes.byref(st)), "moe_backward")
+    ds = [desc(t) for t in (x, W_g, noise, W_up, W_down, dout, dx, dwg, dwu, dwd, dbu, dbd)]
+    o = _opts(act, b_up, b_down)
+    r = [_ref(a) for a in ds]
+    if o is None:
+        rc = lib().moe_backward(r[0], r[1], r[2], r[3], r[4], k, capacity_factor, r[5], r[6],
+                                r[7], r[8], r[9], ctypes.byref(st))
+    else:
+        rc = lib().moe_backward_ex(r[0], r[1], r[2], r[3], r[4], o.ref(), k, capacity_factor,
+                                   r[5], r[6], r[7], r[8], r[9], r[10], r[11], ctypes.byref(st))
+    _check(rc, "moe_backward")
     grads = (dx, dwg, dwu, dwd)
+    if b_up is not None or b_down is not None:
+        grads = grads + (dbu, dbd)
     if export:
         return grads, Stats(idx, gate, slot, used, int(st.capacity))
     return grads
@@ -323,31 +340,43 @@ class Forward:
 
 
 class Backward:
-    """A prepared ``moe_backward`` call: the gradient tensors, workspace and
-    descriptors are built once, so repeated calls only cross the C ABI."""
+    """A prepared ``moe_backward`` / ``moe_backward_ex`` call: the gradient
+    tensors, workspace and descriptors are built once, so repeated calls only
+    cross the C ABI."""
 
-    def __init__(self, x, W_g, noise, W_up, W_down, k, capacity_factor, dout, stream=None):
+    def __init__(self, x, W_g, noise, W_up, W_down, k, capacity_factor, dout, stream=None,
+                 act="relu", b_up=None, b_down=None):
         N, d = x.numel() // x.shape[-1], x.shape[-1]
         E, d_ff = W_up.shape[0], W_up.shape[1]
         dev = x.device
-        self.tensors = (x, W_g, noise, W_up, W_down, dout)
+        self.tensors = (x, W_g, noise, W_up, W_down, dout, b_up, b_down)
         self.dx = torch.empty((N, d), dtype=torch.float32, device=dev)
         self.dW_g = torch.empty((E, d), dtype=torch.float32, device=dev)
         self.dW_up = torch.empty((E, d_ff, d), dtype=torch.float32, device=dev)
         self.dW_down = torch.empty((E, d, d_ff), dtype=torch.float32, device=dev)
+        self.db_up = None if b_up is None else torch.empty((E, d_ff), dtype=torch.float32,
+                                                           device=dev)
+        self.db_down = None if b_down is None else torch.empty((E, d), dtype=torch.float32,
+                                                               device=dev)
         self.workspace = alloc_workspace(
             backward_workspace_size(N, d, E, d_ff, k, capacity_factor, x.dtype), dev)
         self.k, self.cf = k, capacity_factor
         self._d = [desc(t) for t in (x, W_g, noise, W_up, W_down, dout, self.dx, self.dW_g,
-                                     self.dW_up, self.dW_down)]
+                                     self.dW_up, self.dW_down, self.db_up, self.db_down)]
         self._args = [_ref(a) for a in self._d]
+        self._opts = _opts(act, b_up, b_down)
         self.stats = MoeStats(_stream(stream), ctypes.c_void_p(self.workspace.data_ptr()),
                               self.workspace.numel(), None, None, None, None, -1)
 
     def __call__(self):
         a = self._args
-        rc = lib().moe_backward(a[0], a[1], a[2], a[3], a[4], self.k, self.cf, a[5], a[6], a[7],
-                                a[8], a[9], ctypes.byref(self.stats))
+        if self._opts is None:
+            rc = lib().moe_backward(a[0], a[1], a[2], a[3], a[4], self.k, self.cf, a[5], a[6],
+                                    a[7], a[8], a[9], ctypes.byref(self.stats))
+        else:
+            rc = lib().moe_backward_ex(a[0], a[1], a[2], a[3], a[4], self._opts.ref(), self.k,
+                                       self.cf, a[5], a[6], a[7], a[8], a[9], a[10], a[11],
+                                       ctypes.byref(self.stats))
         if rc != 0:
             raise MoeError(rc, "moe_backward")
         return self.dx, self.dW_g, self.dW_up, self.dW_down

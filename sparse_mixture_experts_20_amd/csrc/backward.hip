@@ -136,6 +136,30 @@ __global__ __launch_bounds__(256) void chunk_sum_kernel(const float *__restrict_
     out[i] = acc;
 }
 
+// out[i] = sum of the Kp bf16 values of row i of T (one wave per row; lane
+// partial sums over a fixed stride, then a fixed butterfly).
+__global__ __launch_bounds__(256) void row_sums_kernel(const unsigned short *__restrict__ T,
+                                                       int64_t rows, int Kp,
+                                                       float *__restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= rows)
+        return;
+    const unsigned short *row = T + i * Kp;
+    float acc = 0.f;
+    for (int c = lane * 8; c < Kp; c += 512) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(row + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            acc += __uint_as_float(v[q] << 16) + __uint_as_float(v[q] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        acc += __shfl_xor(acc, off);
+    if (lane == 0)
+        out[i] = acc;
+}
+
 // Tiled transpose through LDS: out[b][c][q*Kp + r] = src row R(b, r), column
 // c, for r below the batch's row count, and 0 for the rest of the Kp columns,
 // for each of `copies` copies q. Row map: 0: b*ceff + r (dense batches of
@@ -248,6 +272,16 @@ hipError_t launch_ds_split(const float *ds, const int32_t *idx, int64_t N, int64
         return hipSuccess;
     hipLaunchKernelGGL(ds_split_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ds,
                        idx, (int)N, (int)Tc, (int)S, E, k, static_cast<unsigned short *>(dsT3));
+    return hipGetLastError();
+}
+
+hipError_t launch_row_sums(const void *T, int64_t rows, int64_t Kp, float *out, hipStream_t s) {
+    if (rows == 0)
+        return hipSuccess;
+    if (Kp % 8 != 0)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(row_sums_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                       static_cast<const unsigned short *>(T), rows, (int)Kp, out);
     return hipGetLastError();
 }
 

@@ -73,12 +73,13 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 constexpr size_t kSplitWorkspaceBytes = (size_t)256 * 256 * 256 * sizeof(float);
 size_t split_workspace_bytes();
 // act: kActRelu or kActGelu (up product); b_up [E, d_ff] / b_down [E, d]
-// fp32 biases or NULL.
+// fp32 biases or NULL. Z (bf16 layers): when not NULL, the pre-activations
+// z = W_up x + b_up are stored there too, [E, ceff, d_ff] like H (no split).
 hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t d,
                             int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                             const int32_t *slot_token, const int32_t *tiles, void *H,
                             int64_t rows_per_expert, void *part, size_t part_bytes, int act,
-                            const float *b_up, hipStream_t s);
+                            const float *b_up, hipStream_t s, void *Z = nullptr);
 hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int64_t d,
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, void *Y,
@@ -86,14 +87,15 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
                               const float *b_down, hipStream_t s);
 
 // Backward products over the dispatch plan (bf16 operands, fp32 accumulate):
-// dZ[e, r, :] = (dY[slot_token[e, r]] W_down[e]) where H[e, r, :] > 0, with
-// W_down transposed ([E, d_ff, d]), bf16 into [E, ceff, d_ff];
+// dZ[e, r, :] = (dY[slot_token[e, r]] W_down[e]) * act'(z[e, r, :]), with
+// W_down transposed ([E, d_ff, d]), bf16 into [E, ceff, d_ff]; act_in is H
+// for ReLU (act' = [H > 0]) and the stored pre-activations Z for GELU;
 // out[slot_token[e, r], :] = A[e, r, :] W_t[e]^T (A dense [E, ceff, K], W_t
 // [E, Nout, K]), fp32.
-hipError_t launch_expert_dz(const void *dY, const void *w_down_t, const void *H, int64_t d,
-                            int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
-                            const int32_t *slot_token, const int32_t *tiles, void *dZ,
-                            int64_t rows_per_expert, hipStream_t s);
+hipError_t launch_expert_dz(const void *dY, const void *w_down_t, const void *act_in, int act,
+                            int64_t d, int64_t d_ff, int E, int k, int64_t ceff,
+                            const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
+                            void *dZ, int64_t rows_per_expert, hipStream_t s);
 hipError_t launch_expert_rows_f32(const void *A, const void *w_t, int64_t K, int64_t Nout, int E,
                                   int k, int64_t ceff, const int32_t *used,
                                   const int32_t *slot_token, const int32_t *tiles, float *out,
@@ -114,6 +116,8 @@ hipError_t launch_combine_backward(const void *dout, const void *Y, const float 
 // i, Tc + i, 2*Tc + i (tokens chunked by Tc).
 hipError_t launch_ds_split(const float *ds, const int32_t *idx, int64_t N, int64_t Tc, int64_t S,
                            int E, int k, void *dsT3, hipStream_t s);
+// out[i] = sum over r < Kp (fixed order) of T[i * Kp + r], bf16 T, fp32 out.
+hipError_t launch_row_sums(const void *T, int64_t rows, int64_t Kp, float *out, hipStream_t s);
 // out[i] = sum over s < S (in order) of part[s * n + i].
 hipError_t launch_chunk_sum(const float *part, int64_t S, int64_t n, float *out, hipStream_t s);
 // out[b][c][q*Kp + r] = src row R(b, r), column c (0 past the batch's rows), for

@@ -79,6 +79,21 @@ __device__ __forceinline__ float gelu(float z) {
     return 0.5f * z * (z >= 0.f ? 2.0f - q : q);
 }
 
+// Its derivative Phi(z) + z phi(z): Phi from the same erf approximation,
+// phi(z) = exp(-z^2 / 2) / sqrt(2 pi) from the same exponential.
+__device__ __forceinline__ float gelu_grad(float z) {
+    const float u = fabsf(z) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, u, 1.0f));
+    const float poly =
+        t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
+                         -0.284496736f),
+                 0.254829592f);
+    const float ex = __expf(-u * u);         // exp(-z^2 / 2)
+    const float q = poly * ex;               // 1 - erf(u)
+    const float Phi = 0.5f * (z >= 0.f ? 2.0f - q : q);
+    return fmaf(z * 0.39894228040143268f, ex, Phi);
+}
+
 // Expert activation: ReLU (page 1 STEP 9) or GELU, chosen at compile time so
 // that the ReLU epilogue carries no trace of the other.
 template <bool GELU>
@@ -170,9 +185,11 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // 2: plain product of ceff rows of A into fp32 rows of O32 (no gather, no
 // schedule table, no split), batched over blockIdx.y with element strides
 // bsa, bsb, bsc of A, W and O32;
-// 3: backward of the down product, dZ = (dY W_down) masked by H > 0: A rows
-// are assignment rows of dY gathered by slot_token, W is W_down transposed,
-// bf16 [E, ceff, Nout] into O16; mask = H;
+// 3: backward of the down product through the activation, dZ = (dY W_down)
+// times act'(z): A rows are assignment rows of dY gathered by slot_token, W
+// is W_down transposed, bf16 [E, ceff, Nout] into O16; for ReLU mask = H
+// (act' = [H > 0]), for GELU mask = the stored pre-activations Z, which may
+// be O16 itself (each element is read before the same thread overwrites it);
 // 4: backward of the up product, dX = dZ W_up: A rows dense like MODE 1, W
 // is W_up transposed, fp32 rows scattered to their assignment into O32.
 // part: scratch for the split of the last round (NULL: no split), P: the
@@ -180,6 +197,8 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // act: activation of the up product (kActRelu, kActGelu); bias: [E, Nout]
 // fp32 added to the product before the activation (MODE 0) or to the output
 // row (MODE 1), or NULL. K-range partials take neither (the fix-up does).
+// Z16 (MODE 0, whole tiles only): when not NULL, the bf16 pre-activations
+// (product plus bias) are stored there too, [E, ceff, Nout] like H.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BKT, int S, int MODE>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void expert_gemm_kernel(
@@ -187,8 +206,8 @@ void expert_gemm_kernel(
     int Nout, int E, int k, int ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
     unsigned short *__restrict__ O16, float *__restrict__ O32, float *__restrict__ part,
-    int P, int act, const float *__restrict__ bias, const unsigned short *__restrict__ mask,
-    int64_t bsa, int64_t bsb, int64_t bsc) {
+    int P, int act, const float *__restrict__ bias, const unsigned short *mask,
+    unsigned short *__restrict__ Z16, int64_t bsa, int64_t bsb, int64_t bsc) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int NTHR = NW * 64;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;   // wave tile
@@ -450,6 +469,17 @@ void expert_gemm_kernel(
                                         ((unsigned)f32_to_bf16_bits(hi) << 16);
                             }
                             *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
+                            if (Z16) {
+                                u32x4 pz;
+#pragma unroll
+                                for (int c = 0; c < 4; ++c) {
+                                    const f32x4 &z = c < 2 ? z0 : z1;
+                                    pz[c] = (unsigned)f32_to_bf16_bits(z[(c % 2) * 2]) |
+                                            ((unsigned)f32_to_bf16_bits(z[(c % 2) * 2 + 1])
+                                             << 16);
+                                }
+                                *reinterpret_cast<u32x4 *>(Z16 + srow * Nout + nb + 8 * h) = pz;
+                            }
                         }
                     }
                 };
@@ -480,27 +510,40 @@ void expert_gemm_kernel(
                     }
                 }
             } else if (MODE == 3) {
-                // dZ = dH where H > 0 (ReLU backward), bf16 like H
+                // dZ = dH act'(z), bf16 like H: ReLU passes dH where H > 0;
+                // GELU scales it by gelu'(z) of the stored pre-activation
                 unsigned short *dst = O16 + srow * Nout + nb;
                 const unsigned short *hm = mask + srow * Nout + nb;
+                auto store_dz = [&](auto use_gelu) {
 #pragma unroll
-                for (int h = 0; h < CPL / 8; ++h) {
-                    if (nb + 8 * h + 8 <= Nout) {
-                        const u32x4 hb = *reinterpret_cast<const u32x4 *>(hm + 8 * h);
-                        u32x4 pk;
+                    for (int h = 0; h < CPL / 8; ++h) {
+                        if (nb + 8 * h + 8 <= Nout) {
+                            const u32x4 hb = *reinterpret_cast<const u32x4 *>(hm + 8 * h);
+                            u32x4 pk;
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const f32x4 &z = c < 2 ? v[2 * h] : v[2 * h + 1];
-                            const unsigned hl = hb[c] & 0xffffu, hh = hb[c] >> 16;
-                            // a bf16 value > 0: sign clear and not zero
-                            const float lo = (hl - 1u) < 0x7fffu ? z[(c % 2) * 2] : 0.f;
-                            const float hi = (hh - 1u) < 0x7fffu ? z[(c % 2) * 2 + 1] : 0.f;
-                            pk[c] = (unsigned)f32_to_bf16_bits(lo) |
-                                    ((unsigned)f32_to_bf16_bits(hi) << 16);
+                            for (int c = 0; c < 4; ++c) {
+                                const f32x4 &z = c < 2 ? v[2 * h] : v[2 * h + 1];
+                                const unsigned hl = hb[c] & 0xffffu, hh = hb[c] >> 16;
+                                float lo, hi;
+                                if constexpr (decltype(use_gelu)::value) {
+                                    lo = z[(c % 2) * 2] * gelu_grad(bf16_bits_to_f32(hl));
+                                    hi = z[(c % 2) * 2 + 1] * gelu_grad(bf16_bits_to_f32(hh));
+                                } else {
+                                    // a bf16 value > 0: sign clear and not zero
+                                    lo = (hl - 1u) < 0x7fffu ? z[(c % 2) * 2] : 0.f;
+                                    hi = (hh - 1u) < 0x7fffu ? z[(c % 2) * 2 + 1] : 0.f;
+                                }
+                                pk[c] = (unsigned)f32_to_bf16_bits(lo) |
+                                        ((unsigned)f32_to_bf16_bits(hi) << 16);
+                            }
+                            *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
                         }
-                        *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
                     }
-                }
+                };
+                if (act == kActGelu)
+                    store_dz(std::true_type{});
+                else
+                    store_dz(std::false_type{});
             } else {
                 const int64_t orow = MODE == 4 ? (int64_t)slot_token[srow] : (int64_t)r;
                 float *dst = O32 + orow * Nout + nb;
@@ -680,7 +723,7 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
                         const int32_t *slot_token, const int32_t *mt, unsigned short *O16,
                         float *part, size_t part_bytes, int act, const float *bias,
                         hipStream_t s, const unsigned short *mask = nullptr,
-                        float *O32 = nullptr) {
+                        float *O32 = nullptr, unsigned short *Z16 = nullptr) {
     auto kern = expert_gemm_kernel<BM, BN, WM, WN, kBK, 2, MODE>;
     constexpr int NTHR = WM * WN * 64;
     static int resident[kMaxDevices];   // per device, filled on first use (0 = unset)
@@ -700,13 +743,13 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
     const int64_t tmax = (int64_t)E * ((ceff + BM - 1) / BM) * ((Nout + BN - 1) / BN);
     // a split needs at least two ranges of kSplitMinSteps, at least one full
     // round of tiles and (by the 15% rule of split_plan) fewer than six
-    const bool split = (MODE == 0 || MODE == 1) && P > 0 && KT >= 2 * kSplitMinSteps &&
+    const bool split = (MODE == 0 || MODE == 1) && !Z16 && P > 0 && KT >= 2 * kSplitMinSteps &&
                        tmax >= P && tmax < 6 * (int64_t)P;
     const int64_t grid = (tmax + kXcds - 1) / kXcds * kXcds +
                          (split ? (int64_t)(P + kXcds - 1) / kXcds * kXcds : 0);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHR), 0, s, A, W, (int)K, (int)Nout, E,
                        k, (int)ceff, used, slot_token, mt, O16, O32, split ? part : nullptr,
-                       split ? P : 0, act, bias, mask, (int64_t)0, (int64_t)0, (int64_t)0);
+                       split ? P : 0, act, bias, mask, Z16, (int64_t)0, (int64_t)0, (int64_t)0);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !split)
         return err;
@@ -723,18 +766,18 @@ hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W,
                        const int32_t *slot_token, const int32_t *tiles, unsigned short *O16,
                        void *part, size_t part_bytes, int act, const float *bias,
                        hipStream_t s, const unsigned short *mask = nullptr,
-                       float *O32 = nullptr) {
+                       float *O32 = nullptr, unsigned short *Z16 = nullptr) {
     float *pf = static_cast<float *>(part);
     if (t == Tile::k256)
         return launch_tiles<256, 256, 2, 4, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
                                                   tiles + E + 1, O16, pf, part_bytes, act, bias,
-                                                  s, mask, O32);
+                                                  s, mask, O32, Z16);
     if (t == Tile::k128x64)
         return launch_tiles<128, 64, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
                                                  tiles, O16, pf, part_bytes, act, bias, s, mask,
-                                                 O32);
+                                                 O32, Z16);
     return launch_tiles<128, 128, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token, tiles,
-                                              O16, pf, part_bytes, act, bias, s, mask, O32);
+                                              O16, pf, part_bytes, act, bias, s, mask, O32, Z16);
 }
 
 }  // namespace
@@ -752,7 +795,7 @@ hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, in
                        (const int32_t *)nullptr, (const int32_t *)nullptr,
                        (const int32_t *)nullptr, (unsigned short *)nullptr, Y, (float *)nullptr,
                        0, kActRelu, (const float *)nullptr, (const unsigned short *)nullptr,
-                       (int64_t)0, (int64_t)0, (int64_t)0);
+                       (unsigned short *)nullptr, (int64_t)0, (int64_t)0, (int64_t)0);
     return hipGetLastError();
 }
 
@@ -760,15 +803,18 @@ hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t 
                             int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                             const int32_t *slot_token, const int32_t *tiles, void *H,
                             int64_t rows_per_expert, void *part, size_t part_bytes, int act,
-                            const float *b_up, hipStream_t s) {
+                            const float *b_up, hipStream_t s, void *Z) {
     if (ceff == 0)
         return hipSuccess;
     if (bf16)
         return launch_gemm<0>(pick_tile(rows_per_expert, d_ff, E),
                               static_cast<const unsigned short *>(x),
                               static_cast<const unsigned short *>(w_up), d, d_ff, E, k, ceff,
-                              used, slot_token, tiles, static_cast<unsigned short *>(H), part,
-                              part_bytes, act, b_up, s);
+                              used, slot_token, tiles, static_cast<unsigned short *>(H),
+                              Z ? nullptr : part, part_bytes, act, b_up, s, nullptr, nullptr,
+                              static_cast<unsigned short *>(Z));
+    if (Z)
+        return hipErrorInvalidValue;   // pre-activations are kept for bf16 layers only
     hipLaunchKernelGGL(experts_f32_kernel<0>,
                        dim3((unsigned)((d_ff + 63) / 64), (unsigned)((ceff + 63) / 64), E),
                        dim3(256), 0, s, static_cast<const float *>(x),
@@ -800,17 +846,17 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
 
 // ---- backward-pass products (bf16 operands, fp32 accumulation) ----------
 
-hipError_t launch_expert_dz(const void *dY, const void *w_down_t, const void *H, int64_t d,
-                            int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
-                            const int32_t *slot_token, const int32_t *tiles, void *dZ,
-                            int64_t rows_per_expert, hipStream_t s) {
+hipError_t launch_expert_dz(const void *dY, const void *w_down_t, const void *act_in, int act,
+                            int64_t d, int64_t d_ff, int E, int k, int64_t ceff,
+                            const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
+                            void *dZ, int64_t rows_per_expert, hipStream_t s) {
     if (ceff == 0)
         return hipSuccess;
     return launch_gemm<3>(pick_tile(rows_per_expert, d_ff, E),
                           static_cast<const unsigned short *>(dY),
                           static_cast<const unsigned short *>(w_down_t), d, d_ff, E, k, ceff,
                           used, slot_token, tiles, static_cast<unsigned short *>(dZ), nullptr, 0,
-                          kActRelu, nullptr, s, static_cast<const unsigned short *>(H));
+                          act, nullptr, s, static_cast<const unsigned short *>(act_in));
 }
 
 hipError_t launch_expert_rows_f32(const void *A, const void *w_t, int64_t K, int64_t Nout, int E,
@@ -843,7 +889,8 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
                            (int)Nout, 1, 1, (int)M, (const int32_t *)nullptr,
                            (const int32_t *)nullptr, (const int32_t *)nullptr,
                            (unsigned short *)nullptr, C, (float *)nullptr, 0, kActRelu,
-                           (const float *)nullptr, (const unsigned short *)nullptr, sa, sb, sc);
+                           (const float *)nullptr, (const unsigned short *)nullptr,
+                           (unsigned short *)nullptr, sa, sb, sc);
         return hipGetLastError();
     }
     const int64_t grid = (((M + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) / kXcds * kXcds;
@@ -852,7 +899,8 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
                        (int)Nout, 1, 1, (int)M, (const int32_t *)nullptr,
                        (const int32_t *)nullptr, (const int32_t *)nullptr,
                        (unsigned short *)nullptr, C, (float *)nullptr, 0, kActRelu,
-                       (const float *)nullptr, (const unsigned short *)nullptr, sa, sb, sc);
+                       (const float *)nullptr, (const unsigned short *)nullptr,
+                           (unsigned short *)nullptr, sa, sb, sc);
     return hipGetLastError();
 }
 

@@ -663,10 +663,12 @@ size_t moe_backward_workspace_size(int64_t N, int64_t d, int64_t E, int64_t d_ff
     return bwd_layout_of(m).total;
 }
 
-int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
-                 const moe_tensor *W_up, const moe_tensor *W_down, int k, float capacity_factor,
-                 const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g, moe_tensor *dW_up,
-                 moe_tensor *dW_down, moe_stats *stats) {
+int moe_backward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                    const moe_tensor *W_up, const moe_tensor *W_down,
+                    const moe_expert_opts *opts, int k, float capacity_factor,
+                    const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g, moe_tensor *dW_up,
+                    moe_tensor *dW_down, moe_tensor *db_up, moe_tensor *db_down,
+                    moe_stats *stats) {
     if (!stats || !W_up || !W_down || !dout)
         return MOE_ERR_NULL;
     int64_t N, d, E;
@@ -703,6 +705,26 @@ int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *n
             (rc = check_grad(dW_down, 3, e_dn)) != MOE_OK)
             return rc;
     }
+    ExpertOpts o;
+    rc = check_opts(opts, E, d, d_ff, o);
+    if (rc != MOE_OK)
+        return rc;
+    // a bias gradient exactly when the layer has that bias
+    if ((o.b_up && !db_up) || (o.b_down && !db_down))
+        return MOE_ERR_NULL;
+    if ((!o.b_up && db_up) || (!o.b_down && db_down))
+        return MOE_ERR_ARG;
+    {
+        const int64_t e_bu[2] = {E, d_ff}, e_bd[2] = {E, d};
+        if (db_up && (rc = check_grad(db_up, 2, e_bu)) != MOE_OK)
+            return rc;
+        if (db_down && (rc = check_grad(db_down, 2, e_bd)) != MOE_OK)
+            return rc;
+        if ((db_up && !db_up->data) || (db_down && !db_down->data))
+            return MOE_ERR_NULL;
+        if ((db_up && !aligned(db_up->data, 16)) || (db_down && !aligned(db_down->data, 16)))
+            return MOE_ERR_ALIGN;
+    }
     Dims m{N, d, E, d_ff, k, 0, 0, x->dtype};
     m.C = capacity_of(N, E, k, capacity_factor);
     m.ceff = m.C < N ? m.C : N;
@@ -722,6 +744,10 @@ int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *n
         MOE_TRY(moe::launch_fill_i32(static_cast<int32_t *>(dW_g->data), E * d, 0, s));
         MOE_TRY(moe::launch_fill_i32(static_cast<int32_t *>(dW_up->data), E * d_ff * d, 0, s));
         MOE_TRY(moe::launch_fill_i32(static_cast<int32_t *>(dW_down->data), E * d * d_ff, 0, s));
+        if (db_up)
+            MOE_TRY(moe::launch_fill_i32(static_cast<int32_t *>(db_up->data), E * d_ff, 0, s));
+        if (db_down)
+            MOE_TRY(moe::launch_fill_i32(static_cast<int32_t *>(db_down->data), E * d, 0, s));
         if (stats->used_capacity)
             return hip_status(moe::launch_fill_i32(stats->used_capacity, E, 0, s));
         return MOE_OK;
@@ -762,10 +788,14 @@ int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *n
     if (rc != MOE_OK)
         return rc;
     MOE_TRY(moe::launch_dispatch(idx, N, Ei, k, ceff, slot, used, st, tiles, s));
+    // (GELU: the pre-activations go to the dZ buffer, which the dZ product
+    // then overwrites element by element)
+    const bool gelu = o.act == moe::kActGelu;
     MOE_TRY(moe::launch_expert_up(true, x->data, W_up->data, d, d_ff, Ei, k, ceff, used, st,
-                                  tiles, H, rpe, nullptr, 0, moe::kActRelu, nullptr, s));
+                                  tiles, H, rpe, nullptr, 0, o.act, o.b_up, s,
+                                  gelu ? dZ : nullptr));
     MOE_TRY(moe::launch_expert_down(true, H, W_down->data, d, d_ff, Ei, k, ceff, used, st, tiles,
-                                    Y, rpe, nullptr, 0, nullptr, s));
+                                    Y, rpe, nullptr, 0, o.b_down, s));
     // combine and softmax backward; router weights: dW_g = ds^T x, per token
     // chunk on the exact split of ds, then the chunks summed in order
     MOE_TRY(moe::launch_combine_backward(dout->data, Y, gate, slot, N, d, k, dY, ds, s));
@@ -778,7 +808,8 @@ int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *n
     // experts, input side: dZ = (dY W_down) [H > 0]; dX = dZ W_up; dx
     MOE_TRY(moe::launch_transpose_rows(W_down->data, d_ff, d, nullptr, E * d, nullptr, k, 0, d, 1,
                                        Ei, WT, s));
-    MOE_TRY(moe::launch_expert_dz(dY, WT, H, d, d_ff, Ei, k, ceff, used, st, tiles, dZ, rpe, s));
+    MOE_TRY(moe::launch_expert_dz(dY, WT, gelu ? dZ : H, o.act, d, d_ff, Ei, k, ceff, used, st,
+                                  tiles, dZ, rpe, s));
     MOE_TRY(moe::launch_transpose_rows(W_up->data, d, d_ff, nullptr, E * d_ff, nullptr, k, 0,
                                        d_ff, 1, Ei, WT, s));
     MOE_TRY(moe::launch_expert_rows_f32(dZ, WT, d_ff, d, Ei, k, ceff, used, st, tiles, dXa, rpe,
@@ -786,15 +817,28 @@ int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *n
     MOE_TRY(moe::launch_dx(dXa, ds, idx, slot, static_cast<const float *>(W_g->data), N, d, k,
                            static_cast<float *>(dx->data), s));
     // experts, weight side: dW_down = dY^T H, dW_up = dZ^T X (K = kept rows)
+    // (bias gradients: the row sums of the transposed dY and dZ)
     MOE_TRY(moe::launch_transpose_rows(dY, d, ceff, used, 0, st, k, 1, Kp, 1, Ei, T1, s));
+    if (db_down)
+        MOE_TRY(moe::launch_row_sums(T1, E * d, Kp, static_cast<float *>(db_down->data), s));
     MOE_TRY(moe::launch_transpose_rows(H, d_ff, ceff, used, 0, st, k, 0, Kp, 1, Ei, T2, s));
     MOE_TRY(moe::launch_batched_gemm_bf16(T1, T2, d, Kp, d_ff, Ei, d * Kp, d_ff * Kp, d * d_ff,
                                           static_cast<float *>(dW_down->data), s));
     MOE_TRY(moe::launch_transpose_rows(x->data, d, ceff, used, 0, st, k, 2, Kp, 1, Ei, T1, s));
     MOE_TRY(moe::launch_transpose_rows(dZ, d_ff, ceff, used, 0, st, k, 0, Kp, 1, Ei, T2, s));
+    if (db_up)
+        MOE_TRY(moe::launch_row_sums(T2, E * d_ff, Kp, static_cast<float *>(db_up->data), s));
     MOE_TRY(moe::launch_batched_gemm_bf16(T2, T1, d_ff, Kp, d, Ei, d_ff * Kp, d * Kp, d_ff * d,
                                           static_cast<float *>(dW_up->data), s));
     return MOE_OK;
+}
+
+int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                 const moe_tensor *W_up, const moe_tensor *W_down, int k, float capacity_factor,
+                 const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g, moe_tensor *dW_up,
+                 moe_tensor *dW_down, moe_stats *stats) {
+    return moe_backward_ex(x, W_g, noise, W_up, W_down, nullptr, k, capacity_factor, dout, dx,
+                           dW_g, dW_up, dW_down, nullptr, nullptr, stats);
 }
 
 }  // extern "C"

@@ -280,3 +280,39 @@ def test_backward_rejects_bad_arguments(L):
     st2 = B.MoeStats(None, ctypes.c_void_p(FAKE + 4), 1 << 40, None, None, None, None, -1)
     assert bwd(st=st2) == -7                                         # misaligned workspace
     assert st.capacity == -1
+
+
+def test_backward_ex_validates_the_expert_variant(L):
+    """moe_backward_ex: options as for the forward, and a bias gradient
+    exactly when the layer has that bias."""
+    N, d, E, dff = 64, 16, 4, 32
+    x, wg, wu, wd, out, st = _good(N=N, d=d, E=E, dff=dff)
+    dout = _t(FAKE, BF16, N, d)
+    r = ctypes.byref
+    g = (_t(FAKE, F32, N, d), _t(FAKE, F32, E, d), _t(FAKE, F32, E, dff, d),
+         _t(FAKE, F32, E, d, dff))
+
+    def opts(act=B.MOE_ACT_GELU, bu=None, bd=None):
+        o = B.MoeExpertOpts(act, None if bu is None else ctypes.addressof(bu),
+                            None if bd is None else ctypes.addressof(bd))
+        o._keep = (bu, bd)
+        return o
+
+    def bwd(o, dbu=None, dbd=None):
+        return L.moe_backward_ex(r(x), r(wg), None, r(wu), r(wd), r(o) if o else None, 2, 1.0,
+                                 r(dout), r(g[0]), r(g[1]), r(g[2]), r(g[3]),
+                                 r(dbu) if dbu else None, r(dbd) if dbd else None, r(st))
+
+    bu, bd = _t(FAKE, F32, E, dff), _t(FAKE, F32, E, d)
+    assert bwd(opts(act=9)) == -4                                       # unknown activation
+    assert bwd(opts(bu=bu)) == -1                                       # db_up missing
+    assert bwd(opts(bd=bd), dbu=_t(FAKE, F32, E, dff), dbd=_t(FAKE, F32, E, d)) == -4  # extra
+    assert bwd(None, dbd=_t(FAKE, F32, E, d)) == -4                     # no bias, gradient given
+    assert bwd(opts(bu=bu), dbu=_t(FAKE, F32, E, dff + 8)) == -2        # db_up [E, d_ff]
+    assert bwd(opts(bd=bd), dbd=_t(FAKE, BF16, E, d)) == -3             # fp32
+    assert bwd(opts(bd=bd), dbd=_t(FAKE + 4, F32, E, d)) == -7          # aligned
+    # valid calls reach the workspace check (1 byte here)
+    assert bwd(opts(bu=bu, bd=bd), dbu=_t(FAKE, F32, E, dff), dbd=_t(FAKE, F32, E, d)) == -5
+    assert bwd(opts()) == -5
+    assert bwd(None) == -5
+    assert st.capacity == -1

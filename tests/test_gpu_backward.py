@@ -56,7 +56,8 @@ def _host(wl):
 def _run(dev, k, cf, stats=False):
     from sparse_mixture_experts_20_amd import binding as B
     return B.backward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], k, cf,
-                      dev["dout"], export=stats)
+                      dev["dout"], export=stats, act=dev["act"], b_up=dev["b_up"],
+                      b_down=dev["b_down"])
 
 
 def _close(name, got, ref):
@@ -119,6 +120,42 @@ def test_small_backward_matches_oracle(torch_mod, name):
     del dev
 
 
+# the slides' expert variants: name -> (N, d, E, k, d_ff, cf, sigma, seed, act, bias_std)
+VARIANTS = {
+    "bwd_gelu_bias": (700, 200, 6, 2, 328, 0.9, 0.4, 311, "gelu", 0.05),
+    "bwd_gelu_nobias": (333, 136, 5, 2, 200, 1.0, 0.3, 312, "gelu", 0.0),
+    "bwd_relu_bias": (1000, 264, 16, 4, 392, 0.8, 0.5, 313, "relu", 0.05),
+    "bwd_gelu_bias_drop": (512, 64, 4, 2, 128, 0.3, 0.0, 314, "gelu", 0.1),
+}
+
+
+@pytest.mark.parametrize("name", list(VARIANTS))
+def test_variant_backward_matches_oracle(torch_mod, name):
+    """GELU and/or biases: every gradient, the bias gradients included."""
+    torch = torch_mod
+    N, d, E, k, d_ff, cf, sg, seed, act, bstd = VARIANTS[name]
+    wl = W.custom(name, N=N, d=d, E=E, k=k, d_ff=d_ff, dtype="bf16", cf=cf, sigma=sg,
+                  seed=seed, w_std=0.05, act=act, bias_std=bstd)
+    G.say(f"[backward] {name}: N={N} d={d} E={E} k={k} d_ff={d_ff} cf={cf} act={act} "
+          f"bias_std={bstd}")
+    dev = _upload(wl)
+    grads, st = _run(dev, k, cf, stats=True)
+    torch.cuda.synchronize()
+    x, wg, noise, wu, wd, dout = _host(wl)
+    res = oracle.forward(wl, rows=[0])
+    G.check_routing(res, st)
+    bu, bd = wl.b_up(), wl.b_down()
+    ref = oracle.backward(x, wg, noise, wu, wd, k, cf, dout, act=act, bup64=bu, bdown64=bd)
+    names = ("dx", "dW_g", "dW_up", "dW_down", "db_up", "db_down")
+    assert len(grads) == len(ref) == (6 if bstd else 4)
+    for nm, got, r in zip(names, grads, ref):
+        _close(nm, G.to_np(got), r)
+    if bstd:
+        for e in np.nonzero(res.used == 0)[0]:
+            assert not G.to_np(grads[4][e]).any() and not G.to_np(grads[5][e]).any()
+    del dev
+
+
 def test_empty_batch_gives_zero_gradients(torch_mod):
     torch = torch_mod
     from sparse_mixture_experts_20_amd import binding as B
@@ -134,29 +171,32 @@ def test_empty_batch_gives_zero_gradients(torch_mod):
     assert not dwg.any() and not dwu.any() and not dwd.any()
 
 
-def test_nanomoe_backward_sampled_rows(torch_mod):
-    """The benchmark's nanoMoE layer: routing for every token, dx on a
-    seeded sample of token rows (tokens that lost a choice included), and
-    bit-identical gradients on a second run."""
+@pytest.mark.parametrize("name", ["nanomoe", "nanomoe_gelu"])
+def test_nanomoe_backward_sampled_rows(torch_mod, name):
+    """The benchmark's nanoMoE layer (and the slides' GELU + bias expert on
+    it): routing for every token, dx on a seeded sample of token rows
+    (tokens that lost a choice included), and bit-identical gradients on a
+    second run."""
     torch = torch_mod
-    wl = W.make("nanomoe")
-    G.say(f"[backward] nanomoe: N={wl.N} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff}")
+    wl = W.make(name)
+    G.say(f"[backward] {name}: N={wl.N} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff}")
     dev = _upload(wl)
-    (dx, dwg, dwu, dwd), st = _run(dev, wl.k, wl.cfg.cf, stats=True)
+    grads, st = _run(dev, wl.k, wl.cfg.cf, stats=True)
     g2 = _run(dev, wl.k, wl.cfg.cf)
     torch.cuda.synchronize()
-    for a, b in zip((dx, dwg, dwu, dwd), g2):
+    for a, b in zip(grads, g2):
         assert torch.equal(a, b)
     route = oracle.forward(wl, rows=[0])
     G.check_routing(route, st)
     rows = G.sample_rows(route, 64, seed=2)
     x, wg, noise, wu, wd, dout = _host(wl)
-    ref = oracle.backward_rows(x, wg, noise, wu, wd, wl.k, wl.cfg.cf, dout, rows)
-    _close("dx[rows]", G.to_np(dx)[rows], ref)
+    ref = oracle.backward_rows(x, wg, noise, wu, wd, wl.k, wl.cfg.cf, dout, rows,
+                               act=wl.cfg.act, bup64=wl.b_up(), bdown64=wl.b_down())
+    _close("dx[rows]", G.to_np(grads[0])[rows], ref)
     del dev
 
 
-@pytest.mark.parametrize("name,nunits", [("nanomoe", 6), ("mixtral", 4)])
+@pytest.mark.parametrize("name,nunits", [("nanomoe", 6), ("mixtral", 4), ("nanomoe_gelu", 6)])
 def test_benchmark_layer_weight_gradients_sampled(torch_mod, name, nunits):
     """The benchmark's layer shapes in the launch configuration the backward
     benchmark times: routing for every token, and for two experts (the most
@@ -166,12 +206,14 @@ def test_benchmark_layer_weight_gradients_sampled(torch_mod, name, nunits):
     wl = W.make(name)
     G.say(f"[backward] {name}: N={wl.N} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff}")
     dev = _upload(wl, keep_host=False)
-    (dx, dwg, dwu, dwd), st = _run(dev, wl.k, wl.cfg.cf, stats=True)
+    grads, st = _run(dev, wl.k, wl.cfg.cf, stats=True)
+    dx, dwg, dwu, dwd = grads[:4]
     torch.cuda.synchronize()
     route = oracle.forward(wl, rows=[0])
     G.check_routing(route, st)
     rng = np.random.default_rng(3)
     x, wg, noise, dout = wl.x64(), wl.wg64(), wl.noise64(), wl.as_f64(wl.dout())
+    bu = wl.b_up()
     top = int(np.argmax(route.used))
     other = int(rng.choice([e for e in range(wl.E) if e != top]))
     for e in (top, other):
@@ -179,7 +221,8 @@ def test_benchmark_layer_weight_gradients_sampled(torch_mod, name, nunits):
         G.say(f"[backward] {name}: expert {e} ({route.used[e]} rows), units {fs.tolist()}")
         up, down = oracle.backward_expert_units(x, wg, noise, e, wl.as_f64(wl.w_up(e)),
                                                 wl.as_f64(wl.w_down(e)), wl.k, wl.cfg.cf, dout,
-                                                fs)
+                                                fs, act=wl.cfg.act,
+                                                bup_e64=None if bu is None else bu[e])
         idx = torch.from_numpy(fs).to("cuda")
         _close(f"dW_up[{e}][f]", G.to_np(dwu[e].index_select(0, idx)), up)
         _close(f"dW_down[{e}][:, f]", G.to_np(dwd[e].index_select(1, idx).t().contiguous()),

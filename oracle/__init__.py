@@ -27,6 +27,9 @@ _dp = ctypes.POINTER(ctypes.c_double)
 _fp = ctypes.POINTER(ctypes.c_float)
 _ip = ctypes.POINTER(ctypes.c_int32)
 _lp = ctypes.POINTER(ctypes.c_int64)
+_u64 = ctypes.c_uint64
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_dbl = ctypes.c_double
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
 
@@ -50,14 +53,22 @@ def lib():
         L.oracle_combine.argtypes = [_i64, _i64, _i32, _dp, _ip, _dp, _dp]
         L.oracle_combine.restype = None
         L.oracle_backward.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _dp, _dp, _dp, _dp, _dp,
-                                      _i32, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+                                      _i32, _dp, _dp, _dbl, _u64, _u64, _dp, _dp, _dp, _dp, _dp,
+                                      _dp, _dp]
         L.oracle_backward.restype = ctypes.c_int
         L.oracle_backward_rows.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _dp, _dp, _dp,
-                                           _dp, _dp, _i32, _dp, _dp, _dp, _i64, _lp, _dp]
+                                           _dp, _dp, _i32, _dp, _dp, _dbl, _u64, _u64, _dp,
+                                           _i64, _lp, _dp]
         L.oracle_backward_rows.restype = ctypes.c_int
         L.oracle_backward_expert_units.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _dp, _dp,
-                                                   _dp, _i64, _dp, _dp, _i32, _dp, _dp, _i64,
-                                                   _lp, _dp, _dp]
+                                                   _dp, _i64, _dp, _dp, _i32, _dp, _dbl, _u64,
+                                                   _u64, _dp, _i64, _lp, _dp, _dp]
+        L.oracle_philox4x64.argtypes = [_u64p, _u64p, _u64p]
+        L.oracle_philox4x64.restype = None
+        L.oracle_dropout_threshold.argtypes = [_dbl]
+        L.oracle_dropout_threshold.restype = ctypes.c_uint32
+        L.oracle_dropout_rows.argtypes = [_i64, _i64, _lp, _dbl, _u64, _u64, _dp]
+        L.oracle_dropout_rows.restype = None
         L.oracle_backward_expert_units.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = ctypes.c_int
@@ -157,6 +168,46 @@ def combine(gate: np.ndarray, slot: np.ndarray, y: np.ndarray) -> np.ndarray:
     return out
 
 
+def _check_dropout(p: float) -> None:
+    if not (0.0 <= p < 1.0):
+        raise ValueError("dropout must be in [0, 1)")
+
+
+def philox4x64(counter: Sequence[int], key: Sequence[int]) -> np.ndarray:
+    """Philox4x64-10 of a 4-word counter under a 2-word key: 4 uint64."""
+    c = np.ascontiguousarray(np.asarray(counter, dtype=np.uint64))
+    kk = np.ascontiguousarray(np.asarray(key, dtype=np.uint64))
+    if c.shape != (4,) or kk.shape != (2,):
+        raise ValueError("counter has 4 words, key 2")
+    out = np.empty(4, dtype=np.uint64)
+    lib().oracle_philox4x64(c.ctypes.data_as(_u64p), kk.ctypes.data_as(_u64p),
+                            out.ctypes.data_as(_u64p))
+    return out
+
+
+def dropout_threshold(p: float) -> int:
+    """floor(p 2^32): an element is kept when its 32-bit word is >= this."""
+    _check_dropout(p)
+    return int(lib().oracle_dropout_threshold(p))
+
+
+def dropout_rows(y64: np.ndarray, arows: Sequence[int], p: float, seed: int,
+                 offset: int = 0) -> np.ndarray:
+    """Training-mode dropout of expert output rows: a copy of y [n, d] where
+    row r (the output of assignment arows[r] = t k + j) keeps element i when
+    its Philox word is at or above floor(p 2^32), scaled by 1 / (1 - p), and
+    is 0 elsewhere."""
+    _check_dropout(p)
+    y = np.array(y64, dtype=np.float64, order="C", copy=True)
+    a = _c(np.asarray(arows, dtype=np.int64), np.int64)
+    if y.ndim != 2 or a.shape != (y.shape[0],):
+        raise ValueError("shapes")
+    if p > 0.0 and y.size:
+        lib().oracle_dropout_rows(y.shape[0], y.shape[1], _ptr(a, _lp), p, seed, offset,
+                                  _ptr(y, _dp))
+    return y
+
+
 def _act_code(act: str) -> int:
     if act not in ("relu", "gelu"):
         raise ValueError("act must be 'relu' or 'gelu'")
@@ -188,12 +239,15 @@ def _bias(b, shape):
 
 
 def backward(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout64,
-             act: str = "relu", bup64=None, bdown64=None):
+             act: str = "relu", bup64=None, bdown64=None, dropout: float = 0.0,
+             seed: int = 0, offset: int = 0):
     """Gradients of the layer for the output gradient dout [N, d]: returns
     (dx [N, d], dW_g [E, d], dW_up [E, d_ff, d], dW_down [E, d, d_ff]), all
     float64, and with biases (bup64 [E, d_ff], bdown64 [E, d]) also
     (db_up [E, d_ff], db_down [E, d]). wups64/wdowns64 are [E, d_ff, d] and
-    [E, d, d_ff] arrays (or lists of per-expert matrices)."""
+    [E, d, d_ff] arrays (or lists of per-expert matrices). dropout, seed,
+    offset: the training-mode dropout on the expert outputs (``dropout_rows``)."""
+    _check_dropout(dropout)
     x64, wg64, n64, wu, wd, dout64, N, d, E, d_ff = _bwd_inputs(x64, wg64, noise64, wups64,
                                                                 wdowns64, dout64)
     bu, bd = _bias(bup64, (E, d_ff)), _bias(bdown64, (E, d))
@@ -207,7 +261,8 @@ def backward(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout64,
     dbd = np.empty((E, d)) if biased else None
     rc = lib().oracle_backward(N, d, E, k, d_ff, C, _ptr(x64, _dp), _ptr(wg64, _dp),
                                _ptr(n64, _dp), _ptr(wu, _dp), _ptr(wd, _dp), _act_code(act),
-                               _ptr(bu, _dp), _ptr(bd, _dp), _ptr(dout64, _dp), _ptr(dx, _dp),
+                               _ptr(bu, _dp), _ptr(bd, _dp), dropout, seed, offset,
+                               _ptr(dout64, _dp), _ptr(dx, _dp),
                                _ptr(dwg, _dp), _ptr(dwu, _dp), _ptr(dwd, _dp), _ptr(dbu, _dp),
                                _ptr(dbd, _dp))
     if rc != 0:
@@ -218,10 +273,12 @@ def backward(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout64,
 
 
 def backward_rows(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout64,
-                  rows: Sequence[int], act: str = "relu", bup64=None, bdown64=None):
+                  rows: Sequence[int], act: str = "relu", bup64=None, bdown64=None,
+                  dropout: float = 0.0, seed: int = 0, offset: int = 0):
     """dx [len(rows), d] (float64) of the listed tokens, as ``backward``
     computes it; the routing covers every token, the expert terms only the
     listed ones (for layers too large for the full backward)."""
+    _check_dropout(dropout)
     x64, wg64, n64, wu, wd, dout64, N, d, E, d_ff = _bwd_inputs(x64, wg64, noise64, wups64,
                                                                 wdowns64, dout64)
     bu, bd = _bias(bup64, (E, d_ff)), _bias(bdown64, (E, d))
@@ -232,18 +289,21 @@ def backward_rows(x64, wg64, noise64, wups64, wdowns64, k: int, cf: float, dout6
     rc = lib().oracle_backward_rows(N, d, E, k, d_ff, capacity(N, E, k, cf), _ptr(x64, _dp),
                                     _ptr(wg64, _dp), _ptr(n64, _dp), _ptr(wu, _dp),
                                     _ptr(wd, _dp), _act_code(act), _ptr(bu, _dp), _ptr(bd, _dp),
-                                    _ptr(dout64, _dp), r.size, _ptr(r, _lp), _ptr(dx, _dp))
+                                    dropout, seed, offset, _ptr(dout64, _dp), r.size,
+                                    _ptr(r, _lp), _ptr(dx, _dp))
     if rc != 0:
         raise MemoryError("oracle_backward_rows: allocation failed")
     return dx
 
 
 def backward_expert_units(x64, wg64, noise64, e: int, wup_e64, wdown_e64, k: int, cf: float,
-                          dout64, units: Sequence[int], act: str = "relu", bup_e64=None):
+                          dout64, units: Sequence[int], act: str = "relu", bup_e64=None,
+                          dropout: float = 0.0, seed: int = 0, offset: int = 0):
     """Sampled weight gradients of expert e, as ``backward`` computes them:
     returns (rows f of dW_up[e] [len(units), d], columns f of dW_down[e]
     [len(units), d]) for the listed hidden units f. Takes only expert e's
     matrices (wup_e64 [d_ff, d], wdown_e64 [d, d_ff]) and up bias [d_ff]."""
+    _check_dropout(dropout)
     x64 = _c(x64, np.float64)
     wg64 = _c(wg64, np.float64)
     wu = _c(wup_e64, np.float64)
@@ -265,7 +325,8 @@ def backward_expert_units(x64, wg64, noise64, e: int, wup_e64, wdown_e64, k: int
     rc = lib().oracle_backward_expert_units(N, d, E, k, d_ff, capacity(N, E, k, cf),
                                             _ptr(x64, _dp), _ptr(wg64, _dp), _ptr(n64, _dp), e,
                                             _ptr(wu, _dp), _ptr(wd, _dp), _act_code(act),
-                                            _ptr(bu, _dp), _ptr(dout64, _dp), f.size,
+                                            _ptr(bu, _dp), dropout, seed, offset,
+                                            _ptr(dout64, _dp), f.size,
                                             _ptr(f, _lp), _ptr(up, _dp), _ptr(down, _dp))
     if rc != 0:
         raise MemoryError("oracle_backward_expert_units: allocation failed")
@@ -309,6 +370,12 @@ def forward(wl, rows: Optional[Sequence[int]] = None, want_y: bool = False) -> R
                          None if bup is None else bup[int(e)].astype(np.float64),
                          None if bdown is None else bdown[int(e)].astype(np.float64))
         y[r_pos, j_pos] = ye
+    p = getattr(wl.cfg, "dropout", 0.0)
+    if p > 0.0:
+        # [P2 slide 32] training-mode dropout on every expert output row
+        arows = (rows[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+        y = dropout_rows(y.reshape(-1, wl.d), arows, p, wl.cfg.dropout_seed,
+                         wl.cfg.dropout_offset).reshape(len(rows), k, wl.d)
     out = combine(gate[rows], slot[rows], y)
     return Result(N=N, E=E, k=k, C=C, scores=scores, idx=idx, gate=gate, slot=slot,
                   used=used, rows=rows, out=out, y=y if want_y else None)

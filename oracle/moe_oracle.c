@@ -131,6 +131,72 @@ static double oracle_gelu(double z)
     return 0.5 * z * (1.0 + erf(z * 0.70710678118654752440));
 }
 
+/* Philox4x64-10, the counter-based generator of Salmon, Moraes, Dror and
+ * Shaw ("Parallel random numbers: as easy as 1, 2, 3", SC 2011): ten rounds
+ * on a 4 x 64-bit counter under a 2 x 64-bit key. A round multiplies
+ * counter words 0 and 2 by the two round multipliers into 128-bit products,
+ * and the new counter is (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); between
+ * rounds each key word grows by its Weyl constant (the golden ratio and
+ * sqrt(3) - 1 in 64-bit fixed point). out = the counter after round ten. */
+void oracle_philox4x64(const uint64_t *ctr, const uint64_t *key, uint64_t *out)
+{
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+    uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint64_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const unsigned __int128 p0 = (unsigned __int128)M0 * c0;
+        const unsigned __int128 p1 = (unsigned __int128)M1 * c2;
+        const uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        const uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* [P2 slide 32] training-mode dropout on an expert's output row (after
+ * the down product and its bias). Element i of the row of assignment a
+ * (a = t k + j) is kept when its 32-bit word w(a, i) >= floor(p 2^32), and
+ * a kept element is scaled by 1 / (1 - p), so its mean is unchanged;
+ * dropped elements become 0. w(a, i) is half (i mod 2; 0 = the low half)
+ * of output word (i mod 8) / 2 of Philox4x64-10 at counter
+ * (i / 8, a, offset, 0) under key (seed, 0). */
+uint32_t oracle_dropout_threshold(double p)
+{
+    return (uint32_t)floor(p * 4294967296.0);
+}
+
+static int dropout_keep(int64_t a, int64_t i, uint32_t thresh, uint64_t seed, uint64_t offset)
+{
+    const uint64_t ctr[4] = {(uint64_t)(i / 8), (uint64_t)a, offset, 0};
+    const uint64_t key[2] = {seed, 0};
+    uint64_t r[4];
+    oracle_philox4x64(ctr, key, r);
+    const uint64_t wd = r[(i % 8) / 2];
+    const uint32_t w = (uint32_t)(i % 2 ? wd >> 32 : wd);
+    return w >= thresh;
+}
+
+/* Dropout of n rows y [n, d], row r being assignment arows[r]'s output. */
+void oracle_dropout_rows(int64_t n, int64_t d, const int64_t *arows, double p, uint64_t seed,
+                         uint64_t offset, double *y)
+{
+    const uint32_t thresh = oracle_dropout_threshold(p);
+    const double scale = 1.0 / (1.0 - p);
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t i = 0; i < d; ++i)
+            y[r * d + i] = dropout_keep(arows[r], i, thresh, seed, offset) ? y[r * d + i] * scale
+                                                                           : 0.0;
+}
+
 /* [P1 STEP 8-10] one expert on a list of its tokens: for each listed token
  * row x_t, z = W_up x_t, h = ReLU(z), y = W_down h. W_up is [d_ff, d] and
  * W_down is [d, d_ff], row-major. y is [n, d]. hbuf must hold
@@ -184,12 +250,15 @@ static double oracle_gelu_grad(double z)
 }
 
 /* The expert variant the backward differentiates: activation (0 ReLU,
- * 1 GELU), optional biases bup [E, d_ff] and bdown [E, d], and where their
- * gradients go (dbup, dbdown; NULL: not accumulated). */
+ * 1 GELU), optional biases bup [E, d_ff] and bdown [E, d], where their
+ * gradients go (dbup, dbdown; NULL: not accumulated), and the dropout on the
+ * expert outputs (p, seed, offset). */
 typedef struct {
     int32_t act;
     const double *bup, *bdown;
     double *dbup, *dbdown;
+    double p;                  /* dropout probability (0: none) */
+    uint64_t seed, offset;     /* its generator's key and counter word */
 } expert_variant;
 
 static double act_of(int32_t act, double z)
@@ -204,18 +273,19 @@ static double act_grad(int32_t act, double z)
 
 /* The backward of one token t: adds its terms to dx_t and, when the
  * pointers are not NULL, to dWg, dWup, dWdown and the bias gradients.
- * gate, slot, idx are the routing of all tokens; z, h, y, dz [d_ff or d] and
- * dg [k] are scratch. */
+ * gate, slot, idx are the routing of all tokens; z, h, y, dz, mk [d_ff or d]
+ * and dg [k] are scratch. */
 static void backward_token(int64_t t, int64_t d, int32_t k, int64_t d_ff,
                            const double *x, const double *Wg, const double *Wup,
                            const double *Wdown, const expert_variant *v,
                            const double *dout, const int32_t *idx, const double *gate,
                            const int32_t *slot, double *dxt, double *dWg, double *dWup,
                            double *dWdown, double *z, double *h, double *y, double *dz,
-                           double *dg)
+                           double *dg, double *mk)
 {
     const double *xt = x + t * d;
     const double *go = dout + t * d;
+    const uint32_t thresh = oracle_dropout_threshold(v->p);
     for (int32_t j = 0; j < k; ++j) {
         dg[j] = 0.0;
         if (slot[t * k + j] < 0)
@@ -233,15 +303,20 @@ static void backward_token(int64_t t, int64_t d, int32_t k, int64_t d_ff,
             z[f] = acc;
             h[f] = act_of(v->act, acc);
         }
+        /* dropout factor m_o of each output element: 1 / (1 - p) or 0 */
+        for (int64_t o = 0; o < d; ++o)
+            mk[o] = v->p > 0.0 ? (dropout_keep(t * k + j, o, thresh, v->seed, v->offset)
+                                      ? 1.0 / (1.0 - v->p) : 0.0)
+                               : 1.0;
         for (int64_t o = 0; o < d; ++o) {
             double acc = 0.0;
             for (int64_t f = 0; f < d_ff; ++f)
                 acc += wd[o * d_ff + f] * h[f];
             if (v->bdown)
                 acc += v->bdown[e * d + o];
-            y[o] = acc;
+            y[o] = acc * mk[o];
         }
-        /* combine: dg = <dout_t, y>, dy = g dout_t */
+        /* combine: dg = <dout_t, y>; through the dropout, dy = g dout_t m */
         double a = 0.0;
         for (int64_t o = 0; o < d; ++o)
             a += go[o] * y[o];
@@ -250,19 +325,19 @@ static void backward_token(int64_t t, int64_t d, int32_t k, int64_t d_ff,
         if (dWdown) {
             double *gwd = dWdown + e * d * d_ff;
             for (int64_t o = 0; o < d; ++o) {
-                const double dyo = g * go[o];
+                const double dyo = g * go[o] * mk[o];
                 for (int64_t f = 0; f < d_ff; ++f)
                     gwd[o * d_ff + f] += dyo * h[f];
             }
         }
         if (v->dbdown)
             for (int64_t o = 0; o < d; ++o)
-                v->dbdown[e * d + o] += g * go[o];
+                v->dbdown[e * d + o] += g * go[o] * mk[o];
         /* activation: dz = dh act'(z) */
         for (int64_t f = 0; f < d_ff; ++f) {
             double acc = 0.0;
             for (int64_t o = 0; o < d; ++o)
-                acc += wd[o * d_ff + f] * (g * go[o]);
+                acc += wd[o * d_ff + f] * (g * go[o] * mk[o]);
             dz[f] = acc * act_grad(v->act, z[f]);
         }
         /* up: dW_up += dz x_t^T, db_up += dz; dx_t += W_up^T dz */
@@ -316,8 +391,9 @@ static int backward_impl(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_f
     double *y = (double *)malloc(sizeof(double) * (size_t)d);
     double *dz = (double *)malloc(sizeof(double) * (size_t)d_ff);
     double *dg = (double *)malloc(sizeof(double) * (size_t)k);
+    double *mk = (double *)malloc(sizeof(double) * (size_t)d);
     int rc = 0;
-    if (!scores || !idx || !gate || !slot || !used || !z || !h || !y || !dz || !dg) {
+    if (!scores || !idx || !gate || !slot || !used || !z || !h || !y || !dz || !dg || !mk) {
         rc = -1;
         goto done;
     }
@@ -343,11 +419,11 @@ static int backward_impl(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_f
     for (int64_t r = 0; r < nrows; ++r) {
         const int64_t t = rows ? rows[r] : r;
         backward_token(t, d, k, d_ff, x, Wg, Wup, Wdown, v, dout, idx, gate, slot, dx + r * d,
-                       dWg, dWup, dWdown, z, h, y, dz, dg);
+                       dWg, dWup, dWdown, z, h, y, dz, dg, mk);
     }
 done:
     free(scores); free(idx); free(gate); free(slot); free(used);
-    free(z); free(h); free(y); free(dz); free(dg);
+    free(z); free(h); free(y); free(dz); free(dg); free(mk);
     return rc;
 }
 
@@ -370,7 +446,9 @@ done:
  *                                                     dx_t += W_up^T dz
  * with act ReLU (act == 0; act'(z) = [z > 0]) or the exact GELU (act == 1;
  * [P2 slide 32]); bup [E, d_ff] and bdown [E, d] may be NULL (no biases),
- * and dbup, dbdown are written when not NULL. The gate derivative treats
+ * and dbup, dbdown are written when not NULL. With dropout p > 0 the expert
+ * output is y m (m the dropout factor of each element, see
+ * oracle_dropout_rows), so dg = <dout_t, y m> and dy = g dout_t m. The gate derivative treats
  * the float32 rounding of the scores as the identity. Sums over tokens run
  * in token order, then choice order. dx [N, d], dWg [E, d], dWup
  * [E, d_ff, d], dWdown [E, d, d_ff]; C = capacity. Scratch is allocated here
@@ -380,10 +458,11 @@ done:
 int oracle_backward(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff, int64_t C,
                     const double *x, const double *Wg, const double *noise,
                     const double *Wup, const double *Wdown, int32_t act, const double *bup,
-                    const double *bdown, const double *dout, double *dx, double *dWg,
-                    double *dWup, double *dWdown, double *dbup, double *dbdown)
+                    const double *bdown, double p, uint64_t seed, uint64_t offset,
+                    const double *dout, double *dx, double *dWg, double *dWup, double *dWdown,
+                    double *dbup, double *dbdown)
 {
-    const expert_variant v = {act, bup, bdown, dbup, dbdown};
+    const expert_variant v = {act, bup, bdown, dbup, dbdown, p, seed, offset};
     return backward_impl(N, d, E, k, d_ff, C, x, Wg, noise, Wup, Wdown, &v, dout, N, NULL, dx,
                          dWg, dWup, dWdown);
 }
@@ -395,10 +474,11 @@ int oracle_backward(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff, in
 int oracle_backward_rows(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_ff, int64_t C,
                          const double *x, const double *Wg, const double *noise,
                          const double *Wup, const double *Wdown, int32_t act,
-                         const double *bup, const double *bdown, const double *dout,
-                         int64_t nrows, const int64_t *rows, double *dx_rows)
+                         const double *bup, const double *bdown, double p, uint64_t seed,
+                         uint64_t offset, const double *dout, int64_t nrows,
+                         const int64_t *rows, double *dx_rows)
 {
-    const expert_variant v = {act, bup, bdown, NULL, NULL};
+    const expert_variant v = {act, bup, bdown, NULL, NULL, p, seed, offset};
     return backward_impl(N, d, E, k, d_ff, C, x, Wg, noise, Wup, Wdown, &v, dout, nrows, rows,
                          dx_rows, NULL, NULL, NULL);
 }
@@ -408,7 +488,8 @@ int oracle_backward_rows(int64_t N, int64_t d, int64_t E, int32_t k, int64_t d_f
  * (dWdown_cols [nf, d], entry o = dW_down[e][o][f]), with the same terms and
  * token order as oracle_backward. Wup_e [d_ff, d] and Wdown_e [d, d_ff] are
  * expert e's matrices, bup_e [d_ff] its up bias or NULL; the routing covers
- * all N tokens. Per token routed to e and kept: g = its gate, dy = g dout_t,
+ * all N tokens; p, seed, offset: the dropout, as in oracle_backward. Per
+ * token routed to e and kept: g = its gate, dy = g dout_t m,
  * z_f = W_up[e][f] x_t + b_up[e][f], dW_down[e][:, f] += dy act(z_f),
  * dz_f = act'(z_f) <W_down[e][:, f], dy>, dW_up[e][f] += dz_f x_t. Returns
  * 0, or -1 if an allocation fails. */
@@ -416,9 +497,11 @@ int oracle_backward_expert_units(int64_t N, int64_t d, int64_t E, int32_t k, int
                                  int64_t C, const double *x, const double *Wg,
                                  const double *noise, int64_t e, const double *Wup_e,
                                  const double *Wdown_e, int32_t act, const double *bup_e,
+                                 double p, uint64_t seed, uint64_t offset,
                                  const double *dout, int64_t nf, const int64_t *fs,
                                  double *dWup_rows, double *dWdown_cols)
 {
+    const uint32_t thresh = oracle_dropout_threshold(p);
     float *scores = (float *)malloc(sizeof(float) * (size_t)(N * E + 1));
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N * k + 1));
     double *gate = (double *)malloc(sizeof(double) * (size_t)(N * k + 1));
@@ -452,7 +535,10 @@ int oracle_backward_expert_units(int64_t N, int64_t d, int64_t E, int32_t k, int
                 const double h = act_of(act, z);
                 double dh = 0.0;
                 for (int64_t o = 0; o < d; ++o) {
-                    const double dyo = g * go[o];
+                    const double m = p > 0.0 ? (dropout_keep(t * k + j, o, thresh, seed, offset)
+                                                    ? 1.0 / (1.0 - p) : 0.0)
+                                             : 1.0;
+                    const double dyo = g * go[o] * m;
                     dWdown_cols[q * d + o] += dyo * h;
                     dh += Wdown_e[o * d_ff + f] * dyo;
                 }

@@ -84,6 +84,9 @@ class Config:
     description: str = ""
     act: str = "relu"      # expert activation: "relu" (page 1) or "gelu" (nanoMoE slide 32)
     bias_std: float = 0.0  # std of the fp32 expert biases (nanoMoE slide 32); 0 -> no biases
+    dropout: float = 0.0   # training-mode dropout on the expert outputs (nanoMoE slide 32)
+    dropout_seed: int = 0  # its generator key
+    dropout_offset: int = 0
 
     @property
     def has_noise(self) -> bool:
@@ -364,12 +367,14 @@ def capacity_example() -> Workload:
 
 def custom(name: str, N: int, d: int, E: int, k: int, d_ff: int, dtype: str, cf: float,
            sigma: float = 0.0, bias0: float = 0.0, seed: int = 1, w_std: float = 0.05,
-           wg_std: float = 0.0, act: str = "relu", bias_std: float = 0.0) -> Workload:
+           wg_std: float = 0.0, act: str = "relu", bias_std: float = 0.0,
+           dropout: float = 0.0, dropout_seed: int = 0, dropout_offset: int = 0) -> Workload:
     """A seeded workload of any shape (test cases: ragged tails, edge cases)."""
     if act not in ("relu", "gelu"):
         raise ValueError("act must be 'relu' or 'gelu'")
     cfg = Config(name, N=N, d=d, E=E, k=k, d_ff=d_ff, dtype=dtype, cf=cf, sigma=sigma,
                  bias0=bias0, seed=seed, w_std=w_std, wg_std=wg_std, act=act,
-                 bias_std=bias_std)
+                 bias_std=bias_std, dropout=dropout, dropout_seed=dropout_seed,
+                 dropout_offset=dropout_offset)
     return make(cfg)
 

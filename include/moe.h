@@ -128,13 +128,27 @@ int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *no
  * b_up:   [E, d_ff] MOE_F32 added to W_up[e] x before the activation, or NULL
  * b_down: [E, d]    MOE_F32 added to W_down[e] h, or NULL
  * Bias data are device pointers, 16-byte aligned (MOE_ERR_ALIGN), checked
- * for dtype and extents like every other tensor. Dropout (training only)
- * is not applied. */
+ * for dtype and extents like every other tensor.
+ * dropout: training-mode dropout on each expert output row (slide 32: the
+ *   expert ends in a dropout), after b_down; 0 (the default of a
+ *   zero-initialised struct) applies none; MOE_ERR_ARG outside [0, 1).
+ *   Element i of the row of assignment a = t k + j is kept when its 32-bit
+ *   random word is >= floor(dropout 2^32), and is then scaled by
+ *   1 / (1 - dropout); dropped elements are 0. The words of elements
+ *   8q .. 8q+7 are the Philox4x64-10 block (Salmon et al., SC 2011) at
+ *   counter (q, a, dropout_offset, 0) under key (dropout_seed, 0): element
+ *   i takes half i % 2 (low half first) of output word (i % 8) / 2. A call
+ *   with the same seed and offset draws the same mask, so moe_backward_ex
+ *   differentiates exactly the forward's dropped-out layer.
+ * Zero-initialise the struct and set the fields used. */
 enum { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1 };
 typedef struct {
     int32_t activation;
     const moe_tensor *b_up;
     const moe_tensor *b_down;
+    float dropout;
+    uint64_t dropout_seed;
+    uint64_t dropout_offset;
 } moe_expert_opts;
 
 /* moe_forward with the expert variant above; opts NULL is moe_forward. */
@@ -257,8 +271,8 @@ int moe_combine(int64_t N, int64_t d, int k, const moe_tensor *Y, const float *t
 
 /* Backward pass of the layer (the row after the forward: gradients through
  * the gates to the router and through the experts), for bf16 layers with
- * ReLU experts and no biases (moe_backward_ex: the GELU / bias variants);
- * dropout is not applied. For a loss whose
+ * ReLU experts and no biases (moe_backward_ex: the GELU / bias / dropout
+ * variants). For a loss whose
  * gradient with respect to out is dout, by the chain rule of moe_forward:
  *   combine: dy = g * dout, dg = <dout, y> (kept choices; dropped: 0);
  *   masked softmax over the kept scores: ds_j = g_j (dg_j - sum_l g_l dg_l),
@@ -285,9 +299,11 @@ int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *n
                  moe_tensor *dW_down, moe_stats *stats);
 
 /* moe_backward for the expert variants of moe_forward_ex (page 2, slide
- * 32): opts as there (NULL: ReLU, no biases). With GELU, dZ = dH gelu'(z),
- * gelu'(z) = Phi(z) + z phi(z), on the bf16 pre-activations z the recomputed
- * up product keeps. Bias gradients, fp32, written exactly when the layer has
+ * 32): opts as there (NULL: ReLU, no biases, no dropout). With GELU,
+ * dZ = dH gelu'(z), gelu'(z) = Phi(z) + z phi(z), on the bf16
+ * pre-activations z the recomputed up product keeps. With dropout, the
+ * same mask as the forward's (same seed and offset): dg = <dout, y m> and
+ * dY = g dout m, m the dropout factor (1 / (1 - p) or 0) of each element. Bias gradients, fp32, written exactly when the layer has
  * that bias (else they must be NULL: MOE_ERR_ARG; a missing one:
  * MOE_ERR_NULL), each the sum over the expert's kept assignments in a fixed
  * order:

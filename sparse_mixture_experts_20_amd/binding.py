@@ -45,7 +45,8 @@ class MoeStats(ctypes.Structure):
 
 class MoeExpertOpts(ctypes.Structure):
     _fields_ = [("activation", ctypes.c_int32), ("b_up", ctypes.c_void_p),
-                ("b_down", ctypes.c_void_p)]
+                ("b_down", ctypes.c_void_p), ("dropout", ctypes.c_float),
+                ("dropout_seed", ctypes.c_uint64), ("dropout_offset", ctypes.c_uint64)]
 
 
 class MoeError(RuntimeError):
@@ -167,26 +168,30 @@ def _stream(stream=None):
 
 
 class ExpertOpts:
-    """``moe_expert_opts`` for an activation name and optional fp32 bias tensors
-    (b_up [E, d_ff], b_down [E, d]); keeps the descriptors alive."""
+    """``moe_expert_opts`` for an activation name, optional fp32 bias tensors
+    (b_up [E, d_ff], b_down [E, d]) and an optional training-mode dropout
+    ``(p, seed, offset)`` on the expert outputs; keeps the descriptors alive."""
 
     def __init__(self, act: str = "relu", b_up: Optional[torch.Tensor] = None,
-                 b_down: Optional[torch.Tensor] = None):
+                 b_down: Optional[torch.Tensor] = None, dropout=None):
         if act not in ACTS:
             raise ValueError("act must be 'relu' or 'gelu'")
+        p, seed, offset = dropout if dropout is not None else (0.0, 0, 0)
         self._d = (desc(b_up), desc(b_down))
         self.c = MoeExpertOpts(ACTS[act],
                                None if self._d[0] is None else ctypes.addressof(self._d[0]),
-                               None if self._d[1] is None else ctypes.addressof(self._d[1]))
+                               None if self._d[1] is None else ctypes.addressof(self._d[1]),
+                               float(p), int(seed), int(offset))
 
     def ref(self):
         return ctypes.byref(self.c)
 
 
-def _opts(act, b_up, b_down):
-    if act == "relu" and b_up is None and b_down is None:
+def _opts(act, b_up, b_down, dropout=None):
+    if act == "relu" and b_up is None and b_down is None and (dropout is None or
+                                                              dropout[0] == 0.0):
         return None
-    return ExpertOpts(act, b_up, b_down)
+    return ExpertOpts(act, b_up, b_down, dropout)
 
 
 def capacity(N: int, E: int, k: int, capacity_factor: float) -> int:
@@ -213,8 +218,10 @@ def forward(x: torch.Tensor, W_g: torch.Tensor, noise: Optional[torch.Tensor],
             W_up: torch.Tensor, W_down: torch.Tensor, k: int, capacity_factor: float,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
             export: bool = True, stream=None, act: str = "relu",
-            b_up: Optional[torch.Tensor] = None, b_down: Optional[torch.Tensor] = None):
-    """Run ``moe_forward``. Returns ``(out, Stats)``; with ``export=False`` the
+            b_up: Optional[torch.Tensor] = None, b_down: Optional[torch.Tensor] = None,
+            dropout=None):
+    """Run ``moe_forward`` (``moe_forward_ex`` for an expert variant; dropout:
+    ``(p, seed, offset)`` or None). Returns ``(out, Stats)``; with ``export=False`` the
     routing arrays stay in the workspace and Stats only carries the capacity."""
     N = x.numel() // x.shape[-1]
     d = x.shape[-1]
@@ -234,7 +241,7 @@ def forward(x: torch.Tensor, W_g: torch.Tensor, noise: Optional[torch.Tensor],
     st = MoeStats(_stream(stream), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                   _ptr(idx), _ptr(gate), _ptr(slot), _ptr(used), -1)
     dx, dg, dn, du, dd, do = desc(x), desc(W_g), desc(noise), desc(W_up), desc(W_down), desc(out)
-    o = _opts(act, b_up, b_down)
+    o = _opts(act, b_up, b_down, dropout)
     if o is None:
         rc = lib().moe_forward(_ref(dx), _ref(dg), _ref(dn), _ref(du), _ref(dd), k,
                                capacity_factor, _ref(do), ctypes.byref(st))
@@ -253,8 +260,9 @@ def backward_workspace_size(N: int, d: int, E: int, d_ff: int, k: int, capacity_
 
 def backward(x, W_g, noise, W_up, W_down, k: int, capacity_factor: float, dout,
              workspace=None, stream=None, export: bool = False, act: str = "relu",
-             b_up: Optional[torch.Tensor] = None, b_down: Optional[torch.Tensor] = None):
-    """Run ``moe_backward`` (``moe_backward_ex`` for GELU or biases): returns
+             b_up: Optional[torch.Tensor] = None, b_down: Optional[torch.Tensor] = None,
+             dropout=None):
+    """Run ``moe_backward`` (``moe_backward_ex`` for GELU, biases or dropout): returns
     (dx [N, d], dW_g [E, d], dW_up [E, d_ff, d], dW_down [E, d, d_ff]), all
     fp32, followed by db_up [E, d_ff] and db_down [E, d] (None where the layer
     has no such bias) when the layer has a bias. With ``export=True`` returns
@@ -280,7 +288,7 @@ def backward(x, W_g, noise, W_up, W_down, k: int, capacity_factor: float, dout,
     st = MoeStats(_stream(stream), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                   _ptr(idx), _ptr(gate), _ptr(slot), _ptr(used), -1)
     ds = [desc(t) for t in (x, W_g, noise, W_up, W_down, dout, dx, dwg, dwu, dwd, dbu, dbd)]
-    o = _opts(act, b_up, b_down)
+    o = _opts(act, b_up, b_down, dropout)
     r = [_ref(a) for a in ds]
     if o is None:
         rc = lib().moe_backward(r[0], r[1], r[2], r[3], r[4], k, capacity_factor, r[5], r[6],
@@ -302,7 +310,8 @@ class Forward:
     timing loops measure only the enqueue of the kernels."""
 
     def __init__(self, x, W_g, noise, W_up, W_down, k, capacity_factor, out=None,
-                 export=False, stream=None, act="relu", b_up=None, b_down=None):
+                 export=False, stream=None, act="relu", b_up=None, b_down=None,
+                 dropout=None):
         self.tensors = (x, W_g, noise, W_up, W_down)
         N, d = x.numel() // x.shape[-1], x.shape[-1]
         E, d_ff = W_up.shape[0], W_up.shape[1]
@@ -322,7 +331,7 @@ class Forward:
                               self.workspace.numel(), _ptr(self.idx), _ptr(self.gate),
                               _ptr(self.slot), _ptr(self.used), -1)
         self._args = [_ref(a) for a in self._d]
-        self._opts = _opts(act, b_up, b_down)
+        self._opts = _opts(act, b_up, b_down, dropout)
         self._biases = (b_up, b_down)
         self._fn = lib().moe_forward if self._opts is None else lib().moe_forward_ex
 
@@ -345,7 +354,7 @@ class Backward:
     cross the C ABI."""
 
     def __init__(self, x, W_g, noise, W_up, W_down, k, capacity_factor, dout, stream=None,
-                 act="relu", b_up=None, b_down=None):
+                 act="relu", b_up=None, b_down=None, dropout=None):
         N, d = x.numel() // x.shape[-1], x.shape[-1]
         E, d_ff = W_up.shape[0], W_up.shape[1]
         dev = x.device
@@ -364,7 +373,7 @@ class Backward:
         self._d = [desc(t) for t in (x, W_g, noise, W_up, W_down, dout, self.dx, self.dW_g,
                                      self.dW_up, self.dW_down, self.db_up, self.db_down)]
         self._args = [_ref(a) for a in self._d]
-        self._opts = _opts(act, b_up, b_down)
+        self._opts = _opts(act, b_up, b_down, dropout)
         self.stats = MoeStats(_stream(stream), ctypes.c_void_p(self.workspace.data_ptr()),
                               self.workspace.numel(), None, None, None, None, -1)
 
@@ -436,7 +445,8 @@ def _ws_args(ws):
 
 
 def experts(x, W_up, W_down, k, capacity_, used, slot_token, tiles, H=None, Y=None,
-            workspace="auto", stream=None, act="relu", b_up=None, b_down=None):
+            workspace="auto", stream=None, act="relu", b_up=None, b_down=None,
+            dropout=None):
     """Returns (H [E, min(C,N), d_ff] and Y [N*k, d], both in x's dtype)."""
     N, d = x.numel() // x.shape[-1], x.shape[-1]
     E, d_ff = W_up.shape[0], W_up.shape[1]
@@ -449,7 +459,7 @@ def experts(x, W_up, W_down, k, capacity_, used, slot_token, tiles, H=None, Y=No
     if not slot_token.is_contiguous():
         raise ValueError("slot_token must be a contiguous [E, min(C, N)] tensor")
     wp, wn = _ws_args(_expert_ws(workspace, x.dtype, x.device))
-    o = _opts(act, b_up, b_down)
+    o = _opts(act, b_up, b_down, dropout)
     if o is None:
         _check(lib().moe_experts(_ref(dx), _ref(du), _ref(dd), k, capacity_, _ptr(used),
                                  _ptr(slot_token), _ptr(tiles), _ptr(H), _ptr(Y), wp, wn,
@@ -480,10 +490,10 @@ def expert_up(x, W_up, k, capacity_, used, slot_token, tiles, H, workspace="auto
 
 
 def expert_down(N, W_down, k, capacity_, used, slot_token, tiles, H, Y, workspace="auto",
-                stream=None, b_down=None):
+                stream=None, b_down=None, dropout=None):
     dd = desc(W_down)
     wp, wn = _ws_args(_expert_ws(workspace, W_down.dtype, W_down.device))
-    o = _opts("relu", None, b_down)
+    o = _opts("relu", None, b_down, dropout)
     if o is None:
         rc = lib().moe_expert_down(N, _ref(dd), k, capacity_, _ptr(used), _ptr(slot_token),
                                    _ptr(tiles), _ptr(H), _ptr(Y), wp, wn, _stream(stream))

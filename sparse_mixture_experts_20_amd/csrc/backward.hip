@@ -1,5 +1,6 @@
 // Backward pass of the layer: gradients of a loss through the gates to the
-// router and through the experts (ReLU experts, no biases, dropout off).
+// router and through the experts (ReLU or GELU experts, optional biases,
+// optional training-mode dropout on the expert outputs).
 // Chain rule of the forward in this library (page 1 STEP 2-12; nanoMoE
 // slides 11-40), for an output gradient dout:
 //   combine  out_t = sum_j g_tj y_tj (kept j)   -> dy_tj = g_tj dout_t,
@@ -39,7 +40,7 @@ __device__ __forceinline__ void split3_bits(float a, unsigned short &hi, unsigne
 __global__ __launch_bounds__(256) void combine_backward_kernel(
     const unsigned short *__restrict__ dout, const unsigned short *__restrict__ Y,
     const float *__restrict__ gate, const int32_t *__restrict__ slot, int N, int d, int k,
-    unsigned short *__restrict__ dY, float *__restrict__ ds) {
+    unsigned short *__restrict__ dY, float *__restrict__ ds, Dropout dp) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= N)
@@ -58,6 +59,10 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
             for (int c = lane; c < chunks; c += 64) {
                 const u32x4 ov = *reinterpret_cast<const u32x4 *>(go + 8 * c);
                 const u32x4 yv = *reinterpret_cast<const u32x4 *>(yr + 8 * c);
+                // Y already carries the dropout; dY = g dout m
+                float m[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+                if (dp.on)
+                    dropout_factors8(dp, a, c, m);
                 u32x4 w;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -65,8 +70,8 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
                     const float o1 = __uint_as_float(ov[q] & 0xffff0000u);
                     p = fmaf(o0, __uint_as_float(yv[q] << 16), p);
                     p = fmaf(o1, __uint_as_float(yv[q] & 0xffff0000u), p);
-                    w[q] = (unsigned)f32_to_bf16_bits(g * o0) |
-                           ((unsigned)f32_to_bf16_bits(g * o1) << 16);
+                    w[q] = (unsigned)f32_to_bf16_bits(g * o0 * m[2 * q]) |
+                           ((unsigned)f32_to_bf16_bits(g * o1 * m[2 * q + 1]) << 16);
                 }
                 *reinterpret_cast<u32x4 *>(dyr + 8 * c) = w;
             }
@@ -255,13 +260,13 @@ __global__ __launch_bounds__(256) void dx_kernel(const float *__restrict__ dXa,
 
 hipError_t launch_combine_backward(const void *dout, const void *Y, const float *gate,
                                    const int32_t *slot, int64_t N, int64_t d, int k, void *dY,
-                                   float *ds, hipStream_t s) {
+                                   float *ds, hipStream_t s, Dropout dp) {
     if (N == 0)
         return hipSuccess;
     hipLaunchKernelGGL(combine_backward_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s,
                        static_cast<const unsigned short *>(dout),
                        static_cast<const unsigned short *>(Y), gate, slot, (int)N, (int)d, k,
-                       static_cast<unsigned short *>(dY), ds);
+                       static_cast<unsigned short *>(dY), ds, dp);
     return hipGetLastError();
 }
 

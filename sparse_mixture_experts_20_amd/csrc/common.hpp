@@ -34,6 +34,61 @@ __device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {
     return __builtin_bit_cast(float, (unsigned int)b << 16);
 }
 
+// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds on a 4 x 64-bit counter; a round
+// takes the 128-bit products of counter words 0 and 2 with the two round
+// multipliers and forms (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key
+// words grow by their Weyl constants between rounds.
+__device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2,
+                                              uint64_t c3, uint64_t k0, uint64_t k1,
+                                              uint64_t (&out)[4]) {
+    constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+        const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+// Training-mode dropout on the expert output rows (nanoMoE slides, slide 32:
+// the expert ends in a dropout). Element i of the row of assignment a is
+// kept when its 32-bit word is >= thresh = floor(p 2^32) and then scaled by
+// `scale` = 1 / (1 - p); dropped elements become 0. The words of elements
+// 8q .. 8q+7 are the Philox4x64-10 block at counter (q, a, offset, 0) under
+// key (seed, 0): element i takes half i % 2 (low half first) of output word
+// (i % 8) / 2.
+struct Dropout {
+    int on = 0;              // 0: no dropout
+    uint32_t thresh = 0;
+    float scale = 1.f;
+    uint64_t seed = 0, offset = 0;
+};
+
+// Dropout factors (scale or 0) of the 8 elements 8q .. 8q+7 of row a.
+__device__ __forceinline__ void dropout_factors8(const Dropout &dp, int64_t a, int64_t q,
+                                                 float (&m)[8]) {
+    uint64_t r[4];
+    philox4x64_10((uint64_t)q, (uint64_t)a, dp.offset, 0ull, dp.seed, 0ull, r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t w = (uint32_t)(i % 2 ? r[i / 2] >> 32 : r[i / 2]);
+        m[i] = w >= dp.thresh ? dp.scale : 0.f;
+    }
+}
+
 // 64-bit lane masks
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const unsigned lane = __lane_id();
@@ -80,11 +135,12 @@ hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t 
                             const int32_t *slot_token, const int32_t *tiles, void *H,
                             int64_t rows_per_expert, void *part, size_t part_bytes, int act,
                             const float *b_up, hipStream_t s, void *Z = nullptr);
+// dp: training-mode dropout on the rows of Y (default: none).
 hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int64_t d,
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, void *Y,
                               int64_t rows_per_expert, void *part, size_t part_bytes,
-                              const float *b_down, hipStream_t s);
+                              const float *b_down, hipStream_t s, Dropout dp = Dropout{});
 
 // Backward products over the dispatch plan (bf16 operands, fp32 accumulate):
 // dZ[e, r, :] = (dY[slot_token[e, r]] W_down[e]) * act'(z[e, r, :]), with
@@ -109,9 +165,10 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
 // Backward element-wise and layout kernels (backward.hip).
 // dY rows (bf16, kept choices) = gate * dout; ds [N, k] = gate * (dg - sum gate*dg)
 // with dg = <dout, Y> (Y: the experts' bf16 outputs, assignment-major). d % 8 == 0.
+// With dropout, dY = gate * dout * (the dropout factor of each Y element).
 hipError_t launch_combine_backward(const void *dout, const void *Y, const float *gate,
                                    const int32_t *slot, int64_t N, int64_t d, int k, void *dY,
-                                   float *ds, hipStream_t s);
+                                   float *ds, hipStream_t s, Dropout dp = Dropout{});
 // dsT3 [S][E][3*Tc] bf16: exact three-term split of ds(s*Tc + i, e) at columns
 // i, Tc + i, 2*Tc + i (tokens chunked by Tc).
 hipError_t launch_ds_split(const float *ds, const int32_t *idx, int64_t N, int64_t Tc, int64_t S,

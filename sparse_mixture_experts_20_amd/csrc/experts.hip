@@ -199,6 +199,7 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // row (MODE 1), or NULL. K-range partials take neither (the fix-up does).
 // Z16 (MODE 0, whole tiles only): when not NULL, the bf16 pre-activations
 // (product plus bias) are stored there too, [E, ceff, Nout] like H.
+// dp (MODE 1): training-mode dropout on the rows of Y, after the bias.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BKT, int S, int MODE>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void expert_gemm_kernel(
@@ -207,7 +208,7 @@ void expert_gemm_kernel(
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
     unsigned short *__restrict__ O16, float *__restrict__ O32, float *__restrict__ part,
     int P, int act, const float *__restrict__ bias, const unsigned short *mask,
-    unsigned short *__restrict__ Z16, int64_t bsa, int64_t bsb, int64_t bsc) {
+    unsigned short *__restrict__ Z16, Dropout dp, int64_t bsa, int64_t bsb, int64_t bsc) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int NTHR = NW * 64;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;   // wave tile
@@ -489,7 +490,8 @@ void expert_gemm_kernel(
                     store_h(std::false_type{});
             } else if (MODE == 1) {
                 // bf16 row of Y at the assignment's position
-                unsigned short *dst = O16 + (int64_t)slot_token[srow] * Nout + nb;
+                const int64_t arow = (int64_t)slot_token[srow];
+                unsigned short *dst = O16 + arow * Nout + nb;
                 const float *bp = bias ? bias + (int64_t)e * Nout + nb : nullptr;
 #pragma unroll
                 for (int h = 0; h < CPL / 8; ++h) {
@@ -498,6 +500,13 @@ void expert_gemm_kernel(
                         if (bp) {
                             z0 += *reinterpret_cast<const f32x4 *>(bp + 8 * h);
                             z1 += *reinterpret_cast<const f32x4 *>(bp + 8 * h + 4);
+                        }
+                        if (dp.on) {
+                            // columns nb + 8h .. +7 share one generator block
+                            float m[8];
+                            dropout_factors8(dp, arow, (nb + 8 * h) / 8, m);
+                            z0 *= f32x4{m[0], m[1], m[2], m[3]};
+                            z1 *= f32x4{m[4], m[5], m[6], m[7]};
                         }
                         u32x4 pk;
 #pragma unroll
@@ -558,14 +567,14 @@ void expert_gemm_kernel(
 
 // Sum of the K-range partials of the cut tiles, in K order, then the same
 // epilogue as a whole tile (MODE 0: bias, activation, bf16 H; MODE 1: bias,
-// bf16 row of Y).
+// dropout, bf16 row of Y).
 // One workgroup per 16-row strip of a cut tile; 4 columns per thread.
 template <int BM, int BN, int BKT, int MODE>
 __global__ __launch_bounds__(256) void split_fixup_kernel(
     int K, int Nout, int E, int ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
     const float *__restrict__ part, int P, unsigned short *__restrict__ O16, int act,
-    const float *__restrict__ bias) {
+    const float *__restrict__ bias, Dropout dp) {
     constexpr int STRIPS = BM / 16;
     __shared__ int s_mt[kMaxExperts + 1];
     for (int i = threadIdx.x; i <= E; i += 256)
@@ -595,6 +604,12 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
         if (bias)
             v += *reinterpret_cast<const f32x4 *>(bias + (int64_t)e * Nout + n);
         int64_t orow = (int64_t)slot_token[srow];   // MODE 1: the row of Y
+        if (MODE == 1 && dp.on) {
+            float m[8];
+            dropout_factors8(dp, orow, n / 8, m);
+            const int o = n % 8;                      // 0 or 4
+            v *= f32x4{m[o], m[o + 1], m[o + 2], m[o + 3]};
+        }
         if (MODE == 0) {
             orow = srow;                              // the row of H
             if (act == kActGelu)
@@ -616,7 +631,7 @@ __global__ __launch_bounds__(256) void experts_f32_kernel(
     const float *__restrict__ A_src, const float *__restrict__ W, int K, int Nout, int k,
     int ceff, const int32_t *__restrict__ used, const int32_t *__restrict__ slot_token,
     float *__restrict__ H_out, float *__restrict__ Y_out, int act,
-    const float *__restrict__ bias) {
+    const float *__restrict__ bias, Dropout dp) {
     constexpr int TM = 64, TN = 64, TK = 16;
     __shared__ float As[TK][TM + 4];
     __shared__ float Bs[TK][TN + 4];
@@ -669,10 +684,18 @@ __global__ __launch_bounds__(256) void experts_f32_kernel(
             if (n >= Nout)
                 continue;
             const float z = bias ? acc[i][j] + bias[(int64_t)e * Nout + n] : acc[i][j];
-            if (MODE == 0)
+            if (MODE == 0) {
                 H_out[srow * Nout + n] = act == kActGelu ? gelu(z) : fmaxf(z, 0.f);
-            else
-                Y_out[(int64_t)slot_token[srow] * Nout + n] = z;
+            } else {
+                const int64_t arow = (int64_t)slot_token[srow];
+                float f = 1.f;
+                if (dp.on) {
+                    float m[8];
+                    dropout_factors8(dp, arow, n / 8, m);
+                    f = m[n % 8];
+                }
+                Y_out[arow * Nout + n] = z * f;
+            }
         }
     }
 }
@@ -723,7 +746,8 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
                         const int32_t *slot_token, const int32_t *mt, unsigned short *O16,
                         float *part, size_t part_bytes, int act, const float *bias,
                         hipStream_t s, const unsigned short *mask = nullptr,
-                        float *O32 = nullptr, unsigned short *Z16 = nullptr) {
+                        float *O32 = nullptr, unsigned short *Z16 = nullptr,
+                        Dropout dp = Dropout{}) {
     auto kern = expert_gemm_kernel<BM, BN, WM, WN, kBK, 2, MODE>;
     constexpr int NTHR = WM * WN * 64;
     static int resident[kMaxDevices];   // per device, filled on first use (0 = unset)
@@ -749,14 +773,15 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
                          (split ? (int64_t)(P + kXcds - 1) / kXcds * kXcds : 0);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHR), 0, s, A, W, (int)K, (int)Nout, E,
                        k, (int)ceff, used, slot_token, mt, O16, O32, split ? part : nullptr,
-                       split ? P : 0, act, bias, mask, Z16, (int64_t)0, (int64_t)0, (int64_t)0);
+                       split ? P : 0, act, bias, mask, Z16, dp, (int64_t)0, (int64_t)0,
+                       (int64_t)0);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !split)
         return err;
     hipLaunchKernelGGL((split_fixup_kernel<BM, BN, kBK, MODE == 1 ? 1 : 0>),
                        dim3((unsigned)(P * (BM / 16))),
                        dim3(256), 0, s, (int)K, (int)Nout, E, (int)ceff, used, slot_token, mt,
-                       (const float *)part, P, O16, act, bias);
+                       (const float *)part, P, O16, act, bias, dp);
     return hipGetLastError();
 }
 
@@ -766,18 +791,20 @@ hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W,
                        const int32_t *slot_token, const int32_t *tiles, unsigned short *O16,
                        void *part, size_t part_bytes, int act, const float *bias,
                        hipStream_t s, const unsigned short *mask = nullptr,
-                       float *O32 = nullptr, unsigned short *Z16 = nullptr) {
+                       float *O32 = nullptr, unsigned short *Z16 = nullptr,
+                       Dropout dp = Dropout{}) {
     float *pf = static_cast<float *>(part);
     if (t == Tile::k256)
         return launch_tiles<256, 256, 2, 4, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
                                                   tiles + E + 1, O16, pf, part_bytes, act, bias,
-                                                  s, mask, O32, Z16);
+                                                  s, mask, O32, Z16, dp);
     if (t == Tile::k128x64)
         return launch_tiles<128, 64, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
                                                  tiles, O16, pf, part_bytes, act, bias, s, mask,
-                                                 O32, Z16);
+                                                 O32, Z16, dp);
     return launch_tiles<128, 128, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token, tiles,
-                                              O16, pf, part_bytes, act, bias, s, mask, O32, Z16);
+                                              O16, pf, part_bytes, act, bias, s, mask, O32, Z16,
+                                              dp);
 }
 
 }  // namespace
@@ -795,7 +822,8 @@ hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, in
                        (const int32_t *)nullptr, (const int32_t *)nullptr,
                        (const int32_t *)nullptr, (unsigned short *)nullptr, Y, (float *)nullptr,
                        0, kActRelu, (const float *)nullptr, (const unsigned short *)nullptr,
-                       (unsigned short *)nullptr, (int64_t)0, (int64_t)0, (int64_t)0);
+                       (unsigned short *)nullptr, Dropout{}, (int64_t)0, (int64_t)0,
+                       (int64_t)0);
     return hipGetLastError();
 }
 
@@ -819,7 +847,8 @@ hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t 
                        dim3((unsigned)((d_ff + 63) / 64), (unsigned)((ceff + 63) / 64), E),
                        dim3(256), 0, s, static_cast<const float *>(x),
                        static_cast<const float *>(w_up), (int)d, (int)d_ff, k, (int)ceff, used,
-                       slot_token, static_cast<float *>(H), (float *)nullptr, act, b_up);
+                       slot_token, static_cast<float *>(H), (float *)nullptr, act, b_up,
+                       Dropout{});
     return hipGetLastError();
 }
 
@@ -827,7 +856,7 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, void *Y,
                               int64_t rows_per_expert, void *part, size_t part_bytes,
-                              const float *b_down, hipStream_t s) {
+                              const float *b_down, hipStream_t s, Dropout dp) {
     if (ceff == 0)
         return hipSuccess;
     if (bf16)
@@ -835,12 +864,13 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
                               static_cast<const unsigned short *>(H),
                               static_cast<const unsigned short *>(w_down), d_ff, d, E, k, ceff,
                               used, slot_token, tiles, static_cast<unsigned short *>(Y), part,
-                              part_bytes, kActRelu, b_down, s);
+                              part_bytes, kActRelu, b_down, s, nullptr, nullptr, nullptr, dp);
     hipLaunchKernelGGL(experts_f32_kernel<1>,
                        dim3((unsigned)((d + 63) / 64), (unsigned)((ceff + 63) / 64), E),
                        dim3(256), 0, s, static_cast<const float *>(H),
                        static_cast<const float *>(w_down), (int)d_ff, (int)d, k, (int)ceff, used,
-                       slot_token, (float *)nullptr, static_cast<float *>(Y), kActRelu, b_down);
+                       slot_token, (float *)nullptr, static_cast<float *>(Y), kActRelu, b_down,
+                       dp);
     return hipGetLastError();
 }
 
@@ -890,7 +920,7 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
                            (const int32_t *)nullptr, (const int32_t *)nullptr,
                            (unsigned short *)nullptr, C, (float *)nullptr, 0, kActRelu,
                            (const float *)nullptr, (const unsigned short *)nullptr,
-                           (unsigned short *)nullptr, sa, sb, sc);
+                           (unsigned short *)nullptr, Dropout{}, sa, sb, sc);
         return hipGetLastError();
     }
     const int64_t grid = (((M + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) / kXcds * kXcds;
@@ -900,7 +930,7 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
                        (const int32_t *)nullptr, (const int32_t *)nullptr,
                        (unsigned short *)nullptr, C, (float *)nullptr, 0, kActRelu,
                        (const float *)nullptr, (const unsigned short *)nullptr,
-                           (unsigned short *)nullptr, sa, sb, sc);
+                           (unsigned short *)nullptr, Dropout{}, sa, sb, sc);
     return hipGetLastError();
 }
 

@@ -237,6 +237,7 @@ int check_router_args(const moe_tensor *x, const moe_tensor *W_g, const moe_tens
 struct ExpertOpts {
     int act = moe::kActRelu;
     const float *b_up = nullptr, *b_down = nullptr;
+    moe::Dropout drop;
 };
 
 int check_bias(const moe_tensor *b, int64_t E, int64_t n, const float *&out) {
@@ -262,6 +263,16 @@ int check_opts(const moe_expert_opts *o, int64_t E, int64_t d, int64_t d_ff, Exp
     if (o->activation != MOE_ACT_RELU && o->activation != MOE_ACT_GELU)
         return MOE_ERR_ARG;
     r.act = o->activation == MOE_ACT_GELU ? moe::kActGelu : moe::kActRelu;
+    if (!(o->dropout >= 0.f && o->dropout < 1.f))      // NaN fails too
+        return MOE_ERR_ARG;
+    if (o->dropout > 0.f) {
+        const double p = o->dropout;
+        r.drop.on = 1;
+        r.drop.thresh = (uint32_t)floor(p * 4294967296.0);
+        r.drop.scale = (float)(1.0 / (1.0 - p));
+        r.drop.seed = o->dropout_seed;
+        r.drop.offset = o->dropout_offset;
+    }
     int rc = check_bias(o->b_up, E, d_ff, r.b_up);
     if (rc != MOE_OK)
         return rc;
@@ -462,7 +473,7 @@ static int expert_down_impl(int64_t N, const moe_tensor *W_down, int k, int64_t 
                                               used, slot_token, tiles, Y,
                                               rows_per_expert(N, k, E, m.ceff), workspace,
                                               workspace ? workspace_bytes : 0, o.b_down,
-                                              static_cast<hipStream_t>(stream)));
+                                              static_cast<hipStream_t>(stream), o.drop));
 }
 
 int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
@@ -638,7 +649,8 @@ int moe_forward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor 
     MOE_TRY(moe::launch_expert_up(bf16, x->data, W_up->data, d, d_ff, (int)E, k, m.ceff, used,
                                   slot_token, tiles, H, rpe, part, part_bytes, o.act, o.b_up, s));
     MOE_TRY(moe::launch_expert_down(bf16, H, W_down->data, d, d_ff, (int)E, k, m.ceff, used,
-                                    slot_token, tiles, Y, rpe, part, part_bytes, o.b_down, s));
+                                    slot_token, tiles, Y, rpe, part, part_bytes, o.b_down, s,
+                                    o.drop));
     MOE_TRY(moe::launch_combine(Y, bf16 ? 1 : 0, gate, slot, N, d, k, out->data, out->dtype, s));
     return MOE_OK;
 }
@@ -795,10 +807,11 @@ int moe_backward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor
                                   tiles, H, rpe, nullptr, 0, o.act, o.b_up, s,
                                   gelu ? dZ : nullptr));
     MOE_TRY(moe::launch_expert_down(true, H, W_down->data, d, d_ff, Ei, k, ceff, used, st, tiles,
-                                    Y, rpe, nullptr, 0, o.b_down, s));
+                                    Y, rpe, nullptr, 0, o.b_down, s, o.drop));
     // combine and softmax backward; router weights: dW_g = ds^T x, per token
     // chunk on the exact split of ds, then the chunks summed in order
-    MOE_TRY(moe::launch_combine_backward(dout->data, Y, gate, slot, N, d, k, dY, ds, s));
+    MOE_TRY(moe::launch_combine_backward(dout->data, Y, gate, slot, N, d, k, dY, ds, s,
+                                         o.drop));
     MOE_TRY(moe::launch_ds_split(ds, idx, N, Tc, S, Ei, k, dsT3, s));
     MOE_TRY(moe::launch_transpose_rows(x->data, d, Tc, nullptr, N, nullptr, k, 0, Tc, 3, (int)S,
                                        xT3, s));

@@ -316,3 +316,15 @@ def test_backward_ex_validates_the_expert_variant(L):
     assert bwd(opts()) == -5
     assert bwd(None) == -5
     assert st.capacity == -1
+
+
+def test_dropout_option_is_validated(L):
+    """The dropout probability of moe_expert_opts lies in [0, 1)."""
+    x, wg, wu, wd, out, st = _good(N=64, d=16, E=4, dff=32)
+    r = ctypes.byref
+    for p, want in ((1.0, -4), (-0.25, -4), (math.nan, -4), (1.5, -4), (math.inf, -4),
+                    (0.5, -5), (0.0, -5)):
+        o = B.MoeExpertOpts(B.MOE_ACT_RELU, None, None, p, 7, 1)
+        assert L.moe_forward_ex(r(x), r(wg), None, r(wu), r(wd), r(o), 2, 1.0, r(out),
+                                r(st)) == want, p
+    assert st.capacity == -1

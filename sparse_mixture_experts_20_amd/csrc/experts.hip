@@ -199,7 +199,9 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // row (MODE 1), or NULL. K-range partials take neither (the fix-up does).
 // Z16 (MODE 0, whole tiles only): when not NULL, the bf16 pre-activations
 // (product plus bias) are stored there too, [E, ceff, Nout] like H.
-// dp (MODE 1): training-mode dropout on the rows of Y, after the bias.
+// 5: MODE 1 with training-mode dropout dp on the rows of Y, after the bias
+// (its own instantiation: the generator's registers would make the plain
+// down product's epilogue spill).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BKT, int S, int MODE>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void expert_gemm_kernel(
@@ -488,7 +490,7 @@ void expert_gemm_kernel(
                     store_h(std::true_type{});
                 else
                     store_h(std::false_type{});
-            } else if (MODE == 1) {
+            } else if (MODE == 1 || MODE == 5) {
                 // bf16 row of Y at the assignment's position
                 const int64_t arow = (int64_t)slot_token[srow];
                 unsigned short *dst = O16 + arow * Nout + nb;
@@ -501,7 +503,7 @@ void expert_gemm_kernel(
                             z0 += *reinterpret_cast<const f32x4 *>(bp + 8 * h);
                             z1 += *reinterpret_cast<const f32x4 *>(bp + 8 * h + 4);
                         }
-                        if (dp.on) {
+                        if constexpr (MODE == 5) {
                             // columns nb + 8h .. +7 share one generator block
                             float m[8];
                             dropout_factors8(dp, arow, (nb + 8 * h) / 8, m);
@@ -767,7 +769,8 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
     const int64_t tmax = (int64_t)E * ((ceff + BM - 1) / BM) * ((Nout + BN - 1) / BN);
     // a split needs at least two ranges of kSplitMinSteps, at least one full
     // round of tiles and (by the 15% rule of split_plan) fewer than six
-    const bool split = (MODE == 0 || MODE == 1) && !Z16 && P > 0 && KT >= 2 * kSplitMinSteps &&
+    const bool split = (MODE == 0 || MODE == 1 || MODE == 5) && !Z16 && P > 0 &&
+                       KT >= 2 * kSplitMinSteps &&
                        tmax >= P && tmax < 6 * (int64_t)P;
     const int64_t grid = (tmax + kXcds - 1) / kXcds * kXcds +
                          (split ? (int64_t)(P + kXcds - 1) / kXcds * kXcds : 0);
@@ -778,7 +781,7 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !split)
         return err;
-    hipLaunchKernelGGL((split_fixup_kernel<BM, BN, kBK, MODE == 1 ? 1 : 0>),
+    hipLaunchKernelGGL((split_fixup_kernel<BM, BN, kBK, MODE == 0 ? 0 : 1>),
                        dim3((unsigned)(P * (BM / 16))),
                        dim3(256), 0, s, (int)K, (int)Nout, E, (int)ceff, used, slot_token, mt,
                        (const float *)part, P, O16, act, bias, dp);
@@ -859,12 +862,18 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
                               const float *b_down, hipStream_t s, Dropout dp) {
     if (ceff == 0)
         return hipSuccess;
+    if (bf16 && dp.on)
+        return launch_gemm<5>(pick_tile(rows_per_expert, d, E),
+                              static_cast<const unsigned short *>(H),
+                              static_cast<const unsigned short *>(w_down), d_ff, d, E, k, ceff,
+                              used, slot_token, tiles, static_cast<unsigned short *>(Y), part,
+                              part_bytes, kActRelu, b_down, s, nullptr, nullptr, nullptr, dp);
     if (bf16)
         return launch_gemm<1>(pick_tile(rows_per_expert, d, E),
                               static_cast<const unsigned short *>(H),
                               static_cast<const unsigned short *>(w_down), d_ff, d, E, k, ceff,
                               used, slot_token, tiles, static_cast<unsigned short *>(Y), part,
-                              part_bytes, kActRelu, b_down, s, nullptr, nullptr, nullptr, dp);
+                              part_bytes, kActRelu, b_down, s);
     hipLaunchKernelGGL(experts_f32_kernel<1>,
                        dim3((unsigned)((d + 63) / 64), (unsigned)((ceff + 63) / 64), E),
                        dim3(256), 0, s, static_cast<const float *>(H),

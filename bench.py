@@ -8,7 +8,9 @@ d_ff=3072, bf16, capacity factor 1.25, noise sigma 1.0).
 
 With --pass backward, one step is one moe_backward call instead (the
 forward state recomputed, then the gradients of x, W_g, W_up and W_down for
-a seeded output gradient), reported in the same JSON form.
+a seeded output gradient); with --pass train, one training step of the
+layer (moe_forward_train, which keeps the forward state, then
+moe_backward_after_forward). Both are reported in the same JSON form.
 
 Prints ONE JSON line on stdout. Besides the contract fields it carries:
   roofline      the dominant kernel (the larger of the two expert GEMMs)
@@ -166,9 +168,12 @@ def cpu_baseline_backward(wl, target_s=15.0):
     }
 
 
-def bench_backward(args, wl, dev):
+def bench_backward(args, wl, dev, train=False):
     """One step = one moe_backward call (forward state recomputed, then every
-    gradient) over the workload, with a seeded output gradient."""
+    gradient) over the workload, with a seeded output gradient; with
+    ``train``, one moe_forward_train + moe_backward_after_forward pair (a
+    training step's layer work: the forward keeps its state for the
+    backward)."""
     import numpy as np
     import torch
     from sparse_mixture_experts_20_amd import binding as B
@@ -178,8 +183,16 @@ def bench_backward(args, wl, dev):
         print("the backward pass runs on bf16 layers", file=sys.stderr)
         sys.exit(2)
     dout = torch.from_numpy(wl.dout().view(np.int16)).view(torch.bfloat16).to("cuda")
-    bwd = B.Backward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
-                     cfg.cf, dout, act=dev["act"], b_up=dev["b_up"], b_down=dev["b_down"])
+    if train:
+        ts = B.TrainStep(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
+                         cfg.cf, act=dev["act"], b_up=dev["b_up"], b_down=dev["b_down"])
+
+        def bwd():
+            ts.forward()
+            return ts.backward(dout)
+    else:
+        bwd = B.Backward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
+                         cfg.cf, dout, act=dev["act"], b_up=dev["b_up"], b_down=dev["b_down"])
     for _ in range(args.warmup):
         bwd()
     torch.cuda.synchronize()
@@ -202,7 +215,8 @@ def bench_backward(args, wl, dev):
     prod = 2.0 * kept * wl.d * wl.d_ff
     flops = 6 * prod + 2 * 2.0 * wl.N * wl.k * wl.d
     achieved = flops / (ms_per_step * 1e-3) / 1e12
-    log(f"[bench] backward {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall "
+    what = "train step" if train else "backward"
+    log(f"[bench] {what} {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall "
         f"{wall_ms * 1e3:.1f}, events {ev_ms * 1e3:.1f}); {achieved:.0f} TFLOP/s over the pass")
     cpu = None
     if not args.no_cpu_baseline:
@@ -210,7 +224,8 @@ def bench_backward(args, wl, dev):
         cpu = cpu_baseline_backward(wl)
         log(f"[bench] cpu_baseline {cpu['value']:.1f} tokens/s")
     line = {
-        "metric": "MoE-layer backward tokens/sec at 1 MI355X",
+        "metric": ("MoE-layer training step (forward + backward) tokens/sec at 1 MI355X"
+                   if train else "MoE-layer backward tokens/sec at 1 MI355X"),
         "value": round(wl.N / (ms_per_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -223,14 +238,18 @@ def bench_backward(args, wl, dev):
         "dtype": cfg.dtype,
         "data": "synthetic (seeded Gaussian inputs, output gradient and random-init weights)",
         "config": {
-            "workload": (cfg.description or cfg.name) + "; backward pass",
+            "workload": (cfg.description or cfg.name) + (
+                "; training step: forward keeping its state, then backward" if train
+                else "; backward pass"),
             "tokens": wl.N, "d": wl.d, "experts": wl.E, "top_k": wl.k, "d_ff": wl.d_ff,
             "capacity_factor": cfg.cf, "capacity": C, "noise_sigma": cfg.sigma,
             "seed": cfg.seed, "kept_assignments": kept, "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "moe_backward pass (6 expert products on the expert GEMM kernel + "
-                      "router gradient)",
+            "kernel": ("forward + backward (2 forward and 4 gradient expert products on the "
+                       "expert GEMM kernel + router gradient)" if train else
+                       "moe_backward pass (6 expert products on the expert GEMM kernel + "
+                       "router gradient)"),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -238,7 +257,9 @@ def bench_backward(args, wl, dev):
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": None,
             "algorithmic_per_launch": (f"6*2*kept*d*d_ff + 4*N*k*d = {flops:.4g} flop "
-                                       f"(kept={kept}; forward recomputed: 2 of the 6)"),
+                                       f"(kept={kept}; " + ("2 forward + 4 gradient products)"
+                                                            if train else
+                                                            "forward recomputed: 2 of the 6)")),
             "avg_launch_us": round(ms_per_step * 1e3, 2),
         },
         "cpu_baseline": cpu,
@@ -256,8 +277,10 @@ def main():
                     choices=["nanomoe", "mixtral", "skew", "finegrained", "tiny", "nanomoe_gelu"])
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
-                    help="time the layer's forward (default) or its backward pass")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "train"],
+                    default="forward",
+                    help="time the layer's forward (default), its backward pass, or a "
+                         "training step (forward keeping its state + backward)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -280,8 +303,8 @@ def main():
     log(f"[bench] workload {cfg.name}: N={wl.N} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff} "
         f"{cfg.dtype} cf={cfg.cf}")
     dev = D.upload(wl, keep_host=not args.no_cpu_baseline)
-    if args.which == "backward":
-        bench_backward(args, wl, dev)
+    if args.which in ("backward", "train"):
+        bench_backward(args, wl, dev, train=args.which == "train")
         return
     fwd = B.Forward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
                     cfg.cf, export=True, act=dev["act"],

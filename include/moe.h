@@ -317,6 +317,30 @@ int moe_backward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor
                     moe_tensor *dW_down, moe_tensor *db_up, moe_tensor *db_down,
                     moe_stats *stats);
 
+/* Training step without recomputation: moe_forward_train is moe_forward_ex
+ * for a bf16 layer (same arguments, same out bit for bit) that also leaves
+ * the forward state the backward needs (routing, dispatch plan, H, the
+ * experts' bf16 output rows and, for GELU, the pre-activations) in
+ * stats->workspace, which must hold moe_backward_workspace_size() bytes
+ * (and in stats' exported routing arrays when given).
+ * moe_backward_after_forward then takes moe_backward_ex's arguments and
+ * computes the same gradients from that state instead of recomputing it:
+ * pass the same inputs, options and moe_stats (workspace and exported
+ * arrays) as to the forward, with no other call on that workspace in
+ * between. The state serves one backward call (the GELU pre-activations are
+ * overwritten by dZ). For callers that keep activations between the passes
+ * of a training step; it saves the two recomputed expert products. */
+int moe_forward_train(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                      const moe_tensor *W_up, const moe_tensor *W_down,
+                      const moe_expert_opts *opts, int k, float capacity_factor, moe_tensor *out,
+                      moe_stats *stats);
+int moe_backward_after_forward(const moe_tensor *x, const moe_tensor *W_g,
+                               const moe_tensor *noise, const moe_tensor *W_up,
+                               const moe_tensor *W_down, const moe_expert_opts *opts, int k,
+                               float capacity_factor, const moe_tensor *dout, moe_tensor *dx,
+                               moe_tensor *dW_g, moe_tensor *dW_up, moe_tensor *dW_down,
+                               moe_tensor *db_up, moe_tensor *db_down, moe_stats *stats);
+
 /* Bytes of workspace moe_backward needs (0 on invalid sizes or a dtype
  * other than MOE_BF16). */
 size_t moe_backward_workspace_size(int64_t N, int64_t d, int64_t E, int64_t d_ff, int k,

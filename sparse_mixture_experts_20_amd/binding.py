@@ -24,7 +24,8 @@ EXPORTS = ("moe_forward", "moe_workspace_size", "moe_capacity", "moe_error_strin
            "moe_router", "moe_router_workspace_size", "moe_dispatch", "moe_experts",
            "moe_expert_up", "moe_expert_down", "moe_expert_workspace_size", "moe_combine",
            "moe_forward_ex", "moe_experts_ex", "moe_expert_up_ex", "moe_expert_down_ex",
-           "moe_backward", "moe_backward_ex", "moe_backward_workspace_size")
+           "moe_backward", "moe_backward_ex", "moe_backward_workspace_size",
+           "moe_forward_train", "moe_backward_after_forward")
 
 MOE_ACT_RELU, MOE_ACT_GELU = 0, 1
 ACTS = {"relu": MOE_ACT_RELU, "gelu": MOE_ACT_GELU}
@@ -92,6 +93,12 @@ def lib():
                                       ctypes.c_int, ctypes.c_float, _T, _T, _T, _T, _T, _T, _T,
                                       ctypes.POINTER(MoeStats)]
         L.moe_backward_ex.restype = ctypes.c_int
+        L.moe_backward_after_forward.argtypes = L.moe_backward_ex.argtypes
+        L.moe_backward_after_forward.restype = ctypes.c_int
+        L.moe_forward_train.argtypes = [_T, _T, _T, _T, _T, ctypes.POINTER(MoeExpertOpts),
+                                        ctypes.c_int, ctypes.c_float, _T,
+                                        ctypes.POINTER(MoeStats)]
+        L.moe_forward_train.restype = ctypes.c_int
         L.moe_backward_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int,
                                                   ctypes.c_float, ctypes.c_int32]
         L.moe_backward_workspace_size.restype = ctypes.c_size_t
@@ -389,6 +396,66 @@ class Backward:
         if rc != 0:
             raise MoeError(rc, "moe_backward")
         return self.dx, self.dW_g, self.dW_up, self.dW_down
+
+
+class TrainStep:
+    """``moe_forward_train`` + ``moe_backward_after_forward`` on one shared
+    workspace: ``forward()`` returns out and keeps the forward state,
+    ``backward(dout)`` returns (dx, dW_g, dW_up, dW_down[, db_up, db_down])
+    from it. Tensors, workspace and descriptors are built once."""
+
+    def __init__(self, x, W_g, noise, W_up, W_down, k, capacity_factor, stream=None,
+                 act="relu", b_up=None, b_down=None, dropout=None, export=False):
+        N, d = x.numel() // x.shape[-1], x.shape[-1]
+        E, d_ff = W_up.shape[0], W_up.shape[1]
+        dev = x.device
+        self.tensors = (x, W_g, noise, W_up, W_down, b_up, b_down)
+        self.out = torch.empty_like(x)
+        self.dx = torch.empty((N, d), dtype=torch.float32, device=dev)
+        self.dW_g = torch.empty((E, d), dtype=torch.float32, device=dev)
+        self.dW_up = torch.empty((E, d_ff, d), dtype=torch.float32, device=dev)
+        self.dW_down = torch.empty((E, d, d_ff), dtype=torch.float32, device=dev)
+        self.db_up = None if b_up is None else torch.empty((E, d_ff), dtype=torch.float32,
+                                                           device=dev)
+        self.db_down = None if b_down is None else torch.empty((E, d), dtype=torch.float32,
+                                                               device=dev)
+        self.workspace = alloc_workspace(
+            backward_workspace_size(N, d, E, d_ff, k, capacity_factor, x.dtype), dev)
+        self.idx = self.gate = self.slot = self.used = None
+        if export:
+            self.idx = torch.empty((N, k), dtype=torch.int32, device=dev)
+            self.gate = torch.empty((N, k), dtype=torch.float32, device=dev)
+            self.slot = torch.empty((N, k), dtype=torch.int32, device=dev)
+            self.used = torch.empty((E,), dtype=torch.int32, device=dev)
+        self.k, self.cf = k, capacity_factor
+        self._opts = ExpertOpts(act, b_up, b_down, dropout)
+        self._d = [desc(t) for t in (x, W_g, noise, W_up, W_down, self.out, self.dx, self.dW_g,
+                                     self.dW_up, self.dW_down, self.db_up, self.db_down)]
+        self._a = [_ref(a) for a in self._d]
+        self._dout = None
+        self.stats = MoeStats(_stream(stream), ctypes.c_void_p(self.workspace.data_ptr()),
+                              self.workspace.numel(), _ptr(self.idx), _ptr(self.gate),
+                              _ptr(self.slot), _ptr(self.used), -1)
+
+    def forward(self):
+        a = self._a
+        _check(lib().moe_forward_train(a[0], a[1], a[2], a[3], a[4], self._opts.ref(), self.k,
+                                       self.cf, a[5], ctypes.byref(self.stats)),
+               "moe_forward_train")
+        return self.out
+
+    def backward(self, dout):
+        if self._dout is None or self._dout[0] is not dout:
+            self._dout = (dout, desc(dout))
+        a = self._a
+        _check(lib().moe_backward_after_forward(
+            a[0], a[1], a[2], a[3], a[4], self._opts.ref(), self.k, self.cf,
+            ctypes.byref(self._dout[1]), a[6], a[7], a[8], a[9], a[10], a[11],
+            ctypes.byref(self.stats)), "moe_backward_after_forward")
+        g = (self.dx, self.dW_g, self.dW_up, self.dW_down)
+        if self.db_up is not None or self.db_down is not None:
+            g = g + (self.db_up, self.db_down)
+        return g
 
 
 def router_workspace_size(N: int, d: int, E: int, dtype: torch.dtype) -> int:

@@ -129,7 +129,7 @@ constexpr size_t kSplitWorkspaceBytes = (size_t)256 * 256 * 256 * sizeof(float);
 size_t split_workspace_bytes();
 // act: kActRelu or kActGelu (up product); b_up [E, d_ff] / b_down [E, d]
 // fp32 biases or NULL. Z (bf16 layers): when not NULL, the pre-activations
-// z = W_up x + b_up are stored there too, [E, ceff, d_ff] like H (no split).
+// z = W_up x + b_up are stored there too, [E, ceff, d_ff] like H.
 hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t d,
                             int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                             const int32_t *slot_token, const int32_t *tiles, void *H,

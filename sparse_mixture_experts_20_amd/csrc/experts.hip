@@ -197,8 +197,8 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // act: activation of the up product (kActRelu, kActGelu); bias: [E, Nout]
 // fp32 added to the product before the activation (MODE 0) or to the output
 // row (MODE 1), or NULL. K-range partials take neither (the fix-up does).
-// Z16 (MODE 0, whole tiles only): when not NULL, the bf16 pre-activations
-// (product plus bias) are stored there too, [E, ceff, Nout] like H.
+// Z16 (MODE 0): when not NULL, the bf16 pre-activations (product plus bias)
+// are stored there too, [E, ceff, Nout] like H (by the fix-up for cut tiles).
 // 5: MODE 1 with training-mode dropout dp on the rows of Y, after the bias
 // (its own instantiation: the generator's registers would make the plain
 // down product's epilogue spill).
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
     int K, int Nout, int E, int ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
     const float *__restrict__ part, int P, unsigned short *__restrict__ O16, int act,
-    const float *__restrict__ bias, Dropout dp) {
+    const float *__restrict__ bias, Dropout dp, unsigned short *__restrict__ Z16) {
     constexpr int STRIPS = BM / 16;
     __shared__ int s_mt[kMaxExperts + 1];
     for (int i = threadIdx.x; i <= E; i += 256)
@@ -614,6 +614,12 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
         }
         if (MODE == 0) {
             orow = srow;                              // the row of H
+            if (Z16) {                                // the pre-activations too
+                u32x2 pz;
+                pz[0] = (unsigned)f32_to_bf16_bits(v[0]) | ((unsigned)f32_to_bf16_bits(v[1]) << 16);
+                pz[1] = (unsigned)f32_to_bf16_bits(v[2]) | ((unsigned)f32_to_bf16_bits(v[3]) << 16);
+                *reinterpret_cast<u32x2 *>(Z16 + orow * Nout + n) = pz;
+            }
             if (act == kActGelu)
                 v = f32x4{gelu(v[0]), gelu(v[1]), gelu(v[2]), gelu(v[3])};
             else
@@ -769,7 +775,7 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
     const int64_t tmax = (int64_t)E * ((ceff + BM - 1) / BM) * ((Nout + BN - 1) / BN);
     // a split needs at least two ranges of kSplitMinSteps, at least one full
     // round of tiles and (by the 15% rule of split_plan) fewer than six
-    const bool split = (MODE == 0 || MODE == 1 || MODE == 5) && !Z16 && P > 0 &&
+    const bool split = (MODE == 0 || MODE == 1 || MODE == 5) && P > 0 &&
                        KT >= 2 * kSplitMinSteps &&
                        tmax >= P && tmax < 6 * (int64_t)P;
     const int64_t grid = (tmax + kXcds - 1) / kXcds * kXcds +
@@ -784,7 +790,7 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
     hipLaunchKernelGGL((split_fixup_kernel<BM, BN, kBK, MODE == 0 ? 0 : 1>),
                        dim3((unsigned)(P * (BM / 16))),
                        dim3(256), 0, s, (int)K, (int)Nout, E, (int)ceff, used, slot_token, mt,
-                       (const float *)part, P, O16, act, bias, dp);
+                       (const float *)part, P, O16, act, bias, dp, Z16);
     return hipGetLastError();
 }
 
@@ -842,7 +848,7 @@ hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t 
                               static_cast<const unsigned short *>(x),
                               static_cast<const unsigned short *>(w_up), d, d_ff, E, k, ceff,
                               used, slot_token, tiles, static_cast<unsigned short *>(H),
-                              Z ? nullptr : part, part_bytes, act, b_up, s, nullptr, nullptr,
+                              part, part_bytes, act, b_up, s, nullptr, nullptr,
                               static_cast<unsigned short *>(Z));
     if (Z)
         return hipErrorInvalidValue;   // pre-activations are kept for bf16 layers only

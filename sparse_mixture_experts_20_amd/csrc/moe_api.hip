@@ -71,7 +71,7 @@ Layout layout_of(const Dims &m) {
 // and the gradient intermediates.
 struct BwdLayout {
     size_t idx, gate, slot, used, tiles, slot_token, H, Y, dY, ds, dZ, dXa, WT, T1, T2, dsT3,
-        xT3, gpart, router, total;
+        xT3, gpart, router, part, total;
     int64_t Kp, Tc, S;
 };
 
@@ -116,6 +116,7 @@ BwdLayout bwd_layout_of(const Dims &m) {
     L.xT3 = o;        o += align_up((size_t)m.d * 3 * tok * 2);
     L.gpart = o;      o += align_up((size_t)(L.S * m.E * m.d) * 4);
     L.router = o;     o += router_bytes(m.N, m.d, m.E, m.dtype);
+    L.part = o;       o += expert_bytes(m.dtype);   // split scratch of the expert products
     L.total = o;
     return L;
 }
@@ -288,6 +289,15 @@ int check_expert_ws(const void *ws) {
 }
 
 }  // namespace
+
+// The forward state the backward needs, in the backward's workspace layout:
+// routing (into the exported arrays when given), dispatch plan, H, the
+// experts' bf16 output rows Y (bias and dropout applied) and, for GELU, the
+// bf16 pre-activations (in the dZ region, which the dZ product overwrites).
+static int forward_state(const BwdLayout &L, char *ws, const moe_tensor *x,
+                         const moe_tensor *W_g, const moe_tensor *noise, const moe_tensor *W_up,
+                         const moe_tensor *W_down, const ExpertOpts &o, const Dims &m,
+                         moe_stats *stats, hipStream_t s);
 
 extern "C" {
 
@@ -675,12 +685,15 @@ size_t moe_backward_workspace_size(int64_t N, int64_t d, int64_t E, int64_t d_ff
     return bwd_layout_of(m).total;
 }
 
-int moe_backward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
-                    const moe_tensor *W_up, const moe_tensor *W_down,
-                    const moe_expert_opts *opts, int k, float capacity_factor,
-                    const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g, moe_tensor *dW_up,
-                    moe_tensor *dW_down, moe_tensor *db_up, moe_tensor *db_down,
-                    moe_stats *stats) {
+// The backward; with `saved`, the forward state is the one a
+// moe_forward_train call left in the workspace (and in the exported routing
+// arrays) instead of being recomputed.
+static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                         const moe_tensor *W_up, const moe_tensor *W_down,
+                         const moe_expert_opts *opts, int k, float capacity_factor,
+                         const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g,
+                         moe_tensor *dW_up, moe_tensor *dW_down, moe_tensor *db_up,
+                         moe_tensor *db_down, moe_stats *stats, bool saved) {
     if (!stats || !W_up || !W_down || !dout)
         return MOE_ERR_NULL;
     int64_t N, d, E;
@@ -796,18 +809,12 @@ int moe_backward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor
     const int Ei = (int)E;
 
     // forward state: routing, plan, H and the experts' bf16 outputs
-    rc = router_checked(x, W_g, noise, N, d, E, k, idx, gate, ws + L.router, s);
-    if (rc != MOE_OK)
-        return rc;
-    MOE_TRY(moe::launch_dispatch(idx, N, Ei, k, ceff, slot, used, st, tiles, s));
-    // (GELU: the pre-activations go to the dZ buffer, which the dZ product
-    // then overwrites element by element)
     const bool gelu = o.act == moe::kActGelu;
-    MOE_TRY(moe::launch_expert_up(true, x->data, W_up->data, d, d_ff, Ei, k, ceff, used, st,
-                                  tiles, H, rpe, nullptr, 0, o.act, o.b_up, s,
-                                  gelu ? dZ : nullptr));
-    MOE_TRY(moe::launch_expert_down(true, H, W_down->data, d, d_ff, Ei, k, ceff, used, st, tiles,
-                                    Y, rpe, nullptr, 0, o.b_down, s, o.drop));
+    if (!saved) {
+        rc = forward_state(L, ws, x, W_g, noise, W_up, W_down, o, m, stats, s);
+        if (rc != MOE_OK)
+            return rc;
+    }
     // combine and softmax backward; router weights: dW_g = ds^T x, per token
     // chunk on the exact split of ds, then the chunks summed in order
     MOE_TRY(moe::launch_combine_backward(dout->data, Y, gate, slot, N, d, k, dY, ds, s,
@@ -846,6 +853,91 @@ int moe_backward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor
     return MOE_OK;
 }
 
+int moe_backward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                    const moe_tensor *W_up, const moe_tensor *W_down,
+                    const moe_expert_opts *opts, int k, float capacity_factor,
+                    const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g, moe_tensor *dW_up,
+                    moe_tensor *dW_down, moe_tensor *db_up, moe_tensor *db_down,
+                    moe_stats *stats) {
+    return backward_call(x, W_g, noise, W_up, W_down, opts, k, capacity_factor, dout, dx, dW_g,
+                         dW_up, dW_down, db_up, db_down, stats, false);
+}
+
+int moe_backward_after_forward(const moe_tensor *x, const moe_tensor *W_g,
+                               const moe_tensor *noise, const moe_tensor *W_up,
+                               const moe_tensor *W_down, const moe_expert_opts *opts, int k,
+                               float capacity_factor, const moe_tensor *dout, moe_tensor *dx,
+                               moe_tensor *dW_g, moe_tensor *dW_up, moe_tensor *dW_down,
+                               moe_tensor *db_up, moe_tensor *db_down, moe_stats *stats) {
+    return backward_call(x, W_g, noise, W_up, W_down, opts, k, capacity_factor, dout, dx, dW_g,
+                         dW_up, dW_down, db_up, db_down, stats, true);
+}
+
+int moe_forward_train(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
+                      const moe_tensor *W_up, const moe_tensor *W_down,
+                      const moe_expert_opts *opts, int k, float capacity_factor, moe_tensor *out,
+                      moe_stats *stats) {
+    if (!stats || !W_up || !W_down || !out)
+        return MOE_ERR_NULL;
+    int64_t N, d, E;
+    int rc = check_router_args(x, W_g, noise, k, N, d, E);
+    if (rc != MOE_OK)
+        return rc;
+    if (!cf_ok(capacity_factor))
+        return MOE_ERR_ARG;
+    if (x->dtype != MOE_BF16)
+        return MOE_ERR_UNSUPPORTED;   // training runs on bf16 layers
+    if (W_up->dtype != x->dtype || W_down->dtype != x->dtype || out->dtype != x->dtype)
+        return MOE_ERR_DTYPE;
+    if (W_up->ndim != 3 || W_down->ndim != 3)
+        return MOE_ERR_SHAPE;
+    const int64_t d_ff = W_up->shape[1];
+    if (W_up->shape[0] != E || W_up->shape[2] != d || W_down->shape[0] != E ||
+        W_down->shape[1] != d || W_down->shape[2] != d_ff)
+        return MOE_ERR_SHAPE;
+    ExpertOpts o;
+    rc = check_opts(opts, E, d, d_ff, o);
+    if (rc != MOE_OK)
+        return rc;
+    int64_t oN, od;
+    if (!act_rows(out, oN, od) || oN != N || od != d)
+        return MOE_ERR_SHAPE;
+    Dims m{N, d, E, d_ff, k, 0, 0, x->dtype};
+    m.C = capacity_of(N, E, k, capacity_factor);
+    m.ceff = m.C < N ? m.C : N;
+    rc = check_sizes(m);
+    if (rc != MOE_OK)
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stats->stream);
+    if (N == 0) {
+        stats->capacity = 0;
+        if (stats->used_capacity)
+            return hip_status(moe::launch_fill_i32(stats->used_capacity, E, 0, s));
+        return MOE_OK;
+    }
+    if (!W_up->data || !W_down->data || !out->data)
+        return MOE_ERR_NULL;
+    if (!stats->workspace)
+        return MOE_ERR_NULL;
+    if (!aligned(stats->workspace, kAlign))
+        return MOE_ERR_ALIGN;
+    if (!aligned(W_up->data, 16) || !aligned(W_down->data, 16) || !aligned(out->data, 16))
+        return MOE_ERR_ALIGN;
+    const BwdLayout L = bwd_layout_of(m);
+    if (stats->workspace_bytes < L.total)
+        return MOE_ERR_WORKSPACE;
+    stats->capacity = m.C;
+    char *ws = static_cast<char *>(stats->workspace);
+    rc = forward_state(L, ws, x, W_g, noise, W_up, W_down, o, m, stats, s);
+    if (rc != MOE_OK)
+        return rc;
+    const float *gate = stats->topk_gate ? stats->topk_gate
+                                         : reinterpret_cast<const float *>(ws + L.gate);
+    const int32_t *slot = stats->slot ? stats->slot : reinterpret_cast<const int32_t *>(ws + L.slot);
+    return hip_status(moe::launch_combine(ws + L.Y, 1, gate, slot, N, d, k, out->data,
+                                          out->dtype, s));
+}
+
 int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
                  const moe_tensor *W_up, const moe_tensor *W_down, int k, float capacity_factor,
                  const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g, moe_tensor *dW_up,
@@ -855,3 +947,34 @@ int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *n
 }
 
 }  // extern "C"
+
+static int forward_state(const BwdLayout &L, char *ws, const moe_tensor *x,
+                         const moe_tensor *W_g, const moe_tensor *noise, const moe_tensor *W_up,
+                         const moe_tensor *W_down, const ExpertOpts &o, const Dims &m,
+                         moe_stats *stats, hipStream_t s) {
+    int32_t *idx = stats->topk_idx ? stats->topk_idx : reinterpret_cast<int32_t *>(ws + L.idx);
+    float *gate = stats->topk_gate ? stats->topk_gate : reinterpret_cast<float *>(ws + L.gate);
+    int32_t *slot = stats->slot ? stats->slot : reinterpret_cast<int32_t *>(ws + L.slot);
+    int32_t *used = stats->used_capacity ? stats->used_capacity
+                                         : reinterpret_cast<int32_t *>(ws + L.used);
+    int32_t *tiles = reinterpret_cast<int32_t *>(ws + L.tiles);
+    int32_t *st = reinterpret_cast<int32_t *>(ws + L.slot_token);
+    const int Ei = (int)m.E;
+    const int64_t rpe = rows_per_expert(m.N, m.k, m.E, m.ceff);
+    int rc = router_checked(x, W_g, noise, m.N, m.d, m.E, m.k, idx, gate, ws + L.router, s);
+    if (rc != MOE_OK)
+        return rc;
+    MOE_TRY(moe::launch_dispatch(idx, m.N, Ei, m.k, m.ceff, slot, used, st, tiles, s));
+    const bool gelu = o.act == moe::kActGelu;
+    // (the same launch configuration as moe_forward_ex, split included, so
+    // the state and out are bit for bit the forward's)
+    void *part = ws + L.part;
+    const size_t part_bytes = L.total - L.part;
+    MOE_TRY(moe::launch_expert_up(true, x->data, W_up->data, m.d, m.d_ff, Ei, m.k, m.ceff, used,
+                                  st, tiles, ws + L.H, rpe, part, part_bytes, o.act, o.b_up, s,
+                                  gelu ? ws + L.dZ : nullptr));
+    MOE_TRY(moe::launch_expert_down(true, ws + L.H, W_down->data, m.d, m.d_ff, Ei, m.k, m.ceff,
+                                    used, st, tiles, ws + L.Y, rpe, part, part_bytes, o.b_down, s,
+                                    o.drop));
+    return MOE_OK;
+}

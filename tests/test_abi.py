@@ -328,3 +328,29 @@ def test_dropout_option_is_validated(L):
         assert L.moe_forward_ex(r(x), r(wg), None, r(wu), r(wd), r(o), 2, 1.0, r(out),
                                 r(st)) == want, p
     assert st.capacity == -1
+
+
+def test_train_entry_points_validate(L):
+    """moe_forward_train: bf16 only, the backward's workspace; and
+    moe_backward_after_forward validates like moe_backward_ex."""
+    x, wg, wu, wd, out, st = _good(N=64, d=16, E=4, dff=32)
+    r = ctypes.byref
+    assert L.moe_forward_train(r(x), r(wg), None, r(wu), r(wd), None, 2, 1.0, r(out),
+                               None) == -1
+    assert L.moe_forward_train(r(x), r(wg), None, r(wu), r(wd), None, 5, 1.0, r(out),
+                               r(st)) == -4
+    xf, wgf, wuf, wdf, outf, _ = _good(N=64, d=16, E=4, dff=32, dt=F32)
+    assert L.moe_forward_train(r(xf), r(wgf), None, r(wuf), r(wdf), None, 2, 1.0, r(outf),
+                               r(st)) == -6
+    assert L.moe_forward_train(r(x), r(wg), None, r(wu), r(wd), None, 2, 1.0, r(out),
+                               r(st)) == -5
+    g = (_t(FAKE, F32, 64, 16), _t(FAKE, F32, 4, 16), _t(FAKE, F32, 4, 32, 16),
+         _t(FAKE, F32, 4, 16, 32))
+    dout = _t(FAKE, BF16, 64, 16)
+    assert L.moe_backward_after_forward(r(x), r(wg), None, r(wu), r(wd), None, 2, 1.0, r(dout),
+                                        r(g[0]), r(g[1]), r(g[2]), r(g[3]), None, None,
+                                        r(st)) == -5
+    assert L.moe_backward_after_forward(r(x), r(wg), None, r(wu), r(wd), None, 2, 1.0,
+                                        r(_t(FAKE, F32, 64, 16)), r(g[0]), r(g[1]), r(g[2]),
+                                        r(g[3]), None, None, r(st)) == -3
+    assert st.capacity == -1

@@ -1,0 +1,134 @@
+"""The training step without recomputation: moe_forward_train followed by
+moe_backward_after_forward on one workspace.
+
+moe_forward_train runs the forward's kernels in the forward's launch
+configuration, so its output must equal moe_forward_ex's bit for bit, and
+the backward from the saved state must equal moe_backward_ex's (which
+recomputes the same state) bit for bit; moe_backward_ex itself is compared
+with the oracle in the backward tests, and here once more on a layer whose
+up product's last round of tiles is cut into K-ranges (GELU and biases: the
+fix-up then also writes the pre-activations the backward uses)."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_mixture_experts_20_amd import workloads as W
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_mod():
+    if not G.have_gpu():
+        pytest.skip("no HIP device")
+    import torch
+    from sparse_mixture_experts_20_amd import binding as B
+    B.lib()
+    return torch
+
+
+def _upload(wl):
+    import torch
+    from sparse_mixture_experts_20_amd import device as D
+    dev = D.upload(wl, keep_host=True)
+    dev["dout"] = torch.from_numpy(wl.dout().view(np.int16)).view(torch.bfloat16).to("cuda")
+    return dev
+
+
+def _drop(wl):
+    return (wl.cfg.dropout, wl.cfg.dropout_seed, wl.cfg.dropout_offset)
+
+
+def _kw(dev, wl):
+    return dict(act=dev["act"], b_up=dev["b_up"], b_down=dev["b_down"], dropout=_drop(wl))
+
+
+# name -> (N, d, E, k, d_ff, cf, seed, act, bias_std, dropout)
+CASES = {
+    "train_relu": (1000, 264, 16, 4, 392, 0.8, 501, "relu", 0.0, 0.0),
+    "train_gelu_bias": (700, 200, 6, 2, 328, 0.9, 502, "gelu", 0.05, 0.0),
+    "train_gelu_bias_dropout": (512, 64, 4, 2, 128, 0.3, 503, "gelu", 0.1, 0.2),
+    "train_one_token": (1, 64, 8, 2, 64, 1.0, 504, "relu", 0.0, 0.0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_train_step_equals_forward_and_backward(torch_mod, name):
+    torch = torch_mod
+    from sparse_mixture_experts_20_amd import binding as B
+    N, d, E, k, d_ff, cf, seed, act, bstd, p = CASES[name]
+    wl = W.custom(name, N=N, d=d, E=E, k=k, d_ff=d_ff, dtype="bf16", cf=cf, sigma=0.3,
+                  seed=seed, w_std=0.05, act=act, bias_std=bstd, dropout=p, dropout_seed=seed)
+    G.say(f"[train] {name}")
+    dev = _upload(wl)
+    args = (dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], k, cf)
+    out_ref, _ = B.forward(*args, **_kw(dev, wl))
+    g_ref = B.backward(*args, dev["dout"], **_kw(dev, wl))
+    step = B.TrainStep(*args, **_kw(dev, wl))
+    for _ in range(2):          # twice: the state is rebuilt by every forward
+        out = step.forward()
+        g = step.backward(dev["dout"])
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), out_ref.view(torch.int16))
+        assert len(g) == len(g_ref)
+        for a, b in zip(g, g_ref):
+            assert torch.equal(a, b)
+    if name == "train_gelu_bias":
+        # and against the oracle
+        wu = np.stack([wl.as_f64(wl.w_up(e)) for e in range(wl.E)])
+        wd = np.stack([wl.as_f64(wl.w_down(e)) for e in range(wl.E)])
+        ref = oracle.backward(wl.x64(), wl.wg64(), wl.noise64(), wu, wd, k, cf,
+                              wl.as_f64(wl.dout()), act=act, bup64=wl.b_up(),
+                              bdown64=wl.b_down())
+        for a, r in zip(g, ref):
+            a = G.to_np(a).astype(np.float64)
+            assert np.linalg.norm(a - r) / np.linalg.norm(r) <= 2e-2
+    del dev, step
+
+
+def test_backward_where_the_up_product_is_split(torch_mod):
+    """16 experts of ~600 rows, d = d_ff = 2048, GELU and biases: the up
+    product's last round of 256x256 tiles is cut into K-ranges, and the
+    fix-up writes the pre-activations. dx on sampled tokens and sampled
+    hidden units of two experts against the oracle; the train step equals
+    the recomputing backward bit for bit."""
+    torch = torch_mod
+    from sparse_mixture_experts_20_amd import binding as B
+    wl = W.custom("split_bwd", N=4800, d=2048, E=16, k=2, d_ff=2048, dtype="bf16", cf=1.25,
+                  sigma=0.5, seed=53, w_std=0.02, act="gelu", bias_std=0.05)
+    G.say("[train] split backward")
+    dev = _upload(wl)
+    args = (dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k, wl.cfg.cf)
+    g, st = B.backward(*args, dev["dout"], export=True, **_kw(dev, wl))
+    step = B.TrainStep(*args, **_kw(dev, wl))
+    step.forward()
+    g2 = step.backward(dev["dout"])
+    torch.cuda.synchronize()
+    for a, b in zip(g, g2):
+        assert torch.equal(a, b)
+    route = oracle.forward(wl, rows=[0])
+    G.check_routing(route, st)
+    x, wg, noise, dout = wl.x64(), wl.wg64(), wl.noise64(), wl.as_f64(wl.dout())
+    rng = np.random.default_rng(5)
+    rows = np.sort(rng.choice(wl.N, 24, replace=False))
+    wu = [wl.as_f64(wl.w_up(e)) for e in range(wl.E)]
+    wd = [wl.as_f64(wl.w_down(e)) for e in range(wl.E)]
+    ref = oracle.backward_rows(x, wg, noise, wu, wd, wl.k, wl.cfg.cf, dout, rows, act="gelu",
+                               bup64=wl.b_up(), bdown64=wl.b_down())
+    got = G.to_np(g[0])[rows].astype(np.float64)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    G.say(f"    dx[rows]: rel_l2={rel:.2e}")
+    assert rel <= 2e-2
+    for e in (wl.E - 1, 0):
+        fs = np.sort(rng.choice(wl.d_ff, 4, replace=False))
+        up, down = oracle.backward_expert_units(x, wg, noise, e, wu[e], wd[e], wl.k, wl.cfg.cf,
+                                                dout, fs, act="gelu", bup_e64=wl.b_up()[e])
+        idx = torch.from_numpy(fs).to("cuda")
+        gu = G.to_np(g[2][e].index_select(0, idx)).astype(np.float64)
+        gd = G.to_np(g[3][e].index_select(1, idx).t().contiguous()).astype(np.float64)
+        for nm, a, r in (("dW_up", gu, up), ("dW_down", gd, down)):
+            rel = np.linalg.norm(a - r) / np.linalg.norm(r)
+            G.say(f"    {nm}[{e}] units: rel_l2={rel:.2e}")
+            assert rel <= 2e-2
+    del dev, step

@@ -142,17 +142,18 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
                               int64_t rows_per_expert, void *part, size_t part_bytes,
                               const float *b_down, hipStream_t s, Dropout dp = Dropout{});
 
-// Backward products over the dispatch plan (bf16 operands, fp32 accumulate):
-// dZ[e, r, :] = (dY[slot_token[e, r]] W_down[e]) * act'(z[e, r, :]), with
-// W_down transposed ([E, d_ff, d]), bf16 into [E, ceff, d_ff]; act_in is H
-// for ReLU (act' = [H > 0]) and the stored pre-activations Z for GELU;
-// out[slot_token[e, r], :] = A[e, r, :] W_t[e]^T (A dense [E, ceff, K], W_t
-// [E, Nout, K]), fp32.
-hipError_t launch_expert_dz(const void *dY, const void *w_down_t, const void *act_in, int act,
+// Backward products over the dispatch plan (bf16 operands, fp32 accumulate;
+// the weights are read K-major, as stored):
+// dZ[e, r, :] = (dY[slot_token[e, r]] W_down[e]) * act'(z[e, r, :]), W_down
+// [E, d, d_ff], bf16 into [E, ceff, d_ff]; act_in is H for ReLU
+// (act' = [H > 0]) and the stored pre-activations Z for GELU;
+// out[slot_token[e, r], :] = A[e, r, :] W[e] (A dense [E, ceff, K], W
+// [E, K, Nout]), fp32.
+hipError_t launch_expert_dz(const void *dY, const void *w_down, const void *act_in, int act,
                             int64_t d, int64_t d_ff, int E, int k, int64_t ceff,
                             const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
                             void *dZ, int64_t rows_per_expert, hipStream_t s);
-hipError_t launch_expert_rows_f32(const void *A, const void *w_t, int64_t K, int64_t Nout, int E,
+hipError_t launch_expert_rows_f32(const void *A, const void *w, int64_t K, int64_t Nout, int E,
                                   int k, int64_t ceff, const int32_t *used,
                                   const int32_t *slot_token, const int32_t *tiles, float *out,
                                   int64_t rows_per_expert, hipStream_t s);

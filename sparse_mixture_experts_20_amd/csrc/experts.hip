@@ -61,6 +61,28 @@ __device__ __forceinline__ unsigned lds_off(const void *p) {
     return (unsigned)(uintptr_t)((__attribute__((address_space(3))) const void *)p);
 }
 
+// A K-major operand tile ([BKT rows of K][BN columns], 16-byte chunks) keeps
+// chunk c of row r at position c ^ tr_swizzle(r): the 16 rows one transposing
+// read touches (4 rows in each of 4 lane groups, rows 8g + 4h + 0..3) take 8
+// distinct even offsets (4 in rows of 8 chunks), so its 64 lanes hit every
+// bank at most twice.
+__device__ __forceinline__ int tr_swizzle(int r, int chunks_per_row) {
+    const int h = (r & 3) | ((((r >> 3) ^ (r >> 2)) & 1) << 2);
+    return (2 * h) & (chunks_per_row - 1);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16
+// lanes, lane l receives element l % 4 of the 8 bytes that lane
+// 4q + l / 4 addresses, as its element q (q = 0..3). With lane s of a group
+// addressing row kb + s / 4, columns 4 (s % 4) .. +3 of a K-major tile,
+// lane l gets column l of rows kb .. kb + 3: a quarter of an MFMA operand
+// fragment.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i16 lds_read_tr16(const void *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(p));
+}
+
 // GELU of the nanoMoE slides' expert (slide 32): z * Phi(z), Phi(z) =
 // (1 + erf(z / sqrt 2)) / 2, with erf from Abramowitz and Stegun, Handbook of
 // Mathematical Functions, formula 7.1.26: for u >= 0,
@@ -187,11 +209,15 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // bsa, bsb, bsc of A, W and O32;
 // 3: backward of the down product through the activation, dZ = (dY W_down)
 // times act'(z): A rows are assignment rows of dY gathered by slot_token, W
-// is W_down transposed, bf16 [E, ceff, Nout] into O16; for ReLU mask = H
+// is W_down, bf16 [E, ceff, Nout] into O16; for ReLU mask = H
 // (act' = [H > 0]), for GELU mask = the stored pre-activations Z, which may
 // be O16 itself (each element is read before the same thread overwrites it);
-// 4: backward of the up product, dX = dZ W_up: A rows dense like MODE 1, W
-// is W_up transposed, fp32 rows scattered to their assignment into O32.
+// 4: backward of the up product, dX = dZ W_up: A rows dense like MODE 1,
+// fp32 rows scattered to their assignment into O32.
+// In modes 3 and 4 the right operand is the weight matrix itself, read
+// K-major: W[e] is [K][Nout] (Nout contiguous: W_down for MODE 3, W_up for
+// MODE 4); its tiles are staged row by row and turned into MFMA fragments
+// by transposing LDS reads.
 // part: scratch for the split of the last round (NULL: no split), P: the
 // number of workgroups of this kernel that fit on the device at once.
 // act: activation of the up product (kActRelu, kActGelu); bias: [E, Nout]
@@ -303,12 +329,28 @@ void expert_gemm_kernel(
                                         : srow;
         ga[i] = A_src + src * K;
     }
+    // K-major right operand: per op, the LDS row (k within the K-step) and a
+    // pointer to its 8 columns in row 0 of W[e]; columns past Nout read the
+    // last 8 (never stored), rows past K read row K - 1 (A's K tail is 0)
+    constexpr bool BT = MODE == 3 || MODE == 4;
+    constexpr int RBT = BN * 2, CPRT = BN / 8;   // bytes, 16-byte chunks per K-major row
+    int bk[BT ? IB : 1];
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
-        const int row = (wv * IB + i) * RPI + lane / CPR;
-        cb[i] = (lane % CPR) ^ ((row / RPB) % CPR);
-        const int n = n0 + row;
-        gb[i] = W + ((int64_t)e * Nout + (n < Nout ? n : 0)) * K;
+        if constexpr (BT) {
+            const int q = (wv * IB + i) * 64 + lane;        // 16-byte slot in the tile
+            const int row = q / CPRT;
+            const int c = (q % CPRT) ^ tr_swizzle(row, CPRT);
+            const int n = n0 + 8 * c;
+            bk[i] = row;
+            cb[i] = 0;
+            gb[i] = W + (int64_t)e * K * Nout + (n < Nout ? n : Nout - 8);
+        } else {
+            const int row = (wv * IB + i) * RPI + lane / CPR;
+            cb[i] = (lane % CPR) ^ ((row / RPB) % CPR);
+            const int n = n0 + row;
+            gb[i] = W + ((int64_t)e * Nout + (n < Nout ? n : 0)) * K;
+        }
     }
     const unsigned smem_off = lds_off(smem);
     auto issue = [&](int kt) {
@@ -320,8 +362,14 @@ void expert_gemm_kernel(
         }
 #pragma unroll
         for (int i = 0; i < IB; ++i) {
-            const int kk = min(kt * BKT + cb[i] * 8, K - 8);
-            dma16(base + (unsigned)(BM * RB + (wv * IB + i) * 1024), gb[i] + kk);
+            if constexpr (BT) {
+                const int kr = min(kt * BKT + bk[i], K - 1);
+                dma16(base + (unsigned)(BM * RB + (wv * IB + i) * 1024),
+                      gb[i] + (int64_t)kr * Nout);
+            } else {
+                const int kk = min(kt * BKT + cb[i] * 8, K - 8);
+                dma16(base + (unsigned)(BM * RB + (wv * IB + i) * 1024), gb[i] + kk);
+            }
         }
     };
 
@@ -350,9 +398,30 @@ void expert_gemm_kernel(
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             af[i] = *reinterpret_cast<const bf16x8 *>(As + (ra0 + i * 16) * RB + ((c ^ xa) << 4));
+        if constexpr (BT) {
+            // rows ks*32 + 8g + 4h + s/4 (g = lane group, h = half), columns
+            // 4 (s % 4) .. +3 of this lane's 16-column block j
+            const int s4 = lane & 15;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            bfr[j] = *reinterpret_cast<const bf16x8 *>(Bs + (rb0 + j * 16) * RB + ((c ^ xb) << 4));
+            for (int j = 0; j < FN; ++j) {
+                const int col = wn * WTN + j * 16 + 4 * (s4 & 3);
+                v4i16 q[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = ks * 32 + 8 * (lane >> 4) + 4 * h + (s4 >> 2);
+                    const int ch = (col >> 3) ^ tr_swizzle(row, CPRT);
+                    q[h] = lds_read_tr16(Bs + row * RBT + ch * 16 + (col & 7) * 2);
+                }
+                const v4i16 lo = q[0], hi = q[1];
+                bfr[j] = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8 *>(Bs + (rb0 + j * 16) * RB +
+                                                           ((c ^ xb) << 4));
+        }
     };
     auto mma = [&](const bf16x8 (&af)[FM], const bf16x8 (&bfr)[FN], auto full) {
 #pragma unroll
@@ -375,14 +444,20 @@ void expert_gemm_kernel(
             mma(af[ks & 1], bfr[ks & 1], full);
         }
     };
-    // zero the chunks of the last K-tile that lie past K (both operands)
+    // zero the chunks of the last K-tile that lie past K (both operands; a
+    // K-major right operand: its rows past K)
     auto zero_tail = [&](int kt) {
         char *st = smem + (kt % S) * STAGE;
-        for (int q = tid; q < (BM + BN) * CPR; q += NTHR) {
+        for (int q = tid; q < (BT ? BM : BM + BN) * CPR; q += NTHR) {
             const int row = q / CPR, c = q % CPR;
             if (kt * BKT + c * 8 >= K)
                 *reinterpret_cast<u32x4 *>(st + row * RB + ((c ^ ((row / RPB) % CPR)) << 4)) =
                     u32x4{0u, 0u, 0u, 0u};
+        }
+        if constexpr (BT) {
+            for (int q = tid; q < BKT * CPRT; q += NTHR)
+                if (kt * BKT + q / CPRT >= K)
+                    *reinterpret_cast<u32x4 *>(st + BM * RB + q * 16) = u32x4{0u, 0u, 0u, 0u};
         }
     };
 
@@ -891,7 +966,7 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
 
 // ---- backward-pass products (bf16 operands, fp32 accumulation) ----------
 
-hipError_t launch_expert_dz(const void *dY, const void *w_down_t, const void *act_in, int act,
+hipError_t launch_expert_dz(const void *dY, const void *w_down, const void *act_in, int act,
                             int64_t d, int64_t d_ff, int E, int k, int64_t ceff,
                             const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
                             void *dZ, int64_t rows_per_expert, hipStream_t s) {
@@ -899,12 +974,12 @@ hipError_t launch_expert_dz(const void *dY, const void *w_down_t, const void *ac
         return hipSuccess;
     return launch_gemm<3>(pick_tile(rows_per_expert, d_ff, E),
                           static_cast<const unsigned short *>(dY),
-                          static_cast<const unsigned short *>(w_down_t), d, d_ff, E, k, ceff,
+                          static_cast<const unsigned short *>(w_down), d, d_ff, E, k, ceff,
                           used, slot_token, tiles, static_cast<unsigned short *>(dZ), nullptr, 0,
                           act, nullptr, s, static_cast<const unsigned short *>(act_in));
 }
 
-hipError_t launch_expert_rows_f32(const void *A, const void *w_t, int64_t K, int64_t Nout, int E,
+hipError_t launch_expert_rows_f32(const void *A, const void *w, int64_t K, int64_t Nout, int E,
                                   int k, int64_t ceff, const int32_t *used,
                                   const int32_t *slot_token, const int32_t *tiles, float *out,
                                   int64_t rows_per_expert, hipStream_t s) {
@@ -912,7 +987,7 @@ hipError_t launch_expert_rows_f32(const void *A, const void *w_t, int64_t K, int
         return hipSuccess;
     return launch_gemm<4>(pick_tile(rows_per_expert, Nout, E),
                           static_cast<const unsigned short *>(A),
-                          static_cast<const unsigned short *>(w_t), K, Nout, E, k, ceff, used,
+                          static_cast<const unsigned short *>(w), K, Nout, E, k, ceff, used,
                           slot_token, tiles, nullptr, nullptr, 0, kActRelu, nullptr, s, nullptr,
                           out);
 }

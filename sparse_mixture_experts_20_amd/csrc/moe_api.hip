@@ -70,7 +70,7 @@ Layout layout_of(const Dims &m) {
 // Workspace of the backward pass (bf16 layers): the recomputed forward state
 // and the gradient intermediates.
 struct BwdLayout {
-    size_t idx, gate, slot, used, tiles, slot_token, H, Y, dY, ds, dZ, dXa, WT, T1, T2, dsT3,
+    size_t idx, gate, slot, used, tiles, slot_token, H, Y, dY, ds, dZ, dXa, T1, T2, dsT3,
         xT3, gpart, router, part, total;
     int64_t Kp, Tc, S;
 };
@@ -109,7 +109,6 @@ BwdLayout bwd_layout_of(const Dims &m) {
     L.ds = o;         o += align_up(nk * 4);
     L.dZ = o;         o += align_up((size_t)(m.E * m.ceff * m.d_ff) * 2);
     L.dXa = o;        o += align_up(nk * (size_t)m.d * 4);
-    L.WT = o;         o += align_up((size_t)(m.E * m.d * m.d_ff) * 2);
     L.T1 = o;         o += align_up((size_t)(m.E * m.d * L.Kp) * 2);
     L.T2 = o;         o += align_up((size_t)(m.E * m.d_ff * L.Kp) * 2);
     L.dsT3 = o;       o += align_up((size_t)m.E * 3 * tok * 2);
@@ -799,7 +798,7 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
                                          : reinterpret_cast<int32_t *>(ws + L.used);
     int32_t *tiles = reinterpret_cast<int32_t *>(ws + L.tiles);
     int32_t *st = reinterpret_cast<int32_t *>(ws + L.slot_token);
-    void *H = ws + L.H, *Y = ws + L.Y, *dY = ws + L.dY, *dZ = ws + L.dZ, *WT = ws + L.WT;
+    void *H = ws + L.H, *Y = ws + L.Y, *dY = ws + L.dY, *dZ = ws + L.dZ;
     void *T1 = ws + L.T1, *T2 = ws + L.T2, *dsT3 = ws + L.dsT3, *xT3 = ws + L.xT3;
     float *ds = reinterpret_cast<float *>(ws + L.ds);
     float *dXa = reinterpret_cast<float *>(ws + L.dXa);
@@ -826,14 +825,11 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
                                           d * 3 * Tc, E * d, gpart, s));
     MOE_TRY(moe::launch_chunk_sum(gpart, S, E * d, static_cast<float *>(dW_g->data), s));
     // experts, input side: dZ = (dY W_down) [H > 0]; dX = dZ W_up; dx
-    MOE_TRY(moe::launch_transpose_rows(W_down->data, d_ff, d, nullptr, E * d, nullptr, k, 0, d, 1,
-                                       Ei, WT, s));
-    MOE_TRY(moe::launch_expert_dz(dY, WT, gelu ? dZ : H, o.act, d, d_ff, Ei, k, ceff, used, st,
-                                  tiles, dZ, rpe, s));
-    MOE_TRY(moe::launch_transpose_rows(W_up->data, d, d_ff, nullptr, E * d_ff, nullptr, k, 0,
-                                       d_ff, 1, Ei, WT, s));
-    MOE_TRY(moe::launch_expert_rows_f32(dZ, WT, d_ff, d, Ei, k, ceff, used, st, tiles, dXa, rpe,
-                                        s));
+    // (the weights are read K-major by the products themselves)
+    MOE_TRY(moe::launch_expert_dz(dY, W_down->data, gelu ? dZ : H, o.act, d, d_ff, Ei, k, ceff,
+                                  used, st, tiles, dZ, rpe, s));
+    MOE_TRY(moe::launch_expert_rows_f32(dZ, W_up->data, d_ff, d, Ei, k, ceff, used, st, tiles,
+                                        dXa, rpe, s));
     MOE_TRY(moe::launch_dx(dXa, ds, idx, slot, static_cast<const float *>(W_g->data), N, d, k,
                            static_cast<float *>(dx->data), s));
     // experts, weight side: dW_down = dY^T H, dW_up = dZ^T X (K = kept rows)

@@ -334,6 +334,7 @@ void expert_gemm_kernel(
     // last 8 (never stored), rows past K read row K - 1 (A's K tail is 0)
     constexpr bool BT = MODE == 3 || MODE == 4;
     constexpr int RBT = BN * 2, CPRT = BN / 8;   // bytes, 16-byte chunks per K-major row
+    static_assert(!BT || (BN & (BN - 1)) == 0, "K-major tiles are a power of two wide");
     int bk[BT ? IB : 1];
 #pragma unroll
     for (int i = 0; i < IB; ++i) {

@@ -196,7 +196,8 @@ def test_nanomoe_backward_sampled_rows(torch_mod, name):
     del dev
 
 
-@pytest.mark.parametrize("name,nunits", [("nanomoe", 6), ("mixtral", 4), ("nanomoe_gelu", 6)])
+@pytest.mark.parametrize("name,nunits", [("nanomoe", 6), ("mixtral", 4), ("nanomoe_gelu", 6),
+                                         ("skew", 4), ("finegrained", 4)])
 def test_benchmark_layer_weight_gradients_sampled(torch_mod, name, nunits):
     """The benchmark's layer shapes in the launch configuration the backward
     benchmark times: routing for every token, and for two experts (the most

@@ -1,6 +1,7 @@
-// C ABI of the MoE layer forward: argument validation, workspace layout and
-// the order of the stages (router -> dispatch plan -> grouped expert FFN ->
-// combine). Every check runs on the host before anything is enqueued.
+// C ABI of the MoE layer: argument validation, workspace layouts and the
+// order of the stages of the forward (router -> dispatch plan -> grouped
+// expert FFN -> combine) and of the backward. Every check runs on the host
+// before anything is enqueued.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>

@@ -84,6 +84,7 @@ CASES = {
     "bwd_row_tiles": (1024, 256, 4, 2, 512, 1.0, 0.5, 0.0, 303),
     "bwd_heavy_drop": (512, 64, 4, 2, 128, 0.1, 0.0, 5.0, 304),
     "bwd_many_experts": (300, 128, 256, 8, 96, 2.0, 0.0, 0.0, 305),
+    "bwd_max_top_k": (200, 64, 64, 16, 72, 0.7, 0.2, 0.0, 310),
     "bwd_k1": (200, 64, 3, 1, 64, 1.0, 0.0, 0.0, 306),
     "bwd_k_equals_E": (100, 32, 4, 4, 48, 1.0, 0.0, 0.0, 307),
     "bwd_single_token": (1, 64, 8, 2, 64, 1.0, 0.0, 0.0, 308),

@@ -47,6 +47,8 @@ SMALL = {
     "mid_bf16": (1536, 512, 8, 2, 1024, "bf16", 1.25, 1.0, 0.0, 104),
     "k1_bf16": (200, 64, 3, 1, 64, "bf16", 1.0, 0.0, 0.0, 105),
     "k_equals_E_bf16": (100, 32, 4, 4, 48, "bf16", 1.0, 0.0, 0.0, 106),
+    "max_top_k_bf16": (200, 64, 64, 16, 72, "bf16", 0.7, 0.2, 0.0, 112),
+    "max_top_k_f32": (40, 24, 20, 16, 40, "f32", 1.0, 0.2, 0.0, 113),
     "ragged_f32": (77, 13, 6, 3, 21, "f32", 0.7, 0.5, 0.0, 107),
     "heavy_drop_bf16": (512, 64, 4, 2, 128, "bf16", 0.1, 0.0, 5.0, 108),
     "single_token_bf16": (1, 64, 8, 2, 64, "bf16", 1.0, 0.0, 0.0, 109),

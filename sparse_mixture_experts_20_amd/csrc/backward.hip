@@ -141,6 +141,44 @@ __global__ __launch_bounds__(256) void chunk_sum_kernel(const float *__restrict_
     out[i] = acc;
 }
 
+// Column sums of an expert's rows: out[e][c] = sum over r < used[e] of
+// src[row(e, r)][c]. A block takes 512 columns (8 per lane) of one expert;
+// its four waves sum contiguous quarters of the rows in order, then the
+// quarters are added in order, so the result does not depend on timing.
+__global__ __launch_bounds__(256) void colsum_rows_kernel(
+    const unsigned short *__restrict__ src, int C, int64_t ceff, const int32_t *__restrict__ used,
+    const int32_t *__restrict__ slot_token, int kdiv, float *__restrict__ out) {
+    __shared__ float part[4][512];
+    const int e = blockIdx.y;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c0 = blockIdx.x * 512 + lane * 8;
+    const int R = used[e];
+    const int r0 = (int)((int64_t)R * w / 4), r1 = (int)((int64_t)R * (w + 1) / 4);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c0 < C) {
+#pragma unroll 4
+        for (int r = r0; r < r1; ++r) {
+            const int64_t sr = (int64_t)e * ceff + r;
+            const int64_t row = slot_token ? (int64_t)(slot_token[sr] / kdiv) : sr;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(src + row * C + c0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += __uint_as_float(v[q] << 16);
+                acc[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        part[w][lane * 8 + q] = acc[q];
+    __syncthreads();
+    for (int i = threadIdx.x; i < 512; i += 256) {
+        const int c = blockIdx.x * 512 + i;
+        if (c < C)
+            out[(int64_t)e * C + c] = ((part[0][i] + part[1][i]) + part[2][i]) + part[3][i];
+    }
+}
+
 // out[i] = sum of the Kp bf16 values of row i of T (one wave per row; lane
 // partial sums over a fixed stride, then a fixed butterfly).
 __global__ __launch_bounds__(256) void row_sums_kernel(const unsigned short *__restrict__ T,
@@ -287,6 +325,19 @@ hipError_t launch_row_sums(const void *T, int64_t rows, int64_t Kp, float *out, 
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(row_sums_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
                        static_cast<const unsigned short *>(T), rows, (int)Kp, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_colsum_rows(const void *src, int64_t C, int E, int64_t ceff,
+                              const int32_t *used, const int32_t *slot_token, int kdiv,
+                              float *out, hipStream_t s) {
+    if (C == 0 || E == 0)
+        return hipSuccess;
+    if (C % 8 != 0 || kdiv < 1)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(colsum_rows_kernel, dim3((unsigned)((C + 511) / 512), (unsigned)E),
+                       dim3(256), 0, s, static_cast<const unsigned short *>(src), (int)C, ceff,
+                       used, slot_token, kdiv, out);
     return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxQ = kMaxExperts / kWave;   // router scores per lane
 constexpr int kFusedMaxExperts = 32;          // larger routers use the GEMM path
 constexpr int kActRelu = 0, kActGelu = 1;     // expert activations (values of the C ABI)
+constexpr int kGradMaxRows = 3072;            // rows per expert of the K-major weight gradients
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -157,6 +158,15 @@ hipError_t launch_expert_rows_f32(const void *A, const void *w, int64_t K, int64
                                   int k, int64_t ceff, const int32_t *used,
                                   const int32_t *slot_token, const int32_t *tiles, float *out,
                                   int64_t rows_per_expert, hipStream_t s);
+// Weight gradient of every expert, O[e] (fp32 [M, N]) = sum over the
+// expert's kept rows r < used[e] of A_r^T B_r, where A_r (M wide) and B_r (N
+// wide) are rows of A and B: the gathered one (gathered == 0: A, 1: B) at
+// slot_token[e*ceff + r] / kdiv, the other at e*ceff + r. Both operands are
+// read K-major (no transposes). Needs ceff <= kGradMaxRows and M, N
+// multiples of 8.
+hipError_t launch_weight_grad(const void *A, int64_t M, const void *B, int64_t N, int E,
+                              int64_t ceff, const int32_t *used, const int32_t *slot_token,
+                              int kdiv, int gathered, float *out, hipStream_t s);
 // C[b] (fp32 [M, Nout]) = A[b] [M, K] * W[b] [Nout, K]^T for b < batch, with
 // element strides sa, sb, sc between batches; bf16 operands, K % 8 == 0.
 hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int64_t K,
@@ -174,6 +184,12 @@ hipError_t launch_combine_backward(const void *dout, const void *Y, const float 
 // i, Tc + i, 2*Tc + i (tokens chunked by Tc).
 hipError_t launch_ds_split(const float *ds, const int32_t *idx, int64_t N, int64_t Tc, int64_t S,
                            int E, int k, void *dsT3, hipStream_t s);
+// out[e][c] = sum over r < used[e] of src[row(e, r)][c] (bf16 rows of C
+// columns, fp32 sums in a fixed order): row(e, r) = slot_token[e*ceff + r] /
+// kdiv when slot_token is given, else e*ceff + r. C % 8 == 0.
+hipError_t launch_colsum_rows(const void *src, int64_t C, int E, int64_t ceff,
+                              const int32_t *used, const int32_t *slot_token, int kdiv,
+                              float *out, hipStream_t s);
 // out[i] = sum over r < Kp (fixed order) of T[i * Kp + r], bf16 T, fp32 out.
 hipError_t launch_row_sums(const void *T, int64_t rows, int64_t Kp, float *out, hipStream_t s);
 // out[i] = sum over s < S (in order) of part[s * n + i].

@@ -228,6 +228,12 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // 5: MODE 1 with training-mode dropout dp on the rows of Y, after the bias
 // (its own instantiation: the generator's registers would make the plain
 // down product's epilogue spill).
+// 6: weight gradient of expert e = blockIdx.y, O32[e] (fp32 [M, Nout]) =
+// sum over the expert's kept rows r < used[e] of A(r, :)^T B(r, :): both
+// operands K-major rows, A rows of width M = bsa, B rows of width Nout; the
+// row of r is slot_token[e*ceff + r] / k for the gathered operand (act == 0:
+// A, act == 1: B) and e*ceff + r for the other; bsc = M*Nout. K is unused
+// (each expert's K is used[e]; kGradMaxRows bounds ceff).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BKT, int S, int MODE>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void expert_gemm_kernel(
@@ -252,17 +258,42 @@ void expert_gemm_kernel(
     static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile/waves mismatch");
     static_assert(WTM % 16 == 0 && WTN % 32 == 0, "16x16 MFMA tiles; 4 lanes x 8k columns per row");
     static_assert(NW * 16 * (WTN + 4) * 4 <= S * STAGE, "epilogue scratch");
-    __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+    __shared__ __attribute__((aligned(1024)))
+    char smem[S * STAGE + (MODE == 6 ? kGradMaxRows * 4 : 0)];
     __shared__ int s_mt[kMaxExperts + 1];
+    int *s_rows = reinterpret_cast<int *>(smem + S * STAGE);   // MODE 6: row of each r
 
     const int tid = threadIdx.x;
     const int NT = (Nout + BN - 1) / BN;
-    const int KT = (K + BKT - 1) / BKT;
+    int Kr = K;            // reduction length (MODE 6: the expert's kept rows)
+    int KT = (K + BKT - 1) / BKT;
     const int b = blockIdx.x;
     int e, m0, n0, rows;
     int kb = 0, ke = KT;   // K-steps of this workgroup
     int piece = -1;        // scratch slot of a K-range, or -1 for a whole tile
-    if constexpr (MODE == 2) {
+    if constexpr (MODE == 6) {
+        e = blockIdx.y;
+        const int M = (int)bsa;
+        O32 += (int64_t)e * bsc;
+        const int mte = (M + BM - 1) / BM;
+        const int T = mte * NT;
+        const int T8 = (T + kXcds - 1) / kXcds * kXcds;
+        if (b >= T8)
+            return;
+        const int L = xcd_index(b, T8);
+        if (L >= T)
+            return;
+        rows = M;
+        m0 = (L % mte) * BM;
+        n0 = (L / mte) * BN;
+        Kr = used[e];
+        KT = (Kr + BKT - 1) / BKT;
+        ke = KT;
+        const int32_t *stp = slot_token + (int64_t)e * ceff;
+        for (int i = tid; i < Kr; i += NTHR)
+            s_rows[i] = stp[i] / k;
+        __syncthreads();
+    } else if constexpr (MODE == 2) {
         // plain product over ceff rows, one "expert" per blockIdx.y: no schedule table
         A_src += blockIdx.y * bsa;
         W += blockIdx.y * bsb;
@@ -318,21 +349,39 @@ void expert_gemm_kernel(
     const unsigned short *ga[IA];
     const unsigned short *gb[IB];
     int ca[IA], cb[IB];
+    // K-major left operand (MODE 6): like the right one below, with M
+    // columns of width bsa
+    constexpr bool AT = MODE == 6;
+    constexpr int RBTA = BM * 2, CPRTA = BM / 8;
+    static_assert(!AT || (BM & (BM - 1)) == 0, "K-major tiles are a power of two wide");
+    int ak[AT ? IA : 1];
+    const bool gatherA = MODE == 6 && act == 0, gatherB = MODE == 6 && act == 1;
 #pragma unroll
     for (int i = 0; i < IA; ++i) {
-        const int row = (wv * IA + i) * RPI + lane / CPR;
-        ca[i] = (lane % CPR) ^ ((row / RPB) % CPR);
-        const int r = m0 + row;
-        const int64_t srow = (int64_t)e * ceff + (r < rows ? r : 0);
-        const int64_t src = MODE == 0   ? (int64_t)(slot_token[srow] / k)
-                            : MODE == 3 ? (int64_t)slot_token[srow]
-                                        : srow;
-        ga[i] = A_src + src * K;
+        if constexpr (AT) {
+            const int M = (int)bsa;
+            const int q = (wv * IA + i) * 64 + lane;        // 16-byte slot in the tile
+            const int row = q / CPRTA;
+            const int c = (q % CPRTA) ^ tr_swizzle(row, CPRTA);
+            const int m = m0 + 8 * c;
+            ak[i] = row;
+            ca[i] = 0;
+            ga[i] = A_src + (m < M ? m : M - 8);
+        } else {
+            const int row = (wv * IA + i) * RPI + lane / CPR;
+            ca[i] = (lane % CPR) ^ ((row / RPB) % CPR);
+            const int r = m0 + row;
+            const int64_t srow = (int64_t)e * ceff + (r < rows ? r : 0);
+            const int64_t src = MODE == 0   ? (int64_t)(slot_token[srow] / k)
+                                : MODE == 3 ? (int64_t)slot_token[srow]
+                                            : srow;
+            ga[i] = A_src + src * K;
+        }
     }
     // K-major right operand: per op, the LDS row (k within the K-step) and a
     // pointer to its 8 columns in row 0 of W[e]; columns past Nout read the
     // last 8 (never stored), rows past K read row K - 1 (A's K tail is 0)
-    constexpr bool BT = MODE == 3 || MODE == 4;
+    constexpr bool BT = MODE == 3 || MODE == 4 || MODE == 6;
     constexpr int RBT = BN * 2, CPRT = BN / 8;   // bytes, 16-byte chunks per K-major row
     static_assert(!BT || (BN & (BN - 1)) == 0, "K-major tiles are a power of two wide");
     int bk[BT ? IB : 1];
@@ -345,7 +394,7 @@ void expert_gemm_kernel(
             const int n = n0 + 8 * c;
             bk[i] = row;
             cb[i] = 0;
-            gb[i] = W + (int64_t)e * K * Nout + (n < Nout ? n : Nout - 8);
+            gb[i] = W + (MODE == 6 ? 0 : (int64_t)e * K * Nout) + (n < Nout ? n : Nout - 8);
         } else {
             const int row = (wv * IB + i) * RPI + lane / CPR;
             cb[i] = (lane % CPR) ^ ((row / RPB) % CPR);
@@ -358,15 +407,23 @@ void expert_gemm_kernel(
         const unsigned base = smem_off + (unsigned)((kt % S) * STAGE);
 #pragma unroll
         for (int i = 0; i < IA; ++i) {
-            const int kk = min(kt * BKT + ca[i] * 8, K - 8);
-            dma16(base + (unsigned)((wv * IA + i) * 1024), ga[i] + kk);
+            if constexpr (AT) {
+                const int kr = min(kt * BKT + ak[i], Kr - 1);
+                const int64_t gi = gatherA ? (int64_t)s_rows[kr] : (int64_t)e * ceff + kr;
+                dma16(base + (unsigned)((wv * IA + i) * 1024), ga[i] + gi * bsa);
+            } else {
+                const int kk = min(kt * BKT + ca[i] * 8, K - 8);
+                dma16(base + (unsigned)((wv * IA + i) * 1024), ga[i] + kk);
+            }
         }
 #pragma unroll
         for (int i = 0; i < IB; ++i) {
             if constexpr (BT) {
-                const int kr = min(kt * BKT + bk[i], K - 1);
-                dma16(base + (unsigned)(BM * RB + (wv * IB + i) * 1024),
-                      gb[i] + (int64_t)kr * Nout);
+                const int kr = min(kt * BKT + bk[i], Kr - 1);
+                const int64_t gi = MODE != 6 ? (int64_t)kr
+                                   : gatherB ? (int64_t)s_rows[kr]
+                                             : (int64_t)e * ceff + kr;
+                dma16(base + (unsigned)(BM * RB + (wv * IB + i) * 1024), gb[i] + gi * Nout);
             } else {
                 const int kk = min(kt * BKT + cb[i] * 8, K - 8);
                 dma16(base + (unsigned)(BM * RB + (wv * IB + i) * 1024), gb[i] + kk);
@@ -396,9 +453,28 @@ void expert_gemm_kernel(
         const char *As = smem + st * STAGE;
         const char *Bs = As + BM * RB;
         const int c = ks * 4 + (lane >> 4);
+        if constexpr (AT) {
+            const int s4 = lane & 15;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            af[i] = *reinterpret_cast<const bf16x8 *>(As + (ra0 + i * 16) * RB + ((c ^ xa) << 4));
+            for (int i = 0; i < FM; ++i) {
+                const int col = wm * WTM + i * 16 + 4 * (s4 & 3);
+                v4i16 q[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = ks * 32 + 8 * (lane >> 4) + 4 * h + (s4 >> 2);
+                    const int ch = (col >> 3) ^ tr_swizzle(row, CPRTA);
+                    q[h] = lds_read_tr16(As + row * RBTA + ch * 16 + (col & 7) * 2);
+                }
+                const v4i16 lo = q[0], hi = q[1];
+                af[i] = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8 *>(As + (ra0 + i * 16) * RB +
+                                                          ((c ^ xa) << 4));
+        }
         if constexpr (BT) {
             // rows ks*32 + 8g + 4h + s/4 (g = lane group, h = half), columns
             // 4 (s % 4) .. +3 of this lane's 16-column block j
@@ -449,15 +525,22 @@ void expert_gemm_kernel(
     // K-major right operand: its rows past K)
     auto zero_tail = [&](int kt) {
         char *st = smem + (kt % S) * STAGE;
-        for (int q = tid; q < (BT ? BM : BM + BN) * CPR; q += NTHR) {
-            const int row = q / CPR, c = q % CPR;
-            if (kt * BKT + c * 8 >= K)
-                *reinterpret_cast<u32x4 *>(st + row * RB + ((c ^ ((row / RPB) % CPR)) << 4)) =
-                    u32x4{0u, 0u, 0u, 0u};
+        if constexpr (!AT) {
+            for (int q = tid; q < (BT ? BM : BM + BN) * CPR; q += NTHR) {
+                const int row = q / CPR, c = q % CPR;
+                if (kt * BKT + c * 8 >= Kr)
+                    *reinterpret_cast<u32x4 *>(st + row * RB +
+                                               ((c ^ ((row / RPB) % CPR)) << 4)) =
+                        u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+            for (int q = tid; q < BKT * CPRTA; q += NTHR)
+                if (kt * BKT + q / CPRTA >= Kr)
+                    *reinterpret_cast<u32x4 *>(st + q * 16) = u32x4{0u, 0u, 0u, 0u};
         }
         if constexpr (BT) {
             for (int q = tid; q < BKT * CPRT; q += NTHR)
-                if (kt * BKT + q / CPRT >= K)
+                if (kt * BKT + q / CPRT >= Kr)
                     *reinterpret_cast<u32x4 *>(st + BM * RB + q * 16) = u32x4{0u, 0u, 0u, 0u};
         }
     };
@@ -480,7 +563,7 @@ void expert_gemm_kernel(
             lds_barrier();
             if (kt + S - 1 < ke)
                 issue(kt + S - 1);
-            if (kt == KT - 1 && (K % BKT) != 0) {
+            if (kt == KT - 1 && (Kr % BKT) != 0) {
                 zero_tail(kt);
                 lds_barrier();
             }
@@ -991,6 +1074,38 @@ hipError_t launch_expert_rows_f32(const void *A, const void *w, int64_t K, int64
                           static_cast<const unsigned short *>(w), K, Nout, E, k, ceff, used,
                           slot_token, tiles, nullptr, nullptr, 0, kActRelu, nullptr, s, nullptr,
                           out);
+}
+
+hipError_t launch_weight_grad(const void *A, int64_t M, const void *B, int64_t N, int E,
+                              int64_t ceff, const int32_t *used, const int32_t *slot_token,
+                              int kdiv, int gathered, float *out, hipStream_t s) {
+    if (M == 0 || N == 0 || E == 0)
+        return hipSuccess;
+    if (ceff > kGradMaxRows || M % 8 != 0 || N % 8 != 0 || kdiv < 1)
+        return hipErrorInvalidValue;
+    const auto *a = static_cast<const unsigned short *>(A);
+    const auto *w = static_cast<const unsigned short *>(B);
+    // 256x256 tiles for large products (at least four rounds of them), else
+    // 128x128
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    if (M >= 512 && N >= 512 && t256 * E >= 1024) {
+        const int64_t grid = (t256 + kXcds - 1) / kXcds * kXcds;
+        hipLaunchKernelGGL((expert_gemm_kernel<256, 256, 2, 4, kBK, 2, 6>),
+                           dim3((unsigned)grid, (unsigned)E), dim3(512), 0, s, a, w, 0, (int)N,
+                           E, kdiv, (int)ceff, used, slot_token, (const int32_t *)nullptr,
+                           (unsigned short *)nullptr, out, (float *)nullptr, 0, gathered,
+                           (const float *)nullptr, (const unsigned short *)nullptr,
+                           (unsigned short *)nullptr, Dropout{}, M, (int64_t)0, M * N);
+        return hipGetLastError();
+    }
+    const int64_t grid = (((M + 127) / 128) * ((N + 127) / 128) + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, kBK, 2, 6>),
+                       dim3((unsigned)grid, (unsigned)E), dim3(256), 0, s, a, w, 0, (int)N, E,
+                       kdiv, (int)ceff, used, slot_token, (const int32_t *)nullptr,
+                       (unsigned short *)nullptr, out, (float *)nullptr, 0, gathered,
+                       (const float *)nullptr, (const unsigned short *)nullptr,
+                       (unsigned short *)nullptr, Dropout{}, M, (int64_t)0, M * N);
+    return hipGetLastError();
 }
 
 hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int64_t K,

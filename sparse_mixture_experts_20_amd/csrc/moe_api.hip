@@ -110,8 +110,11 @@ BwdLayout bwd_layout_of(const Dims &m) {
     L.ds = o;         o += align_up(nk * 4);
     L.dZ = o;         o += align_up((size_t)(m.E * m.ceff * m.d_ff) * 2);
     L.dXa = o;        o += align_up(nk * (size_t)m.d * 4);
-    L.T1 = o;         o += align_up((size_t)(m.E * m.d * L.Kp) * 2);
-    L.T2 = o;         o += align_up((size_t)(m.E * m.d_ff * L.Kp) * 2);
+    // transposed operands of the weight products, only when an expert's rows
+    // exceed what the products read K-major themselves
+    const bool tr = m.ceff > moe::kGradMaxRows;
+    L.T1 = o;         o += tr ? align_up((size_t)(m.E * m.d * L.Kp) * 2) : 0;
+    L.T2 = o;         o += tr ? align_up((size_t)(m.E * m.d_ff * L.Kp) * 2) : 0;
     L.dsT3 = o;       o += align_up((size_t)m.E * 3 * tok * 2);
     L.xT3 = o;        o += align_up((size_t)m.d * 3 * tok * 2);
     L.gpart = o;      o += align_up((size_t)(L.S * m.E * m.d) * 4);
@@ -833,8 +836,23 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
                                         dXa, rpe, s));
     MOE_TRY(moe::launch_dx(dXa, ds, idx, slot, static_cast<const float *>(W_g->data), N, d, k,
                            static_cast<float *>(dx->data), s));
-    // experts, weight side: dW_down = dY^T H, dW_up = dZ^T X (K = kept rows)
-    // (bias gradients: the row sums of the transposed dY and dZ)
+    // experts, weight side: dW_down = dY^T H, dW_up = dZ^T X over each
+    // expert's kept rows, read K-major by the products themselves
+    if (ceff <= moe::kGradMaxRows) {
+        MOE_TRY(moe::launch_weight_grad(dY, d, H, d_ff, Ei, ceff, used, st, 1, 0,
+                                        static_cast<float *>(dW_down->data), s));
+        MOE_TRY(moe::launch_weight_grad(dZ, d_ff, x->data, d, Ei, ceff, used, st, k, 1,
+                                        static_cast<float *>(dW_up->data), s));
+        if (db_down)
+            MOE_TRY(moe::launch_colsum_rows(dY, d, Ei, ceff, used, st, 1,
+                                            static_cast<float *>(db_down->data), s));
+        if (db_up)
+            MOE_TRY(moe::launch_colsum_rows(dZ, d_ff, Ei, ceff, used, nullptr, 1,
+                                            static_cast<float *>(db_up->data), s));
+        return MOE_OK;
+    }
+    // (longer experts: through transposes, K = kept rows padded to Kp;
+    // bias gradients: the row sums of the transposed dY and dZ)
     MOE_TRY(moe::launch_transpose_rows(dY, d, ceff, used, 0, st, k, 1, Kp, 1, Ei, T1, s));
     if (db_down)
         MOE_TRY(moe::launch_row_sums(T1, E * d, Kp, static_cast<float *>(db_down->data), s));

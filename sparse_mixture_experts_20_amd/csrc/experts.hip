@@ -511,14 +511,26 @@ void expert_gemm_kernel(
             }
         }
     };
+    // (the 256x256 weight-gradient tile reads one step's fragments at a time:
+    // with both operands transposed, a second set would not fit in registers)
+    constexpr bool kPrefetchFrags = !(MODE == 6 && BM * BN >= 256 * 256);
     auto compute = [&](int st, auto full) {
-        bf16x8 af[2][FM], bfr[2][FN];
-        read_frags(st, 0, af[0], bfr[0]);
+        if constexpr (kPrefetchFrags) {
+            bf16x8 af[2][FM], bfr[2][FN];
+            read_frags(st, 0, af[0], bfr[0]);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS)
-                read_frags(st, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
-            mma(af[ks & 1], bfr[ks & 1], full);
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 1 < KS)
+                    read_frags(st, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+                mma(af[ks & 1], bfr[ks & 1], full);
+            }
+        } else {
+            bf16x8 af[FM], bfr[FN];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                read_frags(st, ks, af, bfr);
+                mma(af, bfr, full);
+            }
         }
     };
     // zero the chunks of the last K-tile that lie past K (both operands; a

@@ -143,20 +143,23 @@ __global__ __launch_bounds__(256) void chunk_sum_kernel(const float *__restrict_
 
 // Column sums of an expert's rows: out[e][c] = sum over r < used[e] of
 // src[row(e, r)][c]. A block takes 512 columns (8 per lane) of one expert;
-// its four waves sum contiguous quarters of the rows in order, then the
-// quarters are added in order, so the result does not depend on timing.
-__global__ __launch_bounds__(256) void colsum_rows_kernel(
+// its 16 waves sum contiguous sixteenths of the rows in order, then the
+// partial sums are added in wave order, so the result does not depend on
+// timing.
+constexpr int kColsumWaves = 16;
+__global__ __launch_bounds__(kColsumWaves * 64) void colsum_rows_kernel(
     const unsigned short *__restrict__ src, int C, int64_t ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, int kdiv, float *__restrict__ out) {
-    __shared__ float part[4][512];
+    __shared__ float part[kColsumWaves][512];
     const int e = blockIdx.y;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int c0 = blockIdx.x * 512 + lane * 8;
     const int R = used[e];
-    const int r0 = (int)((int64_t)R * w / 4), r1 = (int)((int64_t)R * (w + 1) / 4);
+    const int r0 = (int)((int64_t)R * w / kColsumWaves);
+    const int r1 = (int)((int64_t)R * (w + 1) / kColsumWaves);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (c0 < C) {
-#pragma unroll 4
+#pragma unroll 8
         for (int r = r0; r < r1; ++r) {
             const int64_t sr = (int64_t)e * ceff + r;
             const int64_t row = slot_token ? (int64_t)(slot_token[sr] / kdiv) : sr;
@@ -172,10 +175,15 @@ __global__ __launch_bounds__(256) void colsum_rows_kernel(
     for (int q = 0; q < 8; ++q)
         part[w][lane * 8 + q] = acc[q];
     __syncthreads();
-    for (int i = threadIdx.x; i < 512; i += 256) {
+    for (int i = threadIdx.x; i < 512; i += kColsumWaves * 64) {
         const int c = blockIdx.x * 512 + i;
-        if (c < C)
-            out[(int64_t)e * C + c] = ((part[0][i] + part[1][i]) + part[2][i]) + part[3][i];
+        if (c < C) {
+            float v = 0.f;
+#pragma unroll
+            for (int q = 0; q < kColsumWaves; ++q)
+                v += part[q][i];
+            out[(int64_t)e * C + c] = v;
+        }
     }
 }
 
@@ -336,7 +344,8 @@ hipError_t launch_colsum_rows(const void *src, int64_t C, int E, int64_t ceff,
     if (C % 8 != 0 || kdiv < 1)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(colsum_rows_kernel, dim3((unsigned)((C + 511) / 512), (unsigned)E),
-                       dim3(256), 0, s, static_cast<const unsigned short *>(src), (int)C, ceff,
+                       dim3(kColsumWaves * 64), 0, s, static_cast<const unsigned short *>(src),
+                       (int)C, ceff,
                        used, slot_token, kdiv, out);
     return hipGetLastError();
 }

@@ -70,8 +70,7 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
                     const float o1 = __uint_as_float(ov[q] & 0xffff0000u);
                     p = fmaf(o0, __uint_as_float(yv[q] << 16), p);
                     p = fmaf(o1, __uint_as_float(yv[q] & 0xffff0000u), p);
-                    w[q] = (unsigned)f32_to_bf16_bits(g * o0 * m[2 * q]) |
-                           ((unsigned)f32_to_bf16_bits(g * o1 * m[2 * q + 1]) << 16);
+                    w[q] = pack_bf16x2(g * o0 * m[2 * q], g * o1 * m[2 * q + 1]);
                 }
                 *reinterpret_cast<u32x4 *>(dyr + 8 * c) = w;
             }

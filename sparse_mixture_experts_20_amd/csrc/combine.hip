@@ -82,10 +82,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ Y,
 #pragma unroll
                 for (int q = 0; q < VEC / 4; ++q) {
                     u32x2 pk;
-                    pk[0] = (unsigned)f32_to_bf16_bits(acc[4 * q]) |
-                            ((unsigned)f32_to_bf16_bits(acc[4 * q + 1]) << 16);
-                    pk[1] = (unsigned)f32_to_bf16_bits(acc[4 * q + 2]) |
-                            ((unsigned)f32_to_bf16_bits(acc[4 * q + 3]) << 16);
+                    pk[0] = pack_bf16x2(acc[4 * q], acc[4 * q + 1]);
+                    pk[1] = pack_bf16x2(acc[4 * q + 2], acc[4 * q + 3]);
                     *reinterpret_cast<u32x2 *>(o + 4 * q) = pk;
                 }
             } else {

@@ -22,13 +22,18 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// float -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+// float -> bf16 bits, round to nearest even (NaN stays a quiet NaN), on
+// gfx950's conversion instruction (v_cvt_pk_bf16_f32); a pair converts in
+// one instruction, lo in the low half. (Checked bit for bit against the
+// integer round-to-nearest-even formulation on 2^24 values: ties,
+// denormals, infinities and NaNs included.)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 __device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
-    unsigned int u = __builtin_bit_cast(unsigned int, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (unsigned short)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (unsigned short)(u >> 16);
+    return __builtin_bit_cast(unsigned short, (__bf16)f);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {

@@ -639,8 +639,7 @@ void expert_gemm_kernel(
                                 const float lo = activate<decltype(use_gelu)::value>(z[(c % 2) * 2]);
                                 const float hi =
                                     activate<decltype(use_gelu)::value>(z[(c % 2) * 2 + 1]);
-                                pk[c] = (unsigned)f32_to_bf16_bits(lo) |
-                                        ((unsigned)f32_to_bf16_bits(hi) << 16);
+                                pk[c] = pack_bf16x2(lo, hi);
                             }
                             *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
                             if (Z16) {
@@ -648,9 +647,7 @@ void expert_gemm_kernel(
 #pragma unroll
                                 for (int c = 0; c < 4; ++c) {
                                     const f32x4 &z = c < 2 ? z0 : z1;
-                                    pz[c] = (unsigned)f32_to_bf16_bits(z[(c % 2) * 2]) |
-                                            ((unsigned)f32_to_bf16_bits(z[(c % 2) * 2 + 1])
-                                             << 16);
+                                    pz[c] = pack_bf16x2(z[(c % 2) * 2], z[(c % 2) * 2 + 1]);
                                 }
                                 *reinterpret_cast<u32x4 *>(Z16 + srow * Nout + nb + 8 * h) = pz;
                             }
@@ -685,8 +682,7 @@ void expert_gemm_kernel(
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
                             const f32x4 &z = c < 2 ? z0 : z1;
-                            pk[c] = (unsigned)f32_to_bf16_bits(z[(c % 2) * 2]) |
-                                    ((unsigned)f32_to_bf16_bits(z[(c % 2) * 2 + 1]) << 16);
+                            pk[c] = pack_bf16x2(z[(c % 2) * 2], z[(c % 2) * 2 + 1]);
                         }
                         *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
                     }
@@ -715,8 +711,7 @@ void expert_gemm_kernel(
                                     lo = (hl - 1u) < 0x7fffu ? z[(c % 2) * 2] : 0.f;
                                     hi = (hh - 1u) < 0x7fffu ? z[(c % 2) * 2 + 1] : 0.f;
                                 }
-                                pk[c] = (unsigned)f32_to_bf16_bits(lo) |
-                                        ((unsigned)f32_to_bf16_bits(hi) << 16);
+                                pk[c] = pack_bf16x2(lo, hi);
                             }
                             *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
                         }
@@ -787,8 +782,8 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
             orow = srow;                              // the row of H
             if (Z16) {                                // the pre-activations too
                 u32x2 pz;
-                pz[0] = (unsigned)f32_to_bf16_bits(v[0]) | ((unsigned)f32_to_bf16_bits(v[1]) << 16);
-                pz[1] = (unsigned)f32_to_bf16_bits(v[2]) | ((unsigned)f32_to_bf16_bits(v[3]) << 16);
+                pz[0] = pack_bf16x2(v[0], v[1]);
+                pz[1] = pack_bf16x2(v[2], v[3]);
                 *reinterpret_cast<u32x2 *>(Z16 + orow * Nout + n) = pz;
             }
             if (act == kActGelu)
@@ -797,8 +792,8 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
                 v = f32x4{fmaxf(v[0], 0.f), fmaxf(v[1], 0.f), fmaxf(v[2], 0.f), fmaxf(v[3], 0.f)};
         }
         u32x2 pk;
-        pk[0] = (unsigned)f32_to_bf16_bits(v[0]) | ((unsigned)f32_to_bf16_bits(v[1]) << 16);
-        pk[1] = (unsigned)f32_to_bf16_bits(v[2]) | ((unsigned)f32_to_bf16_bits(v[3]) << 16);
+        pk[0] = pack_bf16x2(v[0], v[1]);
+        pk[1] = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<u32x2 *>(O16 + orow * Nout + n) = pk;
     }
 }

@@ -10,7 +10,8 @@ With --pass backward, one step is one moe_backward call instead (the
 forward state recomputed, then the gradients of x, W_g, W_up and W_down for
 a seeded output gradient); with --pass train, one training step of the
 layer (moe_forward_train, which keeps the forward state, then
-moe_backward_after_forward). Both are reported in the same JSON form.
+moe_backward_after_forward). Both are reported in the same JSON form;
+--dropout P adds the training-mode dropout on the expert outputs to either.
 
 Prints ONE JSON line on stdout. Besides the contract fields it carries:
   roofline      the dominant kernel (the larger of the two expert GEMMs)
@@ -132,7 +133,7 @@ def cpu_baseline(wl, target_s=15.0):
     }
 
 
-def cpu_baseline_backward(wl, target_s=15.0):
+def cpu_baseline_backward(wl, target_s=15.0, dropout=None):
     """The oracle's backward as it stands, on the first S tokens of the
     workload (same weights; capacity recomputed for S tokens), S sized for
     ~target_s of work."""
@@ -150,7 +151,9 @@ def cpu_baseline_backward(wl, target_s=15.0):
     def run(S):
         a = time.perf_counter()
         oracle.backward(x64[:S], wg64, None if nz is None else nz[:S], wu, wd, wl.k, wl.cfg.cf,
-                        dout[:S], act=wl.cfg.act, bup64=bu, bdown64=bd)
+                        dout[:S], act=wl.cfg.act, bup64=bu, bdown64=bd,
+                        **({} if dropout is None else
+                           dict(dropout=dropout[0], seed=dropout[1], offset=dropout[2])))
         return time.perf_counter() - a
 
     S = min(wl.N, 8)
@@ -166,6 +169,15 @@ def cpu_baseline_backward(wl, target_s=15.0):
                    f"workload's weights, capacity recomputed for {S} tokens ({t:.2f} s); "
                    f"tokens/s = S / t, serial float64 C loops"),
     }
+
+
+def _dropout(args):
+    """(p, seed, offset) of the expert-output dropout asked for, or None."""
+    return (args.dropout, 1, 0) if args.dropout > 0 else None
+
+
+def _dropout_note(args):
+    return f"; expert-output dropout p={args.dropout}" if args.dropout > 0 else ""
 
 
 def bench_backward(args, wl, dev, train=False):
@@ -185,14 +197,16 @@ def bench_backward(args, wl, dev, train=False):
     dout = torch.from_numpy(wl.dout().view(np.int16)).view(torch.bfloat16).to("cuda")
     if train:
         ts = B.TrainStep(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
-                         cfg.cf, act=dev["act"], b_up=dev["b_up"], b_down=dev["b_down"])
+                         cfg.cf, act=dev["act"], b_up=dev["b_up"], b_down=dev["b_down"],
+                         dropout=_dropout(args))
 
         def bwd():
             ts.forward()
             return ts.backward(dout)
     else:
         bwd = B.Backward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
-                         cfg.cf, dout, act=dev["act"], b_up=dev["b_up"], b_down=dev["b_down"])
+                         cfg.cf, dout, act=dev["act"], b_up=dev["b_up"], b_down=dev["b_down"],
+                         dropout=_dropout(args))
     for _ in range(args.warmup):
         bwd()
     torch.cuda.synchronize()
@@ -221,7 +235,7 @@ def bench_backward(args, wl, dev, train=False):
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle's backward on a bounded sample ...")
-        cpu = cpu_baseline_backward(wl)
+        cpu = cpu_baseline_backward(wl, dropout=_dropout(args))
         log(f"[bench] cpu_baseline {cpu['value']:.1f} tokens/s")
     line = {
         "metric": ("MoE-layer training step (forward + backward) tokens/sec at 1 MI355X"
@@ -238,7 +252,7 @@ def bench_backward(args, wl, dev, train=False):
         "dtype": cfg.dtype,
         "data": "synthetic (seeded Gaussian inputs, output gradient and random-init weights)",
         "config": {
-            "workload": (cfg.description or cfg.name) + (
+            "workload": (cfg.description or cfg.name) + _dropout_note(args) + (
                 "; training step: forward keeping its state, then backward" if train
                 else "; backward pass"),
             "tokens": wl.N, "d": wl.d, "experts": wl.E, "top_k": wl.k, "d_ff": wl.d_ff,
@@ -281,7 +295,14 @@ def main():
                     default="forward",
                     help="time the layer's forward (default), its backward pass, or a "
                          "training step (forward keeping its state + backward)")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="training-mode dropout probability on the expert outputs "
+                         "(generator seed 1, offset 0); 0 = none")
     args = ap.parse_args()
+    if not 0.0 <= args.dropout < 1.0:
+        ap.error("--dropout must be in [0, 1)")
+    if args.dropout > 0 and args.which == "forward":
+        ap.error("--dropout is training-mode: use it with --pass backward or --pass train")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -50,18 +50,19 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t
                                               uint64_t (&out)[4]) {
     constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
     constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-#pragma unroll
+    // The rounds stay a loop: unrolled, the generator is large enough to stop
+    // the unrolling of the epilogue loops that call it, whose accumulators
+    // would then be indexed at run time and leave the registers.
+#pragma unroll 1
     for (int r = 0; r < 10; ++r) {
-        if (r > 0) {
-            k0 += W0;
-            k1 += W1;
-        }
         const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
         const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
         c0 = hi1 ^ c1 ^ k0;
         c1 = lo1;
         c2 = hi0 ^ c3 ^ k1;
         c3 = lo0;
+        k0 += W0;
+        k1 += W1;
     }
     out[0] = c0;
     out[1] = c1;

@@ -126,16 +126,27 @@ def test_backward_with_dropout_matches_oracle(torch_mod, name):
     del dev
 
 
-def test_nanomoe_dropout_sampled(torch_mod):
-    """The nanoMoE layer with dropout 0.1: layer output on sampled rows and
-    dx on sampled rows, in the benchmark's launch configuration."""
+def _sampled_case(which):
+    import dataclasses
+    if which == "nanomoe":
+        base = W.make("nanomoe").cfg
+        return W.make(dataclasses.replace(base, name="nanomoe_dropout", dropout=0.1,
+                                          dropout_seed=2026, dropout_offset=3))
+    # 512 rows per expert and d = 2048: the down product (and its dropout)
+    # runs on the 256x256 tile, as at the Mixtral shape
+    return W.custom("wide_dropout", N=2048, d=2048, E=8, k=2, d_ff=1024, dtype="bf16", cf=1.25,
+                    sigma=0.3, seed=405, w_std=0.03, dropout=0.1, dropout_seed=2026,
+                    dropout_offset=3)
+
+
+@pytest.mark.parametrize("which", ["nanomoe", "wide"])
+def test_dropout_sampled(torch_mod, which):
+    """Dropout 0.1 on the nanoMoE layer (128x64 down tiles) and on a layer
+    whose down product takes the 256x256 tile: layer output on sampled rows
+    and dx on sampled rows, in the benchmark's launch configuration."""
     torch = torch_mod
     from sparse_mixture_experts_20_amd import binding as B
-    base = W.make("nanomoe").cfg
-    import dataclasses
-    cfg = dataclasses.replace(base, name="nanomoe_dropout", dropout=0.1, dropout_seed=2026,
-                              dropout_offset=3)
-    wl = W.make(cfg)
+    wl = _sampled_case(which)
     dev = _upload(wl)
     out, st = B.forward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
                         wl.cfg.cf, export=True, dropout=_drop(wl))

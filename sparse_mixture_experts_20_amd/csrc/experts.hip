@@ -234,8 +234,15 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // row of r is slot_token[e*ceff + r] / k for the gathered operand (act == 0:
 // A, act == 1: B) and e*ceff + r for the other; bsc = M*Nout. K is unused
 // (each expert's K is used[e]; kGradMaxRows bounds ceff).
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BKT, int S, int MODE>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// WAVES_K > 1 (modes 0, 1, 2, 5): WAVES_K sets of WAVES_M x WAVES_N waves
+// share each K-step, set w taking its 32-wide MFMA steps w, w + WAVES_K, ...;
+// after the last step the sets add their partial tiles into set 0 through
+// LDS, in set order, and set 0 runs the epilogue. Same LDS reads per MFMA as
+// WAVES_K = 1, with WAVES_K times the waves to hide latency.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_K, int BKT, int S, int MODE>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * WAVES_K * 64)
+__attribute__((amdgpu_waves_per_eu(WAVES_M * WAVES_N * WAVES_K >= 16 ? 4 : 2,
+                                   WAVES_M * WAVES_N * WAVES_K >= 16 ? 4 : 2)))
 void expert_gemm_kernel(
     const unsigned short *__restrict__ A_src, const unsigned short *__restrict__ W, int K,
     int Nout, int E, int k, int ceff, const int32_t *__restrict__ used,
@@ -243,7 +250,8 @@ void expert_gemm_kernel(
     unsigned short *__restrict__ O16, float *__restrict__ O32, float *__restrict__ part,
     int P, int act, const float *__restrict__ bias, const unsigned short *mask,
     unsigned short *__restrict__ Z16, Dropout dp, int64_t bsa, int64_t bsb, int64_t bsc) {
-    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int WMN = WAVES_M * WAVES_N;                   // waves of one K set
+    constexpr int NW = WMN * WAVES_K;
     constexpr int NTHR = NW * 64;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;   // wave tile
     constexpr int FM = WTM / 16, FN = WTN / 16;              // 16x16 MFMA tiles per wave
@@ -257,7 +265,10 @@ void expert_gemm_kernel(
     static_assert(BKT % 32 == 0 && S >= 2, "K-step is a multiple of one MFMA K");
     static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile/waves mismatch");
     static_assert(WTM % 16 == 0 && WTN % 32 == 0, "16x16 MFMA tiles; 4 lanes x 8k columns per row");
-    static_assert(NW * 16 * (WTN + 4) * 4 <= S * STAGE, "epilogue scratch");
+    static_assert(WMN * 16 * (WTN + 4) * 4 <= S * STAGE, "epilogue scratch");
+    static_assert(WAVES_K == 1 || (MODE != 3 && MODE != 4 && MODE != 6), "K sets: row-major B");
+    static_assert((WAVES_K & (WAVES_K - 1)) == 0, "K sets: a power of two");
+    static_assert(WAVES_K / 2 * WMN * FM * FN * 64 * 16 <= S * STAGE, "K-set reduction");
     __shared__ __attribute__((aligned(1024)))
     char smem[S * STAGE + (MODE == 6 ? kGradMaxRows * 4 : 0)];
     __shared__ int s_mt[kMaxExperts + 1];
@@ -341,7 +352,8 @@ void expert_gemm_kernel(
 
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv / WAVES_N, wn = wv % WAVES_N;
+    const int wk = WAVES_K == 1 ? 0 : wv / WMN;   // K set
+    const int wm = (wv % WMN) / WAVES_N, wn = wv % WAVES_N;
 
     // Direct-load sources of this lane: one row and one 16-byte chunk per op.
     // Rows past the tile edge read row 0 of the expert (their outputs are
@@ -449,6 +461,8 @@ void expert_gemm_kernel(
     // Operand fragments of K-step ks (32 wide) of stage st; the next step's
     // fragments are read before the current step's MFMAs are issued.
     constexpr int KS = BKT / 32;
+    static_assert(KS % WAVES_K == 0, "MFMA steps split evenly among the K sets");
+    constexpr int KSW = KS / WAVES_K;      // MFMA steps of one K set per K-step
     auto read_frags = [&](int st, int ks, bf16x8 (&af)[FM], bf16x8 (&bfr)[FN]) {
         const char *As = smem + st * STAGE;
         const char *Bs = As + BM * RB;
@@ -517,18 +531,18 @@ void expert_gemm_kernel(
     auto compute = [&](int st, auto full) {
         if constexpr (kPrefetchFrags) {
             bf16x8 af[2][FM], bfr[2][FN];
-            read_frags(st, 0, af[0], bfr[0]);
+            read_frags(st, wk, af[0], bfr[0]);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if (ks + 1 < KS)
-                    read_frags(st, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
-                mma(af[ks & 1], bfr[ks & 1], full);
+            for (int u = 0; u < KSW; ++u) {
+                if (u + 1 < KSW)
+                    read_frags(st, wk + (u + 1) * WAVES_K, af[(u + 1) & 1], bfr[(u + 1) & 1]);
+                mma(af[u & 1], bfr[u & 1], full);
             }
         } else {
             bf16x8 af[FM], bfr[FN];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                read_frags(st, ks, af, bfr);
+            for (int u = 0; u < KSW; ++u) {
+                read_frags(st, wk + u * WAVES_K, af, bfr);
                 mma(af, bfr, full);
             }
         }
@@ -587,6 +601,36 @@ void expert_gemm_kernel(
     else
         mainloop(std::false_type{});
     lds_barrier();
+    if constexpr (WAVES_K > 1) {
+        // pairwise: at each level the upper half of the remaining K sets hands
+        // its partial tiles (lane-interleaved 16-byte slots) to the lower half,
+        // set w adding set w + h, until set 0 holds the sum
+        f32x4 *red = reinterpret_cast<f32x4 *>(smem);
+        const int wmn = wv % WMN;
+#pragma unroll
+        for (int h = WAVES_K / 2; h >= 1; h /= 2) {
+            if (wk >= h && wk < 2 * h) {
+                f32x4 *dst = red + ((wk - h) * WMN + wmn) * (FM * FN * 64) + lane;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        dst[(i * FN + j) * 64] = acc[i][j];
+            }
+            lds_barrier();
+            if (wk < h) {
+                const f32x4 *src = red + (wk * WMN + wmn) * (FM * FN * 64) + lane;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] += src[(i * FN + j) * 64];
+            }
+            lds_barrier();   // the slots (and then the epilogue scratch) are reused
+        }
+        if (wk > 0)
+            return;
+    }
 
     // epilogue: per wave, one 16-row strip at a time through a private LDS
     // scratch, then 16-byte stores of CPL contiguous columns per lane.
@@ -881,20 +925,29 @@ namespace {
 // Tile shapes (rows_per_expert = expected kept rows per expert):
 //  - 256x256, 8 waves of 128x64, one workgroup per CU: experts with >= 512
 //    rows when that still gives a full grid or the product is wide;
-//  - 128x64, 4 waves of 64x32: when 128x128 tiles would leave CUs idle
-//    (fewer than 384 tiles), trading operand reuse for parallelism;
+//  - 128x128 in two K sets (8 waves: 2 x 2 of 64x64 per set, K-step 128,
+//    one workgroup per CU): when 128x128 tiles give between 192 and 384
+//    tiles, i.e. about one per CU (the operand reuse of 64x64 wave tiles,
+//    with two waves per SIMD to hide latency);
+//  - 128x64, 4 waves of 64x32: when 128x128 tiles would leave more CUs idle
+//    (fewer than 192 tiles), trading operand reuse for parallelism;
 //  - 128x128, 4 waves of 64x64, two workgroups per CU: otherwise.
-enum class Tile { k128, k128x64, k256 };
+// Products whose right operand is read K-major (modes 3, 4) take 128x64
+// where the K-set tile would be picked.
+enum class Tile { k128, k128x64, k256, k128k2 };
 
-constexpr int kBK = 64;   // K-step of every bf16 tile shape
+constexpr int kBK = 64;    // K-step of the one-set tile shapes
+constexpr int kBK2 = 128;  // K-step of the K-set tile: two 32-wide MFMA steps per set
 
 Tile pick_tile(int64_t rows_per_expert, int64_t Nout, int E) {
     const int64_t t256 = (int64_t)E * ((rows_per_expert + 255) / 256) * ((Nout + 255) / 256);
     if (rows_per_expert >= 512 && (t256 >= 256 || Nout >= 2048))
         return Tile::k256;
     const int64_t t128 = (int64_t)E * ((rows_per_expert + 127) / 128) * ((Nout + 127) / 128);
-    if (t128 < 384)
+    if (t128 < 192)
         return Tile::k128x64;
+    if (t128 < 384)
+        return Tile::k128k2;
     return Tile::k128;
 }
 
@@ -914,7 +967,7 @@ int resident_blocks(Kern kernel, int threads) {
 
 // One bf16 grouped product on tile shape BM x BN, plus the fix-up of the
 // split last round when the scratch `part` can hold it.
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int WK, int BKT, int MODE>
 hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_t K, int64_t Nout,
                         int E, int k, int64_t ceff, const int32_t *used,
                         const int32_t *slot_token, const int32_t *mt, unsigned short *O16,
@@ -922,8 +975,8 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
                         hipStream_t s, const unsigned short *mask = nullptr,
                         float *O32 = nullptr, unsigned short *Z16 = nullptr,
                         Dropout dp = Dropout{}) {
-    auto kern = expert_gemm_kernel<BM, BN, WM, WN, kBK, 2, MODE>;
-    constexpr int NTHR = WM * WN * 64;
+    auto kern = expert_gemm_kernel<BM, BN, WM, WN, WK, BKT, 2, MODE>;
+    constexpr int NTHR = WM * WN * WK * 64;
     static int resident[kMaxDevices];   // per device, filled on first use (0 = unset)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
@@ -937,7 +990,7 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
     const int64_t slot = (int64_t)BM * BN * sizeof(float);
     if (!part || P <= 0 || (int64_t)P * slot > (int64_t)part_bytes)
         P = 0;
-    const int64_t KT = (K + kBK - 1) / kBK;
+    const int64_t KT = (K + BKT - 1) / BKT;
     const int64_t tmax = (int64_t)E * ((ceff + BM - 1) / BM) * ((Nout + BN - 1) / BN);
     // a split needs at least two ranges of kSplitMinSteps, at least one full
     // round of tiles and (by the 15% rule of split_plan) fewer than six
@@ -953,7 +1006,7 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !split)
         return err;
-    hipLaunchKernelGGL((split_fixup_kernel<BM, BN, kBK, MODE == 0 ? 0 : 1>),
+    hipLaunchKernelGGL((split_fixup_kernel<BM, BN, BKT, MODE == 0 ? 0 : 1>),
                        dim3((unsigned)(P * (BM / 16))),
                        dim3(256), 0, s, (int)K, (int)Nout, E, (int)ceff, used, slot_token, mt,
                        (const float *)part, P, O16, act, bias, dp, Z16);
@@ -969,15 +1022,23 @@ hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W,
                        float *O32 = nullptr, unsigned short *Z16 = nullptr,
                        Dropout dp = Dropout{}) {
     float *pf = static_cast<float *>(part);
+    if (t == Tile::k128k2) {
+        if constexpr (MODE == 0 || MODE == 1 || MODE == 5)
+            return launch_tiles<128, 128, 2, 2, 2, kBK2, MODE>(A, W, K, Nout, E, k, ceff, used,
+                                                              slot_token, tiles, O16, pf,
+                                                              part_bytes, act, bias, s, mask,
+                                                              O32, Z16, dp);
+        t = Tile::k128x64;   // K-major right operands: no K sets
+    }
     if (t == Tile::k256)
-        return launch_tiles<256, 256, 2, 4, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
+        return launch_tiles<256, 256, 2, 4, 1, kBK, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
                                                   tiles + E + 1, O16, pf, part_bytes, act, bias,
                                                   s, mask, O32, Z16, dp);
     if (t == Tile::k128x64)
-        return launch_tiles<128, 64, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
+        return launch_tiles<128, 64, 2, 2, 1, kBK, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
                                                  tiles, O16, pf, part_bytes, act, bias, s, mask,
                                                  O32, Z16, dp);
-    return launch_tiles<128, 128, 2, 2, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token, tiles,
+    return launch_tiles<128, 128, 2, 2, 1, kBK, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token, tiles,
                                               O16, pf, part_bytes, act, bias, s, mask, O32, Z16,
                                               dp);
 }
@@ -991,7 +1052,7 @@ hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, in
     if (rows == 0)
         return hipSuccess;
     const int64_t grid = (((rows + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, kBK, 2, 2>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, 1, kBK, 2, 2>), dim3((unsigned)grid),
                        dim3(256), 0, s, static_cast<const unsigned short *>(A),
                        static_cast<const unsigned short *>(W), (int)K, (int)Nout, 1, 1, (int)rows,
                        (const int32_t *)nullptr, (const int32_t *)nullptr,
@@ -1097,7 +1158,7 @@ hipError_t launch_weight_grad(const void *A, int64_t M, const void *B, int64_t N
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     if (M >= 512 && N >= 512 && t256 * E >= 1024) {
         const int64_t grid = (t256 + kXcds - 1) / kXcds * kXcds;
-        hipLaunchKernelGGL((expert_gemm_kernel<256, 256, 2, 4, kBK, 2, 6>),
+        hipLaunchKernelGGL((expert_gemm_kernel<256, 256, 2, 4, 1, kBK, 2, 6>),
                            dim3((unsigned)grid, (unsigned)E), dim3(512), 0, s, a, w, 0, (int)N,
                            E, kdiv, (int)ceff, used, slot_token, (const int32_t *)nullptr,
                            (unsigned short *)nullptr, out, (float *)nullptr, 0, gathered,
@@ -1106,7 +1167,7 @@ hipError_t launch_weight_grad(const void *A, int64_t M, const void *B, int64_t N
         return hipGetLastError();
     }
     const int64_t grid = (((M + 127) / 128) * ((N + 127) / 128) + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, kBK, 2, 6>),
+    hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, 1, kBK, 2, 6>),
                        dim3((unsigned)grid, (unsigned)E), dim3(256), 0, s, a, w, 0, (int)N, E,
                        kdiv, (int)ceff, used, slot_token, (const int32_t *)nullptr,
                        (unsigned short *)nullptr, out, (float *)nullptr, 0, gathered,
@@ -1127,7 +1188,7 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
     const int64_t t256 = ((M + 255) / 256) * ((Nout + 255) / 256);
     if (M >= 512 && Nout >= 512 && K >= 256 && t256 * batch >= 1024) {
         const int64_t grid = (t256 + kXcds - 1) / kXcds * kXcds;
-        hipLaunchKernelGGL((expert_gemm_kernel<256, 256, 2, 4, kBK, 2, 2>),
+        hipLaunchKernelGGL((expert_gemm_kernel<256, 256, 2, 4, 1, kBK, 2, 2>),
                            dim3((unsigned)grid, (unsigned)batch), dim3(512), 0, s, a, w, (int)K,
                            (int)Nout, 1, 1, (int)M, (const int32_t *)nullptr,
                            (const int32_t *)nullptr, (const int32_t *)nullptr,
@@ -1137,7 +1198,7 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
         return hipGetLastError();
     }
     const int64_t grid = (((M + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, kBK, 2, 2>),
+    hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, 1, kBK, 2, 2>),
                        dim3((unsigned)grid, (unsigned)batch), dim3(256), 0, s, a, w, (int)K,
                        (int)Nout, 1, 1, (int)M, (const int32_t *)nullptr,
                        (const int32_t *)nullptr, (const int32_t *)nullptr,

@@ -82,6 +82,7 @@ CASES = {
     "bwd_ragged": (333, 136, 5, 2, 200, 1.0, 0.3, 0.0, 301),
     "bwd_multi_tile": (1000, 264, 16, 4, 392, 0.8, 0.5, 0.0, 302),
     "bwd_row_tiles": (1024, 256, 4, 2, 512, 1.0, 0.5, 0.0, 303),
+    "bwd_kset": (1024, 392, 64, 4, 520, 1.0, 0.5, 0.0, 315),
     "bwd_heavy_drop": (512, 64, 4, 2, 128, 0.1, 0.0, 5.0, 304),
     "bwd_many_experts": (300, 128, 256, 8, 96, 2.0, 0.0, 0.0, 305),
     "bwd_max_top_k": (200, 64, 64, 16, 72, 0.7, 0.2, 0.0, 310),

@@ -45,6 +45,9 @@ SMALL = {
     "multi_tile_bf16": (1000, 264, 16, 4, 392, "bf16", 0.8, 0.5, 0.0, 102),
     "many_experts_bf16": (300, 128, 256, 8, 96, "bf16", 2.0, 0.0, 0.0, 103),
     "mid_bf16": (1536, 512, 8, 2, 1024, "bf16", 1.25, 1.0, 0.0, 104),
+    # about one 128x128 tile per CU in both products: the two-K-set tile,
+    # with K tails (392, 520 = 128 q + 8), ragged columns and part-filled rows
+    "kset_bf16": (1024, 392, 64, 4, 520, "bf16", 1.0, 0.5, 0.0, 114),
     "k1_bf16": (200, 64, 3, 1, 64, "bf16", 1.0, 0.0, 0.0, 105),
     "k_equals_E_bf16": (100, 32, 4, 4, 48, "bf16", 1.0, 0.0, 0.0, 106),
     "max_top_k_bf16": (200, 64, 64, 16, 72, "bf16", 0.7, 0.2, 0.0, 112),

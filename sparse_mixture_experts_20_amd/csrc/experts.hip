@@ -172,20 +172,93 @@ __device__ __forceinline__ SplitPlan split_plan(int T, int KT, int P) {
     return p;
 }
 
-// Expert e owning tile L of the grouped schedule (tiles of expert e are
-// s_mt[e]*NT .. s_mt[e+1]*NT - 1, row tiles fastest), and its tile origin.
-__device__ __forceinline__ void decode_tile(int L, const int *s_mt, int E, int NT, int BM,
-                                            int BN, int &e, int &m0, int &n0) {
+// Order of the grouped schedule's T = s_mt[E]*NT tiles (s_mt: prefix sums
+// of each expert's row tiles, ceil(used/BM)): expert by expert, row tiles
+// fastest. When all tiles do not fit in one round of resident workgroups
+// but those with more than BM/2 kept rows do, those come first and the
+// light last row tiles (at most BM/2 kept rows) follow, expert by expert,
+// columns fastest: workgroups are dispatched in index order, so it is the
+// light tiles (their padding rows skip the matrix instructions) that wait
+// for the round to free a CU, not heavy ones. Otherwise the plain order
+// stays: a light tile then runs beside the other tiles of its expert and
+// column, on the same XCD, whose operands it shares in that XCD's L2.
+// s_pp[e] (e <= E): experts before e whose last row tile is light.
+// Needs at least 256 threads (E <= 256); ends with a barrier.
+__device__ __forceinline__ void partial_prefix(const int32_t *__restrict__ used, int E, int BM,
+                                               int nthr, int *s_pp, uint64_t *s_msk) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (w < kMaxExperts / 64) {
+        const int e = w * 64 + lane;
+        const int rm = e < E ? used[e] % BM : 0;
+        const uint64_t m = __ballot(rm != 0 && 2 * rm <= BM);
+        if (lane == 0)
+            s_msk[w] = m;
+    }
+    __syncthreads();
+    for (int i = tid; i <= E; i += nthr) {
+        int c = 0;
+        for (int ww = 0; ww < i / 64; ++ww)
+            c += __popcll(s_msk[ww]);
+        if (i % 64)
+            c += __popcll(s_msk[i / 64] & (~0ull >> (64 - i % 64)));
+        s_pp[i] = c;
+    }
+    __syncthreads();
+}
+
+// Largest e in [0, E) with f(e) <= v (f non-decreasing, f(0) <= v).
+template <typename F>
+__device__ __forceinline__ int last_at_most(F f, int E, int v) {
     int lo = 0, hi = E - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_mt[mid] * NT <= L) lo = mid; else hi = mid - 1;
+        if (f(mid) <= v) lo = mid; else hi = mid - 1;
     }
-    e = lo;
-    const int mte = s_mt[e + 1] - s_mt[e];
-    const int local = L - s_mt[e] * NT;
-    m0 = (local % mte) * BM;
-    n0 = (local / mte) * BN;
+    return lo;
+}
+
+// Whether the light tiles go last (see above), P resident workgroups; s_mt
+// must be in LDS. The light-tile prefix is only computed (with s_msk, two
+// barriers) when the order can change: at most one tile per expert and
+// column is light, so with more than P + E*NT tiles the heavy ones overflow
+// the round anyway.
+__device__ __forceinline__ bool light_last(const int32_t *__restrict__ used, const int *s_mt,
+                                          int E, int NT, int BM, int P, int nthr, int *s_pp,
+                                          uint64_t *s_msk) {
+    const int T = s_mt[E] * NT;
+    if (T <= P || T - E * NT > P)
+        return false;
+    partial_prefix(used, E, BM, nthr, s_pp, s_msk);
+    return s_pp[E] > 0 && (s_mt[E] - s_pp[E]) * NT <= P;
+}
+
+// Expert e owning tile L of the schedule above, and its tile origin
+// (s_pp = NULL: the plain order).
+__device__ __forceinline__ void decode_tile(int L, const int *s_mt, const int *s_pp, int E,
+                                            int NT, int BM, int BN, int &e, int &m0, int &n0) {
+    if (!s_pp) {
+        e = last_at_most([&](int x) { return s_mt[x] * NT; }, E, L);
+        const int mte = s_mt[e + 1] - s_mt[e];
+        const int local = L - s_mt[e] * NT;
+        m0 = (local % mte) * BM;
+        n0 = (local / mte) * BN;
+        return;
+    }
+    // heavy row tiles before expert e: s_mt[e] - s_pp[e]
+    const int TA = (s_mt[E] - s_pp[E]) * NT;
+    if (L < TA) {
+        e = last_at_most([&](int x) { return (s_mt[x] - s_pp[x]) * NT; }, E, L);
+        const int f0 = s_mt[e] - s_pp[e];
+        const int nf = s_mt[e + 1] - s_pp[e + 1] - f0;
+        const int local = L - f0 * NT;
+        m0 = (local % nf) * BM;
+        n0 = (local / nf) * BN;
+    } else {
+        const int q = (L - TA) / NT;   // q-th expert with a light last tile
+        e = last_at_most([&](int x) { return s_pp[x]; }, E, q);
+        m0 = (s_mt[e + 1] - s_mt[e] - 1) * BM;
+        n0 = ((L - TA) % NT) * BN;
+    }
 }
 
 // Block b of a launch whose first T8 blocks take whole tiles: block b runs on
@@ -219,7 +292,8 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // MODE 4); its tiles are staged row by row and turned into MFMA fragments
 // by transposing LDS reads.
 // part: scratch for the split of the last round (NULL: no split), P: the
-// number of workgroups of this kernel that fit on the device at once.
+// number of workgroups of this kernel that fit on the device at once (0:
+// unknown; it sizes the split and chooses the tile order).
 // act: activation of the up product (kActRelu, kActGelu); bias: [E, Nout]
 // fp32 added to the product before the activation (MODE 0) or to the output
 // row (MODE 1), or NULL. K-range partials take neither (the fix-up does).
@@ -268,10 +342,13 @@ void expert_gemm_kernel(
     static_assert(WMN * 16 * (WTN + 4) * 4 <= S * STAGE, "epilogue scratch");
     static_assert(WAVES_K == 1 || (MODE != 3 && MODE != 4 && MODE != 6), "K sets: row-major B");
     static_assert((WAVES_K & (WAVES_K - 1)) == 0, "K sets: a power of two");
+    static_assert(MODE == 2 || MODE == 6 || NTHR >= kMaxExperts, "schedule prefix: a lane per expert");
     static_assert(WAVES_K / 2 * WMN * FM * FN * 64 * 16 <= S * STAGE, "K-set reduction");
     __shared__ __attribute__((aligned(1024)))
     char smem[S * STAGE + (MODE == 6 ? kGradMaxRows * 4 : 0)];
     __shared__ int s_mt[kMaxExperts + 1];
+    __shared__ int s_pp[kMaxExperts + 1];
+    __shared__ uint64_t s_msk[kMaxExperts / 64];
     int *s_rows = reinterpret_cast<int *>(smem + S * STAGE);   // MODE 6: row of each r
 
     const int tid = threadIdx.x;
@@ -327,18 +404,28 @@ void expert_gemm_kernel(
         __syncthreads();
         const int T = s_mt[E] * NT;
         const SplitPlan sp = split_plan(T, KT, part ? P : 0);
-        const int T8 = (sp.Tdp + kXcds - 1) / kXcds * kXcds;
+        const bool ll = light_last(used, s_mt, E, NT, BM, P, NTHR, s_pp, s_msk);
+        // whole tiles in two launch segments (heavy ones, then light ones
+        // when those go last), each spread over the XCDs; then the K-ranges
+        // of the cut tiles
+        const int T1 = ll ? min((s_mt[E] - s_pp[E]) * NT, sp.Tdp) : sp.Tdp;
+        const int T18 = (T1 + kXcds - 1) / kXcds * kXcds;
+        const int T28 = (sp.Tdp - T1 + kXcds - 1) / kXcds * kXcds;
         int L;
-        if (b < T8) {
-            L = xcd_index(b, T8);
+        if (b < T18) {
+            L = xcd_index(b, T18);
+            if (L >= T1)
+                return;
+        } else if (b < T18 + T28) {
+            L = T1 + xcd_index(b - T18, T28);
             if (L >= sp.Tdp)
                 return;
         } else {
             const int np = sp.tail * sp.nsplit;
             const int np8 = (np + kXcds - 1) / kXcds * kXcds;
-            if (b - T8 >= np8)
+            if (b - T18 - T28 >= np8)
                 return;
-            piece = xcd_index(b - T8, np8);
+            piece = xcd_index(b - T18 - T28, np8);
             if (piece >= np)
                 return;
             L = sp.Tdp + piece / sp.nsplit;
@@ -346,7 +433,7 @@ void expert_gemm_kernel(
             kb = (int)((int64_t)s * KT / sp.nsplit);
             ke = (int)((int64_t)(s + 1) * KT / sp.nsplit);
         }
-        decode_tile(L, s_mt, E, NT, BM, BN, e, m0, n0);
+        decode_tile(L, s_mt, ll ? s_pp : nullptr, E, NT, BM, BN, e, m0, n0);
         rows = used[e];
     }
 
@@ -789,6 +876,8 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
     const float *__restrict__ bias, Dropout dp, unsigned short *__restrict__ Z16) {
     constexpr int STRIPS = BM / 16;
     __shared__ int s_mt[kMaxExperts + 1];
+    __shared__ int s_pp[kMaxExperts + 1];
+    __shared__ uint64_t s_msk[kMaxExperts / 64];
     for (int i = threadIdx.x; i <= E; i += 256)
         s_mt[i] = mt_off[i];
     __syncthreads();
@@ -796,10 +885,11 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
     const int KT = (K + BKT - 1) / BKT;
     const SplitPlan sp = split_plan(s_mt[E] * NT, KT, P);
     const int t = blockIdx.x / STRIPS, strip = blockIdx.x % STRIPS;
-    if (sp.nsplit < 2 || t >= sp.tail)
+    if (sp.nsplit < 2 || t >= sp.tail)   // (the same for the whole workgroup)
         return;
+    const bool ll = light_last(used, s_mt, E, NT, BM, P, 256, s_pp, s_msk);
     int e, m0, n0;
-    decode_tile(sp.Tdp + t, s_mt, E, NT, BM, BN, e, m0, n0);
+    decode_tile(sp.Tdp + t, s_mt, ll ? s_pp : nullptr, E, NT, BM, BN, e, m0, n0);
     const int rows = used[e];
     for (int i = threadIdx.x; i < 16 * (BN / 4); i += 256) {
         const int rr = i / (BN / 4), c4 = i % (BN / 4);
@@ -987,22 +1077,24 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
             resident[dev] = resident_blocks(kern, NTHR);
         P = resident[dev];
     }
-    const int64_t slot = (int64_t)BM * BN * sizeof(float);
-    if (!part || P <= 0 || (int64_t)P * slot > (int64_t)part_bytes)
+    if (P < 0)
         P = 0;
+    const int64_t slot = (int64_t)BM * BN * sizeof(float);
     const int64_t KT = (K + BKT - 1) / BKT;
     const int64_t tmax = (int64_t)E * ((ceff + BM - 1) / BM) * ((Nout + BN - 1) / BN);
-    // a split needs at least two ranges of kSplitMinSteps, at least one full
-    // round of tiles and (by the 15% rule of split_plan) fewer than six
-    const bool split = (MODE == 0 || MODE == 1 || MODE == 5) && P > 0 &&
+    // a split needs the scratch, at least two ranges of kSplitMinSteps, at
+    // least one full round of tiles and (by the 15% rule of split_plan)
+    // fewer than six
+    const bool split = (MODE == 0 || MODE == 1 || MODE == 5) && part && P > 0 &&
+                       (int64_t)P * slot <= (int64_t)part_bytes &&
                        KT >= 2 * kSplitMinSteps &&
                        tmax >= P && tmax < 6 * (int64_t)P;
-    const int64_t grid = (tmax + kXcds - 1) / kXcds * kXcds +
+    // whole tiles take two XCD-rounded segments (one more group of kXcds)
+    const int64_t grid = (tmax + kXcds - 1) / kXcds * kXcds + kXcds +
                          (split ? (int64_t)(P + kXcds - 1) / kXcds * kXcds : 0);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHR), 0, s, A, W, (int)K, (int)Nout, E,
                        k, (int)ceff, used, slot_token, mt, O16, O32, split ? part : nullptr,
-                       split ? P : 0, act, bias, mask, Z16, dp, (int64_t)0, (int64_t)0,
-                       (int64_t)0);
+                       P, act, bias, mask, Z16, dp, (int64_t)0, (int64_t)0, (int64_t)0);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !split)
         return err;

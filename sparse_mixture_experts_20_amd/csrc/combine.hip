@@ -8,9 +8,13 @@
 // Each thread owns a VEC-wide column slice of one token row: it reads the k
 // expert rows of that token (stored contiguously, assignment-major; bf16 or
 // fp32), accumulates in fp32 in choice order and rounds once to the output
-// type. A pure streaming kernel: k*d*sizeof(Y) bytes read per token (kept
-// rows only) and d*sizeof(out) bytes written. bf16 rows are read 8 columns
-// (16 bytes) at a time.
+// type. A pure streaming kernel: k*d*sizeof(Y) bytes read per token and
+// d*sizeof(out) bytes written. bf16 rows are read 8 columns (16 bytes) at a
+// time. The slots, gates and rows of up to kGroup choices are loaded
+// together (one memory round trip, not two per choice): the row of a
+// dropped assignment is read too (it lies inside Y but was never written)
+// and then not added, by selection rather than by a zero weight, so that
+// whatever it holds cannot reach the sum.
 #include "common.hpp"
 
 namespace moe {
@@ -49,6 +53,8 @@ __device__ __forceinline__ void load_row(const unsigned short *y, float (&v)[VEC
     }
 }
 
+constexpr int kGroup = 4;   // choices whose loads are in flight together
+
 template <typename YT, bool BF16, int VEC>
 __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ Y,
                                                       const float *__restrict__ gate,
@@ -65,16 +71,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ Y,
 #pragma unroll
         for (int v = 0; v < VEC; ++v)
             acc[v] = 0.f;
-        for (int j = 0; j < k; ++j) {
-            const int64_t a = t * k + j;
-            if (slot[a] < 0)
-                continue;
-            const float g = gate[a];
-            float y[VEC];
-            load_row<VEC>(Y + a * d + c, y);
+        for (int j0 = 0; j0 < k; j0 += kGroup) {
+            int sl[kGroup];
+            float g[kGroup], y[kGroup][VEC];
 #pragma unroll
-            for (int v = 0; v < VEC; ++v)
-                acc[v] += g * y[v];
+            for (int u = 0; u < kGroup; ++u) {
+                // past the last choice: reload the group's first (not added)
+                const int64_t a = t * k + (j0 + u < k ? j0 + u : j0);
+                sl[u] = slot[a];
+                g[u] = gate[a];
+                load_row<VEC>(Y + a * d + c, y[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                const bool add = j0 + u < k && sl[u] >= 0;
+#pragma unroll
+                for (int v = 0; v < VEC; ++v)
+                    acc[v] = add ? acc[v] + g[u] * y[u][v] : acc[v];
+            }
         }
         if (BF16) {
             unsigned short *o = static_cast<unsigned short *>(out) + t * d + c;

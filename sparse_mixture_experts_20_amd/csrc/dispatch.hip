@@ -123,15 +123,26 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
         cur_e[s] = e;
     }
     __syncthreads();
-    // per expert: exclusive prefix over the waves, starting at the base
-    for (int e = tid; e < E; e += kThreads) {
-        int run = base[e];
-        for (int ww = 0; ww < kWavesPerBlock; ++ww) {
-            const int c = wcnt[ww * E + e];
-            wcnt[ww * E + e] = run;
-            run += c;
+    // per expert: exclusive prefix over the waves, starting at the base; the
+    // 16 wave counts of an expert sit on 16 lanes of one wave and are scanned
+    // with shuffles (64 experts per pass)
+    static_assert(kWavesPerBlock == 16, "one 16-lane group per expert");
+    for (int e0 = 0; e0 < E; e0 += kThreads / kWavesPerBlock) {
+        const int e = e0 + tid / kWavesPerBlock, ww = tid % kWavesPerBlock;
+        const int c = e < E ? wcnt[ww * E + e] : 0;
+        const int b0 = e < E ? base[e] : 0;
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < kWavesPerBlock; off <<= 1) {
+            const int o = __shfl_up(incl, off, kWavesPerBlock);
+            if (ww >= off)
+                incl += o;
         }
-        base[e] = run;   // assignments up to the end of this chunk
+        if (e < E) {
+            wcnt[ww * E + e] = b0 + incl - c;
+            if (ww == kWavesPerBlock - 1)
+                base[e] = b0 + incl;   // assignments up to the end of this chunk
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -151,18 +162,44 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
         return;
     for (int e = tid; e < E; e += kThreads)
         used[e] = base[e] < ceff ? base[e] : ceff;
-    if (tid == 0) {
-        // tile schedule of the expert kernels: prefix sums of row tiles of 128 and 256
-        int a128 = 0, a256 = 0;
-        for (int e = 0; e < E; ++e) {
-            tiles[e] = a128;
-            tiles[E + 1 + e] = a256;
-            const int u = base[e] < ceff ? base[e] : ceff;
-            a128 += (u + 127) / 128;
-            a256 += (u + 255) / 256;
+    if (tid < kWave) {
+        // tile schedule of the expert kernels: exclusive prefix sums of row
+        // tiles of 128 and 256 over the experts, 4 experts per lane of wave 0
+        constexpr int Q = kMaxExperts / kWave;
+        int c128[Q], c256[Q], s128 = 0, s256 = 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int e = tid * Q + q;
+            const int u = e < E ? (base[e] < ceff ? base[e] : ceff) : 0;
+            c128[q] = (u + 127) / 128;
+            c256[q] = (u + 255) / 256;
+            s128 += c128[q];
+            s256 += c256[q];
         }
-        tiles[E] = a128;
-        tiles[2 * E + 1] = a256;
+        int i128 = s128, i256 = s256;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int o128 = __shfl_up(i128, off), o256 = __shfl_up(i256, off);
+            if (lane >= off) {
+                i128 += o128;
+                i256 += o256;
+            }
+        }
+        int x128 = i128 - s128, x256 = i256 - s256;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int e = tid * Q + q;
+            if (e < E) {
+                tiles[e] = x128;
+                tiles[E + 1 + e] = x256;
+            }
+            x128 += c128[q];
+            x256 += c256[q];
+        }
+        if (lane == kWave - 1) {
+            tiles[E] = i128;
+            tiles[2 * E + 1] = i256;
+        }
     }
 }
 

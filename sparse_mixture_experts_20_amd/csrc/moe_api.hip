@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "common.hpp"
 
@@ -691,6 +693,46 @@ size_t moe_backward_workspace_size(int64_t N, int64_t d, int64_t E, int64_t d_ff
 // The backward; with `saved`, the forward state is the one a
 // moe_forward_train call left in the workspace (and in the exported routing
 // arrays) instead of being recomputed.
+// Second stream of a device for the backward's branch that needs only the
+// combine backward's outputs (the router-weight gradient and the
+// down-projection weight gradient), so that its products fill the CUs the
+// main chain's products leave idle in their last rounds; and the two events
+// that fork it from and join it to the caller's stream. Created on first use
+// with the device current, at the default priority, never destroyed. The
+// fork-to-join section of a call holds the device's lock, so calls from
+// several host threads cannot interleave their event records (their side
+// work serialises on the one side stream). NULL when unavailable: the branch
+// then runs on the caller's stream.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool failed = false;
+    std::mutex mu;
+};
+constexpr int kSideDevices = 64;
+static SideStream g_side[kSideDevices];
+static std::mutex g_side_init;
+
+static SideStream *side_stream() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices)
+        return nullptr;
+    SideStream &ss = g_side[dev];
+    std::lock_guard<std::mutex> g(g_side_init);
+    if (!ss.s && !ss.failed) {
+        if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) {
+            ss.s = nullptr;
+        } else if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+                   hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+            hipStreamDestroy(ss.s);
+            ss.s = nullptr;
+        }
+        ss.failed = ss.s == nullptr;
+        (void)hipGetLastError();   // a failed creation leaves no error behind
+    }
+    return ss.s ? &ss : nullptr;
+}
+
 static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
                          const moe_tensor *W_up, const moe_tensor *W_down,
                          const moe_expert_opts *opts, int k, float capacity_factor,
@@ -822,12 +864,49 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
     // chunk on the exact split of ds, then the chunks summed in order
     MOE_TRY(moe::launch_combine_backward(dout->data, Y, gate, slot, N, d, k, dY, ds, s,
                                          o.drop));
-    MOE_TRY(moe::launch_ds_split(ds, idx, N, Tc, S, Ei, k, dsT3, s));
+    // fork: the side stream s2 takes the router-weight gradient and (when the
+    // products read K-major) the down-projection weight gradient; both read
+    // only the forward state, ds and dY, and write buffers of their own
+    SideStream *ss = side_stream();
+    std::unique_lock<std::mutex> side_lock;
+    hipStream_t s2 = s;
+    if (ss) {
+        side_lock = std::unique_lock<std::mutex>(ss->mu);
+        MOE_TRY(hipEventRecord(ss->fork, s));
+        MOE_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
+        s2 = ss->s;
+    }
+    MOE_TRY(moe::launch_ds_split(ds, idx, N, Tc, S, Ei, k, dsT3, s2));
     MOE_TRY(moe::launch_transpose_rows(x->data, d, Tc, nullptr, N, nullptr, k, 0, Tc, 3, (int)S,
-                                       xT3, s));
+                                       xT3, s2));
     MOE_TRY(moe::launch_batched_gemm_bf16(dsT3, xT3, E, 3 * Tc, d, (int)S, E * 3 * Tc,
-                                          d * 3 * Tc, E * d, gpart, s));
-    MOE_TRY(moe::launch_chunk_sum(gpart, S, E * d, static_cast<float *>(dW_g->data), s));
+                                          d * 3 * Tc, E * d, gpart, s2));
+    MOE_TRY(moe::launch_chunk_sum(gpart, S, E * d, static_cast<float *>(dW_g->data), s2));
+    const bool kmajor = ceff <= moe::kGradMaxRows;
+    if (kmajor) {
+        MOE_TRY(moe::launch_weight_grad(dY, d, H, d_ff, Ei, ceff, used, st, 1, 0,
+                                        static_cast<float *>(dW_down->data), s2));
+        if (db_down)
+            MOE_TRY(moe::launch_colsum_rows(dY, d, Ei, ceff, used, st, 1,
+                                            static_cast<float *>(db_down->data), s2));
+    }
+    // joined at the end of the call (also when a launch below fails)
+    struct Join {
+        SideStream *ss;
+        hipStream_t s, s2;
+        bool done = false;
+        int operator()() {
+            done = true;
+            if (ss && (hipEventRecord(ss->join, s2) != hipSuccess ||
+                       hipStreamWaitEvent(s, ss->join, 0) != hipSuccess))
+                return MOE_ERR_HIP;
+            return MOE_OK;
+        }
+        ~Join() {
+            if (!done)
+                (*this)();
+        }
+    } join{ss, s, s2};
     // experts, input side: dZ = (dY W_down) [H > 0]; dX = dZ W_up; dx
     // (the weights are read K-major by the products themselves)
     MOE_TRY(moe::launch_expert_dz(dY, W_down->data, gelu ? dZ : H, o.act, d, d_ff, Ei, k, ceff,
@@ -836,20 +915,16 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
                                         dXa, rpe, s));
     MOE_TRY(moe::launch_dx(dXa, ds, idx, slot, static_cast<const float *>(W_g->data), N, d, k,
                            static_cast<float *>(dx->data), s));
-    // experts, weight side: dW_down = dY^T H, dW_up = dZ^T X over each
-    // expert's kept rows, read K-major by the products themselves
-    if (ceff <= moe::kGradMaxRows) {
-        MOE_TRY(moe::launch_weight_grad(dY, d, H, d_ff, Ei, ceff, used, st, 1, 0,
-                                        static_cast<float *>(dW_down->data), s));
+    // experts, weight side: dW_down = dY^T H (on the side stream, above),
+    // dW_up = dZ^T X over each expert's kept rows, read K-major by the
+    // products themselves
+    if (kmajor) {
         MOE_TRY(moe::launch_weight_grad(dZ, d_ff, x->data, d, Ei, ceff, used, st, k, 1,
                                         static_cast<float *>(dW_up->data), s));
-        if (db_down)
-            MOE_TRY(moe::launch_colsum_rows(dY, d, Ei, ceff, used, st, 1,
-                                            static_cast<float *>(db_down->data), s));
         if (db_up)
             MOE_TRY(moe::launch_colsum_rows(dZ, d_ff, Ei, ceff, used, nullptr, 1,
                                             static_cast<float *>(db_up->data), s));
-        return MOE_OK;
+        return join();
     }
     // (longer experts: through transposes, K = kept rows padded to Kp;
     // bias gradients: the row sums of the transposed dY and dZ)
@@ -865,7 +940,7 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
         MOE_TRY(moe::launch_row_sums(T2, E * d_ff, Kp, static_cast<float *>(db_up->data), s));
     MOE_TRY(moe::launch_batched_gemm_bf16(T2, T1, d_ff, Kp, d, Ei, d_ff * Kp, d * Kp, d_ff * d,
                                           static_cast<float *>(dW_up->data), s));
-    return MOE_OK;
+    return join();
 }
 
 int moe_backward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,

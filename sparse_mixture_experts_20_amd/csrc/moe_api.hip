@@ -701,8 +701,10 @@ size_t moe_backward_workspace_size(int64_t N, int64_t d, int64_t E, int64_t d_ff
 // with the device current, at the default priority, never destroyed. The
 // fork-to-join section of a call holds the device's lock, so calls from
 // several host threads cannot interleave their event records (their side
-// work serialises on the one side stream). NULL when unavailable: the branch
-// then runs on the caller's stream.
+// work serialises on the one side stream). Under stream capture the events
+// fork and join the side stream inside the captured graph; the stream is
+// not created during a capture (creation is not a capturable operation).
+// NULL when unavailable: the branch then runs on the caller's stream.
 struct SideStream {
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
@@ -713,13 +715,18 @@ constexpr int kSideDevices = 64;
 static SideStream g_side[kSideDevices];
 static std::mutex g_side_init;
 
-static SideStream *side_stream() {
+static SideStream *side_stream(hipStream_t caller) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices)
         return nullptr;
     SideStream &ss = g_side[dev];
     std::lock_guard<std::mutex> g(g_side_init);
     if (!ss.s && !ss.failed) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
         if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) {
             ss.s = nullptr;
         } else if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
@@ -867,7 +874,7 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
     // fork: the side stream s2 takes the router-weight gradient and (when the
     // products read K-major) the down-projection weight gradient; both read
     // only the forward state, ds and dY, and write buffers of their own
-    SideStream *ss = side_stream();
+    SideStream *ss = side_stream(s);
     std::unique_lock<std::mutex> side_lock;
     hipStream_t s2 = s;
     if (ss) {

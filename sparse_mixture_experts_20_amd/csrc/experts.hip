@@ -62,11 +62,16 @@ __device__ __forceinline__ unsigned lds_off(const void *p) {
 }
 
 // A K-major operand tile ([BKT rows of K][BN columns], 16-byte chunks) keeps
-// chunk c of row r at position c ^ tr_swizzle(r): the 16 rows one transposing
-// read touches (4 rows in each of 4 lane groups, rows 8g + 4h + 0..3) take 8
-// distinct even offsets (4 in rows of 8 chunks), so its 64 lanes hit every
-// bank at most twice.
+// chunk c of row r at position c ^ tr_swizzle(r). One transposing read
+// touches 16 rows (4 rows in each of 4 lane groups g: rows 8g + 4h + 0..3)
+// and an aligned pair of chunks in each. Rows of 16 or more chunks: the 16
+// rows take 8 distinct even offsets, so the 64 lanes hit every bank at most
+// twice. Rows of 8 chunks (two rows per 256-byte bank row): rows of equal
+// parity must take distinct pairs, which bits 1 and 3 of r give (rows
+// 8g + 4h + j of two lane groups g, g + 1).
 __device__ __forceinline__ int tr_swizzle(int r, int chunks_per_row) {
+    if (chunks_per_row == 8)
+        return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
     const int h = (r & 3) | ((((r >> 3) ^ (r >> 2)) & 1) << 2);
     return (2 * h) & (chunks_per_row - 1);
 }

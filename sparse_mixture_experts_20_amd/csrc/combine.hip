@@ -10,11 +10,10 @@
 // fp32), accumulates in fp32 in choice order and rounds once to the output
 // type. A pure streaming kernel: k*d*sizeof(Y) bytes read per token and
 // d*sizeof(out) bytes written. bf16 rows are read 8 columns (16 bytes) at a
-// time. The slots, gates and rows of up to kGroup choices are loaded
-// together (one memory round trip, not two per choice): the row of a
-// dropped assignment is read too (it lies inside Y but was never written)
-// and then not added, by selection rather than by a zero weight, so that
-// whatever it holds cannot reach the sum.
+// time. The slots and gates of up to kGroup choices are loaded together,
+// then the rows of the kept ones together (two memory round trips per group
+// rather than two per choice); a dropped assignment's row is neither read
+// nor added.
 #include "common.hpp"
 
 namespace moe {
@@ -72,23 +71,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ Y,
         for (int v = 0; v < VEC; ++v)
             acc[v] = 0.f;
         for (int j0 = 0; j0 < k; j0 += kGroup) {
-            int sl[kGroup];
+            bool kept[kGroup];
             float g[kGroup], y[kGroup][VEC];
 #pragma unroll
             for (int u = 0; u < kGroup; ++u) {
-                // past the last choice: reload the group's first (not added)
-                const int64_t a = t * k + (j0 + u < k ? j0 + u : j0);
-                sl[u] = slot[a];
+                // (past the token's last choice: its last assignment, not added)
+                const int64_t a = t * k + (j0 + u < k ? j0 + u : k - 1);
+                kept[u] = j0 + u < k && slot[a] >= 0;
                 g[u] = gate[a];
-                load_row<VEC>(Y + a * d + c, y[u]);
             }
 #pragma unroll
-            for (int u = 0; u < kGroup; ++u) {
-                const bool add = j0 + u < k && sl[u] >= 0;
+            for (int u = 0; u < kGroup; ++u)
+                if (kept[u])
+                    load_row<VEC>(Y + (t * k + j0 + u) * d + c, y[u]);
 #pragma unroll
-                for (int v = 0; v < VEC; ++v)
-                    acc[v] = add ? acc[v] + g[u] * y[u][v] : acc[v];
-            }
+            for (int u = 0; u < kGroup; ++u)
+                if (kept[u]) {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v)
+                        acc[v] += g[u] * y[u][v];
+                }
         }
         if (BF16) {
             unsigned short *o = static_cast<unsigned short *>(out) + t * d + c;

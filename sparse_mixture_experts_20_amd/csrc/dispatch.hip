@@ -124,9 +124,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     }
     __syncthreads();
     // per expert: exclusive prefix over the waves, starting at the base; the
-    // 16 wave counts of an expert sit on 16 lanes of one wave and are scanned
-    // with shuffles (64 experts per pass)
-    static_assert(kWavesPerBlock == 16, "one 16-lane group per expert");
+    // wave counts of an expert sit on kWavesPerBlock lanes of one wave and are
+    // scanned with shuffles (kThreads / kWavesPerBlock experts per pass)
+    static_assert((kWavesPerBlock & (kWavesPerBlock - 1)) == 0 && kWavesPerBlock <= kWave,
+                  "one power-of-two lane group per expert");
     for (int e0 = 0; e0 < E; e0 += kThreads / kWavesPerBlock) {
         const int e = e0 + tid / kWavesPerBlock, ww = tid % kWavesPerBlock;
         const int c = e < E ? wcnt[ww * E + e] : 0;

@@ -71,14 +71,14 @@ def traffic_for(kernel, workload):
 def gemm_kernel_name(wl, C, mode):
     """Name of the expert-GEMM instantiation the library launches for this
     workload (mirrors the library's tile choice: 256x256 when experts hold
-    >= 512 rows on average and that gives >= 256 tiles or a wide product;
+    >= 256 rows on average and that gives >= 256 tiles or a wide product;
     128x128 in two K sets when 128x128 gives 192 to 383 tiles; 128x64 below
     that; else 128x128). Template arguments: tile rows, columns, waves along
     rows, columns and K, K-step, LDS stages, mode."""
     rpe = min(C, -(-wl.N * wl.k // wl.E))
     nout = wl.d_ff if mode == 0 else wl.d
     t256 = wl.E * -(-rpe // 256) * -(-nout // 256)
-    if rpe >= 512 and (t256 >= 256 or nout >= 2048):
+    if rpe >= 256 and (t256 >= 256 or nout >= 2048):
         return f"expert_gemm_kernel<256, 256, 2, 4, 1, 64, 2, {mode}>"
     t128 = wl.E * -(-rpe // 128) * -(-nout // 128)
     if t128 < 192:

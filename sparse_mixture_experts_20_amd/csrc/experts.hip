@@ -1018,7 +1018,7 @@ __global__ __launch_bounds__(256) void experts_f32_kernel(
 namespace {
 
 // Tile shapes (rows_per_expert = expected kept rows per expert):
-//  - 256x256, 8 waves of 128x64, one workgroup per CU: experts with >= 512
+//  - 256x256, 8 waves of 128x64, one workgroup per CU: experts with >= 256
 //    rows when that still gives a full grid or the product is wide;
 //  - 128x128 in two K sets (8 waves: 2 x 2 of 64x64 per set, K-step 128,
 //    one workgroup per CU): when 128x128 tiles give between 192 and 384
@@ -1036,7 +1036,7 @@ constexpr int kBK2 = 128;  // K-step of the K-set tile: two 32-wide MFMA steps p
 
 Tile pick_tile(int64_t rows_per_expert, int64_t Nout, int E) {
     const int64_t t256 = (int64_t)E * ((rows_per_expert + 255) / 256) * ((Nout + 255) / 256);
-    if (rows_per_expert >= 512 && (t256 >= 256 || Nout >= 2048))
+    if (rows_per_expert >= 256 && (t256 >= 256 || Nout >= 2048))
         return Tile::k256;
     const int64_t t128 = (int64_t)E * ((rows_per_expert + 127) / 128) * ((Nout + 127) / 128);
     if (t128 < 192)

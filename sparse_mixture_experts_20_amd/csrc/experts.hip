@@ -17,8 +17,9 @@
 // assignment-ordered buffer the combine reads. Both accumulate in fp32 and
 // round once to bf16 in the epilogue.
 //
-// bf16 kernel: a BM x BN output tile per workgroup, K-step 64, waves laid out
-// WAVES_M x WAVES_N with a 16x16x32 bf16 MFMA grid each. A and B K-tiles go
+// bf16 kernel: a BM x BN output tile per workgroup, K-step 64 (128 for the
+// tile of two K sets), waves laid out WAVES_M x WAVES_N (times WAVES_K sets
+// that share each K-step) with a 16x16x32 bf16 MFMA grid each. A and B K-tiles go
 // from global memory straight into a two-stage LDS ring (direct 16-byte
 // loads, no register round trip; 16-byte chunks XOR-swizzled per row so the
 // operand reads of a wave hit distinct banks); the loads of step kt+1 are
@@ -34,7 +35,8 @@
 // takes tile (b mod 8) * T/8 + b/8: every XCD works through one contiguous
 // range of tiles and the sharing happens inside its own L2. When the last
 // round of tiles would leave most workgroups idle, its tiles are cut into
-// K-ranges (split_plan below).
+// K-ranges (split_plan below); when the tiles just overflow one round, the
+// light last row tiles of the experts go last (partial_prefix below).
 #include <type_traits>
 
 #include "common.hpp"
@@ -305,8 +307,8 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // Z16 (MODE 0): when not NULL, the bf16 pre-activations (product plus bias)
 // are stored there too, [E, ceff, Nout] like H (by the fix-up for cut tiles).
 // 5: MODE 1 with training-mode dropout dp on the rows of Y, after the bias
-// (its own instantiation: the generator's registers would make the plain
-// down product's epilogue spill).
+// (its own instantiation, so that the plain down product's epilogue carries
+// none of the generator's code or registers).
 // 6: weight gradient of expert e = blockIdx.y, O32[e] (fp32 [M, Nout]) =
 // sum over the expert's kept rows r < used[e] of A(r, :)^T B(r, :): both
 // operands K-major rows, A rows of width M = bsa, B rows of width Nout; the

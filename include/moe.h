@@ -292,7 +292,13 @@ int moe_combine(int64_t N, int64_t d, int k, const moe_tensor *Y, const float *t
  * Products run on the matrix cores with bf16 operands (dy and dZ are rounded
  * to bf16; fp32 ds is split exactly into three bf16 terms) and fp32
  * accumulation; every sum has a fixed order. MOE_ERR_UNSUPPORTED for fp32
- * layers. Device pointers 16-byte aligned (MOE_ERR_ALIGN). */
+ * layers. Device pointers 16-byte aligned (MOE_ERR_ALIGN).
+ * Streams: part of the work (the router-weight gradient and dW_down) runs on
+ * a second stream that the library creates for the device on its first
+ * backward call outside a stream capture (default priority, kept until the
+ * process ends). It is forked from and joined to stats->stream with events
+ * inside the call, so the call stays ordered on stats->stream like a single
+ * launch, and it can be captured in a graph. */
 int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
                  const moe_tensor *W_up, const moe_tensor *W_down, int k, float capacity_factor,
                  const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g, moe_tensor *dW_up,

@@ -148,6 +148,32 @@ def test_benchmark_layer_matches_oracle(torch_mod, name, nrows):
     _free(torch, dev, out)
 
 
+def test_light_tiles_last_with_split(torch_mod):
+    """A layer whose up product (256x256 tiles: 288, of which 192 heavy) and
+    down product (128x128 in two K sets: 320, of which 256 heavy) both
+    overflow one round of 256 workgroups while their heavy tiles fit, and
+    both cut their last round into K-ranges: the light last row tiles run
+    last and are the ones the fix-up sums. Every token with a choice in an
+    expert's last row tile (rank 512 or more) is compared, with random
+    others."""
+    torch = torch_mod
+    wl = W.custom("light_last_split", N=2200, d=1024, E=8, k=2, d_ff=3072, dtype="bf16",
+                  cf=1.25, sigma=0.3, seed=601, w_std=0.03)
+    dev = _upload(wl, keep_host=True)
+    out, st = G.run_forward(dev)
+    torch.cuda.synchronize()
+    route = oracle.forward(wl, rows=[0])
+    assert sorted(route.used.tolist())[0] > 512   # three row tiles of 256 per expert
+    late = np.nonzero((route.slot >= 512).any(axis=1))[0]
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([late, rng.choice(wl.N, size=64, replace=False)]))
+    G.say(f"[parity] light_last_split: {len(late)} tokens in last row tiles, {len(rows)} rows")
+    res = oracle.forward(wl, rows=rows)
+    G.check_routing(res, st)
+    G.check_out("bf16", G.out_f64(wl, out, rows), res.out)
+    _free(torch, dev, out)
+
+
 def test_forward_is_deterministic(torch_mod):
     torch = torch_mod
     wl = W.make("nanomoe")

@@ -79,7 +79,7 @@ def gemm_kernel_name(wl, C, mode):
     nout = wl.d_ff if mode == 0 else wl.d
     t256 = wl.E * -(-rpe // 256) * -(-nout // 256)
     if rpe >= 256 and (t256 >= 256 or nout >= 2048):
-        return f"expert_gemm_kernel<256, 256, 2, 4, 1, 64, 2, {mode}>"
+        return f"expert_gemm_kernel<256, 256, 4, 4, 1, 64, 2, {mode}>"
     t128 = wl.E * -(-rpe // 128) * -(-nout // 128)
     if t128 < 192:
         return f"expert_gemm_kernel<128, 64, 2, 2, 1, 64, 2, {mode}>"

@@ -281,7 +281,8 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // bank row), so the 16 lanes that read 16 consecutive rows at one chunk hit
 // 16 distinct bank groups.
 // Two waves per SIMD (the LDS budget allows no more), so the compiler may use
-// up to 256 registers per lane and schedule for latency rather than occupancy.
+// up to 256 registers per lane and schedule for latency rather than occupancy;
+// a tile of 16 waves runs four per SIMD with up to 128 registers each.
 // MODE 0: up product (gathered token rows, activation, bf16 H into O16);
 // 1: down product (bf16 rows of Y scattered to their assignment, into O16);
 // 2: plain product of ceff rows of A into fp32 rows of O32 (no gather, no
@@ -620,8 +621,10 @@ void expert_gemm_kernel(
         }
     };
     // (the 256x256 weight-gradient tile reads one step's fragments at a time:
-    // with both operands transposed, a second set would not fit in registers)
-    constexpr bool kPrefetchFrags = !(MODE == 6 && BM * BN >= 256 * 256);
+    // with both operands transposed, a second set would not fit in registers;
+    // so does a tile of 16 waves, four per SIMD, whose 128 registers per lane
+    // hold one set)
+    constexpr bool kPrefetchFrags = !(MODE == 6 && BM * BN >= 256 * 256) && NW < 16;
     auto compute = [&](int st, auto full) {
         if constexpr (kPrefetchFrags) {
             bf16x8 af[2][FM], bfr[2][FN];
@@ -1020,8 +1023,9 @@ __global__ __launch_bounds__(256) void experts_f32_kernel(
 namespace {
 
 // Tile shapes (rows_per_expert = expected kept rows per expert):
-//  - 256x256, 8 waves of 128x64, one workgroup per CU: experts with >= 256
-//    rows when that still gives a full grid or the product is wide;
+//  - 256x256, one workgroup per CU: experts with >= 256 rows when that still
+//    gives a full grid or the product is wide (16 waves of 64x64 for the
+//    forward products, 8 of 128x64 for the backward's K-major ones);
 //  - 128x128 in two K sets (8 waves: 2 x 2 of 64x64 per set, K-step 128,
 //    one workgroup per CU): when 128x128 tiles give between 192 and 384
 //    tiles, i.e. about one per CU (the operand reuse of 64x64 wave tiles,
@@ -1129,10 +1133,21 @@ hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W,
                                                               O32, Z16, dp);
         t = Tile::k128x64;   // K-major right operands: no K sets
     }
-    if (t == Tile::k256)
-        return launch_tiles<256, 256, 2, 4, 1, kBK, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
-                                                  tiles + E + 1, O16, pf, part_bytes, act, bias,
-                                                  s, mask, O32, Z16, dp);
+    if (t == Tile::k256) {
+        // forward products: 16 waves of 64x64 (four per SIMD, more latency
+        // hidden than the 8 waves of 128x64 save in LDS reads); the backward's
+        // K-major products keep 8 waves (16 would spill there)
+        if constexpr (MODE == 0 || MODE == 1 || MODE == 5)
+            return launch_tiles<256, 256, 4, 4, 1, kBK, MODE>(A, W, K, Nout, E, k, ceff, used,
+                                                              slot_token, tiles + E + 1, O16, pf,
+                                                              part_bytes, act, bias, s, mask,
+                                                              O32, Z16, dp);
+        else
+            return launch_tiles<256, 256, 2, 4, 1, kBK, MODE>(A, W, K, Nout, E, k, ceff, used,
+                                                              slot_token, tiles + E + 1, O16, pf,
+                                                              part_bytes, act, bias, s, mask,
+                                                              O32, Z16, dp);
+    }
     if (t == Tile::k128x64)
         return launch_tiles<128, 64, 2, 2, 1, kBK, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
                                                  tiles, O16, pf, part_bytes, act, bias, s, mask,

@@ -84,7 +84,7 @@ def gemm_kernel_name(wl, C, mode):
     if t128 < 192:
         return f"expert_gemm_kernel<128, 64, 2, 2, 1, 64, 2, {mode}>"
     if t128 < 384:
-        return f"expert_gemm_kernel<128, 128, 2, 2, 2, 128, 2, {mode}>"
+        return f"expert_gemm_kernel<128, 128, 2, 4, 2, 128, 2, {mode}>"
     return f"expert_gemm_kernel<128, 128, 2, 2, 1, 64, 2, {mode}>"
 
 

@@ -1026,10 +1026,9 @@ namespace {
 //  - 256x256, one workgroup per CU: experts with >= 256 rows when that still
 //    gives a full grid or the product is wide (16 waves of 64x64 for the
 //    forward products, 8 of 128x64 for the backward's K-major ones);
-//  - 128x128 in two K sets (8 waves: 2 x 2 of 64x64 per set, K-step 128,
+//  - 128x128 in two K sets (16 waves: 2 x 4 of 64x32 per set, K-step 128,
 //    one workgroup per CU): when 128x128 tiles give between 192 and 384
-//    tiles, i.e. about one per CU (the operand reuse of 64x64 wave tiles,
-//    with two waves per SIMD to hide latency);
+//    tiles, i.e. about one per CU (four waves per SIMD to hide latency);
 //  - 128x64, 4 waves of 64x32: when 128x128 tiles would leave more CUs idle
 //    (fewer than 192 tiles), trading operand reuse for parallelism;
 //  - 128x128, 4 waves of 64x64, two workgroups per CU: otherwise.
@@ -1127,7 +1126,7 @@ hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W,
     float *pf = static_cast<float *>(part);
     if (t == Tile::k128k2) {
         if constexpr (MODE == 0 || MODE == 1 || MODE == 5)
-            return launch_tiles<128, 128, 2, 2, 2, kBK2, MODE>(A, W, K, Nout, E, k, ceff, used,
+            return launch_tiles<128, 128, 2, 4, 2, kBK2, MODE>(A, W, K, Nout, E, k, ceff, used,
                                                               slot_token, tiles, O16, pf,
                                                               part_bytes, act, bias, s, mask,
                                                               O32, Z16, dp);

@@ -3,8 +3,9 @@
 
 One step = one moe_forward call (router, dispatch plan, grouped expert FFN,
 combine) over one batch of seeded synthetic tokens already resident in HBM.
-Default workload: the nanoMoE-shaped layer (2048 tokens, d=768, E=8, k=2,
-d_ff=3072, bf16, capacity factor 1.25, noise sigma 1.0).
+Default workload: the fine-grained many-expert layer, the largest of the
+layer shapes (8192 tokens, d=7168, E=256, k=8, d_ff=2048, bf16, capacity
+factor 1.5); --workload selects another.
 
 With --pass backward, one step is one moe_backward call instead (the
 forward state recomputed, then the gradients of x, W_g, W_up and W_down for
@@ -14,12 +15,23 @@ moe_backward_after_forward). Both are reported in the same JSON form;
 --dropout P adds the training-mode dropout on the expert outputs to either.
 
 Prints ONE JSON line on stdout. Besides the contract fields it carries:
-  roofline      the dominant kernel (the larger of the two expert GEMMs)
-                against bf16 MFMA peak, its duration timed with HIP events on
-                the stream it runs on;
+  roofline      the dominant kernel (the slower of the two expert products)
+                against its binding roofline: HBM when its arithmetic
+                intensity (flops per algorithmic byte) is below the bf16
+                ridge 2.5 PFLOP/s / 8 TB/s, else the bf16 MFMA peak; both
+                fractions are given. Its duration is timed with HIP events
+                on the stream it runs on, each repetition after a 1 GiB
+                write that flushes the L2 caches and the 256 MB MALL;
   cpu_baseline  the CPU oracle timed on this host on a bounded sample;
-  stages        per-stage average durations (HIP events) and derived rates.
+  secondary     per-stage average durations (flushed and back to back) and
+                derived rates.
 Diagnostics go to stderr.
+
+Measurement helpers (not timed runs):
+  --probe             a 1 GiB device copy (the counter calibration), then
+                      --steps forwards: the program rocprofv3 --pmc runs;
+  --traffic-summary   turns two such counter runs (FETCH_SIZE, WRITE_SIZE)
+                      into HBM bytes per launch in profiles/traffic.json.
 """
 import argparse
 import hashlib
@@ -68,24 +80,13 @@ def traffic_for(kernel, workload):
     return e.get("bytes_per_launch")
 
 
-def gemm_kernel_name(wl, C, mode):
-    """Name of the expert-GEMM instantiation the library launches for this
-    workload (mirrors the library's tile choice: 256x256 when experts hold
-    >= 256 rows on average and that gives >= 256 tiles or a wide product;
-    128x128 in two K sets when 128x128 gives 192 to 383 tiles; 128x64 below
-    that; else 128x128). Template arguments: tile rows, columns, waves along
-    rows, columns and K, K-step, LDS stages, mode."""
-    rpe = min(C, -(-wl.N * wl.k // wl.E))
-    nout = wl.d_ff if mode == 0 else wl.d
-    t256 = wl.E * -(-rpe // 256) * -(-nout // 256)
-    if rpe >= 256 and (t256 >= 256 or nout >= 2048):
-        return f"expert_gemm_kernel<256, 256, 4, 4, 1, 64, 2, {mode}>"
-    t128 = wl.E * -(-rpe // 128) * -(-nout // 128)
-    if t128 < 192:
-        return f"expert_gemm_kernel<128, 64, 2, 2, 1, 64, 2, {mode}>"
-    if t128 < 384:
-        return f"expert_gemm_kernel<128, 128, 2, 4, 2, 128, 2, {mode}>"
-    return f"expert_gemm_kernel<128, 128, 2, 2, 1, 64, 2, {mode}>"
+def gemm_kernel_name(wl, mode):
+    """Name of the expert-product kernel the library launches for this
+    workload (mode 0: up, 1: down), from the library's own query."""
+    import torch
+    from sparse_mixture_experts_20_amd import binding as B
+    dt = torch.bfloat16 if wl.cfg.dtype == "bf16" else torch.float32
+    return B.expert_kernel_name(wl.N, wl.d, wl.E, wl.d_ff, wl.k, wl.cfg.cf, dt, mode)
 
 
 def cpu_baseline(wl, target_s=15.0):
@@ -286,52 +287,71 @@ def bench_backward(args, wl, dev, train=False):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__,
-                                 formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="nanomoe",
-                    choices=["nanomoe", "mixtral", "skew", "finegrained", "tiny", "nanomoe_gelu"])
-    ap.add_argument("--stage-reps", type=int, default=50)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "train"],
-                    default="forward",
-                    help="time the layer's forward (default), its backward pass, or a "
-                         "training step (forward keeping its state + backward)")
-    ap.add_argument("--dropout", type=float, default=0.0,
-                    help="training-mode dropout probability on the expert outputs "
-                         "(generator seed 1, offset 0); 0 = none")
-    args = ap.parse_args()
-    if not 0.0 <= args.dropout < 1.0:
-        ap.error("--dropout must be in [0, 1)")
-    if args.dropout > 0 and args.which == "forward":
-        ap.error("--dropout is training-mode: use it with --pass backward or --pass train")
+FLUSH_BYTES = 1 << 30     # more than the L2 caches and the 256 MB MALL together
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
-              f"{world}); the layer has no multi-GPU path in this build.", file=sys.stderr)
-        sys.exit(2)
+
+class Flusher:
+    """Writes a 1 GiB device buffer (torch's fill kernel on the current
+    stream), evicting every operand of the previous launch from the L2 caches
+    and the MALL before a timed repetition."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(self.i)
+
+
+def time_stage(fn, reps, flush=None):
+    """Average duration (ms) of fn() from HIP events on torch's current
+    stream (the stream the library launches on), each rep bracketed by its
+    own pair of events; with `flush`, a cache flush precedes every rep
+    outside its events."""
+    import torch
+    for _ in range(3):
+        if fn() != 0:
+            raise RuntimeError("stage failed")
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+def algorithmic(wl, kept):
+    """Bytes and flops a launch of each stage must move or compute at least
+    (the layer's own arithmetic, not the kernels'): per stage (bytes, flops)."""
+    xb = 2 if wl.cfg.dtype == "bf16" else 4
+    N, d, E, k, dff = wl.N, wl.d, wl.E, wl.k, wl.d_ff
+    noise = N * E * 4 if wl.noise is not None else 0
+    w = E * dff * d * xb                       # one expert weight tensor
+    prod = 2.0 * kept * d * dff                # one expert product
+    return {
+        "router": (N * d * xb + E * d * 4 + noise + N * k * 8, 2.0 * N * d * E),
+        "dispatch": (N * k * 8 + kept * 4, 0.0),
+        "expert_up": (N * d * xb + w + kept * dff * xb, prod),
+        "expert_down": (kept * dff * xb + w + kept * d * 4, prod),      # Y rows are fp32
+        "combine": (kept * d * 4 + N * k * 8 + N * d * xb, 2.0 * kept * d),
+    }
+
+
+def bench_forward(args, wl, dev):
+    import ctypes
 
     import torch
     from sparse_mixture_experts_20_amd import binding as B
-    from sparse_mixture_experts_20_amd import device as D
-    from sparse_mixture_experts_20_amd import workloads as W
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a HIP device", file=sys.stderr)
-        sys.exit(1)
-    B.lib()
-    wl = W.make(args.workload)
     cfg = wl.cfg
-    log(f"[bench] workload {cfg.name}: N={wl.N} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff} "
-        f"{cfg.dtype} cf={cfg.cf}")
-    dev = D.upload(wl, keep_host=not args.no_cpu_baseline)
-    if args.which in ("backward", "train"):
-        bench_backward(args, wl, dev, train=args.which == "train")
-        return
     fwd = B.Forward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
                     cfg.cf, export=True, act=dev["act"],
                     b_up=dev["b_up"], b_down=dev["b_down"])
@@ -363,11 +383,10 @@ def main():
     slot, usedt, slot_token, tiles = B.dispatch(idx, wl.E, C)
     ceff = min(C, wl.N)
     H = torch.empty((wl.E, max(ceff, 1), wl.d_ff), dtype=x.dtype, device="cuda")
-    Y = torch.empty((wl.N * wl.k, wl.d), dtype=x.dtype, device="cuda")
+    Y = torch.empty((wl.N * wl.k, wl.d), dtype=torch.float32, device="cuda")
     out = torch.empty_like(x)
     # each stage's C entry point with its arguments marshalled once, so the
     # timed loop is not bound by Python-side argument handling
-    import ctypes
     L = B.lib()
     r = ctypes.byref
     dx, dg, dn, du, dd, do, dy = (B.desc(x), B.desc(wg), B.desc(nz), B.desc(wu), B.desc(wd),
@@ -376,13 +395,15 @@ def main():
     p = B._ptr
     rws = B.alloc_workspace(B.router_workspace_size(wl.N, wl.d, wl.E, x.dtype))
     ews = B.alloc_workspace(B.expert_workspace_size(x.dtype))
+    dws = B.alloc_workspace(B.dispatch_workspace_size(wl.N, wl.E, wl.k))
     eo = B.ExpertOpts(dev["act"], dev["b_up"], dev["b_down"])   # the workload's expert
     opts = eo.ref()
     stages = {
         "router": lambda: L.moe_router(r(dx), r(dg), r(dn) if dn else None, wl.k, p(idx),
                                        p(gate), p(rws), rws.numel(), s_),
-        "dispatch": lambda: L.moe_dispatch(wl.N, wl.E, wl.k, C, p(idx), p(slot), p(usedt),
-                                           p(slot_token), p(tiles), s_),
+        "dispatch": lambda: L.moe_dispatch(wl.N, wl.E, wl.k, C, p(idx), p(gate), p(slot),
+                                           p(usedt), p(slot_token), p(tiles), None, None, None,
+                                           p(dws), dws.numel(), s_),
         "expert_up": lambda: L.moe_expert_up_ex(r(dx), r(du), opts, wl.k, C, p(usedt),
                                                 p(slot_token), p(tiles), p(H), p(ews),
                                                 ews.numel(), s_),
@@ -391,49 +412,41 @@ def main():
                                                     ews.numel(), s_),
         "combine": lambda: L.moe_combine(wl.N, wl.d, wl.k, r(dy), p(gate), p(slot), r(do), s_),
     }
-    st_ms = {}
-    for name, fn in stages.items():
-        for _ in range(3):
-            if fn() != 0:
-                raise RuntimeError(f"stage {name} failed")
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.stage_reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        st_ms[name] = e0.elapsed_time(e1) / args.stage_reps
-    gemm_flops = 2.0 * kept * wl.d * wl.d_ff          # one of the two products
-    s = dict(st_ms)
-    xbytes = 2 if cfg.dtype == "bf16" else 4
-    router_bytes = wl.N * wl.d * xbytes + wl.E * wl.d * 4 + wl.N * wl.k * 8 + (
-        wl.N * wl.E * 4 if wl.noise is not None else 0)
-    combine_bytes = kept * wl.d * xbytes + wl.N * wl.k * 8 + wl.N * wl.d * xbytes
-    up_tflops = gemm_flops / (s["expert_up"] * 1e-3) / 1e12
-    down_tflops = gemm_flops / (s["expert_down"] * 1e-3) / 1e12
-    ffn_frac = (2 * gemm_flops) / ((s["expert_up"] + s["expert_down"]) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
-    router_gbps = router_bytes / (s["router"] * 1e-3) / 1e9
-    combine_gbps = combine_bytes / (s["combine"] * 1e-3) / 1e9
-    for n, v in s.items():
-        log(f"[bench] stage {n:12s} {v * 1e3:9.2f} us")
-    log(f"[bench] expert_up {up_tflops:.0f} TFLOP/s, expert_down {down_tflops:.0f} TFLOP/s, "
-        f"FFN {100 * ffn_frac:.1f}% of bf16 peak; router {router_gbps:.0f} GB/s; "
-        f"combine {combine_gbps:.0f} GB/s")
+    flush = Flusher()
+    warm = {n: time_stage(fn, args.stage_reps) for n, fn in stages.items()}
+    cold = {n: time_stage(fn, args.stage_reps, flush) for n, fn in stages.items()}
+    del flush
+    alg = algorithmic(wl, kept)
+    for n in stages:
+        gbps = alg[n][0] / (cold[n] * 1e-3) / 1e9
+        tf = alg[n][1] / (cold[n] * 1e-3) / 1e12
+        log(f"[bench] stage {n:12s} flushed {cold[n] * 1e3:9.2f} us ({gbps:7.0f} GB/s, "
+            f"{tf:6.1f} TFLOP/s); back to back {warm[n] * 1e3:9.2f} us")
 
-    dom = "expert_up" if s["expert_up"] >= s["expert_down"] else "expert_down"
-    dom_kernel = gemm_kernel_name(wl, C, 0 if dom == "expert_up" else 1)
-    achieved = gemm_flops / (s[dom] * 1e-3) / 1e12
+    dom = "expert_up" if cold["expert_up"] >= cold["expert_down"] else "expert_down"
+    dom_kernel = gemm_kernel_name(wl, 0 if dom == "expert_up" else 1)
+    nbytes, flops = alg[dom]
+    t = cold[dom] * 1e-3
+    intensity = flops / nbytes
+    hbm_bound = intensity < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    mfma_frac = flops / t / 1e12 / PEAK_BF16_TFLOPS
+    hbm_frac = nbytes / t / 1e9 / PEAK_HBM_GBPS
     roofline = {
         "kernel": dom_kernel,
-        "bound": "mfma",
-        "achieved": round(achieved, 2),
-        "peak": PEAK_BF16_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "bound": "hbm" if hbm_bound else "mfma",
+        "achieved": round(nbytes / t / 1e9 if hbm_bound else flops / t / 1e12, 2),
+        "peak": PEAK_HBM_GBPS if hbm_bound else PEAK_BF16_TFLOPS,
+        "unit": "GB/s" if hbm_bound else "TFLOP/s",
+        "frac": round(hbm_frac if hbm_bound else mfma_frac, 4),
         "traffic": traffic_for(dom_kernel, cfg.name),
-        "algorithmic_per_launch": f"2*kept*d*d_ff = {gemm_flops:.4g} flop (kept={kept})",
-        "avg_launch_us": round(s[dom] * 1e3, 2),
+        "mfma_frac": round(mfma_frac, 4),
+        "hbm_frac": round(hbm_frac, 4),
+        "algorithmic_per_launch": (f"{nbytes:.4g} B (x + weights + output rows) and "
+                                   f"2*kept*d*d_ff = {flops:.4g} flop (kept={kept}); "
+                                   f"{intensity:.0f} flop/B against the bf16 ridge "
+                                   f"{PEAK_BF16_TFLOPS / PEAK_HBM_GBPS * 1e3:.0f} flop/B"),
+        "avg_launch_us": round(cold[dom] * 1e3, 2),
+        "timing": "HIP events on the launch stream, L2 and MALL flushed before each rep",
     }
 
     cpu = None
@@ -442,6 +455,8 @@ def main():
         cpu = cpu_baseline(wl)
         log(f"[bench] cpu_baseline {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
 
+    ffn_frac = (2 * alg["expert_up"][1]) / ((cold["expert_up"] + cold["expert_down"]) * 1e-3) \
+        / 1e12 / PEAK_BF16_TFLOPS
     value = wl.N / (ms_per_step * 1e-3)
     line = {
         "metric": METRIC,
@@ -466,14 +481,197 @@ def main():
         "cpu_baseline": cpu,
         "secondary": {
             "expert_gemm_pct_mfma_peak": round(100 * ffn_frac, 2),
-            "router_hbm_GBps": round(router_gbps, 1),
-            "combine_hbm_GBps": round(combine_gbps, 1),
-            "expert_tflops": round(2 * gemm_flops / ((s["expert_up"] + s["expert_down"]) * 1e-3)
-                                   / 1e12, 1),
-            "stage_us": {k: round(v * 1e3, 2) for k, v in s.items()},
+            "router_hbm_GBps": round(alg["router"][0] / (cold["router"] * 1e-3) / 1e9, 1),
+            "combine_hbm_GBps": round(alg["combine"][0] / (cold["combine"] * 1e-3) / 1e9, 1),
+            "expert_tflops": round(2 * alg["expert_up"][1] /
+                                   ((cold["expert_up"] + cold["expert_down"]) * 1e-3) / 1e12, 1),
+            "stage_us_flushed": {k: round(v * 1e3, 2) for k, v in cold.items()},
+            "stage_us_back_to_back": {k: round(v * 1e3, 2) for k, v in warm.items()},
         },
     }
     print(json.dumps(line), flush=True)
+
+
+def probe(args, wl, dev):
+    """The program the HBM-traffic counter runs profile: a plain 1 GiB device
+    copy of known size (its counter readings against 1 GiB read and 1 GiB
+    written give the counter-to-bytes factors), then --steps forwards."""
+    import torch
+    from sparse_mixture_experts_20_amd import binding as B
+
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    fwd = B.Forward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
+                    wl.cfg.cf, export=True, act=dev["act"],
+                    b_up=dev["b_up"], b_down=dev["b_down"])
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    if args.probe_info:
+        # sizes and kept assignments, for the algorithmic byte counts
+        info = {"workload": wl.cfg.name, "N": wl.N, "d": wl.d, "E": wl.E, "k": wl.k,
+                "d_ff": wl.d_ff, "dtype": wl.cfg.dtype, "noise": dev["noise"] is not None,
+                "kept": int(fwd.used.sum().item()), "steps": args.steps}
+        with open(args.probe_info, "w") as f:
+            json.dump(info, f)
+    log(f"[bench] probe done: {wl.cfg.name}, {args.steps} forwards")
+
+
+# ---- HBM traffic from two rocprofv3 --pmc runs of --probe ------------------
+COPY = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_20_amd", "csrc")
+
+
+def _short(name):
+    n = name.replace("moe::(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0].strip()
+
+
+def _per_dispatch(run_dir, counter):
+    """Average counter value per dispatch, by kernel; for the calibration
+    copy, the largest dispatch (small copies of other data may share its
+    kernel name)."""
+    import collections
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    vals = collections.defaultdict(list)
+    for fn in files:
+        with open(fn) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    vals[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: (max(v) if k == COPY else sum(v) / len(v)) for k, v in vals.items()}
+
+
+def _algorithmic_bytes(kernel, p):
+    """Bytes a launch must move at least, from the probe's sizes and counts."""
+    N, d, E, k, dff, kept = p["N"], p["d"], p["E"], p["k"], p["d_ff"], p["kept"]
+    sx = 2 if p["dtype"] == "bf16" else 4
+    noise = N * E * 4 if p["noise"] else 0
+    m = re.search(r"expert_gemm_kernel<[^>]*, (\d)>", kernel)
+    if m and m.group(1) == "0":       # x (whole), W_up, H rows written
+        return N * d * sx + E * dff * d * sx + kept * dff * sx, "x + W_up + H"
+    if m and m.group(1) == "1":       # H rows read, W_down, fp32 Y rows written
+        return kept * dff * sx + E * d * dff * sx + kept * d * 4, "H + W_down + Y"
+    if kernel.startswith("router"):
+        return N * d * sx + E * d * 4 + noise + N * k * 8, "x + W_g + noise + ids/gates"
+    if kernel.startswith("combine"):
+        return kept * d * 4 + N * k * 8 + N * d * sx, "Y + ids/gates + out"
+    return None, ""
+
+
+def traffic_summary(workload, fetch_dir, write_dir, probe_json, out_json=TRAFFIC_FILE):
+    """Counter readings (KiB per dispatch) to bytes per launch: writes
+    profiles/traffic.json entries keyed "<kernel>/<workload>" (with the hash of
+    the kernel's source, so that stale entries are recognisable) and prints a
+    markdown table."""
+    with open(probe_json) as f:
+        pr = json.load(f)
+    fetch = _per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _per_dispatch(write_dir, "WRITE_SIZE")
+    ff = COPY_BYTES / (fetch[COPY] * 1024.0)
+    wf = COPY_BYTES / (write[COPY] * 1024.0)
+    try:
+        with open(out_json) as f:
+            out = json.load(f)
+    except (OSError, ValueError):
+        out = {}
+    out["_calibration"] = {
+        "copy_bytes": COPY_BYTES, "fetch_size_kib": fetch[COPY], "write_size_kib": write[COPY],
+        "fetch_factor": ff, "write_factor": wf,
+        "note": "bytes = counter_KiB * 1024 * factor, factors from a 1 GiB device copy"}
+    print("| kernel | fetch MB | write MB | total MB | algorithmic MB | total / algorithmic |")
+    print("|---|---|---|---|---|---|")
+    for kern in sorted(set(fetch) & set(write)):
+        if kern == COPY or kern.startswith("at::") or kern.startswith("void at::"):
+            continue   # the calibration copy and torch's own set-up kernels
+        fb = fetch[kern] * 1024.0 * ff
+        wb = write[kern] * 1024.0 * wf
+        alg, what = _algorithmic_bytes(kern, pr)
+        ratio = f"{(fb + wb) / alg:.2f}" if alg else "-"
+        algs = f"{alg / 1e6:.2f}" if alg else "-"
+        print(f"| `{kern}` | {fb / 1e6:.2f} | {wb / 1e6:.2f} | {(fb + wb) / 1e6:.2f} | {algs} "
+              f"| {ratio} |")
+        src = "experts.hip" if "gemm" in kern or "fixup" in kern else (
+            kern.split("_")[0] + ".hip")
+        path = os.path.join(CSRC, src)
+        out[f"{kern}/{workload}"] = {
+            "bytes_per_launch": int(round(fb + wb)), "fetch_bytes": int(round(fb)),
+            "write_bytes": int(round(wb)), "algorithmic_bytes": alg, "algorithmic": what,
+            "source_sha": source_sha(path) if os.path.exists(path) else None}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+
+
+WORKLOADS = ["finegrained", "mixtral", "skew", "nanomoe", "nanomoe_gelu", "tiny"]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="finegrained", choices=WORKLOADS)
+    ap.add_argument("--stage-reps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "train"],
+                    default="forward",
+                    help="time the layer's forward (default), its backward pass, or a "
+                         "training step (forward keeping its state + backward)")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="training-mode dropout probability on the expert outputs "
+                         "(generator seed 1, offset 0); 0 = none")
+    ap.add_argument("--probe", action="store_true",
+                    help="run the counter-calibration copy and --steps forwards, no timing")
+    ap.add_argument("--probe-info", default="",
+                    help="with --probe: write the workload's sizes and kept count here")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_JSON"),
+                    help="summarise two rocprofv3 --pmc runs of --probe for --workload (host)")
+    args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.workload, *args.traffic_summary)
+        return
+    if not 0.0 <= args.dropout < 1.0:
+        ap.error("--dropout must be in [0, 1)")
+    if args.dropout > 0 and args.which == "forward":
+        ap.error("--dropout is training-mode: use it with --pass backward or --pass train")
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); the layer has no multi-GPU path in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_mixture_experts_20_amd import binding as B
+    from sparse_mixture_experts_20_amd import device as D
+    from sparse_mixture_experts_20_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    B.lib()
+    wl = W.make(args.workload)
+    cfg = wl.cfg
+    log(f"[bench] workload {cfg.name}: N={wl.N} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff} "
+        f"{cfg.dtype} cf={cfg.cf}")
+    dev = D.upload(wl, keep_host=not args.no_cpu_baseline and not args.probe)
+    if args.probe:
+        probe(args, wl, dev)
+    elif args.which in ("backward", "train"):
+        bench_backward(args, wl, dev, train=args.which == "train")
+    else:
+        bench_forward(args, wl, dev)
 
 
 if __name__ == "__main__":

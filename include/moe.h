@@ -22,7 +22,9 @@
  * Conventions for every entry point:
  *  - All tensor data pointers are DEVICE pointers owned by the caller; the
  *    library never allocates, frees or retains device memory, and keeps no
- *    global mutable state. Tensors are row-major and contiguous.
+ *    global mutable state (every value a call needs, the device's compute
+ *    unit count and kernel occupancy included, is queried within the call).
+ *    Tensors are row-major and contiguous.
  *  - Work is enqueued on the given HIP stream (hipStream_t passed as void*;
  *    NULL = the default stream). Calls return without synchronising; the
  *    results are valid once the stream reaches them.
@@ -84,7 +86,27 @@ typedef struct {
  *   topk_gate      fp32  [N, k]  gates of those experts (sum to 1 per token)
  *   slot           int32 [N, k]  capacity slot of each assignment, -1 = dropped
  *   used_capacity  int32 [E]     kept assignments per expert (= min(count, C))
+ * Router statistics (optional device outputs, NULL = not computed). The
+ * pages name load imbalance and capacity drops as what a router must be
+ * watched for ("MoE（Mixture of Experts）とは？", section on MoE's weak
+ * points; "게이팅 위기(Gating Crisis)", section on the load-balancing
+ * challenge and its capacity-drop panel) and give no loss formula, so these
+ * are the counts that define them, with used_capacity (nanoMoE slide 14):
+ *   expert_demand    int32 [E]  assignments routed to expert e before the
+ *                               capacity clip (count[e] of slide 14)
+ *   expert_drops     int32 [E]  of those, the ones past the capacity
+ *                               (= expert_demand - used_capacity)
+ *   expert_gate_sum  fp32  [E]  sum of the gates of every assignment routed
+ *                               to e (kept or dropped), fp32, summed in a
+ *                               fixed order (identical on every run)
  * Host output: capacity (C), written before anything is enqueued.
+ * aux_stream (input, moe_backward* only; ignored by the forward): a second
+ * HIP stream of the same device, owned by the caller, that the backward may
+ * run part of its work on (the router-weight and down-projection weight
+ * gradients) while the rest runs on `stream`. The call forks it from and
+ * joins it back to `stream` with two events it creates and destroys within
+ * the call, so the call stays one stream-ordered operation on `stream` and
+ * can be captured in a graph. NULL: everything runs on `stream`.
  * Dropped assignments per call = N*k - sum(used_capacity). */
 typedef struct {
     void *stream;
@@ -95,6 +117,10 @@ typedef struct {
     int32_t *slot;
     int32_t *used_capacity;
     int64_t capacity;
+    int32_t *expert_demand;
+    int32_t *expert_drops;
+    float *expert_gate_sum;
+    void *aux_stream;
 } moe_stats;
 
 /* The whole layer forward (page 1 STEP 1-12; nanoMoE slides 11-40).
@@ -111,10 +137,10 @@ typedef struct {
  *   out    [N, d] (same shape as x) same dtype as x; every row is written
  *   stats  launch context and optional exports (required)
  * Numerics: scores, top-k and gates in fp32; expert products accumulate in
- * fp32 (bf16 inputs on matrix cores); the hidden activation and each
- * expert's output row are stored in the dtype of x; the combine accumulates
- * in fp32 in choice order and rounds once to the dtype of out (round to
- * nearest even).
+ * fp32 (bf16 inputs on matrix cores); the hidden activation is stored in
+ * the dtype of x and each expert's output row in fp32; the combine
+ * accumulates in fp32 in choice order and rounds once to the dtype of out
+ * (round to nearest even).
  * N = 0 is valid: capacity is 0, used_capacity (if given) is zeroed. */
 int moe_forward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
                 const moe_tensor *W_up, const moe_tensor *W_down, int k,
@@ -199,20 +225,43 @@ size_t moe_router_workspace_size(int64_t N, int64_t d, int64_t E, int32_t dtype)
  *   tiles       int32 [2*(E+1)]       prefix sums of ceil(used[e]/128) and
  *                                     ceil(used[e]/256): the expert kernels'
  *                                     tile schedule
- * An id outside [0, E) in topk_idx is not counted and its slot is -1. */
+ * and, each when not NULL, the router statistics of moe_stats:
+ * expert_demand, expert_drops (int32 [E]) and expert_gate_sum (fp32 [E],
+ * which reads topk_gate [N, k]; topk_gate may be NULL otherwise).
+ * workspace: device scratch of moe_dispatch_workspace_size() bytes (256-byte
+ * aligned; may be NULL when that size is 0, i.e. for N*k <= 4096). An id
+ * outside [0, E) in topk_idx is not counted and its slot is -1. */
 int moe_dispatch(int64_t N, int64_t E, int k, int64_t capacity, const int32_t *topk_idx,
-                 int32_t *slot, int32_t *used, int32_t *slot_token, int32_t *tiles,
+                 const float *topk_gate, int32_t *slot, int32_t *used, int32_t *slot_token,
+                 int32_t *tiles, int32_t *expert_demand, int32_t *expert_drops,
+                 float *expert_gate_sum, void *workspace, size_t workspace_bytes,
                  void *stream);
+
+/* Name of the kernel instantiation moe_forward launches for one expert
+ * product of a layer of these sizes (product 0: the up product, 1: the down
+ * product; dropout != 0: the down product's training-dropout variant), as a
+ * profiler lists it, e.g. "expert_gemm_kernel<256, 256, 4, 4, 1, 64, 2, 0>".
+ * Written to buf, NUL-terminated and truncated to len bytes; returns the
+ * length of the full name, or a negative MOE_ERR_* code (N = 0 is
+ * MOE_ERR_ARG: nothing is launched). For measurement tools that match
+ * profiles to the layer's stages. */
+int moe_expert_kernel_name(int64_t N, int64_t d, int64_t E, int64_t d_ff, int k,
+                           float capacity_factor, int32_t dtype, int product, int dropout,
+                           char *buf, size_t len);
+
+/* Bytes of dispatch scratch for N tokens, E experts and top-k (0 on invalid
+ * sizes or when a call needs none). */
+size_t moe_dispatch_workspace_size(int64_t N, int64_t E, int k);
 
 /* Grouped expert FFN (page 1 STEP 7-10; slides 32-37) over the dispatch plan.
  * For each expert e and r < used[e], with a = slot_token[e, r], t = a / k:
  *   H[e, r, :] = ReLU(W_up[e] x_t)      stored in the dtype of x   [E, min(C,N), d_ff]
- *   Y[a, :]    = W_down[e] H[e, r, :]   stored in the dtype of x   [N*k, d]
- * Both products accumulate in fp32 and round once to the stored dtype (bf16
- * expert outputs, as the slides' experts run under bf16 autocast). The
- * gather of token rows is fused into the first product. Rows of Y whose
- * assignment was dropped are not written. H and Y are caller device buffers
- * (16-byte aligned for bf16).
+ *   Y[a, :]    = W_down[e] H[e, r, :]   stored in fp32             [N*k, d]
+ * Both products accumulate in fp32; H is rounded once to the dtype of x (the
+ * slides' experts run under bf16 autocast), Y is kept in fp32 so that the
+ * combine rounds each output once. The gather of token rows is fused into
+ * the first product. Rows of Y whose assignment was dropped are not written.
+ * H and Y are caller device buffers (16-byte aligned for bf16).
  * workspace: optional device scratch of workspace_bytes (256-byte aligned,
  * MOE_ERR_ALIGN otherwise) in which the bf16 path keeps fp32 partial tiles
  * when it cuts the K loop of a product's last, partly idle round of tiles
@@ -252,7 +301,7 @@ size_t moe_expert_workspace_size(int32_t dtype);
 /* The two halves of moe_experts, one product each (page 1 STEP 8-9 and STEP
  * 10): moe_expert_up writes H from x and W_up; moe_expert_down writes Y from
  * H and W_down ([E, d, d_ff]; H has W_down's dtype and [E, min(C,N), d_ff]
- * rows, Y is [N*k, d] in W_down's dtype). workspace as for moe_experts. */
+ * rows, Y is [N*k, d] fp32). workspace as for moe_experts. */
 int moe_expert_up(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t capacity,
                   const int32_t *used, const int32_t *slot_token, const int32_t *tiles,
                   void *H, void *workspace, size_t workspace_bytes, void *stream);
@@ -280,7 +329,7 @@ int moe_combine(int64_t N, int64_t d, int k, const moe_tensor *Y, const float *t
  *   scores: dW_g = ds^T x, dx += ds W_g;
  *   experts: dZ = (dY W_down) where H > 0, dW_down = dY^T H, dW_up = dZ^T X,
  *   dx += the kept choices' dZ W_up rows, summed in choice order.
- * The forward state (routing, dispatch plan, H and the experts' bf16
+ * The forward state (routing, dispatch plan, H and the experts' fp32
  * outputs, as the forward combined them) is recomputed from the inputs in
  * the workspace, so the call takes the forward's arguments plus:
  *   dout    [N, d]         same dtype as x (MOE_BF16)
@@ -293,12 +342,10 @@ int moe_combine(int64_t N, int64_t d, int k, const moe_tensor *Y, const float *t
  * to bf16; fp32 ds is split exactly into three bf16 terms) and fp32
  * accumulation; every sum has a fixed order. MOE_ERR_UNSUPPORTED for fp32
  * layers. Device pointers 16-byte aligned (MOE_ERR_ALIGN).
- * Streams: part of the work (the router-weight gradient and dW_down) runs on
- * a second stream that the library creates for the device on its first
- * backward call outside a stream capture (default priority, kept until the
- * process ends). It is forked from and joined to stats->stream with events
- * inside the call, so the call stays ordered on stats->stream like a single
- * launch, and it can be captured in a graph. */
+ * Streams: with stats->aux_stream set, part of the work (the router-weight
+ * gradient and dW_down) runs on that caller-owned stream, forked from and
+ * joined to stats->stream inside the call (see moe_stats); with NULL every
+ * launch goes to stats->stream. The results are the same bit for bit. */
 int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
                  const moe_tensor *W_up, const moe_tensor *W_down, int k, float capacity_factor,
                  const moe_tensor *dout, moe_tensor *dx, moe_tensor *dW_g, moe_tensor *dW_up,
@@ -326,7 +373,7 @@ int moe_backward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor
 /* Training step without recomputation: moe_forward_train is moe_forward_ex
  * for a bf16 layer (same arguments, same out bit for bit) that also leaves
  * the forward state the backward needs (routing, dispatch plan, H, the
- * experts' bf16 output rows and, for GELU, the pre-activations) in
+ * experts' fp32 output rows and, for GELU, the pre-activations) in
  * stats->workspace, which must hold moe_backward_workspace_size() bytes
  * (and in stats' exported routing arrays when given).
  * moe_backward_after_forward then takes moe_backward_ex's arguments and

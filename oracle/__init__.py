@@ -47,6 +47,8 @@ def lib():
         L.oracle_capacity.restype = _i64
         L.oracle_assign.argtypes = [_i64, _i64, _i32, _i64, _ip, _ip, _ip]
         L.oracle_assign.restype = None
+        L.oracle_router_stats.argtypes = [_i64, _i64, _i32, _i64, _ip, _dp, _ip, _ip, _dp]
+        L.oracle_router_stats.restype = None
         L.oracle_expert_rows.argtypes = [_i64, _i64, _i64, _lp, _dp, _dp, _dp, _i32, _dp, _dp,
                                          _dp, _dp]
         L.oracle_expert_rows.restype = None
@@ -121,6 +123,20 @@ def assign(idx: np.ndarray, E: int, C: int):
     used = np.empty(E, np.int32)
     lib().oracle_assign(N, E, k, C, _ptr(idx, _ip), _ptr(slot, _ip), _ptr(used, _ip))
     return slot, used
+
+
+def router_stats(idx: np.ndarray, gate: np.ndarray, E: int, C: int):
+    """Per-expert demand before the capacity clip [E], drops [E] and gate sums
+    [E] (float64, token order) of one call's ids and gates [N, k]."""
+    idx = _c(idx, np.int32)
+    gate = _c(gate, np.float64)
+    N, k = idx.shape
+    demand = np.empty(E, np.int32)
+    drops = np.empty(E, np.int32)
+    gsum = np.empty(E, np.float64)
+    lib().oracle_router_stats(N, E, k, C, _ptr(idx, _ip), _ptr(gate, _dp), _ptr(demand, _ip),
+                              _ptr(drops, _ip), _ptr(gsum, _dp))
+    return demand, drops, gsum
 
 
 ACTS = {"relu": 0, "gelu": 1}
@@ -377,5 +393,7 @@ def forward(wl, rows: Optional[Sequence[int]] = None, want_y: bool = False) -> R
         y = dropout_rows(y.reshape(-1, wl.d), arows, p, wl.cfg.dropout_seed,
                          wl.cfg.dropout_offset).reshape(len(rows), k, wl.d)
     out = combine(gate[rows], slot[rows], y)
+    demand, drops, gsum = router_stats(idx, gate, E, C)
     return Result(N=N, E=E, k=k, C=C, scores=scores, idx=idx, gate=gate, slot=slot,
-                  used=used, rows=rows, out=out, y=y if want_y else None)
+                  used=used, rows=rows, out=out, y=y if want_y else None, demand=demand,
+                  expert_drops=drops, gate_sum=gsum)

@@ -123,6 +123,34 @@ void oracle_assign(int64_t N, int64_t E, int32_t k, int64_t C,
         used[e] = (int32_t)(count[e] < C ? count[e] : C);
 }
 
+/* Router statistics of one call. The pages name a router's load imbalance
+ * and its capacity drops as what must be watched ("MoE（Mixture of Experts）
+ * とは？", section on MoE's weak points: the work of experts is easily
+ * skewed; "게이팅 위기(Gating Crisis)", the load-balancing challenge and the
+ * capacity-drop panel), and give no loss formula, so these are the counts
+ * that define them: for expert e, demand[e] = the number of assignments
+ * (t, j) routed to e before the capacity clip (the running count of
+ * [P2 slide 14] at its end), drops[e] = how many of them reach rank C or
+ * more, i.e. demand[e] - min(demand[e], C), and gate_sum[e] = the sum of the
+ * gates g_{t,j} of those assignments (kept or dropped), in token order. */
+void oracle_router_stats(int64_t N, int64_t E, int32_t k, int64_t C, const int32_t *idx,
+                         const double *gate, int32_t *demand, int32_t *drops,
+                         double *gate_sum)
+{
+    for (int64_t e = 0; e < E; ++e) {
+        demand[e] = 0;
+        gate_sum[e] = 0.0;
+    }
+    for (int64_t t = 0; t < N; ++t)
+        for (int32_t j = 0; j < k; ++j) {
+            const int32_t e = idx[t * k + j];
+            demand[e] += 1;
+            gate_sum[e] += gate[t * k + j];
+        }
+    for (int64_t e = 0; e < E; ++e)
+        drops[e] = demand[e] > C ? (int32_t)(demand[e] - C) : 0;
+}
+
 /* [P2 slide 32] the nanoMoE expert's activation, torch's default GELU:
  * x * Phi(x) with Phi the standard normal distribution function,
  * Phi(x) = (1 + erf(x / sqrt(2))) / 2 (C library erf, double).            */

@@ -25,7 +25,8 @@ EXPORTS = ("moe_forward", "moe_workspace_size", "moe_capacity", "moe_error_strin
            "moe_expert_up", "moe_expert_down", "moe_expert_workspace_size", "moe_combine",
            "moe_forward_ex", "moe_experts_ex", "moe_expert_up_ex", "moe_expert_down_ex",
            "moe_backward", "moe_backward_ex", "moe_backward_workspace_size",
-           "moe_forward_train", "moe_backward_after_forward")
+           "moe_forward_train", "moe_backward_after_forward", "moe_dispatch_workspace_size",
+           "moe_expert_kernel_name")
 
 MOE_ACT_RELU, MOE_ACT_GELU = 0, 1
 ACTS = {"relu": MOE_ACT_RELU, "gelu": MOE_ACT_GELU}
@@ -41,7 +42,9 @@ class MoeStats(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t),
                 ("topk_idx", ctypes.c_void_p), ("topk_gate", ctypes.c_void_p),
                 ("slot", ctypes.c_void_p), ("used_capacity", ctypes.c_void_p),
-                ("capacity", ctypes.c_int64)]
+                ("capacity", ctypes.c_int64),
+                ("expert_demand", ctypes.c_void_p), ("expert_drops", ctypes.c_void_p),
+                ("expert_gate_sum", ctypes.c_void_p), ("aux_stream", ctypes.c_void_p)]
 
 
 class MoeExpertOpts(ctypes.Structure):
@@ -113,8 +116,15 @@ def lib():
         L.moe_router.restype = ctypes.c_int
         L.moe_router_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.c_int32]
         L.moe_router_workspace_size.restype = ctypes.c_size_t
-        L.moe_dispatch.argtypes = [_i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_dispatch.argtypes = [_i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_dispatch.restype = ctypes.c_int
+        L.moe_dispatch_workspace_size.argtypes = [_i64, _i64, ctypes.c_int]
+        L.moe_dispatch_workspace_size.restype = ctypes.c_size_t
+        L.moe_expert_kernel_name.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,
+                                             ctypes.c_int32, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_char_p, ctypes.c_size_t]
+        L.moe_expert_kernel_name.restype = ctypes.c_int
         L.moe_experts.argtypes = [_T, _T, _T, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                   ctypes.c_size_t, _vp]
         L.moe_experts.restype = ctypes.c_int
@@ -174,6 +184,17 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _aux_stream(aux, device):
+    """The backward's second stream: ``"auto"`` makes one on the tensors'
+    device (default priority), None runs the call on one stream, or a
+    ``torch.cuda.Stream``. Returns (stream object or None, handle)."""
+    if isinstance(aux, str):
+        if aux != "auto":
+            raise ValueError("aux_stream must be 'auto', None or a torch.cuda.Stream")
+        aux = torch.cuda.Stream(device=device)
+    return aux, (None if aux is None else ctypes.c_void_p(aux.cuda_stream))
+
+
 class ExpertOpts:
     """``moe_expert_opts`` for an activation name, optional fp32 bias tensors
     (b_up [E, d_ff], b_down [E, d]) and an optional training-mode dropout
@@ -217,8 +238,20 @@ def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 
 class Stats:
-    def __init__(self, idx, gate, slot, used, capacity):
+    """Exported routing arrays (device tensors or None) and the capacity; with
+    router statistics, demand / drops (int32 [E]) and gate_sum (fp32 [E])."""
+
+    def __init__(self, idx, gate, slot, used, capacity, demand=None, drops=None, gate_sum=None):
         self.idx, self.gate, self.slot, self.used, self.capacity = idx, gate, slot, used, capacity
+        self.demand, self.drops, self.gate_sum = demand, drops, gate_sum
+
+
+def _router_stats(E, dev, on):
+    if not on:
+        return None, None, None
+    return (torch.empty((E,), dtype=torch.int32, device=dev),
+            torch.empty((E,), dtype=torch.int32, device=dev),
+            torch.empty((E,), dtype=torch.float32, device=dev))
 
 
 def forward(x: torch.Tensor, W_g: torch.Tensor, noise: Optional[torch.Tensor],
@@ -226,10 +259,11 @@ def forward(x: torch.Tensor, W_g: torch.Tensor, noise: Optional[torch.Tensor],
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
             export: bool = True, stream=None, act: str = "relu",
             b_up: Optional[torch.Tensor] = None, b_down: Optional[torch.Tensor] = None,
-            dropout=None):
+            dropout=None, router_stats: bool = False):
     """Run ``moe_forward`` (``moe_forward_ex`` for an expert variant; dropout:
     ``(p, seed, offset)`` or None). Returns ``(out, Stats)``; with ``export=False`` the
-    routing arrays stay in the workspace and Stats only carries the capacity."""
+    routing arrays stay in the workspace and Stats only carries the capacity;
+    ``router_stats`` also exports the per-expert demand, drops and gate sums."""
     N = x.numel() // x.shape[-1]
     d = x.shape[-1]
     E, d_ff = W_up.shape[0], W_up.shape[1]
@@ -245,8 +279,10 @@ def forward(x: torch.Tensor, W_g: torch.Tensor, noise: Optional[torch.Tensor],
         gate = torch.empty((N, k), dtype=torch.float32, device=dev)
         slot = torch.empty((N, k), dtype=torch.int32, device=dev)
         used = torch.empty((E,), dtype=torch.int32, device=dev)
+    dem, drp, gsum = _router_stats(E, dev, router_stats)
     st = MoeStats(_stream(stream), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
-                  _ptr(idx), _ptr(gate), _ptr(slot), _ptr(used), -1)
+                  _ptr(idx), _ptr(gate), _ptr(slot), _ptr(used), -1, _ptr(dem), _ptr(drp),
+                  _ptr(gsum), None)
     dx, dg, dn, du, dd, do = desc(x), desc(W_g), desc(noise), desc(W_up), desc(W_down), desc(out)
     o = _opts(act, b_up, b_down, dropout)
     if o is None:
@@ -256,7 +292,7 @@ def forward(x: torch.Tensor, W_g: torch.Tensor, noise: Optional[torch.Tensor],
         rc = lib().moe_forward_ex(_ref(dx), _ref(dg), _ref(dn), _ref(du), _ref(dd), o.ref(), k,
                                   capacity_factor, _ref(do), ctypes.byref(st))
     _check(rc, "moe_forward")
-    return out, Stats(idx, gate, slot, used, int(st.capacity))
+    return out, Stats(idx, gate, slot, used, int(st.capacity), dem, drp, gsum)
 
 
 def backward_workspace_size(N: int, d: int, E: int, d_ff: int, k: int, capacity_factor: float,
@@ -268,7 +304,7 @@ def backward_workspace_size(N: int, d: int, E: int, d_ff: int, k: int, capacity_
 def backward(x, W_g, noise, W_up, W_down, k: int, capacity_factor: float, dout,
              workspace=None, stream=None, export: bool = False, act: str = "relu",
              b_up: Optional[torch.Tensor] = None, b_down: Optional[torch.Tensor] = None,
-             dropout=None):
+             dropout=None, aux_stream="auto"):
     """Run ``moe_backward`` (``moe_backward_ex`` for GELU, biases or dropout): returns
     (dx [N, d], dW_g [E, d], dW_up [E, d_ff, d], dW_down [E, d, d_ff]), all
     fp32, followed by db_up [E, d_ff] and db_down [E, d] (None where the layer
@@ -292,8 +328,9 @@ def backward(x, W_g, noise, W_up, W_down, k: int, capacity_factor: float, dout,
         gate = torch.empty((N, k), dtype=torch.float32, device=dev)
         slot = torch.empty((N, k), dtype=torch.int32, device=dev)
         used = torch.empty((E,), dtype=torch.int32, device=dev)
+    aux, aux_h = _aux_stream(aux_stream, dev)
     st = MoeStats(_stream(stream), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
-                  _ptr(idx), _ptr(gate), _ptr(slot), _ptr(used), -1)
+                  _ptr(idx), _ptr(gate), _ptr(slot), _ptr(used), -1, None, None, None, aux_h)
     ds = [desc(t) for t in (x, W_g, noise, W_up, W_down, dout, dx, dwg, dwu, dwd, dbu, dbd)]
     o = _opts(act, b_up, b_down, dropout)
     r = [_ref(a) for a in ds]
@@ -318,7 +355,7 @@ class Forward:
 
     def __init__(self, x, W_g, noise, W_up, W_down, k, capacity_factor, out=None,
                  export=False, stream=None, act="relu", b_up=None, b_down=None,
-                 dropout=None):
+                 dropout=None, router_stats=False):
         self.tensors = (x, W_g, noise, W_up, W_down)
         N, d = x.numel() // x.shape[-1], x.shape[-1]
         E, d_ff = W_up.shape[0], W_up.shape[1]
@@ -334,9 +371,11 @@ class Forward:
             self.used = torch.empty((E,), dtype=torch.int32, device=dev)
         self.k, self.cf = k, capacity_factor
         self._d = [desc(x), desc(W_g), desc(noise), desc(W_up), desc(W_down), desc(self.out)]
+        self.demand, self.drops, self.gate_sum = _router_stats(E, dev, router_stats)
         self.stats = MoeStats(_stream(stream), ctypes.c_void_p(self.workspace.data_ptr()),
                               self.workspace.numel(), _ptr(self.idx), _ptr(self.gate),
-                              _ptr(self.slot), _ptr(self.used), -1)
+                              _ptr(self.slot), _ptr(self.used), -1, _ptr(self.demand),
+                              _ptr(self.drops), _ptr(self.gate_sum), None)
         self._args = [_ref(a) for a in self._d]
         self._opts = _opts(act, b_up, b_down, dropout)
         self._biases = (b_up, b_down)
@@ -361,7 +400,7 @@ class Backward:
     cross the C ABI."""
 
     def __init__(self, x, W_g, noise, W_up, W_down, k, capacity_factor, dout, stream=None,
-                 act="relu", b_up=None, b_down=None, dropout=None):
+                 act="relu", b_up=None, b_down=None, dropout=None, aux_stream="auto"):
         N, d = x.numel() // x.shape[-1], x.shape[-1]
         E, d_ff = W_up.shape[0], W_up.shape[1]
         dev = x.device
@@ -381,8 +420,10 @@ class Backward:
                                      self.dW_up, self.dW_down, self.db_up, self.db_down)]
         self._args = [_ref(a) for a in self._d]
         self._opts = _opts(act, b_up, b_down, dropout)
+        self.aux, aux_h = _aux_stream(aux_stream, dev)
         self.stats = MoeStats(_stream(stream), ctypes.c_void_p(self.workspace.data_ptr()),
-                              self.workspace.numel(), None, None, None, None, -1)
+                              self.workspace.numel(), None, None, None, None, -1, None, None,
+                              None, aux_h)
 
     def __call__(self):
         a = self._args
@@ -405,7 +446,8 @@ class TrainStep:
     from it. Tensors, workspace and descriptors are built once."""
 
     def __init__(self, x, W_g, noise, W_up, W_down, k, capacity_factor, stream=None,
-                 act="relu", b_up=None, b_down=None, dropout=None, export=False):
+                 act="relu", b_up=None, b_down=None, dropout=None, export=False,
+                 aux_stream="auto"):
         N, d = x.numel() // x.shape[-1], x.shape[-1]
         E, d_ff = W_up.shape[0], W_up.shape[1]
         dev = x.device
@@ -433,9 +475,10 @@ class TrainStep:
                                      self.dW_up, self.dW_down, self.db_up, self.db_down)]
         self._a = [_ref(a) for a in self._d]
         self._dout = None
+        self.aux, aux_h = _aux_stream(aux_stream, dev)
         self.stats = MoeStats(_stream(stream), ctypes.c_void_p(self.workspace.data_ptr()),
                               self.workspace.numel(), _ptr(self.idx), _ptr(self.gate),
-                              _ptr(self.slot), _ptr(self.used), -1)
+                              _ptr(self.slot), _ptr(self.used), -1, None, None, None, aux_h)
 
     def forward(self):
         a = self._a
@@ -478,8 +521,27 @@ def router(x, W_g, noise, k, idx=None, gate=None, workspace=None, stream=None):
     return idx, gate
 
 
-def dispatch(idx: torch.Tensor, E: int, capacity_: int, stream=None):
-    """Returns (slot [N,k], used [E], slot_token [E, min(C,N)], tiles [2(E+1)])."""
+def expert_kernel_name(N: int, d: int, E: int, d_ff: int, k: int, capacity_factor: float,
+                       dtype: torch.dtype, product: int, dropout: bool = False) -> str:
+    """Name of the kernel instantiation the library launches for the up
+    (product 0) or down (product 1) expert product of such a layer."""
+    code = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    buf = ctypes.create_string_buffer(256)
+    n = lib().moe_expert_kernel_name(N, d, E, d_ff, k, capacity_factor, code, product,
+                                     int(dropout), buf, 256)
+    _check(min(n, 0), "moe_expert_kernel_name")
+    return buf.value.decode()
+
+
+def dispatch_workspace_size(N: int, E: int, k: int) -> int:
+    return int(lib().moe_dispatch_workspace_size(N, E, k))
+
+
+def dispatch(idx: torch.Tensor, E: int, capacity_: int, stream=None, gate=None,
+             router_stats: bool = False, workspace=None):
+    """Returns (slot [N,k], used [E], slot_token [E, min(C,N)], tiles [2(E+1)]);
+    with ``router_stats`` also (demand [E], drops [E], gate_sum [E]) (gate_sum
+    needs ``gate``, else it is None)."""
     N, k = idx.shape
     ceff = min(capacity_, N)
     dev = idx.device
@@ -487,8 +549,18 @@ def dispatch(idx: torch.Tensor, E: int, capacity_: int, stream=None):
     used = torch.empty((E,), dtype=torch.int32, device=dev)
     slot_token = torch.full((E, max(ceff, 1)), -1, dtype=torch.int32, device=dev)
     tiles = torch.empty((2 * (E + 1),), dtype=torch.int32, device=dev)
-    _check(lib().moe_dispatch(N, E, k, capacity_, _ptr(idx), _ptr(slot), _ptr(used),
-                              _ptr(slot_token), _ptr(tiles), _stream(stream)), "moe_dispatch")
+    dem, drp, gsum = _router_stats(E, dev, router_stats)
+    if gate is None:
+        gsum = None
+    if workspace is None:
+        n = dispatch_workspace_size(N, E, k)
+        workspace = alloc_workspace(n, dev) if n > 0 else None
+    wp, wn = _ws_args(workspace)
+    _check(lib().moe_dispatch(N, E, k, capacity_, _ptr(idx), _ptr(gate), _ptr(slot), _ptr(used),
+                              _ptr(slot_token), _ptr(tiles), _ptr(dem), _ptr(drp), _ptr(gsum),
+                              wp, wn, _stream(stream)), "moe_dispatch")
+    if router_stats:
+        return slot, used, slot_token, tiles, (dem, drp, gsum)
     return slot, used, slot_token, tiles
 
 
@@ -514,14 +586,14 @@ def _ws_args(ws):
 def experts(x, W_up, W_down, k, capacity_, used, slot_token, tiles, H=None, Y=None,
             workspace="auto", stream=None, act="relu", b_up=None, b_down=None,
             dropout=None):
-    """Returns (H [E, min(C,N), d_ff] and Y [N*k, d], both in x's dtype)."""
+    """Returns (H [E, min(C,N), d_ff] in x's dtype and Y [N*k, d] fp32)."""
     N, d = x.numel() // x.shape[-1], x.shape[-1]
     E, d_ff = W_up.shape[0], W_up.shape[1]
     ceff = min(capacity_, N)
     if H is None:
         H = torch.zeros((E, max(ceff, 1), d_ff), dtype=x.dtype, device=x.device)
     if Y is None:
-        Y = torch.zeros((N * k, d), dtype=x.dtype, device=x.device)
+        Y = torch.zeros((N * k, d), dtype=torch.float32, device=x.device)
     dx, du, dd = desc(x), desc(W_up), desc(W_down)
     if not slot_token.is_contiguous():
         raise ValueError("slot_token must be a contiguous [E, min(C, N)] tensor")

@@ -35,10 +35,10 @@ __device__ __forceinline__ void split3_bits(float a, unsigned short &hi, unsigne
 
 // One wave per token: dY rows (bf16, kept choices), dg by a wave reduction in
 // a fixed butterfly order, then ds for every choice (dropped ones have dg 0
-// but still took part in the softmax). Y holds the experts' bf16 outputs, the
+// but still took part in the softmax). Y holds the experts' fp32 outputs, the
 // values the forward combined; 8 columns per lane and load.
 __global__ __launch_bounds__(256) void combine_backward_kernel(
-    const unsigned short *__restrict__ dout, const unsigned short *__restrict__ Y,
+    const unsigned short *__restrict__ dout, const float *__restrict__ Y,
     const float *__restrict__ gate, const int32_t *__restrict__ slot, int N, int d, int k,
     unsigned short *__restrict__ dY, float *__restrict__ ds, Dropout dp) {
     const int lane = threadIdx.x & 63;
@@ -54,11 +54,12 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
         float p = 0.f;
         if (slot[a] >= 0) {
             const float g = gate[a];
-            const unsigned short *yr = Y + a * d;
+            const float *yr = Y + a * d;
             unsigned short *dyr = dY + a * d;
             for (int c = lane; c < chunks; c += 64) {
                 const u32x4 ov = *reinterpret_cast<const u32x4 *>(go + 8 * c);
-                const u32x4 yv = *reinterpret_cast<const u32x4 *>(yr + 8 * c);
+                const f32x4 y0 = *reinterpret_cast<const f32x4 *>(yr + 8 * c);
+                const f32x4 y1 = *reinterpret_cast<const f32x4 *>(yr + 8 * c + 4);
                 // Y already carries the dropout; dY = g dout m
                 float m[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
                 if (dp.on)
@@ -68,8 +69,9 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
                 for (int q = 0; q < 4; ++q) {
                     const float o0 = __uint_as_float(ov[q] << 16);
                     const float o1 = __uint_as_float(ov[q] & 0xffff0000u);
-                    p = fmaf(o0, __uint_as_float(yv[q] << 16), p);
-                    p = fmaf(o1, __uint_as_float(yv[q] & 0xffff0000u), p);
+                    const f32x4 &y = q < 2 ? y0 : y1;
+                    p = fmaf(o0, y[(q % 2) * 2], p);
+                    p = fmaf(o1, y[(q % 2) * 2 + 1], p);
                     w[q] = pack_bf16x2(g * o0 * m[2 * q], g * o1 * m[2 * q + 1]);
                 }
                 *reinterpret_cast<u32x4 *>(dyr + 8 * c) = w;
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(256) void dx_kernel(const float *__restrict__ dXa,
                                                  const int32_t *__restrict__ idx,
                                                  const int32_t *__restrict__ slot,
                                                  const float *__restrict__ Wg, int64_t N, int d,
-                                                 int k, float *__restrict__ dx) {
+                                                 int E, int k, float *__restrict__ dx) {
     const int cols = d / 4;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= N * cols)
@@ -294,8 +296,11 @@ __global__ __launch_bounds__(256) void dx_kernel(const float *__restrict__ dXa,
     }
     for (int j = 0; j < k; ++j) {
         const int64_t a = t * k + j;
+        const int e = idx[a];
+        if (e < 0 || e >= E)   // not an expert: no score, no gradient (as in the dispatch)
+            continue;
         const float s = ds[a];
-        const f32x4 w = *reinterpret_cast<const f32x4 *>(Wg + (int64_t)idx[a] * d + c);
+        const f32x4 w = *reinterpret_cast<const f32x4 *>(Wg + (int64_t)e * d + c);
         acc += s * w;
     }
     *reinterpret_cast<f32x4 *>(dx + t * d + c) = acc;
@@ -310,7 +315,7 @@ hipError_t launch_combine_backward(const void *dout, const void *Y, const float 
         return hipSuccess;
     hipLaunchKernelGGL(combine_backward_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s,
                        static_cast<const unsigned short *>(dout),
-                       static_cast<const unsigned short *>(Y), gate, slot, (int)N, (int)d, k,
+                       static_cast<const float *>(Y), gate, slot, (int)N, (int)d, k,
                        static_cast<unsigned short *>(dY), ds, dp);
     return hipGetLastError();
 }
@@ -374,12 +379,13 @@ hipError_t launch_transpose_rows(const void *src, int64_t C, int64_t ceff, const
 }
 
 hipError_t launch_dx(const float *dXa, const float *ds, const int32_t *idx, const int32_t *slot,
-                     const float *Wg, int64_t N, int64_t d, int k, float *dx, hipStream_t s) {
+                     const float *Wg, int64_t N, int64_t d, int E, int k, float *dx,
+                     hipStream_t s) {
     const int64_t n = N * (d / 4);
     if (n == 0)
         return hipSuccess;
     hipLaunchKernelGGL(dx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dXa, ds,
-                       idx, slot, Wg, N, (int)d, k, dx);
+                       idx, slot, Wg, N, (int)d, E, k, dx);
     return hipGetLastError();
 }
 

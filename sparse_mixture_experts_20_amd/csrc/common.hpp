@@ -118,14 +118,19 @@ hipError_t launch_router_f32(const float *x, const float *wg, const float *noise
                              int64_t N, int64_t d, int E, int k,
                              int32_t *idx, float *gate, hipStream_t s);
 
-hipError_t launch_dispatch(const int32_t *idx, int64_t N, int E, int k, int64_t ceff,
-                           int32_t *slot, int32_t *used, int32_t *slot_token,
-                           int32_t *tiles, hipStream_t s);
+// Dispatch plan; demand / drops / gate_sum (router statistics) may each be
+// NULL; gate is read only for gate_sum. ws: dispatch_workspace_bytes()
+// bytes of device scratch (256-aligned; none for a single 4096-assignment chunk).
+size_t dispatch_workspace_bytes(int64_t N, int E, int k);
+hipError_t launch_dispatch(const int32_t *idx, const float *gate, int64_t N, int E, int k,
+                           int64_t ceff, int32_t *slot, int32_t *used, int32_t *slot_token,
+                           int32_t *tiles, int32_t *demand, int32_t *drops, float *gate_sum,
+                           void *ws, hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 
 // Grouped expert products. mode 0: H = act(x[gather] W_up^T + b_up); mode 1:
-// Y[scatter] = H W_down^T + b_down. H and Y have the operands' dtype (bf16 or
-// fp32).
+// Y[scatter] = H W_down^T + b_down. H has the operands' dtype (bf16 or fp32),
+// Y is fp32.
 // bf16 != 0: bf16 operands on matrix cores; otherwise fp32 operands.
 // rows_per_expert: the expected kept rows per expert (picks the tile shape).
 // part/part_bytes: device scratch for the K-split of a product's last round
@@ -148,6 +153,12 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
                               const int32_t *slot_token, const int32_t *tiles, void *Y,
                               int64_t rows_per_expert, void *part, size_t part_bytes,
                               const float *b_down, hipStream_t s, Dropout dp = Dropout{});
+
+// Name of the kernel instantiation the expert product `product` (0: up, 1:
+// down, with or without the dropout) launches for these sizes, as a profiler
+// shows it; snprintf's return value.
+int expert_kernel_name(bool bf16, int product, int64_t d, int64_t d_ff, int E,
+                       int64_t rows_per_expert, bool dropout, char *buf, size_t len);
 
 // Backward products over the dispatch plan (bf16 operands, fp32 accumulate;
 // the weights are read K-major, as stored):
@@ -181,7 +192,7 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
 
 // Backward element-wise and layout kernels (backward.hip).
 // dY rows (bf16, kept choices) = gate * dout; ds [N, k] = gate * (dg - sum gate*dg)
-// with dg = <dout, Y> (Y: the experts' bf16 outputs, assignment-major). d % 8 == 0.
+// with dg = <dout, Y> (Y: the experts' fp32 outputs, assignment-major). d % 8 == 0.
 // With dropout, dY = gate * dout * (the dropout factor of each Y element).
 hipError_t launch_combine_backward(const void *dout, const void *Y, const float *gate,
                                    const int32_t *slot, int64_t N, int64_t d, int k, void *dY,
@@ -206,9 +217,11 @@ hipError_t launch_chunk_sum(const float *part, int64_t S, int64_t n, float *out,
 hipError_t launch_transpose_rows(const void *src, int64_t C, int64_t ceff, const int32_t *used,
                                  int64_t nrows, const int32_t *slot_token, int k, int map,
                                  int64_t Kp, int copies, int batch, void *out, hipStream_t s);
-// dx = sum of the kept choices' dX rows + sum_j ds[t, j] W_g[idx[t, j]] (fp32, d % 4 == 0).
+// dx = sum of the kept choices' dX rows + sum_j ds[t, j] W_g[idx[t, j]] (fp32, d % 4 == 0);
+// ids outside [0, E) contribute nothing.
 hipError_t launch_dx(const float *dXa, const float *ds, const int32_t *idx, const int32_t *slot,
-                     const float *Wg, int64_t N, int64_t d, int k, float *dx, hipStream_t s);
+                     const float *Wg, int64_t N, int64_t d, int E, int k, float *dx,
+                     hipStream_t s);
 
 // Y[rows, Nout] (fp32) = A[rows, K] * W[Nout, K]^T, bf16 operands.
 hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, int64_t K,

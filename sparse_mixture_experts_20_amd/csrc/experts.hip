@@ -6,7 +6,7 @@
 // slide 32 also gives the expert variant with biases and GELU).
 //
 //   up:   H[e, r, :] = act(W_up[e] x_t + b_up[e])  for r < used[e], t = slot_token[e, r] / k
-//   down: Y[a, :]    = W_down[e] H[e, r, :] + b_down[e]  with a = slot_token[e, r]
+//   down: Y[a, :]    = W_down[e] H[e, r, :] + b_down[e]  with a = slot_token[e, r], fp32
 //
 // Both are "NT" products: every operand row is contiguous along the
 // reduction dimension (activation rows along d or d_ff, weight rows are
@@ -14,8 +14,9 @@
 // a CDNA matrix instruction want. The gather of token rows (dispatch) is
 // fused into the up product's operand load, so no packed copy of the tokens
 // is ever written; the down product scatters its rows straight into the
-// assignment-ordered buffer the combine reads. Both accumulate in fp32 and
-// round once to bf16 in the epilogue.
+// assignment-ordered buffer the combine reads. Both accumulate in fp32; H is
+// rounded once to bf16 in the epilogue, Y stays fp32 (the combine rounds the
+// gate-weighted sum once).
 //
 // bf16 kernel: a BM x BN output tile per workgroup, K-step 64 (128 for the
 // tile of two K sets), waves laid out WAVES_M x WAVES_N (times WAVES_K sets
@@ -37,6 +38,8 @@
 // round of tiles would leave most workgroups idle, its tiles are cut into
 // K-ranges (split_plan below); when the tiles just overflow one round, the
 // light last row tiles of the experts go last (partial_prefix below).
+#include <stdio.h>
+
 #include <type_traits>
 
 #include "common.hpp"
@@ -284,7 +287,7 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // up to 256 registers per lane and schedule for latency rather than occupancy;
 // a tile of 16 waves runs four per SIMD with up to 128 registers each.
 // MODE 0: up product (gathered token rows, activation, bf16 H into O16);
-// 1: down product (bf16 rows of Y scattered to their assignment, into O16);
+// 1: down product (fp32 rows of Y scattered to their assignment, into O32);
 // 2: plain product of ceff rows of A into fp32 rows of O32 (no gather, no
 // schedule table, no split), batched over blockIdx.y with element strides
 // bsa, bsb, bsc of A, W and O32;
@@ -800,9 +803,9 @@ void expert_gemm_kernel(
                 else
                     store_h(std::false_type{});
             } else if (MODE == 1 || MODE == 5) {
-                // bf16 row of Y at the assignment's position
+                // fp32 row of Y at the assignment's position
                 const int64_t arow = (int64_t)slot_token[srow];
-                unsigned short *dst = O16 + arow * Nout + nb;
+                float *dst = O32 + arow * Nout + nb;
                 const float *bp = bias ? bias + (int64_t)e * Nout + nb : nullptr;
 #pragma unroll
                 for (int h = 0; h < CPL / 8; ++h) {
@@ -819,13 +822,8 @@ void expert_gemm_kernel(
                             z0 *= f32x4{m[0], m[1], m[2], m[3]};
                             z1 *= f32x4{m[4], m[5], m[6], m[7]};
                         }
-                        u32x4 pk;
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const f32x4 &z = c < 2 ? z0 : z1;
-                            pk[c] = pack_bf16x2(z[(c % 2) * 2], z[(c % 2) * 2 + 1]);
-                        }
-                        *reinterpret_cast<u32x4 *>(dst + 8 * h) = pk;
+                        *reinterpret_cast<f32x4 *>(dst + 8 * h) = z0;
+                        *reinterpret_cast<f32x4 *>(dst + 8 * h + 4) = z1;
                     }
                 }
             } else if (MODE == 3) {
@@ -876,14 +874,15 @@ void expert_gemm_kernel(
 
 // Sum of the K-range partials of the cut tiles, in K order, then the same
 // epilogue as a whole tile (MODE 0: bias, activation, bf16 H; MODE 1: bias,
-// dropout, bf16 row of Y).
+// dropout, fp32 row of Y).
 // One workgroup per 16-row strip of a cut tile; 4 columns per thread.
 template <int BM, int BN, int BKT, int MODE>
 __global__ __launch_bounds__(256) void split_fixup_kernel(
     int K, int Nout, int E, int ceff, const int32_t *__restrict__ used,
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
-    const float *__restrict__ part, int P, unsigned short *__restrict__ O16, int act,
-    const float *__restrict__ bias, Dropout dp, unsigned short *__restrict__ Z16) {
+    const float *__restrict__ part, int P, unsigned short *__restrict__ O16,
+    float *__restrict__ O32, int act, const float *__restrict__ bias, Dropout dp,
+    unsigned short *__restrict__ Z16) {
     constexpr int STRIPS = BM / 16;
     __shared__ int s_mt[kMaxExperts + 1];
     __shared__ int s_pp[kMaxExperts + 1];
@@ -934,6 +933,10 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
                 v = f32x4{gelu(v[0]), gelu(v[1]), gelu(v[2]), gelu(v[3])};
             else
                 v = f32x4{fmaxf(v[0], 0.f), fmaxf(v[1], 0.f), fmaxf(v[2], 0.f), fmaxf(v[3], 0.f)};
+        }
+        if (MODE == 1) {
+            *reinterpret_cast<f32x4 *>(O32 + orow * Nout + n) = v;   // fp32 row of Y
+            continue;
         }
         u32x2 pk;
         pk[0] = pack_bf16x2(v[0], v[1]);
@@ -1051,9 +1054,8 @@ Tile pick_tile(int64_t rows_per_expert, int64_t Nout, int E) {
     return Tile::k128;
 }
 
-constexpr int kMaxDevices = 64;
-
-// Workgroups of `kernel` that run at once on the current device (-1 if unknown).
+// Workgroups of `kernel` that run at once on the current device (-1 if
+// unknown), queried on every launch (the library keeps no state between calls).
 template <typename Kern>
 int resident_blocks(Kern kernel, int threads) {
     int dev = 0, cus = 0, per_cu = 0;
@@ -1077,18 +1079,11 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
                         Dropout dp = Dropout{}) {
     auto kern = expert_gemm_kernel<BM, BN, WM, WN, WK, BKT, 2, MODE>;
     constexpr int NTHR = WM * WN * WK * 64;
-    static int resident[kMaxDevices];   // per device, filled on first use (0 = unset)
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        dev = -1;
-    int P = 0;
-    if (dev >= 0) {
-        if (resident[dev] == 0)
-            resident[dev] = resident_blocks(kern, NTHR);
-        P = resident[dev];
-    }
-    if (P < 0)
+    int P = resident_blocks(kern, NTHR);
+    if (P < 0) {
+        (void)hipGetLastError();   // a failed query leaves no error behind: plan without it
         P = 0;
+    }
     const int64_t slot = (int64_t)BM * BN * sizeof(float);
     const int64_t KT = (K + BKT - 1) / BKT;
     const int64_t tmax = (int64_t)E * ((ceff + BM - 1) / BM) * ((Nout + BN - 1) / BN);
@@ -1111,8 +1106,40 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
     hipLaunchKernelGGL((split_fixup_kernel<BM, BN, BKT, MODE == 0 ? 0 : 1>),
                        dim3((unsigned)(P * (BM / 16))),
                        dim3(256), 0, s, (int)K, (int)Nout, E, (int)ceff, used, slot_token, mt,
-                       (const float *)part, P, O16, act, bias, dp, Z16);
+                       (const float *)part, P, O16, O32, act, bias, dp, Z16);
     return hipGetLastError();
+}
+
+// Template arguments of the kernel a product of this mode runs on tile shape
+// t: BM, BN, waves along rows, columns and K, K-step.
+template <int BM_, int BN_, int WM_, int WN_, int WK_, int BKT_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, WK = WK_, BKT = BKT_;
+};
+
+// Calls f(TileCfg<...>{}, tiles) with the instantiation mode MODE runs for
+// tile shape t and the dispatch plan's schedule table it uses (row tiles of
+// 128 or of 256): the one place that maps a tile shape to a kernel, shared by
+// the launch and by the kernel-name query.
+template <int MODE, typename F>
+auto with_tile(Tile t, const int32_t *tiles, int E, F f) {
+    if (t == Tile::k128k2) {
+        if constexpr (MODE == 0 || MODE == 1 || MODE == 5)
+            return f(TileCfg<128, 128, 2, 4, 2, kBK2>{}, tiles);
+        t = Tile::k128x64;   // K-major right operands: no K sets
+    }
+    if (t == Tile::k256) {
+        // forward products: 16 waves of 64x64 (four per SIMD, more latency
+        // hidden than the 8 waves of 128x64 save in LDS reads); the backward's
+        // K-major products keep 8 waves (16 would spill there)
+        if constexpr (MODE == 0 || MODE == 1 || MODE == 5)
+            return f(TileCfg<256, 256, 4, 4, 1, kBK>{}, tiles + E + 1);
+        else
+            return f(TileCfg<256, 256, 2, 4, 1, kBK>{}, tiles + E + 1);
+    }
+    if (t == Tile::k128x64)
+        return f(TileCfg<128, 64, 2, 2, 1, kBK>{}, tiles);
+    return f(TileCfg<128, 128, 2, 2, 1, kBK>{}, tiles);
 }
 
 template <int MODE>
@@ -1124,36 +1151,12 @@ hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W,
                        float *O32 = nullptr, unsigned short *Z16 = nullptr,
                        Dropout dp = Dropout{}) {
     float *pf = static_cast<float *>(part);
-    if (t == Tile::k128k2) {
-        if constexpr (MODE == 0 || MODE == 1 || MODE == 5)
-            return launch_tiles<128, 128, 2, 4, 2, kBK2, MODE>(A, W, K, Nout, E, k, ceff, used,
-                                                              slot_token, tiles, O16, pf,
-                                                              part_bytes, act, bias, s, mask,
-                                                              O32, Z16, dp);
-        t = Tile::k128x64;   // K-major right operands: no K sets
-    }
-    if (t == Tile::k256) {
-        // forward products: 16 waves of 64x64 (four per SIMD, more latency
-        // hidden than the 8 waves of 128x64 save in LDS reads); the backward's
-        // K-major products keep 8 waves (16 would spill there)
-        if constexpr (MODE == 0 || MODE == 1 || MODE == 5)
-            return launch_tiles<256, 256, 4, 4, 1, kBK, MODE>(A, W, K, Nout, E, k, ceff, used,
-                                                              slot_token, tiles + E + 1, O16, pf,
-                                                              part_bytes, act, bias, s, mask,
-                                                              O32, Z16, dp);
-        else
-            return launch_tiles<256, 256, 2, 4, 1, kBK, MODE>(A, W, K, Nout, E, k, ceff, used,
-                                                              slot_token, tiles + E + 1, O16, pf,
-                                                              part_bytes, act, bias, s, mask,
-                                                              O32, Z16, dp);
-    }
-    if (t == Tile::k128x64)
-        return launch_tiles<128, 64, 2, 2, 1, kBK, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token,
-                                                 tiles, O16, pf, part_bytes, act, bias, s, mask,
-                                                 O32, Z16, dp);
-    return launch_tiles<128, 128, 2, 2, 1, kBK, MODE>(A, W, K, Nout, E, k, ceff, used, slot_token, tiles,
-                                              O16, pf, part_bytes, act, bias, s, mask, O32, Z16,
-                                              dp);
+    return with_tile<MODE>(t, tiles, E, [&](auto c, const int32_t *tt) {
+        using C = decltype(c);
+        return launch_tiles<C::BM, C::BN, C::WM, C::WN, C::WK, C::BKT, MODE>(
+            A, W, K, Nout, E, k, ceff, used, slot_token, tt, O16, pf, part_bytes, act, bias, s,
+            mask, O32, Z16, dp);
+    });
 }
 
 }  // namespace
@@ -1212,14 +1215,14 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
         return launch_gemm<5>(pick_tile(rows_per_expert, d, E),
                               static_cast<const unsigned short *>(H),
                               static_cast<const unsigned short *>(w_down), d_ff, d, E, k, ceff,
-                              used, slot_token, tiles, static_cast<unsigned short *>(Y), part,
-                              part_bytes, kActRelu, b_down, s, nullptr, nullptr, nullptr, dp);
+                              used, slot_token, tiles, nullptr, part, part_bytes, kActRelu,
+                              b_down, s, nullptr, static_cast<float *>(Y), nullptr, dp);
     if (bf16)
         return launch_gemm<1>(pick_tile(rows_per_expert, d, E),
                               static_cast<const unsigned short *>(H),
                               static_cast<const unsigned short *>(w_down), d_ff, d, E, k, ceff,
-                              used, slot_token, tiles, static_cast<unsigned short *>(Y), part,
-                              part_bytes, kActRelu, b_down, s);
+                              used, slot_token, tiles, nullptr, part, part_bytes, kActRelu,
+                              b_down, s, nullptr, static_cast<float *>(Y));
     hipLaunchKernelGGL(experts_f32_kernel<1>,
                        dim3((unsigned)((d + 63) / 64), (unsigned)((ceff + 63) / 64), E),
                        dim3(256), 0, s, static_cast<const float *>(H),
@@ -1227,6 +1230,25 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
                        slot_token, (float *)nullptr, static_cast<float *>(Y), kActRelu, b_down,
                        dp);
     return hipGetLastError();
+}
+
+int expert_kernel_name(bool bf16, int product, int64_t d, int64_t d_ff, int E,
+                       int64_t rows_per_expert, bool dropout, char *buf, size_t len) {
+    if (!bf16)
+        return snprintf(buf, len, "experts_f32_kernel<%d>", product);
+    const int64_t nout = product == 0 ? d_ff : d;
+    const int mode = product == 0 ? 0 : (dropout ? 5 : 1);
+    auto name = [&](auto c, const int32_t *) {
+        using C = decltype(c);
+        return snprintf(buf, len, "expert_gemm_kernel<%d, %d, %d, %d, %d, %d, 2, %d>", C::BM,
+                        C::BN, C::WM, C::WN, C::WK, C::BKT, mode);
+    };
+    const Tile t = pick_tile(rows_per_expert, nout, E);
+    if (mode == 0)
+        return with_tile<0>(t, nullptr, E, name);
+    if (mode == 5)
+        return with_tile<5>(t, nullptr, E, name);
+    return with_tile<1>(t, nullptr, E, name);
 }
 
 // ---- backward-pass products (bf16 operands, fp32 accumulation) ----------

@@ -6,8 +6,6 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <mutex>
-
 #include "../../include/moe.h"
 #include "common.hpp"
 
@@ -39,7 +37,7 @@ struct Dims {
 
 // Workspace regions (byte offsets from the base).
 struct Layout {
-    size_t idx, gate, slot, used, tiles, slot_token, H, Y, router, part, total;
+    size_t idx, gate, slot, used, tiles, slot_token, H, Y, router, dispatch, part, total;
 };
 
 // Router scratch: the bf16 split of W_g (and partial scores for many experts).
@@ -63,8 +61,9 @@ Layout layout_of(const Dims &m) {
     L.tiles = o;      o += align_up((size_t)(2 * (m.E + 1)) * 4);
     L.slot_token = o; o += align_up((size_t)(m.E * m.ceff) * 4);
     L.H = o;          o += align_up((size_t)(m.E * m.ceff * m.d_ff) * dtype_size(m.dtype));
-    L.Y = o;          o += align_up(nk * (size_t)m.d * dtype_size(m.dtype));
+    L.Y = o;          o += align_up(nk * (size_t)m.d * 4);   // fp32 expert output rows
     L.router = o;     o += router_bytes(m.N, m.d, m.E, m.dtype);
+    L.dispatch = o;   o += align_up(moe::dispatch_workspace_bytes(m.N, (int)m.E, m.k));
     L.part = o;       o += expert_bytes(m.dtype);
     L.total = o;
     return L;
@@ -74,7 +73,7 @@ Layout layout_of(const Dims &m) {
 // and the gradient intermediates.
 struct BwdLayout {
     size_t idx, gate, slot, used, tiles, slot_token, H, Y, dY, ds, dZ, dXa, T1, T2, dsT3,
-        xT3, gpart, router, part, total;
+        xT3, gpart, router, dispatch, part, total;
     int64_t Kp, Tc, S;
 };
 
@@ -107,7 +106,7 @@ BwdLayout bwd_layout_of(const Dims &m) {
     L.tiles = o;      o += align_up((size_t)(2 * (m.E + 1)) * 4);
     L.slot_token = o; o += align_up((size_t)(m.E * m.ceff) * 4);
     L.H = o;          o += align_up((size_t)(m.E * m.ceff * m.d_ff) * 2);
-    L.Y = o;          o += align_up(nk * (size_t)m.d * 2);
+    L.Y = o;          o += align_up(nk * (size_t)m.d * 4);   // fp32 expert output rows
     L.dY = o;         o += align_up(nk * (size_t)m.d * 2);
     L.ds = o;         o += align_up(nk * 4);
     L.dZ = o;         o += align_up((size_t)(m.E * m.ceff * m.d_ff) * 2);
@@ -121,6 +120,7 @@ BwdLayout bwd_layout_of(const Dims &m) {
     L.xT3 = o;        o += align_up((size_t)m.d * 3 * tok * 2);
     L.gpart = o;      o += align_up((size_t)(L.S * m.E * m.d) * 4);
     L.router = o;     o += router_bytes(m.N, m.d, m.E, m.dtype);
+    L.dispatch = o;   o += align_up(moe::dispatch_workspace_bytes(m.N, (int)m.E, m.k));
     L.part = o;       o += expert_bytes(m.dtype);   // split scratch of the expert products
     L.total = o;
     return L;
@@ -297,7 +297,7 @@ int check_expert_ws(const void *ws) {
 
 // The forward state the backward needs, in the backward's workspace layout:
 // routing (into the exported arrays when given), dispatch plan, H, the
-// experts' bf16 output rows Y (bias and dropout applied) and, for GELU, the
+// experts' fp32 output rows Y (bias and dropout applied) and, for GELU, the
 // bf16 pre-activations (in the dZ region, which the dZ product overwrites).
 static int forward_state(const BwdLayout &L, char *ws, const moe_tensor *x,
                          const moe_tensor *W_g, const moe_tensor *noise, const moe_tensor *W_up,
@@ -375,8 +375,48 @@ int moe_router(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noi
                           static_cast<hipStream_t>(stream));
 }
 
+int moe_expert_kernel_name(int64_t N, int64_t d, int64_t E, int64_t d_ff, int k,
+                           float capacity_factor, int32_t dtype, int product, int dropout,
+                           char *buf, size_t len) {
+    if (!buf && len > 0)
+        return MOE_ERR_NULL;
+    if (!valid_dtype(dtype))
+        return MOE_ERR_DTYPE;
+    if (!cf_ok(capacity_factor) || (product != 0 && product != 1) || N <= 0)
+        return MOE_ERR_ARG;
+    Dims m{N, d, E, d_ff, k, 0, 0, dtype};
+    m.C = capacity_of(N, E, k, capacity_factor);
+    m.ceff = m.C < N ? m.C : N;
+    const int rc = check_sizes(m);
+    if (rc != MOE_OK)
+        return rc;
+    return moe::expert_kernel_name(dtype == MOE_BF16, product, d, d_ff, (int)E,
+                                   rows_per_expert(N, k, E, m.ceff), dropout != 0, buf, len);
+}
+
+size_t moe_dispatch_workspace_size(int64_t N, int64_t E, int k) {
+    if (N < 0 || E <= 0 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK ||
+        N * (int64_t)k >= ((int64_t)1 << 31))
+        return 0;
+    return moe::dispatch_workspace_bytes(N, (int)E, k);
+}
+
+// Zeroes the router statistics a call exports when it has no tokens.
+static int zero_router_stats(int64_t E, int32_t *demand, int32_t *drops, float *gate_sum,
+                             hipStream_t s) {
+    if (demand)
+        MOE_TRY(moe::launch_fill_i32(demand, E, 0, s));
+    if (drops)
+        MOE_TRY(moe::launch_fill_i32(drops, E, 0, s));
+    if (gate_sum)   // 0.0f has the bit pattern of integer 0
+        MOE_TRY(moe::launch_fill_i32(reinterpret_cast<int32_t *>(gate_sum), E, 0, s));
+    return MOE_OK;
+}
+
 int moe_dispatch(int64_t N, int64_t E, int k, int64_t capacity, const int32_t *topk_idx,
-                 int32_t *slot, int32_t *used, int32_t *slot_token, int32_t *tiles,
+                 const float *topk_gate, int32_t *slot, int32_t *used, int32_t *slot_token,
+                 int32_t *tiles, int32_t *expert_demand, int32_t *expert_drops,
+                 float *expert_gate_sum, void *workspace, size_t workspace_bytes,
                  void *stream) {
     if (N < 0 || E <= 0 || k < 1 || k > E || capacity < 0 || (N > 0 && capacity == 0))
         return MOE_ERR_ARG;
@@ -387,13 +427,26 @@ int moe_dispatch(int64_t N, int64_t E, int k, int64_t capacity, const int32_t *t
         return MOE_ERR_UNSUPPORTED;
     if (!used || !tiles || (N > 0 && (!topk_idx || !slot || !slot_token)))
         return MOE_ERR_NULL;
+    if (N > 0 && expert_gate_sum && !topk_gate)
+        return MOE_ERR_NULL;
+    const size_t need = moe::dispatch_workspace_bytes(N, (int)E, k);
+    if (need > 0) {
+        if (!workspace)
+            return MOE_ERR_NULL;
+        if (!aligned(workspace, kAlign))
+            return MOE_ERR_ALIGN;
+        if (workspace_bytes < need)
+            return MOE_ERR_WORKSPACE;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (N == 0) {
         MOE_TRY(moe::launch_fill_i32(used, E, 0, s));
-        return hip_status(moe::launch_fill_i32(tiles, 2 * (E + 1), 0, s));
+        MOE_TRY(moe::launch_fill_i32(tiles, 2 * (E + 1), 0, s));
+        return zero_router_stats(E, expert_demand, expert_drops, expert_gate_sum, s);
     }
-    return hip_status(moe::launch_dispatch(topk_idx, N, (int)E, k, ceff, slot, used,
-                                           slot_token, tiles, s));
+    return hip_status(moe::launch_dispatch(topk_idx, topk_gate, N, (int)E, k, ceff, slot, used,
+                                           slot_token, tiles, expert_demand, expert_drops,
+                                           expert_gate_sum, workspace, s));
 }
 
 static int expert_up_impl(const moe_tensor *x, const moe_tensor *W_up, int k, int64_t capacity,
@@ -623,8 +676,9 @@ int moe_forward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor 
     if (N == 0) {
         stats->capacity = 0;
         if (stats->used_capacity)
-            return hip_status(moe::launch_fill_i32(stats->used_capacity, E, 0, s));
-        return MOE_OK;
+            MOE_TRY(moe::launch_fill_i32(stats->used_capacity, E, 0, s));
+        return zero_router_stats(E, stats->expert_demand, stats->expert_drops,
+                                 stats->expert_gate_sum, s);
     }
     if (!W_up->data || !W_down->data || !out->data)
         return MOE_ERR_NULL;
@@ -650,13 +704,15 @@ int moe_forward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor 
     int32_t *tiles = reinterpret_cast<int32_t *>(ws + L.tiles);
     int32_t *slot_token = reinterpret_cast<int32_t *>(ws + L.slot_token);
     void *H = ws + L.H;
-    void *Y = ws + L.Y;   // expert outputs in the dtype of x
+    void *Y = ws + L.Y;   // expert outputs, fp32
     stats->capacity = m.C;
 
     rc = router_checked(x, W_g, noise, N, d, E, k, idx, gate, ws + L.router, s);
     if (rc != MOE_OK)
         return rc;
-    MOE_TRY(moe::launch_dispatch(idx, N, (int)E, k, m.ceff, slot, used, slot_token, tiles, s));
+    MOE_TRY(moe::launch_dispatch(idx, gate, N, (int)E, k, m.ceff, slot, used, slot_token, tiles,
+                                 stats->expert_demand, stats->expert_drops,
+                                 stats->expert_gate_sum, ws + L.dispatch, s));
     const bool bf16 = x->dtype == MOE_BF16;
     const int64_t rpe = rows_per_expert(N, k, E, m.ceff);
     void *part = ws + L.part;
@@ -666,7 +722,7 @@ int moe_forward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor 
     MOE_TRY(moe::launch_expert_down(bf16, H, W_down->data, d, d_ff, (int)E, k, m.ceff, used,
                                     slot_token, tiles, Y, rpe, part, part_bytes, o.b_down, s,
                                     o.drop));
-    MOE_TRY(moe::launch_combine(Y, bf16 ? 1 : 0, gate, slot, N, d, k, out->data, out->dtype, s));
+    MOE_TRY(moe::launch_combine(Y, 0, gate, slot, N, d, k, out->data, out->dtype, s));
     return MOE_OK;
 }
 
@@ -693,52 +749,49 @@ size_t moe_backward_workspace_size(int64_t N, int64_t d, int64_t E, int64_t d_ff
 // The backward; with `saved`, the forward state is the one a
 // moe_forward_train call left in the workspace (and in the exported routing
 // arrays) instead of being recomputed.
-// Second stream of a device for the backward's branch that needs only the
-// combine backward's outputs (the router-weight gradient and the
-// down-projection weight gradient), so that its products fill the CUs the
-// main chain's products leave idle in their last rounds; and the two events
-// that fork it from and join it to the caller's stream. Created on first use
-// with the device current, at the default priority, never destroyed. The
-// fork-to-join section of a call holds the device's lock, so calls from
-// several host threads cannot interleave their event records (their side
-// work serialises on the one side stream). Under stream capture the events
-// fork and join the side stream inside the captured graph; the stream is
-// not created during a capture (creation is not a capturable operation).
-// NULL when unavailable: the branch then runs on the caller's stream.
-struct SideStream {
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-    bool failed = false;
-    std::mutex mu;
-};
-constexpr int kSideDevices = 64;
-static SideStream g_side[kSideDevices];
-static std::mutex g_side_init;
-
-static SideStream *side_stream(hipStream_t caller) {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices)
-        return nullptr;
-    SideStream &ss = g_side[dev];
-    std::lock_guard<std::mutex> g(g_side_init);
-    if (!ss.s && !ss.failed) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-            (void)hipGetLastError();
-            return nullptr;
-        }
-        if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) {
-            ss.s = nullptr;
-        } else if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-                   hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
-            hipStreamDestroy(ss.s);
-            ss.s = nullptr;
-        }
-        ss.failed = ss.s == nullptr;
-        (void)hipGetLastError();   // a failed creation leaves no error behind
+// Fork of the backward's second branch onto the caller's aux stream: the
+// router-weight gradient and the down-projection weight gradient need only
+// the combine backward's outputs, so on a second stream their products fill
+// the CUs the main chain's products leave idle in their last rounds. Two
+// events created for the call fork the aux stream from the caller's stream
+// and join it back; they are destroyed when the call returns (HIP releases an
+// event whose record is still pending once it completes, and a wait already
+// enqueued on it is unaffected), so nothing outlives the call. Under stream
+// capture the record/wait pairs become the graph's fork and join edges.
+// Without an aux stream the branch runs on the caller's stream.
+struct Fork {
+    hipStream_t s, s2;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    bool open = false;
+    explicit Fork(hipStream_t main) : s(main), s2(main) {}
+    int begin(void *aux) {
+        if (!aux || static_cast<hipStream_t>(aux) == s)
+            return MOE_OK;
+        if (hipEventCreateWithFlags(&ev[0], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&ev[1], hipEventDisableTiming) != hipSuccess ||
+            hipEventRecord(ev[0], s) != hipSuccess ||
+            hipStreamWaitEvent(static_cast<hipStream_t>(aux), ev[0], 0) != hipSuccess)
+            return MOE_ERR_HIP;
+        s2 = static_cast<hipStream_t>(aux);
+        open = true;
+        return MOE_OK;
     }
-    return ss.s ? &ss : nullptr;
-}
+    // join the aux stream back into the caller's stream (idempotent)
+    int join() {
+        if (!open)
+            return MOE_OK;
+        open = false;
+        if (hipEventRecord(ev[1], s2) != hipSuccess || hipStreamWaitEvent(s, ev[1], 0) != hipSuccess)
+            return MOE_ERR_HIP;
+        return MOE_OK;
+    }
+    ~Fork() {
+        (void)join();
+        for (hipEvent_t e : ev)
+            if (e)
+                (void)hipEventDestroy(e);
+    }
+};
 
 static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
                          const moe_tensor *W_up, const moe_tensor *W_down,
@@ -826,8 +879,9 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
         if (db_down)
             MOE_TRY(moe::launch_fill_i32(static_cast<int32_t *>(db_down->data), E * d, 0, s));
         if (stats->used_capacity)
-            return hip_status(moe::launch_fill_i32(stats->used_capacity, E, 0, s));
-        return MOE_OK;
+            MOE_TRY(moe::launch_fill_i32(stats->used_capacity, E, 0, s));
+        return zero_router_stats(E, stats->expert_demand, stats->expert_drops,
+                                 stats->expert_gate_sum, s);
     }
     if (!W_up->data || !W_down->data || !dout->data || !dx->data)
         return MOE_ERR_NULL;
@@ -860,7 +914,7 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
     const int64_t rpe = rows_per_expert(N, k, E, ceff);
     const int Ei = (int)E;
 
-    // forward state: routing, plan, H and the experts' bf16 outputs
+    // forward state: routing, plan, H and the experts' fp32 outputs
     const bool gelu = o.act == moe::kActGelu;
     if (!saved) {
         rc = forward_state(L, ws, x, W_g, noise, W_up, W_down, o, m, stats, s);
@@ -871,18 +925,15 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
     // chunk on the exact split of ds, then the chunks summed in order
     MOE_TRY(moe::launch_combine_backward(dout->data, Y, gate, slot, N, d, k, dY, ds, s,
                                          o.drop));
-    // fork: the side stream s2 takes the router-weight gradient and (when the
+    // fork: the aux stream s2 takes the router-weight gradient and (when the
     // products read K-major) the down-projection weight gradient; both read
-    // only the forward state, ds and dY, and write buffers of their own
-    SideStream *ss = side_stream(s);
-    std::unique_lock<std::mutex> side_lock;
-    hipStream_t s2 = s;
-    if (ss) {
-        side_lock = std::unique_lock<std::mutex>(ss->mu);
-        MOE_TRY(hipEventRecord(ss->fork, s));
-        MOE_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
-        s2 = ss->s;
-    }
+    // only the forward state, ds and dY, and write buffers of their own. The
+    // fork is joined back when `fork` goes out of scope on every return path.
+    Fork fork(s);
+    rc = fork.begin(stats->aux_stream);
+    if (rc != MOE_OK)
+        return rc;
+    const hipStream_t s2 = fork.s2;
     MOE_TRY(moe::launch_ds_split(ds, idx, N, Tc, S, Ei, k, dsT3, s2));
     MOE_TRY(moe::launch_transpose_rows(x->data, d, Tc, nullptr, N, nullptr, k, 0, Tc, 3, (int)S,
                                        xT3, s2));
@@ -897,31 +948,14 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
             MOE_TRY(moe::launch_colsum_rows(dY, d, Ei, ceff, used, st, 1,
                                             static_cast<float *>(db_down->data), s2));
     }
-    // joined at the end of the call (also when a launch below fails)
-    struct Join {
-        SideStream *ss;
-        hipStream_t s, s2;
-        bool done = false;
-        int operator()() {
-            done = true;
-            if (ss && (hipEventRecord(ss->join, s2) != hipSuccess ||
-                       hipStreamWaitEvent(s, ss->join, 0) != hipSuccess))
-                return MOE_ERR_HIP;
-            return MOE_OK;
-        }
-        ~Join() {
-            if (!done)
-                (*this)();
-        }
-    } join{ss, s, s2};
     // experts, input side: dZ = (dY W_down) [H > 0]; dX = dZ W_up; dx
     // (the weights are read K-major by the products themselves)
     MOE_TRY(moe::launch_expert_dz(dY, W_down->data, gelu ? dZ : H, o.act, d, d_ff, Ei, k, ceff,
                                   used, st, tiles, dZ, rpe, s));
     MOE_TRY(moe::launch_expert_rows_f32(dZ, W_up->data, d_ff, d, Ei, k, ceff, used, st, tiles,
                                         dXa, rpe, s));
-    MOE_TRY(moe::launch_dx(dXa, ds, idx, slot, static_cast<const float *>(W_g->data), N, d, k,
-                           static_cast<float *>(dx->data), s));
+    MOE_TRY(moe::launch_dx(dXa, ds, idx, slot, static_cast<const float *>(W_g->data), N, d, Ei,
+                           k, static_cast<float *>(dx->data), s));
     // experts, weight side: dW_down = dY^T H (on the side stream, above),
     // dW_up = dZ^T X over each expert's kept rows, read K-major by the
     // products themselves
@@ -931,7 +965,7 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
         if (db_up)
             MOE_TRY(moe::launch_colsum_rows(dZ, d_ff, Ei, ceff, used, nullptr, 1,
                                             static_cast<float *>(db_up->data), s));
-        return join();
+        return fork.join();
     }
     // (longer experts: through transposes, K = kept rows padded to Kp;
     // bias gradients: the row sums of the transposed dY and dZ)
@@ -947,7 +981,7 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
         MOE_TRY(moe::launch_row_sums(T2, E * d_ff, Kp, static_cast<float *>(db_up->data), s));
     MOE_TRY(moe::launch_batched_gemm_bf16(T2, T1, d_ff, Kp, d, Ei, d_ff * Kp, d * Kp, d_ff * d,
                                           static_cast<float *>(dW_up->data), s));
-    return join();
+    return fork.join();
 }
 
 int moe_backward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
@@ -1009,8 +1043,9 @@ int moe_forward_train(const moe_tensor *x, const moe_tensor *W_g, const moe_tens
     if (N == 0) {
         stats->capacity = 0;
         if (stats->used_capacity)
-            return hip_status(moe::launch_fill_i32(stats->used_capacity, E, 0, s));
-        return MOE_OK;
+            MOE_TRY(moe::launch_fill_i32(stats->used_capacity, E, 0, s));
+        return zero_router_stats(E, stats->expert_demand, stats->expert_drops,
+                                 stats->expert_gate_sum, s);
     }
     if (!W_up->data || !W_down->data || !out->data)
         return MOE_ERR_NULL;
@@ -1031,7 +1066,7 @@ int moe_forward_train(const moe_tensor *x, const moe_tensor *W_g, const moe_tens
     const float *gate = stats->topk_gate ? stats->topk_gate
                                          : reinterpret_cast<const float *>(ws + L.gate);
     const int32_t *slot = stats->slot ? stats->slot : reinterpret_cast<const int32_t *>(ws + L.slot);
-    return hip_status(moe::launch_combine(ws + L.Y, 1, gate, slot, N, d, k, out->data,
+    return hip_status(moe::launch_combine(ws + L.Y, 0, gate, slot, N, d, k, out->data,
                                           out->dtype, s));
 }
 
@@ -1061,7 +1096,9 @@ static int forward_state(const BwdLayout &L, char *ws, const moe_tensor *x,
     int rc = router_checked(x, W_g, noise, m.N, m.d, m.E, m.k, idx, gate, ws + L.router, s);
     if (rc != MOE_OK)
         return rc;
-    MOE_TRY(moe::launch_dispatch(idx, m.N, Ei, m.k, m.ceff, slot, used, st, tiles, s));
+    MOE_TRY(moe::launch_dispatch(idx, gate, m.N, Ei, m.k, m.ceff, slot, used, st, tiles,
+                                 stats->expert_demand, stats->expert_drops,
+                                 stats->expert_gate_sum, ws + L.dispatch, s));
     const bool gelu = o.act == moe::kActGelu;
     // (the same launch configuration as moe_forward_ex, split included, so
     // the state and out are bit for bit the forward's)

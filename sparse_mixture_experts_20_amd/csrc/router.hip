@@ -81,9 +81,12 @@ __device__ __forceinline__ void topk_softmax_group(const float (&v)[Q], int E, i
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const int e = lg + G * q;
+            // a NaN score ranks as -inf, so every lane of the group holds a
+            // candidate in [0, E) while an untaken expert is left
+            const float vq = v[q] != v[q] ? -INFINITY : v[q];
             if (e < E && !((taken >> q) & 1u)) {
-                if (v[q] > bv || (v[q] == bv && e < be)) {
-                    bv = v[q];
+                if (vq > bv || (vq == bv && e < be)) {
+                    bv = vq;
                     be = e;
                 }
             }

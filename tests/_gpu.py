@@ -57,11 +57,22 @@ def out_f64(wl, out_t, rows=None):
     return a.astype(np.float64)
 
 
-def run_forward(dev):
+def run_forward(dev, router_stats=True):
     from sparse_mixture_experts_20_amd import binding as B
     return B.forward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"],
                      dev["k"], dev["cf"], export=True, act=dev.get("act", "relu"),
-                     b_up=dev.get("b_up"), b_down=dev.get("b_down"))
+                     b_up=dev.get("b_up"), b_down=dev.get("b_down"),
+                     router_stats=router_stats)
+
+
+def check_router_stats(res, stats):
+    """Per-expert demand and drops bit-exact; gate sums within GATE_TOL per
+    summed gate (each gate is within GATE_TOL) plus fp32 summation error."""
+    np.testing.assert_array_equal(to_np(stats.demand), res.demand)
+    np.testing.assert_array_equal(to_np(stats.drops), res.expert_drops)
+    g = to_np(stats.gate_sum).astype(np.float64)
+    tol = GATE_TOL * res.demand + 1e-6 * np.abs(res.gate_sum) + 1e-6
+    assert np.all(np.abs(g - res.gate_sum) <= tol), np.abs(g - res.gate_sum).max()
 
 
 def check_routing(res, stats):
@@ -97,3 +108,23 @@ def sample_rows(res, n, seed=0):
         pick += list(rng.choice(dropped, size=min(len(dropped), n // 4), replace=False))
     pick += list(rng.choice(N, size=min(N, n), replace=False))
     return np.unique(np.array(pick, dtype=np.int64))
+
+
+def strata_rows(res, bm=128):
+    """Tokens that exercise every (expert, bm-row tile) of both expert
+    products: for each tile holding kept rows, the tokens of its first and
+    of its last kept row (a 256-row tile is two 128-row strata). Returns
+    (sorted token ids, number of (expert, tile) pairs covered)."""
+    ceff = max(int(res.used.max(initial=0)), 1)
+    tok = np.full((res.E, ceff), -1, np.int64)
+    t_i, j_i = np.nonzero(res.slot >= 0)
+    tok[res.idx[t_i, j_i], res.slot[t_i, j_i]] = t_i
+    pick, pairs = set(), 0
+    for e in range(res.E):
+        u = int(res.used[e])
+        for r0 in range(0, u, bm):
+            pairs += 1
+            pick.add(int(tok[e, r0]))
+            pick.add(int(tok[e, min(r0 + bm, u) - 1]))
+    assert -1 not in pick
+    return np.array(sorted(pick), dtype=np.int64), pairs

@@ -140,10 +140,22 @@ def test_forward_rejects_bad_arguments(L):
 def test_stage_entry_points_reject_bad_arguments(L):
     v = ctypes.c_void_p(FAKE)
     # dispatch: k > E, capacity 0 with tokens, E > 256, NULL outputs
-    assert L.moe_dispatch(10, 4, 5, 3, v, v, v, v, v, None) == -4
-    assert L.moe_dispatch(10, 4, 2, 0, v, v, v, v, v, None) == -4
-    assert L.moe_dispatch(10, 300, 2, 3, v, v, v, v, v, None) == -6
-    assert L.moe_dispatch(10, 4, 2, 3, None, v, v, v, v, None) == -1
+    def disp(N, E, k, C, idx=v, gate=v, gsum=None, ws=None, wsb=0):
+        return L.moe_dispatch(N, E, k, C, idx, gate, v, v, v, v, None, None, gsum, ws, wsb,
+                              None)
+    assert disp(10, 4, 5, 3) == -4
+    assert disp(10, 4, 2, 0) == -4
+    assert disp(10, 300, 2, 3) == -6
+    assert disp(10, 4, 2, 3, idx=None) == -1
+    # the gate sums read the gates
+    assert disp(10, 4, 2, 3, gate=None, gsum=v) == -1
+    # more than one 4096-assignment chunk needs the scratch: NULL, misaligned, short
+    need = B.dispatch_workspace_size(5000, 4, 2)
+    assert need > 0 and B.dispatch_workspace_size(2048, 4, 2) == 0
+    assert B.dispatch_workspace_size(10, 4, 5) == 0 and B.dispatch_workspace_size(-1, 4, 2) == 0
+    assert disp(5000, 4, 2, 3000) == -1
+    assert disp(5000, 4, 2, 3000, ws=ctypes.c_void_p(FAKE + 4), wsb=need) == -7
+    assert disp(5000, 4, 2, 3000, ws=v, wsb=need - 1) == -5
     # combine: shape mismatch, bad dtype, Y rows [N*k, d] of fp32 or bf16
     out = _t(FAKE, F32, 10, 8)
     yb = _t(FAKE, BF16, 20, 8)

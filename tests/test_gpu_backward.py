@@ -90,6 +90,9 @@ CASES = {
     "bwd_k_equals_E": (100, 32, 4, 4, 48, 1.0, 0.0, 0.0, 307),
     "bwd_single_token": (1, 64, 8, 2, 64, 1.0, 0.0, 0.0, 308),
     "bwd_one_expert": (50, 32, 1, 1, 40, 1.0, 0.0, 0.0, 309),
+    # experts longer than the K-major weight products take (3072 rows): the
+    # weight gradients go through transposes and the padded batched product
+    "bwd_long_experts": (8192, 64, 4, 2, 128, 1.0, 0.5, 0.0, 316),
 }
 
 
@@ -119,6 +122,8 @@ def test_small_backward_matches_oracle(torch_mod, name):
         assert alldrop.sum() > 0
     if name == "bwd_k1":
         assert not G.to_np(dwg).any()       # one choice: the gate is 1, ds is 0
+    if name == "bwd_long_experts":
+        assert res.used.max() > 3072
     del dev
 
 
@@ -128,6 +133,9 @@ VARIANTS = {
     "bwd_gelu_nobias": (333, 136, 5, 2, 200, 1.0, 0.3, 312, "gelu", 0.0),
     "bwd_relu_bias": (1000, 264, 16, 4, 392, 0.8, 0.5, 313, "relu", 0.05),
     "bwd_gelu_bias_drop": (512, 64, 4, 2, 128, 0.3, 0.0, 314, "gelu", 0.1),
+    # the transposed weight-gradient path (experts past 3072 rows) with GELU
+    # and both biases: db_up and db_down from the transposed dZ and dY
+    "bwd_long_experts_gelu_bias": (8192, 64, 4, 2, 128, 1.0, 0.5, 317, "gelu", 0.05),
 }
 
 
@@ -155,6 +163,36 @@ def test_variant_backward_matches_oracle(torch_mod, name):
     if bstd:
         for e in np.nonzero(res.used == 0)[0]:
             assert not G.to_np(grads[4][e]).any() and not G.to_np(grads[5][e]).any()
+    if name.startswith("bwd_long_experts"):
+        assert res.used.max() > 3072
+    del dev
+
+
+def test_nan_token_routes_in_range_and_backward_runs(torch_mod):
+    """A token row of NaNs: its scores rank as -inf, so the forward still
+    writes expert ids in [0, E) for it (checked on the host before the
+    backward reads W_g rows by those ids); the backward then runs, and every
+    other token keeps a finite dx (its gradient involves only its own rows
+    and the weights)."""
+    torch = torch_mod
+    from sparse_mixture_experts_20_amd import binding as B
+    wl = W.custom("nan_row", N=256, d=64, E=8, k=2, d_ff=64, dtype="bf16", cf=2.0, sigma=0.0,
+                  seed=401, w_std=0.05)
+    dev = _upload(wl, keep_host=False)
+    dev["x"][5] = float("nan")
+    out, st = B.forward(dev["x"], dev["W_g"], None, dev["W_up"], dev["W_down"], wl.k,
+                        wl.cfg.cf, export=True)
+    torch.cuda.synchronize()
+    idx = G.to_np(st.idx)
+    assert idx.min() >= 0 and idx.max() < wl.E
+    assert len(set(idx[5].tolist())) == wl.k
+    grads = B.backward(dev["x"], dev["W_g"], None, dev["W_up"], dev["W_down"], wl.k, wl.cfg.cf,
+                       dev["dout"])
+    torch.cuda.synchronize()
+    dx = G.to_np(grads[0])
+    others = np.ones(wl.N, bool)
+    others[5] = False
+    assert np.all(np.isfinite(dx[others]))
     del dev
 
 

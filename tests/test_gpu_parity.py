@@ -1,9 +1,11 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
 Small cases compare every output element; the five layer shapes of the
-benchmark table compare routing, slots and drops for all tokens and the
-layer output on a seeded sample of token rows (tokens that lost a choice to
-capacity included), in the launch configuration the benchmark times.
+benchmark table compare routing, slots, drops and the router statistics for
+all tokens and the layer output, in the launch configuration the benchmark
+times, on every token row except at the fine-grained layer (256 experts,
+15 GB of weights), where it is compared on the tokens that hold the first and
+last kept row of every (expert, 128-row tile) of the expert products.
 """
 import numpy as np
 import pytest
@@ -108,6 +110,7 @@ def test_small_layer_matches_oracle(torch_mod, name):
     out, st = G.run_forward(dev)
     torch.cuda.synchronize()
     G.check_routing(res, st)
+    G.check_router_stats(res, st)
     got = G.out_f64(wl, out)
     G.check_out(wl.cfg.dtype, got, res.out)
     alldrop = (res.slot < 0).all(axis=1)
@@ -119,32 +122,72 @@ def test_small_layer_matches_oracle(torch_mod, name):
     _free(torch, dev, out)
 
 
-# (workload, rows checked): every token of the two nanoMoE-shaped layers (the
-# GELU one overflows one round of 256x256 up-product tiles, so its light
-# tiles go last), sampled tokens of the larger ones
-FULL = [("nanomoe", 2048), ("mixtral", 48), ("skew", 96), ("finegrained", 32),
-        ("nanomoe_gelu", 2048)]
+# (workload, rows checked): every token, except at the fine-grained layer,
+# where the rows are the strata of every (expert, 128-row tile)
+FULL = [("nanomoe", "all"), ("mixtral", "all"), ("skew", "all"), ("finegrained", "strata"),
+        ("nanomoe_gelu", "all")]
 
 
-@pytest.mark.parametrize("name,nrows", FULL)
-def test_benchmark_layer_matches_oracle(torch_mod, name, nrows):
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,rows_mode", FULL)
+def test_benchmark_layer_matches_oracle(torch_mod, name, rows_mode):
     torch = torch_mod
     wl = W.make(name)
     G.say(f"[parity] {name}: N={wl.N} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff}")
     dev = _upload(wl, keep_host=True)
     out, st = G.run_forward(dev)
     torch.cuda.synchronize()
-    G.say(f"[parity] {name}: gpu done; oracle routing + {nrows} sampled rows")
     route = oracle.forward(wl, rows=[0])
-    rows = G.sample_rows(route, nrows, seed=1)
+    G.check_routing(route, st)
+    G.check_router_stats(route, st)
+    rows, pairs = G.strata_rows(route)
+    if rows_mode == "all":
+        rows = np.arange(wl.N)
+    G.say(f"[parity] {name}: routing and router statistics exact; oracle on {len(rows)} rows "
+          f"covering all {pairs} (expert, 128-row tile) pairs with kept rows")
     res = oracle.forward(wl, rows=rows)
-    G.check_routing(res, st)
     err = G.check_out(wl.cfg.dtype, G.out_f64(wl, out, rows), res.out)
     G.say(f"[parity] {name}: drops={res.drops} rows={len(rows)} max_abs_err={err:.3e}")
     if name == "skew":
         assert res.drops > 8000 and res.used[0] == res.C
     else:
         assert res.drops == 0
+    _free(torch, dev, out)
+
+
+def _tied_layer(name, E, k, dtype, N=512, d_ff=64, seed=701):
+    """W_g = I (d = E) and token entries from {-1, -0.5, 0, 0.5, 1}: the
+    scores are the entries themselves, so many tokens have exactly equal
+    scores inside and at the edge of their top-k."""
+    rng = np.random.default_rng(seed)
+    x32 = rng.choice(np.array([-1.0, -0.5, 0.0, 0.5, 1.0], np.float32), size=(N, E))
+    cfg = W.Config(name, N=N, d=E, E=E, k=k, d_ff=d_ff, dtype=dtype, cf=1.5, w_std=0.05,
+                   seed=seed)
+    x = W.f32_to_bf16_bits(x32) if dtype == "bf16" else x32
+    return W.Workload(cfg, x, np.eye(E, dtype=np.float32), None, seed)
+
+
+@pytest.mark.parametrize("E,k,dtype", [(16, 4, "bf16"), (32, 3, "bf16"), (256, 8, "bf16"),
+                                       (12, 4, "f32")])
+def test_tied_scores_rank_lower_id_first(torch_mod, E, k, dtype):
+    """Exactly tied scores (nanoMoE slide 12's top-k; equal scores take the
+    lower expert id first) on each router path: the fused kernel for up to 16
+    and up to 32 experts, the score product + ranking for 256, and fp32.
+    Ids, slots and drops bit-exact against the oracle, outputs in tolerance."""
+    torch = torch_mod
+    wl = _tied_layer(f"ties_{E}_{dtype}", E, k, dtype)
+    res = oracle.forward(wl)
+    s = np.sort(res.scores, axis=1)[:, ::-1]
+    ties = int(((s[:, :k] == s[:, 1:k + 1])).any(axis=1).sum())
+    G.say(f"[parity] ties E={E} k={k} {dtype}: {ties} of {wl.N} tokens with a tie in the "
+          f"top-{k + 1}")
+    assert ties > wl.N // 2
+    dev = _upload(wl)
+    out, st = G.run_forward(dev)
+    torch.cuda.synchronize()
+    G.check_routing(res, st)
+    G.check_router_stats(res, st)
+    G.check_out(dtype, G.out_f64(wl, out), res.out)
     _free(torch, dev, out)
 
 

@@ -98,6 +98,53 @@ def test_capacity_example_matches_slides():
                                rtol=1e-13, atol=1e-14)
 
 
+def test_router_stats_match_the_capacity_example():
+    """Router statistics on the slides' capacity example (slides 15-29):
+    demand [4, 2, 2] before the mask, drops [3, 1, 1]; each token's gates sum
+    to one, so the gate sums add up to the token count."""
+    rows = _rows("capacity_example.txt")
+    demand = [int(v) for v in next(r for r in rows if r[0] == "demand")[1:]]
+    drops = [int(v) for v in next(r for r in rows if r[0] == "expert_drops")[1:]]
+    wl = W.capacity_example()
+    r = oracle.forward(wl)
+    assert r.demand.tolist() == demand
+    assert r.expert_drops.tolist() == drops
+    assert (r.demand - r.used).tolist() == drops
+    assert r.gate_sum.sum() == pytest.approx(wl.N, abs=1e-12)
+    # expert 0 is every token's first choice here
+    np.testing.assert_allclose(r.gate_sum[0], r.gate[:, 0].sum(), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("N,E,k,cf,sigma,seed", [(300, 6, 2, 0.5, 0.5, 41),
+                                                 (257, 16, 4, 1.0, 1.0, 42),
+                                                 (64, 5, 5, 0.3, 0.0, 43)])
+def test_router_stats_invariants(N, E, k, cf, sigma, seed):
+    """demand is the column sum of the dense one-hot of the ids (brute force),
+    drops are exactly the assignments whose slot is -1, and gate_sum is the
+    column sum of the dense [N, E] gate matrix (non-top-k entries 0)."""
+    wl = W.custom("stats", N=N, d=12, E=E, k=k, d_ff=8, dtype="f32", cf=cf, sigma=sigma,
+                  seed=seed)
+    r = oracle.forward(wl, rows=[0])
+    onehot = np.zeros((N, E), np.int64)
+    dense = np.zeros((N, E))
+    for t in range(N):
+        for j in range(k):
+            onehot[t, r.idx[t, j]] += 1
+            dense[t, r.idx[t, j]] = r.gate[t, j]
+    assert onehot.max() == 1   # distinct experts per token
+    np.testing.assert_array_equal(r.demand, onehot.sum(axis=0))
+    dropped = np.zeros(E, np.int64)
+    for t in range(N):
+        for j in range(k):
+            if r.slot[t, j] < 0:
+                dropped[r.idx[t, j]] += 1
+    np.testing.assert_array_equal(r.expert_drops, dropped)
+    np.testing.assert_allclose(r.gate_sum, dense.sum(axis=0), rtol=1e-13, atol=1e-13)
+    assert int(r.demand.sum()) == N * k
+    assert int(r.expert_drops.sum()) == r.drops
+    assert r.gate_sum.sum() == pytest.approx(N, rel=1e-12)
+
+
 # ----------------------------------------------------------------------------
 # independent brute force (all experts, dense masked gates) on tiny inputs
 # ----------------------------------------------------------------------------

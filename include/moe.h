@@ -23,7 +23,8 @@
  *  - All tensor data pointers are DEVICE pointers owned by the caller; the
  *    library never allocates, frees or retains device memory, and keeps no
  *    global mutable state (every value a call needs, the device's compute
- *    unit count and kernel occupancy included, is queried within the call).
+ *    unit count and kernel occupancy included, is queried within the call),
+ *    except the per-device address of moe_dispatch_noalloc's static scratch.
  *    Tensors are row-major and contiguous.
  *  - Work is enqueued on the given HIP stream (hipStream_t passed as void*;
  *    NULL = the default stream). Calls return without synchronising; the
@@ -248,6 +249,25 @@ int moe_dispatch(int64_t N, int64_t E, int k, int64_t capacity, const int32_t *t
 int moe_expert_kernel_name(int64_t N, int64_t d, int64_t E, int64_t d_ff, int k,
                            float capacity_factor, int32_t dtype, int product, int dropout,
                            char *buf, size_t len);
+
+/* moe_dispatch for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same plan, outputs and limits as moe_dispatch, but the per-chunk
+ * scratch lives in a static device array of the library (4 MiB, held by
+ * each GPU the library runs on until the process ends) instead of a
+ * workspace argument, and the call allocates nothing. MOE_ERR_UNSUPPORTED
+ * when moe_dispatch_workspace_size(N, E, k) exceeds 4 MiB (about 2 million
+ * assignments at E = 256, more with fewer experts). The library keeps the
+ * array's device address per device (taken once per device on its first
+ * call there). Calls that overlap on one GPU (on different streams, or from
+ * several host threads) share that GPU's array and race; calls ordered on
+ * one stream do not (the array holds the last call's partials, which the
+ * next call overwrites before it reads them). */
+int moe_dispatch_noalloc(int64_t N, int64_t E, int k, int64_t capacity,
+                         const int32_t *topk_idx, const float *topk_gate, int32_t *slot,
+                         int32_t *used, int32_t *slot_token, int32_t *tiles,
+                         int32_t *expert_demand, int32_t *expert_drops,
+                         float *expert_gate_sum, void *stream);
 
 /* Bytes of dispatch scratch for N tokens, E experts and top-k (0 on invalid
  * sizes or when a call needs none). */

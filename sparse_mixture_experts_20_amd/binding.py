@@ -26,7 +26,7 @@ EXPORTS = ("moe_forward", "moe_workspace_size", "moe_capacity", "moe_error_strin
            "moe_forward_ex", "moe_experts_ex", "moe_expert_up_ex", "moe_expert_down_ex",
            "moe_backward", "moe_backward_ex", "moe_backward_workspace_size",
            "moe_forward_train", "moe_backward_after_forward", "moe_dispatch_workspace_size",
-           "moe_expert_kernel_name")
+           "moe_expert_kernel_name", "moe_dispatch_noalloc")
 
 MOE_ACT_RELU, MOE_ACT_GELU = 0, 1
 ACTS = {"relu": MOE_ACT_RELU, "gelu": MOE_ACT_GELU}
@@ -119,6 +119,9 @@ def lib():
         L.moe_dispatch.argtypes = [_i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_dispatch.restype = ctypes.c_int
+        L.moe_dispatch_noalloc.argtypes = [_i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_dispatch_noalloc.restype = ctypes.c_int
         L.moe_dispatch_workspace_size.argtypes = [_i64, _i64, ctypes.c_int]
         L.moe_dispatch_workspace_size.restype = ctypes.c_size_t
         L.moe_expert_kernel_name.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float,

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/moe.h"
 #include "common.hpp"
 
@@ -392,6 +394,57 @@ int moe_expert_kernel_name(int64_t N, int64_t d, int64_t E, int64_t d_ff, int k,
         return rc;
     return moe::expert_kernel_name(dtype == MOE_BF16, product, d, d_ff, (int)E,
                                    rows_per_expert(N, k, E, m.ceff), dropout != 0, buf, len);
+}
+
+}  // extern "C"
+
+// Scratch of moe_dispatch_noalloc: a file-scope device array (each GPU that
+// runs the library holds its own copy until the process ends). Host code
+// never uses the array's name as an address: the device address of each
+// GPU's copy comes from hipGetSymbolAddress, taken once per device with that
+// device current and kept in g_noalloc_scratch.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kNoAllocDevices = 64;
+static std::atomic<void *> g_noalloc_scratch[kNoAllocDevices];
+
+// The current device's copy of `scratch` (NULL on failure).
+static void *noalloc_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocDevices)
+        return nullptr;
+    void *p = g_noalloc_scratch[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    g_noalloc_scratch[dev].store(p, std::memory_order_release);   // same value in every racer
+    return p;
+}
+
+extern "C" {
+
+int moe_dispatch_noalloc(int64_t N, int64_t E, int k, int64_t capacity,
+                         const int32_t *topk_idx, const float *topk_gate, int32_t *slot,
+                         int32_t *used, int32_t *slot_token, int32_t *tiles,
+                         int32_t *expert_demand, int32_t *expert_drops,
+                         float *expert_gate_sum, void *stream) {
+    if (N < 0 || E <= 0 || k < 1 || k > E || capacity < 0 || (N > 0 && capacity == 0))
+        return MOE_ERR_ARG;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || N * (int64_t)k >= ((int64_t)1 << 31))
+        return MOE_ERR_UNSUPPORTED;
+    const size_t need = moe::dispatch_workspace_bytes(N, (int)E, k);
+    if (need > kNoAllocScratchBytes)
+        return MOE_ERR_UNSUPPORTED;   // beyond the static scratch: use moe_dispatch
+    void *ws = nullptr;
+    if (need > 0 && !(ws = noalloc_scratch()))
+        return MOE_ERR_HIP;
+    return moe_dispatch(N, E, k, capacity, topk_idx, topk_gate, slot, used, slot_token, tiles,
+                        expert_demand, expert_drops, expert_gate_sum, ws,
+                        ws ? kNoAllocScratchBytes : 0, stream);
 }
 
 size_t moe_dispatch_workspace_size(int64_t N, int64_t E, int k) {

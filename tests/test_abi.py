@@ -156,6 +156,14 @@ def test_stage_entry_points_reject_bad_arguments(L):
     assert disp(5000, 4, 2, 3000) == -1
     assert disp(5000, 4, 2, 3000, ws=ctypes.c_void_p(FAKE + 4), wsb=need) == -7
     assert disp(5000, 4, 2, 3000, ws=v, wsb=need - 1) == -5
+    # the variant with the library's static scratch: same argument checks, and
+    # sizes whose scratch would exceed its 4 MiB are refused before any launch
+    def nod(N, E, k, C, idx=v):
+        return L.moe_dispatch_noalloc(N, E, k, C, idx, v, v, v, v, v, None, None, None, None)
+    assert nod(10, 4, 5, 3) == -4
+    assert nod(10, 300, 2, 3) == -6
+    assert B.dispatch_workspace_size(1 << 21, 256, 8) > 4 << 20
+    assert nod(1 << 21, 256, 8, 100000) == -6
     # combine: shape mismatch, bad dtype, Y rows [N*k, d] of fp32 or bf16
     out = _t(FAKE, F32, 10, 8)
     yb = _t(FAKE, BF16, 20, 8)

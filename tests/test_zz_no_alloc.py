@@ -1,0 +1,85 @@
+"""moe_dispatch_noalloc (the dispatch plan with its scratch in the library's
+static device array, for callers that cannot allocate) against moe_dispatch
+(the same plan with a caller workspace), through the C ABI: two calls in a
+row on one stream, the second smaller than the first, each with several
+4096-assignment chunks so that the scratch is used. Every output must be
+identical bit for bit."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_mod():
+    if not G.have_gpu():
+        pytest.skip("no HIP device")
+    import torch
+    from sparse_mixture_experts_20_amd import binding as B
+    B.lib()
+    return torch
+
+
+def _routing(N, E, k, seed):
+    """Seeded top-k ids (k distinct experts per token) and positive gates
+    summing to one per token."""
+    rng = np.random.default_rng(seed)
+    idx = np.argsort(rng.random((N, E)), axis=1)[:, :k].astype(np.int32)
+    g = rng.random((N, k)).astype(np.float32) + np.float32(0.05)
+    return idx, (g / g.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def _outputs(torch, N, E, k, ceff):
+    dev = "cuda"
+    return dict(slot=torch.full((N, k), -7, dtype=torch.int32, device=dev),
+                used=torch.full((E,), -7, dtype=torch.int32, device=dev),
+                slot_token=torch.full((E, max(ceff, 1)), -7, dtype=torch.int32, device=dev),
+                tiles=torch.full((2 * (E + 1),), -7, dtype=torch.int32, device=dev),
+                demand=torch.full((E,), -7, dtype=torch.int32, device=dev),
+                drops=torch.full((E,), -7, dtype=torch.int32, device=dev),
+                gate_sum=torch.full((E,), -7.0, dtype=torch.float32, device=dev))
+
+
+def _args(o):
+    from sparse_mixture_experts_20_amd import binding as B
+    p = B._ptr
+    return (p(o["slot"]), p(o["used"]), p(o["slot_token"]), p(o["tiles"]), p(o["demand"]),
+            p(o["drops"]), p(o["gate_sum"]))
+
+
+def test_noalloc_dispatch_equals_dispatch(torch_mod):
+    torch = torch_mod
+    from sparse_mixture_experts_20_amd import binding as B
+    L = B.lib()
+    s = B._stream()
+    # (N, E, k, C): 20 chunks, then 3 (the second call is the smaller one)
+    for N, E, k, C, seed in ((20000, 64, 4, 1100, 1), (5000, 16, 2, 600, 2)):
+        G.say(f"[noalloc] N={N} E={E} k={k} C={C}")
+        idx_np, gate_np = _routing(N, E, k, seed)
+        idx = torch.from_numpy(idx_np).cuda()
+        gate = torch.from_numpy(gate_np).cuda()
+        ceff = min(C, N)
+        ref, got = _outputs(torch, N, E, k, ceff), _outputs(torch, N, E, k, ceff)
+        wsb = B.dispatch_workspace_size(N, E, k)
+        assert wsb > 0
+        ws = B.alloc_workspace(wsb)
+        rc = L.moe_dispatch(N, E, k, C, B._ptr(idx), B._ptr(gate), *_args(ref),
+                            B._ptr(ws), ws.numel(), s)
+        assert rc == 0
+        rc = L.moe_dispatch_noalloc(N, E, k, C, B._ptr(idx), B._ptr(gate), *_args(got), s)
+        assert rc == 0
+        torch.cuda.synchronize()
+        for name in ref:
+            if name == "slot_token":   # rows past used[e] are left untouched by both
+                u = ref["used"].cpu().numpy()
+                a, b = ref[name].cpu().numpy(), got[name].cpu().numpy()
+                for e in range(E):
+                    assert np.array_equal(a[e, :u[e]], b[e, :u[e]]), (name, e)
+            else:
+                assert torch.equal(ref[name], got[name]), name
+        assert int(ref["demand"].sum()) == N * k
+        assert int((ref["slot"] < 0).sum()) == int(ref["drops"].sum()) > 0

@@ -21,7 +21,7 @@ Prints ONE JSON line on stdout. Besides the contract fields it carries:
                 ridge 2.5 PFLOP/s / 8 TB/s, else the bf16 MFMA peak; both
                 fractions are given. Its duration is timed with HIP events
                 on the stream it runs on, each repetition after a 1 GiB
-                write that flushes the L2 caches and the 256 MB MALL;
+                write and read that flush the L2 caches and the 256 MB MALL;
   cpu_baseline  the CPU oracle timed on this host on a bounded sample;
   secondary     per-stage average durations (flushed and back to back) and
                 derived rates.
@@ -291,9 +291,11 @@ FLUSH_BYTES = 1 << 30     # more than the L2 caches and the 256 MB MALL together
 
 
 class Flusher:
-    """Writes a 1 GiB device buffer (torch's fill kernel on the current
-    stream), evicting every operand of the previous launch from the L2 caches
-    and the MALL before a timed repetition."""
+    """Writes, then reads, a 1 GiB device buffer on the current stream (torch's
+    fill and sum kernels), evicting every operand of the previous launch from
+    the L2 caches and the 256 MB MALL before a timed repetition; the read pass
+    leaves the caches holding clean lines, so that the timed kernel does not
+    pay for writing the flush's own data back."""
 
     def __init__(self):
         import torch
@@ -303,22 +305,31 @@ class Flusher:
     def __call__(self):
         self.i += 1
         self.buf.fill_(self.i)
+        self.sink = self.buf.sum()
 
 
 def time_stage(fn, reps, flush=None):
     """Average duration (ms) of fn() from HIP events on torch's current
-    stream (the stream the library launches on), each rep bracketed by its
-    own pair of events; with `flush`, a cache flush precedes every rep
-    outside its events."""
+    stream (the stream the library launches on). Without `flush`: reps
+    back-to-back calls between one pair of events. With `flush`: a cache
+    flush precedes every rep outside its own pair of events (the event pair
+    adds a few microseconds, which matters only for the smallest stages)."""
     import torch
     for _ in range(3):
         if fn() != 0:
             raise RuntimeError("stage failed")
     torch.cuda.synchronize()
+    if flush is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
     evs = []
     for _ in range(reps):
-        if flush is not None:
-            flush()
+        flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         fn()
@@ -413,7 +424,7 @@ def bench_forward(args, wl, dev):
         "combine": lambda: L.moe_combine(wl.N, wl.d, wl.k, r(dy), p(gate), p(slot), r(do), s_),
     }
     flush = Flusher()
-    warm = {n: time_stage(fn, args.stage_reps) for n, fn in stages.items()}
+    warm = {n: time_stage(fn, 5 * args.stage_reps) for n, fn in stages.items()}
     cold = {n: time_stage(fn, args.stage_reps, flush) for n, fn in stages.items()}
     del flush
     alg = algorithmic(wl, kept)

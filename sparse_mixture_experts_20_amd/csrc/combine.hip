@@ -9,11 +9,11 @@
 // expert rows of that token (stored contiguously, assignment-major; bf16 or
 // fp32), accumulates in fp32 in choice order and rounds once to the output
 // type. A pure streaming kernel: k*d*sizeof(Y) bytes read per token and
-// d*sizeof(out) bytes written. bf16 rows are read 8 columns (16 bytes) at a
-// time. The slots and gates of up to kGroup choices are loaded together,
-// then the rows of the kept ones together (two memory round trips per group
-// rather than two per choice); a dropped assignment's row is neither read
-// nor added.
+// d*sizeof(out) bytes written. Rows are read 8 columns at a time (16 bytes of
+// bf16, 32 of fp32). The slots and gates of a group of choices (8 for fp32
+// rows, 4 for bf16) are loaded together, then the rows of the kept ones
+// together (two memory round trips per group rather than two per choice); a
+// dropped assignment's row is neither read nor added.
 #include "common.hpp"
 
 namespace moe {
@@ -52,7 +52,10 @@ __device__ __forceinline__ void load_row(const unsigned short *y, float (&v)[VEC
     }
 }
 
-constexpr int kGroup = 4;   // choices whose loads are in flight together
+// choices whose loads are in flight together: 4 rows of 16 bytes for bf16
+// rows, 8 rows of 32 bytes for fp32 rows (the layer's expert outputs)
+template <typename YT>
+constexpr int group_of() { return sizeof(YT) == 4 ? 8 : 4; }
 
 template <typename YT, bool BF16, int VEC>
 __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ Y,
@@ -60,6 +63,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ Y,
                                                       const int32_t *__restrict__ slot,
                                                       int64_t N, int d, int k,
                                                       void *__restrict__ out) {
+    constexpr int kGroup = group_of<YT>();
     const int cols = d / VEC;
     const int64_t total = N * cols;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -146,6 +150,8 @@ hipError_t launch_combine(const void *Y, int y_dtype, const float *gate, const i
             return launch_out<unsigned short, 8>(Y, gate, slot, N, d, k, out, out_dtype, s);
         return launch_out<unsigned short, 1>(Y, gate, slot, N, d, k, out, out_dtype, s);
     }
+    if (d % 8 == 0)
+        return launch_out<float, 8>(Y, gate, slot, N, d, k, out, out_dtype, s);
     if (d % 4 == 0)
         return launch_out<float, 4>(Y, gate, slot, N, d, k, out, out_dtype, s);
     return launch_out<float, 1>(Y, gate, slot, N, d, k, out, out_dtype, s);

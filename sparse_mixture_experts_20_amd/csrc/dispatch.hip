@@ -19,7 +19,10 @@
 //     against the lanes holding the same id (found with one ballot per id
 //     bit), the per-wave counts become exclusive prefixes across the 16 waves,
 //     and the slot is the earlier chunks' count plus the rank in the chunk.
-// A call with a single chunk runs pass 3 alone (it finishes the plan itself).
+// A call with a single chunk runs pass 3 alone (it finishes the plan itself);
+// one with at most 32 chunks and no gate sums asked for runs a single pass
+// (dispatch_fused_kernel) in which every workgroup recounts the earlier
+// chunks.
 // Ranks are positional, never taken from atomics, so the plan is the same on
 // every run.
 #include "common.hpp"
@@ -326,6 +329,114 @@ __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
         p[i] = v;
 }
 
+// One-launch plan for at most kFusedChunks chunks when no gate sums are
+// asked for: every workgroup counts, per expert, the assignments of the
+// earlier chunks itself (reading the ids in their [N, k] layout, 4 per load,
+// and keeping those whose (choice, token) position lies before its chunk;
+// integer adds, so their order does not matter), then ranks its chunk as
+// dispatch_kernel does; the last workgroup, which also counts its own chunk,
+// finishes the plan. The slots, used counts and tile schedule are those of
+// the three-pass plan.
+constexpr int kFusedChunks = 32;
+
+__global__ __launch_bounds__(kThreads) void dispatch_fused_kernel(
+    const int32_t *__restrict__ idx, int N, int E, int k, int ceff, int32_t *__restrict__ slot,
+    int32_t *__restrict__ used, int32_t *__restrict__ slot_token, int32_t *__restrict__ tiles,
+    int32_t *__restrict__ demand, int32_t *__restrict__ drops) {
+    __shared__ int base[kMaxExperts];
+    __shared__ int wcnt[kWavesPerBlock * kMaxExperts];
+    __shared__ int cnt[kMaxExperts];
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const uint64_t lt = lanemask_lt();
+    const int total = N * k;
+    const int nbits = id_bits(E);
+    const int64_t p0 = (int64_t)blockIdx.x * kPhase;
+    const bool last = blockIdx.x == gridDim.x - 1;
+    int cur_a[kItems], cur_e[kItems];
+    load_chunk(idx, p0, total, N, k, E, cur_a, cur_e);
+    for (int e = tid; e < E; e += kThreads) {
+        base[e] = 0;
+        cnt[e] = 0;
+    }
+    for (int i = tid; i < kWavesPerBlock * E; i += kThreads)
+        wcnt[i] = 0;
+    __syncthreads();
+    // earlier chunks: assignments a = t*k + j with j*N + t < p0 (p0 > 0 only)
+    if (p0 > 0) {
+        const bool vec = ((uintptr_t)idx & 15) == 0;
+        for (int a0 = tid * 4; a0 < total; a0 += kThreads * 4) {
+            int ev[4];
+            if (vec && a0 + 4 <= total) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(idx + a0);
+                ev[0] = (int)v[0]; ev[1] = (int)v[1]; ev[2] = (int)v[2]; ev[3] = (int)v[3];
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    ev[q] = a0 + q < total ? idx[a0 + q] : -1;
+            }
+            int t = a0 / k, j = a0 - t * k;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int e = ev[q];
+                if (a0 + q < total && e >= 0 && e < E && (int64_t)j * N + t < p0)
+                    atomicAdd(&base[e], 1);
+                if (++j == k) {
+                    j = 0;
+                    ++t;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // rank of each assignment among the wave's earlier ones with its id
+    int my_r[kItems];
+#pragma unroll
+    for (int s = 0; s < kItems; ++s) {
+        const int e = cur_e[s];
+        if (cur_a[s] >= 0 && e < 0)
+            slot[cur_a[s]] = -1;
+        const uint64_t m = match_ids(e, e >= 0, nbits);
+        const int before = __popcll(m & lt);
+        my_r[s] = e >= 0 ? wcnt[w * E + e] + before : 0;
+        if (e >= 0 && before == 0)
+            wcnt[w * E + e] += __popcll(m);
+    }
+    __syncthreads();
+    for (int e0 = 0; e0 < E; e0 += kThreads / kWavesPerBlock) {
+        const int e = e0 + tid / kWavesPerBlock, ww = tid % kWavesPerBlock;
+        const int c = e < E ? wcnt[ww * E + e] : 0;
+        const int b0 = e < E ? base[e] : 0;
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < kWavesPerBlock; off <<= 1) {
+            const int o = __shfl_up(incl, off, kWavesPerBlock);
+            if (ww >= off)
+                incl += o;
+        }
+        if (e < E) {
+            wcnt[ww * E + e] = b0 + incl - c;
+            if (ww == kWavesPerBlock - 1)
+                cnt[e] = b0 + incl;   // assignments up to the end of this chunk
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kItems; ++s) {
+        const int e = cur_e[s];
+        if (e < 0)
+            continue;
+        const int r = wcnt[w * E + e] + my_r[s];
+        const int a = cur_a[s];
+        const bool kept = r < ceff;
+        slot[a] = kept ? r : -1;
+        if (kept)
+            slot_token[(int64_t)e * ceff + r] = a;
+    }
+    if (last)
+        finish_plan(cnt, nullptr, E, ceff, used, tiles, demand, drops, nullptr);
+}
+
 }  // namespace
 
 int64_t dispatch_chunks(int64_t N, int k) { return (N * k + kPhase - 1) / kPhase; }
@@ -345,6 +456,12 @@ hipError_t launch_dispatch(const int32_t *idx, const float *gate, int64_t N, int
     if (chunks == 0)
         return hipSuccess;
     const float *g = gate_sum ? gate : nullptr;
+    if (chunks <= kFusedChunks && !gate_sum) {
+        hipLaunchKernelGGL(dispatch_fused_kernel, dim3((unsigned)chunks), dim3(kThreads), 0, s,
+                           idx, (int)N, E, k, (int)ceff, slot, used, slot_token, tiles, demand,
+                           drops);
+        return hipGetLastError();
+    }
     int32_t *hist = nullptr;
     if (chunks > 1) {
         hist = static_cast<int32_t *>(ws);

@@ -29,7 +29,7 @@ namespace moe {
 namespace {
 
 constexpr int kTokTile = 16;   // tokens per block (one MFMA M-tile)
-constexpr int kWaves = 4;      // split-K over the waves of a block
+constexpr int kRankWaves = 4;  // waves that rank the block's tokens
 
 // Exact three-term split of two fp32 weights, w = hi + mid + lo, by
 // truncation: hi keeps the upper 16 bits of w (sign, exponent and the top 7
@@ -173,15 +173,19 @@ __global__ __launch_bounds__(256) void rank_scores_kernel(const float *__restric
     topk_softmax_group<G, Q>(v, E, k, t, active, idx_out, gate_out);
 }
 
-// One block = 16 tokens; wave w accumulates K-chunks c = w, w+4, ... with
-// 16x16x32 bf16 MFMAs over NT tiles of 16 experts, then the four partial
-// score tiles are summed in wave order through LDS.
-template <int NT>
-__global__ __launch_bounds__(256) void router_bf16_kernel(
+// One block = 16 tokens; wave w of NW accumulates K-chunks c = w, w+NW, ...
+// with 16x16x32 bf16 MFMAs over NT tiles of 16 experts, then the NW partial
+// score tiles are summed in wave order through LDS and the first four waves
+// rank the tokens. Wide rows (d >= 2048) take 16 waves, so that a CU keeps
+// four times the loads in flight.
+template <int NT, int NW>
+__global__ __launch_bounds__(NW * 64) void router_bf16_kernel(
     const unsigned short *__restrict__ x, const float *__restrict__ wg,
     const float *__restrict__ noise, int N, int d, int E, int k,
     int32_t *__restrict__ idx_out, float *__restrict__ gate_out) {
     constexpr int EP = NT * 16;
+    constexpr int kWaves = NW;
+    static_assert(NW >= kRankWaves, "four ranking waves");
     __shared__ float red[kWaves * kTokTile * EP];
 
     const int lane = threadIdx.x & 63;
@@ -201,20 +205,21 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     // Ranking layout: groups of G lanes rank one token each, 64/G tokens per
     // pass, TPW/TPP passes for the 4 tokens 4w .. 4w+3 this wave ranks. Their
     // noise rows are loaded up front, overlapping the score product.
-    constexpr int TPW = kTokTile / kWaves;
+    constexpr int TPW = kTokTile / kRankWaves;
     constexpr int G = EP <= 16 ? 16 : (EP <= 32 ? 32 : 64);
     constexpr int QG = (EP + G - 1) / G;   // scores per lane
     constexpr int TPP = 64 / G;             // tokens per pass
     constexpr int PASSES = TPW / TPP;
     const int lg = lane % G;
     float nz[PASSES][QG];
+    const bool ranker = w < kRankWaves;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
         const int64_t t = t0 + w * TPW + ps * TPP + lane / G;
 #pragma unroll
         for (int q = 0; q < QG; ++q) {
             const int e = lg + G * q;
-            nz[ps][q] = (noise && t < N && e < E) ? noise[t * E + e] : 0.f;
+            nz[ps][q] = (ranker && noise && t < N && e < E) ? noise[t * E + e] : 0.f;
         }
     }
     // K-chunks are processed in batches of U: all loads of a batch are issued
@@ -269,6 +274,8 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
         for (int i = 0; i < 4; ++i)
             red[(w * kTokTile + 4 * kg + i) * EP + nt * 16 + row] = acc[nt][i];
     __syncthreads();
+    if (!ranker)
+        return;
 
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
@@ -334,9 +341,14 @@ template <int NT>
 hipError_t launch_fused(const void *x, const float *wg, const float *noise, int64_t N,
                         int64_t d, int E, int k, int32_t *idx, float *gate, hipStream_t s) {
     const int blocks = (int)((N + kTokTile - 1) / kTokTile);
-    hipLaunchKernelGGL(router_bf16_kernel<NT>, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const unsigned short *>(x), wg, noise, (int)N, (int)d, E, k,
-                       idx, gate);
+    if (d >= 2048)
+        hipLaunchKernelGGL((router_bf16_kernel<NT, 16>), dim3(blocks), dim3(1024), 0, s,
+                           static_cast<const unsigned short *>(x), wg, noise, (int)N, (int)d, E,
+                           k, idx, gate);
+    else
+        hipLaunchKernelGGL((router_bf16_kernel<NT, 4>), dim3(blocks), dim3(256), 0, s,
+                           static_cast<const unsigned short *>(x), wg, noise, (int)N, (int)d, E,
+                           k, idx, gate);
     return hipGetLastError();
 }
 

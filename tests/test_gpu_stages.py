@@ -20,23 +20,42 @@ def torch_mod():
     return torch
 
 
+@pytest.mark.parametrize("stats", [False, True])
 @pytest.mark.parametrize("N,E,k,C,seed", [
     (5000, 37, 3, 300, 1), (4096, 8, 2, 640, 2), (20000, 16, 2, 1500, 3),
     (7, 4, 2, 1, 4), (65536 // 8, 256, 8, 200, 5), (1, 1, 1, 1, 6), (4097, 5, 5, 4097, 7),
+    (70001, 64, 2, 2000, 8),
 ])
-def test_dispatch_matches_oracle(torch_mod, N, E, k, C, seed):
+def test_dispatch_matches_oracle(torch_mod, N, E, k, C, seed, stats):
+    """The plan bit-exact against the oracle, both without router statistics
+    (one launch up to 32 chunks of 4096 assignments, three passes beyond) and
+    with them (three passes)."""
     torch = torch_mod
     from sparse_mixture_experts_20_amd import binding as B
-    G.say(f"[stage] dispatch N={N} E={E} k={k} C={C}")
+    G.say(f"[stage] dispatch N={N} E={E} k={k} C={C} stats={stats}")
     rng = np.random.default_rng(seed)
     # skewed expert popularity so that some experts overflow
     p = rng.dirichlet(np.full(E, 0.5))
-    idx = np.empty((N, k), np.int32)
-    for t in range(N):
-        idx[t] = rng.choice(E, size=k, replace=False, p=p if k < E else None)
-    slot, used, slot_token, tiles = B.dispatch(torch.from_numpy(idx).cuda(), E, C)
+    if k < E:
+        idx = np.argsort(rng.random((N, E)) ** (1.0 / p)[None, :], axis=1)[:, ::-1][:, :k]
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+    else:
+        idx = np.argsort(rng.random((N, E)), axis=1).astype(np.int32)
+    gate = rng.random((N, k)).astype(np.float32)
+    gate /= gate.sum(axis=1, keepdims=True)
+    if stats:
+        slot, used, slot_token, tiles, (dem, drp, gsum) = B.dispatch(
+            torch.from_numpy(idx).cuda(), E, C, gate=torch.from_numpy(gate).cuda(),
+            router_stats=True)
+    else:
+        slot, used, slot_token, tiles = B.dispatch(torch.from_numpy(idx).cuda(), E, C)
     torch.cuda.synchronize()
     ref_slot, ref_used = oracle.assign(idx, E, C)
+    if stats:
+        rd, rdr, rg = oracle.router_stats(idx, gate.astype(np.float64), E, C)
+        np.testing.assert_array_equal(G.to_np(dem), rd)
+        np.testing.assert_array_equal(G.to_np(drp), rdr)
+        assert np.all(np.abs(G.to_np(gsum) - rg) <= 1e-5 * np.abs(rg) + 1e-5)
     np.testing.assert_array_equal(G.to_np(slot), ref_slot)
     np.testing.assert_array_equal(G.to_np(used), ref_used)
     st = G.to_np(slot_token)

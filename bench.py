@@ -579,6 +579,23 @@ def _algorithmic_bytes(kernel, p):
     return None, ""
 
 
+# source file of each kernel family of the library (by name prefix)
+KERNEL_SOURCES = (("expert_gemm", "experts.hip"), ("split_fixup", "experts.hip"),
+                  ("experts_f32", "experts.hip"), ("router_", "router.hip"),
+                  ("rank_scores", "router.hip"), ("split_router", "router.hip"),
+                  ("dispatch", "dispatch.hip"), ("chunk_hist", "dispatch.hip"),
+                  ("chunk_scan", "dispatch.hip"), ("combine_backward", "backward.hip"),
+                  ("combine", "combine.hip"))
+
+
+def kernel_source(kern):
+    """The csrc file that defines a library kernel (by its name)."""
+    for prefix, src in KERNEL_SOURCES:
+        if kern.startswith(prefix):
+            return src
+    return kern.split("_")[0] + ".hip"
+
+
 def traffic_summary(workload, fetch_dir, write_dir, probe_json, out_json=TRAFFIC_FILE):
     """Counter readings (KiB per dispatch) to bytes per launch: writes
     profiles/traffic.json entries keyed "<kernel>/<workload>" (with the hash of
@@ -611,9 +628,7 @@ def traffic_summary(workload, fetch_dir, write_dir, probe_json, out_json=TRAFFIC
         algs = f"{alg / 1e6:.2f}" if alg else "-"
         print(f"| `{kern}` | {fb / 1e6:.2f} | {wb / 1e6:.2f} | {(fb + wb) / 1e6:.2f} | {algs} "
               f"| {ratio} |")
-        src = "experts.hip" if "gemm" in kern or "fixup" in kern else (
-            kern.split("_")[0] + ".hip")
-        path = os.path.join(CSRC, src)
+        path = os.path.join(CSRC, kernel_source(kern))
         out[f"{kern}/{workload}"] = {
             "bytes_per_launch": int(round(fb + wb)), "fetch_bytes": int(round(fb)),
             "write_bytes": int(round(wb)), "algorithmic_bytes": alg, "algorithmic": what,

@@ -302,6 +302,32 @@ def test_backward_rejects_bad_arguments(L):
     assert st.capacity == -1
 
 
+def test_stats_struct_matches_the_header_and_aux_stream_is_read_last(L):
+    """The binding's moe_stats has the header's fields in the header's order
+    (aux_stream last, at the C layout's offset: eight 8-byte pointers or
+    sizes, then the int64 capacity, three pointers and aux_stream), and a
+    backward whose arguments fail validation returns before it uses
+    aux_stream: a handle that is not a stream is never touched."""
+    with open(HEADER) as f:
+        hdr = f.read()
+    body = hdr[hdr.index("typedef struct {\n    void *stream;"):hdr.index("} moe_stats;")]
+    names = re.findall(r"\*?(\w+);", body)
+    assert [f[0] for f in B.MoeStats._fields_] == names
+    assert names[-1] == "aux_stream"
+    assert B.MoeStats.aux_stream.offset == 88 and ctypes.sizeof(B.MoeStats) == 96
+    N, d, E, dff = 64, 16, 4, 32
+    x, wg, wu, wd, out, st = _good(N=N, d=d, E=E, dff=dff)
+    dout = _t(FAKE, BF16, N, d)
+    g = (_t(FAKE, F32, N, d), _t(FAKE, F32, E, d), _t(FAKE, F32, E, dff, d),
+         _t(FAKE, F32, E, d, dff))
+    st.aux_stream = ctypes.c_void_p(FAKE)
+    r = ctypes.byref
+    assert L.moe_backward(r(x), r(wg), None, r(wu), r(wd), 5, 1.0, r(dout), r(g[0]), r(g[1]),
+                          r(g[2]), r(g[3]), r(st)) == -4                       # k > E
+    assert L.moe_backward(r(x), r(wg), None, r(wu), r(wd), 2, 1.0, r(dout), r(g[0]), r(g[1]),
+                          r(g[2]), r(g[3]), r(st)) == -5                       # workspace
+
+
 def test_backward_ex_validates_the_expert_variant(L):
     """moe_backward_ex: options as for the forward, and a bias gradient
     exactly when the layer has that bias."""

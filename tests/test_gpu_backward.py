@@ -236,6 +236,39 @@ def test_nanomoe_backward_sampled_rows(torch_mod, name):
     del dev
 
 
+@pytest.mark.parametrize("name", ["nanomoe", "nanomoe_gelu"])
+def test_aux_stream_changes_nothing(torch_mod, name):
+    """moe_stats.aux_stream: the backward with no second stream (NULL), with
+    the caller's own stream given again (aux == stream: one stream), and with
+    a second stream of the caller's gives bitwise-identical gradients; once
+    the caller's stream is synchronised the second stream has nothing left
+    (the call joins it back)."""
+    torch = torch_mod
+    from sparse_mixture_experts_20_amd import binding as B
+    wl = W.make(name)
+    G.say(f"[backward] {name}: aux_stream NULL / same / second")
+    dev = _upload(wl)
+
+    def run(aux):
+        return B.backward(dev["x"], dev["W_g"], dev["noise"], dev["W_up"], dev["W_down"], wl.k,
+                          wl.cfg.cf, dev["dout"], act=dev["act"], b_up=dev["b_up"],
+                          b_down=dev["b_down"], aux_stream=aux)
+
+    second = torch.cuda.Stream()
+    ref = run(None)
+    same = run(torch.cuda.current_stream())
+    two = run(second)
+    torch.cuda.current_stream().synchronize()
+    assert second.query()
+    torch.cuda.synchronize()
+    for a, b, c in zip(ref, same, two):
+        if a is None:
+            assert b is None and c is None
+            continue
+        assert torch.equal(a, b) and torch.equal(a, c)
+    del dev
+
+
 @pytest.mark.parametrize("name,nunits", [("nanomoe", 6), ("mixtral", 4), ("nanomoe_gelu", 6),
                                          ("skew", 4), ("finegrained", 4)])
 def test_benchmark_layer_weight_gradients_sampled(torch_mod, name, nunits):

@@ -187,14 +187,23 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+_AUX_STREAMS = {}   # device index -> the binding's second stream for "auto"
+
+
 def _aux_stream(aux, device):
-    """The backward's second stream: ``"auto"`` makes one on the tensors'
-    device (default priority), None runs the call on one stream, or a
-    ``torch.cuda.Stream``. Returns (stream object or None, handle)."""
+    """The backward's second stream: ``"auto"`` takes the binding's own stream
+    of the tensors' device (created once at the default priority and reused:
+    creating a stream per call would cost more than the overlap gains), None
+    runs the call on one stream, or pass a ``torch.cuda.Stream``. Returns
+    (stream object or None, handle)."""
     if isinstance(aux, str):
         if aux != "auto":
             raise ValueError("aux_stream must be 'auto', None or a torch.cuda.Stream")
-        aux = torch.cuda.Stream(device=device)
+        dev = torch.device(device)
+        index = dev.index if dev.index is not None else torch.cuda.current_device()
+        aux = _AUX_STREAMS.get(index)
+        if aux is None:
+            aux = _AUX_STREAMS[index] = torch.cuda.Stream(device=index)
     return aux, (None if aux is None else ctypes.c_void_p(aux.cuda_stream))
 
 

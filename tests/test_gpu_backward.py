@@ -258,14 +258,18 @@ def test_aux_stream_changes_nothing(torch_mod, name):
     ref = run(None)
     same = run(torch.cuda.current_stream())
     two = run(second)
+    auto1 = run("auto")
+    auto2 = run("auto")   # the binding's own second stream, made once per device
+    assert len(B._AUX_STREAMS) == 1
     torch.cuda.current_stream().synchronize()
     assert second.query()
     torch.cuda.synchronize()
-    for a, b, c in zip(ref, same, two):
+    for a, b, c, d1, d2 in zip(ref, same, two, auto1, auto2):
         if a is None:
-            assert b is None and c is None
+            assert b is None and c is None and d1 is None and d2 is None
             continue
-        assert torch.equal(a, b) and torch.equal(a, c)
+        assert torch.equal(a, b) and torch.equal(a, c) and torch.equal(a, d1)
+        assert torch.equal(a, d2)
     del dev
 
 

@@ -127,6 +127,12 @@ def cpu_baseline(wl, target_s=15.0):
     S = int(min(wl.N, max(16, target_s / max(per_tok, 1e-9))))
     rows = np.sort(rng.choice(wl.N, size=S, replace=False))
     t_ffn = ffn(rows)
+    if t_ffn < 0.5 * target_s and S < wl.N:
+        # a probe of 16 tokens over many experts overstates the cost per
+        # token (an expert's call has a fixed part): size the sample again
+        S = int(min(wl.N, S * target_s / max(t_ffn, 1e-9)))
+        rows = np.sort(rng.choice(wl.N, size=S, replace=False))
+        t_ffn = ffn(rows)
     est_full = t_route + t_ffn * wl.N / S
     return {
         "value": wl.N / est_full,

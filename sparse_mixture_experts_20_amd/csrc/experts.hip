@@ -242,6 +242,36 @@ __device__ __forceinline__ bool light_last(const int32_t *__restrict__ used, con
     return s_pp[E] > 0 && (s_mt[E] - s_pp[E]) * NT <= P;
 }
 
+// s_mt[e] = sum over e' < e of ceil(used[e'] / BM), for e <= E: the row
+// tiles of a tile height the dispatch plan has no table for. Needs
+// nthr >= kMaxExperts; s_tmp holds one int per wave; ends with a barrier.
+__device__ __forceinline__ void row_tile_prefix(const int32_t *__restrict__ used, int E, int BM,
+                                                int *s_mt, int *s_tmp) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int c = 0;
+    if (tid < E)
+        c = (used[tid] + BM - 1) / BM;
+    int inc = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(inc, off);
+        if (lane >= off)
+            inc += o;
+    }
+    if (w < kMaxExperts / 64 && lane == 63)
+        s_tmp[w] = inc;
+    __syncthreads();
+    if (tid < kMaxExperts) {
+        for (int ww = 0; ww < w; ++ww)
+            inc += s_tmp[ww];
+        if (tid < E)
+            s_mt[tid + 1] = inc;
+        if (tid == 0)
+            s_mt[0] = 0;
+    }
+    __syncthreads();
+}
+
 // Expert e owning tile L of the schedule above, and its tile origin
 // (s_pp = NULL: the plain order).
 __device__ __forceinline__ void decode_tile(int L, const int *s_mt, const int *s_pp, int E,
@@ -344,11 +374,23 @@ void expert_gemm_kernel(
     constexpr int CPR = BKT / 8;                             // 16-byte chunks per row
     constexpr int RPB = 256 / RB;                            // rows per 256-byte bank row
     constexpr int RPI = 1024 / RB;                           // rows per direct-load wave op
-    constexpr int IA = BM / (RPI * NW), IB = BN / (RPI * NW);  // ops per wave per stage
-    constexpr int G = IA + IB;
+    constexpr bool AT = MODE == 6;                           // A read K-major
+    constexpr bool BT = MODE == 3 || MODE == 4 || MODE == 6; // B read K-major
+    constexpr bool RM = !AT && !BT;                          // both row-major
+    // Row-major operands: the A and B rows of a stage form one space of TOT
+    // direct-load ops (RPI rows each), op q filling LDS bytes [q KB, q KB +
+    // 1 KB) of the stage: A rows first, then B rows, the stage's layout.
+    // Wave w issues ops w*GC .. w*GC + GC - 1 that exist.
+    constexpr int TOT = (BM + BN) / RPI;
+    constexpr int GC = (TOT + NW - 1) / NW;
+    // K-major operands: IA and IB ops per wave per stage
+    constexpr int IA = RM ? 0 : BM / (RPI * NW), IB = RM ? 0 : BN / (RPI * NW);
+    constexpr int G = RM ? GC : IA + IB;                     // ops per wave per stage (at most)
     constexpr int STAGE = (BM + BN) * RB;                    // bytes per stage
     static_assert(BKT % 32 == 0 && S >= 2, "K-step is a multiple of one MFMA K");
-    static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile/waves mismatch");
+    static_assert(RM ? (BM % RPI == 0 && BN % RPI == 0 && (S == 2 || TOT % NW == 0))
+                     : (BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0),
+                  "tile/waves mismatch");
     static_assert(WTM % 16 == 0 && WTN % 32 == 0, "16x16 MFMA tiles; 4 lanes x 8k columns per row");
     static_assert(WMN * 16 * (WTN + 4) * 4 <= S * STAGE, "epilogue scratch");
     static_assert(WAVES_K == 1 || (MODE != 3 && MODE != 4 && MODE != 6), "K sets: row-major B");
@@ -360,6 +402,7 @@ void expert_gemm_kernel(
     __shared__ int s_mt[kMaxExperts + 1];
     __shared__ int s_pp[kMaxExperts + 1];
     __shared__ uint64_t s_msk[kMaxExperts / 64];
+    __shared__ int s_tok[MODE == 0 ? BM : 1];   // MODE 0: token of each tile row
     int *s_rows = reinterpret_cast<int *>(smem + S * STAGE);   // MODE 6: row of each r
 
     const int tid = threadIdx.x;
@@ -410,9 +453,13 @@ void expert_gemm_kernel(
         m0 = (L % mte) * BM;
         n0 = (L / mte) * BN;
     } else {
-        for (int i = tid; i <= E; i += NTHR)
-            s_mt[i] = mt_off[i];
-        __syncthreads();
+        if (mt_off) {
+            for (int i = tid; i <= E; i += NTHR)
+                s_mt[i] = mt_off[i];
+            __syncthreads();
+        } else {
+            row_tile_prefix(used, E, BM, s_mt, reinterpret_cast<int *>(s_msk));
+        }
         const int T = s_mt[E] * NT;
         const SplitPlan sp = split_plan(T, KT, part ? P : 0);
         const bool ll = light_last(used, s_mt, E, NT, BM, P, NTHR, s_pp, s_msk);
@@ -456,12 +503,38 @@ void expert_gemm_kernel(
     // Direct-load sources of this lane: one row and one 16-byte chunk per op.
     // Rows past the tile edge read row 0 of the expert (their outputs are
     // never stored); the K tail is zeroed in LDS after the last step lands.
-    const unsigned short *ga[IA];
-    const unsigned short *gb[IB];
-    int ca[IA], cb[IB];
+    const unsigned short *gc[RM ? GC : 1];
+    int cc[RM ? GC : 1];
+    const unsigned short *We = W + (int64_t)__builtin_amdgcn_readfirstlane(e) * Nout * K;
+    if constexpr (RM) {
+        if constexpr (MODE == 0) {
+            // the tile's token rows, one load per thread rather than a chain
+            // of dependent loads per op
+            for (int i = tid; i < BM; i += NTHR) {
+                const int r = m0 + i;
+                s_tok[i] = slot_token[(int64_t)e * ceff + (r < rows ? r : 0)] / k;
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int i = 0; i < GC; ++i) {
+            const int q = min(wv * GC + i, TOT - 1);   // ops past TOT are not issued
+            const bool isA = q * RPI < BM;              // the same for the whole op
+            const int row = (isA ? q * RPI : q * RPI - BM) + lane / CPR;
+            const int c = (lane % CPR) ^ ((row / RPB) % CPR);
+            const int r = m0 + row, n = n0 + row;
+            const int64_t srow = (int64_t)e * ceff + (r < rows ? r : 0);
+            const int64_t asrc = MODE == 0 ? (int64_t)s_tok[min(row, BM - 1)] : srow;
+            const int64_t src = isA ? asrc : (int64_t)(n < Nout ? n : 0);
+            cc[i] = c;
+            gc[i] = (isA ? A_src : We) + src * K;
+        }
+    }
+    const unsigned short *ga[IA > 0 ? IA : 1];
+    const unsigned short *gb[IB > 0 ? IB : 1];
+    int ca[IA > 0 ? IA : 1], cb[IB > 0 ? IB : 1];
     // K-major left operand (MODE 6): like the right one below, with M
     // columns of width bsa
-    constexpr bool AT = MODE == 6;
     constexpr int RBTA = BM * 2, CPRTA = BM / 8;
     static_assert(!AT || (BM & (BM - 1)) == 0, "K-major tiles are a power of two wide");
     int ak[AT ? IA : 1];
@@ -491,7 +564,6 @@ void expert_gemm_kernel(
     // K-major right operand: per op, the LDS row (k within the K-step) and a
     // pointer to its 8 columns in row 0 of W[e]; columns past Nout read the
     // last 8 (never stored), rows past K read row K - 1 (A's K tail is 0)
-    constexpr bool BT = MODE == 3 || MODE == 4 || MODE == 6;
     constexpr int RBT = BN * 2, CPRT = BN / 8;   // bytes, 16-byte chunks per K-major row
     static_assert(!BT || (BN & (BN - 1)) == 0, "K-major tiles are a power of two wide");
     int bk[BT ? IB : 1];
@@ -515,6 +587,15 @@ void expert_gemm_kernel(
     const unsigned smem_off = lds_off(smem);
     auto issue = [&](int kt) {
         const unsigned base = smem_off + (unsigned)((kt % S) * STAGE);
+        if constexpr (RM) {
+#pragma unroll
+            for (int i = 0; i < GC; ++i) {
+                if (TOT % NW == 0 || wv * GC + i < TOT) {
+                    const int kk = min(kt * BKT + cc[i] * 8, K - 8);
+                    dma16(base + (unsigned)((wv * GC + i) * 1024), gc[i] + kk);
+                }
+            }
+        }
 #pragma unroll
         for (int i = 0; i < IA; ++i) {
             if constexpr (AT) {
@@ -627,7 +708,8 @@ void expert_gemm_kernel(
     // with both operands transposed, a second set would not fit in registers;
     // so does a tile of 16 waves, four per SIMD, whose 128 registers per lane
     // hold one set)
-    constexpr bool kPrefetchFrags = !(MODE == 6 && BM * BN >= 256 * 256) && NW < 16;
+    constexpr bool kPrefetchFrags =
+        !(MODE == 6 && BM * BN >= 256 * 256) && NW < 16 && FM * FN < 40;
     auto compute = [&](int st, auto full) {
         if constexpr (kPrefetchFrags) {
             bf16x8 af[2][FM], bfr[2][FN];
@@ -887,9 +969,13 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
     __shared__ int s_mt[kMaxExperts + 1];
     __shared__ int s_pp[kMaxExperts + 1];
     __shared__ uint64_t s_msk[kMaxExperts / 64];
-    for (int i = threadIdx.x; i <= E; i += 256)
-        s_mt[i] = mt_off[i];
-    __syncthreads();
+    if (mt_off) {
+        for (int i = threadIdx.x; i <= E; i += 256)
+            s_mt[i] = mt_off[i];
+        __syncthreads();
+    } else {
+        row_tile_prefix(used, E, BM, s_mt, reinterpret_cast<int *>(s_msk));
+    }
     const int NT = (Nout + BN - 1) / BN;
     const int KT = (K + BKT - 1) / BKT;
     const SplitPlan sp = split_plan(s_mt[E] * NT, KT, P);
@@ -1037,12 +1123,14 @@ namespace {
 //  - 128x128, 4 waves of 64x64, two workgroups per CU: otherwise.
 // Products whose right operand is read K-major (modes 3, 4) take 128x64
 // where the K-set tile would be picked.
-enum class Tile { k128, k128x64, k256, k128k2 };
+enum class Tile { k128, k128x64, k256, k128k2, k320 };
 
 constexpr int kBK = 64;    // K-step of the one-set tile shapes
 constexpr int kBK2 = 128;  // K-step of the K-set tile: two 32-wide MFMA steps per set
 
 Tile pick_tile(int64_t rows_per_expert, int64_t Nout, int E) {
+    if (rows_per_expert >= 232 && rows_per_expert <= 288)
+        return Tile::k320;
     const int64_t t256 = (int64_t)E * ((rows_per_expert + 255) / 256) * ((Nout + 255) / 256);
     if (rows_per_expert >= 256 && (t256 >= 256 || Nout >= 2048))
         return Tile::k256;
@@ -1069,7 +1157,7 @@ int resident_blocks(Kern kernel, int threads) {
 
 // One bf16 grouped product on tile shape BM x BN, plus the fix-up of the
 // split last round when the scratch `part` can hold it.
-template <int BM, int BN, int WM, int WN, int WK, int BKT, int MODE>
+template <int BM, int BN, int WM, int WN, int WK, int BKT, int MODE, int S = 2>
 hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_t K, int64_t Nout,
                         int E, int k, int64_t ceff, const int32_t *used,
                         const int32_t *slot_token, const int32_t *mt, unsigned short *O16,
@@ -1077,7 +1165,7 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
                         hipStream_t s, const unsigned short *mask = nullptr,
                         float *O32 = nullptr, unsigned short *Z16 = nullptr,
                         Dropout dp = Dropout{}) {
-    auto kern = expert_gemm_kernel<BM, BN, WM, WN, WK, BKT, 2, MODE>;
+    auto kern = expert_gemm_kernel<BM, BN, WM, WN, WK, BKT, S, MODE>;
     constexpr int NTHR = WM * WN * WK * 64;
     int P = resident_blocks(kern, NTHR);
     if (P < 0) {
@@ -1112,9 +1200,9 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
 
 // Template arguments of the kernel a product of this mode runs on tile shape
 // t: BM, BN, waves along rows, columns and K, K-step.
-template <int BM_, int BN_, int WM_, int WN_, int WK_, int BKT_>
+template <int BM_, int BN_, int WM_, int WN_, int WK_, int BKT_, int S_ = 2>
 struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, WK = WK_, BKT = BKT_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, WK = WK_, BKT = BKT_, S = S_;
 };
 
 // Calls f(TileCfg<...>{}, tiles) with the instantiation mode MODE runs for
@@ -1123,6 +1211,13 @@ struct TileCfg {
 // the launch and by the kernel-name query.
 template <int MODE, typename F>
 auto with_tile(Tile t, const int32_t *tiles, int E, F f) {
+    if (t == Tile::k320) {
+        // forward products: 8 waves of 160x64 (two per SIMD); the schedule
+        // table of 320-row tiles is computed by the kernel itself
+        if constexpr (MODE == 0 || MODE == 1 || MODE == 5)
+            return f(TileCfg<320, 256, 2, 4, 1, kBK>{}, (const int32_t *)nullptr);
+        t = Tile::k256;
+    }
     if (t == Tile::k128k2) {
         if constexpr (MODE == 0 || MODE == 1 || MODE == 5)
             return f(TileCfg<128, 128, 2, 4, 2, kBK2>{}, tiles);
@@ -1153,7 +1248,7 @@ hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W,
     float *pf = static_cast<float *>(part);
     return with_tile<MODE>(t, tiles, E, [&](auto c, const int32_t *tt) {
         using C = decltype(c);
-        return launch_tiles<C::BM, C::BN, C::WM, C::WN, C::WK, C::BKT, MODE>(
+        return launch_tiles<C::BM, C::BN, C::WM, C::WN, C::WK, C::BKT, MODE, C::S>(
             A, W, K, Nout, E, k, ceff, used, slot_token, tt, O16, pf, part_bytes, act, bias, s,
             mask, O32, Z16, dp);
     });

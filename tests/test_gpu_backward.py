@@ -83,6 +83,8 @@ CASES = {
     "bwd_multi_tile": (1000, 264, 16, 4, 392, 0.8, 0.5, 0.0, 302),
     "bwd_row_tiles": (1024, 256, 4, 2, 512, 1.0, 0.5, 0.0, 303),
     "bwd_kset": (1024, 392, 64, 4, 520, 1.0, 0.5, 0.0, 315),
+    # forward state recomputed on the 320-row tile, one expert at capacity
+    "bwd_tile320": (2048, 264, 64, 8, 392, 1.5, 0.3, 0.5, 317),
     "bwd_heavy_drop": (512, 64, 4, 2, 128, 0.1, 0.0, 5.0, 304),
     "bwd_many_experts": (300, 128, 256, 8, 96, 2.0, 0.0, 0.0, 305),
     "bwd_max_top_k": (200, 64, 64, 16, 72, 0.7, 0.2, 0.0, 310),

@@ -47,6 +47,8 @@ CASES = {
                             5),
     "drop_f32": (77, 13, 6, 3, 21, "f32", 0.7, 403, "relu", 0.3, 0.5, 9, 2**33),
     "drop_multi_tile_bf16": (1000, 264, 16, 4, 392, "bf16", 0.8, 404, "relu", 0.0, 0.05, 1, 1),
+    # the 320-row tile's dropout epilogue (256 expected rows per expert)
+    "drop_tile320_bf16": (2048, 264, 64, 8, 392, "bf16", 1.5, 406, "relu", 0.0, 0.1, 5, 7),
 }
 
 

@@ -54,6 +54,10 @@ SMALL = {
     # 128x128 tile (two workgroups per CU) in both products, ragged K and N
     # (weights scaled down, see W_STD)
     "plain128_bf16": (1024, 1544, 32, 2, 1544, "bf16", 1.0, 0.5, 0.0, 115),
+    # 256 expected rows per expert: the 320-row tile in both products (the
+    # kernel's own schedule prefix), K tails (264, 392), a partial column
+    # tile (392) and one expert at capacity (384 rows: a second row tile)
+    "tile320_bf16": (2048, 264, 64, 8, 392, "bf16", 1.5, 0.3, 0.5, 116),
     "k1_bf16": (200, 64, 3, 1, 64, "bf16", 1.0, 0.0, 0.0, 105),
     "k_equals_E_bf16": (100, 32, 4, 4, 48, "bf16", 1.0, 0.0, 0.0, 106),
     "max_top_k_bf16": (200, 64, 64, 16, 72, "bf16", 0.7, 0.2, 0.0, 112),
@@ -73,6 +77,7 @@ VARIANT = {
     "gelu_bias_bf16": (700, 200, 6, 2, 328, "bf16", 0.9, 0.4, 202, "gelu", 0.05),
     "relu_bias_bf16": (1000, 264, 16, 4, 392, "bf16", 0.8, 0.5, 203, "relu", 0.05),
     "gelu_nobias_bf16": (333, 136, 5, 2, 200, "bf16", 1.0, 0.3, 204, "gelu", 0.0),
+    "gelu_bias_tile320_bf16": (2048, 264, 64, 8, 392, "bf16", 1.5, 0.3, 205, "gelu", 0.05),
 }
 
 

@@ -50,6 +50,7 @@ CASES = {
     "train_gelu_bias": (700, 200, 6, 2, 328, 0.9, 502, "gelu", 0.05, 0.0),
     "train_gelu_bias_dropout": (512, 64, 4, 2, 128, 0.3, 503, "gelu", 0.1, 0.2),
     "train_one_token": (1, 64, 8, 2, 64, 1.0, 504, "relu", 0.0, 0.0),
+    "train_tile320_gelu_bias": (2048, 264, 64, 8, 392, 1.5, 505, "gelu", 0.05, 0.1),
 }
 
 

@@ -223,9 +223,17 @@ hipError_t launch_dx(const float *dXa, const float *ds, const int32_t *idx, cons
                      const float *Wg, int64_t N, int64_t d, int E, int k, float *dx,
                      hipStream_t s);
 
-// Y[rows, Nout] (fp32) = A[rows, K] * W[Nout, K]^T, bf16 operands.
-hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, int64_t K,
-                                  int64_t Nout, float *Y, hipStream_t s);
+// Router scores for more than 32 experts: x [N, d] bf16 against the split
+// weights wsp [Ep][3 d] bf16 (hi, mid and lo terms of each expert's row),
+// all three terms accumulated into one fp32 score; the K dimension is cut
+// into router_score_splits() ranges whose partial scores go to
+// P [splits][N][Ep] fp32 (summed in range order by the ranking).
+int router_score_splits(int64_t N, int64_t d, int64_t Ep);
+// Whether the split weights interleave the three terms per 64 columns
+// (row layout [d / 64][3][64]) rather than placing them one after the other.
+bool router_terms_interleaved(int64_t d);
+hipError_t launch_router_scores_bf16(const void *x, const void *wsp, int64_t N, int64_t d,
+                                     int64_t Ep, float *P, hipStream_t s);
 
 // Y: [N*k, d] rows of dtype y_dtype (0 fp32, 1 bf16); out of dtype out_dtype.
 hipError_t launch_combine(const void *Y, int y_dtype, const float *gate, const int32_t *slot,

@@ -40,6 +40,7 @@
 // light last row tiles of the experts go last (partial_prefix below).
 #include <stdio.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -349,6 +350,14 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // row of r is slot_token[e*ceff + r] / k for the gathered operand (act == 0:
 // A, act == 1: B) and e*ceff + r for the other; bsc = M*Nout. K is unused
 // (each expert's K is used[e]; kGradMaxRows bounds ceff).
+// 7: router scores, a plain product of ceff rows of A (x, rows of bsa = d)
+// with W = the three-term split of the router weights, [Nout][K] with
+// K = 3 d (row e: the hi, mid and lo terms of expert e's weights, either
+// interleaved per 64 columns, bsb = 1, each 64 columns of x read three
+// times in a row, or one term after the other, bsb = 0), A's column taken
+// from the term's, so that all three terms of an expert accumulate into
+// one fp32 score; K is cut into gridDim.y ranges of K-steps,
+// range s writing its fp32 partial scores to O32 + s * bsc.
 // WAVES_K > 1 (modes 0, 1, 2, 5): WAVES_K sets of WAVES_M x WAVES_N waves
 // share each K-step, set w taking its 32-wide MFMA steps w, w + WAVES_K, ...;
 // after the last step the sets add their partial tiles into set 0 through
@@ -395,7 +404,8 @@ void expert_gemm_kernel(
     static_assert(WMN * 16 * (WTN + 4) * 4 <= S * STAGE, "epilogue scratch");
     static_assert(WAVES_K == 1 || (MODE != 3 && MODE != 4 && MODE != 6), "K sets: row-major B");
     static_assert((WAVES_K & (WAVES_K - 1)) == 0, "K sets: a power of two");
-    static_assert(MODE == 2 || MODE == 6 || NTHR >= kMaxExperts, "schedule prefix: a lane per expert");
+    static_assert(MODE == 2 || MODE == 6 || MODE == 7 || NTHR >= kMaxExperts,
+                  "schedule prefix: a lane per expert");
     static_assert(WAVES_K / 2 * WMN * FM * FN * 64 * 16 <= S * STAGE, "K-set reduction");
     __shared__ __attribute__((aligned(1024)))
     char smem[S * STAGE + (MODE == 6 ? kGradMaxRows * 4 : 0)];
@@ -435,10 +445,16 @@ void expert_gemm_kernel(
         for (int i = tid; i < Kr; i += NTHR)
             s_rows[i] = stp[i] / k;
         __syncthreads();
-    } else if constexpr (MODE == 2) {
-        // plain product over ceff rows, one "expert" per blockIdx.y: no schedule table
-        A_src += blockIdx.y * bsa;
-        W += blockIdx.y * bsb;
+    } else if constexpr (MODE == 2 || MODE == 7) {
+        // plain product over ceff rows, one "expert" (MODE 2) or K-range
+        // (MODE 7) per blockIdx.y: no schedule table
+        if constexpr (MODE == 2) {
+            A_src += blockIdx.y * bsa;
+            W += blockIdx.y * bsb;
+        } else {
+            kb = (int)((int64_t)blockIdx.y * KT / gridDim.y);
+            ke = (int)((int64_t)(blockIdx.y + 1) * KT / gridDim.y);
+        }
         O32 += blockIdx.y * bsc;
         const int mte = (ceff + BM - 1) / BM;
         const int T = mte * NT;
@@ -527,7 +543,7 @@ void expert_gemm_kernel(
             const int64_t asrc = MODE == 0 ? (int64_t)s_tok[min(row, BM - 1)] : srow;
             const int64_t src = isA ? asrc : (int64_t)(n < Nout ? n : 0);
             cc[i] = c;
-            gc[i] = (isA ? A_src : We) + src * K;
+            gc[i] = (isA ? A_src : We) + src * (MODE == 7 && isA ? (int)bsa : K);
         }
     }
     const unsigned short *ga[IA > 0 ? IA : 1];
@@ -591,7 +607,15 @@ void expert_gemm_kernel(
 #pragma unroll
             for (int i = 0; i < GC; ++i) {
                 if (TOT % NW == 0 || wv * GC + i < TOT) {
-                    const int kk = min(kt * BKT + cc[i] * 8, K - 8);
+                    int kk = min(kt * BKT + cc[i] * 8, K - 8);
+                    if (MODE == 7 && (wv * GC + i) * RPI < BM) {
+                        // A's column of the term this chunk belongs to:
+                        // terms interleaved per 64 columns (bsb = 1), or
+                        // one after the other
+                        const int d = (int)bsa;
+                        kk = bsb ? (kk / 192) * 64 + kk % 64
+                                 : kk >= 2 * d ? kk - 2 * d : kk >= d ? kk - d : kk;
+                    }
                     dma16(base + (unsigned)((wv * GC + i) * 1024), gc[i] + kk);
                 }
             }
@@ -1258,19 +1282,34 @@ hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W,
 
 size_t split_workspace_bytes() { return kSplitWorkspaceBytes; }
 
-hipError_t launch_plain_gemm_bf16(const void *A, const void *W, int64_t rows, int64_t K,
-                                  int64_t Nout, float *Y, hipStream_t s) {
-    if (rows == 0)
+bool router_terms_interleaved(int64_t d) { return d % 64 == 0; }
+
+int router_score_splits(int64_t N, int64_t d, int64_t Ep) {
+    // about one round of 256x256 tiles (one workgroup per CU), ranges of at
+    // least 8 K-steps
+    const int64_t tiles = ((N + 255) / 256) * ((Ep + 255) / 256);
+    const int64_t KT = (3 * d + kBK - 1) / kBK;
+    int64_t ns = std::max<int64_t>(256 / std::max<int64_t>(tiles, 1), 1);
+    ns = std::min<int64_t>(ns, std::max<int64_t>(KT / 8, 1));
+    return (int)ns;
+}
+
+hipError_t launch_router_scores_bf16(const void *x, const void *wsp, int64_t N, int64_t d,
+                                     int64_t Ep, float *P, hipStream_t s) {
+    if (N == 0)
         return hipSuccess;
-    const int64_t grid = (((rows + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((expert_gemm_kernel<128, 128, 2, 2, 1, kBK, 2, 2>), dim3((unsigned)grid),
-                       dim3(256), 0, s, static_cast<const unsigned short *>(A),
-                       static_cast<const unsigned short *>(W), (int)K, (int)Nout, 1, 1, (int)rows,
-                       (const int32_t *)nullptr, (const int32_t *)nullptr,
-                       (const int32_t *)nullptr, (unsigned short *)nullptr, Y, (float *)nullptr,
+    const int ns = router_score_splits(N, d, Ep);
+    const int64_t tiles = ((N + 255) / 256) * ((Ep + 255) / 256);
+    const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((expert_gemm_kernel<256, 256, 4, 4, 1, kBK, 2, 7>),
+                       dim3((unsigned)grid, (unsigned)ns), dim3(1024), 0, s,
+                       static_cast<const unsigned short *>(x),
+                       static_cast<const unsigned short *>(wsp), (int)(3 * d), (int)Ep, 1, 1,
+                       (int)N, (const int32_t *)nullptr, (const int32_t *)nullptr,
+                       (const int32_t *)nullptr, (unsigned short *)nullptr, P, (float *)nullptr,
                        0, kActRelu, (const float *)nullptr, (const unsigned short *)nullptr,
-                       (unsigned short *)nullptr, Dropout{}, (int64_t)0, (int64_t)0,
-                       (int64_t)0);
+                       (unsigned short *)nullptr, Dropout{}, d,
+                       (int64_t)router_terms_interleaved(d), N * Ep);
     return hipGetLastError();
 }
 

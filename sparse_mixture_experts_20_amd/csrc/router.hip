@@ -15,11 +15,16 @@
 // dot product of the exact inputs, at a fraction of the cost of fp32 MFMA.
 // Up to 32 experts one fused kernel splits the weights in registers,
 // computes the scores of 16 tokens and ranks them. With more experts the
-// split is done once per call into the workspace (rows e, Ep+e, 2Ep+e of a
-// [3*Ep, d] bf16 matrix hold hi, mid, lo of expert e; Ep = E rounded up to
-// 16, padding rows zero), the score product is a plain GEMM on the
-// expert-product kernel ([N, 3*Ep] fp32 partial scores), and a ranking
-// kernel finishes.
+// split is done once per call into the workspace (a [Ep][3 d] bf16 matrix
+// whose row pi(e) holds hi, mid and lo of expert e one after the other;
+// Ep = E rounded up to 16, or to 64 past 64 experts, padding rows zero;
+// pi(e) = (e mod 64) Q + e / 64 with Q = Ep / 64 puts the Q experts a
+// ranking lane holds, e, e + 64, ..., in adjacent score columns), the score
+// product runs on the
+// expert-product kernel with the token row read once per term, so that the
+// three terms of an expert accumulate into one fp32 score, its K dimension
+// cut into ranges that write partial scores, and a ranking kernel adds the
+// ranges in order and finishes.
 #include "common.hpp"
 
 #include <float.h>
@@ -120,9 +125,12 @@ __device__ __forceinline__ void topk_softmax_group(const float (&v)[Q], int E, i
     }
 }
 
-// W_g [E, d] fp32 -> Wsp [3*Ep, d] bf16 (hi, mid, lo blocks); 8 elements per thread.
+// W_g [E, d] fp32 -> Wsp [Ep][3 d] bf16 (row pi(e): hi, mid, lo of expert e, per
+// 64 columns when interleaved);
+// 8 elements per thread.
 __global__ __launch_bounds__(256) void split_router_weights_kernel(const float *__restrict__ wg,
                                                                    int E, int Ep, int d,
+                                                                   bool inter,
                                                                    unsigned short *__restrict__ wsp) {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // group of 8
     const int64_t groups = (int64_t)Ep * (d / 8);
@@ -137,15 +145,22 @@ __global__ __launch_bounds__(256) void split_router_weights_kernel(const float *
     }
     u32x4 hi, mid, lo;
     split8(w0, w1, hi, mid, lo);
-    *reinterpret_cast<u32x4 *>(wsp + (int64_t)e * d + i) = hi;
-    *reinterpret_cast<u32x4 *>(wsp + ((int64_t)Ep + e) * d + i) = mid;
-    *reinterpret_cast<u32x4 *>(wsp + ((int64_t)2 * Ep + e) * d + i) = lo;
+    const int Q = Ep > 64 ? Ep / 64 : 1;
+    unsigned short *row = wsp + (int64_t)((e % 64) * Q + e / 64) * 3 * d;
+    // the terms of 64 columns one after the other, or each term's d columns
+    const int64_t o = inter ? (int64_t)(i / 64) * 192 + i % 64 : i;
+    const int64_t step = inter ? 64 : d;
+    *reinterpret_cast<u32x4 *>(row + o) = hi;
+    *reinterpret_cast<u32x4 *>(row + o + step) = mid;
+    *reinterpret_cast<u32x4 *>(row + o + 2 * step) = lo;
 }
 
-// Ranking of one token per G-lane group from precomputed partial scores
-// s3 [N, 3*Ep] (hi, mid, lo products, summed here in that order) plus noise.
+// Ranking of one token per 64-lane wave from the partial scores of ns
+// K-ranges, P [ns][N][Ep] (summed here in range order), plus noise. Lane g
+// holds experts g + 64 q, q < Q, which the permuted columns place at
+// g Q .. g Q + Q - 1: one load of Q scores per range.
 template <int G, int Q>
-__global__ __launch_bounds__(256) void rank_scores_kernel(const float *__restrict__ s3,
+__global__ __launch_bounds__(256) void rank_scores_kernel(const float *__restrict__ P, int ns,
                                                           const float *__restrict__ noise, int N,
                                                           int E, int Ep, int k,
                                                           int32_t *__restrict__ idx_out,
@@ -155,14 +170,34 @@ __global__ __launch_bounds__(256) void rank_scores_kernel(const float *__restric
     const int64_t t = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / G) + lane / G;
     const bool active = t < N;
     const int64_t tc = active ? t : 0;
+    static_assert(G == 64 && (Q == 1 || Q == 2 || Q == 4), "one token per wave");
     float v[Q];
+    const float *r = P + tc * Ep + (int64_t)lg * Q;
+    auto load = [&](const float *p, float (&o)[Q]) {
+        if constexpr (Q == 4) {
+            const f32x4 t4 = *reinterpret_cast<const f32x4 *>(p);
+            o[0] = t4[0]; o[1] = t4[1]; o[2] = t4[2]; o[3] = t4[3];
+        } else if constexpr (Q == 2) {
+            const f32x2_t t2 = *reinterpret_cast<const f32x2_t *>(p);
+            o[0] = t2[0]; o[1] = t2[1];
+        } else {
+            o[0] = p[0];
+        }
+    };
+    load(r, v);
+    for (int sp = 1; sp < ns; ++sp) {
+        float w[Q];
+        load(r + (int64_t)sp * N * Ep, w);
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            v[q] += w[q];
+    }
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int e = lg + G * q;
         float sc = -INFINITY;
         if (e < E) {
-            const float *r = s3 + tc * 3 * Ep;
-            sc = (r[e] + r[Ep + e]) + r[2 * Ep + e];
+            sc = v[q];
             if (noise)
                 sc += noise[tc * E + e];
             if (sc != sc)
@@ -353,24 +388,27 @@ hipError_t launch_fused(const void *x, const float *wg, const float *noise, int6
 }
 
 template <int G, int Q>
-hipError_t launch_rank(const float *s3, const float *noise, int64_t N, int E, int Ep, int k,
-                       int32_t *idx, float *gate, hipStream_t s) {
+hipError_t launch_rank(const float *P, int ns, const float *noise, int64_t N, int E, int Ep,
+                       int k, int32_t *idx, float *gate, hipStream_t s) {
     const int64_t tokens_per_block = 4 * (64 / G);
     const int blocks = (int)((N + tokens_per_block - 1) / tokens_per_block);
-    hipLaunchKernelGGL((rank_scores_kernel<G, Q>), dim3(blocks), dim3(256), 0, s, s3, noise,
+    hipLaunchKernelGGL((rank_scores_kernel<G, Q>), dim3(blocks), dim3(256), 0, s, P, ns, noise,
                        (int)N, E, Ep, k, idx, gate);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int64_t router_padded_experts(int E) { return (E + 15) / 16 * 16; }
+int64_t router_padded_experts(int E) {
+    return E <= 64 ? (E + 15) / 16 * 16 : (E + 63) / 64 * 64;
+}
 
 size_t router_workspace_bytes(int64_t N, int64_t d, int E) {
     const int64_t Ep = router_padded_experts(E);
     if (Ep <= kFusedMaxExperts)
         return 0;
-    return (size_t)(3 * Ep * d * 2 + 255) / 256 * 256 + (size_t)(N * 3 * Ep * 4 + 255) / 256 * 256;
+    const int64_t ns = router_score_splits(N, d, Ep);
+    return (size_t)(3 * Ep * d * 2 + 255) / 256 * 256 + (size_t)(ns * N * Ep * 4 + 255) / 256 * 256;
 }
 
 hipError_t launch_router_bf16(const void *x, const float *wg, const float *noise, int64_t N,
@@ -384,18 +422,19 @@ hipError_t launch_router_bf16(const void *x, const float *wg, const float *noise
     unsigned short *wsp = static_cast<unsigned short *>(ws);
     const int64_t groups = (int64_t)Ep * (d / 8);
     hipLaunchKernelGGL(split_router_weights_kernel, dim3((unsigned)((groups + 255) / 256)),
-                       dim3(256), 0, s, wg, E, Ep, (int)d, wsp);
+                       dim3(256), 0, s, wg, E, Ep, (int)d, router_terms_interleaved(d), wsp);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    float *s3 = reinterpret_cast<float *>(static_cast<char *>(ws) +
-                                          (size_t)(3 * Ep * d * 2 + 255) / 256 * 256);
-    err = launch_plain_gemm_bf16(x, wsp, N, d, 3 * Ep, s3, s);
+    float *P = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                         (size_t)(3 * Ep * d * 2 + 255) / 256 * 256);
+    err = launch_router_scores_bf16(x, wsp, N, d, Ep, P, s);
     if (err != hipSuccess)
         return err;
-    if (Ep <= 64) return launch_rank<64, 1>(s3, noise, N, E, Ep, k, idx, gate, s);
-    if (Ep <= 128) return launch_rank<64, 2>(s3, noise, N, E, Ep, k, idx, gate, s);
-    return launch_rank<64, 4>(s3, noise, N, E, Ep, k, idx, gate, s);
+    const int ns = router_score_splits(N, d, Ep);
+    if (Ep <= 64) return launch_rank<64, 1>(P, ns, noise, N, E, Ep, k, idx, gate, s);
+    if (Ep <= 128) return launch_rank<64, 2>(P, ns, noise, N, E, Ep, k, idx, gate, s);
+    return launch_rank<64, 4>(P, ns, noise, N, E, Ep, k, idx, gate, s);
 }
 
 hipError_t launch_router_f32(const float *x, const float *wg, const float *noise, int64_t N,

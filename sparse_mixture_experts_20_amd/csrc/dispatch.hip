@@ -8,21 +8,23 @@
 // the top-1 block comes first so first choices have priority.
 //
 // The running count is never materialised as a [k*N, E] one-hot matrix.
-// Assignments are taken in (j, t) order in chunks of 4096, in three passes:
+// Assignments are taken in (j, t) order. A call of at most 4096 of them is
+// one chunk, planned by one workgroup (dispatch_kernel<4>): each wave ranks
+// its 4 x 64 assignments against the lanes holding the same id (found with
+// one ballot per id bit), the per-wave counts become exclusive prefixes
+// across the 16 waves, and the workgroup finishes the plan. Larger calls
+// take chunks of 1024 (one assignment per thread) in two passes:
 //  1. chunk_hist_kernel: per chunk, the count of assignments to each expert
 //     (integer adds, so their order does not matter) and, when asked for, the
 //     sum of their gates in a fixed order;
-//  2. chunk_scan_kernel: one thread per expert turns the counts into
-//     exclusive prefixes over the chunks, in chunk order, and finishes the
-//     plan: used[], the router statistics and the GEMM tile schedule;
-//  3. dispatch_kernel: per chunk, each wave ranks its 4 x 64 assignments
-//     against the lanes holding the same id (found with one ballot per id
-//     bit), the per-wave counts become exclusive prefixes across the 16 waves,
-//     and the slot is the earlier chunks' count plus the rank in the chunk.
-// A call with a single chunk runs pass 3 alone (it finishes the plan itself);
-// one with at most 32 chunks and no gate sums asked for runs a single pass
-// (dispatch_fused_kernel) in which every workgroup recounts the earlier
-// chunks.
+//  2. dispatch_kernel<1>: per chunk, the count of each expert's assignments
+//     in the earlier chunks (the sum of their counts, four ranges of chunks
+//     added by four threads per expert; integers, so the order does not
+//     matter), then the ranking of its chunk as above; the last workgroup
+//     finishes the plan: used[], the router statistics and the GEMM tile
+//     schedule.
+// Past 128 chunks the earlier chunks' counts come from chunk_scan_kernel,
+// one thread per expert adding the chunks in order, between the two passes.
 // Ranks are positional, never taken from atomics, so the plan is the same on
 // every run.
 #include "common.hpp"
@@ -32,8 +34,9 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWavesPerBlock = kThreads / kWave;   // 16
-constexpr int kItems = 4;                           // 64-assignment groups per wave per chunk
-constexpr int kPhase = kThreads * kItems;           // 4096 assignments per chunk
+constexpr int kOneChunk = kThreads * 4;             // a call planned by one workgroup
+constexpr int kChunk = kThreads;                    // assignments per chunk of larger calls
+constexpr int kInlineChunks = 128;                  // the ranking pass sums earlier chunks itself
 
 // Lanes of the wave holding the same expert id as this lane (among lanes
 // with valid ids): one ballot per id bit, O(log E) with no memory traffic.
@@ -55,15 +58,16 @@ __device__ __forceinline__ int assignment_of(int p, int N, int k) {
     return (p - j * N) * k + j;
 }
 
-// This thread's assignments of chunk p0 (item s: wave w's group s, lane),
-// with their expert ids (-1: past the end or not an expert id).
+// This thread's assignments of the chunk starting at p0 (item s: wave w's
+// group s, lane), with their expert ids (-1: past the end or not an id).
+template <int ITEMS>
 __device__ __forceinline__ void load_chunk(const int32_t *__restrict__ idx, int64_t p0, int total,
-                                           int N, int k, int E, int (&cur_a)[kItems],
-                                           int (&cur_e)[kItems]) {
+                                           int N, int k, int E, int (&cur_a)[ITEMS],
+                                           int (&cur_e)[ITEMS]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int s = 0; s < kItems; ++s) {
-        const int64_t p = p0 + w * (kItems * 64) + s * 64 + lane;
+    for (int s = 0; s < ITEMS; ++s) {
+        const int64_t p = p0 + w * (ITEMS * 64) + s * 64 + lane;
         cur_a[s] = p < total ? assignment_of((int)p, N, k) : -1;
         const int e = cur_a[s] >= 0 ? idx[cur_a[s]] : -1;
         cur_e[s] = (e >= 0 && e < E) ? e : -1;
@@ -75,7 +79,8 @@ __device__ __forceinline__ void load_chunk(const int32_t *__restrict__ idx, int6
 // gsum[e] in a fixed order: lanes in order within each 64-assignment group
 // (summed by the group's first lane with that id), groups in order within a
 // wave, then the waves in order. wsum: LDS scratch [16][E] floats, wg: [16][64].
-__device__ void chunk_counts(const int (&cur_a)[kItems], const int (&cur_e)[kItems], int E,
+template <int ITEMS>
+__device__ void chunk_counts(const int (&cur_a)[ITEMS], const int (&cur_e)[ITEMS], int E,
                              const float *__restrict__ gate, int *cnt, float *gsum,
                              float *wsum, float *wg) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -86,7 +91,7 @@ __device__ void chunk_counts(const int (&cur_a)[kItems], const int (&cur_e)[kIte
             wsum[i] = 0.f;
     __syncthreads();
 #pragma unroll
-    for (int s = 0; s < kItems; ++s) {
+    for (int s = 0; s < ITEMS; ++s) {
         const int e = cur_e[s];
         const uint64_t m = match_ids(e, e >= 0, nbits);
         const bool lead = e >= 0 && __popcll(m & lt) == 0;
@@ -186,12 +191,12 @@ __global__ __launch_bounds__(kThreads) void chunk_hist_kernel(
     __shared__ float wsum[kWavesPerBlock * kMaxExperts];
     __shared__ float wg[kWavesPerBlock * 64];
     const int total = N * k;
-    const int64_t p0 = (int64_t)blockIdx.x * kPhase;
-    int cur_a[kItems], cur_e[kItems];
-    load_chunk(idx, p0, total, N, k, E, cur_a, cur_e);
+    const int64_t p0 = (int64_t)blockIdx.x * kChunk;
+    int cur_a[1], cur_e[1];
+    load_chunk<1>(idx, p0, total, N, k, E, cur_a, cur_e);
     for (int e = threadIdx.x; e < E; e += kThreads)
         cnt[e] = 0;
-    chunk_counts(cur_a, cur_e, E, gate, cnt, gsum, wsum, wg);
+    chunk_counts<1>(cur_a, cur_e, E, gate, cnt, gsum, wsum, wg);
     for (int e = threadIdx.x; e < E; e += kThreads) {
         hist[(int64_t)blockIdx.x * E + e] = cnt[e];
         if (gate)
@@ -199,53 +204,48 @@ __global__ __launch_bounds__(kThreads) void chunk_hist_kernel(
     }
 }
 
-// Pass 2 (one workgroup of 256 threads): hist[c][e] becomes the exclusive
-// prefix over chunks c' < c, in chunk order; the totals finish the plan.
-__global__ __launch_bounds__(256) void chunk_scan_kernel(
-    int32_t *__restrict__ hist, const float *__restrict__ gpart, int chunks, int E, int ceff,
-    int32_t *__restrict__ used, int32_t *__restrict__ tiles, int32_t *__restrict__ demand,
-    int32_t *__restrict__ drops, float *__restrict__ gate_sum) {
-    __shared__ int cnt[kMaxExperts];
-    __shared__ float gsum[kMaxExperts];
+// Between the passes, past kInlineChunks chunks (one workgroup of 256
+// threads): hist[c][e] becomes the exclusive prefix over chunks c' < c, in
+// chunk order.
+__global__ __launch_bounds__(256) void chunk_scan_kernel(int32_t *__restrict__ hist, int chunks,
+                                                         int E) {
     const int e = threadIdx.x;
-    if (e < E) {
-        constexpr int U = 8;   // loads of U chunks in flight
-        int run = 0;
-        float gs = 0.f;
-        for (int c0 = 0; c0 < chunks; c0 += U) {
-            int h[U];
-            float g[U];
+    if (e >= E)
+        return;
+    constexpr int U = 8;   // loads of U chunks in flight
+    int run = 0;
+    for (int c0 = 0; c0 < chunks; c0 += U) {
+        int h[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                h[u] = c0 + u < chunks ? hist[(int64_t)(c0 + u) * E + e] : 0;
-                g[u] = (gate_sum && c0 + u < chunks) ? gpart[(int64_t)(c0 + u) * E + e] : 0.f;
-            }
+        for (int u = 0; u < U; ++u)
+            h[u] = c0 + u < chunks ? hist[(int64_t)(c0 + u) * E + e] : 0;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (c0 + u < chunks) {
-                    hist[(int64_t)(c0 + u) * E + e] = run;
-                    run += h[u];
-                    gs += g[u];
-                }
+        for (int u = 0; u < U; ++u) {
+            if (c0 + u < chunks) {
+                hist[(int64_t)(c0 + u) * E + e] = run;
+                run += h[u];
             }
         }
-        cnt[e] = run;
-        gsum[e] = gs;
     }
-    __syncthreads();
-    finish_plan(cnt, gsum, E, ceff, used, tiles, demand, drops, gate_sum);
 }
 
-// Pass 3: the slots of chunk c. excl: the exclusive prefixes of pass 2 (NULL
-// for a single chunk, which then also finishes the plan).
+// The slots of one chunk (ITEMS = 4: a call of one chunk of up to 4096
+// assignments, which also counts itself and finishes the plan; ITEMS = 1:
+// chunk blockIdx.x of 1024 of a larger call, after pass 1). hist: the
+// per-chunk counts of pass 1 (the ranking sums those of the earlier chunks),
+// or, with scanned, their exclusive prefixes; gpart: the per-chunk gate sums
+// of pass 1 (read by the last workgroup when gate_sum is asked for).
+template <int ITEMS>
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     const int32_t *__restrict__ idx, const float *__restrict__ gate, int N, int E, int k,
-    int ceff, const int32_t *__restrict__ excl, int32_t *__restrict__ slot,
-    int32_t *__restrict__ used, int32_t *__restrict__ slot_token, int32_t *__restrict__ tiles,
-    int32_t *__restrict__ demand, int32_t *__restrict__ drops, float *__restrict__ gate_sum) {
+    int ceff, const int32_t *__restrict__ hist, const float *__restrict__ gpart, int scanned,
+    int32_t *__restrict__ slot, int32_t *__restrict__ used, int32_t *__restrict__ slot_token,
+    int32_t *__restrict__ tiles, int32_t *__restrict__ demand, int32_t *__restrict__ drops,
+    float *__restrict__ gate_sum) {
+    constexpr int kParts = kThreads / kMaxExperts;        // threads per expert in the sums
     __shared__ int base[kMaxExperts];                     // assignments of earlier chunks
     __shared__ int wcnt[kWavesPerBlock * kMaxExperts];    // per-wave counts, then prefixes
-    __shared__ int cnt[kMaxExperts];                      // single chunk: its counts
+    __shared__ int cnt[kMaxExperts];                      // totals up to this chunk's end
     __shared__ float gsum[kMaxExperts];
     __shared__ float wg[kWavesPerBlock * 64];
 
@@ -254,31 +254,65 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     const uint64_t lt = lanemask_lt();
     const int total = N * k;   // < 2^31
     const int nbits = id_bits(E);
-    const int64_t p0 = (int64_t)blockIdx.x * kPhase;   // this workgroup's chunk
+    const int c = blockIdx.x;
+    const int64_t p0 = (int64_t)c * (ITEMS * kThreads);   // this workgroup's chunk
+    const bool last = c == (int)gridDim.x - 1;
 
-    int cur_a[kItems], cur_e[kItems];
-    load_chunk(idx, p0, total, N, k, E, cur_a, cur_e);
-    for (int e = tid; e < E; e += kThreads) {
-        base[e] = excl ? excl[(int64_t)blockIdx.x * E + e] : 0;
+    int cur_a[ITEMS], cur_e[ITEMS];
+    load_chunk<ITEMS>(idx, p0, total, N, k, E, cur_a, cur_e);
+    for (int e = tid; e < E; e += kThreads)
         cnt[e] = 0;
+    if constexpr (ITEMS == 1) {
+        // the earlier chunks' counts: kParts consecutive ranges of chunks,
+        // one thread each, added into base (integers: any order)
+        int *part = wcnt;   // [kParts][kMaxExperts], zeroed again below
+        const int e = tid % kMaxExperts, q = tid / kMaxExperts;
+        if (e < E) {
+            int acc = 0;
+            if (scanned) {
+                if (q == 0)
+                    acc = hist[(int64_t)c * E + e];
+            } else {
+                const int c0 = q * c / kParts, c1 = (q + 1) * c / kParts;
+                constexpr int U = 8;
+                for (int cc = c0; cc < c1; cc += U) {
+                    int h[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        h[u] = cc + u < c1 ? hist[(int64_t)(cc + u) * E + e] : 0;
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        acc += h[u];
+                }
+            }
+            part[q * kMaxExperts + e] = acc;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += kThreads) {
+            int b = 0;
+#pragma unroll
+            for (int qq = 0; qq < kParts; ++qq)
+                b += part[qq * kMaxExperts + ee];
+            base[ee] = b;
+        }
+        __syncthreads();
+    } else {
+        for (int e = tid; e < E; e += kThreads)
+            base[e] = 0;
+        // one chunk: its counts and gate sums finish the plan (wsum borrows
+        // wcnt, which is zeroed again below)
+        chunk_counts<ITEMS>(cur_a, cur_e, E, gate_sum ? gate : nullptr, cnt, gsum,
+                            reinterpret_cast<float *>(wcnt), wg);
+        finish_plan(cnt, gsum, E, ceff, used, tiles, demand, drops, gate_sum);
     }
     for (int i = tid; i < kWavesPerBlock * E; i += kThreads)
         wcnt[i] = 0;
-    if (!excl) {
-        // single chunk: its counts and gate sums finish the plan (wsum
-        // borrows wcnt, which is zeroed again below)
-        chunk_counts(cur_a, cur_e, E, gate_sum ? gate : nullptr, cnt, gsum,
-                     reinterpret_cast<float *>(wcnt), wg);
-        finish_plan(cnt, gsum, E, ceff, used, tiles, demand, drops, gate_sum);
-        for (int i = tid; i < kWavesPerBlock * E; i += kThreads)
-            wcnt[i] = 0;
-    }
     __syncthreads();
 
     // rank of each assignment among the wave's earlier ones with its id
-    int my_r[kItems];
+    int my_r[ITEMS];
 #pragma unroll
-    for (int s = 0; s < kItems; ++s) {
+    for (int s = 0; s < ITEMS; ++s) {
         const int e = cur_e[s];
         if (cur_a[s] >= 0 && e < 0)   // not an expert id: the assignment is dropped
             slot[cur_a[s]] = -1;
@@ -296,21 +330,24 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
                   "one power-of-two lane group per expert");
     for (int e0 = 0; e0 < E; e0 += kThreads / kWavesPerBlock) {
         const int e = e0 + tid / kWavesPerBlock, ww = tid % kWavesPerBlock;
-        const int c = e < E ? wcnt[ww * E + e] : 0;
+        const int cw = e < E ? wcnt[ww * E + e] : 0;
         const int b0 = e < E ? base[e] : 0;
-        int incl = c;
+        int incl = cw;
 #pragma unroll
         for (int off = 1; off < kWavesPerBlock; off <<= 1) {
             const int o = __shfl_up(incl, off, kWavesPerBlock);
             if (ww >= off)
                 incl += o;
         }
-        if (e < E)
-            wcnt[ww * E + e] = b0 + incl - c;
+        if (e < E) {
+            wcnt[ww * E + e] = b0 + incl - cw;
+            if (ITEMS == 1 && ww == kWavesPerBlock - 1)
+                cnt[e] = b0 + incl;   // assignments up to the end of this chunk
+        }
     }
     __syncthreads();
 #pragma unroll
-    for (int s = 0; s < kItems; ++s) {
+    for (int s = 0; s < ITEMS; ++s) {
         const int e = cur_e[s];
         if (e < 0)
             continue;
@@ -321,6 +358,33 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
         if (kept)
             slot_token[(int64_t)e * ceff + r] = a;
     }
+    if (ITEMS != 1 || !last)
+        return;
+    if (gate_sum) {
+        // gate sums of all chunks: kParts consecutive ranges, each in chunk
+        // order, then the ranges in order
+        float *gp = reinterpret_cast<float *>(wcnt);   // ranking done: free
+        __syncthreads();
+        const int e = tid % kMaxExperts, q = tid / kMaxExperts;
+        const int nc = (int)gridDim.x;
+        if (e < E) {
+            float acc = 0.f;
+            const int c0 = q * nc / kParts, c1 = (q + 1) * nc / kParts;
+            for (int cc = c0; cc < c1; ++cc)
+                acc += gpart[(int64_t)cc * E + e];
+            gp[q * kMaxExperts + e] = acc;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += kThreads) {
+            float g = gp[ee];
+#pragma unroll
+            for (int qq = 1; qq < kParts; ++qq)
+                g += gp[qq * kMaxExperts + ee];
+            gsum[ee] = g;
+        }
+    }
+    __syncthreads();
+    finish_plan(cnt, gsum, E, ceff, used, tiles, demand, drops, gate_sum);
 }
 
 __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
@@ -329,117 +393,12 @@ __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
         p[i] = v;
 }
 
-// One-launch plan for at most kFusedChunks chunks when no gate sums are
-// asked for: every workgroup counts, per expert, the assignments of the
-// earlier chunks itself (reading the ids in their [N, k] layout, 4 per load,
-// and keeping those whose (choice, token) position lies before its chunk;
-// integer adds, so their order does not matter), then ranks its chunk as
-// dispatch_kernel does; the last workgroup, which also counts its own chunk,
-// finishes the plan. The slots, used counts and tile schedule are those of
-// the three-pass plan.
-constexpr int kFusedChunks = 32;
-
-__global__ __launch_bounds__(kThreads) void dispatch_fused_kernel(
-    const int32_t *__restrict__ idx, int N, int E, int k, int ceff, int32_t *__restrict__ slot,
-    int32_t *__restrict__ used, int32_t *__restrict__ slot_token, int32_t *__restrict__ tiles,
-    int32_t *__restrict__ demand, int32_t *__restrict__ drops) {
-    __shared__ int base[kMaxExperts];
-    __shared__ int wcnt[kWavesPerBlock * kMaxExperts];
-    __shared__ int cnt[kMaxExperts];
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const uint64_t lt = lanemask_lt();
-    const int total = N * k;
-    const int nbits = id_bits(E);
-    const int64_t p0 = (int64_t)blockIdx.x * kPhase;
-    const bool last = blockIdx.x == gridDim.x - 1;
-    int cur_a[kItems], cur_e[kItems];
-    load_chunk(idx, p0, total, N, k, E, cur_a, cur_e);
-    for (int e = tid; e < E; e += kThreads) {
-        base[e] = 0;
-        cnt[e] = 0;
-    }
-    for (int i = tid; i < kWavesPerBlock * E; i += kThreads)
-        wcnt[i] = 0;
-    __syncthreads();
-    // earlier chunks: assignments a = t*k + j with j*N + t < p0 (p0 > 0 only)
-    if (p0 > 0) {
-        const bool vec = ((uintptr_t)idx & 15) == 0;
-        for (int a0 = tid * 4; a0 < total; a0 += kThreads * 4) {
-            int ev[4];
-            if (vec && a0 + 4 <= total) {
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(idx + a0);
-                ev[0] = (int)v[0]; ev[1] = (int)v[1]; ev[2] = (int)v[2]; ev[3] = (int)v[3];
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    ev[q] = a0 + q < total ? idx[a0 + q] : -1;
-            }
-            int t = a0 / k, j = a0 - t * k;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int e = ev[q];
-                if (a0 + q < total && e >= 0 && e < E && (int64_t)j * N + t < p0)
-                    atomicAdd(&base[e], 1);
-                if (++j == k) {
-                    j = 0;
-                    ++t;
-                }
-            }
-        }
-    }
-    __syncthreads();
-    // rank of each assignment among the wave's earlier ones with its id
-    int my_r[kItems];
-#pragma unroll
-    for (int s = 0; s < kItems; ++s) {
-        const int e = cur_e[s];
-        if (cur_a[s] >= 0 && e < 0)
-            slot[cur_a[s]] = -1;
-        const uint64_t m = match_ids(e, e >= 0, nbits);
-        const int before = __popcll(m & lt);
-        my_r[s] = e >= 0 ? wcnt[w * E + e] + before : 0;
-        if (e >= 0 && before == 0)
-            wcnt[w * E + e] += __popcll(m);
-    }
-    __syncthreads();
-    for (int e0 = 0; e0 < E; e0 += kThreads / kWavesPerBlock) {
-        const int e = e0 + tid / kWavesPerBlock, ww = tid % kWavesPerBlock;
-        const int c = e < E ? wcnt[ww * E + e] : 0;
-        const int b0 = e < E ? base[e] : 0;
-        int incl = c;
-#pragma unroll
-        for (int off = 1; off < kWavesPerBlock; off <<= 1) {
-            const int o = __shfl_up(incl, off, kWavesPerBlock);
-            if (ww >= off)
-                incl += o;
-        }
-        if (e < E) {
-            wcnt[ww * E + e] = b0 + incl - c;
-            if (ww == kWavesPerBlock - 1)
-                cnt[e] = b0 + incl;   // assignments up to the end of this chunk
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < kItems; ++s) {
-        const int e = cur_e[s];
-        if (e < 0)
-            continue;
-        const int r = wcnt[w * E + e] + my_r[s];
-        const int a = cur_a[s];
-        const bool kept = r < ceff;
-        slot[a] = kept ? r : -1;
-        if (kept)
-            slot_token[(int64_t)e * ceff + r] = a;
-    }
-    if (last)
-        finish_plan(cnt, nullptr, E, ceff, used, tiles, demand, drops, nullptr);
-}
-
 }  // namespace
 
-int64_t dispatch_chunks(int64_t N, int k) { return (N * k + kPhase - 1) / kPhase; }
+int64_t dispatch_chunks(int64_t N, int k) {
+    const int64_t total = N * k;
+    return total <= kOneChunk ? (total > 0 ? 1 : 0) : (total + kChunk - 1) / kChunk;
+}
 
 size_t dispatch_workspace_bytes(int64_t N, int E, int k) {
     const int64_t chunks = dispatch_chunks(N, k);
@@ -456,32 +415,30 @@ hipError_t launch_dispatch(const int32_t *idx, const float *gate, int64_t N, int
     if (chunks == 0)
         return hipSuccess;
     const float *g = gate_sum ? gate : nullptr;
-    if (chunks <= kFusedChunks && !gate_sum) {
-        hipLaunchKernelGGL(dispatch_fused_kernel, dim3((unsigned)chunks), dim3(kThreads), 0, s,
-                           idx, (int)N, E, k, (int)ceff, slot, used, slot_token, tiles, demand,
-                           drops);
+    if (chunks == 1) {
+        hipLaunchKernelGGL(dispatch_kernel<4>, dim3(1), dim3(kThreads), 0, s, idx, g, (int)N, E,
+                           k, (int)ceff, (const int32_t *)nullptr, (const float *)nullptr, 0,
+                           slot, used, slot_token, tiles, demand, drops, gate_sum);
         return hipGetLastError();
     }
-    int32_t *hist = nullptr;
-    if (chunks > 1) {
-        hist = static_cast<int32_t *>(ws);
-        float *gpart = reinterpret_cast<float *>(static_cast<char *>(ws) +
-                                                 (size_t)(chunks * E * 4 + 255) / 256 * 256);
-        hipLaunchKernelGGL(chunk_hist_kernel, dim3((unsigned)chunks), dim3(kThreads), 0, s, idx,
-                           g, (int)N, E, k, hist, gpart);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess)
-            return err;
-        hipLaunchKernelGGL(chunk_scan_kernel, dim3(1), dim3(256), 0, s, hist,
-                           (const float *)gpart, (int)chunks, E, (int)ceff, used, tiles, demand,
-                           drops, gate_sum);
+    int32_t *hist = static_cast<int32_t *>(ws);
+    float *gpart = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                             (size_t)(chunks * E * 4 + 255) / 256 * 256);
+    hipLaunchKernelGGL(chunk_hist_kernel, dim3((unsigned)chunks), dim3(kThreads), 0, s, idx, g,
+                       (int)N, E, k, hist, gpart);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const int scanned = chunks > kInlineChunks;
+    if (scanned) {
+        hipLaunchKernelGGL(chunk_scan_kernel, dim3(1), dim3(256), 0, s, hist, (int)chunks, E);
         err = hipGetLastError();
         if (err != hipSuccess)
             return err;
     }
-    hipLaunchKernelGGL(dispatch_kernel, dim3((unsigned)chunks), dim3(kThreads), 0, s, idx, g,
-                       (int)N, E, k, (int)ceff, (const int32_t *)hist, slot, used, slot_token,
-                       tiles, demand, drops, gate_sum);
+    hipLaunchKernelGGL(dispatch_kernel<1>, dim3((unsigned)chunks), dim3(kThreads), 0, s, idx, g,
+                       (int)N, E, k, (int)ceff, (const int32_t *)hist, (const float *)gpart,
+                       scanned, slot, used, slot_token, tiles, demand, drops, gate_sum);
     return hipGetLastError();
 }
 

@@ -2,7 +2,7 @@
 static device array, for callers that cannot allocate) against moe_dispatch
 (the same plan with a caller workspace), through the C ABI: two calls in a
 row on one stream, the second smaller than the first, each with several
-4096-assignment chunks so that the scratch is used. Every output must be
+1024-assignment chunks so that the scratch is used. Every output must be
 identical bit for bit."""
 import ctypes
 
@@ -56,7 +56,7 @@ def test_noalloc_dispatch_equals_dispatch(torch_mod):
     from sparse_mixture_experts_20_amd import binding as B
     L = B.lib()
     s = B._stream()
-    # (N, E, k, C): 20 chunks, then 3 (the second call is the smaller one)
+    # (N, E, k, C): 79 chunks, then 10 (the second call is the smaller one)
     for N, E, k, C, seed in ((20000, 64, 4, 1100, 1), (5000, 16, 2, 600, 2)):
         G.say(f"[noalloc] N={N} E={E} k={k} C={C}")
         idx_np, gate_np = _routing(N, E, k, seed)

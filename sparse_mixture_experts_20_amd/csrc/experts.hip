@@ -478,7 +478,9 @@ void expert_gemm_kernel(
         }
         const int T = s_mt[E] * NT;
         const SplitPlan sp = split_plan(T, KT, part ? P : 0);
-        const bool ll = light_last(used, s_mt, E, NT, BM, P, NTHR, s_pp, s_msk);
+        // (the 320-row tile holds every expert of up to 320 rows: a light
+        // last tile is rare there and not worth the extra pass over used)
+        const bool ll = BM == 320 ? false : light_last(used, s_mt, E, NT, BM, P, NTHR, s_pp, s_msk);
         // whole tiles in two launch segments (heavy ones, then light ones
         // when those go last), each spread over the XCDs; then the K-ranges
         // of the cut tiles
@@ -511,6 +513,20 @@ void expert_gemm_kernel(
         rows = used[e];
     }
 
+    if constexpr ((MODE == 1 || MODE == 5) && BM == 320) {
+        // Staggered start of the first round: its workgroups begin in 8
+        // groups 4 us apart (by position within their XCD). Every tile of
+        // this product ends by writing BM x BN fp32 output rows (320 KB);
+        // when all CUs start together they all write at once and the write
+        // phases add up, while spread out they overlap other CUs' products.
+        // At most 28 us once per launch; every wave leaves the wait.
+        if (b < P && piece < 0) {
+            const long long t0 = wall_clock64();   // 100 MHz
+            const long long dt = (long long)((b / kXcds) % 8) * 400;
+            while (wall_clock64() - t0 < dt)
+                __builtin_amdgcn_s_sleep(8);
+        }
+    }
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wk = WAVES_K == 1 ? 0 : wv / WMN;   // K set

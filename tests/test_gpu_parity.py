@@ -58,6 +58,8 @@ SMALL = {
     # kernel's own schedule prefix), K tails (264, 392), a partial column
     # tile (392) and one expert at capacity (384 rows: a second row tile)
     "tile320_bf16": (2048, 264, 64, 8, 392, "bf16", 1.5, 0.3, 0.5, 116),
+    # the 320-row tile with few experts (fewer tiles than workgroups)
+    "tile320_e8_bf16": (1024, 264, 8, 2, 392, "bf16", 1.25, 0.3, 0.0, 117),
     "k1_bf16": (200, 64, 3, 1, 64, "bf16", 1.0, 0.0, 0.0, 105),
     "k_equals_E_bf16": (100, 32, 4, 4, 48, "bf16", 1.0, 0.0, 0.0, 106),
     "max_top_k_bf16": (200, 64, 64, 16, 72, "bf16", 0.7, 0.2, 0.0, 112),

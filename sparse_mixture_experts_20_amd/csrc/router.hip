@@ -17,7 +17,8 @@
 // computes the scores of 16 tokens and ranks them. With more experts the
 // split is done once per call into the workspace (a [Ep][3 d] bf16 matrix
 // whose row pi(e) holds hi, mid and lo of expert e one after the other;
-// Ep = E rounded up to 16, or to 64 past 64 experts, padding rows zero;
+// Ep = E rounded up to 16, or to 128 or 256 past 64 experts, padding rows
+// zero;
 // pi(e) = (e mod 64) Q + e / 64 with Q = Ep / 64 puts the Q experts a
 // ranking lane holds, e, e + 64, ..., in adjacent score columns), the score
 // product runs on the
@@ -400,7 +401,8 @@ hipError_t launch_rank(const float *P, int ns, const float *noise, int64_t N, in
 }  // namespace
 
 int64_t router_padded_experts(int E) {
-    return E <= 64 ? (E + 15) / 16 * 16 : (E + 63) / 64 * 64;
+    // past 64 experts a ranking lane holds Q = Ep / 64 in {2, 4} scores
+    return E <= 64 ? (E + 15) / 16 * 16 : E <= 128 ? 128 : 256;
 }
 
 size_t router_workspace_bytes(int64_t N, int64_t d, int E) {

@@ -100,6 +100,7 @@ def test_router_matches_oracle(torch_mod, name):
 @pytest.mark.parametrize("N,d,E,k,sigma,seed", [
     (2000, 1024, 256, 8, 0.0, 31), (777, 200, 48, 4, 0.5, 32), (1500, 136, 100, 6, 0.3, 33),
     (1200, 192, 100, 5, 0.0, 34), (3000, 2056, 200, 8, 0.2, 35), (520, 640, 33, 2, 0.0, 36),
+    (900, 256, 150, 8, 0.1, 37),
 ])
 def test_router_many_experts(torch_mod, N, d, E, k, sigma, seed):
     torch = torch_mod

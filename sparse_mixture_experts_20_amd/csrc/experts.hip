@@ -1022,7 +1022,8 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
     const int t = blockIdx.x / STRIPS, strip = blockIdx.x % STRIPS;
     if (sp.nsplit < 2 || t >= sp.tail)   // (the same for the whole workgroup)
         return;
-    const bool ll = light_last(used, s_mt, E, NT, BM, P, 256, s_pp, s_msk);
+    // (the same order as the product kernel: no light-last pass for 320 rows)
+    const bool ll = BM == 320 ? false : light_last(used, s_mt, E, NT, BM, P, 256, s_pp, s_msk);
     int e, m0, n0;
     decode_tile(sp.Tdp + t, s_mt, ll ? s_pp : nullptr, E, NT, BM, BN, e, m0, n0);
     const int rows = used[e];

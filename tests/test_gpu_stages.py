@@ -179,6 +179,50 @@ def test_experts_match_oracle(torch_mod, name):
     assert np.abs(got - ref).max() <= G.BF16_MAX_ABS
 
 
+def test_experts_split_last_round_tile320(torch_mod):
+    """The 320-row tile with its last round cut into K-ranges, which needs a
+    caller scratch larger than the default (one fp32 320x256 partial tile per
+    resident workgroup): 128 experts of ~256 rows and one at capacity (two
+    row tiles), 516 tiles per product against 256 resident workgroups, so
+    the last round holds four tiles. The schedule and the fix-up must agree
+    on the tile order: sampled rows (with every token of the expert at
+    capacity) against the oracle, the split run repeatable, and every kept
+    row within a bf16 unit of the uncut run."""
+    torch = torch_mod
+    from sparse_mixture_experts_20_amd import binding as B
+    from sparse_mixture_experts_20_amd import device as D
+    wl = W.custom("split320", N=4096, d=1024, E=128, k=8, d_ff=1024, dtype="bf16", cf=1.5,
+                  sigma=0.3, bias0=0.5, seed=54, w_std=0.03)
+    G.say("[stage] experts split last round, 320-row tile")
+    _, idx, _ = oracle.router(wl.x64(), wl.wg64(), wl.noise64(), wl.k)
+    rng = np.random.default_rng(4)
+    route = oracle.forward(wl, rows=[0])
+    assert route.used.max() > 320 and np.sort(route.used)[-2] <= 320
+    full = np.nonzero((idx == int(np.argmax(route.used))).any(axis=1))[0]
+    rows = np.unique(np.concatenate([[0, wl.N - 1], full, rng.choice(wl.N, 64, replace=False)]))
+    res = oracle.forward(wl, rows=rows, want_y=True)
+    dev = D.upload(wl)
+    slot, used, slot_token, tiles = B.dispatch(torch.from_numpy(res.idx).cuda(), wl.E, res.C)
+    big = torch.empty(96 << 20, dtype=torch.uint8, device="cuda")
+    ys = []
+    for ws in (big, big, None):
+        _, Y = B.experts(dev["x"], dev["W_up"], dev["W_down"], wl.k, res.C, used, slot_token,
+                         tiles, workspace=ws)
+        torch.cuda.synchronize()
+        ys.append(G.f64(Y).reshape(wl.N, wl.k, wl.d))
+    np.testing.assert_array_equal(ys[0], ys[1])
+    kept = res.slot[rows] >= 0
+    for Yg in (ys[0], ys[2]):
+        got, ref = Yg[rows][kept], res.y[kept]
+        rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert rel <= G.BF16_REL_L2, rel
+        assert np.abs(got - ref).max() <= G.BF16_MAX_ABS
+    allk = res.slot >= 0
+    a, b = ys[0][allk], ys[2][allk]
+    assert np.all(np.abs(a - b) <= np.abs(b) * 2.0**-7 + 2e-3)
+    assert not np.array_equal(a, b)   # the split was taken (fp32 order differs)
+
+
 @pytest.mark.parametrize("act,bias_std", [("relu", 0.0), ("gelu", 0.05)])
 def test_experts_split_last_round(torch_mod, act, bias_std):
     """Shapes whose last round of 256x256 tiles is cut into K-ranges (16

@@ -353,13 +353,21 @@ def algorithmic(wl, kept):
     noise = N * E * 4 if wl.noise is not None else 0
     w = E * dff * d * xb                       # one expert weight tensor
     prod = 2.0 * kept * d * dff                # one expert product
+    yb = y_row_bytes(wl.cfg.dtype, d)          # one expert output row
     return {
         "router": (N * d * xb + E * d * 4 + noise + N * k * 8, 2.0 * N * d * E),
         "dispatch": (N * k * 8 + kept * 4, 0.0),
         "expert_up": (N * d * xb + w + kept * dff * xb, prod),
-        "expert_down": (kept * dff * xb + w + kept * d * 4, prod),      # Y rows are fp32
-        "combine": (kept * d * 4 + N * k * 8 + N * d * xb, 2.0 * kept * d),
+        "expert_down": (kept * dff * xb + w + kept * yb, prod),
+        "combine": (kept * yb + N * k * 8 + N * d * xb, 2.0 * kept * d),
     }
+
+
+def y_row_bytes(dtype, d):
+    """Bytes of one expert output row as the layer stores it: fp32 for an
+    fp32 layer; for a bf16 layer fp16 values plus one shift byte per 32
+    columns."""
+    return d * 2 + (d + 31) // 32 if dtype == "bf16" else d * 4
 
 
 def bench_forward(args, wl, dev):
@@ -400,14 +408,19 @@ def bench_forward(args, wl, dev):
     slot, usedt, slot_token, tiles = B.dispatch(idx, wl.E, C)
     ceff = min(C, wl.N)
     H = torch.empty((wl.E, max(ceff, 1), wl.d_ff), dtype=x.dtype, device="cuda")
-    Y = torch.empty((wl.N * wl.k, wl.d), dtype=torch.float32, device="cuda")
+    # expert output rows in the layer's own form: compact for a bf16 layer
+    # (fp16 values and one shift per 32 columns), fp32 otherwise
+    compact = x.dtype == torch.bfloat16
+    Y = torch.empty((wl.N * wl.k, wl.d), dtype=torch.float16 if compact else torch.float32,
+                    device="cuda")
+    Ysh = torch.empty((wl.N * wl.k, B.y_groups(wl.d)), dtype=torch.int8, device="cuda")
     out = torch.empty_like(x)
     # each stage's C entry point with its arguments marshalled once, so the
     # timed loop is not bound by Python-side argument handling
     L = B.lib()
     r = ctypes.byref
     dx, dg, dn, du, dd, do, dy = (B.desc(x), B.desc(wg), B.desc(nz), B.desc(wu), B.desc(wd),
-                                  B.desc(out), B.desc(Y))
+                                  B.desc(out), None if compact else B.desc(Y))
     s_ = B._stream()
     p = B._ptr
     rws = B.alloc_workspace(B.router_workspace_size(wl.N, wl.d, wl.E, x.dtype))
@@ -424,10 +437,16 @@ def bench_forward(args, wl, dev):
         "expert_up": lambda: L.moe_expert_up_ex(r(dx), r(du), opts, wl.k, C, p(usedt),
                                                 p(slot_token), p(tiles), p(H), p(ews),
                                                 ews.numel(), s_),
-        "expert_down": lambda: L.moe_expert_down_ex(wl.N, r(dd), opts, wl.k, C, p(usedt),
-                                                    p(slot_token), p(tiles), p(H), p(Y), p(ews),
-                                                    ews.numel(), s_),
-        "combine": lambda: L.moe_combine(wl.N, wl.d, wl.k, r(dy), p(gate), p(slot), r(do), s_),
+        "expert_down": (
+            (lambda: L.moe_expert_down_compact(wl.N, r(dd), opts, wl.k, C, p(usedt),
+                                               p(slot_token), p(tiles), p(H), p(Y), p(Ysh),
+                                               p(ews), ews.numel(), s_)) if compact else
+            (lambda: L.moe_expert_down_ex(wl.N, r(dd), opts, wl.k, C, p(usedt), p(slot_token),
+                                          p(tiles), p(H), p(Y), p(ews), ews.numel(), s_))),
+        "combine": (
+            (lambda: L.moe_combine_compact(wl.N, wl.d, wl.k, p(Y), p(Ysh), p(gate), p(slot),
+                                           r(do), s_)) if compact else
+            (lambda: L.moe_combine(wl.N, wl.d, wl.k, r(dy), p(gate), p(slot), r(do), s_))),
     }
     flush = Flusher()
     warm = {n: time_stage(fn, 5 * args.stage_reps) for n, fn in stages.items()}
@@ -576,12 +595,13 @@ def _algorithmic_bytes(kernel, p):
     m = re.search(r"expert_gemm_kernel<[^>]*, (\d)>", kernel)
     if m and m.group(1) == "0":       # x (whole), W_up, H rows written
         return N * d * sx + E * dff * d * sx + kept * dff * sx, "x + W_up + H"
-    if m and m.group(1) == "1":       # H rows read, W_down, fp32 Y rows written
-        return kept * dff * sx + E * d * dff * sx + kept * d * 4, "H + W_down + Y"
+    yb = y_row_bytes(p["dtype"], d)
+    if m and m.group(1) == "1":       # H rows read, W_down, Y rows written
+        return kept * dff * sx + E * d * dff * sx + kept * yb, "H + W_down + Y"
     if kernel.startswith("router"):
         return N * d * sx + E * d * 4 + noise + N * k * 8, "x + W_g + noise + ids/gates"
     if kernel.startswith("combine"):
-        return kept * d * 4 + N * k * 8 + N * d * sx, "Y + ids/gates + out"
+        return kept * yb + N * k * 8 + N * d * sx, "Y + ids/gates + out"
     return None, ""
 
 

@@ -139,7 +139,11 @@ typedef struct {
  *   stats  launch context and optional exports (required)
  * Numerics: scores, top-k and gates in fp32; expert products accumulate in
  * fp32 (bf16 inputs on matrix cores); the hidden activation is stored in
- * the dtype of x and each expert's output row in fp32; the combine
+ * the dtype of x. Each expert's output row is stored in fp32 for an fp32
+ * layer; for a bf16 layer it is stored compact in the workspace: every group
+ * of 32 columns as fp16 values of y * 2^sh with one power-of-two shift sh
+ * per group, chosen from the group's largest finite magnitude (relative
+ * error at most 2^-11, no overflow at any magnitude). The combine
  * accumulates in fp32 in choice order and rounds once to the dtype of out
  * (round to nearest even).
  * N = 0 is valid: capacity is 0, used_capacity (if given) is zeroed. */
@@ -330,6 +334,18 @@ int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity
                     const void *H, void *Y, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* moe_expert_down_ex writing Y compact, the form in which the fused entry
+ * points of a bf16 layer keep it (see moe_forward's numerics): Y16 [N*k, d]
+ * fp16 bits and Ysh [N*k][ceil(d / 32)] int8 shifts, row a standing for
+ * y[a, c] = Y16[a, c] * 2^-Ysh[a][c / 32]. Y16 16-byte aligned. bf16 layers
+ * only (MOE_ERR_DTYPE otherwise); rows of dropped assignments are not
+ * written. Callers that time or check the fused layer's stages use it. */
+int moe_expert_down_compact(int64_t N, const moe_tensor *W_down, const moe_expert_opts *opts,
+                            int k, int64_t capacity, const int32_t *used,
+                            const int32_t *slot_token, const int32_t *tiles, const void *H,
+                            void *Y16, int8_t *Ysh, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
 /* Combine (page 1 STEP 11-12; slides 38-40): out[t] = sum over j < k with
  * slot[t, j] >= 0 of topk_gate[t, j] * Y[t*k + j], accumulated in fp32 in
  * order j = 0..k-1, rounded once to out's dtype; rows with every choice
@@ -337,6 +353,13 @@ int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity
  * values), out is [N, d] MOE_F32 or MOE_BF16. */
 int moe_combine(int64_t N, int64_t d, int k, const moe_tensor *Y, const float *topk_gate,
                 const int32_t *slot, moe_tensor *out, void *stream);
+
+/* moe_combine over compact rows (Y16, Ysh as moe_expert_down_compact writes
+ * them), each value taken as Y16 * 2^-Ysh exactly; d % 8 == 0
+ * (MOE_ERR_UNSUPPORTED otherwise), Y16 and out 16-byte aligned. */
+int moe_combine_compact(int64_t N, int64_t d, int k, const void *Y16, const int8_t *Ysh,
+                        const float *topk_gate, const int32_t *slot, moe_tensor *out,
+                        void *stream);
 
 /* Backward pass of the layer (the row after the forward: gradients through
  * the gates to the router and through the experts), for bf16 layers with
@@ -349,8 +372,8 @@ int moe_combine(int64_t N, int64_t d, int k, const moe_tensor *Y, const float *t
  *   scores: dW_g = ds^T x, dx += ds W_g;
  *   experts: dZ = (dY W_down) where H > 0, dW_down = dY^T H, dW_up = dZ^T X,
  *   dx += the kept choices' dZ W_up rows, summed in choice order.
- * The forward state (routing, dispatch plan, H and the experts' fp32
- * outputs, as the forward combined them) is recomputed from the inputs in
+ * The forward state (routing, dispatch plan, H and the experts' output
+ * rows, as the forward combined them) is recomputed from the inputs in
  * the workspace, so the call takes the forward's arguments plus:
  *   dout    [N, d]         same dtype as x (MOE_BF16)
  *   dx      [N, d]         MOE_F32, written
@@ -393,7 +416,7 @@ int moe_backward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor
 /* Training step without recomputation: moe_forward_train is moe_forward_ex
  * for a bf16 layer (same arguments, same out bit for bit) that also leaves
  * the forward state the backward needs (routing, dispatch plan, H, the
- * experts' fp32 output rows and, for GELU, the pre-activations) in
+ * experts' output rows and, for GELU, the pre-activations) in
  * stats->workspace, which must hold moe_backward_workspace_size() bytes
  * (and in stats' exported routing arrays when given).
  * moe_backward_after_forward then takes moe_backward_ex's arguments and

@@ -26,7 +26,8 @@ EXPORTS = ("moe_forward", "moe_workspace_size", "moe_capacity", "moe_error_strin
            "moe_forward_ex", "moe_experts_ex", "moe_expert_up_ex", "moe_expert_down_ex",
            "moe_backward", "moe_backward_ex", "moe_backward_workspace_size",
            "moe_forward_train", "moe_backward_after_forward", "moe_dispatch_workspace_size",
-           "moe_expert_kernel_name", "moe_dispatch_noalloc")
+           "moe_expert_kernel_name", "moe_dispatch_noalloc", "moe_expert_down_compact",
+           "moe_combine_compact")
 
 MOE_ACT_RELU, MOE_ACT_GELU = 0, 1
 ACTS = {"relu": MOE_ACT_RELU, "gelu": MOE_ACT_GELU}
@@ -89,6 +90,10 @@ def lib():
                                          _i64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                          _vp]
         L.moe_expert_down_ex.restype = ctypes.c_int
+        L.moe_expert_down_compact.argtypes = [_i64, _T, ctypes.POINTER(MoeExpertOpts),
+                                              ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _vp, ctypes.c_size_t, _vp]
+        L.moe_expert_down_compact.restype = ctypes.c_int
         L.moe_backward.argtypes = [_T, _T, _T, _T, _T, ctypes.c_int, ctypes.c_float, _T, _T, _T,
                                    _T, _T, ctypes.POINTER(MoeStats)]
         L.moe_backward.restype = ctypes.c_int
@@ -141,6 +146,8 @@ def lib():
         L.moe_expert_workspace_size.restype = ctypes.c_size_t
         L.moe_combine.argtypes = [_i64, _i64, ctypes.c_int, _T, _vp, _vp, _T, _vp]
         L.moe_combine.restype = ctypes.c_int
+        L.moe_combine_compact.argtypes = [_i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _T, _vp]
+        L.moe_combine_compact.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -654,6 +661,42 @@ def expert_down(N, W_down, k, capacity_, used, slot_token, tiles, H, Y, workspac
                                       _stream(stream))
     _check(rc, "moe_expert_down")
     return Y
+
+
+def y_groups(d):
+    """Shift bytes per compact expert output row (one per 32 columns)."""
+    return (d + 31) // 32
+
+
+def expert_down_compact(N, W_down, k, capacity_, used, slot_token, tiles, H, Y16=None,
+                        Ysh=None, workspace="auto", stream=None, b_down=None, dropout=None):
+    """The down product writing compact rows, as the fused bf16 layer keeps
+    them: returns (Y16 [N*k, d] float16, Ysh [N*k, ceil(d/32)] int8), value
+    = Y16 * 2**-Ysh per group of 32 columns."""
+    import torch
+    d = W_down.shape[1]
+    if Y16 is None:
+        Y16 = torch.zeros((N * k, d), dtype=torch.float16, device=W_down.device)
+    if Ysh is None:
+        Ysh = torch.zeros((N * k, y_groups(d)), dtype=torch.int8, device=W_down.device)
+    dd = desc(W_down)
+    wp, wn = _ws_args(_expert_ws(workspace, W_down.dtype, W_down.device))
+    o = _opts("relu", None, b_down, dropout) or ExpertOpts("relu", None, b_down)
+    rc = lib().moe_expert_down_compact(N, _ref(dd), o.ref(), k, capacity_, _ptr(used),
+                                       _ptr(slot_token), _ptr(tiles), _ptr(H), _ptr(Y16),
+                                       _ptr(Ysh), wp, wn, _stream(stream))
+    _check(rc, "moe_expert_down_compact")
+    return Y16, Ysh
+
+
+def combine_compact(Y16, Ysh, gate, slot, out, stream=None):
+    """Combine over compact rows (expert_down_compact's Y16, Ysh)."""
+    N, k = gate.shape
+    d = out.shape[-1]
+    do = desc(out)
+    _check(lib().moe_combine_compact(N, d, k, _ptr(Y16), _ptr(Ysh), _ptr(gate), _ptr(slot),
+                                     _ref(do), _stream(stream)), "moe_combine_compact")
+    return out
 
 
 def combine(Y, gate, slot, out, stream=None):

@@ -35,12 +35,15 @@ __device__ __forceinline__ void split3_bits(float a, unsigned short &hi, unsigne
 
 // One wave per token: dY rows (bf16, kept choices), dg by a wave reduction in
 // a fixed butterfly order, then ds for every choice (dropped ones have dg 0
-// but still took part in the softmax). Y holds the experts' fp32 outputs, the
-// values the forward combined; 8 columns per lane and load.
+// but still took part in the softmax). Y holds the experts' outputs, the
+// values the forward combined: fp32 rows, or (ysh not NULL) the compact fp16
+// rows with one exponent shift per kYGroup columns; 8 columns per lane and
+// load.
 __global__ __launch_bounds__(256) void combine_backward_kernel(
-    const unsigned short *__restrict__ dout, const float *__restrict__ Y,
-    const float *__restrict__ gate, const int32_t *__restrict__ slot, int N, int d, int k,
-    unsigned short *__restrict__ dY, float *__restrict__ ds, Dropout dp) {
+    const unsigned short *__restrict__ dout, const void *__restrict__ Y,
+    const signed char *__restrict__ ysh, const float *__restrict__ gate,
+    const int32_t *__restrict__ slot, int N, int d, int k, unsigned short *__restrict__ dY,
+    float *__restrict__ ds, Dropout dp) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= N)
@@ -54,12 +57,24 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
         float p = 0.f;
         if (slot[a] >= 0) {
             const float g = gate[a];
-            const float *yr = Y + a * d;
             unsigned short *dyr = dY + a * d;
             for (int c = lane; c < chunks; c += 64) {
                 const u32x4 ov = *reinterpret_cast<const u32x4 *>(go + 8 * c);
-                const f32x4 y0 = *reinterpret_cast<const f32x4 *>(yr + 8 * c);
-                const f32x4 y1 = *reinterpret_cast<const f32x4 *>(yr + 8 * c + 4);
+                f32x4 y0, y1;
+                if (ysh) {
+                    const u32x4 h = *reinterpret_cast<const u32x4 *>(
+                        static_cast<const unsigned short *>(Y) + a * d + 8 * c);
+                    const float sc =
+                        pow2f(-(int)ysh[a * ((d + kYGroup - 1) / kYGroup) + 8 * c / kYGroup]);
+                    const f32x2_t p0 = unpack_f16x2(h[0]), p1 = unpack_f16x2(h[1]);
+                    const f32x2_t p2 = unpack_f16x2(h[2]), p3 = unpack_f16x2(h[3]);
+                    y0 = f32x4{p0[0], p0[1], p1[0], p1[1]} * sc;
+                    y1 = f32x4{p2[0], p2[1], p3[0], p3[1]} * sc;
+                } else {
+                    const float *yr = static_cast<const float *>(Y) + a * d;
+                    y0 = *reinterpret_cast<const f32x4 *>(yr + 8 * c);
+                    y1 = *reinterpret_cast<const f32x4 *>(yr + 8 * c + 4);
+                }
                 // Y already carries the dropout; dY = g dout m
                 float m[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
                 if (dp.on)
@@ -308,15 +323,14 @@ __global__ __launch_bounds__(256) void dx_kernel(const float *__restrict__ dXa,
 
 }  // namespace
 
-hipError_t launch_combine_backward(const void *dout, const void *Y, const float *gate,
-                                   const int32_t *slot, int64_t N, int64_t d, int k, void *dY,
-                                   float *ds, hipStream_t s, Dropout dp) {
+hipError_t launch_combine_backward(const void *dout, const void *Y, const signed char *ysh,
+                                   const float *gate, const int32_t *slot, int64_t N, int64_t d,
+                                   int k, void *dY, float *ds, hipStream_t s, Dropout dp) {
     if (N == 0)
         return hipSuccess;
     hipLaunchKernelGGL(combine_backward_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s,
-                       static_cast<const unsigned short *>(dout),
-                       static_cast<const float *>(Y), gate, slot, (int)N, (int)d, k,
-                       static_cast<unsigned short *>(dY), ds, dp);
+                       static_cast<const unsigned short *>(dout), Y, ysh, gate, slot, (int)N,
+                       (int)d, k, static_cast<unsigned short *>(dY), ds, dp);
     return hipGetLastError();
 }
 

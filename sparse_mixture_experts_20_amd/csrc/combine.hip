@@ -6,8 +6,9 @@
 // choice was dropped gets 0).
 //
 // Each thread owns a VEC-wide column slice of one token row: it reads the k
-// expert rows of that token (stored contiguously, assignment-major; bf16 or
-// fp32), accumulates in fp32 in choice order and rounds once to the output
+// expert rows of that token (stored contiguously, assignment-major; bf16,
+// fp32, or the compact fp16 rows with a shift per group of columns that the
+// fused layer writes), accumulates in fp32 in choice order and rounds once to the output
 // type. A pure streaming kernel: k*d*sizeof(Y) bytes read per token and
 // d*sizeof(out) bytes written. Rows are read 8 columns at a time (16 bytes of
 // bf16, 32 of fp32). The slots and gates of a group of choices (8 for fp32
@@ -120,6 +121,78 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ Y,
     }
 }
 
+// The same combine over compact rows of Y (the fused layer's own format):
+// VEC columns per thread (16: as many bytes per choice as 8 fp32 columns),
+// the slots and gates of 8 choices loaded together, then their kept rows
+// and shifts, accumulated in choice order. The rows stay fp16 in registers
+// until they are added (half the registers of fp32 rows).
+template <bool BF16, int VEC>
+__global__ __launch_bounds__(256) void combine_compact_kernel(
+    const unsigned short *__restrict__ Y, const signed char *__restrict__ ysh,
+    const float *__restrict__ gate, const int32_t *__restrict__ slot, int64_t N, int d, int k,
+    void *__restrict__ out) {
+    static_assert(VEC % 8 == 0 && kYGroup % VEC == 0, "16-byte loads within one group");
+    constexpr int kGroup = 8;
+    const int cols = d / VEC;
+    const int G = (d + kYGroup - 1) / kYGroup;
+    const int64_t total = N * cols;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = i / cols;
+        const int c = (int)(i - t * cols) * VEC;
+        float acc[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+            acc[v] = 0.f;
+        for (int j0 = 0; j0 < k; j0 += kGroup) {
+            bool kept[kGroup];
+            float g[kGroup], sc[kGroup];
+            u32x4 raw[kGroup][VEC / 8];
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                const int64_t a = t * k + (j0 + u < k ? j0 + u : k - 1);
+                kept[u] = j0 + u < k && slot[a] >= 0;
+                g[u] = gate[a];
+            }
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u)
+                if (kept[u]) {
+                    const int64_t a = t * k + j0 + u;
+#pragma unroll
+                    for (int q = 0; q < VEC / 8; ++q)
+                        raw[u][q] = *reinterpret_cast<const u32x4 *>(Y + a * d + c + 8 * q);
+                    sc[u] = pow2f(-(int)ysh[a * G + c / kYGroup]);
+                }
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u)
+                if (kept[u]) {
+#pragma unroll
+                    for (int q = 0; q < VEC / 8; ++q)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const f32x2_t p = unpack_f16x2(raw[u][q][i]);
+                            acc[8 * q + 2 * i] += g[u] * (p[0] * sc[u]);
+                            acc[8 * q + 2 * i + 1] += g[u] * (p[1] * sc[u]);
+                        }
+                }
+        }
+#pragma unroll
+        for (int q = 0; q < VEC / 8; ++q) {
+            const float *a8 = acc + 8 * q;
+            if (BF16) {
+                unsigned short *o = static_cast<unsigned short *>(out) + t * d + c + 8 * q;
+                *reinterpret_cast<u32x4 *>(o) =
+                    u32x4{pack_bf16x2(a8[0], a8[1]), pack_bf16x2(a8[2], a8[3]),
+                          pack_bf16x2(a8[4], a8[5]), pack_bf16x2(a8[6], a8[7])};
+            } else {
+                float *o = static_cast<float *>(out) + t * d + c + 8 * q;
+                *reinterpret_cast<f32x4 *>(o) = f32x4{a8[0], a8[1], a8[2], a8[3]};
+                *reinterpret_cast<f32x4 *>(o + 4) = f32x4{a8[4], a8[5], a8[6], a8[7]};
+            }
+        }
+    }
+}
+
 template <typename YT, bool BF16, int VEC>
 hipError_t launch(const void *Y, const float *gate, const int32_t *slot, int64_t N, int64_t d,
                   int k, void *out, hipStream_t s) {
@@ -140,6 +213,29 @@ hipError_t launch_out(const void *Y, const float *gate, const int32_t *slot, int
 }
 
 }  // namespace
+
+hipError_t launch_combine_compact(const void *Y, const signed char *ysh, const float *gate,
+                                  const int32_t *slot, int64_t N, int64_t d, int k, void *out,
+                                  int out_dtype, hipStream_t s) {
+    if (N == 0 || d == 0)
+        return hipSuccess;
+    if (d % 8 != 0)
+        return hipErrorInvalidValue;
+    auto go = [&](auto kern, int vec) {
+        int64_t blocks = (N * (d / vec) + 255) / 256;
+        if (blocks > 65536)
+            blocks = 65536;
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s,
+                           static_cast<const unsigned short *>(Y), ysh, gate, slot, N, (int)d, k,
+                           out);
+        return hipGetLastError();
+    };
+    if (d % 16 == 0)
+        return out_dtype == 1 ? go(combine_compact_kernel<true, 16>, 16)
+                              : go(combine_compact_kernel<false, 16>, 16);
+    return out_dtype == 1 ? go(combine_compact_kernel<true, 8>, 8)
+                          : go(combine_compact_kernel<false, 8>, 8);
+}
 
 hipError_t launch_combine(const void *Y, int y_dtype, const float *gate, const int32_t *slot,
                           int64_t N, int64_t d, int k, void *out, int out_dtype, hipStream_t s) {

@@ -40,6 +40,39 @@ __device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {
     return __builtin_bit_cast(float, (unsigned int)b << 16);
 }
 
+// Compact expert output rows (the fused entry points of bf16 layers): each
+// group of kYGroup columns of a row of Y is stored as the fp16 values of
+// y * 2^sh with one exponent shift sh (int8) per group, sh chosen from the
+// group's largest finite magnitude m so that m * 2^sh lies in [2^14, 2^15).
+// Scaling by a power of two is exact, so every value keeps fp16's 11
+// significant bits (relative error at most 2^-11, round to nearest even),
+// none can overflow, and values below m * 2^-28 (fp16 subnormals) lose at
+// most m * 2^-39. Infinities and NaNs pass through. y' = fp16 * 2^-sh.
+constexpr int kYGroup = 32;
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// 2^s as an fp32 bit pattern, s in [-126, 127]
+__device__ __forceinline__ float pow2f(int s) {
+    return __uint_as_float((unsigned)(127 + s) << 23);
+}
+// Shift of a group whose largest finite magnitude is m (>= 0): 141 - the
+// biased exponent of m, at most 126 (m = 0 or below 2^-112), so that both
+// 2^sh and 2^-sh are normal fp32 values.
+__device__ __forceinline__ int yshift_of(float m) {
+    const int sh = 141 - (int)((__float_as_uint(m) >> 23) & 0xffu);
+    return sh > 126 ? 126 : sh;
+}
+// acc raised to |v| when v is finite (NaN and infinities are ignored).
+__device__ __forceinline__ float finite_max(float acc, float v) {
+    const float a = fabsf(v);
+    return a < __builtin_inff() ? fmaxf(acc, a) : acc;
+}
+__device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
+}
+__device__ __forceinline__ f32x2_t unpack_f16x2(unsigned w) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
+}
+
 // Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC 2011): ten rounds on a 4 x 64-bit counter; a round
 // takes the 128-bit products of counter words 0 and 2 with the two round
@@ -147,12 +180,15 @@ hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t 
                             const int32_t *slot_token, const int32_t *tiles, void *H,
                             int64_t rows_per_expert, void *part, size_t part_bytes, int act,
                             const float *b_up, hipStream_t s, void *Z = nullptr);
-// dp: training-mode dropout on the rows of Y (default: none).
+// dp: training-mode dropout on the rows of Y (default: none). ysh (bf16
+// layers): when not NULL, Y is written compact, fp16 [N*k, d] with the
+// shifts in ysh [N*k][ceil(d / kYGroup)]; otherwise Y is fp32 [N*k, d].
 hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int64_t d,
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, void *Y,
                               int64_t rows_per_expert, void *part, size_t part_bytes,
-                              const float *b_down, hipStream_t s, Dropout dp = Dropout{});
+                              const float *b_down, hipStream_t s, Dropout dp = Dropout{},
+                              signed char *ysh = nullptr);
 
 // Name of the kernel instantiation the expert product `product` (0: up, 1:
 // down, with or without the dropout) launches for these sizes, as a profiler
@@ -192,11 +228,13 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
 
 // Backward element-wise and layout kernels (backward.hip).
 // dY rows (bf16, kept choices) = gate * dout; ds [N, k] = gate * (dg - sum gate*dg)
-// with dg = <dout, Y> (Y: the experts' fp32 outputs, assignment-major). d % 8 == 0.
+// with dg = <dout, Y> (Y: the experts' outputs, assignment-major, fp32 or,
+// with ysh, compact as launch_expert_down writes them). d % 8 == 0.
 // With dropout, dY = gate * dout * (the dropout factor of each Y element).
-hipError_t launch_combine_backward(const void *dout, const void *Y, const float *gate,
-                                   const int32_t *slot, int64_t N, int64_t d, int k, void *dY,
-                                   float *ds, hipStream_t s, Dropout dp = Dropout{});
+hipError_t launch_combine_backward(const void *dout, const void *Y, const signed char *ysh,
+                                   const float *gate, const int32_t *slot, int64_t N, int64_t d,
+                                   int k, void *dY, float *ds, hipStream_t s,
+                                   Dropout dp = Dropout{});
 // dsT3 [S][E][3*Tc] bf16: exact three-term split of ds(s*Tc + i, e) at columns
 // i, Tc + i, 2*Tc + i (tokens chunked by Tc).
 hipError_t launch_ds_split(const float *ds, const int32_t *idx, int64_t N, int64_t Tc, int64_t S,
@@ -239,5 +277,10 @@ hipError_t launch_router_scores_bf16(const void *x, const void *wsp, int64_t N, 
 hipError_t launch_combine(const void *Y, int y_dtype, const float *gate, const int32_t *slot,
                           int64_t N, int64_t d, int k, void *out, int out_dtype,
                           hipStream_t s);
+// The same over compact rows: Y fp16 [N*k, d] with shifts ysh [N*k][ceil(d /
+// kYGroup)] (see kYGroup); d % 8 == 0.
+hipError_t launch_combine_compact(const void *Y, const signed char *ysh, const float *gate,
+                                  const int32_t *slot, int64_t N, int64_t d, int k, void *out,
+                                  int out_dtype, hipStream_t s);
 
 }  // namespace moe

@@ -341,6 +341,9 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // row (MODE 1), or NULL. K-range partials take neither (the fix-up does).
 // Z16 (MODE 0): when not NULL, the bf16 pre-activations (product plus bias)
 // are stored there too, [E, ceff, Nout] like H (by the fix-up for cut tiles).
+// ysh (MODES 1, 5): when not NULL, the rows of Y are stored compact (fp16
+// values into O16 and one exponent shift per kYGroup columns into ysh,
+// [rows of Y][ceil(Nout / kYGroup)]) instead of fp32 into O32.
 // 5: MODE 1 with training-mode dropout dp on the rows of Y, after the bias
 // (its own instantiation, so that the plain down product's epilogue carries
 // none of the generator's code or registers).
@@ -373,7 +376,8 @@ void expert_gemm_kernel(
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
     unsigned short *__restrict__ O16, float *__restrict__ O32, float *__restrict__ part,
     int P, int act, const float *__restrict__ bias, const unsigned short *mask,
-    unsigned short *__restrict__ Z16, Dropout dp, int64_t bsa, int64_t bsb, int64_t bsc) {
+    unsigned short *__restrict__ Z16, Dropout dp, int64_t bsa, int64_t bsb, int64_t bsc,
+    signed char *__restrict__ ysh) {
     constexpr int WMN = WAVES_M * WAVES_N;                   // waves of one K set
     constexpr int NW = WMN * WAVES_K;
     constexpr int NTHR = NW * 64;
@@ -925,10 +929,14 @@ void expert_gemm_kernel(
                 else
                     store_h(std::false_type{});
             } else if (MODE == 1 || MODE == 5) {
-                // fp32 row of Y at the assignment's position
+                // the row of Y at the assignment's position: fp32, or compact
+                // (the lanes of a kYGroup-column group hold the same row, so
+                // they all take this branch and agree on the group's shift)
+                static_assert(!(MODE == 1 || MODE == 5) || kYGroup % CPL == 0,
+                              "a lane's columns lie in one group of Y");
                 const int64_t arow = (int64_t)slot_token[srow];
-                float *dst = O32 + arow * Nout + nb;
                 const float *bp = bias ? bias + (int64_t)e * Nout + nb : nullptr;
+                float amax = 0.f;
 #pragma unroll
                 for (int h = 0; h < CPL / 8; ++h) {
                     if (nb + 8 * h + 8 <= Nout) {
@@ -944,8 +952,42 @@ void expert_gemm_kernel(
                             z0 *= f32x4{m[0], m[1], m[2], m[3]};
                             z1 *= f32x4{m[4], m[5], m[6], m[7]};
                         }
-                        *reinterpret_cast<f32x4 *>(dst + 8 * h) = z0;
-                        *reinterpret_cast<f32x4 *>(dst + 8 * h + 4) = z1;
+                        v[2 * h] = z0;
+                        v[2 * h + 1] = z1;
+                        if (ysh) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                amax = finite_max(finite_max(amax, z0[q]), z1[q]);
+                        }
+                    }
+                }
+                if (ysh) {
+#pragma unroll
+                    for (int o = 1; o < kYGroup / CPL; o <<= 1)
+                        amax = fmaxf(amax, __shfl_xor(amax, o));
+                    const int sh = yshift_of(amax);
+                    const float sc = pow2f(sh);
+                    unsigned short *dst = O16 + arow * Nout + nb;
+#pragma unroll
+                    for (int h = 0; h < CPL / 8; ++h) {
+                        if (nb + 8 * h + 8 <= Nout) {
+                            const f32x4 z0 = v[2 * h] * sc, z1 = v[2 * h + 1] * sc;
+                            *reinterpret_cast<u32x4 *>(dst + 8 * h) =
+                                u32x4{pack_f16x2(z0[0], z0[1]), pack_f16x2(z0[2], z0[3]),
+                                      pack_f16x2(z1[0], z1[1]), pack_f16x2(z1[2], z1[3])};
+                        }
+                    }
+                    if (nb % kYGroup == 0 && nb < Nout)   // (groups past Nout: none)
+                        ysh[arow * ((Nout + kYGroup - 1) / kYGroup) + nb / kYGroup] =
+                            (signed char)sh;
+                } else {
+                    float *dst = O32 + arow * Nout + nb;
+#pragma unroll
+                    for (int h = 0; h < CPL / 8; ++h) {
+                        if (nb + 8 * h + 8 <= Nout) {
+                            *reinterpret_cast<f32x4 *>(dst + 8 * h) = v[2 * h];
+                            *reinterpret_cast<f32x4 *>(dst + 8 * h + 4) = v[2 * h + 1];
+                        }
                     }
                 }
             } else if (MODE == 3) {
@@ -996,7 +1038,7 @@ void expert_gemm_kernel(
 
 // Sum of the K-range partials of the cut tiles, in K order, then the same
 // epilogue as a whole tile (MODE 0: bias, activation, bf16 H; MODE 1: bias,
-// dropout, fp32 row of Y).
+// dropout, the row of Y, fp32 or compact when ysh is given).
 // One workgroup per 16-row strip of a cut tile; 4 columns per thread.
 template <int BM, int BN, int BKT, int MODE>
 __global__ __launch_bounds__(256) void split_fixup_kernel(
@@ -1004,8 +1046,9 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
     const float *__restrict__ part, int P, unsigned short *__restrict__ O16,
     float *__restrict__ O32, int act, const float *__restrict__ bias, Dropout dp,
-    unsigned short *__restrict__ Z16) {
+    unsigned short *__restrict__ Z16, signed char *__restrict__ ysh) {
     constexpr int STRIPS = BM / 16;
+    static_assert((BN / 4) % (kYGroup / 4) == 0, "a group of Y lies in one row of threads");
     __shared__ int s_mt[kMaxExperts + 1];
     __shared__ int s_pp[kMaxExperts + 1];
     __shared__ uint64_t s_msk[kMaxExperts / 64];
@@ -1027,12 +1070,48 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
     int e, m0, n0;
     decode_tile(sp.Tdp + t, s_mt, ll ? s_pp : nullptr, E, NT, BM, BN, e, m0, n0);
     const int rows = used[e];
+    static_assert((16 * (BN / 4)) % 256 == 0, "every thread takes every trip");
     for (int i = threadIdx.x; i < 16 * (BN / 4); i += 256) {
         const int rr = i / (BN / 4), c4 = i % (BN / 4);
         const int tr = strip * 16 + rr;
         const int r = m0 + tr;
         const int n = n0 + 4 * c4;
-        if (r >= rows || n + 4 > Nout)
+        const bool ok = r < rows && n + 4 <= Nout;
+        if (MODE == 1 && ysh) {
+            // compact row of Y: the kYGroup / 4 threads of a group (adjacent
+            // lanes of one row) agree on its shift; all of them take part
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            int64_t orow = 0;
+            if (ok) {
+                const float *src = part + ((int64_t)t * sp.nsplit * BM + tr) * BN + 4 * c4;
+                v = *reinterpret_cast<const f32x4 *>(src);
+                for (int s = 1; s < sp.nsplit; ++s)
+                    v += *reinterpret_cast<const f32x4 *>(src + (int64_t)s * BM * BN);
+                if (bias)
+                    v += *reinterpret_cast<const f32x4 *>(bias + (int64_t)e * Nout + n);
+                orow = (int64_t)slot_token[(int64_t)e * ceff + r];
+                if (dp.on) {
+                    float m[8];
+                    dropout_factors8(dp, orow, n / 8, m);
+                    const int o = n % 8;
+                    v *= f32x4{m[o], m[o + 1], m[o + 2], m[o + 3]};
+                }
+            }
+            float amax = finite_max(finite_max(finite_max(finite_max(0.f, v[0]), v[1]), v[2]), v[3]);
+#pragma unroll
+            for (int o = 1; o < kYGroup / 4; o <<= 1)
+                amax = fmaxf(amax, __shfl_xor(amax, o));
+            if (ok) {
+                const int sh = yshift_of(amax);
+                const f32x4 z = v * pow2f(sh);
+                *reinterpret_cast<u32x2 *>(O16 + orow * Nout + n) =
+                    u32x2{pack_f16x2(z[0], z[1]), pack_f16x2(z[2], z[3])};
+                if (n % kYGroup == 0)
+                    ysh[orow * ((Nout + kYGroup - 1) / kYGroup) + n / kYGroup] = (signed char)sh;
+            }
+            continue;
+        }
+        if (!ok)
             continue;
         const float *src = part + ((int64_t)t * sp.nsplit * BM + tr) * BN + 4 * c4;
         f32x4 v = *reinterpret_cast<const f32x4 *>(src);
@@ -1205,7 +1284,7 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
                         float *part, size_t part_bytes, int act, const float *bias,
                         hipStream_t s, const unsigned short *mask = nullptr,
                         float *O32 = nullptr, unsigned short *Z16 = nullptr,
-                        Dropout dp = Dropout{}) {
+                        Dropout dp = Dropout{}, signed char *ysh = nullptr) {
     auto kern = expert_gemm_kernel<BM, BN, WM, WN, WK, BKT, S, MODE>;
     constexpr int NTHR = WM * WN * WK * 64;
     int P = resident_blocks(kern, NTHR);
@@ -1228,14 +1307,14 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
                          (split ? (int64_t)(P + kXcds - 1) / kXcds * kXcds : 0);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHR), 0, s, A, W, (int)K, (int)Nout, E,
                        k, (int)ceff, used, slot_token, mt, O16, O32, split ? part : nullptr,
-                       P, act, bias, mask, Z16, dp, (int64_t)0, (int64_t)0, (int64_t)0);
+                       P, act, bias, mask, Z16, dp, (int64_t)0, (int64_t)0, (int64_t)0, ysh);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !split)
         return err;
     hipLaunchKernelGGL((split_fixup_kernel<BM, BN, BKT, MODE == 0 ? 0 : 1>),
                        dim3((unsigned)(P * (BM / 16))),
                        dim3(256), 0, s, (int)K, (int)Nout, E, (int)ceff, used, slot_token, mt,
-                       (const float *)part, P, O16, O32, act, bias, dp, Z16);
+                       (const float *)part, P, O16, O32, act, bias, dp, Z16, ysh);
     return hipGetLastError();
 }
 
@@ -1285,13 +1364,13 @@ hipError_t launch_gemm(Tile t, const unsigned short *A, const unsigned short *W,
                        void *part, size_t part_bytes, int act, const float *bias,
                        hipStream_t s, const unsigned short *mask = nullptr,
                        float *O32 = nullptr, unsigned short *Z16 = nullptr,
-                       Dropout dp = Dropout{}) {
+                       Dropout dp = Dropout{}, signed char *ysh = nullptr) {
     float *pf = static_cast<float *>(part);
     return with_tile<MODE>(t, tiles, E, [&](auto c, const int32_t *tt) {
         using C = decltype(c);
         return launch_tiles<C::BM, C::BN, C::WM, C::WN, C::WK, C::BKT, MODE, C::S>(
             A, W, K, Nout, E, k, ceff, used, slot_token, tt, O16, pf, part_bytes, act, bias, s,
-            mask, O32, Z16, dp);
+            mask, O32, Z16, dp, ysh);
     });
 }
 
@@ -1326,7 +1405,7 @@ hipError_t launch_router_scores_bf16(const void *x, const void *wsp, int64_t N, 
                        (const int32_t *)nullptr, (unsigned short *)nullptr, P, (float *)nullptr,
                        0, kActRelu, (const float *)nullptr, (const unsigned short *)nullptr,
                        (unsigned short *)nullptr, Dropout{}, d,
-                       (int64_t)router_terms_interleaved(d), N * Ep);
+                       (int64_t)router_terms_interleaved(d), N * Ep, (signed char *)nullptr);
     return hipGetLastError();
 }
 
@@ -1359,21 +1438,27 @@ hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int6
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, void *Y,
                               int64_t rows_per_expert, void *part, size_t part_bytes,
-                              const float *b_down, hipStream_t s, Dropout dp) {
+                              const float *b_down, hipStream_t s, Dropout dp,
+                              signed char *ysh) {
     if (ceff == 0)
         return hipSuccess;
+    if (ysh && !bf16)
+        return hipErrorInvalidValue;   // compact rows are for bf16 layers only
+    // compact rows: fp16 values through O16, fp32 rows through O32
+    unsigned short *y16 = ysh ? static_cast<unsigned short *>(Y) : nullptr;
+    float *y32 = ysh ? nullptr : static_cast<float *>(Y);
     if (bf16 && dp.on)
         return launch_gemm<5>(pick_tile(rows_per_expert, d, E),
                               static_cast<const unsigned short *>(H),
                               static_cast<const unsigned short *>(w_down), d_ff, d, E, k, ceff,
-                              used, slot_token, tiles, nullptr, part, part_bytes, kActRelu,
-                              b_down, s, nullptr, static_cast<float *>(Y), nullptr, dp);
+                              used, slot_token, tiles, y16, part, part_bytes, kActRelu,
+                              b_down, s, nullptr, y32, nullptr, dp, ysh);
     if (bf16)
         return launch_gemm<1>(pick_tile(rows_per_expert, d, E),
                               static_cast<const unsigned short *>(H),
                               static_cast<const unsigned short *>(w_down), d_ff, d, E, k, ceff,
-                              used, slot_token, tiles, nullptr, part, part_bytes, kActRelu,
-                              b_down, s, nullptr, static_cast<float *>(Y));
+                              used, slot_token, tiles, y16, part, part_bytes, kActRelu,
+                              b_down, s, nullptr, y32, nullptr, Dropout{}, ysh);
     hipLaunchKernelGGL(experts_f32_kernel<1>,
                        dim3((unsigned)((d + 63) / 64), (unsigned)((ceff + 63) / 64), E),
                        dim3(256), 0, s, static_cast<const float *>(H),
@@ -1449,7 +1534,8 @@ hipError_t launch_weight_grad(const void *A, int64_t M, const void *B, int64_t N
                            E, kdiv, (int)ceff, used, slot_token, (const int32_t *)nullptr,
                            (unsigned short *)nullptr, out, (float *)nullptr, 0, gathered,
                            (const float *)nullptr, (const unsigned short *)nullptr,
-                           (unsigned short *)nullptr, Dropout{}, M, (int64_t)0, M * N);
+                           (unsigned short *)nullptr, Dropout{}, M, (int64_t)0, M * N,
+                           (signed char *)nullptr);
         return hipGetLastError();
     }
     const int64_t grid = (((M + 127) / 128) * ((N + 127) / 128) + kXcds - 1) / kXcds * kXcds;
@@ -1458,7 +1544,8 @@ hipError_t launch_weight_grad(const void *A, int64_t M, const void *B, int64_t N
                        kdiv, (int)ceff, used, slot_token, (const int32_t *)nullptr,
                        (unsigned short *)nullptr, out, (float *)nullptr, 0, gathered,
                        (const float *)nullptr, (const unsigned short *)nullptr,
-                       (unsigned short *)nullptr, Dropout{}, M, (int64_t)0, M * N);
+                       (unsigned short *)nullptr, Dropout{}, M, (int64_t)0, M * N,
+                           (signed char *)nullptr);
     return hipGetLastError();
 }
 
@@ -1480,7 +1567,7 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
                            (const int32_t *)nullptr, (const int32_t *)nullptr,
                            (unsigned short *)nullptr, C, (float *)nullptr, 0, kActRelu,
                            (const float *)nullptr, (const unsigned short *)nullptr,
-                           (unsigned short *)nullptr, Dropout{}, sa, sb, sc);
+                           (unsigned short *)nullptr, Dropout{}, sa, sb, sc, (signed char *)nullptr);
         return hipGetLastError();
     }
     const int64_t grid = (((M + 127) / 128) * ((Nout + 127) / 128) + kXcds - 1) / kXcds * kXcds;
@@ -1490,7 +1577,7 @@ hipError_t launch_batched_gemm_bf16(const void *A, const void *W, int64_t M, int
                        (const int32_t *)nullptr, (const int32_t *)nullptr,
                        (unsigned short *)nullptr, C, (float *)nullptr, 0, kActRelu,
                        (const float *)nullptr, (const unsigned short *)nullptr,
-                           (unsigned short *)nullptr, Dropout{}, sa, sb, sc);
+                           (unsigned short *)nullptr, Dropout{}, sa, sb, sc, (signed char *)nullptr);
     return hipGetLastError();
 }
 

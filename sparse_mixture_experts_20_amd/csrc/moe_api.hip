@@ -39,8 +39,19 @@ struct Dims {
 
 // Workspace regions (byte offsets from the base).
 struct Layout {
-    size_t idx, gate, slot, used, tiles, slot_token, H, Y, router, dispatch, part, total;
+    size_t idx, gate, slot, used, tiles, slot_token, H, Y, Ysh, router, dispatch, part, total;
 };
+
+// Expert output rows of the fused entry points: compact for bf16 layers (fp16
+// values and one int8 exponent shift per kYGroup columns), fp32 otherwise.
+size_t y_bytes(size_t nk, int64_t d, int32_t dtype) {
+    return align_up(nk * (size_t)d * (dtype == MOE_BF16 ? 2 : 4));
+}
+size_t ysh_bytes(size_t nk, int64_t d, int32_t dtype) {
+    return dtype == MOE_BF16
+               ? align_up(nk * (size_t)((d + moe::kYGroup - 1) / moe::kYGroup))
+               : 0;
+}
 
 // Router scratch: the bf16 split of W_g (and partial scores for many experts).
 size_t router_bytes(int64_t N, int64_t d, int64_t E, int32_t dtype) {
@@ -63,7 +74,8 @@ Layout layout_of(const Dims &m) {
     L.tiles = o;      o += align_up((size_t)(2 * (m.E + 1)) * 4);
     L.slot_token = o; o += align_up((size_t)(m.E * m.ceff) * 4);
     L.H = o;          o += align_up((size_t)(m.E * m.ceff * m.d_ff) * dtype_size(m.dtype));
-    L.Y = o;          o += align_up(nk * (size_t)m.d * 4);   // fp32 expert output rows
+    L.Y = o;          o += y_bytes(nk, m.d, m.dtype);   // expert output rows
+    L.Ysh = o;        o += ysh_bytes(nk, m.d, m.dtype);
     L.router = o;     o += router_bytes(m.N, m.d, m.E, m.dtype);
     L.dispatch = o;   o += align_up(moe::dispatch_workspace_bytes(m.N, (int)m.E, m.k));
     L.part = o;       o += expert_bytes(m.dtype);
@@ -74,7 +86,7 @@ Layout layout_of(const Dims &m) {
 // Workspace of the backward pass (bf16 layers): the recomputed forward state
 // and the gradient intermediates.
 struct BwdLayout {
-    size_t idx, gate, slot, used, tiles, slot_token, H, Y, dY, ds, dZ, dXa, T1, T2, dsT3,
+    size_t idx, gate, slot, used, tiles, slot_token, H, Y, Ysh, dY, ds, dZ, dXa, T1, T2, dsT3,
         xT3, gpart, router, dispatch, part, total;
     int64_t Kp, Tc, S;
 };
@@ -108,7 +120,8 @@ BwdLayout bwd_layout_of(const Dims &m) {
     L.tiles = o;      o += align_up((size_t)(2 * (m.E + 1)) * 4);
     L.slot_token = o; o += align_up((size_t)(m.E * m.ceff) * 4);
     L.H = o;          o += align_up((size_t)(m.E * m.ceff * m.d_ff) * 2);
-    L.Y = o;          o += align_up(nk * (size_t)m.d * 4);   // fp32 expert output rows
+    L.Y = o;          o += y_bytes(nk, m.d, m.dtype);   // compact expert output rows
+    L.Ysh = o;        o += ysh_bytes(nk, m.d, m.dtype);
     L.dY = o;         o += align_up(nk * (size_t)m.d * 2);
     L.ds = o;         o += align_up(nk * 4);
     L.dZ = o;         o += align_up((size_t)(m.E * m.ceff * m.d_ff) * 2);
@@ -299,7 +312,7 @@ int check_expert_ws(const void *ws) {
 
 // The forward state the backward needs, in the backward's workspace layout:
 // routing (into the exported arrays when given), dispatch plan, H, the
-// experts' fp32 output rows Y (bias and dropout applied) and, for GELU, the
+// experts' compact output rows Y (bias and dropout applied) and, for GELU, the
 // bf16 pre-activations (in the dZ region, which the dZ product overwrites).
 static int forward_state(const BwdLayout &L, char *ws, const moe_tensor *x,
                          const moe_tensor *W_g, const moe_tensor *noise, const moe_tensor *W_up,
@@ -566,7 +579,8 @@ int moe_expert_up_ex(const moe_tensor *x, const moe_tensor *W_up, const moe_expe
 static int expert_down_impl(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
                             const int32_t *used, const int32_t *slot_token,
                             const int32_t *tiles, const void *H, void *Y, void *workspace,
-                            size_t workspace_bytes, void *stream, const ExpertOpts &o) {
+                            size_t workspace_bytes, void *stream, const ExpertOpts &o,
+                            int8_t *ysh = nullptr, bool compact = false) {
     if (!W_down)
         return MOE_ERR_NULL;
     if (!valid_dtype(W_down->dtype))
@@ -582,9 +596,11 @@ static int expert_down_impl(int64_t N, const moe_tensor *W_down, int k, int64_t 
         return rc;
     if (N == 0)
         return MOE_OK;
-    if (!W_down->data || !used || !slot_token || !tiles || !H || !Y)
+    if (!W_down->data || !used || !slot_token || !tiles || !H || !Y || (compact && !ysh))
         return MOE_ERR_NULL;
     const bool bf16 = W_down->dtype == MOE_BF16;
+    if (compact && !bf16)
+        return MOE_ERR_DTYPE;
     if (bf16 && (!aligned(W_down->data, 16) || !aligned(H, 16) || !aligned(Y, 16)))
         return MOE_ERR_ALIGN;
     rc = check_expert_ws(workspace);
@@ -594,7 +610,26 @@ static int expert_down_impl(int64_t N, const moe_tensor *W_down, int k, int64_t 
                                               used, slot_token, tiles, Y,
                                               rows_per_expert(N, k, E, m.ceff), workspace,
                                               workspace ? workspace_bytes : 0, o.b_down,
-                                              static_cast<hipStream_t>(stream), o.drop));
+                                              static_cast<hipStream_t>(stream), o.drop,
+                                              compact ? reinterpret_cast<signed char *>(ysh)
+                                                      : nullptr));
+}
+
+int moe_expert_down_compact(int64_t N, const moe_tensor *W_down, const moe_expert_opts *opts,
+                            int k, int64_t capacity, const int32_t *used,
+                            const int32_t *slot_token, const int32_t *tiles, const void *H,
+                            void *Y16, int8_t *Ysh, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    if (!W_down)
+        return MOE_ERR_NULL;
+    if (W_down->ndim != 3)
+        return MOE_ERR_SHAPE;
+    ExpertOpts o;
+    const int rc = check_opts(opts, W_down->shape[0], W_down->shape[1], W_down->shape[2], o);
+    if (rc != MOE_OK)
+        return rc;
+    return expert_down_impl(N, W_down, k, capacity, used, slot_token, tiles, H, Y16, workspace,
+                            workspace_bytes, stream, o, Ysh, true);
 }
 
 int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity,
@@ -692,6 +727,31 @@ int moe_combine(int64_t N, int64_t d, int k, const moe_tensor *Y, const float *t
                                           static_cast<hipStream_t>(stream)));
 }
 
+int moe_combine_compact(int64_t N, int64_t d, int k, const void *Y16, const int8_t *Ysh,
+                        const float *topk_gate, const int32_t *slot, moe_tensor *out,
+                        void *stream) {
+    if (!out)
+        return MOE_ERR_NULL;
+    if (N < 0 || d <= 0 || k < 1 || k > MOE_MAX_TOPK)
+        return MOE_ERR_ARG;
+    int64_t oN, od;
+    if (!act_rows(out, oN, od) || oN != N || od != d)
+        return MOE_ERR_SHAPE;
+    if (!valid_dtype(out->dtype))
+        return MOE_ERR_DTYPE;
+    if (d % 8 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    if (N == 0)
+        return MOE_OK;
+    if (!Y16 || !Ysh || !topk_gate || !slot || !out->data)
+        return MOE_ERR_NULL;
+    if (!aligned(Y16, 16) || !aligned(out->data, 16))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_combine_compact(Y16, reinterpret_cast<const signed char *>(Ysh),
+                                                  topk_gate, slot, N, d, k, out->data,
+                                                  out->dtype, static_cast<hipStream_t>(stream)));
+}
+
 int moe_forward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
                    const moe_tensor *W_up, const moe_tensor *W_down,
                    const moe_expert_opts *opts, int k, float capacity_factor, moe_tensor *out,
@@ -757,7 +817,8 @@ int moe_forward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor 
     int32_t *tiles = reinterpret_cast<int32_t *>(ws + L.tiles);
     int32_t *slot_token = reinterpret_cast<int32_t *>(ws + L.slot_token);
     void *H = ws + L.H;
-    void *Y = ws + L.Y;   // expert outputs, fp32
+    void *Y = ws + L.Y;   // expert outputs: compact (bf16 layers) or fp32
+    signed char *ysh = x->dtype == MOE_BF16 ? reinterpret_cast<signed char *>(ws + L.Ysh) : nullptr;
     stats->capacity = m.C;
 
     rc = router_checked(x, W_g, noise, N, d, E, k, idx, gate, ws + L.router, s);
@@ -774,8 +835,12 @@ int moe_forward_ex(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor 
                                   slot_token, tiles, H, rpe, part, part_bytes, o.act, o.b_up, s));
     MOE_TRY(moe::launch_expert_down(bf16, H, W_down->data, d, d_ff, (int)E, k, m.ceff, used,
                                     slot_token, tiles, Y, rpe, part, part_bytes, o.b_down, s,
-                                    o.drop));
-    MOE_TRY(moe::launch_combine(Y, 0, gate, slot, N, d, k, out->data, out->dtype, s));
+                                    o.drop, ysh));
+    if (ysh)
+        MOE_TRY(moe::launch_combine_compact(Y, ysh, gate, slot, N, d, k, out->data, out->dtype,
+                                            s));
+    else
+        MOE_TRY(moe::launch_combine(Y, 0, gate, slot, N, d, k, out->data, out->dtype, s));
     return MOE_OK;
 }
 
@@ -967,7 +1032,7 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
     const int64_t rpe = rows_per_expert(N, k, E, ceff);
     const int Ei = (int)E;
 
-    // forward state: routing, plan, H and the experts' fp32 outputs
+    // forward state: routing, plan, H and the experts' output rows
     const bool gelu = o.act == moe::kActGelu;
     if (!saved) {
         rc = forward_state(L, ws, x, W_g, noise, W_up, W_down, o, m, stats, s);
@@ -976,8 +1041,9 @@ static int backward_call(const moe_tensor *x, const moe_tensor *W_g, const moe_t
     }
     // combine and softmax backward; router weights: dW_g = ds^T x, per token
     // chunk on the exact split of ds, then the chunks summed in order
-    MOE_TRY(moe::launch_combine_backward(dout->data, Y, gate, slot, N, d, k, dY, ds, s,
-                                         o.drop));
+    MOE_TRY(moe::launch_combine_backward(dout->data, Y,
+                                         reinterpret_cast<const signed char *>(ws + L.Ysh), gate,
+                                         slot, N, d, k, dY, ds, s, o.drop));
     // fork: the aux stream s2 takes the router-weight gradient and (when the
     // products read K-major) the down-projection weight gradient; both read
     // only the forward state, ds and dY, and write buffers of their own. The
@@ -1119,8 +1185,9 @@ int moe_forward_train(const moe_tensor *x, const moe_tensor *W_g, const moe_tens
     const float *gate = stats->topk_gate ? stats->topk_gate
                                          : reinterpret_cast<const float *>(ws + L.gate);
     const int32_t *slot = stats->slot ? stats->slot : reinterpret_cast<const int32_t *>(ws + L.slot);
-    return hip_status(moe::launch_combine(ws + L.Y, 0, gate, slot, N, d, k, out->data,
-                                          out->dtype, s));
+    return hip_status(moe::launch_combine_compact(
+        ws + L.Y, reinterpret_cast<const signed char *>(ws + L.Ysh), gate, slot, N, d, k,
+        out->data, out->dtype, s));
 }
 
 int moe_backward(const moe_tensor *x, const moe_tensor *W_g, const moe_tensor *noise,
@@ -1162,6 +1229,6 @@ static int forward_state(const BwdLayout &L, char *ws, const moe_tensor *x,
                                   gelu ? ws + L.dZ : nullptr));
     MOE_TRY(moe::launch_expert_down(true, ws + L.H, W_down->data, m.d, m.d_ff, Ei, m.k, m.ceff,
                                     used, st, tiles, ws + L.Y, rpe, part, part_bytes, o.b_down, s,
-                                    o.drop));
+                                    o.drop, reinterpret_cast<signed char *>(ws + L.Ysh)));
     return MOE_OK;
 }

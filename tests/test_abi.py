@@ -205,6 +205,29 @@ def test_stage_entry_points_reject_bad_arguments(L):
                            ctypes.c_void_p(FAKE + 8), 1 << 30, None) == -7
     assert L.moe_expert_down(10, ctypes.byref(wd_ok), 2, 5, v, v, v, v, v,
                              ctypes.c_void_p(FAKE + 8), 1 << 30, None) == -7
+    # compact expert rows: the shifts are required, bf16 weights only, the
+    # same alignment rules
+    sh = ctypes.c_void_p(FAKE)
+    assert L.moe_expert_down_compact(10, ctypes.byref(wd_ok), None, 2, 5, v, v, v, v, v, None,
+                                     None, 0, None) == -1
+    wd_f32 = _t(FAKE, F32, 4, 16, 32)
+    assert L.moe_expert_down_compact(10, ctypes.byref(wd_f32), None, 2, 5, v, v, v, v, v, sh,
+                                     None, 0, None) == -3
+    assert L.moe_expert_down_compact(10, ctypes.byref(wd_ok), None, 2, 5, v, v, v, v,
+                                     ctypes.c_void_p(FAKE + 8), sh, None, 0, None) == -7
+    assert L.moe_expert_down_compact(0, ctypes.byref(wd_ok), None, 2, 5, None, None, None, None,
+                                     None, None, None, 0, None) == 0
+    # compact combine: shapes, d % 8, pointers, alignment
+    ob = _t(FAKE, BF16, 10, 16)
+    assert L.moe_combine_compact(10, 16, 2, v, sh, v, v, None, None) == -1
+    assert L.moe_combine_compact(11, 16, 2, v, sh, v, v, r(ob), None) == -2
+    assert L.moe_combine_compact(10, 12, 2, v, sh, v, v, r(_t(FAKE, BF16, 10, 12)), None) == -6
+    assert L.moe_combine_compact(10, 16, 2, v, None, v, v, r(ob), None) == -1
+    assert L.moe_combine_compact(10, 16, 2, ctypes.c_void_p(FAKE + 8), sh, v, v, r(ob),
+                                 None) == -7
+    assert L.moe_combine_compact(10, 16, 0, v, sh, v, v, r(ob), None) == -4
+    assert L.moe_combine_compact(0, 16, 2, None, None, None, None, r(_t(FAKE, BF16, 0, 16)),
+                                 None) == 0
 
 
 def test_expert_workspace_size(L):

@@ -224,6 +224,43 @@ def test_light_tiles_last_with_split(torch_mod):
     _free(torch, dev, out)
 
 
+def test_compact_rows_keep_every_magnitude(torch_mod):
+    """A bf16 layer keeps its experts' output rows as fp16 values with one
+    power-of-two shift per 32 columns. Experts whose outputs lie far above
+    fp16's range (W_down scaled by 2^24 and 2^60), far below it (2^-80,
+    2^-90) and at ordinary magnitudes share one layer whose width (d = 200)
+    leaves a partial last group of 8 columns; every token row matches the
+    oracle relative to its own largest output (a token may mix experts of
+    very different scales), and rows of ordinary magnitude within the
+    layer's absolute bound."""
+    torch = torch_mod
+    wl = W.custom("compact_range", N=600, d=200, E=6, k=2, d_ff=136, dtype="bf16", cf=1.0,
+                  sigma=0.3, seed=77, w_std=0.05)
+    scale = [2.0**24, 2.0**-90, 1.0, 2.0**60, 2.0**-80, 1.0]
+    for e in range(wl.E):
+        w = W.bf16_bits_to_f32(wl.w_down(e)) * np.float32(scale[e])   # exact: powers of two
+        wl.memo("down", e, W.f32_to_bf16_bits(w))
+    G.say("[parity] compact_range: W_down scaled by 2^24, 2^-90, 1, 2^60, 2^-80, 1")
+    res = oracle.forward(wl)
+    dev = _upload(wl)
+    out, st = G.run_forward(dev)
+    torch.cuda.synchronize()
+    G.check_routing(res, st)
+    got = G.out_f64(wl, out)
+    assert np.all(np.isfinite(got))
+    peak = np.abs(res.out).max(axis=1)
+    live = peak > 0
+    err = np.abs(got - res.out).max(axis=1)
+    assert np.all(err[live] <= 8e-3 * peak[live]), (err / np.maximum(peak, 1e-300)).max()
+    assert np.all(got[~live] == 0.0)
+    # both ends of the range are exercised, and rows of ordinary size
+    assert peak.max() > 1e15 and peak[live].min() < 1e-20
+    plain = (peak > 1e-3) & (peak < 1e3)
+    assert plain.sum() > 0
+    G.check_out("bf16", got[plain], res.out[plain])
+    _free(torch, dev, out)
+
+
 def test_forward_is_deterministic(torch_mod):
     torch = torch_mod
     wl = W.make("nanomoe")

@@ -244,14 +244,19 @@ __device__ __forceinline__ bool light_last(const int32_t *__restrict__ used, con
 }
 
 // s_mt[e] = sum over e' < e of ceil(used[e'] / BM), for e <= E: the row
-// tiles of a tile height the dispatch plan has no table for. Needs
-// nthr >= kMaxExperts; s_tmp holds one int per wave; ends with a barrier.
+// tiles of a tile height the dispatch plan has no table for (and used[e]
+// itself in s_used when given). Needs nthr >= kMaxExperts; s_tmp holds one
+// int per wave; ends with a barrier.
 __device__ __forceinline__ void row_tile_prefix(const int32_t *__restrict__ used, int E, int BM,
-                                                int *s_mt, int *s_tmp) {
+                                                int *s_mt, int *s_tmp, int *s_used = nullptr) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     int c = 0;
-    if (tid < E)
-        c = (used[tid] + BM - 1) / BM;
+    if (tid < E) {
+        const int u = used[tid];
+        c = (u + BM - 1) / BM;
+        if (s_used)
+            s_used[tid] = u;
+    }
     int inc = c;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -415,8 +420,13 @@ void expert_gemm_kernel(
     char smem[S * STAGE + (MODE == 6 ? kGradMaxRows * 4 : 0)];
     __shared__ int s_mt[kMaxExperts + 1];
     __shared__ int s_pp[kMaxExperts + 1];
+    __shared__ int s_used[kMaxExperts];   // used[], read once per workgroup
     __shared__ uint64_t s_msk[kMaxExperts / 64];
-    __shared__ int s_tok[MODE == 0 ? BM : 1];   // MODE 0: token of each tile row
+    // MODE 0: token of each tile row; 1, 4, 5: the assignment row its output
+    // goes to (read by the epilogue from LDS, so that its stores never wait
+    // behind a global load)
+    constexpr bool TOK = MODE == 0 || MODE == 1 || MODE == 4 || MODE == 5;
+    __shared__ int s_tok[TOK ? BM : 1];
     int *s_rows = reinterpret_cast<int *>(smem + S * STAGE);   // MODE 6: row of each r
 
     const int tid = threadIdx.x;
@@ -476,9 +486,11 @@ void expert_gemm_kernel(
         if (mt_off) {
             for (int i = tid; i <= E; i += NTHR)
                 s_mt[i] = mt_off[i];
+            for (int i = tid; i < E; i += NTHR)
+                s_used[i] = used[i];
             __syncthreads();
         } else {
-            row_tile_prefix(used, E, BM, s_mt, reinterpret_cast<int *>(s_msk));
+            row_tile_prefix(used, E, BM, s_mt, reinterpret_cast<int *>(s_msk), s_used);
         }
         const int T = s_mt[E] * NT;
         const SplitPlan sp = split_plan(T, KT, part ? P : 0);
@@ -514,7 +526,7 @@ void expert_gemm_kernel(
             ke = (int)((int64_t)(s + 1) * KT / sp.nsplit);
         }
         decode_tile(L, s_mt, ll ? s_pp : nullptr, E, NT, BM, BN, e, m0, n0);
-        rows = used[e];
+        rows = s_used[e];
     }
 
     if constexpr ((MODE == 1 || MODE == 5) && BM == 320) {
@@ -542,16 +554,23 @@ void expert_gemm_kernel(
     const unsigned short *gc[RM ? GC : 1];
     int cc[RM ? GC : 1];
     const unsigned short *We = W + (int64_t)__builtin_amdgcn_readfirstlane(e) * Nout * K;
-    if constexpr (RM) {
-        if constexpr (MODE == 0) {
-            // the tile's token rows, one load per thread rather than a chain
-            // of dependent loads per op
-            for (int i = tid; i < BM; i += NTHR) {
-                const int r = m0 + i;
-                s_tok[i] = slot_token[(int64_t)e * ceff + (r < rows ? r : 0)] / k;
-            }
-            __syncthreads();
+    // the tile's token rows (MODE 0) or assignment rows, one load per thread
+    // rather than a chain of dependent loads per op or per strip. The
+    // assignment rows are only read by the epilogue: they are loaded after
+    // the first K-step's operand loads are issued, so that the two round
+    // trips overlap, and published by the main loop's barriers.
+    auto fill_tok = [&]() {
+        for (int i = tid; i < BM; i += NTHR) {
+            const int r = m0 + i;
+            const int v = slot_token[(int64_t)e * ceff + (r < rows ? r : 0)];
+            s_tok[i] = MODE == 0 ? v / k : v;
         }
+    };
+    if constexpr (MODE == 0) {
+        fill_tok();
+        __syncthreads();
+    }
+    if constexpr (RM) {
 #pragma unroll
         for (int i = 0; i < GC; ++i) {
             const int q = min(wv * GC + i, TOT - 1);   // ops past TOT are not issued
@@ -802,6 +821,8 @@ void expert_gemm_kernel(
         for (int s = 0; s < S - 1; ++s)
             if (kb + s < ke)
                 issue(kb + s);
+        if constexpr (TOK && MODE != 0)
+            fill_tok();   // (every workgroup has at least one K-step, so a barrier follows)
         for (int kt = kb; kt < ke; ++kt) {
             // step kt must have landed: later steps issued so far may stay in flight
             const int later = min(S - 2, ke - 1 - kt);
@@ -934,7 +955,7 @@ void expert_gemm_kernel(
                 // they all take this branch and agree on the group's shift)
                 static_assert(!(MODE == 1 || MODE == 5) || kYGroup % CPL == 0,
                               "a lane's columns lie in one group of Y");
-                const int64_t arow = (int64_t)slot_token[srow];
+                const int64_t arow = (int64_t)s_tok[tr];
                 const float *bp = bias ? bias + (int64_t)e * Nout + nb : nullptr;
                 float amax = 0.f;
 #pragma unroll
@@ -1025,7 +1046,7 @@ void expert_gemm_kernel(
                 else
                     store_dz(std::false_type{});
             } else {
-                const int64_t orow = MODE == 4 ? (int64_t)slot_token[srow] : (int64_t)r;
+                const int64_t orow = MODE == 4 ? (int64_t)s_tok[tr] : (int64_t)r;
                 float *dst = O32 + orow * Nout + nb;
 #pragma unroll
                 for (int c = 0; c < CPL / 4; ++c)

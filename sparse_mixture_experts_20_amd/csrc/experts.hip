@@ -433,9 +433,45 @@ void expert_gemm_kernel(
     const int NT = (Nout + BN - 1) / BN;
     int Kr = K;            // reduction length (MODE 6: the expert's kept rows)
     int KT = (K + BKT - 1) / BKT;
-    const int b = blockIdx.x;
+    // Grouped products (modes 0, 1, 3, 4, 5): the schedule (row-tile prefix
+    // of the experts, split plan, tile order) is set up once per workgroup.
+    // Work items: whole tiles in two launch segments (heavy ones, then light
+    // ones when those go last), each spread over the XCDs, then the K-ranges
+    // of the cut tiles. With the 320-row tiles of the forward products the
+    // launch is persistent: one workgroup per resident slot (a multiple of
+    // the XCD count, so that items b, b + gridDim.x, ... stay on one XCD)
+    // walks items b, b + gridDim.x, ..., and a tile's fixed costs (workgroup
+    // start, schedule set-up) are paid once per workgroup; otherwise one
+    // item per workgroup.
+    constexpr bool GROUPED = MODE != 2 && MODE != 6 && MODE != 7;
+    constexpr bool PERSIST = BM == 320 && (MODE == 0 || MODE == 1 || MODE == 5);
+    SplitPlan sp{0, 0, 1};
+    bool ll = false;
+    int T1 = 0, T18 = 0, T28 = 0, np8 = 0;
+    if constexpr (GROUPED) {
+        if (mt_off) {
+            for (int i = tid; i <= E; i += NTHR)
+                s_mt[i] = mt_off[i];
+            for (int i = tid; i < E; i += NTHR)
+                s_used[i] = used[i];
+            __syncthreads();
+        } else {
+            row_tile_prefix(used, E, BM, s_mt, reinterpret_cast<int *>(s_msk), s_used);
+        }
+        const int T = s_mt[E] * NT;
+        sp = split_plan(T, KT, part ? P : 0);
+        // (the 320-row tile holds every expert of up to 320 rows: a light
+        // last tile is rare there and not worth the extra pass over used)
+        ll = BM == 320 ? false : light_last(used, s_mt, E, NT, BM, P, NTHR, s_pp, s_msk);
+        T1 = ll ? min((s_mt[E] - s_pp[E]) * NT, sp.Tdp) : sp.Tdp;
+        T18 = (T1 + kXcds - 1) / kXcds * kXcds;
+        T28 = (sp.Tdp - T1 + kXcds - 1) / kXcds * kXcds;
+        np8 = (sp.tail * sp.nsplit + kXcds - 1) / kXcds * kXcds;
+    }
+    const int nitems = PERSIST ? T18 + T28 + np8 : (int)blockIdx.x + 1;
+    for (int b = blockIdx.x; b < nitems; b += gridDim.x) {
     int e, m0, n0, rows;
-    int kb = 0, ke = KT;   // K-steps of this workgroup
+    int kb = 0, ke = KT;   // K-steps of this item
     int piece = -1;        // scratch slot of a K-range, or -1 for a whole tile
     if constexpr (MODE == 6) {
         e = blockIdx.y;
@@ -483,43 +519,24 @@ void expert_gemm_kernel(
         m0 = (L % mte) * BM;
         n0 = (L / mte) * BN;
     } else {
-        if (mt_off) {
-            for (int i = tid; i <= E; i += NTHR)
-                s_mt[i] = mt_off[i];
-            for (int i = tid; i < E; i += NTHR)
-                s_used[i] = used[i];
-            __syncthreads();
-        } else {
-            row_tile_prefix(used, E, BM, s_mt, reinterpret_cast<int *>(s_msk), s_used);
-        }
-        const int T = s_mt[E] * NT;
-        const SplitPlan sp = split_plan(T, KT, part ? P : 0);
-        // (the 320-row tile holds every expert of up to 320 rows: a light
-        // last tile is rare there and not worth the extra pass over used)
-        const bool ll = BM == 320 ? false : light_last(used, s_mt, E, NT, BM, P, NTHR, s_pp, s_msk);
-        // whole tiles in two launch segments (heavy ones, then light ones
-        // when those go last), each spread over the XCDs; then the K-ranges
-        // of the cut tiles
-        const int T1 = ll ? min((s_mt[E] - s_pp[E]) * NT, sp.Tdp) : sp.Tdp;
-        const int T18 = (T1 + kXcds - 1) / kXcds * kXcds;
-        const int T28 = (sp.Tdp - T1 + kXcds - 1) / kXcds * kXcds;
+        // (an item past the schedule's end: `continue` leaves the loop, or
+        // goes on to this workgroup's next item, with every wave alike)
         int L;
         if (b < T18) {
             L = xcd_index(b, T18);
             if (L >= T1)
-                return;
+                continue;
         } else if (b < T18 + T28) {
             L = T1 + xcd_index(b - T18, T28);
             if (L >= sp.Tdp)
-                return;
+                continue;
         } else {
             const int np = sp.tail * sp.nsplit;
-            const int np8 = (np + kXcds - 1) / kXcds * kXcds;
             if (b - T18 - T28 >= np8)
-                return;
+                continue;
             piece = xcd_index(b - T18 - T28, np8);
             if (piece >= np)
-                return;
+                continue;
             L = sp.Tdp + piece / sp.nsplit;
             const int s = piece % sp.nsplit;
             kb = (int)((int64_t)s * KT / sp.nsplit);
@@ -536,7 +553,7 @@ void expert_gemm_kernel(
         // when all CUs start together they all write at once and the write
         // phases add up, while spread out they overlap other CUs' products.
         // At most 28 us once per launch; every wave leaves the wait.
-        if (b < P && piece < 0) {
+        if (b == (int)blockIdx.x && b < P && piece < 0) {
             const long long t0 = wall_clock64();   // 100 MHz
             const long long dt = (long long)((b / kXcds) % 8) * 400;
             while (wall_clock64() - t0 < dt)
@@ -1055,6 +1072,9 @@ void expert_gemm_kernel(
             }
         }
     }
+    if constexpr (PERSIST)
+        __syncthreads();   // the next item reuses the LDS (operand stages, epilogue scratch, s_tok)
+    }   // items of this workgroup
 }
 
 // Sum of the K-range partials of the cut tiles, in K order, then the same
@@ -1324,8 +1344,12 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
                        KT >= 2 * kSplitMinSteps &&
                        tmax >= P && tmax < 6 * (int64_t)P;
     // whole tiles take two XCD-rounded segments (one more group of kXcds)
-    const int64_t grid = (tmax + kXcds - 1) / kXcds * kXcds + kXcds +
-                         (split ? (int64_t)(P + kXcds - 1) / kXcds * kXcds : 0);
+    int64_t grid = (tmax + kXcds - 1) / kXcds * kXcds + kXcds +
+                   (split ? (int64_t)(P + kXcds - 1) / kXcds * kXcds : 0);
+    // the 320-row tiles' persistent launch: one workgroup per resident slot,
+    // a multiple of the XCD count (the kernel walks the items)
+    if (BM == 320 && (MODE == 0 || MODE == 1 || MODE == 5) && P >= kXcds)
+        grid = std::min<int64_t>(grid, P / kXcds * kXcds);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHR), 0, s, A, W, (int)K, (int)Nout, E,
                        k, (int)ceff, used, slot_token, mt, O16, O32, split ? part : nullptr,
                        P, act, bias, mask, Z16, dp, (int64_t)0, (int64_t)0, (int64_t)0, ysh);

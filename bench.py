@@ -413,7 +413,7 @@ def bench_forward(args, wl, dev):
     compact = x.dtype == torch.bfloat16
     Y = torch.empty((wl.N * wl.k, wl.d), dtype=torch.float16 if compact else torch.float32,
                     device="cuda")
-    Ysh = torch.empty((wl.N * wl.k, B.y_groups(wl.d)), dtype=torch.int8, device="cuda")
+    Ysh = torch.empty((wl.N, B.y_groups(wl.d), wl.k), dtype=torch.int8, device="cuda")
     out = torch.empty_like(x)
     # each stage's C entry point with its arguments marshalled once, so the
     # timed loop is not bound by Python-side argument handling

@@ -336,8 +336,9 @@ int moe_expert_down(int64_t N, const moe_tensor *W_down, int k, int64_t capacity
 
 /* moe_expert_down_ex writing Y compact, the form in which the fused entry
  * points of a bf16 layer keep it (see moe_forward's numerics): Y16 [N*k, d]
- * fp16 bits and Ysh [N*k][ceil(d / 32)] int8 shifts, row a standing for
- * y[a, c] = Y16[a, c] * 2^-Ysh[a][c / 32]. Y16 16-byte aligned. bf16 layers
+ * fp16 bits and Ysh [N][ceil(d / 32)][k] int8 shifts, assignment a = t*k + j
+ * standing for y[a, c] = Y16[a, c] * 2^-Ysh[t][c / 32][j] (a token's k
+ * shifts of one group adjacent). Y16 16-byte aligned. bf16 layers
  * only (MOE_ERR_DTYPE otherwise); rows of dropped assignments are not
  * written. Callers that time or check the fused layer's stages use it. */
 int moe_expert_down_compact(int64_t N, const moe_tensor *W_down, const moe_expert_opts *opts,

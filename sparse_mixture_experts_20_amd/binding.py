@@ -671,14 +671,14 @@ def y_groups(d):
 def expert_down_compact(N, W_down, k, capacity_, used, slot_token, tiles, H, Y16=None,
                         Ysh=None, workspace="auto", stream=None, b_down=None, dropout=None):
     """The down product writing compact rows, as the fused bf16 layer keeps
-    them: returns (Y16 [N*k, d] float16, Ysh [N*k, ceil(d/32)] int8), value
-    = Y16 * 2**-Ysh per group of 32 columns."""
+    them: returns (Y16 [N*k, d] float16, Ysh [N, ceil(d/32), k] int8); the
+    value of Y16[t*k + j, c] is Y16[t*k + j, c] * 2**-Ysh[t, c // 32, j]."""
     import torch
     d = W_down.shape[1]
     if Y16 is None:
         Y16 = torch.zeros((N * k, d), dtype=torch.float16, device=W_down.device)
     if Ysh is None:
-        Ysh = torch.zeros((N * k, y_groups(d)), dtype=torch.int8, device=W_down.device)
+        Ysh = torch.zeros((N, y_groups(d), k), dtype=torch.int8, device=W_down.device)
     dd = desc(W_down)
     wp, wn = _ws_args(_expert_ws(workspace, W_down.dtype, W_down.device))
     o = _opts("relu", None, b_down, dropout) or ExpertOpts("relu", None, b_down)

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ Y,
 // the slots and gates of 8 choices loaded together, then their kept rows
 // and shifts, accumulated in choice order. The rows stay fp16 in registers
 // until they are added (half the registers of fp32 rows).
-template <bool BF16, int VEC>
+template <bool BF16, int VEC, bool OFF32, bool SH8>
 __global__ __launch_bounds__(256) void combine_compact_kernel(
     const unsigned short *__restrict__ Y, const signed char *__restrict__ ysh,
     const float *__restrict__ gate, const int32_t *__restrict__ slot, int64_t N, int d, int k,
@@ -154,14 +154,28 @@ __global__ __launch_bounds__(256) void combine_compact_kernel(
                 kept[u] = j0 + u < k && slot[a] >= 0;
                 g[u] = gate[a];
             }
+            // the shifts of these choices' group are adjacent (token, group,
+            // choice order): with k a multiple of 8, one 8-byte load (SH8)
+            const int64_t sbase = (t * G + c / kYGroup) * k + j0;
+            uint64_t sh8 = 0;
+            if constexpr (SH8)
+                sh8 = *reinterpret_cast<const uint64_t *>(ysh + sbase);
 #pragma unroll
             for (int u = 0; u < kGroup; ++u)
                 if (kept[u]) {
                     const int64_t a = t * k + j0 + u;
+                    // (OFF32: every offset fits in 32 bits, so a load takes a
+                    // 32-bit offset from the uniform base: fewer registers)
+                    const unsigned short *yr;
+                    if constexpr (OFF32)
+                        yr = Y + (uint32_t)((uint32_t)a * (uint32_t)d + (uint32_t)c);
+                    else
+                        yr = Y + a * d + c;
 #pragma unroll
                     for (int q = 0; q < VEC / 8; ++q)
-                        raw[u][q] = *reinterpret_cast<const u32x4 *>(Y + a * d + c + 8 * q);
-                    sc[u] = pow2f(-(int)ysh[a * G + c / kYGroup]);
+                        raw[u][q] = *reinterpret_cast<const u32x4 *>(yr + 8 * q);
+                    const int sh = SH8 ? (int)(signed char)(sh8 >> (8 * u)) : (int)ysh[sbase + u];
+                    sc[u] = pow2f(-sh);
                 }
 #pragma unroll
             for (int u = 0; u < kGroup; ++u)
@@ -230,11 +244,21 @@ hipError_t launch_combine_compact(const void *Y, const signed char *ysh, const f
                            out);
         return hipGetLastError();
     };
+    // 32-bit element offsets when the rows of Y fit; the shifts of 8 choices
+    // in one load when k is a multiple of 8 and they are 8-byte aligned
+    const bool off32 = N * k * d < ((int64_t)1 << 32);
+    const bool sh8 = k % 8 == 0 && reinterpret_cast<uintptr_t>(ysh) % 8 == 0;
+    if (off32 && sh8 && d % 16 == 0)
+        return out_dtype == 1 ? go(combine_compact_kernel<true, 16, true, true>, 16)
+                              : go(combine_compact_kernel<false, 16, true, true>, 16);
+    if (off32 && d % 16 == 0)
+        return out_dtype == 1 ? go(combine_compact_kernel<true, 16, true, false>, 16)
+                              : go(combine_compact_kernel<false, 16, true, false>, 16);
     if (d % 16 == 0)
-        return out_dtype == 1 ? go(combine_compact_kernel<true, 16>, 16)
-                              : go(combine_compact_kernel<false, 16>, 16);
-    return out_dtype == 1 ? go(combine_compact_kernel<true, 8>, 8)
-                          : go(combine_compact_kernel<false, 8>, 8);
+        return out_dtype == 1 ? go(combine_compact_kernel<true, 16, false, false>, 16)
+                              : go(combine_compact_kernel<false, 16, false, false>, 16);
+    return out_dtype == 1 ? go(combine_compact_kernel<true, 8, false, false>, 8)
+                          : go(combine_compact_kernel<false, 8, false, false>, 8);
 }
 
 hipError_t launch_combine(const void *Y, int y_dtype, const float *gate, const int32_t *slot,

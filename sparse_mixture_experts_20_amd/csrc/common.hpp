@@ -61,6 +61,13 @@ __device__ __forceinline__ int yshift_of(float m) {
     const int sh = 141 - (int)((__float_as_uint(m) >> 23) & 0xffu);
     return sh > 126 ? 126 : sh;
 }
+// Shifts are stored per token, then per group, then per choice: the shift of
+// assignment a = t*k + j's group g is at (t*G + g)*k + j (G groups per row),
+// so a token's k shifts of one group are adjacent.
+__device__ __forceinline__ int64_t yshift_index(int64_t a, int k, int G, int g) {
+    const int64_t t = a / k;
+    return (t * G + g) * k + (a - t * k);
+}
 // acc raised to |v| when v is finite (NaN and infinities are ignored).
 __device__ __forceinline__ float finite_max(float acc, float v) {
     const float a = fabsf(v);
@@ -182,7 +189,7 @@ hipError_t launch_expert_up(bool bf16, const void *x, const void *w_up, int64_t 
                             const float *b_up, hipStream_t s, void *Z = nullptr);
 // dp: training-mode dropout on the rows of Y (default: none). ysh (bf16
 // layers): when not NULL, Y is written compact, fp16 [N*k, d] with the
-// shifts in ysh [N*k][ceil(d / kYGroup)]; otherwise Y is fp32 [N*k, d].
+// shifts in ysh [N][ceil(d / kYGroup)][k]; otherwise Y is fp32 [N*k, d].
 hipError_t launch_expert_down(bool bf16, const void *H, const void *w_down, int64_t d,
                               int64_t d_ff, int E, int k, int64_t ceff, const int32_t *used,
                               const int32_t *slot_token, const int32_t *tiles, void *Y,
@@ -277,8 +284,8 @@ hipError_t launch_router_scores_bf16(const void *x, const void *wsp, int64_t N, 
 hipError_t launch_combine(const void *Y, int y_dtype, const float *gate, const int32_t *slot,
                           int64_t N, int64_t d, int k, void *out, int out_dtype,
                           hipStream_t s);
-// The same over compact rows: Y fp16 [N*k, d] with shifts ysh [N*k][ceil(d /
-// kYGroup)] (see kYGroup); d % 8 == 0.
+// The same over compact rows: Y fp16 [N*k, d] with shifts ysh [N][ceil(d /
+// kYGroup)][k] (see yshift_index); d % 8 == 0.
 hipError_t launch_combine_compact(const void *Y, const signed char *ysh, const float *gate,
                                   const int32_t *slot, int64_t N, int64_t d, int k, void *out,
                                   int out_dtype, hipStream_t s);

@@ -347,8 +347,8 @@ __device__ __forceinline__ int xcd_index(int b, int T8) {
 // Z16 (MODE 0): when not NULL, the bf16 pre-activations (product plus bias)
 // are stored there too, [E, ceff, Nout] like H (by the fix-up for cut tiles).
 // ysh (MODES 1, 5): when not NULL, the rows of Y are stored compact (fp16
-// values into O16 and one exponent shift per kYGroup columns into ysh,
-// [rows of Y][ceil(Nout / kYGroup)]) instead of fp32 into O32.
+// values into O16 and one exponent shift per kYGroup columns into ysh, at
+// yshift_index) instead of fp32 into O32.
 // 5: MODE 1 with training-mode dropout dp on the rows of Y, after the bias
 // (its own instantiation, so that the plain down product's epilogue carries
 // none of the generator's code or registers).
@@ -1016,8 +1016,8 @@ void expert_gemm_kernel(
                         }
                     }
                     if (nb % kYGroup == 0 && nb < Nout)   // (groups past Nout: none)
-                        ysh[arow * ((Nout + kYGroup - 1) / kYGroup) + nb / kYGroup] =
-                            (signed char)sh;
+                        ysh[yshift_index(arow, k, (Nout + kYGroup - 1) / kYGroup,
+                                         nb / kYGroup)] = (signed char)sh;
                 } else {
                     float *dst = O32 + arow * Nout + nb;
 #pragma unroll
@@ -1087,7 +1087,7 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
     const int32_t *__restrict__ slot_token, const int32_t *__restrict__ mt_off,
     const float *__restrict__ part, int P, unsigned short *__restrict__ O16,
     float *__restrict__ O32, int act, const float *__restrict__ bias, Dropout dp,
-    unsigned short *__restrict__ Z16, signed char *__restrict__ ysh) {
+    unsigned short *__restrict__ Z16, signed char *__restrict__ ysh, int k) {
     constexpr int STRIPS = BM / 16;
     static_assert((BN / 4) % (kYGroup / 4) == 0, "a group of Y lies in one row of threads");
     __shared__ int s_mt[kMaxExperts + 1];
@@ -1148,7 +1148,8 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
                 *reinterpret_cast<u32x2 *>(O16 + orow * Nout + n) =
                     u32x2{pack_f16x2(z[0], z[1]), pack_f16x2(z[2], z[3])};
                 if (n % kYGroup == 0)
-                    ysh[orow * ((Nout + kYGroup - 1) / kYGroup) + n / kYGroup] = (signed char)sh;
+                    ysh[yshift_index(orow, k, (Nout + kYGroup - 1) / kYGroup, n / kYGroup)] =
+                        (signed char)sh;
             }
             continue;
         }
@@ -1359,7 +1360,7 @@ hipError_t launch_tiles(const unsigned short *A, const unsigned short *W, int64_
     hipLaunchKernelGGL((split_fixup_kernel<BM, BN, BKT, MODE == 0 ? 0 : 1>),
                        dim3((unsigned)(P * (BM / 16))),
                        dim3(256), 0, s, (int)K, (int)Nout, E, (int)ceff, used, slot_token, mt,
-                       (const float *)part, P, O16, O32, act, bias, dp, Z16, ysh);
+                       (const float *)part, P, O16, O32, act, bias, dp, Z16, ysh, k);
     return hipGetLastError();
 }
 

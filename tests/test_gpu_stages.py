@@ -322,7 +322,10 @@ def test_compact_rows_encode_the_fp32_rows(torch_mod, name):
     y32 = G.to_np(Y32)[kept]
     vals, sh = _encode_compact(y32)
     got_v = Y16.cpu().numpy()[kept]
-    got_s = Ysh.cpu().numpy()[kept]
+    # shifts stored [token, group, choice]: as rows of assignments [N*k, groups]
+    gs = Ysh.cpu().numpy()
+    assert gs.shape == (wl.N, (wl.d + 31) // 32, wl.k)
+    got_s = gs.transpose(0, 2, 1).reshape(wl.N * wl.k, -1)[kept]
     np.testing.assert_array_equal(got_s, sh)
     np.testing.assert_array_equal(got_v.view(np.uint16), vals.view(np.uint16))
     # the combine over compact rows against the combine over their values

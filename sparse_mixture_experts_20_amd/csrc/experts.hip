@@ -137,6 +137,21 @@ __device__ __forceinline__ float activate(float z) {
         return fmaxf(z, 0.f);
 }
 
+// Largest v over aligned groups of G (1, 2 or 4) adjacent lanes, by
+// data-parallel moves within each quad of lanes (quad_perm: lane ^ 1, then
+// lane ^ 2): no LDS round trip. Every lane of a group must be active.
+template <int G>
+__device__ __forceinline__ float quad_group_max(float v) {
+    static_assert(G == 1 || G == 2 || G == 4, "groups within a quad");
+    if constexpr (G >= 2)
+        v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF,
+                                                               0xF, false)));   // [1,0,3,2]
+    if constexpr (G == 4)
+        v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF,
+                                                               0xF, false)));   // [2,3,0,1]
+    return v;
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
 // LDS offset m0 + 16*l (one wave moves 1 KB). Issued in asm so that the
 // compiler's wait insertion does not treat every later LDS read as aliasing
@@ -904,6 +919,12 @@ void expert_gemm_kernel(
     float *scr = reinterpret_cast<float *>(smem) + wv * 16 * SLD;
     const int rr = lane >> 2;            // strip row read back by this lane
     const int cg = (lane & 3) * CPL;     // its first column
+    // The loop over the strips is instantiated per (bias given, compact rows
+    // of Y), so that no strip branches on them (the epilogue's vector
+    // instructions are a visible share of a short tile's time).
+    auto epilogue = [&](auto has_bias, auto compact_y) {
+    constexpr bool HB = decltype(has_bias)::value;
+    constexpr bool CY = decltype(compact_y)::value;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -930,13 +951,13 @@ void expert_gemm_kernel(
                         *reinterpret_cast<f32x4 *>(dst + 4 * c) = v[c];
             } else if (MODE == 0) {
                 unsigned short *dst = O16 + srow * Nout + nb;
-                const float *bp = bias ? bias + (int64_t)e * Nout + nb : nullptr;
+                const float *bp = HB ? bias + (int64_t)e * Nout + nb : nullptr;
                 auto store_h = [&](auto use_gelu) {
 #pragma unroll
                     for (int h = 0; h < CPL / 8; ++h) {
                         if (nb + 8 * h + 8 <= Nout) {
                             f32x4 z0 = v[2 * h], z1 = v[2 * h + 1];
-                            if (bp) {
+                            if constexpr (HB) {
                                 z0 += *reinterpret_cast<const f32x4 *>(bp + 8 * h);
                                 z1 += *reinterpret_cast<const f32x4 *>(bp + 8 * h + 4);
                             }
@@ -973,13 +994,13 @@ void expert_gemm_kernel(
                 static_assert(!(MODE == 1 || MODE == 5) || kYGroup % CPL == 0,
                               "a lane's columns lie in one group of Y");
                 const int64_t arow = (int64_t)s_tok[tr];
-                const float *bp = bias ? bias + (int64_t)e * Nout + nb : nullptr;
+                const float *bp = HB ? bias + (int64_t)e * Nout + nb : nullptr;
                 float amax = 0.f;
 #pragma unroll
                 for (int h = 0; h < CPL / 8; ++h) {
                     if (nb + 8 * h + 8 <= Nout) {
                         f32x4 z0 = v[2 * h], z1 = v[2 * h + 1];
-                        if (bp) {
+                        if constexpr (HB) {
                             z0 += *reinterpret_cast<const f32x4 *>(bp + 8 * h);
                             z1 += *reinterpret_cast<const f32x4 *>(bp + 8 * h + 4);
                         }
@@ -992,17 +1013,30 @@ void expert_gemm_kernel(
                         }
                         v[2 * h] = z0;
                         v[2 * h + 1] = z1;
-                        if (ysh) {
+                        if constexpr (CY) {
+                            // (max of magnitudes, NaN ignored; an infinity
+                            // is taken out below, on the rare path)
 #pragma unroll
                             for (int q = 0; q < 4; ++q)
-                                amax = finite_max(finite_max(amax, z0[q]), z1[q]);
+                                amax = fmaxf(fmaxf(amax, fabsf(z0[q])), fabsf(z1[q]));
                         }
                     }
                 }
-                if (ysh) {
+                if constexpr (CY) {
+                    amax = quad_group_max<kYGroup / CPL>(amax);
+                    if (amax == __builtin_inff()) {
+                        // the group holds an infinity: its largest finite
+                        // magnitude instead (the whole group takes this path)
+                        amax = 0.f;
 #pragma unroll
-                    for (int o = 1; o < kYGroup / CPL; o <<= 1)
-                        amax = fmaxf(amax, __shfl_xor(amax, o));
+                        for (int h = 0; h < CPL / 8; ++h)
+                            if (nb + 8 * h + 8 <= Nout)
+#pragma unroll
+                                for (int q = 0; q < 4; ++q)
+                                    amax = finite_max(finite_max(amax, v[2 * h][q]),
+                                                      v[2 * h + 1][q]);
+                        amax = quad_group_max<kYGroup / CPL>(amax);
+                    }
                     const int sh = yshift_of(amax);
                     const float sc = pow2f(sh);
                     unsigned short *dst = O16 + arow * Nout + nb;
@@ -1071,6 +1105,27 @@ void expert_gemm_kernel(
                         *reinterpret_cast<f32x4 *>(dst + 4 * c) = v[c];
             }
         }
+    }
+    };
+    if constexpr (MODE == 0) {
+        if (bias)
+            epilogue(std::true_type{}, std::false_type{});
+        else
+            epilogue(std::false_type{}, std::false_type{});
+    } else if constexpr (MODE == 1 || MODE == 5) {
+        if (bias) {
+            if (ysh)
+                epilogue(std::true_type{}, std::true_type{});
+            else
+                epilogue(std::true_type{}, std::false_type{});
+        } else {
+            if (ysh)
+                epilogue(std::false_type{}, std::true_type{});
+            else
+                epilogue(std::false_type{}, std::false_type{});
+        }
+    } else {
+        epilogue(std::false_type{}, std::false_type{});
     }
     if constexpr (PERSIST)
         __syncthreads();   // the next item reuses the LDS (operand stages, epilogue scratch, s_tok)

@@ -483,8 +483,10 @@ void expert_gemm_kernel(
         T28 = (sp.Tdp - T1 + kXcds - 1) / kXcds * kXcds;
         np8 = (sp.tail * sp.nsplit + kXcds - 1) / kXcds * kXcds;
     }
-    const int nitems = PERSIST ? T18 + T28 + np8 : (int)blockIdx.x + 1;
-    for (int b = blockIdx.x; b < nitems; b += gridDim.x) {
+    const int nitems = PERSIST ? T18 + T28 + np8 : 0;
+    const int stride = PERSIST ? (int)gridDim.x : 0;
+    // (one trip, known at compile time, unless persistent)
+    for (int it = 0, b = blockIdx.x; PERSIST ? b < nitems : it < 1; ++it, b += stride) {
     int e, m0, n0, rows;
     int kb = 0, ke = KT;   // K-steps of this item
     int piece = -1;        // scratch slot of a K-range, or -1 for a whole tile

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
                     const u32x4 h = *reinterpret_cast<const u32x4 *>(
                         static_cast<const unsigned short *>(Y) + a * d + 8 * c);
                     const float sc = pow2f(-(int)ysh[yshift_index(
-                        a, k, (d + kYGroup - 1) / kYGroup, 8 * c / kYGroup)]);
+                        t, j, k, (d + kYGroup - 1) / kYGroup, 8 * c / kYGroup)]);
                     const f32x2_t p0 = unpack_f16x2(h[0]), p1 = unpack_f16x2(h[1]);
                     const f32x2_t p2 = unpack_f16x2(h[2]), p3 = unpack_f16x2(h[3]);
                     y0 = f32x4{p0[0], p0[1], p1[0], p1[1]} * sc;

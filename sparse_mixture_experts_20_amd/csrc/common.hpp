@@ -63,10 +63,15 @@ __device__ __forceinline__ int yshift_of(float m) {
 }
 // Shifts are stored per token, then per group, then per choice: the shift of
 // assignment a = t*k + j's group g is at (t*G + g)*k + j (G groups per row),
-// so a token's k shifts of one group are adjacent.
-__device__ __forceinline__ int64_t yshift_index(int64_t a, int k, int G, int g) {
-    const int64_t t = a / k;
-    return (t * G + g) * k + (a - t * k);
+// so a token's k shifts of one group are adjacent. Assignment indices fit in
+// 31 bits (N*k < 2^31), so the token comes from a 32-bit division.
+__device__ __forceinline__ int64_t yshift_index(int a, int k, int G, int g) {
+    const unsigned t = (unsigned)a / (unsigned)k;
+    return ((int64_t)t * G + g) * k + (a - (int)t * k);
+}
+// The same for a known token t and choice j.
+__device__ __forceinline__ int64_t yshift_index(int64_t t, int j, int k, int G, int g) {
+    return (t * G + g) * k + j;
 }
 // acc raised to |v| when v is finite (NaN and infinities are ignored).
 __device__ __forceinline__ float finite_max(float acc, float v) {

@@ -1052,7 +1052,7 @@ void expert_gemm_kernel(
                         }
                     }
                     if (nb % kYGroup == 0 && nb < Nout)   // (groups past Nout: none)
-                        ysh[yshift_index(arow, k, (Nout + kYGroup - 1) / kYGroup,
+                        ysh[yshift_index((int)arow, k, (Nout + kYGroup - 1) / kYGroup,
                                          nb / kYGroup)] = (signed char)sh;
                 } else {
                     float *dst = O32 + arow * Nout + nb;
@@ -1205,7 +1205,7 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(
                 *reinterpret_cast<u32x2 *>(O16 + orow * Nout + n) =
                     u32x2{pack_f16x2(z[0], z[1]), pack_f16x2(z[2], z[3])};
                 if (n % kYGroup == 0)
-                    ysh[yshift_index(orow, k, (Nout + kYGroup - 1) / kYGroup, n / kYGroup)] =
+                    ysh[yshift_index((int)orow, k, (Nout + kYGroup - 1) / kYGroup, n / kYGroup)] =
                         (signed char)sh;
             }
             continue;

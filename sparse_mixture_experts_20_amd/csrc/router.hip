@@ -186,12 +186,20 @@ __global__ __launch_bounds__(256) void rank_scores_kernel(const float *__restric
         }
     };
     load(r, v);
-    for (int sp = 1; sp < ns; ++sp) {
-        float w[Q];
-        load(r + (int64_t)sp * N * Ep, w);
+    // the ranges' loads in batches of B in flight, added in range order
+    constexpr int B = 8;
+    for (int s0 = 1; s0 < ns; s0 += B) {
+        float w[B][Q];
 #pragma unroll
-        for (int q = 0; q < Q; ++q)
-            v[q] += w[q];
+        for (int u = 0; u < B; ++u)
+            if (s0 + u < ns)
+                load(r + (int64_t)(s0 + u) * N * Ep, w[u]);
+#pragma unroll
+        for (int u = 0; u < B; ++u)
+            if (s0 + u < ns)
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+                    v[q] += w[u][q];
     }
 #pragma unroll
     for (int q = 0; q < Q; ++q) {

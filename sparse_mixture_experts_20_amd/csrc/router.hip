@@ -68,6 +68,87 @@ __device__ __forceinline__ void split8(const f32x4 &w0, const f32x4 &w1, u32x4 &
     lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
+// Ranking key of (score, expert): ordered as the scores, descending, then the
+// ids, ascending (NaN ranks as -inf; -0 as +0, which compare equal).
+__device__ __forceinline__ uint64_t rank_key(float v, int e) {
+    const float c = v != v ? -INFINITY : v + 0.f;
+    const unsigned b = __float_as_uint(c);
+    const unsigned o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint64_t)(0xffffffffu - (unsigned)e);
+}
+__device__ __forceinline__ float key_score(uint64_t key) {
+    const unsigned o = (unsigned)(key >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint64_t dpp_max(uint64_t x) {
+    const int lo = (int)(unsigned)x, hi = (int)(unsigned)(x >> 32);
+    const unsigned olo = (unsigned)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
+    const unsigned ohi = (unsigned)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    return o > x ? o : x;
+}
+// The largest key of the wave, on every lane: within quads, rows of 16, then
+// across rows; lane 63 ends with the maximum of all 64.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t x) {
+    x = dpp_max<0xb1>(x);          // quad_perm [1,0,3,2]
+    x = dpp_max<0x4e>(x);          // quad_perm [2,3,0,1]
+    x = dpp_max<0x124>(x);         // row_ror:4
+    x = dpp_max<0x128>(x);         // row_ror:8
+    x = dpp_max<0x142, 0xa>(x);    // row_bcast:15 into rows 1 and 3
+    x = dpp_max<0x143, 0xc>(x);    // row_bcast:31 into rows 2 and 3
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)x, 63);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(x >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Top-k of one token's scores held by a whole wave (lane g holds experts g,
+// g+64, ...), as topk_softmax_group below for G = 64: every round takes the
+// wave's largest ranking key by DPP moves (no LDS shuffles) and the softmax
+// sums the kept choices' terms in choice order from uniform reads.
+template <int Q>
+__device__ __forceinline__ void topk_softmax_wave(const float (&v)[Q], int E, int k, int64_t t,
+                                                  bool active, int32_t *__restrict__ idx_out,
+                                                  float *__restrict__ gate_out) {
+    const int lane = __lane_id();
+    uint64_t key[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int e = lane + 64 * q;
+        key[q] = e < E ? rank_key(v[q], e) : 0ull;   // 0: no candidate
+    }
+    float my_v = -INFINITY, v0 = -INFINITY;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+        uint64_t b = key[0];
+#pragma unroll
+        for (int q = 1; q < Q; ++q)
+            b = key[q] > b ? key[q] : b;
+        b = wave_max_key(b);
+        const int be = (int)(0xffffffffu - (unsigned)b);
+        const float bv = key_score(b);
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            if (be == lane + 64 * q)
+                key[q] = 0ull;
+        if (lane == j) {
+            my_v = bv;
+            my_e = be;
+        }
+        if (j == 0)
+            v0 = bv;
+    }
+    const float ex = lane < k ? expf(my_v - v0) : 0.f;
+    float den = 0.f;
+    for (int j = 0; j < k; ++j)   // choice order
+        den += __uint_as_float(
+            (unsigned)__builtin_amdgcn_readlane((int)__float_as_uint(ex), j));
+    if (active && lane < k) {
+        idx_out[t * k + lane] = my_e;
+        gate_out[t * k + lane] = ex / den;
+    }
+}
+
 // Top-k of one token's scores held by a group of G lanes (lane g of the
 // group holds experts g, g+G, ...; a wave ranks 64/G tokens at once) and the
 // softmax of the kept scores. Every lane of a group ends with the same
@@ -76,6 +157,10 @@ template <int G, int Q>
 __device__ __forceinline__ void topk_softmax_group(const float (&v)[Q], int E, int k, int64_t t,
                                                    bool active, int32_t *__restrict__ idx_out,
                                                    float *__restrict__ gate_out) {
+    if constexpr (G == 64) {
+        topk_softmax_wave<Q>(v, E, k, t, active, idx_out, gate_out);
+        return;
+    }
     const int lane = __lane_id();
     const int lg = lane % G, gbase = lane - lg;
     unsigned taken = 0;

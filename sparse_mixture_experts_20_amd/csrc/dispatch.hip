@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
                     acc = hist[(int64_t)c * E + e];
             } else {
                 const int c0 = q * c / kParts, c1 = (q + 1) * c / kParts;
-                constexpr int U = 8;
+                constexpr int U = 16;
                 for (int cc = c0; cc < c1; cc += U) {
                     int h[U];
 #pragma unroll
@@ -370,8 +370,17 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
         if (e < E) {
             float acc = 0.f;
             const int c0 = q * nc / kParts, c1 = (q + 1) * nc / kParts;
-            for (int cc = c0; cc < c1; ++cc)
-                acc += gpart[(int64_t)cc * E + e];
+            constexpr int U = 8;   // loads in flight, added in chunk order
+            for (int cc = c0; cc < c1; cc += U) {
+                float h[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    h[u] = cc + u < c1 ? gpart[(int64_t)(cc + u) * E + e] : 0.f;
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (cc + u < c1)
+                        acc += h[u];
+            }
             gp[q * kMaxExperts + e] = acc;
         }
         __syncthreads();
